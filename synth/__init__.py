@@ -1,0 +1,9 @@
+"""Seeded synthetic inputs shared by the tests, the bench and the oracle's callers.
+
+This package draws random tensors and nothing else: it holds none of the KDA
+arithmetic, and neither the oracle nor the HIP path lives here.
+"""
+
+from .inputs import CONFIGS, decode_inputs, prefill_inputs, config_inputs
+
+__all__ = ["CONFIGS", "decode_inputs", "prefill_inputs", "config_inputs"]

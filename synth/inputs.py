@@ -1,0 +1,116 @@
+"""Seeded CPU synthesis of KDA inputs.
+
+Value distributions (the layer shapes and distributions of the five workloads):
+
+* q, k ``[B, T, H, K]``: standard normal, then divided by their L2 norm over K
+  (in float32, no epsilon), then cast to the workload dtype;
+* v ``[B, T, HV, V]``: standard normal;
+* g ``[B, T, HV, K]``: ``max(-5, -softplus(N(0, 1)))`` (natural-log decay,
+  the "safe gate" lower bound of -5);
+* beta ``[B, T, HV]``: ``sigmoid(N(0, 1))``;
+* initial state ``[B, HV, K, V]`` float32: ``0.1 * N(0, 1)`` or absent (zeros).
+
+Draw order is q, k, v, g, beta, state from one ``torch.Generator('cpu')``
+seeded with ``seed``; everything is computed in float32 and rounded to the
+workload dtype (round to nearest even for bfloat16). The gate and beta modes
+are stress variants used for parity only.
+"""
+
+import math
+
+import torch
+import torch.nn.functional as F
+
+# The five workloads. 'prefill' entries run kda_chunk_fwd; 'decode' runs
+# kda_recurrent_step `steps` times on one in-place state.
+CONFIGS = {
+    0: dict(name="tiny-fp32", kind="prefill", B=2, T=16, H=2, HV=4, K=8, V=8,
+            dtype="fp32", chunk=8, init_state=False),
+    1: dict(name="gva-bf16", kind="prefill", B=2, T=512, H=4, HV=8, K=64, V=64,
+            dtype="bf16", chunk=64, init_state=True),
+    2: dict(name="prefill-B4-T8192-H16-K128", kind="prefill", B=4, T=8192, H=16, HV=16,
+            K=128, V=128, dtype="bf16", chunk=64, init_state=False),
+    3: dict(name="decode-B256-H16-K128-64steps", kind="decode", steps=64, B=256, H=16,
+            HV=16, K=128, V=128, dtype="bf16", init_state=True),
+    4: dict(name="prefill-B1-T32768-H96-K128", kind="prefill", B=1, T=32768, H=96, HV=96,
+            K=128, V=128, dtype="bf16", chunk=64, init_state=True),
+}
+
+DTYPES = {"fp32": torch.float32, "bf16": torch.bfloat16}
+
+
+def _gate(shape, gen, mode):
+    x = torch.randn(shape, generator=gen, dtype=torch.float32)
+    if mode == "default":
+        return torch.clamp(-F.softplus(x), min=-5.0)
+    if mode == "slow":
+        return -0.01 * F.softplus(x)
+    if mode == "zero":
+        return torch.zeros(shape)
+    if mode == "bound":
+        return torch.full(shape, -5.0)
+    raise ValueError(mode)
+
+
+def _beta(shape, gen, mode):
+    x = torch.randn(shape, generator=gen, dtype=torch.float32)
+    if mode == "default":
+        return torch.sigmoid(x)
+    if mode == "small":
+        return torch.sigmoid(x - 7.0)
+    if mode == "large":
+        return torch.sigmoid(x + 7.0)
+    raise ValueError(mode)
+
+
+def _unit(shape, gen):
+    x = torch.randn(shape, generator=gen, dtype=torch.float32)
+    return x / x.norm(dim=-1, keepdim=True)
+
+
+def prefill_inputs(B, T, H, HV, K, V, dtype="bf16", init_state=True, seed=0,
+                   gate="default", beta="default"):
+    """Inputs for one chunked forward. Returns a dict of CPU tensors plus 'scale'."""
+    gen = torch.Generator("cpu").manual_seed(seed)
+    dt = DTYPES[dtype]
+    q = _unit((B, T, H, K), gen).to(dt)
+    k = _unit((B, T, H, K), gen).to(dt)
+    v = torch.randn((B, T, HV, V), generator=gen, dtype=torch.float32).to(dt)
+    g = _gate((B, T, HV, K), gen, gate).to(dt)
+    b = _beta((B, T, HV), gen, beta).to(dt)
+    s0 = None
+    if init_state:
+        s0 = 0.1 * torch.randn((B, HV, K, V), generator=gen, dtype=torch.float32)
+    return dict(q=q, k=k, v=v, g=g, beta=b, initial_state=s0, scale=1.0 / math.sqrt(K))
+
+
+def decode_inputs(steps, B, H, HV, K, V, dtype="bf16", init_state=True, seed=0,
+                  gate="default", beta="default"):
+    """Inputs for `steps` single-token decode steps on one state.
+
+    q, k [steps, B, H, K]; v [steps, B, HV, V]; g [steps, B, HV, K];
+    beta [steps, B, HV]; state [B, HV, K, V] float32."""
+    gen = torch.Generator("cpu").manual_seed(seed)
+    dt = DTYPES[dtype]
+    q = _unit((steps, B, H, K), gen).to(dt)
+    k = _unit((steps, B, H, K), gen).to(dt)
+    v = torch.randn((steps, B, HV, V), generator=gen, dtype=torch.float32).to(dt)
+    g = _gate((steps, B, HV, K), gen, gate).to(dt)
+    b = _beta((steps, B, HV), gen, beta).to(dt)
+    if init_state:
+        s0 = 0.1 * torch.randn((B, HV, K, V), generator=gen, dtype=torch.float32)
+    else:
+        s0 = torch.zeros((B, HV, K, V), dtype=torch.float32)
+    return dict(q=q, k=k, v=v, g=g, beta=b, state=s0, scale=1.0 / math.sqrt(K))
+
+
+def config_inputs(index, **overrides):
+    """Inputs for workload `index` with its standard seed (1234 + index)."""
+    c = dict(CONFIGS[index])
+    c.update(overrides)
+    seed = c.pop("seed", 1234 + index)
+    if c["kind"] == "decode":
+        return decode_inputs(c["steps"], c["B"], c["H"], c["HV"], c["K"], c["V"],
+                             c["dtype"], c["init_state"], seed)
+    return prefill_inputs(c["B"], c["T"], c["H"], c["HV"], c["K"], c["V"], c["dtype"],
+                          c["init_state"], seed)
