@@ -1,0 +1,141 @@
+"""MI355X-native Kimi Delta Attention (KDA) forward: Python binding of libkda.so.
+
+The binding only marshals arguments: it checks devices, dtypes, shapes and
+contiguity, allocates outputs with torch (device memory and streams are all
+torch is used for) and calls the C ABI declared in ``include/kda.h``. Every step
+of the computation runs in the HIP kernels. There is no CPU or PyTorch fallback:
+if ``libkda.so`` is missing or a call fails, an error is raised.
+
+Entry points (same names as the C ABI):
+
+* ``kda_chunk_fwd(q, k, v, g, beta, scale=None, initial_state=None,
+  output_final_state=True, chunk_size=64) -> (o, final_state)``
+* ``kda_recurrent_step(q, k, v, g, beta, state, scale=None) -> o`` (updates
+  ``state`` in place)
+"""
+
+import ctypes
+import math
+import os
+
+import torch
+
+__all__ = ["kda_chunk_fwd", "kda_recurrent_step", "library", "library_path", "status_string",
+           "KDA_OK", "KDA_ERR_INVALID", "KDA_ERR_UNSUPPORTED", "KDA_ERR_HIP"]
+
+KDA_OK, KDA_ERR_INVALID, KDA_ERR_UNSUPPORTED, KDA_ERR_HIP = 0, -1, -2, -3
+_DTYPE = {torch.float32: 0, torch.bfloat16: 1}
+
+library_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
+_lib = None
+
+
+def library():
+    """Load libkda.so (once) and declare its C signatures. Raises if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(library_path):
+        raise RuntimeError(f"{library_path} is not built; run `python -m gated_delta_rule_67_amd.build`")
+    lib = ctypes.CDLL(library_path)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.kda_chunk_fwd.argtypes = [vp] * 8 + [i] * 6 + [f, i, i, vp, sz, vp]
+    lib.kda_chunk_fwd.restype = i
+    lib.kda_chunk_fwd_workspace_size.argtypes = [i] * 8
+    lib.kda_chunk_fwd_workspace_size.restype = sz
+    lib.kda_recurrent_step.argtypes = [vp] * 7 + [i] * 5 + [f, i, vp]
+    lib.kda_recurrent_step.restype = i
+    lib.kda_status_string.argtypes = [i]
+    lib.kda_status_string.restype = ctypes.c_char_p
+    lib.kda_version.argtypes = []
+    lib.kda_version.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def status_string(rc):
+    return library().kda_status_string(int(rc)).decode()
+
+
+def _check(rc):
+    if rc != KDA_OK:
+        raise RuntimeError(status_string(rc))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _require(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _check_tensors(named, dtype, device):
+    for name, t in named:
+        _require(t.device == device, f"{name} is on {t.device}, expected {device}")
+        _require(t.dtype == dtype, f"{name} has dtype {t.dtype}, expected {dtype}")
+        _require(t.is_contiguous(), f"{name} must be contiguous")
+
+
+def kda_chunk_fwd(q, k, v, g, beta, scale=None, initial_state=None, output_final_state=True,
+                  chunk_size=64):
+    """Chunked KDA prefill. q, k [B,T,H,K]; v [B,T,HV,V]; g [B,T,HV,K]; beta [B,T,HV];
+    initial_state [B,HV,K,V] float32 or None. Returns (o [B,T,HV,V], final_state or None)."""
+    _require(q.is_cuda, "inputs must be on a GPU")
+    dev, dt = q.device, q.dtype
+    _require(dt in _DTYPE, f"unsupported dtype {dt}")
+    B, T, H, K = q.shape
+    HV, V = v.shape[2], v.shape[3]
+    _require(k.shape == q.shape, "k must match q")
+    _require(tuple(v.shape[:2]) == (B, T), "v must be [B, T, HV, V]")
+    _require(tuple(g.shape) == (B, T, HV, K), "g must be [B, T, HV, K]")
+    _require(tuple(beta.shape) == (B, T, HV), "beta must be [B, T, HV]")
+    _check_tensors([("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta)], dt, dev)
+    if initial_state is not None:
+        _require(tuple(initial_state.shape) == (B, HV, K, V), "initial_state must be [B, HV, K, V]")
+        _check_tensors([("initial_state", initial_state)], torch.float32, dev)
+    if scale is None:
+        scale = 1.0 / math.sqrt(K)
+    lib = library()
+    o = torch.empty((B, T, HV, V), dtype=dt, device=dev)
+    final = torch.empty((B, HV, K, V), dtype=torch.float32, device=dev) if output_final_state else None
+    ws_bytes = lib.kda_chunk_fwd_workspace_size(B, T, H, HV, K, V, chunk_size, _DTYPE[dt])
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        rc = lib.kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
+                               _ptr(final), _ptr(o), B, T, H, HV, K, V, float(scale),
+                               int(chunk_size), _DTYPE[dt], _ptr(ws), ws_bytes,
+                               ctypes.c_void_p(stream))
+    _check(rc)
+    return o, final
+
+
+def kda_recurrent_step(q, k, v, g, beta, state, scale=None):
+    """One decode token. q, k [B,H,K] (or [B,1,H,K]); v [B,HV,V]; g [B,HV,K]; beta [B,HV];
+    state [B,HV,K,V] float32, updated in place. Returns o [B,HV,V]."""
+    _require(q.is_cuda, "inputs must be on a GPU")
+    dev, dt = q.device, q.dtype
+    _require(dt in _DTYPE, f"unsupported dtype {dt}")
+    if q.dim() == 4:
+        q, k, v, g, beta = q[:, 0], k[:, 0], v[:, 0], g[:, 0], beta[:, 0]
+    B, H, K = q.shape
+    HV, V = v.shape[1], v.shape[2]
+    _require(k.shape == q.shape, "k must match q")
+    _require(tuple(g.shape) == (B, HV, K), "g must be [B, HV, K]")
+    _require(tuple(beta.shape) == (B, HV), "beta must be [B, HV]")
+    _require(tuple(state.shape) == (B, HV, K, V), "state must be [B, HV, K, V]")
+    _check_tensors([("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta)], dt, dev)
+    _check_tensors([("state", state)], torch.float32, dev)
+    if scale is None:
+        scale = 1.0 / math.sqrt(K)
+    lib = library()
+    o = torch.empty((B, HV, V), dtype=dt, device=dev)
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        rc = lib.kda_recurrent_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state),
+                                    _ptr(o), B, H, HV, K, V, float(scale), _DTYPE[dt],
+                                    ctypes.c_void_p(stream))
+    _check(rc)
+    return o

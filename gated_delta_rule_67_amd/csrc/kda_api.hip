@@ -1,0 +1,93 @@
+// C ABI of the KDA library: argument validation, then kernel dispatch.
+// Nothing here allocates device memory or synchronises.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/kda.h"
+#include "kda_device.h"
+
+namespace kda {
+template <typename Tin>
+hipError_t launch_decode(const void*, const void*, const void*, const void*, const void*, float*,
+                         void*, int, int, int, int, int, float, hipStream_t);
+hipError_t launch_prefill(const void*, const void*, const void*, const void*, const void*,
+                          const float*, float*, void*, int, int, int, int, int, int, float, bool,
+                          hipStream_t);
+}  // namespace kda
+
+namespace {
+
+constexpr int kMaxDim = 128;
+
+bool positive(int x) { return x >= 1; }
+
+int check_common(int B, int H, int HV, int K, int V, float scale, int dtype) {
+  if (!positive(B) || !positive(H) || !positive(HV) || !positive(K) || !positive(V))
+    return KDA_ERR_INVALID;
+  if (HV % H != 0) return KDA_ERR_INVALID;
+  if (!isfinite(scale)) return KDA_ERR_INVALID;
+  if (dtype != KDA_DTYPE_F32 && dtype != KDA_DTYPE_BF16) return KDA_ERR_INVALID;
+  if (K > kMaxDim || V > kMaxDim) return KDA_ERR_UNSUPPORTED;
+  return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kda_status_string(int status) {
+  switch (status) {
+    case KDA_OK: return "KDA_OK";
+    case KDA_ERR_INVALID: return "KDA_ERR_INVALID: invalid argument (null pointer, dims, chunk size or scale)";
+    case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED: valid shape with no kernel in this build";
+    case KDA_ERR_HIP: return "KDA_ERR_HIP: the HIP runtime reported an error at launch";
+    default: return "KDA: unknown status";
+  }
+}
+
+const char* kda_version(void) { return "kda-gfx950 0.1"; }
+
+size_t kda_chunk_fwd_workspace_size(int, int, int, int, int, int, int, int) {
+  return 0;  // the fused prefill keeps every intermediate on chip
+}
+
+int kda_chunk_fwd(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                  const float* initial_state, float* final_state, void* o, int B, int T, int H,
+                  int HV, int K, int V, float scale, int chunk_size, int dtype, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  if (!q || !k || !v || !g || !beta || !o) return KDA_ERR_INVALID;
+  if (!positive(T)) return KDA_ERR_INVALID;
+  if (chunk_size != 8 && chunk_size != 16 && chunk_size != 32 && chunk_size != 64)
+    return KDA_ERR_INVALID;
+  if (T % chunk_size != 0) return KDA_ERR_INVALID;
+  const int rc = check_common(B, H, HV, K, V, scale, dtype);
+  if (rc != KDA_OK) return rc;
+  if (dtype == KDA_DTYPE_F32 && K > 64) return KDA_ERR_UNSUPPORTED;
+  if ((int64_t)B * HV * ((V + 15) / 16) > INT32_MAX) return KDA_ERR_UNSUPPORTED;
+  const hipError_t e = kda::launch_prefill(q, k, v, g, beta, initial_state, final_state, o, B, T,
+                                           H, HV, K, V, scale, dtype == KDA_DTYPE_BF16,
+                                           static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+int kda_recurrent_step(const void* q, const void* k, const void* v, const void* g,
+                       const void* beta, float* state, void* o, int B, int H, int HV, int K,
+                       int V, float scale, int dtype, void* stream) {
+  if (!q || !k || !v || !g || !beta || !state || !o) return KDA_ERR_INVALID;
+  const int rc = check_common(B, H, HV, K, V, scale, dtype);
+  if (rc != KDA_OK) return rc;
+  if (V % 4 != 0) return KDA_ERR_UNSUPPORTED;
+  if ((int64_t)B * HV * 2 > INT32_MAX) return KDA_ERR_UNSUPPORTED;
+  if ((reinterpret_cast<uintptr_t>(state) & 15) != 0) return KDA_ERR_INVALID;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = dtype == KDA_DTYPE_BF16
+                           ? kda::launch_decode<kda::bf16>(q, k, v, g, beta, state, o, B, H, HV,
+                                                           K, V, scale, s)
+                           : kda::launch_decode<float>(q, k, v, g, beta, state, o, B, H, HV, K,
+                                                       V, scale, s);
+  return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,148 @@
+// Fused single-token KDA decode step on an in-place [B, HV, K, V] float32 state.
+//
+// Per value head (K3 README page "KDA 训练 → 推理 手写实现", roadmap row L6, the
+// recurrent decode against a [B, HV, K, V] state; the step itself is the row-L1
+// recurrence):
+//   s = diag(exp(g)) S                 decay every key row
+//   a = s^T k,  b = s^T (scale q)      two reductions over K, fused in one pass
+//   u = beta (v - a)                   prediction error against the decayed state
+//   o = b + (scale q . k) u            = S_new^T (scale q), without a second pass
+//   S_new = s + k u^T                  written back in place
+//
+// The step is HBM-bound (~1 flop per state byte): one workgroup streams one
+// (b, hv[, V half]) state slab through registers exactly once, with 16-byte
+// coalesced accesses along V and non-temporal hints (the 268 MB state of a
+// 256-sequence, 16-head, 128x128 cache does not fit the last-level cache).
+#include "kda_device.h"
+
+namespace kda {
+
+constexpr int kDecodeThreads = 256;
+constexpr int kDecodeMaxRows = 16;  // K <= 128 with >= 8 row groups per workgroup
+
+template <typename Tin, int VSPLIT>
+__global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(
+    const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
+    const Tin* __restrict__ g, const Tin* __restrict__ beta, float* __restrict__ state,
+    Tin* __restrict__ o, int H, int HV, int K, int V, float scale) {
+  __shared__ float s_dec[128], s_k[128], s_q[128], s_v[128], s_u[128];
+  __shared__ f32x4 s_pa[kDecodeThreads], s_pb[kDecodeThreads];
+  __shared__ float s_qk;
+
+  const int part = blockIdx.x % VSPLIT;
+  const int bh = blockIdx.x / VSPLIT;  // b * HV + hv
+  const int b = bh / HV;
+  const int hv = bh - b * HV;
+  const int h = hv / (HV / H);
+  const int vw = V / VSPLIT;           // columns of this workgroup, multiple of 4
+  const int v0 = part * vw;
+  const int nc = vw >> 2;              // float4 columns
+  const int rgc = kDecodeThreads / nc; // row groups
+  const int t = threadIdx.x;
+  const int c4 = t % nc;
+  const int rg = t / nc;
+  const bool active = rg < rgc;
+
+  float* S = state + (size_t)bh * K * V + v0 + 4 * c4;
+
+  // Issue the whole slab's loads first: they are the critical resource.
+  f32x4 s[kDecodeMaxRows];
+#pragma unroll
+  for (int i = 0; i < kDecodeMaxRows; ++i) {
+    const int r = rg + i * rgc;
+    if (active && r < K)
+      s[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(S + (size_t)r * V));
+    else
+      s[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  const size_t qk_off = ((size_t)b * H + h) * K;
+  const size_t g_off = (size_t)bh * K;
+  if (t < K) {
+    s_dec[t] = fast_exp2(to_f32(g[g_off + t]) * kLog2e);
+    s_k[t] = to_f32(k[qk_off + t]);
+    s_q[t] = to_f32(q[qk_off + t]) * scale;
+  }
+  if (t < vw) s_v[t] = to_f32(v[(size_t)bh * V + v0 + t]);
+  const float bt = to_f32(beta[bh]);
+  __syncthreads();
+
+  if (t < 64) {  // (scale q) . k, one wave
+    float p = 0.f;
+    for (int r = t; r < K; r += 64) p += s_q[r] * s_k[r];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) p += __shfl_xor(p, off);
+    if (t == 0) s_qk = p;
+  }
+
+  f32x4 pa = {0.f, 0.f, 0.f, 0.f}, pb = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < kDecodeMaxRows; ++i) {
+    const int r = rg + i * rgc;
+    if (active && r < K) {
+      s[i] *= s_dec[r];
+      pa += s[i] * s_k[r];
+      pb += s[i] * s_q[r];
+    }
+  }
+  if (active) {
+    s_pa[rg * nc + c4] = pa;
+    s_pb[rg * nc + c4] = pb;
+  }
+  __syncthreads();
+
+  if (t < vw) {
+    const int cc = t >> 2, e = t & 3;
+    float a = 0.f, bq = 0.f;
+    for (int j = 0; j < rgc; ++j) {
+      a += s_pa[j * nc + cc][e];
+      bq += s_pb[j * nc + cc][e];
+    }
+    const float u = bt * (s_v[t] - a);
+    s_u[t] = u;
+    o[(size_t)bh * V + v0 + t] = from_f32<Tin>(bq + s_qk * u);
+  }
+  __syncthreads();
+
+  if (active) {
+    const f32x4 u4 = {s_u[4 * c4], s_u[4 * c4 + 1], s_u[4 * c4 + 2], s_u[4 * c4 + 3]};
+#pragma unroll
+    for (int i = 0; i < kDecodeMaxRows; ++i) {
+      const int r = rg + i * rgc;
+      if (r < K)
+        __builtin_nontemporal_store(s[i] + s_k[r] * u4, reinterpret_cast<f32x4*>(S + (size_t)r * V));
+    }
+  }
+}
+
+// Host-side launcher (called from the C ABI after validation).
+template <typename Tin>
+hipError_t launch_decode(const void* q, const void* k, const void* v, const void* g,
+                         const void* beta, float* state, void* o, int B, int H, int HV,
+                         int K, int V, float scale, hipStream_t stream) {
+  const Tin* q_ = static_cast<const Tin*>(q);
+  const Tin* k_ = static_cast<const Tin*>(k);
+  const Tin* v_ = static_cast<const Tin*>(v);
+  const Tin* g_ = static_cast<const Tin*>(g);
+  const Tin* b_ = static_cast<const Tin*>(beta);
+  Tin* o_ = static_cast<Tin*>(o);
+  const int heads = B * HV;
+  // Split V in two when that keeps >= 4 workgroups per CU-slot worth of work.
+  if (V % 8 == 0 && heads < 8192) {
+    hipLaunchKernelGGL((decode_step_kernel<Tin, 2>), dim3(heads * 2), dim3(kDecodeThreads), 0,
+                       stream, q_, k_, v_, g_, b_, state, o_, H, HV, K, V, scale);
+  } else {
+    hipLaunchKernelGGL((decode_step_kernel<Tin, 1>), dim3(heads), dim3(kDecodeThreads), 0, stream,
+                       q_, k_, v_, g_, b_, state, o_, H, HV, K, V, scale);
+  }
+  return hipGetLastError();
+}
+
+template hipError_t launch_decode<float>(const void*, const void*, const void*, const void*,
+                                         const void*, float*, void*, int, int, int, int, int,
+                                         float, hipStream_t);
+template hipError_t launch_decode<bf16>(const void*, const void*, const void*, const void*,
+                                        const void*, float*, void*, int, int, int, int, int,
+                                        float, hipStream_t);
+
+}  // namespace kda

@@ -1,0 +1,112 @@
+/*
+ * kda.h — C ABI of the MI355X (gfx950) Kimi Delta Attention (KDA) forward library.
+ *
+ * The operator, per value head hv with a K x V float32 state S (the recurrence of
+ * the K3 README page "KDA 训练 → 推理 手写实现", roadmap table row L1, in the order
+ * of operations of the KDA CUDA Trainer README's model paragraph):
+ *
+ *     S'  = diag(exp(g_t)) S                        per-key-channel decay
+ *     S_t = S' + k_t (beta_t (v_t - S'^T k_t))^T     delta-rule write vs. the decayed state
+ *     o_t = S_t^T (scale * q_t)                      read from the updated state
+ *
+ * Grouped value heads (same page, key-constraints table, GVA row): HV = G * H and
+ * value head hv reads q/k head hv / G (q and k repeated G times, interleaved).
+ * scale multiplies q at the entry (same table, scale row); pass 1/sqrt(K).
+ * No fp16 (same page, training notes: fp16 diverges on exp(g) and the cumsum).
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers on the device that owns `stream`;
+ *     tensors are dense, contiguous, row-major in the shapes given below.
+ *   - q, k, v, g, beta and o share one element type `dtype` (float32 or bfloat16);
+ *     states are always float32. o is written in `dtype` (round to nearest even).
+ *   - g is the natural-log decay as given; kernels neither clamp nor transform it.
+ *     Precondition for kda_chunk_fwd's accuracy: -5 <= g <= 0 (the pages' safe-gate
+ *     lower bound); values below -5 are not detected.
+ *   - beta is used as given (already in (0, 1)); one value per (token, value head).
+ *   - `stream` is a hipStream_t (NULL = the null stream). Work is enqueued
+ *     asynchronously; the library never synchronises and keeps no device
+ *     allocations or mutable global state (re-entrant, thread-safe).
+ *   - The caller owns every buffer. Arguments are validated before any launch;
+ *     on a nonzero return nothing was enqueued. Faults inside a kernel surface at
+ *     the caller's next synchronisation. No C++ exception crosses this ABI.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KDA_OK = 0,
+  KDA_ERR_INVALID = -1,     /* null required pointer, bad dims, bad chunk size, non-finite scale */
+  KDA_ERR_UNSUPPORTED = -2, /* valid arguments this build has no kernel for (e.g. K or V > 128) */
+  KDA_ERR_HIP = -3          /* the HIP runtime reported an error at launch */
+} kda_status;
+
+typedef enum { KDA_DTYPE_F32 = 0, KDA_DTYPE_BF16 = 1 } kda_dtype;
+
+/*
+ * Chunked prefill over a whole sequence batch (K3 README, roadmap rows L2 and L3:
+ * in-chunk cumsum of g, a decay-weighted lower-triangular system solved by forward
+ * substitution, intra-chunk attention, sequential state passing between chunks).
+ *
+ *   q, k           [B, T, H, K]   dtype
+ *   v              [B, T, HV, V]  dtype
+ *   g              [B, T, HV, K]  dtype   natural-log decay, -5 <= g <= 0
+ *   beta           [B, T, HV]     dtype
+ *   initial_state  [B, HV, K, V]  float32, or NULL for zeros
+ *   final_state    [B, HV, K, V]  float32 out, or NULL (not returned); may equal
+ *                                 initial_state (each state is read before it is written)
+ *   o              [B, T, HV, V]  dtype out; must not overlap any input
+ *   scale          finite; multiplies q
+ *   chunk_size     8, 16, 32 or 64 and T % chunk_size == 0 (same page, key-constraints
+ *                  table, chunk_size row). The result does not depend on it beyond
+ *                  rounding: kernels tile time by 64 tokens and mask a partial last tile.
+ *   workspace      device scratch of kda_chunk_fwd_workspace_size() bytes (may be NULL
+ *                  when that size is 0)
+ *
+ * Constraints: B, T, H, HV, K, V >= 1; HV % H == 0; K <= 128 and V <= 128 (else
+ * KDA_ERR_UNSUPPORTED); float32 needs K <= 64 (else KDA_ERR_UNSUPPORTED).
+ */
+size_t kda_chunk_fwd_workspace_size(int B, int T, int H, int HV, int K, int V,
+                                    int chunk_size, int dtype);
+
+int kda_chunk_fwd(const void* q, const void* k, const void* v, const void* g,
+                  const void* beta, const float* initial_state, float* final_state,
+                  void* o, int B, int T, int H, int HV, int K, int V, float scale,
+                  int chunk_size, int dtype, void* workspace, size_t workspace_bytes,
+                  void* stream);
+
+/*
+ * One decode token for every (b, hv), state updated IN PLACE (K3 README, roadmap
+ * row L6: recurrent decode against a [B, HV, K, V] state cache; the DM-KDAGQA-1.7B
+ * model card's usage notes: cached generation costs one such step per token).
+ *
+ *   q, k   [B, H, K]      dtype (one token; the same memory as [B, 1, H, K])
+ *   v      [B, HV, V]     dtype
+ *   g      [B, HV, K]     dtype
+ *   beta   [B, HV]        dtype
+ *   state  [B, HV, K, V]  float32, read and overwritten with the new state
+ *   o      [B, HV, V]     dtype out; must not overlap any input or the state
+ *
+ * Constraints: B, H, HV, K, V >= 1; HV % H == 0; K <= 128 and V <= 128, V % 4 == 0
+ * (else KDA_ERR_UNSUPPORTED); scale finite.
+ */
+int kda_recurrent_step(const void* q, const void* k, const void* v, const void* g,
+                       const void* beta, float* state, void* o, int B, int H, int HV,
+                       int K, int V, float scale, int dtype, void* stream);
+
+/* Static, NUL-terminated description of a status code; never NULL. */
+const char* kda_status_string(int status);
+
+/* Library version string, e.g. "kda-gfx950 0.1". */
+const char* kda_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */

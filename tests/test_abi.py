@@ -1,0 +1,115 @@
+"""C-ABI checks that run without a GPU: the library loads, exports every function
+that include/kda.h declares, and rejects invalid arguments before any launch
+(validation returns before the first HIP call, so no device is touched)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_delta_rule_67_amd as kda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(kda.library_path):
+        pytest.skip("libkda.so not built")
+    return kda.library()
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for required in ("kda_chunk_fwd", "kda_chunk_fwd_workspace_size", "kda_recurrent_step",
+                     "kda_status_string", "kda_version"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), f"libkda.so does not export {name}"
+
+
+def test_status_strings(lib):
+    for rc in (kda.KDA_OK, kda.KDA_ERR_INVALID, kda.KDA_ERR_UNSUPPORTED, kda.KDA_ERR_HIP, 7):
+        s = kda.status_string(rc)
+        assert isinstance(s, str) and s
+    assert kda.status_string(kda.KDA_OK) == "KDA_OK"
+    assert lib.kda_version().decode().startswith("kda-gfx950")
+
+
+def test_workspace_is_zero(lib):
+    assert lib.kda_chunk_fwd_workspace_size(4, 8192, 16, 16, 128, 128, 64, 1) == 0
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation
+
+
+def _chunk(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, s0=None, sT=None, o=FAKE, B=2, T=64, H=2,
+             HV=4, K=64, V=64, scale=0.125, chunk=64, dtype=1)
+    a.update(kw)
+    return lib.kda_chunk_fwd(a["q"], a["k"], a["v"], a["g"], a["beta"], a["s0"], a["sT"], a["o"],
+                             a["B"], a["T"], a["H"], a["HV"], a["K"], a["V"], a["scale"],
+                             a["chunk"], a["dtype"], None, 0, None)
+
+
+@pytest.mark.parametrize("bad,rc", [
+    (dict(q=None), kda.KDA_ERR_INVALID),
+    (dict(o=None), kda.KDA_ERR_INVALID),
+    (dict(beta=None), kda.KDA_ERR_INVALID),
+    (dict(B=0), kda.KDA_ERR_INVALID),
+    (dict(T=-1), kda.KDA_ERR_INVALID),
+    (dict(HV=3), kda.KDA_ERR_INVALID),            # HV % H != 0
+    (dict(T=72), kda.KDA_ERR_INVALID),            # T % chunk != 0
+    (dict(chunk=48), kda.KDA_ERR_INVALID),        # not a supported chunk size
+    (dict(chunk=128, T=128), kda.KDA_ERR_INVALID),
+    (dict(scale=float("nan")), kda.KDA_ERR_INVALID),
+    (dict(scale=float("inf")), kda.KDA_ERR_INVALID),
+    (dict(dtype=2), kda.KDA_ERR_INVALID),         # no fp16
+    (dict(K=256), kda.KDA_ERR_UNSUPPORTED),
+    (dict(V=160), kda.KDA_ERR_UNSUPPORTED),
+    (dict(K=128, dtype=0), kda.KDA_ERR_UNSUPPORTED),  # fp32 needs K <= 64
+])
+def test_chunk_fwd_rejects_invalid_arguments(lib, bad, rc):
+    assert _chunk(lib, **bad) == rc
+
+
+def _step(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, state=FAKE, o=FAKE, B=2, H=2, HV=4, K=64,
+             V=64, scale=0.125, dtype=1)
+    a.update(kw)
+    return lib.kda_recurrent_step(a["q"], a["k"], a["v"], a["g"], a["beta"], a["state"], a["o"],
+                                  a["B"], a["H"], a["HV"], a["K"], a["V"], a["scale"], a["dtype"],
+                                  None)
+
+
+@pytest.mark.parametrize("bad,rc", [
+    (dict(state=None), kda.KDA_ERR_INVALID),
+    (dict(q=None), kda.KDA_ERR_INVALID),
+    (dict(H=0), kda.KDA_ERR_INVALID),
+    (dict(HV=6, H=4), kda.KDA_ERR_INVALID),
+    (dict(scale=float("nan")), kda.KDA_ERR_INVALID),
+    (dict(dtype=5), kda.KDA_ERR_INVALID),
+    (dict(state=ctypes.c_void_p(0x1004)), kda.KDA_ERR_INVALID),  # state not 16-byte aligned
+    (dict(V=62), kda.KDA_ERR_UNSUPPORTED),
+    (dict(K=129), kda.KDA_ERR_UNSUPPORTED),
+])
+def test_recurrent_step_rejects_invalid_arguments(lib, bad, rc):
+    assert _step(lib, **bad) == rc
+
+
+def test_binding_fails_loudly_without_a_gpu_tensor():
+    import torch
+    x = torch.zeros(1, 64, 1, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        kda.kda_chunk_fwd(x, x, x, x, torch.zeros(1, 64, 1, dtype=torch.bfloat16))

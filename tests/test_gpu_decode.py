@@ -1,0 +1,98 @@
+"""GPU parity of kda_recurrent_step against the fp64 oracle (called through the C ABI
+via the binding). Tolerances: float32 1e-5 max-abs for the decode step (the K3 README's
+roadmap row L6 checks decode per token at 1e-5), bf16 2e-2 x RMS."""
+
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_67_amd as kda
+from oracle import decode_step
+from synth import CONFIGS, decode_inputs
+from tests.helpers import assert_parity, log, to64
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(steps, B, H, HV, K, V, dtype, seed, sample=None, **modes):
+    inp = decode_inputs(steps, B, H, HV, K, V, dtype, True, seed, **modes)
+    dev = "cuda"
+    state = inp["state"].to(dev).clone()
+    q, k, v, g, beta = (inp[n].to(dev) for n in ("q", "k", "v", "g", "beta"))
+    outs = []
+    for t in range(steps):
+        outs.append(kda.kda_recurrent_step(q[t], k[t], v[t], g[t], beta[t], state, inp["scale"]))
+    torch.cuda.synchronize()
+    o_gpu = torch.stack(outs)
+    bs = np.arange(B) if sample is None else sample[0]
+    hs = np.arange(HV) if sample is None else sample[1]
+    G = HV // H
+    s_ref = to64(inp["state"])[np.ix_(bs, hs)]
+    for t in range(steps):
+        q_t = to64(inp["q"][t])[bs][:, [h // G for h in hs]]
+        k_t = to64(inp["k"][t])[bs][:, [h // G for h in hs]]
+        o_ref, s_ref = decode_step(q_t, k_t, to64(inp["v"][t])[np.ix_(bs, hs)],
+                                   to64(inp["g"][t])[np.ix_(bs, hs)],
+                                   to64(inp["beta"][t])[np.ix_(bs, hs)], s_ref, inp["scale"])
+        og = to64(o_gpu[t])[np.ix_(bs, hs)]
+        if dtype == "fp32":
+            assert np.max(np.abs(og - o_ref)) <= 1e-5, f"step {t}"
+        else:
+            assert_parity(og, o_ref, torch.bfloat16, f"o step {t}")
+    sg = to64(state)[np.ix_(bs, hs)]
+    if dtype == "fp32":
+        assert np.max(np.abs(sg - s_ref)) <= 1e-5
+    else:
+        assert_parity(sg, s_ref, torch.bfloat16, "state")
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("shape", [(3, 2, 4, 8, 8), (2, 4, 8, 64, 64), (2, 1, 3, 128, 128),
+                                   (1, 2, 2, 20, 12)])
+def test_decode_small(dtype, shape):
+    B, H, HV, K, V = shape
+    log(f"decode small dtype={dtype} B={B} H={H} HV={HV} K={K} V={V}")
+    _run(6, B, H, HV, K, V, dtype, seed=100 + K)
+
+
+@pytest.mark.parametrize("gate,beta", [("slow", "default"), ("zero", "large"), ("bound", "small")])
+def test_decode_stress_gates(gate, beta):
+    log(f"decode stress gate={gate} beta={beta}")
+    _run(8, 2, 2, 4, 128, 128, "bf16", seed=7, gate=gate, beta=beta)
+
+
+def test_decode_full_size_sampled_heads():
+    c = CONFIGS[3]
+    log("decode full size B=256 H=16 K=V=128, 64 steps, sampled heads")
+    rng = np.random.default_rng(0)
+    sample = (np.sort(rng.choice(c["B"], 6, replace=False)), np.sort(rng.choice(c["HV"], 3, replace=False)))
+    _run(c["steps"], c["B"], c["H"], c["HV"], c["K"], c["V"], c["dtype"], seed=1234 + 3, sample=sample)
+
+
+def test_decode_leaves_other_heads_alone_and_writes_all_outputs():
+    log("decode poison check")
+    inp = decode_inputs(1, 4, 2, 4, 64, 64, "bf16", True, 3)
+    state = inp["state"].cuda()
+    before = state.clone()
+    o = torch.full((4, 4, 64), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lib = kda.library()
+    import ctypes
+    p = lambda t: ctypes.c_void_p(t.data_ptr())
+    q, k, v, g, beta = (inp[n][0].cuda().contiguous() for n in ("q", "k", "v", "g", "beta"))
+    rc = lib.kda_recurrent_step(p(q), p(k), p(v), p(g), p(beta), p(state), p(o), 4, 2, 4, 64, 64,
+                                float(inp["scale"]), 1, None)
+    torch.cuda.synchronize()
+    assert rc == kda.KDA_OK
+    assert not torch.isnan(o.float()).any()
+    assert not torch.equal(state, before)
+
+
+def test_decode_error_path_raises():
+    log("decode error path")
+    x = torch.zeros(2, 2, 62, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(RuntimeError, match="UNSUPPORTED"):
+        kda.kda_recurrent_step(torch.zeros(2, 2, 8, dtype=torch.bfloat16, device="cuda"),
+                               torch.zeros(2, 2, 8, dtype=torch.bfloat16, device="cuda"), x,
+                               torch.zeros(2, 2, 8, dtype=torch.bfloat16, device="cuda"),
+                               torch.zeros(2, 2, dtype=torch.bfloat16, device="cuda"),
+                               torch.zeros(2, 2, 8, 62, device="cuda"))
