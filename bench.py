@@ -1,0 +1,251 @@
+"""Benchmark of the KDA forward on one MI355X.
+
+A step is one chunked prefill (kda_chunk_fwd) over the prefill workload
+B=4, T=8192, H=HV=16, K=V=128, bf16 inputs, fp32 state, chunk 64 (synthetic,
+seeded; the 16 x 128 head layout and 8,192-token context of the pages' KDA
+layers). `value` is prefill tokens/s (B*T per step). The decode step
+(kda_recurrent_step, 64 consecutive steps on a B=256, H=HV=16, K=V=128 fp32
+state cache) is timed in the same run and reported under "decode".
+
+Timing uses HIP events recorded on the stream the kernels are launched on,
+bracketed by device synchronisation. The roofline object prices the prefill
+kernel's algorithmic bytes (q, k, v, g, beta read once, o and the final state
+written once) against MI355X's 8 TB/s HBM3E peak; the decode object prices its
+algorithmic bytes (state read + write, plus the token vectors) the same way.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFS = 2516.6     # MI355X dense bf16 MFMA, published (no sparsity)
+METRIC = "KDA prefill tokens/s + MFMA util (H=16,K=V=128,T=8192); decode state HBM GB/s"
+PREFILL_KERNEL = "prefill_kernel"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_traffic.json")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def prefill_algorithmic(B, T, H, HV, K, V, ib, state_in, state_out):
+    """Bytes and flops the operator must move / do, per launch.
+
+    Bytes: q, k read once per q/k head; v, g, beta read once; o written once;
+    the K x V fp32 state read (if given) and written once per value head.
+    Flops per token-head (chunk C, triangle-aware): C(3K + 2V) + 6KV + C^2/3."""
+    C = 64
+    tok = B * T
+    byts = tok * (H * 2 * K * ib + HV * (V + K + 1 + V) * ib)
+    byts += B * HV * K * V * 4 * (int(state_in) + int(state_out))
+    flops = tok * HV * (C * (3 * K + 2 * V) + 6 * K * V + C * C / 3.0)
+    return byts, flops
+
+
+def decode_algorithmic(B, H, HV, K, V, ib):
+    """Bytes per decode step: fp32 state read + write, q/k per q/k head, v/g/beta/o per value head."""
+    return B * HV * 2 * K * V * 4 + B * (H * 2 * K + HV * (V + K + 1 + V)) * ib
+
+
+def source_hash():
+    path = os.path.join(ROOT, "gated_delta_rule_67_amd", "csrc", "kda_prefill.hip")
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per prefill launch from the committed rocprofv3 --pmc summary, if the
+    kernel source has not changed since the counters were taken; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256_16") != source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def time_launches(fn, steps, warmup, torch):
+    """Average launch duration in ms over `steps` back-to-back launches (events on the
+    launch stream), plus per-launch median."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record(stream)
+    for i in range(steps):
+        fn()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    total = ev[0].elapsed_time(ev[steps])
+    per.sort()
+    return total / steps, per[len(per) // 2], per[0]
+
+
+def cpu_baseline(tokens):
+    """The fp64 oracle on the first `tokens` tokens of the prefill workload (all batches and
+    heads), single-threaded, on this host."""
+    from oracle import recurrent
+    from synth import config_inputs
+
+    inp = config_inputs(2)
+    sl = {k: (v[:, :tokens] if k in ("q", "k", "v", "g", "beta") else v) for k, v in inp.items()}
+    try:
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(1)
+    except ImportError:  # pragma: no cover
+        limiter = None
+    t0 = time.perf_counter()
+    recurrent(**sl)
+    dt = time.perf_counter() - t0
+    if limiter is not None:
+        limiter.restore_original_limits()
+    B = inp["q"].shape[0]
+    return dict(value=B * tokens / dt, unit="tokens/s", cores=1, kind="oracle",
+                sample=f"first {tokens} of 8192 tokens of the prefill workload, all B=4 x 16 heads "
+                       f"({B * tokens} tokens, {dt:.1f} s, numpy float64, one thread)")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-reps", type=int, default=3)
+    ap.add_argument("--cpu-tokens", type=int, default=768)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path has no multi-GPU code: it would shard by (batch, value head) with no "
+              "communication).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import gated_delta_rule_67_amd as kda
+    from synth import CONFIGS, config_inputs
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    # ---------------- prefill workload
+    c = CONFIGS[2]
+    log(f"bench: generating prefill workload {c['name']}")
+    inp = config_inputs(2)
+    d = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    del inp
+
+    def prefill():
+        return kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["scale"],
+                                 d["initial_state"], True, c["chunk"])
+
+    o, s = prefill()
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all() and torch.isfinite(s).all(), "non-finite prefill output"
+    log(f"bench: timing {args.steps} prefill steps after {args.warmup} warmup")
+    avg_ms, med_ms, min_ms = time_launches(prefill, args.steps, args.warmup, torch)
+    tokens = c["B"] * c["T"]
+    byts, flops = prefill_algorithmic(c["B"], c["T"], c["H"], c["HV"], c["K"], c["V"], 2,
+                                      c["init_state"], True)
+    achieved = byts / (avg_ms * 1e-3) / 1e9
+    tflops = flops / (avg_ms * 1e-3) / 1e12
+    traffic = measured_traffic()
+    del d, o, s
+
+    result = {
+        "metric": METRIC,
+        "value": tokens / (avg_ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": avg_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "KDA chunked prefill B=4 T=8192 H=HV=16 K=V=128 bf16 in, fp32 state, "
+                               "chunk 64, zero initial state",
+                   "B": c["B"], "T": c["T"], "H": c["H"], "HV": c["HV"], "K": c["K"], "V": c["V"],
+                   "chunk_size": c["chunk"], "seed": 1236},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": PREFILL_KERNEL, "algorithmic_bytes_per_launch": byts,
+                     "avg_launch_ms": avg_ms, "median_launch_ms": med_ms, "min_launch_ms": min_ms},
+        "mfma": {"algorithmic_tflops": tflops, "peak_tflops": MFMA_BF16_PEAK_TFS,
+                 "frac": tflops / MFMA_BF16_PEAK_TFS, "algorithmic_flops_per_launch": flops},
+    }
+
+    # ---------------- decode workload
+    if not args.no_decode:
+        c3 = CONFIGS[3]
+        log(f"bench: generating decode workload {c3['name']}")
+        dinp = config_inputs(3)
+        dd = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in dinp.items()}
+        del dinp
+        state = dd["state"].clone()
+        steps = c3["steps"]
+        views = [[dd[n][t] for n in ("q", "k", "v", "g", "beta")] for t in range(steps)]
+
+        def one(t):
+            return kda.kda_recurrent_step(*views[t], state, dd["scale"])
+
+        for t in range(3):  # warm-up on a scratch copy of the state
+            one(t)
+        per_step = []
+        totals = []
+        stream = torch.cuda.current_stream()
+        for _ in range(args.decode_reps):
+            state.copy_(dd["state"])
+            torch.cuda.synchronize()
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+            ev[0].record(stream)
+            for t in range(steps):
+                one(t)
+                ev[t + 1].record(stream)
+            torch.cuda.synchronize()
+            per_step += [ev[t].elapsed_time(ev[t + 1]) for t in range(steps)]
+            totals.append(ev[0].elapsed_time(ev[steps]))
+        step_ms = min(totals) / steps
+        dbytes = decode_algorithmic(c3["B"], c3["H"], c3["HV"], c3["K"], c3["V"], 2)
+        gbs = dbytes / (step_ms * 1e-3) / 1e9
+        per_step.sort()
+        result["decode"] = {
+            "workload": "KDA decode, 64 consecutive steps, B=256 H=HV=16 K=V=128, bf16 vectors, "
+                        "fp32 state [256,16,128,128] updated in place",
+            "value": gbs, "unit": "GB/s", "ms_per_step": step_ms,
+            "tokens_per_s": c3["B"] / (step_ms * 1e-3),
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS, "kernel": "decode_step_kernel",
+                         "algorithmic_bytes_per_launch": dbytes,
+                         "median_launch_ms": per_step[len(per_step) // 2]},
+        }
+        del dd, state, views
+
+    # ---------------- oracle on the host
+    if not args.no_cpu_baseline:
+        log(f"bench: timing the CPU oracle on {args.cpu_tokens} tokens")
+        result["cpu_baseline"] = cpu_baseline(args.cpu_tokens)
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

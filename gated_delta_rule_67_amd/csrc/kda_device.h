@@ -27,4 +27,91 @@ template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return sta
 // +75*log2(e), so the result is finite; denormal results may flush to zero.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS operations, not for
+// its outstanding global loads or stores (a plain __syncthreads() also drains those, which
+// would expose every prefetch and every output store).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Arguments of one chunked-prefill launch (validated by the C ABI).
+struct PrefillArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* g;
+  const void* beta;
+  const float* s0;
+  float* sT;
+  void* o;
+  int B, T, H, HV, K, V;
+  float scale;
+  int vec_qkg, vec_v;
+};
+
+}  // namespace kda
+
+namespace kda {
+
+// ---- MFMA tile products out of LDS (gfx950 v_mfma_f32_16x16x32_bf16).
+// acc(16x16) += A(16 x kk) * B(kk x 16). A is row-major (a[row * lda + k]); B is given
+// transposed and row-major (bt[col * ldb + k]); kk is a multiple of 16. Accumulator
+// layout: lane l holds column l % 16, rows 4 * (l / 16) + 0..3. Operand layout: lane l
+// supplies row (A) / column (B) l % 16 and the 8 consecutive k at 8 * (l / 16) of each
+// 32-wide k step; A and B use the same k order, so the contraction is exact.
+__device__ __forceinline__ void mma16(f32x4& acc, const bf16* a, int lda, const bf16* bt, int ldb,
+                                      int kk, int lane) {
+  const int r = lane & 15, q8 = (lane >> 4) * 8;
+  for (int k0 = 0; k0 < kk; k0 += 32) {
+    bf16x8 av, bv;
+    if (k0 + q8 < kk) {
+      av = *reinterpret_cast<const bf16x8*>(a + r * lda + k0 + q8);
+      bv = *reinterpret_cast<const bf16x8*>(bt + r * ldb + k0 + q8);
+    } else {
+      av = bf16x8{};
+      bv = bf16x8{};
+    }
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc, 0, 0, 0);
+  }
+}
+
+// float32 operands (v_mfma_f32_16x16x4_f32): lane l supplies k = l / 16 of each 4-wide step.
+__device__ __forceinline__ void mma16(f32x4& acc, const float* a, int lda, const float* bt,
+                                      int ldb, int kk, int lane) {
+  const int r = lane & 15, q = lane >> 4;
+  for (int k0 = 0; k0 < kk; k0 += 4)
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[r * lda + k0 + q], bt[r * ldb + k0 + q], acc, 0,
+                                               0, 0);
+}
+
+// As mma16, with an fp32 A operand rounded to the compute type on load.
+__device__ __forceinline__ void mma16_a32(f32x4& acc, const float* a, int lda, const bf16* bt,
+                                          int ldb, int kk, int lane) {
+  const int r = lane & 15, q8 = (lane >> 4) * 8;
+  for (int k0 = 0; k0 < kk; k0 += 32) {
+    bf16x8 av, bv;
+    if (k0 + q8 < kk) {
+      const f32x4 lo = *reinterpret_cast<const f32x4*>(a + r * lda + k0 + q8);
+      const f32x4 hi = *reinterpret_cast<const f32x4*>(a + r * lda + k0 + q8 + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        av[e] = static_cast<bf16>(lo[e]);
+        av[e + 4] = static_cast<bf16>(hi[e]);
+      }
+      bv = *reinterpret_cast<const bf16x8*>(bt + r * ldb + k0 + q8);
+    } else {
+      av = bf16x8{};
+      bv = bf16x8{};
+    }
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc, 0, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void mma16_a32(f32x4& acc, const float* a, int lda, const float* bt,
+                                          int ldb, int kk, int lane) {
+  mma16(acc, a, lda, bt, ldb, kk, lane);
+}
+
 }  // namespace kda

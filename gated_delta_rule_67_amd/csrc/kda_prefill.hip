@@ -74,57 +74,6 @@ struct Lds {
   static_assert(total <= 160 * 1024, "LDS budget");
 };
 
-// acc(16x16) += A(16 x kk) * B(kk x 16). A is row-major (a[row * lda + k]); B is given
-// transposed and row-major (bt[col * ldb + k]). kk is a multiple of 16. The 16x16
-// accumulator layout: lane l holds column l % 16, rows 4 * (l / 16) + 0..3.
-__device__ __forceinline__ void mma16(f32x4& acc, const bf16* a, int lda, const bf16* bt, int ldb,
-                                      int kk, int lane) {
-  const int r = lane & 15, q8 = (lane >> 4) * 8;
-  for (int k0 = 0; k0 < kk; k0 += 32) {
-    bf16x8 av, bv;
-    if (k0 + q8 < kk) {
-      av = *reinterpret_cast<const bf16x8*>(a + r * lda + k0 + q8);
-      bv = *reinterpret_cast<const bf16x8*>(bt + r * ldb + k0 + q8);
-    } else {
-      av = bf16x8{};
-      bv = bf16x8{};
-    }
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc, 0, 0, 0);
-  }
-}
-
-__device__ __forceinline__ void mma16(f32x4& acc, const float* a, int lda, const float* bt,
-                                      int ldb, int kk, int lane) {
-  const int r = lane & 15, q = lane >> 4;
-  for (int k0 = 0; k0 < kk; k0 += 4)
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[r * lda + k0 + q], bt[r * ldb + k0 + q], acc, 0,
-                                               0, 0);
-}
-
-// Same, with an fp32 A operand converted to the compute type on load.
-__device__ __forceinline__ void mma16_a32(f32x4& acc, const float* a, int lda, const bf16* bt,
-                                          int ldb, int kk, int lane) {
-  const int r = lane & 15, q8 = (lane >> 4) * 8;
-  for (int k0 = 0; k0 < kk; k0 += 32) {
-    bf16x8 av, bv;
-    if (k0 + q8 < kk) {
-      const float* ap = a + r * lda + k0 + q8;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) av[e] = static_cast<bf16>(ap[e]);
-      bv = *reinterpret_cast<const bf16x8*>(bt + r * ldb + k0 + q8);
-    } else {
-      av = bf16x8{};
-      bv = bf16x8{};
-    }
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc, 0, 0, 0);
-  }
-}
-
-__device__ __forceinline__ void mma16_a32(f32x4& acc, const float* a, int lda, const float* bt,
-                                          int ldb, int kk, int lane) {
-  mma16(acc, a, lda, bt, ldb, kk, lane);
-}
-
 template <typename T> struct Pair;
 template <> struct Pair<bf16> { typedef bf16x2 type; };
 template <> struct Pair<float> { typedef f32x2 type; };
@@ -154,19 +103,6 @@ __device__ __forceinline__ void load_tile(T* dst, int ldd, const T* __restrict__
   }
 }
 
-struct PrefillArgs {
-  const void* q;
-  const void* k;
-  const void* v;
-  const void* g;
-  const void* beta;
-  const float* s0;
-  float* sT;
-  void* o;
-  int B, T, H, HV, K, V;
-  float scale;
-  int vec_qkg, vec_v;
-};
 
 template <typename CT, int KT, int BV>
 __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs p) {
@@ -534,6 +470,8 @@ static hipError_t launch_prefill_cfg(const PrefillArgs& a, hipStream_t stream) {
 
 static inline bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15) == 0; }
 
+hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
+
 // Returns hipErrorInvalidValue for shapes this build does not instantiate.
 hipError_t launch_prefill(const void* q, const void* k, const void* v, const void* g,
                           const void* beta, const float* s0, float* sT, void* o, int B, int T,
@@ -543,6 +481,9 @@ hipError_t launch_prefill(const void* q, const void* k, const void* v, const voi
   const int vw = bf16_inputs ? 8 : 4;
   a.vec_qkg = (K % vw == 0) && aligned16(q) && aligned16(k) && aligned16(g);
   a.vec_v = (V % vw == 0) && aligned16(v);
+  // The bf16 kernel addresses each batch's tensors through 32-bit buffer offsets.
+  const size_t batch_bytes = (size_t)T * (H > HV ? H : HV) * (K > V ? K : V) * 2;
+  if (bf16_inputs && a.vec_qkg && batch_bytes < ((size_t)1 << 31)) return launch_prefill_bf16(a, stream);
   if (bf16_inputs) {
     if (K <= 32) return V <= 16 ? launch_prefill_cfg<bf16, 32, 16>(a, stream) : launch_prefill_cfg<bf16, 32, 32>(a, stream);
     if (K <= 64) return V <= 16 ? launch_prefill_cfg<bf16, 64, 16>(a, stream) : launch_prefill_cfg<bf16, 64, 32>(a, stream);
