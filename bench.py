@@ -115,7 +115,7 @@ def cpu_baseline(tokens):
         limiter.restore_original_limits()
     B = inp["q"].shape[0]
     return dict(value=B * tokens / dt, unit="tokens/s", cores=1, kind="oracle",
-                sample=f"first {tokens} of 8192 tokens of the prefill workload, all B=4 x 16 heads "
+                sample=f"first {tokens} of the 8192 tokens of the prefill workload, all B=4 x 16 heads "
                        f"({B * tokens} tokens, {dt:.1f} s, numpy float64, one thread)")
 
 
@@ -125,7 +125,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--decode-reps", type=int, default=3)
-    ap.add_argument("--cpu-tokens", type=int, default=768)
+    ap.add_argument("--cpu-tokens", type=int, default=8192)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     args = ap.parse_args()
