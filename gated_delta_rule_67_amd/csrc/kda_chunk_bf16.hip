@@ -68,6 +68,23 @@ __device__ __forceinline__ float row_shr(float v) {
 }
 
 __device__ __forceinline__ bf16x8 load8(const bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
+__device__ __forceinline__ bf16x4 load4(const bf16* p) { return *reinterpret_cast<const bf16x4*>(p); }
+__device__ __forceinline__ bf16x4 cvt4(f32x4 v) {
+  return bf16x4{static_cast<bf16>(v[0]), static_cast<bf16>(v[1]), static_cast<bf16>(v[2]), static_cast<bf16>(v[3])};
+}
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+// D(16x16) += A(16x16) B(16x16), bf16 operands: lane l supplies row (A) / column (B) l%16
+// and k = 4(l/16)..+3; D: column l%16, rows 4(l/16)..+3.
+__device__ __forceinline__ f32x4 mfma16x16x16(bf16x4 a, bf16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+}
+
+// Load a fragment unconditionally and zero it in lanes where `on` is false (a select,
+// not a branch: the load's latency then overlaps the other fragment loads).
+__device__ __forceinline__ bf16x8 load8_if(const bf16* p, bool on) {
+  const bf16x8 v = load8(p);
+  return on ? v : bf16x8{};
+}
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
@@ -122,7 +139,8 @@ __global__ __launch_bounds__(kThreads) void kernel(PrefillArgs p) {
   float* sFo = reinterpret_cast<float*>(lds + L::tFo);
   float* sGam = reinterpret_cast<float*>(lds + L::gam);
 
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches
   const int lr = lane & 15, lq = lane >> 4;
 
   // Workgroup -> (head, V tile); sibling V tiles of a head share an XCD (workgroups
@@ -214,21 +232,47 @@ __global__ __launch_bounds__(kThreads) void kernel(PrefillArgs p) {
   for (int t0 = 0; t0 < T; t0 += kC) {
     const int nrow = min(kC, T - t0);
 
-    // ---------------- in-block cumsum of g (log2 units): d = G_i - G_first, DPP row scan
+    // ---------------- in-block cumsum of g (log2 units): d = G_i - G_first, DPP row scan.
+    // Each scan step runs over all of the lane's channels so the DPP hazards overlap.
     float d[NKS][8];
 #pragma unroll
-    for (int s = 0; s < NKS; ++s) {
+    for (int s = 0; s < NKS; ++s)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float x = to_f32(rg[s][e]) * kLog2e;
-        float y = lr == 0 ? 0.f : x;
-        y += row_shr<1>(y);
-        y += row_shr<2>(y);
-        y += row_shr<4>(y);
-        y += row_shr<8>(y);
-        d[s][e] = y;
-        if (lr == 0) sFirst[w * KT + 32 * s + 8 * lq + e] = x;
-        if (lr == 15) sD15[w * KT + 32 * s + 8 * lq + e] = y;
+      for (int e = 0; e < 8; ++e) d[s][e] = lr == 0 ? 0.f : to_f32(rg[s][e]) * kLog2e;
+#pragma unroll
+    for (int s = 0; s < NKS; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) d[s][e] += row_shr<1>(d[s][e]);
+#pragma unroll
+    for (int s = 0; s < NKS; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) d[s][e] += row_shr<2>(d[s][e]);
+#pragma unroll
+    for (int s = 0; s < NKS; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) d[s][e] += row_shr<4>(d[s][e]);
+#pragma unroll
+    for (int s = 0; s < NKS; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) d[s][e] += row_shr<8>(d[s][e]);
+    if (lr == 0) {  // g of the block's first token
+#pragma unroll
+      for (int s = 0; s < NKS; ++s) {
+        f32x4 lo, hi;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          lo[e] = to_f32(rg[s][e]) * kLog2e;
+          hi[e] = to_f32(rg[s][e + 4]) * kLog2e;
+        }
+        *reinterpret_cast<f32x4*>(sFirst + w * KT + 32 * s + 8 * lq) = lo;
+        *reinterpret_cast<f32x4*>(sFirst + w * KT + 32 * s + 8 * lq + 4) = hi;
+      }
+    }
+    if (lr == 15) {  // block sum minus the first token
+#pragma unroll
+      for (int s = 0; s < NKS; ++s) {
+        *reinterpret_cast<f32x4*>(sD15 + w * KT + 32 * s + 8 * lq) = f32x4{d[s][0], d[s][1], d[s][2], d[s][3]};
+        *reinterpret_cast<f32x4*>(sD15 + w * KT + 32 * s + 8 * lq + 4) = f32x4{d[s][4], d[s][5], d[s][6], d[s][7]};
       }
     }
     lds_barrier();
@@ -254,16 +298,30 @@ __global__ __launch_bounds__(kThreads) void kernel(PrefillArgs p) {
     }
     lds_barrier();
 
-    // ---------------- decay factors and MFMA operands of this wave's token block
-    bf16x8 QR[NKS], KR[NKS], KC[NKS], QG[NKS], KG[NKS];
+    // ---------------- decay factors fused with the local MFMAs, one 32-channel k step at a
+    // time: the step's diagonal Akk^T / Aq^T and X = (K*Gam) S, P = (Q*Gam) S products run on
+    // the matrix core while the next step's factors run on the VALU. Akk^T / Aq^T tiles have
+    // column j of block J as rows and token i of block w as columns, so they leave the
+    // accumulators as row vectors of M and Aq.
+    bf16x8 QR[NKS], KR[NKS];
+    f32x4 aK[3], aQ[3], aKd, aQd, aX[NVT], aP[NVT];  // off-diagonal J < w; diagonal J = w
+#pragma unroll
+    for (int J = 0; J < 3; ++J) aK[J] = aQ[J] = f32x4{0.f, 0.f, 0.f, 0.f};
+    aKd = aQd = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int vt = 0; vt < NVT; ++vt) aX[vt] = aP[vt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < NKS; ++s) {
       const int c0 = 32 * s + 8 * lq;
+      bf16x8 sf[NVT];
+#pragma unroll
+      for (int vt = 0; vt < NVT; ++vt) sf[vt] = load8(tST + (vt * 16 + lr) * PK + c0);
       const f32x4 e0 = *reinterpret_cast<const f32x4*>(sE + w * KT + c0);
       const f32x4 e1 = *reinterpret_cast<const f32x4*>(sE + w * KT + c0 + 4);
       const f32x4 f0 = *reinterpret_cast<const f32x4*>(sF + w * KT + c0);
       const f32x4 f1 = *reinterpret_cast<const f32x4*>(sF + w * KT + c0 + 4);
       float kc[8];
+      bf16x8 KC, QG, KG;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float E = e < 4 ? e0[e] : e1[e - 4];
@@ -274,10 +332,17 @@ __global__ __launch_bounds__(kThreads) void kernel(PrefillArgs p) {
         kc[e] = kv * Cf;
         QR[s][e] = static_cast<bf16>(qr);
         KR[s][e] = static_cast<bf16>(kr);
-        KC[s][e] = static_cast<bf16>(kc[e]);
-        QG[s][e] = static_cast<bf16>(qr * E);
-        KG[s][e] = static_cast<bf16>(kr * E);
+        KC[e] = static_cast<bf16>(kc[e]);
+        QG[e] = static_cast<bf16>(qr * E);
+        KG[e] = static_cast<bf16>(kr * E);
         tKdT[(c0 + e) * PC + 16 * w + lr] = static_cast<bf16>(kc[e] * F);
+      }
+      aKd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(KC, KR[s], aKd, 0, 0, 0);
+      aQd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(KC, QR[s], aQd, 0, 0, 0);
+#pragma unroll
+      for (int vt = 0; vt < NVT; ++vt) {
+        aX[vt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(KG, sf[vt], aX[vt], 0, 0, 0);
+        aP[vt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(QG, sf[vt], aP[vt], 0, 0, 0);
       }
 #pragma unroll
       for (int I = 1; I < 4; ++I) {
@@ -292,44 +357,18 @@ __global__ __launch_bounds__(kThreads) void kernel(PrefillArgs p) {
         }
       }
     }
-    // raw q, k, g of this chunk are consumed: fetch the next chunk's now
-    unsigned cbeta[4], cv[NVT][4];
-    const unsigned rowbeta = rrowbeta;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      cbeta[r] = rbeta[r];
-#pragma unroll
-      for (int vt = 0; vt < NVT; ++vt) cv[vt][r] = rv[vt][r];
-    }
-    if (t0 + kC < T) prefetch(t0 + kC);
     lds_barrier();
 
-    // ---------------- stage 1 MFMA: Akk^T and Aq^T tiles (column j of block J <= w as rows,
-    // token i of block w as columns, so the accumulators leave as row vectors of M and Aq);
-    // X = (K*Gam) S and P = (Q*Gam) S for the rows of block w
-    f32x4 aK[4], aQ[4], aX[NVT], aP[NVT];
+    // ---------------- off-diagonal Akk^T / Aq^T tiles (J < w): column factors from block J's wave
 #pragma unroll
-    for (int J = 0; J < 4; ++J) {
-      aK[J] = f32x4{0.f, 0.f, 0.f, 0.f};
-      aQ[J] = aK[J];
-      if (J <= w) {
+    for (int J = 0; J < 3; ++J) {
+      if (J < w) {
 #pragma unroll
         for (int s = 0; s < NKS; ++s) {
-          const bf16x8 afr = J == w ? KC[s] : load8(tKCo + (pair_index(w, J) * 16 + lr) * PK + 32 * s + 8 * lq);
+          const bf16x8 afr = load8(tKCo + (pair_index(w, J) * 16 + lr) * PK + 32 * s + 8 * lq);
           aK[J] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, KR[s], aK[J], 0, 0, 0);
           aQ[J] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, QR[s], aQ[J], 0, 0, 0);
         }
-      }
-    }
-#pragma unroll
-    for (int vt = 0; vt < NVT; ++vt) {
-      aX[vt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      aP[vt] = aX[vt];
-#pragma unroll
-      for (int s = 0; s < NKS; ++s) {
-        const bf16x8 sf = load8(tST + (vt * 16 + lr) * PK + 32 * s + 8 * lq);
-        aX[vt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(KG[s], sf, aX[vt], 0, 0, 0);
-        aP[vt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(QG[s], sf, aP[vt], 0, 0, 0);
       }
     }
     // M (beta-scaled strictly lower), Aq (lower incl.), (beta Y)^T. Lane: row i = 16w + lr,
@@ -337,14 +376,16 @@ __global__ __launch_bounds__(kThreads) void kernel(PrefillArgs p) {
 #pragma unroll
     for (int J = 0; J < 4; ++J) {
       if (J <= w) {
+        const f32x4 ak = J == w ? aKd : aK[J < 3 ? J : 0];
+        const f32x4 aq = J == w ? aQd : aQ[J < 3 ? J : 0];
         const int i = 16 * w + lr;
         f32x4 mv;
         bf16x4 qv;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int j = 16 * J + 4 * lq + r;
-          mv[r] = (j < i) ? bits_to_f32(rowbeta) * aK[J][r] : 0.f;
-          qv[r] = static_cast<bf16>((j <= i) ? aQ[J][r] : 0.f);
+          mv[r] = (j < i) ? bits_to_f32(rrowbeta) * ak[r] : 0.f;
+          qv[r] = static_cast<bf16>((j <= i) ? aq[r] : 0.f);
         }
         *reinterpret_cast<f32x4*>(sM + i * PM + 16 * J + 4 * lq) = mv;
         *reinterpret_cast<bf16x4*>(tAq + i * PC + 16 * J + 4 * lq) = qv;
@@ -354,9 +395,11 @@ __global__ __launch_bounds__(kThreads) void kernel(PrefillArgs p) {
     for (int vt = 0; vt < NVT; ++vt) {
       bf16x4 yb;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) yb[r] = static_cast<bf16>(bits_to_f32(cbeta[r]) * (bits_to_f32(cv[vt][r]) - aX[vt][r]));
+      for (int r = 0; r < 4; ++r) yb[r] = static_cast<bf16>(bits_to_f32(rbeta[r]) * (bits_to_f32(rv[vt][r]) - aX[vt][r]));
       *reinterpret_cast<bf16x4*>(tBY + (vt * 16 + lr) * PC + 16 * w + 4 * lq) = yb;
     }
+    // this chunk's raw inputs are consumed: fetch the next chunk's (in flight until its scan)
+    if (t0 + kC < T) prefetch(t0 + kC);
     lds_barrier();
 
     // ---------------- T = (I + M)^-1, diagonal block w: right-looking forward substitution.
@@ -388,94 +431,142 @@ __global__ __launch_bounds__(kThreads) void kernel(PrefillArgs p) {
     }
     lds_barrier();
 
-    // level A: T[I][I-1] = -T[I][I] M[I][I-1] T[I-1][I-1] for I = 1 (wave 0), 3 (wave 1)
-    f32x4 acc;
+    // Merges with v_mfma_f32_16x16x16_bf16: its accumulator (lane: column l%16, rows
+    // 4(l/16)..+3) is exactly its B-operand layout, so each level chains its two products
+    // in registers. A operands are rows read from LDS (4 consecutive k per lane).
+    // level A: T[I][I-1] = -T[I][I] (M[I][I-1] T[I-1][I-1]) for I = 1 (wave 0), 3 (wave 1)
     if (w < 2) {
       const int I = w == 0 ? 1 : 3;
-      acc = f32x4{0.f, 0.f, 0.f, 0.f};
-      mma16_a32(acc, sM + (I * 16) * PM + (I - 1) * 16, PM, tTT + ((I - 1) * 16) * PC + (I - 1) * 16,
-                PC, 16, lane);
-      bf16x4 zb;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) zb[r] = static_cast<bf16>(acc[r]);
-      *reinterpret_cast<bf16x4*>(tZ + (w * 16 + lr) * PC + lq * 4) = zb;
-    }
-    lds_barrier();
-    if (w < 2) {
-      const int I = w == 0 ? 1 : 3;
-      acc = f32x4{0.f, 0.f, 0.f, 0.f};
-      mma16(acc, tT + (I * 16) * PC + I * 16, PC, tZ + (w * 16) * PC, PC, 16, lane);
+      const f32x4 mv = *reinterpret_cast<const f32x4*>(sM + (16 * I + lr) * PM + 16 * (I - 1) + 4 * lq);
+      f32x4 z = mfma16x16x16(cvt4(mv), load4(tTT + (16 * (I - 1) + lr) * PC + 16 * (I - 1) + 4 * lq),
+                             f32x4{0.f, 0.f, 0.f, 0.f});
+      const f32x4 t = mfma16x16x16(load4(tT + (16 * I + lr) * PC + 16 * I + 4 * lq), cvt4(z),
+                                   f32x4{0.f, 0.f, 0.f, 0.f});
       bf16x4 tb;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int i = I * 16 + lq * 4 + r, j = (I - 1) * 16 + lr;
-        tb[r] = static_cast<bf16>(-acc[r]);
-        tT[i * PC + j] = tb[r];
+        tb[r] = static_cast<bf16>(-t[r]);
+        tT[(16 * I + 4 * lq + r) * PC + 16 * (I - 1) + lr] = tb[r];
       }
-      *reinterpret_cast<bf16x4*>(tTT + ((I - 1) * 16 + lr) * PC + I * 16 + lq * 4) = tb;
+      *reinterpret_cast<bf16x4*>(tTT + (16 * (I - 1) + lr) * PC + 16 * I + 4 * lq) = tb;
     }
     lds_barrier();
 
-    // level B: T[23][01] = -T[23][23] M[23][01] T[01][01]; wave -> (I, J)
+    // level B: T[I][J] = -sum_{K=2,3} T[I][K] Z2[K][J], Z2[K][J] = sum_{L=0,1} M[K][L] T[L][J];
+    // wave -> (I, J) and computes both Z2 tiles it needs (T[0][1] = T[2][3] = 0 are skipped)
     {
       const int I = 2 + (w >> 1), J = w & 1;
-      acc = f32x4{0.f, 0.f, 0.f, 0.f};
-      mma16_a32(acc, sM + (I * 16) * PM, PM, tTT + (J * 16) * PC, PC, 32, lane);
-      bf16x4 zb;
+      f32x4 z2[2];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) zb[r] = static_cast<bf16>(acc[r]);
-      *reinterpret_cast<bf16x4*>(tZ + (J * 16 + lr) * PC + (I - 2) * 16 + lq * 4) = zb;
-    }
-    lds_barrier();
-    {
-      const int I = 2 + (w >> 1), J = w & 1;
-      acc = f32x4{0.f, 0.f, 0.f, 0.f};
-      mma16(acc, tT + (I * 16) * PC + 32, PC, tZ + (J * 16) * PC, PC, 32, lane);
+      for (int K = 2; K < 4; ++K) {
+        f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int r = 0; r < 4; ++r) tT[(I * 16 + lq * 4 + r) * PC + J * 16 + lr] = static_cast<bf16>(-acc[r]);
+        for (int L = 0; L < 2; ++L) {
+          if (L >= J) {
+            const f32x4 mv = *reinterpret_cast<const f32x4*>(sM + (16 * K + lr) * PM + 16 * L + 4 * lq);
+            z = mfma16x16x16(cvt4(mv), load4(tTT + (16 * J + lr) * PC + 16 * L + 4 * lq), z);
+          }
+        }
+        z2[K - 2] = z;
+      }
+      f32x4 t = mfma16x16x16(load4(tT + (16 * I + lr) * PC + 32 + 4 * lq), cvt4(z2[0]),
+                             f32x4{0.f, 0.f, 0.f, 0.f});
+      if (I == 3) t = mfma16x16x16(load4(tT + (16 * I + lr) * PC + 48 + 4 * lq), cvt4(z2[1]), t);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) tT[(16 * I + 4 * lq + r) * PC + 16 * J + lr] = static_cast<bf16>(-t[r]);
     }
     lds_barrier();
 
-    // ---------------- U = T (beta Y), rows of block w
+    // ---------------- U = T (beta Y), rows of block w (k range 16 (w + 1))
+    {
+      const int kk = 16 * (w + 1);
+      bf16x8 ta[2], yb[NVT][2];
 #pragma unroll
-    for (int vt = 0; vt < NVT; ++vt) {
-      acc = f32x4{0.f, 0.f, 0.f, 0.f};
-      mma16(acc, tT + (w * 16) * PC, PC, tBY + (vt * 16) * PC, PC, (w + 1) * 16, lane);
-      bf16x4 ub;
+      for (int ks = 0; ks < 2; ++ks) {
+        const bool on = 32 * ks + 8 * lq < kk;
+        ta[ks] = load8_if(tT + (16 * w + lr) * PC + 32 * ks + 8 * lq, on);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) ub[r] = static_cast<bf16>(acc[r]);
-      *reinterpret_cast<bf16x4*>(tUT + (vt * 16 + lr) * PC + w * 16 + lq * 4) = ub;
+        for (int vt = 0; vt < NVT; ++vt)
+          yb[vt][ks] = load8_if(tBY + (16 * vt + lr) * PC + 32 * ks + 8 * lq, on);
+      }
+      f32x4 ua[NVT];
+#pragma unroll
+      for (int vt = 0; vt < NVT; ++vt) ua[vt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int vt = 0; vt < NVT; ++vt) ua[vt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ta[ks], yb[vt][ks], ua[vt], 0, 0, 0);
+#pragma unroll
+      for (int vt = 0; vt < NVT; ++vt) {
+        bf16x4 ub;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ub[r] = static_cast<bf16>(ua[vt][r]);
+        *reinterpret_cast<bf16x4*>(tUT + (vt * 16 + lr) * PC + w * 16 + lq * 4) = ub;
+      }
     }
     lds_barrier();
 
     // ---------------- O = scale (P + Aq U), store
+    {
+      const int kk = 16 * (w + 1);
+      bf16x8 qa[2], ub[NVT][2];
 #pragma unroll
-    for (int vt = 0; vt < NVT; ++vt) {
-      mma16(aP[vt], tAq + (w * 16) * PC, PC, tUT + (vt * 16) * PC, PC, (w + 1) * 16, lane);
-      const int vc = vt * 16 + lr;
+      for (int ks = 0; ks < 2; ++ks) {
+        const bool on = 32 * ks + 8 * lq < kk;
+        qa[ks] = load8_if(tAq + (16 * w + lr) * PC + 32 * ks + 8 * lq, on);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = w * 16 + lq * 4 + r;
-        const bool ok = (i < nrow) & (vc < vvalid);
-        const unsigned oo = (unsigned)(((t0 + i) * p.HV + hv) * V + v0 + vc) * 2u;
-        buf_store1(static_cast<bf16>(p.scale * aP[vt][r]), ro_, ok ? oo : kOutOfRange);
+        for (int vt = 0; vt < NVT; ++vt)
+          ub[vt][ks] = load8_if(tUT + (16 * vt + lr) * PC + 32 * ks + 8 * lq, on);
+      }
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int vt = 0; vt < NVT; ++vt) aP[vt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks], ub[vt][ks], aP[vt], 0, 0, 0);
+#pragma unroll
+      for (int vt = 0; vt < NVT; ++vt) {
+        const int vc = vt * 16 + lr;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = w * 16 + lq * 4 + r;
+          const bool ok = (i < nrow) & (vc < vvalid);
+          const unsigned oo = (unsigned)(((t0 + i) * p.HV + hv) * V + v0 + vc) * 2u;
+          buf_store1(static_cast<bf16>(p.scale * aP[vt][r]), ro_, ok ? oo : kOutOfRange);
+        }
       }
     }
 
-    // ---------------- S = diag(Gam_C) S + (K*Gam_C/Gam)^T U
+    // ---------------- S = diag(Gam_C) S + (K*Gam_C/Gam)^T U   (all fragments first)
+    {
+      bf16x8 ka[NSW][2], ub[NSW][2];
+      f32x4 gm[NSW];
 #pragma unroll
-    for (int n = 0; n < NSW; ++n) {
-      const int s = w + 4 * n;
-      if (s < NST) {
-        const int ct = s / NVT, vt = s % NVT;
-        const f32x4 gm = *reinterpret_cast<const f32x4*>(sGam + ct * 16 + lq * 4);
+      for (int n = 0; n < NSW; ++n) {
+        const int s = w + 4 * n, ct = s / NVT, vt = s % NVT;
+        const int cts = s < NST ? ct : 0;  // wave-uniform; rows of tile 0 when the tile is unused
 #pragma unroll
-        for (int r = 0; r < 4; ++r) S[n][r] *= gm[r];
-        mma16(S[n], tKdT + (ct * 16) * PC, PC, tUT + (vt * 16) * PC, PC, kC, lane);
-        bf16x4 sb;
+        for (int ks = 0; ks < 2; ++ks) {
+          ka[n][ks] = load8(tKdT + (cts * 16 + lr) * PC + 32 * ks + 8 * lq);
+          ub[n][ks] = load8(tUT + (vt * 16 + lr) * PC + 32 * ks + 8 * lq);
+        }
+        gm[n] = *reinterpret_cast<const f32x4*>(sGam + cts * 16 + lq * 4);
+      }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sb[r] = static_cast<bf16>(S[n][r]);
-        *reinterpret_cast<bf16x4*>(tST + (vt * 16 + lr) * PK + ct * 16 + lq * 4) = sb;
+      for (int n = 0; n < NSW; ++n)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) S[n][r] *= gm[n][r];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int n = 0; n < NSW; ++n) S[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[n][ks], ub[n][ks], S[n], 0, 0, 0);
+#pragma unroll
+      for (int n = 0; n < NSW; ++n) {
+        const int s = w + 4 * n, ct = s / NVT, vt = s % NVT;
+        if (s < NST) {
+          bf16x4 sb;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sb[r] = static_cast<bf16>(S[n][r]);
+          *reinterpret_cast<bf16x4*>(tST + (vt * 16 + lr) * PK + ct * 16 + lq * 4) = sb;
+        }
       }
     }
     lds_barrier();
@@ -504,12 +595,32 @@ hipError_t launch_cfg(const PrefillArgs& a, hipStream_t stream) {
 
 }  // namespace chunk_bf16
 
-// bf16 inputs with K % 8 == 0 and 16-byte aligned q/k/g rows.
+// Number of compute units of the current device (queried once per device).
+static int device_cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+// bf16 inputs with K % 8 == 0 and 16-byte aligned q/k/g rows. One workgroup per CU at a
+// time (LDS-bound), so the V tile is the narrowest that keeps the grid within one round
+// of the device's CUs: every V tile repeats the chunk's V-independent work.
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
   using namespace chunk_bf16;
+  const int heads = a.B * a.HV;
+  const bool wide = a.V > 32 && heads * ((a.V + 31) / 32) > device_cu_count();
   if (a.K <= 32) return a.V <= 16 ? launch_cfg<32, 16>(a, stream) : launch_cfg<32, 32>(a, stream);
   if (a.K <= 64) return a.V <= 16 ? launch_cfg<64, 16>(a, stream) : launch_cfg<64, 32>(a, stream);
-  if (a.K <= 128) return a.V <= 16 ? launch_cfg<128, 16>(a, stream) : launch_cfg<128, 32>(a, stream);
+  if (a.K <= 128) {
+    if (a.V <= 16) return launch_cfg<128, 16>(a, stream);
+    return wide ? launch_cfg<128, 64>(a, stream) : launch_cfg<128, 32>(a, stream);
+  }
   return hipErrorInvalidValue;
 }
 
