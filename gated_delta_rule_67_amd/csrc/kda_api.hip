@@ -12,7 +12,8 @@ hipError_t launch_decode(const void*, const void*, const void*, const void*, con
                          void*, int, int, int, int, int, float, hipStream_t);
 hipError_t launch_prefill(const void*, const void*, const void*, const void*, const void*,
                           const float*, float*, void*, int, int, int, int, int, int, float, bool,
-                          hipStream_t);
+                          void*, hipStream_t);
+size_t wy_workspace_bytes(int B, int T, int HV, int K);
 }  // namespace kda
 
 namespace {
@@ -47,16 +48,20 @@ const char* kda_status_string(int status) {
 
 const char* kda_version(void) { return "kda-gfx950 0.1"; }
 
-size_t kda_chunk_fwd_workspace_size(int, int, int, int, int, int, int, int) {
-  return 0;  // the fused prefill keeps every intermediate on chip
+size_t kda_chunk_fwd_workspace_size(int B, int T, int H, int HV, int K, int V, int chunk_size,
+                                    int dtype) {
+  // bf16 with K % 8 == 0 and V % 8 == 0 runs as per-chunk factors + state pass, which keeps
+  // one block of factors per (b, hv, 64-token chunk); everything else needs none.
+  if (chunk_size < 1 || !positive(T)) return 0;
+  if (check_common(B, H, HV, K, V, 1.f, dtype) != KDA_OK) return 0;
+  if (dtype != KDA_DTYPE_BF16 || K % 8 != 0 || V % 8 != 0) return 0;
+  return kda::wy_workspace_bytes(B, T, HV, K);
 }
 
 int kda_chunk_fwd(const void* q, const void* k, const void* v, const void* g, const void* beta,
                   const float* initial_state, float* final_state, void* o, int B, int T, int H,
                   int HV, int K, int V, float scale, int chunk_size, int dtype, void* workspace,
                   size_t workspace_bytes, void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   if (!q || !k || !v || !g || !beta || !o) return KDA_ERR_INVALID;
   if (!positive(T)) return KDA_ERR_INVALID;
   if (chunk_size != 8 && chunk_size != 16 && chunk_size != 32 && chunk_size != 64)
@@ -66,8 +71,14 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const void* g, co
   if (rc != KDA_OK) return rc;
   if (dtype == KDA_DTYPE_F32 && K > 64) return KDA_ERR_UNSUPPORTED;
   if ((int64_t)B * HV * ((V + 15) / 16) > INT32_MAX) return KDA_ERR_UNSUPPORTED;
+  if ((int64_t)B * HV * ((T + 63) / 64) > INT32_MAX) return KDA_ERR_UNSUPPORTED;
+  // A workspace, when given, must hold what kda_chunk_fwd_workspace_size asks for.
+  const size_t need = kda_chunk_fwd_workspace_size(B, T, H, HV, K, V, chunk_size, dtype);
+  if (workspace && workspace_bytes < need) return KDA_ERR_INVALID;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0) return KDA_ERR_INVALID;
   const hipError_t e = kda::launch_prefill(q, k, v, g, beta, initial_state, final_state, o, B, T,
                                            H, HV, K, V, scale, dtype == KDA_DTYPE_BF16,
+                                           need ? workspace : nullptr,
                                            static_cast<hipStream_t>(stream));
   return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }

@@ -1,0 +1,751 @@
+// Chunked KDA prefill for bfloat16 inputs in two kernels: per-chunk WY factors, then the
+// sequential state pass.
+//
+// The chunk algebra is the one of the K3 README page "KDA 训练 → 推理 手写实现" (roadmap
+// rows L2/L3): in-chunk cumsum of g, the decay-weighted strictly lower triangular system and
+// its forward-substitution solve, intra-chunk attention with relative decay, then the state
+// handed from chunk to chunk. Per 64-token chunk, with Gam = exp(G) (G the in-chunk cumsum):
+//
+//   M[i,j]  = beta_i sum_c k_i[c] k_j[c] exp(G_i[c]-G_j[c])      (j < i)
+//   Aq[i,j] =        sum_c q_i[c] k_j[c] exp(G_i[c]-G_j[c])      (j <= i)
+//   T       = (I + M)^-1
+//   U       = T diag(beta) (V - (K*Gam) S),   O = scale ((Q*Gam) S + Aq U)
+//   S_next  = diag(Gam_C) S + (K * Gam_C/Gam)^T U
+//
+// Everything left of S is independent of the state, so it is computed for all chunks at once
+// (factors_kernel: one workgroup per chunk and value head, the whole device busy) and written
+// to a workspace as MFMA-ready bf16 tiles. state_kernel then walks the chunks of one
+// (b, hv, V tile) in order; its per-chunk work is five MFMA products with the state kept in
+// registers, and the chunk's tiles are streamed into LDS by DMA one chunk ahead.
+//
+// Contractions over a 32-wide k step use v_mfma_f32_16x16x32_bf16, whose lane l supplies 8
+// consecutive k of row/column l%16. The state pass feeds accumulator tiles (lane l: column
+// l%16, rows 4(l/16)..+3) back in as B operands, so each lane's 8 k values are rows
+// 4(l/16)..+3 of two consecutive 16-row tiles. The stored tiles use the matching order:
+// inside every 32-wide group the index 32m + 16h + 4q + r sits at 32m + 8q + 4h + r.
+//
+// Decay factors (factors_kernel): with r the first token of a 16-token block,
+// d_i = G_i - G_r <= 0, R_i = 2^(d log2 e) <= 1 and C_i = 1/R_i <= e^75 (g >= -5). Diagonal
+// blocks use (x_i R_i).(k_j C_j); block I > J uses the column factor k_j C_j exp(G_rI - G_rJ);
+// Gam_i = exp(G_rI) R_i and Gam_C/Gam_j = exp(G_C - G_rJ) C_j.
+#include "kda_device.h"
+
+namespace kda {
+namespace wy {
+
+constexpr int kC = 64;
+
+// One chunk's factors in the workspace (bytes; every tile 16-byte aligned). Rounded up to
+// whole kilobytes so the state pass streams it in 1 KB DMA rounds.
+template <int KT>
+struct Blk {
+  static constexpr int qg = 0;                  // [64][KT] bf16 Q*Gam, channel order permuted
+  static constexpr int kg = qg + kC * KT * 2;   // [64][KT] bf16 K*Gam, channel order permuted
+  static constexpr int kdt = kg + kC * KT * 2;  // [KT][64] bf16 (K*Gam_C/Gam)^T, token order permuted
+  static constexpr int t = kdt + KT * kC * 2;   // [64][64] bf16 T, column order permuted
+  static constexpr int aq = t + kC * kC * 2;    // [64][64] bf16 Aq, column order permuted
+  static constexpr int gam = aq + kC * kC * 2;  // [KT] fp32 Gam_C
+  static constexpr int beta = gam + KT * 4;     // [64] fp32 beta
+  static constexpr int used = beta + kC * 4;
+  static constexpr int bytes = (used + 1023) / 1024 * 1024;
+};
+
+size_t block_bytes(int K) {
+  return K <= 32 ? Blk<32>::bytes : K <= 64 ? Blk<64>::bytes : Blk<128>::bytes;
+}
+
+// Stored position of index x inside its 32-wide group: 32m + 16h + 4q + r -> 32m + 8q + 4h + r.
+__device__ __forceinline__ int perm32(int x) {
+  return (x & ~31) | ((x & 12) << 1) | ((x & 16) >> 2) | (x & 3);
+}
+
+__device__ __forceinline__ int pair_index(int I, int J) { return I * (I - 1) / 2 + J; }
+
+template <int N>
+__device__ __forceinline__ float row_shr(float v) {  // 16-lane row shift right, zero fill
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                               0x110 + N, 0xf, 0xf, false));
+}
+
+__device__ __forceinline__ bf16x8 load8(const void* p) { return *reinterpret_cast<const bf16x8*>(p); }
+__device__ __forceinline__ bf16x4 load4(const void* p) { return *reinterpret_cast<const bf16x4*>(p); }
+__device__ __forceinline__ f32x4 load4f(const void* p) { return *reinterpret_cast<const f32x4*>(p); }
+__device__ __forceinline__ bf16x4 cvt4(f32x4 v) {
+  return bf16x4{static_cast<bf16>(v[0]), static_cast<bf16>(v[1]), static_cast<bf16>(v[2]), static_cast<bf16>(v[3])};
+}
+__device__ __forceinline__ bf16x8 cat8(bf16x4 a, bf16x4 b) {
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+__device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+// 16x16x16 product: lane l supplies row (A) / column (B) l%16 and k = 4(l/16)..+3.
+__device__ __forceinline__ f32x4 mfma16(bf16x4 a, bf16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+}
+
+// Raw buffer resources: a lane whose offset is kOutOfRange (or past the range) reads zeros
+// and its stores are dropped, so masked loads need no branches.
+constexpr unsigned kOutOfRange = 0x80000000u;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ bf16x4 buf_load4(__amdgpu_buffer_rsrc_t r, unsigned off) {
+  return __builtin_bit_cast(bf16x4, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+__device__ __forceinline__ unsigned buf_load1(__amdgpu_buffer_rsrc_t r, unsigned off) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+__device__ __forceinline__ float bits_to_f32(unsigned u) { return __builtin_bit_cast(float, u << 16); }
+__device__ __forceinline__ void buf_store1(bf16 x, __amdgpu_buffer_rsrc_t r, unsigned off) {
+  __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, x), r, off, 0, 0);
+}
+
+// The workspace holds each chunk's tiles exactly as the state pass keeps them in LDS, so a
+// chunk moves with contiguous DMA. Inside a row of R 16-byte chunks, logical chunk c sits at
+// c ^ swz-key(row): 16 consecutive rows read at one logical chunk then hit 16 distinct
+// 16-byte slots of a 256-byte LDS bank window.
+template <int R>
+__device__ __forceinline__ int swz(int row, int c) { return c ^ ((row / (16 / R)) & (R - 1)); }
+
+struct WyArgs {
+  PrefillArgs p;
+  unsigned char* ws;  // B * HV * NT blocks of Blk<KT>::bytes, (b, hv, chunk) order
+  int NT;             // chunks per sequence
+};
+
+// ================================================================ per-chunk factors
+template <int KT>
+struct LdsA {
+  static constexpr int PK = KT + 8, PC = kC + 8, PM = kC + 4;
+  // phase 1: scan .. off-diagonal products
+  static constexpr int kco = 0;                        // [6][16][PK] bf16 off-diagonal column factors
+  static constexpr int first = kco + 6 * 16 * PK * 2;  // [4][KT] fp32 g (log2 units) at block start
+  static constexpr int d15 = first + 4 * KT * 4;       // [4][KT] fp32 block sum minus first
+  static constexpr int tE = d15 + 4 * KT * 4;          // [4][KT] fp32 exp(G at block start)
+  static constexpr int tF = tE + 4 * KT * 4;           // [4][KT] fp32 exp(G_C - G at block start)
+  static constexpr int tFo = tF + 4 * KT * 4;          // [6][KT] fp32 exp(G_rI - G_rJ), I > J
+  static constexpr int end1 = tFo + 6 * KT * 4;
+  // phase 2: M .. copy-out (same bytes)
+  static constexpr int m = 0;                          // [64][PM] fp32 M
+  static constexpr int t = m + kC * PM * 4;            // [64][PC] bf16 T
+  static constexpr int tt = t + kC * PC * 2;           // [64][PC] bf16 T^T
+  static constexpr int end2 = tt + kC * PC * 2;
+  static constexpr int endX = end1 > end2 ? end1 : end2;
+  static constexpr int kdt = endX;                     // [KT][PC] bf16 (K*Gam_C/Gam)^T, tokens permuted
+  static constexpr int gam = kdt + KT * PC * 2;        // [KT] fp32 Gam_C
+  static constexpr int total = gam + KT * 4;
+  static_assert(total <= 64 * 1024, "two workgroups per CU");
+};
+
+// One workgroup of 4 waves per (b, hv, chunk) item, looping over items with a stride of
+// gridDim.x (the next item's q, k, g are loaded while the current one finishes). Wave w owns
+// the 16-token block w; lane (lr, lq) holds token 16w + lr and, for k step s, the channels
+// whose stored positions are 32s + 8lq..+7, i.e. 32s + 4lq..+3 and 32s + 16 + 4lq..+3.
+template <int KT>
+__global__ __launch_bounds__(256) void factors_kernel(WyArgs a) {
+  using L = LdsA<KT>;
+  using W = Blk<KT>;
+  constexpr int PK = L::PK, PC = L::PC, PM = L::PM;
+  constexpr int NKS = KT / 32;
+  const PrefillArgs& p = a.p;
+
+  __shared__ __attribute__((aligned(16))) unsigned char lds[L::total];
+  bf16* tKCo = reinterpret_cast<bf16*>(lds + L::kco);
+  float* sFirst = reinterpret_cast<float*>(lds + L::first);
+  float* sD15 = reinterpret_cast<float*>(lds + L::d15);
+  float* sE = reinterpret_cast<float*>(lds + L::tE);
+  float* sF = reinterpret_cast<float*>(lds + L::tF);
+  float* sFo = reinterpret_cast<float*>(lds + L::tFo);
+  float* sM = reinterpret_cast<float*>(lds + L::m);
+  bf16* tT = reinterpret_cast<bf16*>(lds + L::t);
+  bf16* tTT = reinterpret_cast<bf16*>(lds + L::tt);
+  bf16* tKdT = reinterpret_cast<bf16*>(lds + L::kdt);
+  float* sGam = reinterpret_cast<float*>(lds + L::gam);
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = lane & 15, lq = lane >> 4;
+  const int K = p.K, T = p.T, NT = a.NT;
+  const int items = p.B * p.HV * NT;
+  const int i_row = 16 * w + lr;  // the lane's token inside the chunk
+
+  // Per-lane byte offsets of the two 4-channel groups of each k step; channels >= K start
+  // at kOutOfRange, which stays out of range whatever row offset is added.
+  unsigned cq[NKS][2], cg[NKS][2];
+#pragma unroll
+  for (int s = 0; s < NKS; ++s)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int c = 32 * s + 16 * hh + 4 * lq;
+      cq[s][hh] = c < K ? (unsigned)((i_row * p.H * K + c) * 2) : kOutOfRange;
+      cg[s][hh] = c < K ? (unsigned)((i_row * p.HV * K + c) * 2) : kOutOfRange;
+    }
+
+  bf16x8 rq[NKS], rk[NKS], rg[NKS];
+  unsigned rbeta;
+  auto prefetch = [&](int it) {
+    const int head = it / NT, n = it - head * NT;
+    const int b = head / p.HV, hv = head - b * p.HV, h = hv / (p.HV / p.H);
+    const int t0 = n * kC, nrow = min(kC, T - t0);
+    const size_t row0 = (size_t)b * T + t0;
+    // ranges end at the last token of the sequence: later rows read as zeros
+    const auto rq_ = make_rsrc(static_cast<const bf16*>(p.q) + (row0 * p.H + h) * K, (unsigned)(nrow * p.H * K * 2));
+    const auto rk_ = make_rsrc(static_cast<const bf16*>(p.k) + (row0 * p.H + h) * K, (unsigned)(nrow * p.H * K * 2));
+    const auto rg_ = make_rsrc(static_cast<const bf16*>(p.g) + (row0 * p.HV + hv) * K, (unsigned)(nrow * p.HV * K * 2));
+    const auto rb_ = make_rsrc(static_cast<const bf16*>(p.beta) + row0 * p.HV + hv, (unsigned)(nrow * p.HV * 2));
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) {
+      bf16x4 q2[2], k2[2], g2[2];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        q2[hh] = buf_load4(rq_, cq[s][hh]);
+        k2[hh] = buf_load4(rk_, cq[s][hh]);
+        g2[hh] = buf_load4(rg_, cg[s][hh]);
+      }
+      rq[s] = cat8(q2[0], q2[1]);
+      rk[s] = cat8(k2[0], k2[1]);
+      rg[s] = cat8(g2[0], g2[1]);
+    }
+    rbeta = buf_load1(rb_, (unsigned)(i_row * p.HV * 2));
+  };
+
+  if ((int)blockIdx.x < items) prefetch(blockIdx.x);
+
+  for (int it = blockIdx.x; it < items; it += gridDim.x) {
+    unsigned char* blk = a.ws + (size_t)it * W::bytes;
+
+    // ---------------- in-block cumsum of g (log2 units): d = G_i - G_first, DPP row scan
+    float d[NKS][8];
+#pragma unroll
+    for (int s = 0; s < NKS; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) d[s][e] = lr == 0 ? 0.f : to_f32(rg[s][e]) * kLog2e;
+#pragma unroll
+    for (int s = 0; s < NKS; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) d[s][e] += row_shr<1>(d[s][e]);
+#pragma unroll
+    for (int s = 0; s < NKS; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) d[s][e] += row_shr<2>(d[s][e]);
+#pragma unroll
+    for (int s = 0; s < NKS; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) d[s][e] += row_shr<4>(d[s][e]);
+#pragma unroll
+    for (int s = 0; s < NKS; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) d[s][e] += row_shr<8>(d[s][e]);
+    if (lr == 0) {  // g of the block's first token
+#pragma unroll
+      for (int s = 0; s < NKS; ++s) {
+        f32x4 lo, hi;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          lo[e] = to_f32(rg[s][e]) * kLog2e;
+          hi[e] = to_f32(rg[s][e + 4]) * kLog2e;
+        }
+        *reinterpret_cast<f32x4*>(sFirst + w * KT + 32 * s + 4 * lq) = lo;
+        *reinterpret_cast<f32x4*>(sFirst + w * KT + 32 * s + 16 + 4 * lq) = hi;
+      }
+    }
+    if (lr == 15) {  // block sum minus the first token
+#pragma unroll
+      for (int s = 0; s < NKS; ++s) {
+        *reinterpret_cast<f32x4*>(sD15 + w * KT + 32 * s + 4 * lq) = f32x4{d[s][0], d[s][1], d[s][2], d[s][3]};
+        *reinterpret_cast<f32x4*>(sD15 + w * KT + 32 * s + 16 + 4 * lq) = f32x4{d[s][4], d[s][5], d[s][6], d[s][7]};
+      }
+    }
+    lds_barrier();
+
+    // ---------------- per-(block, channel) decay constants
+    if (tid < KT) {
+      const int c = tid;
+      float gr[4], run = 0.f;
+#pragma unroll
+      for (int J = 0; J < 4; ++J) {
+        const float f = sFirst[J * KT + c];
+        gr[J] = run + f;
+        run += f + sD15[J * KT + c];
+      }
+#pragma unroll
+      for (int J = 0; J < 4; ++J) {
+        sE[J * KT + c] = fast_exp2(gr[J]);
+        sF[J * KT + c] = fast_exp2(run - gr[J]);
+#pragma unroll
+        for (int I = J + 1; I < 4; ++I) sFo[pair_index(I, J) * KT + c] = fast_exp2(gr[I] - gr[J]);
+      }
+      sGam[c] = fast_exp2(run);
+    }
+    lds_barrier();
+
+    // ---------------- decay factors; Q*Gam and K*Gam leave straight to the workspace, the
+    // diagonal Akk^T / Aq^T tiles (rows: tokens j of block w, columns: tokens i) accumulate
+    // on the matrix core while the next k step's factors run on the VALU.
+    bf16x8 QR[NKS], KR[NKS];
+    f32x4 aK[3], aQ[3], aKd = {0.f, 0.f, 0.f, 0.f}, aQd = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int J = 0; J < 3; ++J) aK[J] = aQ[J] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) {
+      const int cA = 32 * s + 4 * lq, cB = cA + 16;  // channels of elements 0..3 and 4..7
+      const f32x4 e0 = load4f(sE + w * KT + cA), e1 = load4f(sE + w * KT + cB);
+      const f32x4 f0 = load4f(sF + w * KT + cA), f1 = load4f(sF + w * KT + cB);
+      float kc[8];
+      bf16x8 KC, QG, KG;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float E = e < 4 ? e0[e] : e1[e - 4];
+        const float F = e < 4 ? f0[e] : f1[e - 4];
+        const float R = fast_exp2(d[s][e]), Cf = fast_exp2(-d[s][e]);
+        const float qv = to_f32(rq[s][e]), kv = to_f32(rk[s][e]);
+        const float qr = qv * R, kr = kv * R;
+        kc[e] = kv * Cf;
+        QR[s][e] = static_cast<bf16>(qr);
+        KR[s][e] = static_cast<bf16>(kr);
+        KC[e] = static_cast<bf16>(kc[e]);
+        QG[e] = static_cast<bf16>(qr * E);
+        KG[e] = static_cast<bf16>(kr * E);
+        const int c = (e < 4 ? cA : cB) + (e & 3);
+        tKdT[c * PC + perm32(i_row)] = static_cast<bf16>(kc[e] * F);
+      }
+      const int qk_off = (i_row * (KT / 8) + swz<KT / 8>(i_row, 4 * s + lq)) * 16;
+      *reinterpret_cast<bf16x8*>(blk + W::qg + qk_off) = QG;
+      *reinterpret_cast<bf16x8*>(blk + W::kg + qk_off) = KG;
+      aKd = mfma32(KC, KR[s], aKd);
+      aQd = mfma32(KC, QR[s], aQd);
+#pragma unroll
+      for (int I = 1; I < 4; ++I) {
+        if (I > w) {
+          const int pi = pair_index(I, w);
+          const f32x4 o0 = load4f(sFo + pi * KT + cA), o1 = load4f(sFo + pi * KT + cB);
+          bf16x8 kco;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) kco[e] = static_cast<bf16>(kc[e] * (e < 4 ? o0[e] : o1[e - 4]));
+          *reinterpret_cast<bf16x8*>(tKCo + (pi * 16 + lr) * PK + 32 * s + 8 * lq) = kco;
+        }
+      }
+    }
+    const float brow = bits_to_f32(rbeta);
+    if (lq == 0) *reinterpret_cast<float*>(blk + W::beta + i_row * 4) = brow;
+    // this item's raw inputs are consumed: fetch the next item's
+    if (it + (int)gridDim.x < items) prefetch(it + gridDim.x);
+    lds_barrier();
+
+    // ---------------- off-diagonal Akk^T / Aq^T tiles (J < w): column factors of block J
+#pragma unroll
+    for (int J = 0; J < 3; ++J) {
+      if (J < w) {
+#pragma unroll
+        for (int s = 0; s < NKS; ++s) {
+          const bf16x8 afr = load8(tKCo + (pair_index(w, J) * 16 + lr) * PK + 32 * s + 8 * lq);
+          aK[J] = mfma32(afr, KR[s], aK[J]);
+          aQ[J] = mfma32(afr, QR[s], aQ[J]);
+        }
+      }
+    }
+    lds_barrier();  // the column factors and tables are dead: M and T reuse their bytes
+
+    // ---------------- M (beta-scaled, strictly lower) to LDS; Aq (lower incl.) to the
+    // workspace. Lane: row i = 16w + lr, columns j = 16J + 4lq + r.
+    {
+      bf16x4 qv[4];
+#pragma unroll
+      for (int J = 0; J < 4; ++J) {
+        qv[J] = bf16x4{};
+        if (J <= w) {
+          const f32x4 ak = J == w ? aKd : aK[J < 3 ? J : 0];
+          const f32x4 aqv = J == w ? aQd : aQ[J < 3 ? J : 0];
+          f32x4 mv;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int j = 16 * J + 4 * lq + r;
+            mv[r] = (j < i_row) ? brow * ak[r] : 0.f;
+            qv[J][r] = static_cast<bf16>((j <= i_row) ? aqv[r] : 0.f);
+          }
+          *reinterpret_cast<f32x4*>(sM + i_row * PM + 16 * J + 4 * lq) = mv;
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+        *reinterpret_cast<bf16x8*>(blk + W::aq + (i_row * 8 + swz<8>(i_row, 4 * m + lq)) * 16) = cat8(qv[2 * m], qv[2 * m + 1]);
+    }
+    lds_barrier();
+
+    // ---------------- T = (I + M)^-1, diagonal block w: forward substitution. Lane: column
+    // j = lr, rows 4lq + r; M is strictly lower, so T[k][j] is final when step k uses it.
+    {
+      float tc[4];
+      f32x4 mr[4][4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        tc[r] = (4 * lq + r == lr) ? 1.f : 0.f;
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4) mr[r][c4] = load4f(sM + (16 * w + 4 * lq + r) * PM + 16 * w + 4 * c4);
+      }
+#pragma unroll
+      for (int kk = 0; kk < 15; ++kk) {
+        const float tk = __shfl(tc[kk & 3], (kk >> 2) * 16 + lr);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) tc[r] -= mr[r][kk >> 2][kk & 3] * tk;
+      }
+      bf16x4 tb;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        tb[r] = static_cast<bf16>(tc[r]);
+        tT[(16 * w + 4 * lq + r) * PC + 16 * w + lr] = tb[r];
+      }
+      *reinterpret_cast<bf16x4*>(tTT + (16 * w + lr) * PC + 16 * w + 4 * lq) = tb;
+    }
+    lds_barrier();
+
+    // level A: T[I][I-1] = -T[I][I] (M[I][I-1] T[I-1][I-1]) for I = 1 (wave 0), 3 (wave 1)
+    if (w < 2) {
+      const int I = w == 0 ? 1 : 3;
+      const f32x4 mv = load4f(sM + (16 * I + lr) * PM + 16 * (I - 1) + 4 * lq);
+      const f32x4 z = mfma16(cvt4(mv), load4(tTT + (16 * (I - 1) + lr) * PC + 16 * (I - 1) + 4 * lq),
+                             f32x4{0.f, 0.f, 0.f, 0.f});
+      const f32x4 t = mfma16(load4(tT + (16 * I + lr) * PC + 16 * I + 4 * lq), cvt4(z), f32x4{0.f, 0.f, 0.f, 0.f});
+      bf16x4 tb;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        tb[r] = static_cast<bf16>(-t[r]);
+        tT[(16 * I + 4 * lq + r) * PC + 16 * (I - 1) + lr] = tb[r];
+      }
+      *reinterpret_cast<bf16x4*>(tTT + (16 * (I - 1) + lr) * PC + 16 * I + 4 * lq) = tb;
+    }
+    lds_barrier();
+
+    // level B: T[I][J] = -sum_{K=2,3} T[I][K] Z2[K][J], Z2[K][J] = sum_{L=0,1} M[K][L] T[L][J];
+    // wave -> (I, J) (T[0][1] = T[2][3] = 0 are skipped)
+    {
+      const int I = 2 + (w >> 1), J = w & 1;
+      f32x4 z2[2];
+#pragma unroll
+      for (int K2 = 2; K2 < 4; ++K2) {
+        f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int L2 = 0; L2 < 2; ++L2) {
+          if (L2 >= J) {
+            const f32x4 mv = load4f(sM + (16 * K2 + lr) * PM + 16 * L2 + 4 * lq);
+            z = mfma16(cvt4(mv), load4(tTT + (16 * J + lr) * PC + 16 * L2 + 4 * lq), z);
+          }
+        }
+        z2[K2 - 2] = z;
+      }
+      f32x4 t = mfma16(load4(tT + (16 * I + lr) * PC + 32 + 4 * lq), cvt4(z2[0]), f32x4{0.f, 0.f, 0.f, 0.f});
+      if (I == 3) t = mfma16(load4(tT + (16 * I + lr) * PC + 48 + 4 * lq), cvt4(z2[1]), t);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) tT[(16 * I + 4 * lq + r) * PC + 16 * J + lr] = static_cast<bf16>(-t[r]);
+    }
+    lds_barrier();
+
+    // ---------------- copy-out: T (upper blocks written as zeros), (K*Gam_C/Gam)^T, Gam_C
+#pragma unroll
+    for (int rep = 0; rep < 2; ++rep) {
+      const int task = tid + 256 * rep, i = task >> 3, c8 = task & 7;
+      const int m = c8 >> 2, q = c8 & 3, I = i >> 4;
+      const bf16x4 lo = (2 * m <= I) ? load4(tT + i * PC + 32 * m + 4 * q) : bf16x4{};
+      const bf16x4 hi = (2 * m + 1 <= I) ? load4(tT + i * PC + 32 * m + 16 + 4 * q) : bf16x4{};
+      *reinterpret_cast<bf16x8*>(blk + W::t + (i * 8 + swz<8>(i, c8)) * 16) = cat8(lo, hi);
+    }
+#pragma unroll
+    for (int rep = 0; rep < KT / 32; ++rep) {
+      const int task = tid + 256 * rep, c = task >> 3, c8 = task & 7;
+      *reinterpret_cast<bf16x8*>(blk + W::kdt + (c * 8 + swz<8>(c, c8)) * 16) = load8(tKdT + c * PC + 8 * c8);
+    }
+    if (tid < KT / 4) *reinterpret_cast<f32x4*>(blk + W::gam + tid * 16) = load4f(sGam + 4 * tid);
+    lds_barrier();  // the next item's scan writes over T
+  }
+}
+
+// ================================================================ sequential state pass
+
+template <int KT>
+__device__ __forceinline__ void dma_block(unsigned char* dst, const unsigned char* src, int wv, int nw, int lane) {
+  constexpr int NB = Blk<KT>::bytes / 1024;
+  for (int j = wv; j < NB; j += nw) {
+#if __HIP_DEVICE_COMPILE__  // device-only builtin (LDS address space)
+    __builtin_amdgcn_global_load_lds(src + 1024 * j + 16 * lane,
+                                     (__attribute__((address_space(3))) void*)(dst + 1024 * j), 16, 0, 0);
+#endif
+  }
+}
+
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+
+// One workgroup per (b, hv, 16*NW-column V tile): NW compute waves and two DMA waves.
+// Compute wave wv owns V columns v0 + 16wv + lr and the whole K x 16 state slab in
+// accumulator layout (S[ct]: rows 16ct + 4lq..+3); the DMA waves stream the next chunk's
+// factors into the other LDS buffer, so the compute waves never wait on memory issue.
+constexpr int kDmaWaves = 2;
+
+template <int KT, int NW>
+__global__ __launch_bounds__(64 * (NW + kDmaWaves)) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void state_kernel(WyArgs a) {
+  using W = Blk<KT>;
+  constexpr int RQ = KT / 8;
+  constexpr int NKS = KT / 32, NCT = KT / 16;
+  constexpr int BV = 16 * NW;
+  const PrefillArgs& p = a.p;
+
+  // per buffer: the chunk's factors, then v^T of the V tile ([BV][64 + 8] bf16)
+  constexpr int PV = kC + 8;
+  constexpr int VT = W::bytes, BUF = W::bytes + BV * PV * 2;
+  __shared__ __attribute__((aligned(1024))) unsigned char buf0[BUF];
+  __shared__ __attribute__((aligned(1024))) unsigned char buf1[BUF];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = lane & 15, lq = lane >> 4;
+
+  const int nvt = (p.V + BV - 1) / BV;
+  const int nh = p.B * p.HV;
+  int head, vt_idx;
+  if (nh % 8 == 0) {  // sibling V tiles of a head on one XCD (round-robin dispatch over 8)
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    head = (slot / nvt) * 8 + xcd;
+    vt_idx = slot % nvt;
+  } else {
+    head = blockIdx.x / nvt;
+    vt_idx = blockIdx.x % nvt;
+  }
+  const int b = head / p.HV, hv = head - b * p.HV;
+  const int K = p.K, V = p.V, T = p.T, NT = a.NT;
+  const unsigned char* wsh = a.ws + (size_t)head * NT * W::bytes;
+
+  // Both roles pass the same barriers: one before each chunk. Before a buffer is read, the
+  // DMA waves have waited for their loads into it; before it is refilled, every compute
+  // wave has passed the barrier that follows its last read.
+  const unsigned rowb = (unsigned)(p.HV * V * 2);  // bytes between consecutive tokens of v / o
+  if (wv >= NW) {
+    // DMA waves: the factors by LDS DMA; the v tile by range-checked loads (zeros past T
+    // or V), written transposed so a compute lane reads 4 consecutive tokens at once.
+    // v tile: 64 rows x BV/8 pieces of 8 columns; lane pl takes pieces pl + 128 e (V % 8 == 0,
+    // so a piece is wholly inside or outside the row)
+    const int pw = wv - NW, pl = 64 * pw + lane;  // 128 lanes
+    constexpr int NPL = BV / 16;                      // pieces per lane
+    constexpr int PPR = BV / 8;                       // pieces per row
+    unsigned voff[NPL];
+#pragma unroll
+    for (int e = 0; e < NPL; ++e) {
+      const int pc = pl + 128 * e, row = pc / PPR, c8 = pc % PPR;
+      const int col = vt_idx * BV + 8 * c8;
+      voff[e] = col < V ? (unsigned)(col * 2) + (unsigned)row * rowb : kOutOfRange;
+    }
+    bf16x8 rvv[NPL];
+    auto load_v = [&](int n) {
+      const int t0 = n * kC, nrow = min(kC, T - t0);
+      const auto rv_ = make_rsrc(static_cast<const bf16*>(p.v) + (((size_t)b * T + t0) * p.HV + hv) * V,
+                                 (unsigned)nrow * rowb);
+#pragma unroll
+      for (int e = 0; e < NPL; ++e)
+        rvv[e] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rv_, voff[e], 0, 0));
+    };
+    auto store_v = [&](unsigned char* dst) {
+      bf16* vt = reinterpret_cast<bf16*>(dst + VT);
+#pragma unroll
+      for (int e = 0; e < NPL; ++e) {
+        const int pc = pl + 128 * e, row = pc / PPR, c8 = pc % PPR;
+#pragma unroll
+        for (int x = 0; x < 8; ++x) vt[(8 * c8 + x) * PV + row] = rvv[e][x];
+      }
+    };
+    dma_block<KT>(buf0, wsh, pw, kDmaWaves, lane);
+    load_v(0);
+    wait_vmem();
+    store_v(buf0);
+    for (int n = 0; n < NT; n += 2) {
+      lds_barrier();
+      if (n + 1 < NT) {
+        dma_block<KT>(buf1, wsh + (size_t)(n + 1) * W::bytes, pw, kDmaWaves, lane);
+        load_v(n + 1);
+        wait_vmem();
+        store_v(buf1);
+      }
+      if (n + 1 >= NT) break;
+      lds_barrier();
+      if (n + 2 < NT) {
+        dma_block<KT>(buf0, wsh + (size_t)(n + 2) * W::bytes, pw, kDmaWaves, lane);
+        load_v(n + 2);
+        wait_vmem();
+        store_v(buf0);
+      }
+    }
+    return;
+  }
+
+  const int vc = vt_idx * BV + 16 * wv + lr;  // the lane's V column
+  const bool vok = vc < V;
+  // lane part of an o offset (column, rows 4lq); columns >= V start out of range. The row
+  // part (16I + r) * rowb goes in the scalar offset.
+  const unsigned vlane = vok ? (unsigned)(vc * 2) + 4u * lq * rowb : kOutOfRange;
+
+  f32x4 S[NCT];
+  {
+    const float* s0 = p.s0 ? p.s0 + (size_t)head * K * V : nullptr;
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int c = 16 * ct + 4 * lq + r;
+        S[ct][r] = (s0 && vok && c < K) ? s0[(size_t)c * V + vc] : 0.f;
+      }
+  }
+
+  auto step = [&](const unsigned char* bk, int n) {
+    const int t0 = n * kC, nrow = min(kC, T - t0);
+    auto frag_q = [&](int tile, int J, int m) {  // rows of Q*Gam / K*Gam
+      const int row = 16 * J + lr;
+      return load8(bk + tile + (row * RQ + swz<RQ>(row, 4 * m + lq)) * 16);
+    };
+    auto frag64 = [&](int tile, int row, int m) {  // rows of T, Aq, (K*Gam_C/Gam)^T
+      return load8(bk + tile + (row * 8 + swz<8>(row, 4 * m + lq)) * 16);
+    };
+    // X = (K*Gam) S and P = (Q*Gam) S: A fragments double-buffered one k step ahead
+    f32x4 X[4], P[4];
+#pragma unroll
+    for (int J = 0; J < 4; ++J) X[J] = P[J] = f32x4{0.f, 0.f, 0.f, 0.f};
+    bf16x8 fx[2][8];
+#pragma unroll
+    for (int J = 0; J < 4; ++J) {
+      fx[0][J] = frag_q(W::kg, J, 0);
+      fx[0][4 + J] = frag_q(W::qg, J, 0);
+    }
+    bf16x8 ft[6], fa[6];  // T and Aq fragments (I, m <= I/2), loaded under the X/P products
+#pragma unroll
+    for (int m = 0; m < NKS; ++m) {
+      if (m + 1 < NKS) {
+#pragma unroll
+        for (int J = 0; J < 4; ++J) {
+          fx[(m + 1) & 1][J] = frag_q(W::kg, J, m + 1);
+          fx[(m + 1) & 1][4 + J] = frag_q(W::qg, J, m + 1);
+        }
+      }
+      if (m == NKS - 1) {
+#pragma unroll
+        for (int I = 0, f = 0; I < 4; ++I)
+#pragma unroll
+          for (int mm = 0; mm <= I / 2; ++mm, ++f) {
+            ft[f] = frag64(W::t, 16 * I + lr, mm);
+            fa[f] = frag64(W::aq, 16 * I + lr, mm);
+          }
+      }
+      const bf16x8 sb = cat8(cvt4(S[2 * m]), cvt4(S[2 * m + 1]));
+#pragma unroll
+      for (int J = 0; J < 4; ++J) {
+        X[J] = mfma32(fx[m & 1][J], sb, X[J]);
+        P[J] = mfma32(fx[m & 1][4 + J], sb, P[J]);
+      }
+    }
+    // beta (V - X), bf16, as B operands of the 32-token steps
+    bf16x8 yb[2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      bf16x4 y[2];
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int J = 2 * m + h2;
+        const f32x4 bt = load4f(bk + W::beta + (16 * J + 4 * lq) * 4);
+        const bf16x4 vv = load4(bk + VT + ((16 * wv + lr) * PV + 16 * J + 4 * lq) * 2);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) y[h2][r] = static_cast<bf16>(bt[r] * (to_f32(vv[r]) - X[J][r]));
+      }
+      yb[m] = cat8(y[0], y[1]);
+    }
+    // (K*Gam_C/Gam)^T fragments and Gam_C for the state update, loaded under U and O
+    bf16x8 fk[NCT][2];
+    f32x4 gm[NCT];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      fk[ct][0] = frag64(W::kdt, 16 * ct + lr, 0);
+      fk[ct][1] = frag64(W::kdt, 16 * ct + lr, 1);
+      gm[ct] = load4f(bk + W::gam + (16 * ct + 4 * lq) * 4);
+    }
+    // U = T (beta Y); T is lower block-triangular, so block I needs 32-token steps m <= I/2
+    f32x4 U[4];
+    U[0] = mfma32(ft[0], yb[0], f32x4{0.f, 0.f, 0.f, 0.f});
+    U[1] = mfma32(ft[1], yb[0], f32x4{0.f, 0.f, 0.f, 0.f});
+    U[2] = mfma32(ft[3], yb[1], mfma32(ft[2], yb[0], f32x4{0.f, 0.f, 0.f, 0.f}));
+    U[3] = mfma32(ft[5], yb[1], mfma32(ft[4], yb[0], f32x4{0.f, 0.f, 0.f, 0.f}));
+    bf16x8 ub[2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) ub[m] = cat8(cvt4(U[2 * m]), cvt4(U[2 * m + 1]));
+    // O = scale (P + Aq U)
+    f32x4 O[4];
+    O[0] = mfma32(fa[0], ub[0], P[0]);
+    O[1] = mfma32(fa[1], ub[0], P[1]);
+    O[2] = mfma32(fa[3], ub[1], mfma32(fa[2], ub[0], P[2]));
+    O[3] = mfma32(fa[5], ub[1], mfma32(fa[4], ub[0], P[3]));
+    // stores go out before the state update so they drain under its products
+    const auto ro_ = make_rsrc(static_cast<const bf16*>(p.o) + (((size_t)b * T + t0) * p.HV + hv) * V,
+                               (unsigned)nrow * rowb);
+#pragma unroll
+    for (int I = 0; I < 4; ++I)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, static_cast<bf16>(p.scale * O[I][r])),
+                                              ro_, vlane, (16 * I + r) * rowb, 0);
+    // S = diag(Gam_C) S + (K*Gam_C/Gam)^T U
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) S[ct] = mfma32(fk[ct][1], ub[1], mfma32(fk[ct][0], ub[0], S[ct] * gm[ct]));
+  };
+
+  for (int n = 0; n < NT; n += 2) {
+    lds_barrier();
+    step(buf0, n);
+    if (n + 1 >= NT) break;
+    lds_barrier();
+    step(buf1, n + 1);
+  }
+
+  if (p.sT) {
+    float* sT = p.sT + (size_t)head * K * V;
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int c = 16 * ct + 4 * lq + r;
+        if (vok && c < K) sT[(size_t)c * V + vc] = S[ct][r];
+      }
+  }
+}
+
+template <int KT, int NW>
+hipError_t launch_cfg(const WyArgs& a, int cus, hipStream_t stream) {
+  const int items = a.p.B * a.p.HV * a.NT;
+  const int grid_a = items < 2 * cus ? items : 2 * cus;
+  hipLaunchKernelGGL((factors_kernel<KT>), dim3(grid_a), dim3(256), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int nvt = (a.p.V + 16 * NW - 1) / (16 * NW);
+  hipLaunchKernelGGL((state_kernel<KT, NW>), dim3(a.p.B * a.p.HV * nvt), dim3(64 * (NW + kDmaWaves)), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace wy
+
+int device_cu_count();
+
+size_t wy_workspace_bytes(int B, int T, int HV, int K) {
+  return (size_t)B * HV * ((T + wy::kC - 1) / wy::kC) * wy::block_bytes(K);
+}
+
+// bf16 inputs, K % 8 == 0, 16-byte aligned q/k/g, and a workspace of wy_workspace_bytes.
+// The state pass runs one workgroup per CU (double-buffered LDS); its V tile is the widest
+// of 16, 32 or 64 columns that still gives every CU a workgroup.
+hipError_t launch_prefill_wy(const PrefillArgs& p, void* workspace, hipStream_t stream) {
+  using namespace wy;
+  WyArgs a{p, static_cast<unsigned char*>(workspace), (p.T + kC - 1) / kC};
+  const int cus = device_cu_count();
+  const int heads = p.B * p.HV;
+  const int nw = p.V <= 16 ? 1 : (p.V <= 32 || heads * ((p.V + 31) / 32) <= cus) ? 2 : 4;
+  if (p.K <= 32) return nw == 1 ? launch_cfg<32, 1>(a, cus, stream) : nw == 2 ? launch_cfg<32, 2>(a, cus, stream) : launch_cfg<32, 4>(a, cus, stream);
+  if (p.K <= 64) return nw == 1 ? launch_cfg<64, 1>(a, cus, stream) : nw == 2 ? launch_cfg<64, 2>(a, cus, stream) : launch_cfg<64, 4>(a, cus, stream);
+  if (p.K <= 128) return nw == 1 ? launch_cfg<128, 1>(a, cus, stream) : nw == 2 ? launch_cfg<128, 2>(a, cus, stream) : launch_cfg<128, 4>(a, cus, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace kda

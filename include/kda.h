@@ -65,12 +65,23 @@ typedef enum { KDA_DTYPE_F32 = 0, KDA_DTYPE_BF16 = 1 } kda_dtype;
  *   chunk_size     8, 16, 32 or 64 and T % chunk_size == 0 (same page, key-constraints
  *                  table, chunk_size row). The result does not depend on it beyond
  *                  rounding: kernels tile time by 64 tokens and mask a partial last tile.
- *   workspace      device scratch of kda_chunk_fwd_workspace_size() bytes (may be NULL
- *                  when that size is 0)
+ *   workspace      NULL, or device memory of at least kda_chunk_fwd_workspace_size()
+ *                  bytes, 256-byte aligned, owned by the caller and overwritten by the
+ *                  call (calls sharing one workspace must be ordered on one stream).
+ *                  For bf16 with K % 8 == 0 and V % 8 == 0 (16-byte aligned q, k, g, v)
+ *                  a workspace selects the two-kernel path: the state-independent
+ *                  per-chunk factors of the same roadmap rows (Q*Gam, K*Gam,
+ *                  (K*Gam_C/Gam)^T, T = (I + M)^-1, Aq, Gam_C, beta) are computed for all
+ *                  chunks at once, then a sequential pass carries the state. NULL selects
+ *                  the single fused kernel, which needs no workspace. A non-NULL
+ *                  workspace that is too small or misaligned returns KDA_ERR_INVALID.
  *
  * Constraints: B, T, H, HV, K, V >= 1; HV % H == 0; K <= 128 and V <= 128 (else
  * KDA_ERR_UNSUPPORTED); float32 needs K <= 64 (else KDA_ERR_UNSUPPORTED).
  */
+/* Bytes of workspace the two-kernel path uses for these arguments: one block per
+ * (b, hv, 64-token chunk) for bf16 with K % 8 == 0 and V % 8 == 0, else 0 (also 0 for
+ * arguments kda_chunk_fwd would reject). */
 size_t kda_chunk_fwd_workspace_size(int B, int T, int H, int HV, int K, int V,
                                     int chunk_size, int dtype);
 

@@ -47,8 +47,20 @@ def test_status_strings(lib):
     assert lib.kda_version().decode().startswith("kda-gfx950")
 
 
-def test_workspace_is_zero(lib):
-    assert lib.kda_chunk_fwd_workspace_size(4, 8192, 16, 16, 128, 128, 64, 1) == 0
+def test_workspace_size(lib):
+    ws = lib.kda_chunk_fwd_workspace_size
+    per = ws(1, 64, 1, 1, 128, 128, 64, 1)  # one (b, hv, 64-token chunk) block, K = 128
+    # the block holds Q*Gam, K*Gam, (K*Gam_C/Gam)^T (64 x 128 bf16 each), T and Aq (64 x 64
+    # bf16), Gam_C (128 fp32) and beta (64 fp32), in whole kilobytes
+    need = 3 * 64 * 128 * 2 + 2 * 64 * 64 * 2 + 128 * 4 + 64 * 4
+    assert need <= per < need + 1024 and per % 1024 == 0
+    assert ws(4, 8192, 16, 16, 128, 128, 64, 1) == 4 * 16 * 128 * per
+    assert ws(2, 65, 4, 8, 128, 64, 1, 1) == 2 * 8 * 2 * per     # a partial last chunk counts
+    assert ws(1, 64, 1, 1, 64, 64, 64, 1) < per                   # K = 64 blocks are smaller
+    assert ws(4, 8192, 16, 16, 64, 64, 64, 0) == 0                # fp32: fused, no workspace
+    assert ws(4, 8192, 16, 16, 124, 128, 64, 1) == 0              # K % 8 != 0: generic kernel
+    assert ws(4, 8192, 16, 16, 128, 36, 64, 1) == 0               # V % 8 != 0: fused kernel
+    assert ws(0, 64, 1, 1, 128, 128, 64, 1) == 0                  # invalid shapes ask for none
 
 
 FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation
@@ -60,7 +72,7 @@ def _chunk(lib, **kw):
     a.update(kw)
     return lib.kda_chunk_fwd(a["q"], a["k"], a["v"], a["g"], a["beta"], a["s0"], a["sT"], a["o"],
                              a["B"], a["T"], a["H"], a["HV"], a["K"], a["V"], a["scale"],
-                             a["chunk"], a["dtype"], None, 0, None)
+                             a["chunk"], a["dtype"], a.get("ws"), a.get("ws_bytes", 0), None)
 
 
 @pytest.mark.parametrize("bad,rc", [
@@ -79,6 +91,8 @@ def _chunk(lib, **kw):
     (dict(K=256), kda.KDA_ERR_UNSUPPORTED),
     (dict(V=160), kda.KDA_ERR_UNSUPPORTED),
     (dict(K=128, dtype=0), kda.KDA_ERR_UNSUPPORTED),  # fp32 needs K <= 64
+    (dict(ws=FAKE, ws_bytes=1024), kda.KDA_ERR_INVALID),          # workspace too small
+    (dict(ws=ctypes.c_void_p(0x1010), ws_bytes=1 << 30), kda.KDA_ERR_INVALID),  # misaligned
 ])
 def test_chunk_fwd_rejects_invalid_arguments(lib, bad, rc):
     assert _chunk(lib, **bad) == rc

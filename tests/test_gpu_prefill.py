@@ -128,21 +128,56 @@ def test_prefill_equals_decode_steps():
     assert_parity(to64(state), ref_s, torch.bfloat16, "decode state")
 
 
-def test_in_place_state_and_poisoned_output():
-    log("prefill in-place state (final_state == initial_state) with NaN-poisoned o")
+def _abi_fwd(d, state_in, state_out, o, workspace, chunk=64):
+    """kda_chunk_fwd through the C ABI; workspace=False passes NULL (single fused kernel),
+    True passes a workspace of the queried size (per-chunk factors + state pass)."""
+    B, T, H, K = d["q"].shape
+    HV, V = d["v"].shape[2], d["v"].shape[3]
+    lib = kda.library()
+    ws = None
+    if workspace:
+        nbytes = lib.kda_chunk_fwd_workspace_size(B, T, H, HV, K, V, chunk, 1)
+        assert nbytes > 0
+        ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    p = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else None
+    rc = lib.kda_chunk_fwd(p(d["q"]), p(d["k"]), p(d["v"]), p(d["g"]), p(d["beta"]),
+                           p(state_in), p(state_out), p(o), B, T, H, HV, K, V,
+                           float(d["scale"]), chunk, 1, p(ws), ws.numel() if ws is not None else 0,
+                           None)
+    torch.cuda.synchronize()
+    return rc
+
+
+@pytest.mark.parametrize("workspace", [False, True], ids=["fused", "factored"])
+def test_in_place_state_and_poisoned_output(workspace):
+    log(f"prefill in-place state (final_state == initial_state) with NaN-poisoned o, "
+        f"workspace={workspace}")
     inp = prefill_inputs(2, 192, 2, 4, 128, 128, "bf16", True, 31)
     d = gpu(inp)
     state = d["initial_state"].clone()
     o = torch.full(d["v"].shape, float("nan"), dtype=torch.bfloat16, device="cuda")
-    p = lambda t: ctypes.c_void_p(t.data_ptr())
-    rc = kda.library().kda_chunk_fwd(p(d["q"]), p(d["k"]), p(d["v"]), p(d["g"]), p(d["beta"]),
-                                     p(state), p(state), p(o), 2, 192, 2, 4, 128, 128,
-                                     float(d["scale"]), 64, 1, None, 0, None)
-    torch.cuda.synchronize()
-    assert rc == kda.KDA_OK
+    assert _abi_fwd(d, state, state, o, workspace) == kda.KDA_OK
     ref_o, ref_s = recurrent(**inp)
     assert_parity(to64(o), ref_o, torch.bfloat16, "o")
     assert_parity(to64(state), ref_s, torch.bfloat16, "state")
+
+
+@pytest.mark.parametrize("shape", [
+    dict(B=2, T=192, H=2, HV=4, K=128, V=128),
+    dict(B=1, T=200, H=1, HV=2, K=64, V=48),       # ragged last chunk, V tile partly empty
+    dict(B=3, T=136, H=1, HV=3, K=40, V=16),       # K between tile sizes
+])
+def test_fused_and_factored_paths(shape):
+    log(f"prefill fused vs factored path {shape}")
+    inp = prefill_inputs(**shape, dtype="bf16", init_state=True, seed=shape["T"] + shape["K"])
+    d = gpu(inp)
+    ref_o, ref_s = recurrent(**inp)
+    for workspace in (False, True):
+        o = torch.empty_like(d["v"])
+        s = torch.empty_like(d["initial_state"])
+        assert _abi_fwd(d, d["initial_state"], s, o, workspace, chunk=8) == kda.KDA_OK
+        assert_parity(to64(o), ref_o, torch.bfloat16, f"o workspace={workspace}")
+        assert_parity(to64(s), ref_s, torch.bfloat16, f"state workspace={workspace}")
 
 
 def test_no_initial_state_and_no_final_state():
