@@ -8,10 +8,13 @@ layers). `value` is prefill tokens/s (B*T per step). The decode step
 state cache) is timed in the same run and reported under "decode".
 
 Timing uses HIP events recorded on the stream the kernels are launched on,
-bracketed by device synchronisation. The roofline object prices the prefill
-kernel's algorithmic bytes (q, k, v, g, beta read once, o and the final state
-written once) against MI355X's 8 TB/s HBM3E peak; the decode object prices its
-algorithmic bytes (state read + write, plus the token vectors) the same way.
+bracketed by device synchronisation. One prefill call is two kernels on that
+stream (factors_kernel: the state-independent per-chunk factors for all chunks;
+state_kernel: the sequential state pass), timed together. The roofline object
+prices the call's algorithmic bytes (q, k, v, g, beta read once, o and the final
+state written once) against MI355X's 8 TB/s HBM3E peak; the decode object prices
+its algorithmic bytes (state read + write, plus the token vectors) the same way.
+A 1 GiB device copy is timed in the same run as the measured HBM ceiling.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -30,8 +33,9 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFS = 2516.6     # MI355X dense bf16 MFMA, published (no sparsity)
 METRIC = "KDA prefill tokens/s + MFMA util (H=16,K=V=128,T=8192); decode state HBM GB/s"
-PREFILL_KERNEL = "prefill_kernel"
+PREFILL_KERNELS = ["kda::wy::factors_kernel<128>", "kda::wy::state_kernel<128, 2>"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_traffic.json")
+MEASURED_SOURCES = ["kda_chunk_wy.hip", "kda_device.h"]
 
 
 def log(msg):
@@ -58,9 +62,13 @@ def decode_algorithmic(B, H, HV, K, V, ib):
 
 
 def source_hash():
-    path = os.path.join(ROOT, "gated_delta_rule_67_amd", "csrc", "kda_prefill.hip")
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the sources of the measured prefill kernels (traffic counters go stale when
+    they change)."""
+    h = hashlib.sha256()
+    for name in MEASURED_SOURCES:
+        with open(os.path.join(ROOT, "gated_delta_rule_67_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic():
@@ -93,6 +101,24 @@ def time_launches(fn, steps, warmup, torch):
     total = ev[0].elapsed_time(ev[steps])
     per.sort()
     return total / steps, per[len(per) // 2], per[0]
+
+
+def copy_ceiling(torch, nbytes=1 << 30, reps=5):
+    """Measured HBM ceiling: GB/s of a 1 GiB device-to-device copy (read + write bytes)."""
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    for _ in range(reps):
+        dst.copy_(src)
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / reps
+    del src, dst
+    return 2 * nbytes / (ms * 1e-3) / 1e9
 
 
 def cpu_baseline(tokens):
@@ -167,6 +193,8 @@ def main():
     tflops = flops / (avg_ms * 1e-3) / 1e12
     traffic = measured_traffic()
     del d, o, s
+    ceiling = copy_ceiling(torch)
+    t_bound = max(flops / (MFMA_BF16_PEAK_TFS * 1e12), byts / (HBM_PEAK_GBS * 1e9))
 
     result = {
         "metric": METRIC,
@@ -187,8 +215,11 @@ def main():
                    "chunk_size": c["chunk"], "seed": 1236},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": PREFILL_KERNEL, "algorithmic_bytes_per_launch": byts,
-                     "avg_launch_ms": avg_ms, "median_launch_ms": med_ms, "min_launch_ms": min_ms},
+                     "kernel": " + ".join(PREFILL_KERNELS) + " (one kda_chunk_fwd call)",
+                     "algorithmic_bytes_per_launch": byts,
+                     "avg_launch_ms": avg_ms, "median_launch_ms": med_ms, "min_launch_ms": min_ms,
+                     "roofline_frac": t_bound * 1e3 / avg_ms,
+                     "measured_copy_ceiling_gbs": ceiling, "frac_of_copy_ceiling": achieved / ceiling},
         "mfma": {"algorithmic_tflops": tflops, "peak_tflops": MFMA_BF16_PEAK_TFS,
                  "frac": tflops / MFMA_BF16_PEAK_TFS, "algorithmic_flops_per_launch": flops},
     }
@@ -233,7 +264,8 @@ def main():
             "value": gbs, "unit": "GB/s", "ms_per_step": step_ms,
             "tokens_per_s": c3["B"] / (step_ms * 1e-3),
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": gbs / HBM_PEAK_GBS, "kernel": "decode_step_kernel",
+                         "frac": gbs / HBM_PEAK_GBS, "frac_of_copy_ceiling": gbs / ceiling,
+                         "kernel": "decode_step_kernel",
                          "algorithmic_bytes_per_launch": dbytes,
                          "median_launch_ms": per_step[len(per_step) // 2]},
         }

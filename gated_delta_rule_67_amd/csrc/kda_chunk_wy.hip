@@ -85,6 +85,8 @@ __device__ __forceinline__ f32x4 mfma16(bf16x4 a, bf16x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
 }
 
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
 // Raw buffer resources: a lane whose offset is kOutOfRange (or past the range) reads zeros
 // and its stores are dropped, so masked loads need no branches.
 constexpr unsigned kOutOfRange = 0x80000000u;
@@ -463,24 +465,38 @@ __global__ __launch_bounds__(256) void factors_kernel(WyArgs a) {
 
 // ================================================================ sequential state pass
 
+constexpr int kDmaWaves = 2;
+
+// Wave pw of the DMA waves copies rows pw, pw + kDmaWaves, ... (1 KB each) of a block into
+// dst; lane l moves bytes 16l..16l+15 of a row (buffer DMA: the row offset is a scalar).
 template <int KT>
-__device__ __forceinline__ void dma_block(unsigned char* dst, const unsigned char* src, int wv, int nw, int lane) {
+__device__ __forceinline__ void dma_block(unsigned char* dst, const unsigned char* src, int pw, int lane) {
   constexpr int NB = Blk<KT>::bytes / 1024;
-  for (int j = wv; j < NB; j += nw) {
+  const __amdgpu_buffer_rsrc_t r = make_rsrc(src, Blk<KT>::bytes);
+  const unsigned voff = 1024u * pw + 16u * lane;
+#pragma unroll
+  for (int i = 0; i < (NB + kDmaWaves - 1) / kDmaWaves; ++i) {
+    const int j = kDmaWaves * i + pw;
+    if (j < NB) {
 #if __HIP_DEVICE_COMPILE__  // device-only builtin (LDS address space)
-    __builtin_amdgcn_global_load_lds(src + 1024 * j + 16 * lane,
-                                     (__attribute__((address_space(3))) void*)(dst + 1024 * j), 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(dst + 1024 * j), 16,
+                                                voff, 1024 * kDmaWaves * i, 0, 0);
 #endif
+    }
   }
 }
 
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+// s_waitcnt vmcnt(N) (expcnt and lgkmcnt left unconstrained)
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
 
 // One workgroup per (b, hv, 16*NW-column V tile): NW compute waves and two DMA waves.
 // Compute wave wv owns V columns v0 + 16wv + lr and the whole K x 16 state slab in
 // accumulator layout (S[ct]: rows 16ct + 4lq..+3); the DMA waves stream the next chunk's
 // factors into the other LDS buffer, so the compute waves never wait on memory issue.
-constexpr int kDmaWaves = 2;
 
 template <int KT, int NW>
 __global__ __launch_bounds__(64 * (NW + kDmaWaves)) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -536,7 +552,8 @@ void state_kernel(WyArgs a) {
       voff[e] = col < V ? (unsigned)(col * 2) + (unsigned)row * rowb : kOutOfRange;
     }
     bf16x8 rvv[NPL];
-    auto load_v = [&](int n) {
+    auto load_v = [&](int n) {  // n past the end re-reads the last chunk (no branch)
+      n = min(n, NT - 1);
       const int t0 = n * kC, nrow = min(kC, T - t0);
       const auto rv_ = make_rsrc(static_cast<const bf16*>(p.v) + (((size_t)b * T + t0) * p.HV + hv) * V,
                                  (unsigned)nrow * rowb);
@@ -553,27 +570,45 @@ void state_kernel(WyArgs a) {
         for (int x = 0; x < 8; ++x) vt[(8 * c8 + x) * PV + row] = rvv[e][x];
       }
     };
-    dma_block<KT>(buf0, wsh, pw, kDmaWaves, lane);
+    // L2 warm-up one chunk further ahead: the sibling workgroups of a head (V tiles) split
+    // each block's 1 KB rows between their DMA waves, so the block comes from HBM once and
+    // the DMA an interval later hits L2. The loaded values are not used. The warm-up loads
+    // are issued after the wait for the DMA (vmcnt is in order), so they stay in flight
+    // across the barrier; their registers are consumed just before the next reuse.
+    constexpr int NB = W::bytes / 1024;
+    constexpr int NPF = (NB * NW + 15) / 16;  // rows per wave when V tiles cover 128 columns
+    u32x4 pf[NPF];
+#pragma unroll
+    for (int i = 0; i < NPF; ++i) pf[i] = u32x4{0u, 0u, 0u, 0u};
+    const int pf_row0 = (vt_idx * kDmaWaves + pw) * NPF;
+    auto warm = [&](int n) {  // n past the end re-reads the last block (no branch)
+      const unsigned char* src = wsh + (size_t)min(n, NT - 1) * W::bytes + 16 * lane;
+#pragma unroll
+      for (int i = 0; i < NPF; ++i) {
+        asm volatile("" ::"v"(pf[i]));
+        pf[i] = *reinterpret_cast<const u32x4*>(src + 1024 * ((pf_row0 + i) % NB));
+      }
+    };
+    // chunk n into dst (its v tile was loaded an interval earlier); then v of chunk n + 1
+    // and the L2 warm-up of chunk n + 1 go out and stay in flight across the barrier
+    auto fill = [&](unsigned char* dst, int n) {
+      dma_block<KT>(dst, wsh + (size_t)n * W::bytes, pw, lane);
+      wait_vmem<0>();
+      store_v(dst);
+      load_v(n + 1);
+      warm(n + 1);
+    };
     load_v(0);
-    wait_vmem();
-    store_v(buf0);
+    fill(buf0, 0);
     for (int n = 0; n < NT; n += 2) {
       lds_barrier();
-      if (n + 1 < NT) {
-        dma_block<KT>(buf1, wsh + (size_t)(n + 1) * W::bytes, pw, kDmaWaves, lane);
-        load_v(n + 1);
-        wait_vmem();
-        store_v(buf1);
-      }
+      if (n + 1 < NT) fill(buf1, n + 1);
       if (n + 1 >= NT) break;
       lds_barrier();
-      if (n + 2 < NT) {
-        dma_block<KT>(buf0, wsh + (size_t)(n + 2) * W::bytes, pw, kDmaWaves, lane);
-        load_v(n + 2);
-        wait_vmem();
-        store_v(buf0);
-      }
+      if (n + 2 < NT) fill(buf0, n + 2);
     }
+#pragma unroll
+    for (int i = 0; i < NPF; ++i) asm volatile("" ::"v"(pf[i]));
     return;
   }
 
