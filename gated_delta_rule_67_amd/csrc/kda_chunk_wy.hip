@@ -21,8 +21,12 @@
 // Contractions over a 32-wide k step use v_mfma_f32_16x16x32_bf16, whose lane l supplies 8
 // consecutive k of row/column l%16. The state pass feeds accumulator tiles (lane l: column
 // l%16, rows 4(l/16)..+3) back in as B operands, so each lane's 8 k values are rows
-// 4(l/16)..+3 of two consecutive 16-row tiles. The stored tiles use the matching order:
-// inside every 32-wide group the index 32m + 16h + 4q + r sits at 32m + 8q + 4h + r.
+// 4(l/16)..+3 of two consecutive 16-row tiles. perm32 names the matching order: inside every
+// 32-wide group, index 32m + 16h + 4q + r goes with 32m + 8q + 4h + r. Contractions over
+// tokens (U = T Y, Aq U, the state update) store T, Aq and (K*Gam_C/Gam)^T with their token
+// index at position perm32(token). For contractions over channels the state pass instead keeps
+// state row rho = channel perm32(rho), so Q*Gam and K*Gam are stored in natural channel order
+// (and (K*Gam_C/Gam)^T row rho, Gam_C[rho] belong to channel perm32(rho)).
 //
 // Decay factors (factors_kernel): with r the first token of a 16-token block,
 // d_i = G_i - G_r <= 0, R_i = 2^(d log2 e) <= 1 and C_i = 1/R_i <= e^75 (g >= -5). Diagonal
@@ -39,12 +43,12 @@ constexpr int kC = 64;
 // whole kilobytes so the state pass streams it in 1 KB DMA rounds.
 template <int KT>
 struct Blk {
-  static constexpr int qg = 0;                  // [64][KT] bf16 Q*Gam, channel order permuted
-  static constexpr int kg = qg + kC * KT * 2;   // [64][KT] bf16 K*Gam, channel order permuted
-  static constexpr int kdt = kg + kC * KT * 2;  // [KT][64] bf16 (K*Gam_C/Gam)^T, token order permuted
+  static constexpr int qg = 0;                  // [64][KT] bf16 Q*Gam
+  static constexpr int kg = qg + kC * KT * 2;   // [64][KT] bf16 K*Gam
+  static constexpr int kdt = kg + kC * KT * 2;  // [KT][64] bf16 (K*Gam_C/Gam)^T, rows and tokens permuted
   static constexpr int t = kdt + KT * kC * 2;   // [64][64] bf16 T, column order permuted
   static constexpr int aq = t + kC * kC * 2;    // [64][64] bf16 Aq, column order permuted
-  static constexpr int gam = aq + kC * kC * 2;  // [KT] fp32 Gam_C
+  static constexpr int gam = aq + kC * kC * 2;  // [KT] fp32 Gam_C, rows permuted
   static constexpr int beta = gam + KT * 4;     // [64] fp32 beta
   static constexpr int used = beta + kC * 4;
   static constexpr int bytes = (used + 1023) / 1024 * 1024;
@@ -54,7 +58,7 @@ size_t block_bytes(int K) {
   return K <= 32 ? Blk<32>::bytes : K <= 64 ? Blk<64>::bytes : Blk<128>::bytes;
 }
 
-// Stored position of index x inside its 32-wide group: 32m + 16h + 4q + r -> 32m + 8q + 4h + r.
+// Position of index x inside its 32-wide group: 32m + 16h + 4q + r -> 32m + 8q + 4h + r.
 __device__ __forceinline__ int perm32(int x) {
   return (x & ~31) | ((x & 12) << 1) | ((x & 16) >> 2) | (x & 3);
 }
@@ -93,8 +97,8 @@ constexpr unsigned kOutOfRange = 0x80000000u;
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, unsigned bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
 }
-__device__ __forceinline__ bf16x4 buf_load4(__amdgpu_buffer_rsrc_t r, unsigned off) {
-  return __builtin_bit_cast(bf16x4, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+__device__ __forceinline__ bf16x8 buf_load8(__amdgpu_buffer_rsrc_t r, unsigned off) {
+  return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 __device__ __forceinline__ unsigned buf_load1(__amdgpu_buffer_rsrc_t r, unsigned off) {
   return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
@@ -143,8 +147,8 @@ struct LdsA {
 
 // One workgroup of 4 waves per (b, hv, chunk) item, looping over items with a stride of
 // gridDim.x (the next item's q, k, g are loaded while the current one finishes). Wave w owns
-// the 16-token block w; lane (lr, lq) holds token 16w + lr and, for k step s, the channels
-// whose stored positions are 32s + 8lq..+7, i.e. 32s + 4lq..+3 and 32s + 16 + 4lq..+3.
+// the 16-token block w; lane (lr, lq) holds token 16w + lr and, for k step s, channels
+// 32s + 8lq..+7.
 template <int KT>
 __global__ __launch_bounds__(256) void factors_kernel(WyArgs a) {
   using L = LdsA<KT>;
@@ -173,17 +177,15 @@ __global__ __launch_bounds__(256) void factors_kernel(WyArgs a) {
   const int items = p.B * p.HV * NT;
   const int i_row = 16 * w + lr;  // the lane's token inside the chunk
 
-  // Per-lane byte offsets of the two 4-channel groups of each k step; channels >= K start
+  // Per-lane byte offsets of the 8 channels of each k step; channels >= K (K % 8 == 0) start
   // at kOutOfRange, which stays out of range whatever row offset is added.
-  unsigned cq[NKS][2], cg[NKS][2];
+  unsigned cq[NKS], cg[NKS];
 #pragma unroll
-  for (int s = 0; s < NKS; ++s)
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      const int c = 32 * s + 16 * hh + 4 * lq;
-      cq[s][hh] = c < K ? (unsigned)((i_row * p.H * K + c) * 2) : kOutOfRange;
-      cg[s][hh] = c < K ? (unsigned)((i_row * p.HV * K + c) * 2) : kOutOfRange;
-    }
+  for (int s = 0; s < NKS; ++s) {
+    const int c = 32 * s + 8 * lq;
+    cq[s] = c < K ? (unsigned)((i_row * p.H * K + c) * 2) : kOutOfRange;
+    cg[s] = c < K ? (unsigned)((i_row * p.HV * K + c) * 2) : kOutOfRange;
+  }
 
   bf16x8 rq[NKS], rk[NKS], rg[NKS];
   unsigned rbeta;
@@ -199,16 +201,9 @@ __global__ __launch_bounds__(256) void factors_kernel(WyArgs a) {
     const auto rb_ = make_rsrc(static_cast<const bf16*>(p.beta) + row0 * p.HV + hv, (unsigned)(nrow * p.HV * 2));
 #pragma unroll
     for (int s = 0; s < NKS; ++s) {
-      bf16x4 q2[2], k2[2], g2[2];
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        q2[hh] = buf_load4(rq_, cq[s][hh]);
-        k2[hh] = buf_load4(rk_, cq[s][hh]);
-        g2[hh] = buf_load4(rg_, cg[s][hh]);
-      }
-      rq[s] = cat8(q2[0], q2[1]);
-      rk[s] = cat8(k2[0], k2[1]);
-      rg[s] = cat8(g2[0], g2[1]);
+      rq[s] = buf_load8(rq_, cq[s]);
+      rk[s] = buf_load8(rk_, cq[s]);
+      rg[s] = buf_load8(rg_, cg[s]);
     }
     rbeta = buf_load1(rb_, (unsigned)(i_row * p.HV * 2));
   };
@@ -249,15 +244,15 @@ __global__ __launch_bounds__(256) void factors_kernel(WyArgs a) {
           lo[e] = to_f32(rg[s][e]) * kLog2e;
           hi[e] = to_f32(rg[s][e + 4]) * kLog2e;
         }
-        *reinterpret_cast<f32x4*>(sFirst + w * KT + 32 * s + 4 * lq) = lo;
-        *reinterpret_cast<f32x4*>(sFirst + w * KT + 32 * s + 16 + 4 * lq) = hi;
+        *reinterpret_cast<f32x4*>(sFirst + w * KT + 32 * s + 8 * lq) = lo;
+        *reinterpret_cast<f32x4*>(sFirst + w * KT + 32 * s + 8 * lq + 4) = hi;
       }
     }
     if (lr == 15) {  // block sum minus the first token
 #pragma unroll
       for (int s = 0; s < NKS; ++s) {
-        *reinterpret_cast<f32x4*>(sD15 + w * KT + 32 * s + 4 * lq) = f32x4{d[s][0], d[s][1], d[s][2], d[s][3]};
-        *reinterpret_cast<f32x4*>(sD15 + w * KT + 32 * s + 16 + 4 * lq) = f32x4{d[s][4], d[s][5], d[s][6], d[s][7]};
+        *reinterpret_cast<f32x4*>(sD15 + w * KT + 32 * s + 8 * lq) = f32x4{d[s][0], d[s][1], d[s][2], d[s][3]};
+        *reinterpret_cast<f32x4*>(sD15 + w * KT + 32 * s + 8 * lq + 4) = f32x4{d[s][4], d[s][5], d[s][6], d[s][7]};
       }
     }
     lds_barrier();
@@ -292,9 +287,21 @@ __global__ __launch_bounds__(256) void factors_kernel(WyArgs a) {
     for (int J = 0; J < 3; ++J) aK[J] = aQ[J] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < NKS; ++s) {
-      const int cA = 32 * s + 4 * lq, cB = cA + 16;  // channels of elements 0..3 and 4..7
+      const int cA = 32 * s + 8 * lq, cB = cA + 4;  // channels of elements 0..3 and 4..7
       const f32x4 e0 = load4f(sE + w * KT + cA), e1 = load4f(sE + w * KT + cB);
       const f32x4 f0 = load4f(sF + w * KT + cA), f1 = load4f(sF + w * KT + cB);
+      // column-factor constants of this step for the pairs (I, w), I > w, read up front
+      f32x4 fo[3][2];
+#pragma unroll
+      for (int I = 1; I < 4; ++I) {
+        if (I > w) {
+          const int pi = pair_index(I, w);
+          fo[I - 1][0] = load4f(sFo + pi * KT + cA);
+          fo[I - 1][1] = load4f(sFo + pi * KT + cB);
+        } else {
+          fo[I - 1][0] = fo[I - 1][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+      }
       float kc[8];
       bf16x8 KC, QG, KG;
 #pragma unroll
@@ -310,8 +317,7 @@ __global__ __launch_bounds__(256) void factors_kernel(WyArgs a) {
         KC[e] = static_cast<bf16>(kc[e]);
         QG[e] = static_cast<bf16>(qr * E);
         KG[e] = static_cast<bf16>(kr * E);
-        const int c = (e < 4 ? cA : cB) + (e & 3);
-        tKdT[c * PC + perm32(i_row)] = static_cast<bf16>(kc[e] * F);
+        tKdT[(cA + e) * PC + perm32(i_row)] = static_cast<bf16>(kc[e] * F);
       }
       const int qk_off = (i_row * (KT / 8) + swz<KT / 8>(i_row, 4 * s + lq)) * 16;
       *reinterpret_cast<bf16x8*>(blk + W::qg + qk_off) = QG;
@@ -322,10 +328,9 @@ __global__ __launch_bounds__(256) void factors_kernel(WyArgs a) {
       for (int I = 1; I < 4; ++I) {
         if (I > w) {
           const int pi = pair_index(I, w);
-          const f32x4 o0 = load4f(sFo + pi * KT + cA), o1 = load4f(sFo + pi * KT + cB);
           bf16x8 kco;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) kco[e] = static_cast<bf16>(kc[e] * (e < 4 ? o0[e] : o1[e - 4]));
+          for (int e = 0; e < 8; ++e) kco[e] = static_cast<bf16>(kc[e] * fo[I - 1][e >> 2][e & 3]);
           *reinterpret_cast<bf16x8*>(tKCo + (pi * 16 + lr) * PK + 32 * s + 8 * lq) = kco;
         }
       }
@@ -454,11 +459,11 @@ __global__ __launch_bounds__(256) void factors_kernel(WyArgs a) {
       *reinterpret_cast<bf16x8*>(blk + W::t + (i * 8 + swz<8>(i, c8)) * 16) = cat8(lo, hi);
     }
 #pragma unroll
-    for (int rep = 0; rep < KT / 32; ++rep) {
-      const int task = tid + 256 * rep, c = task >> 3, c8 = task & 7;
-      *reinterpret_cast<bf16x8*>(blk + W::kdt + (c * 8 + swz<8>(c, c8)) * 16) = load8(tKdT + c * PC + 8 * c8);
+    for (int rep = 0; rep < KT / 32; ++rep) {  // row rho holds channel perm32(rho)
+      const int task = tid + 256 * rep, rho = task >> 3, c8 = task & 7;
+      *reinterpret_cast<bf16x8*>(blk + W::kdt + (rho * 8 + swz<8>(rho, c8)) * 16) = load8(tKdT + perm32(rho) * PC + 8 * c8);
     }
-    if (tid < KT / 4) *reinterpret_cast<f32x4*>(blk + W::gam + tid * 16) = load4f(sGam + 4 * tid);
+    if (tid < KT / 4) *reinterpret_cast<f32x4*>(blk + W::gam + tid * 16) = load4f(sGam + perm32(4 * tid));
     lds_barrier();  // the next item's scan writes over T
   }
 }
@@ -495,8 +500,9 @@ __device__ __forceinline__ void wait_vmem() {
 
 // One workgroup per (b, hv, 16*NW-column V tile): NW compute waves and two DMA waves.
 // Compute wave wv owns V columns v0 + 16wv + lr and the whole K x 16 state slab in
-// accumulator layout (S[ct]: rows 16ct + 4lq..+3); the DMA waves stream the next chunk's
-// factors into the other LDS buffer, so the compute waves never wait on memory issue.
+// accumulator layout (S[ct]: state rows 16ct + 4lq..+3, row rho holding channel
+// perm32(rho)); the DMA waves stream the next chunk's factors into the other LDS buffer, so
+// the compute waves never wait on memory issue.
 
 template <int KT, int NW>
 __global__ __launch_bounds__(64 * (NW + kDmaWaves)) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -625,7 +631,7 @@ void state_kernel(WyArgs a) {
     for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int c = 16 * ct + 4 * lq + r;
+        const int c = perm32(16 * ct + 4 * lq + r);  // state row rho holds channel perm32(rho)
         S[ct][r] = (s0 && vok && c < K) ? s0[(size_t)c * V + vc] : 0.f;
       }
   }
@@ -742,7 +748,7 @@ void state_kernel(WyArgs a) {
     for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int c = 16 * ct + 4 * lq + r;
+        const int c = perm32(16 * ct + 4 * lq + r);
         if (vok && c < K) sT[(size_t)c * V + vc] = S[ct][r];
       }
   }
