@@ -39,6 +39,10 @@ namespace wy {
 
 constexpr int kC = 64;
 
+// T and Aq are lower block-triangular, so a row of tokens 0..31 keeps only its first 32-token
+// step (4 chunks of 16 bytes) and a row of tokens 32..63 both steps (8 chunks): 6 KB a tile.
+constexpr int kTri = (32 * 4 + 32 * 8) * 16;
+
 // One chunk's factors in the workspace (bytes; every tile 16-byte aligned). Rounded up to
 // whole kilobytes so the state pass streams it in 1 KB DMA rounds.
 template <int KT>
@@ -46,9 +50,9 @@ struct Blk {
   static constexpr int qg = 0;                  // [64][KT] bf16 Q*Gam
   static constexpr int kg = qg + kC * KT * 2;   // [64][KT] bf16 K*Gam
   static constexpr int kdt = kg + kC * KT * 2;  // [KT][64] bf16 (K*Gam_C/Gam)^T, rows and tokens permuted
-  static constexpr int t = kdt + KT * kC * 2;   // [64][64] bf16 T, column order permuted
-  static constexpr int aq = t + kC * kC * 2;    // [64][64] bf16 Aq, column order permuted
-  static constexpr int gam = aq + kC * kC * 2;  // [KT] fp32 Gam_C, rows permuted
+  static constexpr int t = kdt + KT * kC * 2;   // T, lower 32-token steps only (tri_off), columns permuted
+  static constexpr int aq = t + kTri;           // Aq, the same layout
+  static constexpr int gam = aq + kTri;         // [KT] fp32 Gam_C, rows permuted
   static constexpr int beta = gam + KT * 4;     // [64] fp32 beta
   static constexpr int used = beta + kC * 4;
   static constexpr int bytes = (used + 1023) / 1024 * 1024;
@@ -114,6 +118,11 @@ __device__ __forceinline__ void buf_store1(bf16 x, __amdgpu_buffer_rsrc_t r, uns
 // 16-byte slots of a 256-byte LDS bank window.
 template <int R>
 __device__ __forceinline__ int swz(int row, int c) { return c ^ ((row / (16 / R)) & (R - 1)); }
+
+// Byte offset of (row, logical 16-byte chunk c) in a T / Aq tile (c < 4 for rows < 32).
+__device__ __forceinline__ int tri_off(int row, int c) {
+  return row < 32 ? (row * 4 + swz<4>(row, c)) * 16 : (32 * 4 + (row - 32) * 8 + swz<8>(row, c)) * 16;
+}
 
 struct WyArgs {
   PrefillArgs p;
@@ -377,7 +386,8 @@ __global__ __launch_bounds__(256) void factors_kernel(WyArgs a) {
       }
 #pragma unroll
       for (int m = 0; m < 2; ++m)
-        *reinterpret_cast<bf16x8*>(blk + W::aq + (i_row * 8 + swz<8>(i_row, 4 * m + lq)) * 16) = cat8(qv[2 * m], qv[2 * m + 1]);
+        if (m == 0 || w >= 2)  // rows of tokens 0..31 keep only the first 32-token step
+          *reinterpret_cast<bf16x8*>(blk + W::aq + tri_off(i_row, 4 * m + lq)) = cat8(qv[2 * m], qv[2 * m + 1]);
     }
     lds_barrier();
 
@@ -449,14 +459,17 @@ __global__ __launch_bounds__(256) void factors_kernel(WyArgs a) {
     }
     lds_barrier();
 
-    // ---------------- copy-out: T (upper blocks written as zeros), (K*Gam_C/Gam)^T, Gam_C
+    // ---------------- copy-out: T (zero blocks above the diagonal inside the kept steps),
+    // (K*Gam_C/Gam)^T, Gam_C
 #pragma unroll
     for (int rep = 0; rep < 2; ++rep) {
       const int task = tid + 256 * rep, i = task >> 3, c8 = task & 7;
       const int m = c8 >> 2, q = c8 & 3, I = i >> 4;
-      const bf16x4 lo = (2 * m <= I) ? load4(tT + i * PC + 32 * m + 4 * q) : bf16x4{};
-      const bf16x4 hi = (2 * m + 1 <= I) ? load4(tT + i * PC + 32 * m + 16 + 4 * q) : bf16x4{};
-      *reinterpret_cast<bf16x8*>(blk + W::t + (i * 8 + swz<8>(i, c8)) * 16) = cat8(lo, hi);
+      if (i >= 32 || m == 0) {
+        const bf16x4 lo = (2 * m <= I) ? load4(tT + i * PC + 32 * m + 4 * q) : bf16x4{};
+        const bf16x4 hi = (2 * m + 1 <= I) ? load4(tT + i * PC + 32 * m + 16 + 4 * q) : bf16x4{};
+        *reinterpret_cast<bf16x8*>(blk + W::t + tri_off(i, c8)) = cat8(lo, hi);
+      }
     }
 #pragma unroll
     for (int rep = 0; rep < KT / 32; ++rep) {  // row rho holds channel perm32(rho)
@@ -642,8 +655,11 @@ void state_kernel(WyArgs a) {
       const int row = 16 * J + lr;
       return load8(bk + tile + (row * RQ + swz<RQ>(row, 4 * m + lq)) * 16);
     };
-    auto frag64 = [&](int tile, int row, int m) {  // rows of T, Aq, (K*Gam_C/Gam)^T
+    auto frag64 = [&](int tile, int row, int m) {  // rows of (K*Gam_C/Gam)^T
       return load8(bk + tile + (row * 8 + swz<8>(row, 4 * m + lq)) * 16);
+    };
+    auto frag_tri = [&](int tile, int row, int m) {  // rows of T, Aq
+      return load8(bk + tile + tri_off(row, 4 * m + lq));
     };
     // X = (K*Gam) S and P = (Q*Gam) S: A fragments double-buffered one k step ahead
     f32x4 X[4], P[4];
@@ -670,8 +686,8 @@ void state_kernel(WyArgs a) {
         for (int I = 0, f = 0; I < 4; ++I)
 #pragma unroll
           for (int mm = 0; mm <= I / 2; ++mm, ++f) {
-            ft[f] = frag64(W::t, 16 * I + lr, mm);
-            fa[f] = frag64(W::aq, 16 * I + lr, mm);
+            ft[f] = frag_tri(W::t, 16 * I + lr, mm);
+            fa[f] = frag_tri(W::aq, 16 * I + lr, mm);
           }
       }
       const bf16x8 sb = cat8(cvt4(S[2 * m]), cvt4(S[2 * m + 1]));
