@@ -71,17 +71,21 @@ def source_hash():
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per prefill launch from the committed rocprofv3 --pmc summary, if the
-    kernel source has not changed since the counters were taken; else None."""
+def counter_record():
+    """The committed rocprofv3 --pmc record for the prefill kernels, if the kernel source has
+    not changed since the counters were taken; else None."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("source_sha256_16") != source_hash():
-        return None
-    return rec.get("bytes_per_launch")
+    return rec if rec.get("source_sha256_16") == source_hash() else None
+
+
+def measured_traffic():
+    """HBM bytes per prefill launch from the counter record, or None."""
+    rec = counter_record()
+    return rec.get("bytes_per_launch") if rec else None
 
 
 def time_launches(fn, steps, warmup, torch):
@@ -223,6 +227,15 @@ def main():
         "mfma": {"algorithmic_tflops": tflops, "peak_tflops": MFMA_BF16_PEAK_TFS,
                  "frac": tflops / MFMA_BF16_PEAK_TFS, "algorithmic_flops_per_launch": flops},
     }
+    rec = counter_record()
+    if rec and "issued_bf16_flops_per_launch" in rec:
+        # issued MFMA work (full tiles, V-tile duplication) from the counter record, priced at
+        # this run's call time; and the counters' own MFMA-busy fraction
+        issued = rec["issued_bf16_flops_per_launch"]
+        result["mfma"].update({"issued_tflops_counters": issued / (avg_ms * 1e-3) / 1e12,
+                               "issued_frac_counters": issued / (avg_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS,
+                               "issued_bf16_flops_per_launch": issued,
+                               "mfma_busy_frac_counters": rec.get("mfma_busy_frac")})
 
     # ---------------- decode workload
     if not args.no_decode:
