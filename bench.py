@@ -36,6 +36,8 @@ METRIC = "KDA prefill tokens/s + MFMA util (H=16,K=V=128,T=8192); decode state H
 PREFILL_KERNELS = ["kda::wy::factors_kernel<128>", "kda::wy::state_kernel<128, 2>"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_traffic.json")
 MEASURED_SOURCES = ["kda_chunk_wy.hip", "kda_device.h"]
+PREFILL_WORKLOAD = "prefill-B4-T8192-H16-K128"
+DECODE_WORKLOAD = "decode-B256-H16-K128-64steps"
 
 
 def log(msg):
@@ -129,9 +131,9 @@ def cpu_baseline(tokens):
     """The fp64 oracle on the first `tokens` tokens of the prefill workload (all batches and
     heads), single-threaded, on this host."""
     from oracle import recurrent
-    from synth import config_inputs
+    from synth import workload_inputs
 
-    inp = config_inputs(2)
+    inp = workload_inputs(PREFILL_WORKLOAD)
     sl = {k: (v[:, :tokens] if k in ("q", "k", "v", "g", "beta") else v) for k, v in inp.items()}
     try:
         from threadpoolctl import threadpool_limits
@@ -168,16 +170,16 @@ def main():
     import torch
 
     import gated_delta_rule_67_amd as kda
-    from synth import CONFIGS, config_inputs
+    from synth import WORKLOADS, workload_inputs
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
     # ---------------- prefill workload
-    c = CONFIGS[2]
-    log(f"bench: generating prefill workload {c['name']}")
-    inp = config_inputs(2)
+    c = WORKLOADS[PREFILL_WORKLOAD]
+    log(f"bench: generating prefill workload {PREFILL_WORKLOAD}")
+    inp = workload_inputs(PREFILL_WORKLOAD)
     d = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
     del inp
 
@@ -216,7 +218,7 @@ def main():
         "config": {"workload": "KDA chunked prefill B=4 T=8192 H=HV=16 K=V=128 bf16 in, fp32 state, "
                                "chunk 64, zero initial state",
                    "B": c["B"], "T": c["T"], "H": c["H"], "HV": c["HV"], "K": c["K"], "V": c["V"],
-                   "chunk_size": c["chunk"], "seed": 1236},
+                   "chunk_size": c["chunk"], "seed": c["seed"]},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": " + ".join(PREFILL_KERNELS) + " (one kda_chunk_fwd call)",
@@ -239,9 +241,9 @@ def main():
 
     # ---------------- decode workload
     if not args.no_decode:
-        c3 = CONFIGS[3]
-        log(f"bench: generating decode workload {c3['name']}")
-        dinp = config_inputs(3)
+        c3 = WORKLOADS[DECODE_WORKLOAD]
+        log(f"bench: generating decode workload {DECODE_WORKLOAD}")
+        dinp = workload_inputs(DECODE_WORKLOAD)
         dd = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in dinp.items()}
         del dinp
         state = dd["state"].clone()

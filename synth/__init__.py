@@ -4,6 +4,6 @@ This package draws random tensors and nothing else: it holds none of the KDA
 arithmetic, and neither the oracle nor the HIP path lives here.
 """
 
-from .inputs import CONFIGS, decode_inputs, prefill_inputs, config_inputs
+from .inputs import WORKLOADS, decode_inputs, prefill_inputs, workload_inputs
 
-__all__ = ["CONFIGS", "decode_inputs", "prefill_inputs", "config_inputs"]
+__all__ = ["WORKLOADS", "decode_inputs", "prefill_inputs", "workload_inputs"]

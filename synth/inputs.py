@@ -21,19 +21,24 @@ import math
 import torch
 import torch.nn.functional as F
 
-# The five workloads. 'prefill' entries run kda_chunk_fwd; 'decode' runs
-# kda_recurrent_step `steps` times on one in-place state.
-CONFIGS = {
-    0: dict(name="tiny-fp32", kind="prefill", B=2, T=16, H=2, HV=4, K=8, V=8,
-            dtype="fp32", chunk=8, init_state=False),
-    1: dict(name="gva-bf16", kind="prefill", B=2, T=512, H=4, HV=8, K=64, V=64,
-            dtype="bf16", chunk=64, init_state=True),
-    2: dict(name="prefill-B4-T8192-H16-K128", kind="prefill", B=4, T=8192, H=16, HV=16,
-            K=128, V=128, dtype="bf16", chunk=64, init_state=False),
-    3: dict(name="decode-B256-H16-K128-64steps", kind="decode", steps=64, B=256, H=16,
-            HV=16, K=128, V=128, dtype="bf16", init_state=True),
-    4: dict(name="prefill-B1-T32768-H96-K128", kind="prefill", B=1, T=32768, H=96, HV=96,
-            K=128, V=128, dtype="bf16", chunk=64, init_state=True),
+# The five workloads, by name. 'prefill' entries run kda_chunk_fwd; 'decode' runs
+# kda_recurrent_step `steps` times on one in-place state. Each has its own seed.
+WORKLOADS = {
+    "tiny-B2-T16-H2-HV4-K8-fp32": dict(
+        kind="prefill", B=2, T=16, H=2, HV=4, K=8, V=8, dtype="fp32", chunk=8,
+        init_state=False, seed=1234),
+    "gva-B2-T512-H4-HV8-K64-bf16": dict(
+        kind="prefill", B=2, T=512, H=4, HV=8, K=64, V=64, dtype="bf16", chunk=64,
+        init_state=True, seed=1235),
+    "prefill-B4-T8192-H16-K128": dict(
+        kind="prefill", B=4, T=8192, H=16, HV=16, K=128, V=128, dtype="bf16", chunk=64,
+        init_state=False, seed=1236),
+    "decode-B256-H16-K128-64steps": dict(
+        kind="decode", steps=64, B=256, H=16, HV=16, K=128, V=128, dtype="bf16",
+        init_state=True, seed=1237),
+    "prefill-B1-T32768-H96-K128": dict(
+        kind="prefill", B=1, T=32768, H=96, HV=96, K=128, V=128, dtype="bf16", chunk=64,
+        init_state=True, seed=1238),
 }
 
 DTYPES = {"fp32": torch.float32, "bf16": torch.bfloat16}
@@ -104,11 +109,11 @@ def decode_inputs(steps, B, H, HV, K, V, dtype="bf16", init_state=True, seed=0,
     return dict(q=q, k=k, v=v, g=g, beta=b, state=s0, scale=1.0 / math.sqrt(K))
 
 
-def config_inputs(index, **overrides):
-    """Inputs for workload `index` with its standard seed (1234 + index)."""
-    c = dict(CONFIGS[index])
+def workload_inputs(name, **overrides):
+    """Inputs for the named workload with its own seed."""
+    c = dict(WORKLOADS[name])
     c.update(overrides)
-    seed = c.pop("seed", 1234 + index)
+    seed = c.pop("seed")
     if c["kind"] == "decode":
         return decode_inputs(c["steps"], c["B"], c["H"], c["HV"], c["K"], c["V"],
                              c["dtype"], c["init_state"], seed)

@@ -8,7 +8,7 @@ import torch
 
 import gated_delta_rule_67_amd as kda
 from oracle import decode_step
-from synth import CONFIGS, decode_inputs
+from synth import WORKLOADS, decode_inputs
 from tests.helpers import assert_parity, log, to64
 
 pytestmark = pytest.mark.gpu
@@ -62,11 +62,11 @@ def test_decode_stress_gates(gate, beta):
 
 
 def test_decode_full_size_sampled_heads():
-    c = CONFIGS[3]
+    c = WORKLOADS["decode-B256-H16-K128-64steps"]
     log("decode full size B=256 H=16 K=V=128, 64 steps, sampled heads")
     rng = np.random.default_rng(0)
     sample = (np.sort(rng.choice(c["B"], 6, replace=False)), np.sort(rng.choice(c["HV"], 3, replace=False)))
-    _run(c["steps"], c["B"], c["H"], c["HV"], c["K"], c["V"], c["dtype"], seed=1234 + 3, sample=sample)
+    _run(c["steps"], c["B"], c["H"], c["HV"], c["K"], c["V"], c["dtype"], seed=c["seed"], sample=sample)
 
 
 def test_decode_leaves_other_heads_alone_and_writes_all_outputs():

@@ -14,7 +14,7 @@ import torch
 
 import gated_delta_rule_67_amd as kda
 from oracle import brute, recurrent
-from synth import CONFIGS, config_inputs, prefill_inputs
+from synth import WORKLOADS, prefill_inputs, workload_inputs
 from tests.helpers import assert_parity, gpu, head_slice, log, to64
 
 pytestmark = pytest.mark.gpu
@@ -37,9 +37,9 @@ def _check_full(inp, dtype, chunk=64, what=""):
     assert_parity(to64(s), s_ref, DT[dtype], f"{what} state")
 
 
-def test_config0_tiny_fp32():
-    log("prefill config 0 (B2 T16 H2 HV4 K=V=8 fp32, chunk 8)")
-    inp = config_inputs(0)
+def test_tiny_fp32():
+    log("prefill tiny-B2-T16-H2-HV4-K8-fp32 (chunk 8)")
+    inp = workload_inputs("tiny-B2-T16-H2-HV4-K8-fp32")
     o, s = _gpu_fwd(inp, chunk=8)
     o_ref, s_ref = recurrent(**inp)
     assert_parity(to64(o), o_ref, torch.float32, "o")
@@ -48,9 +48,9 @@ def test_config0_tiny_fp32():
     assert_parity(to64(o), o_b, torch.float32, "o vs brute force")
 
 
-def test_config1_gva_bf16():
-    log("prefill config 1 (B2 T512 H4 HV8 K=V=64 bf16, S0)")
-    _check_full(config_inputs(1), "bf16", what="config1")
+def test_gva_bf16():
+    log("prefill gva-B2-T512-H4-HV8-K64-bf16 (S0)")
+    _check_full(workload_inputs("gva-B2-T512-H4-HV8-K64-bf16"), "bf16", what="gva")
 
 
 @pytest.mark.parametrize("shape", [
@@ -199,13 +199,13 @@ def test_error_path_raises():
         kda.kda_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], chunk_size=64)
 
 
-@pytest.mark.parametrize("index", [2, 4])
-def test_full_size_sampled_heads(index):
-    c = CONFIGS[index]
-    log(f"prefill full size config {index}: {c['name']}")
-    inp = config_inputs(index)
+@pytest.mark.parametrize("name", ["prefill-B4-T8192-H16-K128", "prefill-B1-T32768-H96-K128"])
+def test_full_size_sampled_heads(name):
+    c = WORKLOADS[name]
+    log(f"prefill full size {name}")
+    inp = workload_inputs(name)
     o, s = _gpu_fwd(inp)
-    rng = np.random.default_rng(index)
+    rng = np.random.default_rng(c["seed"])
     for _ in range(2):
         b, hv = int(rng.integers(c["B"])), int(rng.integers(c["HV"]))
         log(f"  oracle for head b={b} hv={hv}")
