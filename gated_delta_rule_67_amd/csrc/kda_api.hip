@@ -64,7 +64,8 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const void* g, co
                   size_t workspace_bytes, void* stream) {
   if (!q || !k || !v || !g || !beta || !o) return KDA_ERR_INVALID;
   if (!positive(T)) return KDA_ERR_INVALID;
-  if (chunk_size != 8 && chunk_size != 16 && chunk_size != 32 && chunk_size != 64)
+  if (chunk_size != 8 && chunk_size != 16 && chunk_size != 32 && chunk_size != 64 &&
+      chunk_size != 128)
     return KDA_ERR_INVALID;
   if (T % chunk_size != 0) return KDA_ERR_INVALID;
   const int rc = check_common(B, H, HV, K, V, scale, dtype);

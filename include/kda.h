@@ -62,7 +62,7 @@ typedef enum { KDA_DTYPE_F32 = 0, KDA_DTYPE_BF16 = 1 } kda_dtype;
  *                                 initial_state (each state is read before it is written)
  *   o              [B, T, HV, V]  dtype out; must not overlap any input
  *   scale          finite; multiplies q
- *   chunk_size     8, 16, 32 or 64 and T % chunk_size == 0 (same page, key-constraints
+ *   chunk_size     8, 16, 32, 64 or 128 and T % chunk_size == 0 (same page, key-constraints
  *                  table, chunk_size row). The result does not depend on it beyond
  *                  rounding: kernels tile time by 64 tokens and mask a partial last tile.
  *   workspace      NULL, or device memory of at least kda_chunk_fwd_workspace_size()

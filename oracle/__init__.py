@@ -17,6 +17,9 @@ Three independent CPU formulations, all in float64 numpy:
   triangular system, triangular solve, state passed between chunks).
 * ``brute`` (O3): each token written as an affine map of the state, composed
   explicitly with K x K matrices. Only for tiny shapes.
+* ``transforms``: the optional in-operator input transforms (q/k L2
+  normalisation, beta sigmoid) that ``recurrent`` / ``decode_step`` apply on
+  request.
 
 Pins (tests/test_oracle_*.py) tie these to each other and to closed forms, a
 hand-worked example, invariants and brute force. No function here is
@@ -26,6 +29,7 @@ hand-worked example, invariants and brute force. No function here is
 from .recurrent import decode_step, recurrent
 from .chunked import chunked, forward_substitution_inverse
 from .brute import brute
+from .transforms import l2_normalize, sigmoid
 
 __all__ = [
     "decode_step",
@@ -33,4 +37,6 @@ __all__ = [
     "chunked",
     "forward_substitution_inverse",
     "brute",
+    "l2_normalize",
+    "sigmoid",
 ]

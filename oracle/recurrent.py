@@ -25,6 +25,8 @@ no transform); the initial state defaults to zeros.
 
 import numpy as np
 
+from .transforms import l2_normalize, sigmoid
+
 
 def _f64(x):
     """Copy any array-like (numpy, or a CPU torch tensor of any float dtype) to float64 numpy."""
@@ -42,7 +44,7 @@ def _expand_heads(x, hv):
     return np.repeat(x, hv // h, axis=1)
 
 
-def decode_step(q, k, v, g, beta, state, scale):
+def decode_step(q, k, v, g, beta, state, scale, qk_l2norm=False, beta_sigmoid=False):
     """One token of the recurrence for every (b, hv).
 
     Shapes: q, k [B, H, K]; v [B, HV, V]; g [B, HV, K]; beta [B, HV];
@@ -51,8 +53,14 @@ def decode_step(q, k, v, g, beta, state, scale):
 
     This is the single step the K3 README's roadmap row L6 (recurrent decode
     against a [B, HV, K, V] state cache) repeats per generated token.
+    ``qk_l2norm`` / ``beta_sigmoid`` first apply the input transforms of
+    ``oracle.transforms`` to q, k / beta.
     """
     q, k, v, g, beta, s = (_f64(a) for a in (q, k, v, g, beta, state))
+    if qk_l2norm:
+        q, k = l2_normalize(q), l2_normalize(k)
+    if beta_sigmoid:
+        beta = sigmoid(beta)
     hv = v.shape[1]
     qh = _expand_heads(q, hv) * float(scale)
     kh = _expand_heads(k, hv)
@@ -67,12 +75,13 @@ def decode_step(q, k, v, g, beta, state, scale):
     return o, s
 
 
-def recurrent(q, k, v, g, beta, scale, initial_state=None):
+def recurrent(q, k, v, g, beta, scale, initial_state=None, qk_l2norm=False, beta_sigmoid=False):
     """The whole sequence, token by token.
 
     Shapes: q, k [B, T, H, K]; v [B, T, HV, V]; g [B, T, HV, K]; beta [B, T, HV];
     initial_state [B, HV, K, V] or None (zeros). Returns ``(o [B, T, HV, V],
-    final_state [B, HV, K, V])`` in float64.
+    final_state [B, HV, K, V])`` in float64. ``qk_l2norm`` / ``beta_sigmoid`` as in
+    ``decode_step``.
     """
     q, k, v, g, beta = (_f64(a) for a in (q, k, v, g, beta))
     b, t_len, _, kd = q.shape
@@ -83,5 +92,6 @@ def recurrent(q, k, v, g, beta, scale, initial_state=None):
         s = _f64(initial_state)
     o = np.zeros((b, t_len, hv, vd))
     for t in range(t_len):
-        o[:, t], s = decode_step(q[:, t], k[:, t], v[:, t], g[:, t], beta[:, t], s, scale)
+        o[:, t], s = decode_step(q[:, t], k[:, t], v[:, t], g[:, t], beta[:, t], s, scale,
+                                 qk_l2norm, beta_sigmoid)
     return o, s

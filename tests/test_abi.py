@@ -85,7 +85,7 @@ def _chunk(lib, **kw):
     (dict(HV=3), kda.KDA_ERR_INVALID),            # HV % H != 0
     (dict(T=72), kda.KDA_ERR_INVALID),            # T % chunk != 0
     (dict(chunk=48), kda.KDA_ERR_INVALID),        # not a supported chunk size
-    (dict(chunk=128, T=128), kda.KDA_ERR_INVALID),
+    (dict(chunk=256, T=256), kda.KDA_ERR_INVALID),       # larger than the pages' 128
     (dict(scale=float("nan")), kda.KDA_ERR_INVALID),
     (dict(scale=float("inf")), kda.KDA_ERR_INVALID),
     (dict(dtype=2), kda.KDA_ERR_INVALID),         # no fp16

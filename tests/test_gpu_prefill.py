@@ -91,10 +91,10 @@ def test_zero_input_leaves_state_unchanged():
 
 
 def test_chunk_size_does_not_change_the_result():
-    log("prefill chunk sizes 8/16/32/64")
-    inp = prefill_inputs(1, 128, 2, 2, 64, 64, "bf16", True, 9)
+    log("prefill chunk sizes 8/16/32/64/128")
+    inp = prefill_inputs(1, 256, 2, 2, 64, 64, "bf16", True, 9)
     o64, s64 = _gpu_fwd(inp, 64)
-    for c in (8, 16, 32):
+    for c in (8, 16, 32, 128):
         o, s = _gpu_fwd(inp, c)
         assert torch.equal(o, o64) and torch.equal(s, s64)
 
