@@ -9,9 +9,13 @@ if ``libkda.so`` is missing or a call fails, an error is raised.
 Entry points (same names as the C ABI):
 
 * ``kda_chunk_fwd(q, k, v, g, beta, scale=None, initial_state=None,
-  output_final_state=True, chunk_size=64) -> (o, final_state)``
-* ``kda_recurrent_step(q, k, v, g, beta, state, scale=None) -> o`` (updates
-  ``state`` in place)
+  output_final_state=True, chunk_size=64, qk_l2norm=False, beta_sigmoid=False)
+  -> (o, final_state)``
+* ``kda_recurrent_step(q, k, v, g, beta, state, scale=None, qk_l2norm=False,
+  beta_sigmoid=False) -> o`` (updates ``state`` in place)
+
+``qk_l2norm`` / ``beta_sigmoid`` ask the kernels to L2-normalise q and k and to
+apply the sigmoid to beta (``kda_chunk_fwd_ex`` / ``kda_recurrent_step_ex``).
 """
 
 import ctypes
@@ -21,9 +25,11 @@ import os
 import torch
 
 __all__ = ["kda_chunk_fwd", "kda_recurrent_step", "library", "library_path", "status_string",
-           "KDA_OK", "KDA_ERR_INVALID", "KDA_ERR_UNSUPPORTED", "KDA_ERR_HIP"]
+           "KDA_OK", "KDA_ERR_INVALID", "KDA_ERR_UNSUPPORTED", "KDA_ERR_HIP",
+           "KDA_FLAG_QK_L2NORM", "KDA_FLAG_BETA_SIGMOID"]
 
 KDA_OK, KDA_ERR_INVALID, KDA_ERR_UNSUPPORTED, KDA_ERR_HIP = 0, -1, -2, -3
+KDA_FLAG_QK_L2NORM, KDA_FLAG_BETA_SIGMOID = 1, 2
 _DTYPE = {torch.float32: 0, torch.bfloat16: 1}
 
 library_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
@@ -41,10 +47,14 @@ def library():
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.kda_chunk_fwd.argtypes = [vp] * 8 + [i] * 6 + [f, i, i, vp, sz, vp]
     lib.kda_chunk_fwd.restype = i
+    lib.kda_chunk_fwd_ex.argtypes = [vp] * 8 + [i] * 6 + [f, i, i, vp, sz, ctypes.c_uint, vp]
+    lib.kda_chunk_fwd_ex.restype = i
     lib.kda_chunk_fwd_workspace_size.argtypes = [i] * 8
     lib.kda_chunk_fwd_workspace_size.restype = sz
     lib.kda_recurrent_step.argtypes = [vp] * 7 + [i] * 5 + [f, i, vp]
     lib.kda_recurrent_step.restype = i
+    lib.kda_recurrent_step_ex.argtypes = [vp] * 7 + [i] * 5 + [f, i, ctypes.c_uint, vp]
+    lib.kda_recurrent_step_ex.restype = i
     lib.kda_status_string.argtypes = [i]
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_version.argtypes = []
@@ -78,10 +88,15 @@ def _check_tensors(named, dtype, device):
         _require(t.is_contiguous(), f"{name} must be contiguous")
 
 
+def _flags(qk_l2norm, beta_sigmoid):
+    return (KDA_FLAG_QK_L2NORM if qk_l2norm else 0) | (KDA_FLAG_BETA_SIGMOID if beta_sigmoid else 0)
+
+
 def kda_chunk_fwd(q, k, v, g, beta, scale=None, initial_state=None, output_final_state=True,
-                  chunk_size=64):
+                  chunk_size=64, qk_l2norm=False, beta_sigmoid=False):
     """Chunked KDA prefill. q, k [B,T,H,K]; v [B,T,HV,V]; g [B,T,HV,K]; beta [B,T,HV];
-    initial_state [B,HV,K,V] float32 or None. Returns (o [B,T,HV,V], final_state or None)."""
+    initial_state [B,HV,K,V] float32 or None. Returns (o [B,T,HV,V], final_state or None).
+    qk_l2norm / beta_sigmoid: apply those input transforms in the kernels."""
     _require(q.is_cuda, "inputs must be on a GPU")
     dev, dt = q.device, q.dtype
     _require(dt in _DTYPE, f"unsupported dtype {dt}")
@@ -104,17 +119,18 @@ def kda_chunk_fwd(q, k, v, g, beta, scale=None, initial_state=None, output_final
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
     with torch.cuda.device(dev):
         stream = torch.cuda.current_stream(dev).cuda_stream
-        rc = lib.kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
-                               _ptr(final), _ptr(o), B, T, H, HV, K, V, float(scale),
-                               int(chunk_size), _DTYPE[dt], _ptr(ws), ws_bytes,
-                               ctypes.c_void_p(stream))
+        rc = lib.kda_chunk_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                  _ptr(initial_state), _ptr(final), _ptr(o), B, T, H, HV, K, V,
+                                  float(scale), int(chunk_size), _DTYPE[dt], _ptr(ws), ws_bytes,
+                                  _flags(qk_l2norm, beta_sigmoid), ctypes.c_void_p(stream))
     _check(rc)
     return o, final
 
 
-def kda_recurrent_step(q, k, v, g, beta, state, scale=None):
+def kda_recurrent_step(q, k, v, g, beta, state, scale=None, qk_l2norm=False, beta_sigmoid=False):
     """One decode token. q, k [B,H,K] (or [B,1,H,K]); v [B,HV,V]; g [B,HV,K]; beta [B,HV];
-    state [B,HV,K,V] float32, updated in place. Returns o [B,HV,V]."""
+    state [B,HV,K,V] float32, updated in place. Returns o [B,HV,V].
+    qk_l2norm / beta_sigmoid: apply those input transforms in the kernel."""
     _require(q.is_cuda, "inputs must be on a GPU")
     dev, dt = q.device, q.dtype
     _require(dt in _DTYPE, f"unsupported dtype {dt}")
@@ -134,8 +150,9 @@ def kda_recurrent_step(q, k, v, g, beta, state, scale=None):
     o = torch.empty((B, HV, V), dtype=dt, device=dev)
     with torch.cuda.device(dev):
         stream = torch.cuda.current_stream(dev).cuda_stream
-        rc = lib.kda_recurrent_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state),
-                                    _ptr(o), B, H, HV, K, V, float(scale), _DTYPE[dt],
-                                    ctypes.c_void_p(stream))
+        rc = lib.kda_recurrent_step_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                       _ptr(state), _ptr(o), B, H, HV, K, V, float(scale),
+                                       _DTYPE[dt], _flags(qk_l2norm, beta_sigmoid),
+                                       ctypes.c_void_p(stream))
     _check(rc)
     return o

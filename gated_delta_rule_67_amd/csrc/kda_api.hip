@@ -9,10 +9,10 @@
 namespace kda {
 template <typename Tin>
 hipError_t launch_decode(const void*, const void*, const void*, const void*, const void*, float*,
-                         void*, int, int, int, int, int, float, hipStream_t);
+                         void*, int, int, int, int, int, float, unsigned, hipStream_t);
 hipError_t launch_prefill(const void*, const void*, const void*, const void*, const void*,
                           const float*, float*, void*, int, int, int, int, int, int, float, bool,
-                          void*, hipStream_t);
+                          void*, unsigned, hipStream_t);
 size_t wy_workspace_bytes(int B, int T, int HV, int K);
 }  // namespace kda
 
@@ -58,11 +58,13 @@ size_t kda_chunk_fwd_workspace_size(int B, int T, int H, int HV, int K, int V, i
   return kda::wy_workspace_bytes(B, T, HV, K);
 }
 
-int kda_chunk_fwd(const void* q, const void* k, const void* v, const void* g, const void* beta,
-                  const float* initial_state, float* final_state, void* o, int B, int T, int H,
-                  int HV, int K, int V, float scale, int chunk_size, int dtype, void* workspace,
-                  size_t workspace_bytes, void* stream) {
+int kda_chunk_fwd_ex(const void* q, const void* k, const void* v, const void* g,
+                     const void* beta, const float* initial_state, float* final_state, void* o,
+                     int B, int T, int H, int HV, int K, int V, float scale, int chunk_size,
+                     int dtype, void* workspace, size_t workspace_bytes, unsigned flags,
+                     void* stream) {
   if (!q || !k || !v || !g || !beta || !o) return KDA_ERR_INVALID;
+  if (flags & ~(unsigned)(KDA_FLAG_QK_L2NORM | KDA_FLAG_BETA_SIGMOID)) return KDA_ERR_INVALID;
   if (!positive(T)) return KDA_ERR_INVALID;
   if (chunk_size != 8 && chunk_size != 16 && chunk_size != 32 && chunk_size != 64 &&
       chunk_size != 128)
@@ -77,17 +79,29 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const void* g, co
   const size_t need = kda_chunk_fwd_workspace_size(B, T, H, HV, K, V, chunk_size, dtype);
   if (workspace && workspace_bytes < need) return KDA_ERR_INVALID;
   if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0) return KDA_ERR_INVALID;
+  // The input transforms are applied by the factors kernel of the two-kernel path only.
+  if (flags && (need == 0 || !workspace)) return KDA_ERR_UNSUPPORTED;
   const hipError_t e = kda::launch_prefill(q, k, v, g, beta, initial_state, final_state, o, B, T,
                                            H, HV, K, V, scale, dtype == KDA_DTYPE_BF16,
-                                           need ? workspace : nullptr,
+                                           need ? workspace : nullptr, flags,
                                            static_cast<hipStream_t>(stream));
+  if (e == hipErrorNotSupported) return KDA_ERR_UNSUPPORTED;  // flags, unaligned tensors
   return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
-int kda_recurrent_step(const void* q, const void* k, const void* v, const void* g,
-                       const void* beta, float* state, void* o, int B, int H, int HV, int K,
-                       int V, float scale, int dtype, void* stream) {
+int kda_chunk_fwd(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                  const float* initial_state, float* final_state, void* o, int B, int T, int H,
+                  int HV, int K, int V, float scale, int chunk_size, int dtype, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+  return kda_chunk_fwd_ex(q, k, v, g, beta, initial_state, final_state, o, B, T, H, HV, K, V,
+                          scale, chunk_size, dtype, workspace, workspace_bytes, 0u, stream);
+}
+
+int kda_recurrent_step_ex(const void* q, const void* k, const void* v, const void* g,
+                          const void* beta, float* state, void* o, int B, int H, int HV, int K,
+                          int V, float scale, int dtype, unsigned flags, void* stream) {
   if (!q || !k || !v || !g || !beta || !state || !o) return KDA_ERR_INVALID;
+  if (flags & ~(unsigned)(KDA_FLAG_QK_L2NORM | KDA_FLAG_BETA_SIGMOID)) return KDA_ERR_INVALID;
   const int rc = check_common(B, H, HV, K, V, scale, dtype);
   if (rc != KDA_OK) return rc;
   if (V % 4 != 0) return KDA_ERR_UNSUPPORTED;
@@ -96,10 +110,17 @@ int kda_recurrent_step(const void* q, const void* k, const void* v, const void* 
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const hipError_t e = dtype == KDA_DTYPE_BF16
                            ? kda::launch_decode<kda::bf16>(q, k, v, g, beta, state, o, B, H, HV,
-                                                           K, V, scale, s)
+                                                           K, V, scale, flags, s)
                            : kda::launch_decode<float>(q, k, v, g, beta, state, o, B, H, HV, K,
-                                                       V, scale, s);
+                                                       V, scale, flags, s);
   return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+int kda_recurrent_step(const void* q, const void* k, const void* v, const void* g,
+                       const void* beta, float* state, void* o, int B, int H, int HV, int K,
+                       int V, float scale, int dtype, void* stream) {
+  return kda_recurrent_step_ex(q, k, v, g, beta, state, o, B, H, HV, K, V, scale, dtype, 0u,
+                               stream);
 }
 
 }  // extern "C"

@@ -157,8 +157,9 @@ struct LdsA {
 // One workgroup of 4 waves per (b, hv, chunk) item, looping over items with a stride of
 // gridDim.x (the next item's q, k, g are loaded while the current one finishes). Wave w owns
 // the 16-token block w; lane (lr, lq) holds token 16w + lr and, for k step s, channels
-// 32s + 8lq..+7.
-template <int KT>
+// 32s + 8lq..+7. L2N: q and k are L2-normalised here (an instantiation of its own, so the
+// plain path keeps its register budget: two workgroups per CU).
+template <int KT, bool L2N>
 __global__ __launch_bounds__(256) void factors_kernel(WyArgs a) {
   using L = LdsA<KT>;
   using W = Blk<KT>;
@@ -287,6 +288,29 @@ __global__ __launch_bounds__(256) void factors_kernel(WyArgs a) {
     }
     lds_barrier();
 
+    // optional L2 normalisation of q and k: a token row's K channels sit in the 4 lanes
+    // lq = 0..3 of its lr, so two cross-lane sums give the row's squared norms. The squares
+    // are summed on the packed bf16 pairs (products exact in fp32), which keeps the raw
+    // registers as they are for the factor loop below.
+    float inv_q = 1.f, inv_k = 1.f;
+    if constexpr (L2N) {
+      float sq = 0.f, sk = 0.f;
+#pragma unroll
+      for (int s = 0; s < NKS; ++s)
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const bf16x2 q2 = {rq[s][e], rq[s][e + 1]}, k2 = {rk[s][e], rk[s][e + 1]};
+          sq = __builtin_amdgcn_fdot2_f32_bf16(q2, q2, sq, false);
+          sk = __builtin_amdgcn_fdot2_f32_bf16(k2, k2, sk, false);
+        }
+      sq += __shfl_xor(sq, 16);
+      sk += __shfl_xor(sk, 16);
+      sq += __shfl_xor(sq, 32);
+      sk += __shfl_xor(sk, 32);
+      inv_q = rsqrtf(sq + kL2normEps);
+      inv_k = rsqrtf(sk + kL2normEps);
+    }
+
     // ---------------- decay factors; Q*Gam and K*Gam leave straight to the workspace, the
     // diagonal Akk^T / Aq^T tiles (rows: tokens j of block w, columns: tokens i) accumulate
     // on the matrix core while the next k step's factors run on the VALU.
@@ -318,7 +342,7 @@ __global__ __launch_bounds__(256) void factors_kernel(WyArgs a) {
         const float E = e < 4 ? e0[e] : e1[e - 4];
         const float F = e < 4 ? f0[e] : f1[e - 4];
         const float R = fast_exp2(d[s][e]), Cf = fast_exp2(-d[s][e]);
-        const float qv = to_f32(rq[s][e]), kv = to_f32(rk[s][e]);
+        const float qv = to_f32(rq[s][e]) * inv_q, kv = to_f32(rk[s][e]) * inv_k;
         const float qr = qv * R, kr = kv * R;
         kc[e] = kv * Cf;
         QR[s][e] = static_cast<bf16>(qr);
@@ -344,7 +368,7 @@ __global__ __launch_bounds__(256) void factors_kernel(WyArgs a) {
         }
       }
     }
-    const float brow = bits_to_f32(rbeta);
+    const float brow = (p.flags & kFlagBetaSigmoid) ? sigmoid_f32(bits_to_f32(rbeta)) : bits_to_f32(rbeta);
     if (lq == 0) *reinterpret_cast<float*>(blk + W::beta + i_row * 4) = brow;
     // this item's raw inputs are consumed: fetch the next item's
     if (it + (int)gridDim.x < items) prefetch(it + gridDim.x);
@@ -774,7 +798,10 @@ template <int KT, int NW>
 hipError_t launch_cfg(const WyArgs& a, int cus, hipStream_t stream) {
   const int items = a.p.B * a.p.HV * a.NT;
   const int grid_a = items < 2 * cus ? items : 2 * cus;
-  hipLaunchKernelGGL((factors_kernel<KT>), dim3(grid_a), dim3(256), 0, stream, a);
+  if (a.p.flags & kFlagQkL2norm)
+    hipLaunchKernelGGL((factors_kernel<KT, true>), dim3(grid_a), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((factors_kernel<KT, false>), dim3(grid_a), dim3(256), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nvt = (a.p.V + 16 * NW - 1) / (16 * NW);

@@ -8,6 +8,8 @@
 //   u = beta (v - a)                   prediction error against the decayed state
 //   o = b + (scale q . k) u            = S_new^T (scale q), without a second pass
 //   S_new = s + k u^T                  written back in place
+// Optional input transforms (kFlag*): q and k L2-normalised over K, beta through a sigmoid.
+// The reductions run on the raw q and k; their norms and scale are applied to the results.
 //
 // The step is HBM-bound (~1 flop per state byte): one workgroup streams one
 // (b, hv[, V half]) state slab through registers exactly once, with 16-byte
@@ -26,10 +28,10 @@ template <typename Tin, int VSPLIT>
 __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(
     const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
     const Tin* __restrict__ g, const Tin* __restrict__ beta, float* __restrict__ state,
-    Tin* __restrict__ o, int H, int HV, int K, int V, float scale) {
+    Tin* __restrict__ o, int H, int HV, int K, int V, float scale, unsigned flags) {
   __shared__ float s_dec[128], s_k[128], s_q[128], s_v[128], s_u[128];
   __shared__ f32x4 s_pa[kDecodeThreads], s_pb[kDecodeThreads];
-  __shared__ float s_qk;
+  __shared__ float s_qk, s_iq, s_ik;  // q.k (raw), scale/|q|, 1/|k| (norms only when asked)
 
   const int part = blockIdx.x % VSPLIT;
   const int bh = blockIdx.x / VSPLIT;  // b * HV + hv
@@ -47,7 +49,17 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(
 
   float* S = state + (size_t)bh * K * V + v0 + 4 * c4;
 
-  // Issue the whole slab's loads first: they are the critical resource.
+  // The per-head vectors go first, unconditionally (clamped index), so that one wait
+  // covers them while the slab's loads below stay in flight.
+  const size_t qk_off = ((size_t)b * H + h) * K;
+  const size_t g_off = (size_t)bh * K;
+  const int tk = t < K ? t : K - 1;
+  const int tv = t < vw ? t : vw - 1;
+  const Tin xg = g[g_off + tk], xk = k[qk_off + tk], xq = q[qk_off + tk];
+  const Tin xv = v[(size_t)bh * V + v0 + tv];
+  const Tin xb = beta[bh];
+
+  // Then the whole slab: it is the critical resource.
   f32x4 s[kDecodeMaxRows];
 #pragma unroll
   for (int i = 0; i < kDecodeMaxRows; ++i) {
@@ -58,23 +70,34 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(
       s[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  const size_t qk_off = ((size_t)b * H + h) * K;
-  const size_t g_off = (size_t)bh * K;
   if (t < K) {
-    s_dec[t] = fast_exp2(to_f32(g[g_off + t]) * kLog2e);
-    s_k[t] = to_f32(k[qk_off + t]);
-    s_q[t] = to_f32(q[qk_off + t]) * scale;
+    s_dec[t] = fast_exp2(to_f32(xg) * kLog2e);
+    s_k[t] = to_f32(xk);
+    s_q[t] = to_f32(xq);
   }
-  if (t < vw) s_v[t] = to_f32(v[(size_t)bh * V + v0 + t]);
-  const float bt = to_f32(beta[bh]);
+  if (t < vw) s_v[t] = to_f32(xv);
+  const float bt = (flags & kFlagBetaSigmoid) ? sigmoid_f32(to_f32(xb)) : to_f32(xb);
   __syncthreads();
 
-  if (t < 64) {  // (scale q) . k, one wave
-    float p = 0.f;
-    for (int r = t; r < K; r += 64) p += s_q[r] * s_k[r];
+  if (t < 64) {  // q . k and the squared norms, one wave
+    float p = 0.f, nq = 0.f, nk = 0.f;
+    for (int r = t; r < K; r += 64) {
+      p += s_q[r] * s_k[r];
+      nq += s_q[r] * s_q[r];
+      nk += s_k[r] * s_k[r];
+    }
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) p += __shfl_xor(p, off);
-    if (t == 0) s_qk = p;
+    for (int off = 32; off > 0; off >>= 1) {
+      p += __shfl_xor(p, off);
+      nq += __shfl_xor(nq, off);
+      nk += __shfl_xor(nk, off);
+    }
+    if (t == 0) {
+      const bool l2 = flags & kFlagQkL2norm;
+      s_qk = p;
+      s_iq = scale * (l2 ? rsqrtf(nq + kL2normEps) : 1.f);
+      s_ik = l2 ? rsqrtf(nk + kL2normEps) : 1.f;
+    }
   }
 
   f32x4 pa = {0.f, 0.f, 0.f, 0.f}, pb = {0.f, 0.f, 0.f, 0.f};
@@ -100,9 +123,10 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(
       a += s_pa[j * nc + cc][e];
       bq += s_pb[j * nc + cc][e];
     }
-    const float u = bt * (s_v[t] - a);
-    s_u[t] = u;
-    o[(size_t)bh * V + v0 + t] = from_f32<Tin>(bq + s_qk * u);
+    const float iq = s_iq, ik = s_ik;
+    const float u = bt * (s_v[t] - ik * a);
+    s_u[t] = ik * u;  // the state update writes (k / |k|) u^T
+    o[(size_t)bh * V + v0 + t] = from_f32<Tin>(iq * bq + iq * ik * s_qk * u);
   }
   __syncthreads();
 
@@ -121,7 +145,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(
 template <typename Tin>
 hipError_t launch_decode(const void* q, const void* k, const void* v, const void* g,
                          const void* beta, float* state, void* o, int B, int H, int HV,
-                         int K, int V, float scale, hipStream_t stream) {
+                         int K, int V, float scale, unsigned flags, hipStream_t stream) {
   const Tin* q_ = static_cast<const Tin*>(q);
   const Tin* k_ = static_cast<const Tin*>(k);
   const Tin* v_ = static_cast<const Tin*>(v);
@@ -132,19 +156,19 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, const void
   // Split V in two when that keeps >= 4 workgroups per CU-slot worth of work.
   if (V % 8 == 0 && heads < 8192) {
     hipLaunchKernelGGL((decode_step_kernel<Tin, 2>), dim3(heads * 2), dim3(kDecodeThreads), 0,
-                       stream, q_, k_, v_, g_, b_, state, o_, H, HV, K, V, scale);
+                       stream, q_, k_, v_, g_, b_, state, o_, H, HV, K, V, scale, flags);
   } else {
     hipLaunchKernelGGL((decode_step_kernel<Tin, 1>), dim3(heads), dim3(kDecodeThreads), 0, stream,
-                       q_, k_, v_, g_, b_, state, o_, H, HV, K, V, scale);
+                       q_, k_, v_, g_, b_, state, o_, H, HV, K, V, scale, flags);
   }
   return hipGetLastError();
 }
 
 template hipError_t launch_decode<float>(const void*, const void*, const void*, const void*,
                                          const void*, float*, void*, int, int, int, int, int,
-                                         float, hipStream_t);
+                                         float, unsigned, hipStream_t);
 template hipError_t launch_decode<bf16>(const void*, const void*, const void*, const void*,
                                         const void*, float*, void*, int, int, int, int, int,
-                                        float, hipStream_t);
+                                        float, unsigned, hipStream_t);
 
 }  // namespace kda

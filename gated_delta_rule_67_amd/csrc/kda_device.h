@@ -36,6 +36,13 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Input transforms a caller may leave to the kernels (same values as the C ABI's flags).
+constexpr unsigned kFlagQkL2norm = 1u;     // q, k <- x / sqrt(sum x^2 + 1e-6) over K
+constexpr unsigned kFlagBetaSigmoid = 2u;  // beta <- 1 / (1 + exp(-beta))
+constexpr float kL2normEps = 1e-6f;
+
+__device__ __forceinline__ float sigmoid_f32(float x) { return 1.f / (1.f + fast_exp2(-x * kLog2e)); }
+
 // Arguments of one chunked-prefill launch (validated by the C ABI).
 struct PrefillArgs {
   const void* q;
@@ -49,6 +56,7 @@ struct PrefillArgs {
   int B, T, H, HV, K, V;
   float scale;
   int vec_qkg, vec_v;
+  unsigned flags;  // kFlag* input transforms (two-kernel bf16 path only)
 };
 
 }  // namespace kda

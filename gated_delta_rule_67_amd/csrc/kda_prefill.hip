@@ -477,13 +477,15 @@ hipError_t launch_prefill_wy(const PrefillArgs& a, void* workspace, hipStream_t 
 hipError_t launch_prefill(const void* q, const void* k, const void* v, const void* g,
                           const void* beta, const float* s0, float* sT, void* o, int B, int T,
                           int H, int HV, int K, int V, float scale, bool bf16_inputs,
-                          void* workspace, hipStream_t stream) {
-  PrefillArgs a{q, k, v, g, beta, s0, sT, o, B, T, H, HV, K, V, scale, 0, 0};
+                          void* workspace, unsigned flags, hipStream_t stream) {
+  PrefillArgs a{q, k, v, g, beta, s0, sT, o, B, T, H, HV, K, V, scale, 0, 0, flags};
   const int vw = bf16_inputs ? 8 : 4;
   a.vec_qkg = (K % vw == 0) && aligned16(q) && aligned16(k) && aligned16(g);
   a.vec_v = (V % vw == 0) && aligned16(v);
   // With a workspace (sized by the caller), bf16 runs as per-chunk factors + state pass.
   if (bf16_inputs && a.vec_qkg && a.vec_v && workspace) return launch_prefill_wy(a, workspace, stream);
+  // the input transforms exist only in the two-kernel path
+  if (flags) return hipErrorNotSupported;
   // The bf16 kernel addresses each batch's tensors through 32-bit buffer offsets.
   const size_t batch_bytes = (size_t)T * (H > HV ? H : HV) * (K > V ? K : V) * 2;
   if (bf16_inputs && a.vec_qkg && batch_bytes < ((size_t)1 << 31)) return launch_prefill_bf16(a, stream);

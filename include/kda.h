@@ -48,6 +48,15 @@ typedef enum {
 
 typedef enum { KDA_DTYPE_F32 = 0, KDA_DTYPE_BF16 = 1 } kda_dtype;
 
+/* Input transforms the *_ex entry points can apply inside the kernels, for callers that pass
+ * raw projections. The K3 README's test-status table runs the chunk kernels on q and k
+ * L2-normalised inside the operator; the KDA CUDA Trainer README's usage notes name a CUDA
+ * path that applies the sigmoid to beta itself. */
+typedef enum {
+  KDA_FLAG_QK_L2NORM = 1,    /* q, k <- x / sqrt(sum_K x^2 + 1e-6), per (token, head), fp32 */
+  KDA_FLAG_BETA_SIGMOID = 2  /* beta <- 1 / (1 + exp(-beta)), fp32 */
+} kda_flags;
+
 /*
  * Chunked prefill over a whole sequence batch (K3 README, roadmap rows L2 and L3:
  * in-chunk cumsum of g, a decay-weighted lower-triangular system solved by forward
@@ -92,6 +101,18 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const void* g,
                   void* stream);
 
 /*
+ * kda_chunk_fwd with input transforms: flags is 0 or an OR of kda_flags (other bits:
+ * KDA_ERR_INVALID). Nonzero flags need the two-kernel path (bf16, K % 8 == 0, V % 8 == 0,
+ * 16-byte aligned q, k, g, v, a workspace); elsewhere they return KDA_ERR_UNSUPPORTED.
+ * kda_chunk_fwd(...) is kda_chunk_fwd_ex(..., 0, stream).
+ */
+int kda_chunk_fwd_ex(const void* q, const void* k, const void* v, const void* g,
+                     const void* beta, const float* initial_state, float* final_state,
+                     void* o, int B, int T, int H, int HV, int K, int V, float scale,
+                     int chunk_size, int dtype, void* workspace, size_t workspace_bytes,
+                     unsigned flags, void* stream);
+
+/*
  * One decode token for every (b, hv), state updated IN PLACE (K3 README, roadmap
  * row L6: recurrent decode against a [B, HV, K, V] state cache; the DM-KDAGQA-1.7B
  * model card's usage notes: cached generation costs one such step per token).
@@ -109,6 +130,13 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const void* g,
 int kda_recurrent_step(const void* q, const void* k, const void* v, const void* g,
                        const void* beta, float* state, void* o, int B, int H, int HV,
                        int K, int V, float scale, int dtype, void* stream);
+
+/* kda_recurrent_step with input transforms (flags as for kda_chunk_fwd_ex; every dtype and
+ * shape kda_recurrent_step takes). kda_recurrent_step(...) is
+ * kda_recurrent_step_ex(..., 0, stream). */
+int kda_recurrent_step_ex(const void* q, const void* k, const void* v, const void* g,
+                          const void* beta, float* state, void* o, int B, int H, int HV,
+                          int K, int V, float scale, int dtype, unsigned flags, void* stream);
 
 /* Static, NUL-terminated description of a status code; never NULL. */
 const char* kda_status_string(int status);

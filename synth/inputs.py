@@ -59,6 +59,8 @@ def _gate(shape, gen, mode):
 
 def _beta(shape, gen, mode):
     x = torch.randn(shape, generator=gen, dtype=torch.float32)
+    if mode == "logit":  # for callers that apply the sigmoid themselves
+        return x
     if mode == "default":
         return torch.sigmoid(x)
     if mode == "small":
@@ -68,18 +70,19 @@ def _beta(shape, gen, mode):
     raise ValueError(mode)
 
 
-def _unit(shape, gen):
+def _unit(shape, gen, raw=False):
     x = torch.randn(shape, generator=gen, dtype=torch.float32)
-    return x / x.norm(dim=-1, keepdim=True)
+    return x if raw else x / x.norm(dim=-1, keepdim=True)
 
 
 def prefill_inputs(B, T, H, HV, K, V, dtype="bf16", init_state=True, seed=0,
-                   gate="default", beta="default"):
-    """Inputs for one chunked forward. Returns a dict of CPU tensors plus 'scale'."""
+                   gate="default", beta="default", raw_qk=False):
+    """Inputs for one chunked forward. Returns a dict of CPU tensors plus 'scale'.
+    raw_qk: q and k stay standard normal (not normalised), for callers that normalise."""
     gen = torch.Generator("cpu").manual_seed(seed)
     dt = DTYPES[dtype]
-    q = _unit((B, T, H, K), gen).to(dt)
-    k = _unit((B, T, H, K), gen).to(dt)
+    q = _unit((B, T, H, K), gen, raw_qk).to(dt)
+    k = _unit((B, T, H, K), gen, raw_qk).to(dt)
     v = torch.randn((B, T, HV, V), generator=gen, dtype=torch.float32).to(dt)
     g = _gate((B, T, HV, K), gen, gate).to(dt)
     b = _beta((B, T, HV), gen, beta).to(dt)
@@ -90,15 +93,15 @@ def prefill_inputs(B, T, H, HV, K, V, dtype="bf16", init_state=True, seed=0,
 
 
 def decode_inputs(steps, B, H, HV, K, V, dtype="bf16", init_state=True, seed=0,
-                  gate="default", beta="default"):
+                  gate="default", beta="default", raw_qk=False):
     """Inputs for `steps` single-token decode steps on one state.
 
     q, k [steps, B, H, K]; v [steps, B, HV, V]; g [steps, B, HV, K];
     beta [steps, B, HV]; state [B, HV, K, V] float32."""
     gen = torch.Generator("cpu").manual_seed(seed)
     dt = DTYPES[dtype]
-    q = _unit((steps, B, H, K), gen).to(dt)
-    k = _unit((steps, B, H, K), gen).to(dt)
+    q = _unit((steps, B, H, K), gen, raw_qk).to(dt)
+    k = _unit((steps, B, H, K), gen, raw_qk).to(dt)
     v = torch.randn((steps, B, HV, V), generator=gen, dtype=torch.float32).to(dt)
     g = _gate((steps, B, HV, K), gen, gate).to(dt)
     b = _beta((steps, B, HV), gen, beta).to(dt)

@@ -29,8 +29,9 @@ def lib():
 
 def test_header_declares_the_boundary():
     names = _declared_functions()
-    for required in ("kda_chunk_fwd", "kda_chunk_fwd_workspace_size", "kda_recurrent_step",
-                     "kda_status_string", "kda_version"):
+    for required in ("kda_chunk_fwd", "kda_chunk_fwd_ex", "kda_chunk_fwd_workspace_size",
+                     "kda_recurrent_step", "kda_recurrent_step_ex", "kda_status_string",
+                     "kda_version"):
         assert required in names
 
 
@@ -128,3 +129,46 @@ def test_binding_fails_loudly_without_a_gpu_tensor():
     x = torch.zeros(1, 64, 1, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         kda.kda_chunk_fwd(x, x, x, x, torch.zeros(1, 64, 1, dtype=torch.bfloat16))
+
+
+def _chunk_ex(lib, flags, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, s0=None, sT=None, o=FAKE, B=2, T=64, H=2,
+             HV=4, K=64, V=64, scale=0.125, chunk=64, dtype=1)
+    a.update(kw)
+    return lib.kda_chunk_fwd_ex(a["q"], a["k"], a["v"], a["g"], a["beta"], a["s0"], a["sT"],
+                                a["o"], a["B"], a["T"], a["H"], a["HV"], a["K"], a["V"],
+                                a["scale"], a["chunk"], a["dtype"], a.get("ws"),
+                                a.get("ws_bytes", 0), flags, None)
+
+
+def test_flag_constants_match_header():
+    text = open(HEADER).read()
+    assert re.search(r"KDA_FLAG_QK_L2NORM\s*=\s*%d" % kda.KDA_FLAG_QK_L2NORM, text)
+    assert re.search(r"KDA_FLAG_BETA_SIGMOID\s*=\s*%d" % kda.KDA_FLAG_BETA_SIGMOID, text)
+
+
+@pytest.mark.parametrize("flags,kw,rc", [
+    (4, {}, kda.KDA_ERR_INVALID),                         # unknown flag bit
+    (0x80000000, {}, kda.KDA_ERR_INVALID),
+    (1, dict(dtype=0), kda.KDA_ERR_UNSUPPORTED),          # fp32 has no transform path
+    (2, {}, kda.KDA_ERR_UNSUPPORTED),                     # bf16 without a workspace
+    (3, dict(V=36), kda.KDA_ERR_UNSUPPORTED),             # V % 8 != 0: fused kernel only
+    (1, dict(q=None), kda.KDA_ERR_INVALID),               # validation order: pointers first
+])
+def test_chunk_fwd_ex_rejects_unsupported_flags(lib, flags, kw, rc):
+    assert _chunk_ex(lib, flags, **kw) == rc
+
+
+@pytest.mark.parametrize("flags,kw,rc", [
+    (4, {}, kda.KDA_ERR_INVALID),
+    (8, dict(dtype=0), kda.KDA_ERR_INVALID),
+    (3, dict(V=62), kda.KDA_ERR_UNSUPPORTED),
+    (1, dict(state=None), kda.KDA_ERR_INVALID),
+])
+def test_recurrent_step_ex_rejects_invalid_arguments(lib, flags, kw, rc):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, state=FAKE, o=FAKE, B=2, H=2, HV=4, K=64,
+             V=64, scale=0.125, dtype=1)
+    a.update(kw)
+    assert lib.kda_recurrent_step_ex(a["q"], a["k"], a["v"], a["g"], a["beta"], a["state"],
+                                     a["o"], a["B"], a["H"], a["HV"], a["K"], a["V"], a["scale"],
+                                     a["dtype"], flags, None) == rc
