@@ -17,6 +17,8 @@ Three independent CPU formulations, all in float64 numpy:
   triangular system, triangular solve, state passed between chunks).
 * ``brute`` (O3): each token written as an affine map of the state, composed
   explicitly with K x K matrices. Only for tiny shapes.
+* ``recurrent_bwd``: gradients of O1 by reverse-mode differentiation of each
+  token step, written out (K3 README roadmap rows L1/L4).
 * ``transforms``: the optional in-operator input transforms (q/k L2
   normalisation, beta sigmoid) that ``recurrent`` / ``decode_step`` apply on
   request.
@@ -30,6 +32,7 @@ from .recurrent import decode_step, recurrent
 from .chunked import chunked, forward_substitution_inverse
 from .brute import brute
 from .transforms import l2_normalize, sigmoid
+from .backward import recurrent_bwd
 
 __all__ = [
     "decode_step",
@@ -39,4 +42,5 @@ __all__ = [
     "brute",
     "l2_normalize",
     "sigmoid",
+    "recurrent_bwd",
 ]
