@@ -24,7 +24,7 @@ import os
 
 import torch
 
-__all__ = ["kda_chunk_fwd", "kda_recurrent_step", "library", "library_path", "status_string",
+__all__ = ["kda_chunk_fwd", "kda_chunk_bwd", "kda_recurrent_step", "library", "library_path", "status_string",
            "KDA_OK", "KDA_ERR_INVALID", "KDA_ERR_UNSUPPORTED", "KDA_ERR_HIP",
            "KDA_FLAG_QK_L2NORM", "KDA_FLAG_BETA_SIGMOID"]
 
@@ -51,6 +51,10 @@ def library():
     lib.kda_chunk_fwd_ex.restype = i
     lib.kda_chunk_fwd_workspace_size.argtypes = [i] * 8
     lib.kda_chunk_fwd_workspace_size.restype = sz
+    lib.kda_chunk_bwd.argtypes = [vp] * 14 + [i] * 6 + [f, i, i, vp, sz, vp]
+    lib.kda_chunk_bwd.restype = i
+    lib.kda_chunk_bwd_workspace_size.argtypes = [i] * 8
+    lib.kda_chunk_bwd_workspace_size.restype = sz
     lib.kda_recurrent_step.argtypes = [vp] * 7 + [i] * 5 + [f, i, vp]
     lib.kda_recurrent_step.restype = i
     lib.kda_recurrent_step_ex.argtypes = [vp] * 7 + [i] * 5 + [f, i, ctypes.c_uint, vp]
@@ -125,6 +129,48 @@ def kda_chunk_fwd(q, k, v, g, beta, scale=None, initial_state=None, output_final
                                   _flags(qk_l2norm, beta_sigmoid), ctypes.c_void_p(stream))
     _check(rc)
     return o, final
+
+
+def kda_chunk_bwd(q, k, v, g, beta, do, scale=None, initial_state=None, dht=None, chunk_size=64,
+                  need_dh0=True):
+    """Gradients of <o, do> + <final_state, dht> for kda_chunk_fwd's inputs (bf16).
+    Shapes as kda_chunk_fwd; do [B,T,HV,V]; dht [B,HV,K,V] float32 or None.
+    Returns (dq, dk, dv, dg, dbeta, dh0 or None); dh0 is float32 [B,HV,K,V]."""
+    _require(q.is_cuda, "inputs must be on a GPU")
+    dev, dt = q.device, q.dtype
+    _require(dt in _DTYPE, f"unsupported dtype {dt}")
+    B, T, H, K = q.shape
+    HV, V = v.shape[2], v.shape[3]
+    _require(k.shape == q.shape, "k must match q")
+    _require(tuple(v.shape[:2]) == (B, T), "v must be [B, T, HV, V]")
+    _require(tuple(g.shape) == (B, T, HV, K), "g must be [B, T, HV, K]")
+    _require(tuple(beta.shape) == (B, T, HV), "beta must be [B, T, HV]")
+    _require(tuple(do.shape) == (B, T, HV, V), "do must be [B, T, HV, V]")
+    _check_tensors([("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("do", do)], dt, dev)
+    for name, t in (("initial_state", initial_state), ("dht", dht)):
+        if t is not None:
+            _require(tuple(t.shape) == (B, HV, K, V), f"{name} must be [B, HV, K, V]")
+            _check_tensors([(name, t)], torch.float32, dev)
+    if scale is None:
+        scale = 1.0 / math.sqrt(K)
+    lib = library()
+    dq = torch.empty((B, T, H, K), dtype=dt, device=dev)
+    dk = torch.empty((B, T, H, K), dtype=dt, device=dev)
+    dv = torch.empty((B, T, HV, V), dtype=dt, device=dev)
+    dg = torch.empty((B, T, HV, K), dtype=dt, device=dev)
+    dbeta = torch.empty((B, T, HV), dtype=dt, device=dev)
+    dh0 = torch.empty((B, HV, K, V), dtype=torch.float32, device=dev) if need_dh0 else None
+    ws_bytes = lib.kda_chunk_bwd_workspace_size(B, T, H, HV, K, V, chunk_size, _DTYPE[dt])
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        rc = lib.kda_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                               _ptr(initial_state), _ptr(do), _ptr(dht), _ptr(dq), _ptr(dk),
+                               _ptr(dv), _ptr(dg), _ptr(dbeta), _ptr(dh0), B, T, H, HV, K, V,
+                               float(scale), int(chunk_size), _DTYPE[dt], _ptr(ws), ws_bytes,
+                               ctypes.c_void_p(stream))
+    _check(rc)
+    return dq, dk, dv, dg, dbeta, dh0
 
 
 def kda_recurrent_step(q, k, v, g, beta, state, scale=None, qk_l2norm=False, beta_sigmoid=False):

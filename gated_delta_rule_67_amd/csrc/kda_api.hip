@@ -14,6 +14,11 @@ hipError_t launch_prefill(const void*, const void*, const void*, const void*, co
                           const float*, float*, void*, int, int, int, int, int, int, float, bool,
                           void*, unsigned, hipStream_t);
 size_t wy_workspace_bytes(int B, int T, int HV, int K);
+size_t bwd_workspace_bytes(int B, int T, int H, int HV, int K, int V);
+hipError_t launch_chunk_bwd(const void*, const void*, const void*, const void*, const void*,
+                            const float*, const void*, const float*, void*, void*, void*, void*,
+                            void*, float*, int, int, int, int, int, int, float, void*,
+                            hipStream_t);
 }  // namespace kda
 
 namespace {
@@ -21,6 +26,20 @@ namespace {
 constexpr int kMaxDim = 128;
 
 bool positive(int x) { return x >= 1; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+bool valid_chunk(int T, int chunk_size) {
+  if (chunk_size != 8 && chunk_size != 16 && chunk_size != 32 && chunk_size != 64 &&
+      chunk_size != 128)
+    return false;
+  return T % chunk_size == 0;
+}
+
+// Shapes the chunked backward has kernels for (after the common checks).
+bool bwd_shape(int K, int V, int dtype) {
+  return dtype == KDA_DTYPE_BF16 && (K == 32 || K == 64 || K == 128) && V % 16 == 0 && V <= 128;
+}
 
 int check_common(int B, int H, int HV, int K, int V, float scale, int dtype) {
   if (!positive(B) || !positive(H) || !positive(HV) || !positive(K) || !positive(V))
@@ -95,6 +114,38 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const void* g, co
                   size_t workspace_bytes, void* stream) {
   return kda_chunk_fwd_ex(q, k, v, g, beta, initial_state, final_state, o, B, T, H, HV, K, V,
                           scale, chunk_size, dtype, workspace, workspace_bytes, 0u, stream);
+}
+
+size_t kda_chunk_bwd_workspace_size(int B, int T, int H, int HV, int K, int V, int chunk_size,
+                                    int dtype) {
+  if (!positive(T) || !valid_chunk(T, chunk_size)) return 0;
+  if (check_common(B, H, HV, K, V, 1.f, dtype) != KDA_OK || !bwd_shape(K, V, dtype)) return 0;
+  return kda::bwd_workspace_bytes(B, T, H, HV, K, V);
+}
+
+int kda_chunk_bwd(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                  const float* initial_state, const void* dout, const float* dht, void* dq,
+                  void* dk, void* dv, void* dg, void* dbeta, float* dh0, int B, int T, int H,
+                  int HV, int K, int V, float scale, int chunk_size, int dtype, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !g || !beta || !dout || !dq || !dk || !dv || !dg || !dbeta)
+    return KDA_ERR_INVALID;
+  if (!positive(T) || !valid_chunk(T, chunk_size)) return KDA_ERR_INVALID;
+  const int rc = check_common(B, H, HV, K, V, scale, dtype);
+  if (rc != KDA_OK) return rc;
+  if (!bwd_shape(K, V, dtype)) return KDA_ERR_UNSUPPORTED;
+  if ((int64_t)B * HV * ((T + 63) / 64) > INT32_MAX) return KDA_ERR_UNSUPPORTED;
+  if ((int64_t)B * T * H * K / 256 > INT32_MAX) return KDA_ERR_UNSUPPORTED;
+  const size_t need = kda::bwd_workspace_bytes(B, T, H, HV, K, V);
+  if (!workspace || workspace_bytes < need) return KDA_ERR_INVALID;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0) return KDA_ERR_INVALID;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g) || !aligned16(dout) ||
+      !aligned16(dv))
+    return KDA_ERR_UNSUPPORTED;
+  const hipError_t e = kda::launch_chunk_bwd(q, k, v, g, beta, initial_state, dout, dht, dq, dk,
+                                             dv, dg, dbeta, dh0, B, T, H, HV, K, V, scale,
+                                             workspace, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
 int kda_recurrent_step_ex(const void* q, const void* k, const void* v, const void* g,

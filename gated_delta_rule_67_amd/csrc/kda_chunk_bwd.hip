@@ -1,0 +1,1005 @@
+// Chunked KDA backward (bfloat16 inputs, fp32 arithmetic on bf16 MFMA operands).
+//
+// Gradients dq, dk, dv, dg, dbeta (and dh0) of L = <o, do> + <S_T, dht>, the end-to-end
+// backward of the chunked forward that the K3 README page ("KDA 训练 → 推理 手写实现")
+// lists as roadmap row L4, with dq, dk summed over the G value heads that share a q/k head
+// (key-constraints table, GVA and "L4 dxs" rows).
+//
+// Per 64-token chunk and value head, with G the in-chunk cumsum of g, Gam = exp(G),
+// Gam_C = Gam of the last token, Kg = K*Gam, Qg = Q*Gam, Kc = K*Gam_C/Gam, and
+//   Aq[i,j] = sum_c q_ic k_jc exp(G_ic - G_jc) (j <= i),   Mr[i,j] = the same with k_i (j < i),
+//   T = (I + diag(beta) Mr)^-1,  W0 = V - Kg h,  U = T diag(beta) W0,
+//   O = scale (Qg h + Aq U),  h' = Gam_C h + Kc^T U   (h: the state entering the chunk),
+// the reverse of one chunk, given dO and dS (the gradient reaching h'), is
+//   dU = scale Aq^T dO + Kc dS,   Ut = T^T dU,   dv = beta Ut,
+//   dh = Gam_C dS + scale Qg^T dO - Kg^T (beta Ut)                       (to the previous chunk)
+//   F = scale dO U^T (j <= i),   E = -diag(beta) Ut U^T (j < i)            (gradients of Aq, Mr)
+//   dbeta_i = Ut_i . W0_i + sum_j (-Ut U^T)_ij Mr_ij
+//   dq = F (x) K + Gam * scale dO h^T
+//   dk = E (x) K + F^T (x) Q + E^T (x) K - Gam * (beta Ut) h^T + Gam_C/Gam * U dS^T
+// where X (x) Y is the relative-decay product sum_j X_ij y_jc exp(G_ic - G_jc) (and its
+// transposed form), and dG = q*dq + k*(terms where G_i enters with +) - k*(terms with -),
+// plus, on the last token, sum_j k_j Gam_C/Gam_j dKc_j + Gam_C * rowsum(dS * h); dg is the
+// reverse cumsum of dG inside the chunk.
+//
+// Four kernels: prep (per chunk: G, Aq, Mr, T and the transposed factor tiles), a forward
+// sweep that recomputes h, U and W0 chunk by chunk, a reverse sweep that carries dS and keeps
+// Ut and dS per chunk, and a per-chunk local kernel for everything else. Relative decays in
+// the products are factored per 16-token block: with r the block's first token and e its
+// last, exp(G_i - G_j) = exp(G_i - G_r) exp(G_r - G_j) for an output row in block I (r of I),
+// or exp(G_i - G_e) exp(G_e - G_j) for an output column in block J (e of J). Every factor is
+// <= 1 except exp(G_r - G_j) for j in block r's own block and exp(G_i - G_e) for i in e's,
+// which stay below e^75 when g >= -5.
+#include "kda_device.h"
+
+namespace kda {
+namespace bwd {
+
+constexpr int kC = 64;
+constexpr int kPC = kC + 8;  // bf16 LDS pitch of token-contiguous rows
+
+struct BwdArgs {
+  const bf16* q;
+  const bf16* k;
+  const bf16* v;
+  const bf16* g;
+  const bf16* beta;
+  const bf16* dout;
+  const float* s0;   // initial state [B, HV, K, V] or null (zeros)
+  const float* dht;  // gradient of the final state or null (zeros)
+  bf16* dq;
+  bf16* dk;
+  bf16* dv;
+  bf16* dg;
+  bf16* dbeta;
+  float* dh0;  // gradient of the initial state or null
+  int B, T, H, HV, K, V, NT;
+  float scale;
+  unsigned char* blocks;  // prep blocks, (b, hv, chunk) order
+  bf16* h;                // [B*HV][NT][K][V] state entering each chunk
+  bf16* dsn;              // [B*HV][NT][K][V] gradient reaching the state leaving each chunk
+  bf16* u;                // [B*HV][NT*64][V]
+  bf16* w0;               // [B*HV][NT*64][V]
+  bf16* ut;               // [B*HV][NT*64][V]
+  float* dq32;            // [B, T, HV, K] per value head (G > 1), else null
+  float* dk32;
+};
+
+// One chunk's prep block (bytes).
+template <int KT>
+struct PB {
+  static constexpr int kg = 0;                     // [64][KT] bf16 K*Gam
+  static constexpr int kc = kg + kC * KT * 2;      // [64][KT] bf16 K*Gam_C/Gam
+  static constexpr int kct = kc + kC * KT * 2;     // [KT][64] bf16 (K*Gam_C/Gam)^T
+  static constexpr int qgt = kct + KT * kC * 2;    // [KT][64] bf16 (Q*Gam)^T
+  static constexpr int kgt = qgt + KT * kC * 2;    // [KT][64] bf16 (K*Gam)^T
+  static constexpr int tm = kgt + KT * kC * 2;     // [64][64] bf16 T
+  static constexpr int tt = tm + kC * kC * 2;      // [64][64] bf16 T^T
+  static constexpr int aqt = tt + kC * kC * 2;     // [64][64] bf16 Aq^T
+  static constexpr int mr = aqt + kC * kC * 2;     // [64][64] fp32 Mr
+  static constexpr int gam = mr + kC * kC * 4;     // [KT] fp32 Gam_C
+  static constexpr int beta = gam + KT * 4;        // [64] fp32 beta
+  static constexpr int bytes = (beta + kC * 4 + 255) / 256 * 256;
+};
+
+size_t prep_block_bytes(int K) {
+  return K <= 32 ? PB<32>::bytes : K <= 64 ? PB<64>::bytes : PB<128>::bytes;
+}
+
+__device__ __forceinline__ float ldf(const bf16* p) { return static_cast<float>(*p); }
+__device__ __forceinline__ float ex(float x) { return fast_exp2(x * kLog2e); }
+__device__ __forceinline__ bf16x8 ld8(const void* p) { return *reinterpret_cast<const bf16x8*>(p); }
+__device__ __forceinline__ void st8(void* p, bf16x8 x) { *reinterpret_cast<bf16x8*>(p) = x; }
+__device__ __forceinline__ void st4(void* p, f32x4 x) {
+  *reinterpret_cast<bf16x4*>(p) =
+      bf16x4{static_cast<bf16>(x[0]), static_cast<bf16>(x[1]), static_cast<bf16>(x[2]), static_cast<bf16>(x[3])};
+}
+
+// ============================================================================ prep
+template <int KT>
+struct PrepLds {
+  static constexpr int PK = KT + 8, PG = KT + 4;
+  static constexpr int g = 0;                      // [64][PG] fp32 G
+  static constexpr int tot = g + kC * PG * 4;      // [4][KT] fp32 16-token block sums
+  static constexpr int bt = tot + 4 * KT * 4;      // [64] fp32 beta
+  static constexpr int qs = bt + kC * 4;           // [64][PK] bf16 q exp(G - G_r), r own block
+  static constexpr int ks = qs + kC * PK * 2;      // [64][PK] bf16 k exp(G - G_r)
+  static constexpr int bop = ks + kC * PK * 2;     // [160][PK] bf16 k_j exp(G_rw - G_j), wave w
+  static constexpr int end1 = bop + 160 * PK * 2;
+  static constexpr int mr = qs;                    // [64][65] fp32 Mr (after the products)
+  static constexpr int tf = mr + kC * 65 * 4;      // [64][65] fp32 T
+  static constexpr int end2 = tf + kC * 65 * 4;
+  static constexpr int total = end1 > end2 ? end1 : end2;
+  static_assert(total <= 160 * 1024, "LDS");
+};
+
+template <int KT>
+__global__ __launch_bounds__(256) void prep_kernel(BwdArgs a) {
+  using L = PrepLds<KT>;
+  using P = PB<KT>;
+  constexpr int PK = L::PK, PG = L::PG;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[L::total];
+  float* G = reinterpret_cast<float*>(lds + L::g);
+  float* tot = reinterpret_cast<float*>(lds + L::tot);
+  float* sb = reinterpret_cast<float*>(lds + L::bt);
+  bf16* qs = reinterpret_cast<bf16*>(lds + L::qs);
+  bf16* ks = reinterpret_cast<bf16*>(lds + L::ks);
+  bf16* bop = reinterpret_cast<bf16*>(lds + L::bop);
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int item = blockIdx.x;
+  const int n = item % a.NT, head = item / a.NT;
+  const int b = head / a.HV, hv = head - b * a.HV, hh = hv / (a.HV / a.H);
+  const int t0 = n * kC, nrow = min(kC, a.T - t0);
+  const size_t qrow = (size_t)a.H * KT, grow = (size_t)a.HV * KT;
+  const bf16* qb = a.q + ((size_t)b * a.T + t0) * qrow + (size_t)hh * KT;
+  const bf16* kb = a.k + ((size_t)b * a.T + t0) * qrow + (size_t)hh * KT;
+  const bf16* gb = a.g + ((size_t)b * a.T + t0) * grow + (size_t)hv * KT;
+  unsigned char* blk = a.blocks + (size_t)item * P::bytes;
+
+  // G: each (16-token block, channel) scanned by one thread, then block prefixes added
+  for (int it = tid; it < 4 * KT; it += 256) {
+    const int wb = it / KT, c = it % KT;
+    float acc = 0.f;
+    for (int i = 0; i < 16; ++i) {
+      const int t = 16 * wb + i;
+      acc += t < nrow ? ldf(gb + (size_t)t * grow + c) : 0.f;
+      G[t * PG + c] = acc;
+    }
+    tot[wb * KT + c] = acc;
+  }
+  if (tid < kC) {
+    const float bv = tid < nrow ? ldf(a.beta + ((size_t)b * a.T + t0 + tid) * a.HV + hv) : 0.f;
+    sb[tid] = bv;
+    reinterpret_cast<float*>(blk + P::beta)[tid] = bv;
+  }
+  __syncthreads();
+  for (int it = tid; it < 4 * KT; it += 256) {
+    const int wb = it / KT, c = it % KT;
+    float pre = 0.f;
+    for (int j = 0; j < wb; ++j) pre += tot[j * KT + c];
+    for (int i = 0; i < 16; ++i) G[(16 * wb + i) * PG + c] += pre;
+  }
+  __syncthreads();
+
+  // operands of the row-block-w products, built by wave w
+  {
+    const int r0 = 16 * w;
+    for (int u = lane; u < 16 * (KT / 8); u += 64) {  // q, k of block w relative to its first token
+      const int i = r0 + u / (KT / 8), c8 = 8 * (u % (KT / 8));
+      bf16x8 qv{}, kv{};
+      if (i < nrow) {
+        qv = ld8(qb + (size_t)i * qrow + c8);
+        kv = ld8(kb + (size_t)i * qrow + c8);
+      }
+      bf16x8 qo, ko;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float f = ex(G[i * PG + c8 + e] - G[r0 * PG + c8 + e]);
+        qo[e] = static_cast<bf16>(static_cast<float>(qv[e]) * f);
+        ko[e] = static_cast<bf16>(static_cast<float>(kv[e]) * f);
+      }
+      st8(qs + i * PK + c8, qo);
+      st8(ks + i * PK + c8, ko);
+    }
+    bf16* bw = bop + 8 * w * (w + 1) * PK;  // rows 0 .. 16w + 15
+    for (int u = lane; u < 16 * (w + 1) * (KT / 8); u += 64) {
+      const int j = u / (KT / 8), c8 = 8 * (u % (KT / 8));
+      bf16x8 kv{};
+      if (j < nrow) kv = ld8(kb + (size_t)j * qrow + c8);
+      bf16x8 ko;
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        ko[e] = static_cast<bf16>(static_cast<float>(kv[e]) * ex(G[r0 * PG + c8 + e] - G[j * PG + c8 + e]));
+      st8(bw + j * PK + c8, ko);
+    }
+  }
+  __syncthreads();
+
+  // Aq and Mr row block w; tiles J <= w
+  f32x4 aq[4], mr[4];
+  {
+    const bf16* bw = bop + 8 * w * (w + 1) * PK;
+    for (int J = 0; J < 4; ++J) {
+      aq[J] = mr[J] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (J <= w) {
+        mma16(aq[J], qs + 16 * w * PK, PK, bw + 16 * J * PK, PK, KT, lane);
+        mma16(mr[J], ks + 16 * w * PK, PK, bw + 16 * J * PK, PK, KT, lane);
+      }
+    }
+  }
+  __syncthreads();  // qs / ks / bop are dead from here; mr / tf reuse them
+  float* smr = reinterpret_cast<float*>(lds + L::mr);
+  float* stf = reinterpret_cast<float*>(lds + L::tf);
+  {
+    const int col = lane & 15, rq = 4 * (lane >> 4);
+    bf16* aqt = reinterpret_cast<bf16*>(blk + P::aqt);
+    float* gmr = reinterpret_cast<float*>(blk + P::mr);
+    for (int J = 0; J < 4; ++J) {
+      const int j = 16 * J + col;
+      f32x4 av = aq[J], mv = mr[J];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * w + rq + r;
+        if (j > i) av[r] = 0.f;
+        if (j >= i) mv[r] = 0.f;
+        smr[i * 65 + j] = mv[r];
+        gmr[i * kC + j] = mv[r];
+      }
+      st4(aqt + j * kC + 16 * w + rq, av);  // Aq^T row j, tokens i .. i+3
+    }
+  }
+  __syncthreads();
+
+  // T = (I + diag(beta) Mr)^-1 by forward substitution, one row at a time
+  {
+    const int c = tid >> 2, p = tid & 3;
+    for (int i = 0; i < kC; ++i) {
+      float s = 0.f;
+      for (int j = c + p; j < i; j += 4) s += smr[i * 65 + j] * stf[j * 65 + c];
+      s += __shfl_xor(s, 1);
+      s += __shfl_xor(s, 2);
+      if (p == 0) stf[i * 65 + c] = c == i ? 1.f : (c < i ? -sb[i] * s : 0.f);
+      __syncthreads();
+    }
+  }
+  // T, T^T (bf16)
+  {
+    bf16* tm = reinterpret_cast<bf16*>(blk + P::tm);
+    bf16* tt = reinterpret_cast<bf16*>(blk + P::tt);
+    for (int u = tid; u < kC * kC / 8; u += 256) {
+      const int row = u / 8, c8 = 8 * (u % 8);
+      bf16x8 x, y;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        x[e] = static_cast<bf16>(stf[row * 65 + c8 + e]);
+        y[e] = static_cast<bf16>(stf[(c8 + e) * 65 + row]);
+      }
+      st8(tm + row * kC + c8, x);
+      st8(tt + row * kC + c8, y);
+    }
+  }
+  // Gam_C; K*Gam, K*Gam_C/Gam (natural); their transposes and (Q*Gam)^T
+  if (tid < KT) reinterpret_cast<float*>(blk + P::gam)[tid] = ex(G[(kC - 1) * PG + tid]);
+  {
+    bf16* kg = reinterpret_cast<bf16*>(blk + P::kg);
+    bf16* kc = reinterpret_cast<bf16*>(blk + P::kc);
+    for (int u = tid; u < kC * KT / 8; u += 256) {
+      const int i = u / (KT / 8), c8 = 8 * (u % (KT / 8));
+      bf16x8 kv{};
+      if (i < nrow) kv = ld8(kb + (size_t)i * qrow + c8);
+      bf16x8 x, y;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float gi = G[i * PG + c8 + e], gl = G[(kC - 1) * PG + c8 + e];
+        x[e] = static_cast<bf16>(static_cast<float>(kv[e]) * ex(gi));
+        y[e] = static_cast<bf16>(static_cast<float>(kv[e]) * ex(gl - gi));
+      }
+      st8(kg + i * KT + c8, x);
+      st8(kc + i * KT + c8, y);
+    }
+    bf16* kct = reinterpret_cast<bf16*>(blk + P::kct);
+    bf16* qgt = reinterpret_cast<bf16*>(blk + P::qgt);
+    bf16* kgt = reinterpret_cast<bf16*>(blk + P::kgt);
+    for (int u = tid; u < KT * kC / 8; u += 256) {
+      const int c = u % KT, i8 = 8 * (u / KT);
+      bf16x8 x, y, z;
+      const float gl = G[(kC - 1) * PG + c];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int i = i8 + e;
+        const float kv = i < nrow ? ldf(kb + (size_t)i * qrow + c) : 0.f;
+        const float qv = i < nrow ? ldf(qb + (size_t)i * qrow + c) : 0.f;
+        const float gi = G[i * PG + c];
+        x[e] = static_cast<bf16>(kv * ex(gl - gi));
+        y[e] = static_cast<bf16>(qv * ex(gi));
+        z[e] = static_cast<bf16>(kv * ex(gi));
+      }
+      st8(kct + c * kC + i8, x);
+      st8(qgt + c * kC + i8, y);
+      st8(kgt + c * kC + i8, z);
+    }
+  }
+}
+
+// Copies rows x cols bf16 (cols a multiple of 8) from a dense global tile into LDS with pitch ld.
+__device__ __forceinline__ void copy_tile(bf16* dst, int ld, const bf16* src, int rows, int cols,
+                                          int tid, int nthreads) {
+  const int per = cols / 8;
+  for (int u = tid; u < rows * per; u += nthreads) {
+    const int r = u / per, c8 = 8 * (u % per);
+    st8(dst + r * ld + c8, ld8(src + (size_t)r * cols + c8));
+  }
+}
+
+// ==================================================================== forward sweep
+// One workgroup of NW waves per (b, hv, 16 NW-column V tile); wave w owns 16 columns and
+// keeps their state h (K x 16, fp32) in MFMA accumulators. Per chunk: store h, then
+// W0 = V - Kg h, U = T (beta W0), h <- Gam_C h + Kc^T U.
+template <int KT, int NW>
+struct SweepLds {
+  static constexpr int PK = KT + 8, BV = 16 * NW, PV = BV + 8;
+  // forward sweep
+  static constexpr int kg = 0;                          // [64][PK]
+  static constexpr int kct = kg + kC * PK * 2;          // [KT][kPC]
+  static constexpr int tm = kct + KT * kPC * 2;         // [64][kPC]
+  static constexpr int gam = tm + kC * kPC * 2;         // [KT] fp32
+  static constexpr int bt = gam + KT * 4;               // [64] fp32
+  static constexpr int vt = bt + kC * 4;                // [64][PV] v tile
+  static constexpr int ht = vt + kC * PV * 2;           // [BV][PK] h^T
+  static constexpr int yt = ht + BV * PK * 2;           // [BV][kPC] (beta W0)^T
+  static constexpr int uu = yt + BV * kPC * 2;          // [BV][kPC] U^T
+  static constexpr int fwd_total = uu + BV * kPC * 2;
+  // reverse sweep
+  static constexpr int kc = 0;                          // [64][PK]
+  static constexpr int qgt = kc + kC * PK * 2;          // [KT][kPC]
+  static constexpr int kgt = qgt + KT * kPC * 2;        // [KT][kPC]
+  static constexpr int tt = kgt + KT * kPC * 2;         // [64][kPC]
+  static constexpr int aqt = tt + kC * kPC * 2;         // [64][kPC]
+  static constexpr int rgam = aqt + kC * kPC * 2;       // [KT] fp32
+  static constexpr int rbt = rgam + KT * 4;             // [64] fp32
+  static constexpr int dot = rbt + kC * 4;              // [BV][kPC] dO^T
+  static constexpr int dst = dot + BV * kPC * 2;        // [BV][PK] dS^T
+  static constexpr int dut = dst + BV * PK * 2;         // [BV][kPC] dU^T
+  static constexpr int but = dut + BV * kPC * 2;        // [BV][kPC] (beta Ut)^T
+  static constexpr int rev_total = but + BV * kPC * 2;
+  static constexpr int total = fwd_total > rev_total ? fwd_total : rev_total;
+  static_assert(total <= 160 * 1024, "LDS");
+};
+
+template <int KT, int NW>
+__global__ __launch_bounds__(64 * NW) void fwd_sweep_kernel(BwdArgs a) {
+  using L = SweepLds<KT, NW>;
+  using P = PB<KT>;
+  constexpr int PK = L::PK, BV = L::BV, PV = L::PV, NCT = KT / 16;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[L::total];
+  bf16* s_kg = reinterpret_cast<bf16*>(lds + L::kg);
+  bf16* s_kct = reinterpret_cast<bf16*>(lds + L::kct);
+  bf16* s_tm = reinterpret_cast<bf16*>(lds + L::tm);
+  float* s_gam = reinterpret_cast<float*>(lds + L::gam);
+  float* s_bt = reinterpret_cast<float*>(lds + L::bt);
+  bf16* s_vt = reinterpret_cast<bf16*>(lds + L::vt);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int lr = lane & 15, lq = lane >> 4;
+  bf16* s_ht = reinterpret_cast<bf16*>(lds + L::ht) + 16 * w * PK;
+  bf16* s_yt = reinterpret_cast<bf16*>(lds + L::yt) + 16 * w * kPC;
+  bf16* s_uu = reinterpret_cast<bf16*>(lds + L::uu) + 16 * w * kPC;
+
+  const int nvt = (a.V + BV - 1) / BV;
+  const int head = blockIdx.x / nvt, vt_idx = blockIdx.x % nvt;
+  const int b = head / a.HV, hv = head - b * a.HV;
+  const int V = a.V, T = a.T;
+  const int vc = vt_idx * BV + 16 * w + lr;  // this lane's column
+  const bool vok = vc < V;
+
+  f32x4 S[NCT];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int c = 16 * ct + 4 * lq + r;
+      S[ct][r] = (a.s0 && vok) ? a.s0[((size_t)head * KT + c) * V + vc] : 0.f;
+    }
+
+  for (int n = 0; n < a.NT; ++n) {
+    const int t0 = n * kC, nrow = min(kC, T - t0);
+    const unsigned char* blk = a.blocks + ((size_t)head * a.NT + n) * P::bytes;
+    __syncthreads();
+    for (int u = tid; u < kC * KT / 8; u += 64 * NW) {
+      const int r = u / (KT / 8), c8 = 8 * (u % (KT / 8));
+      st8(s_kg + r * PK + c8, ld8(blk + P::kg + (r * KT + c8) * 2));
+    }
+    for (int u = tid; u < KT * kC / 8; u += 64 * NW) {
+      const int r = u / 8, c8 = 8 * (u % 8);
+      st8(s_kct + r * kPC + c8, ld8(blk + P::kct + (r * kC + c8) * 2));
+    }
+    for (int u = tid; u < kC * kC / 8; u += 64 * NW) {
+      const int r = u / 8, c8 = 8 * (u % 8);
+      st8(s_tm + r * kPC + c8, ld8(blk + P::tm + (r * kC + c8) * 2));
+    }
+    for (int u = tid; u < KT; u += 64 * NW) s_gam[u] = reinterpret_cast<const float*>(blk + P::gam)[u];
+    for (int u = tid; u < kC; u += 64 * NW) s_bt[u] = reinterpret_cast<const float*>(blk + P::beta)[u];
+    for (int u = tid; u < kC * BV / 8; u += 64 * NW) {  // v tile, zeros past T or V
+      const int r = u / (BV / 8), c8 = 8 * (u % (BV / 8));
+      const int col = vt_idx * BV + c8;
+      bf16x8 x{};
+      if (r < nrow && col < V) x = ld8(a.v + (((size_t)b * T + t0 + r) * a.HV + hv) * V + col);
+      st8(s_vt + r * PV + c8, x);
+    }
+    // h of this chunk: to the workspace (bf16, [K][V]) and transposed into LDS
+    bf16* hg = a.h + ((size_t)head * a.NT + n) * KT * V;
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      st4(s_ht + lr * PK + 16 * ct + 4 * lq, S[ct]);
+      if (vok)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) hg[(size_t)(16 * ct + 4 * lq + r) * V + vc] = static_cast<bf16>(S[ct][r]);
+    }
+    __syncthreads();
+    // X = Kg h, W0 = V - X, Y = beta W0
+    const size_t trow = ((size_t)head * a.NT + n) * kC;
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+      f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
+      mma16(x, s_kg + 16 * I * PK, PK, s_ht, PK, KT, lane);
+      f32x4 w0, y;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * I + 4 * lq + r;
+        w0[r] = static_cast<float>(s_vt[i * PV + 16 * w + lr]) - x[r];
+        y[r] = s_bt[i] * w0[r];
+        if (vok) a.w0[(trow + i) * V + vc] = static_cast<bf16>(w0[r]);
+      }
+      st4(s_yt + lr * kPC + 16 * I + 4 * lq, y);
+    }
+    // U = T Y
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+      f32x4 uv = f32x4{0.f, 0.f, 0.f, 0.f};
+      mma16(uv, s_tm + 16 * I * kPC, kPC, s_yt, kPC, kC, lane);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (vok) a.u[(trow + 16 * I + 4 * lq + r) * V + vc] = static_cast<bf16>(uv[r]);
+      st4(s_uu + lr * kPC + 16 * I + 4 * lq, uv);
+    }
+    // h <- Gam_C h + Kc^T U
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) S[ct][r] *= s_gam[16 * ct + 4 * lq + r];
+      mma16(S[ct], s_kct + 16 * ct * kPC, kPC, s_uu, kPC, kC, lane);
+    }
+  }
+}
+
+// ==================================================================== reverse sweep
+template <int KT, int NW>
+__global__ __launch_bounds__(64 * NW) void rev_sweep_kernel(BwdArgs a) {
+  using L = SweepLds<KT, NW>;
+  using P = PB<KT>;
+  constexpr int PK = L::PK, BV = L::BV, NCT = KT / 16;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[L::total];
+  bf16* s_kc = reinterpret_cast<bf16*>(lds + L::kc);
+  bf16* s_qgt = reinterpret_cast<bf16*>(lds + L::qgt);
+  bf16* s_kgt = reinterpret_cast<bf16*>(lds + L::kgt);
+  bf16* s_tt = reinterpret_cast<bf16*>(lds + L::tt);
+  bf16* s_aqt = reinterpret_cast<bf16*>(lds + L::aqt);
+  float* s_gam = reinterpret_cast<float*>(lds + L::rgam);
+  float* s_bt = reinterpret_cast<float*>(lds + L::rbt);
+  bf16* s_dot = reinterpret_cast<bf16*>(lds + L::dot);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int lr = lane & 15, lq = lane >> 4;
+  bf16* s_dst = reinterpret_cast<bf16*>(lds + L::dst) + 16 * w * PK;
+  bf16* s_dut = reinterpret_cast<bf16*>(lds + L::dut) + 16 * w * kPC;
+  bf16* s_but = reinterpret_cast<bf16*>(lds + L::but) + 16 * w * kPC;
+  bf16* s_dow = s_dot + 16 * w * kPC;
+
+  const int nvt = (a.V + BV - 1) / BV;
+  const int head = blockIdx.x / nvt, vt_idx = blockIdx.x % nvt;
+  const int b = head / a.HV, hv = head - b * a.HV;
+  const int V = a.V, T = a.T;
+  const int vc = vt_idx * BV + 16 * w + lr;
+  const bool vok = vc < V;
+
+  f32x4 D[NCT];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int c = 16 * ct + 4 * lq + r;
+      D[ct][r] = (a.dht && vok) ? a.dht[((size_t)head * KT + c) * V + vc] : 0.f;
+    }
+
+  for (int n = a.NT - 1; n >= 0; --n) {
+    const int t0 = n * kC, nrow = min(kC, T - t0);
+    const unsigned char* blk = a.blocks + ((size_t)head * a.NT + n) * P::bytes;
+    __syncthreads();
+    for (int u = tid; u < kC * KT / 8; u += 64 * NW) {
+      const int r = u / (KT / 8), c8 = 8 * (u % (KT / 8));
+      st8(s_kc + r * PK + c8, ld8(blk + P::kc + (r * KT + c8) * 2));
+    }
+    for (int u = tid; u < KT * kC / 8; u += 64 * NW) {
+      const int r = u / 8, c8 = 8 * (u % 8);
+      st8(s_qgt + r * kPC + c8, ld8(blk + P::qgt + (r * kC + c8) * 2));
+      st8(s_kgt + r * kPC + c8, ld8(blk + P::kgt + (r * kC + c8) * 2));
+    }
+    for (int u = tid; u < kC * kC / 8; u += 64 * NW) {
+      const int r = u / 8, c8 = 8 * (u % 8);
+      st8(s_tt + r * kPC + c8, ld8(blk + P::tt + (r * kC + c8) * 2));
+      st8(s_aqt + r * kPC + c8, ld8(blk + P::aqt + (r * kC + c8) * 2));
+    }
+    for (int u = tid; u < KT; u += 64 * NW) s_gam[u] = reinterpret_cast<const float*>(blk + P::gam)[u];
+    for (int u = tid; u < kC; u += 64 * NW) s_bt[u] = reinterpret_cast<const float*>(blk + P::beta)[u];
+    // dO^T of the tile: lane (lr, lq) of wave w reads tokens 4 lq .. + 3 (+16 I) of its column
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+      bf16x4 x;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * I + 4 * lq + r;
+        x[r] = (i < nrow && vok) ? a.dout[(((size_t)b * T + t0 + i) * a.HV + hv) * V + vc] : static_cast<bf16>(0.f);
+      }
+      *reinterpret_cast<bf16x4*>(s_dow + lr * kPC + 16 * I + 4 * lq) = x;
+    }
+    // dS reaching the state that leaves this chunk: to the workspace, and transposed into LDS
+    bf16* dg_ = a.dsn + ((size_t)head * a.NT + n) * KT * V;
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      st4(s_dst + lr * PK + 16 * ct + 4 * lq, D[ct]);
+      if (vok)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dg_[(size_t)(16 * ct + 4 * lq + r) * V + vc] = static_cast<bf16>(D[ct][r]);
+    }
+    __syncthreads();
+    // dU = scale Aq^T dO + Kc dS
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+      f32x4 p = f32x4{0.f, 0.f, 0.f, 0.f}, q = f32x4{0.f, 0.f, 0.f, 0.f};
+      mma16(p, s_aqt + 16 * I * kPC, kPC, s_dow, kPC, kC, lane);
+      mma16(q, s_kc + 16 * I * PK, PK, s_dst, PK, KT, lane);
+      st4(s_dut + lr * kPC + 16 * I + 4 * lq, a.scale * p + q);
+    }
+    // Ut = T^T dU; dv = beta Ut
+    const size_t trow = ((size_t)head * a.NT + n) * kC;
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+      f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
+      mma16(x, s_tt + 16 * I * kPC, kPC, s_dut, kPC, kC, lane);
+      f32x4 y;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * I + 4 * lq + r;
+        y[r] = s_bt[i] * x[r];
+        if (vok) a.ut[(trow + i) * V + vc] = static_cast<bf16>(x[r]);
+      }
+      st4(s_but + lr * kPC + 16 * I + 4 * lq, y);
+    }
+    // dS <- Gam_C dS + scale Qg^T dO - Kg^T (beta Ut)
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      f32x4 p = f32x4{0.f, 0.f, 0.f, 0.f}, q = f32x4{0.f, 0.f, 0.f, 0.f};
+      mma16(p, s_qgt + 16 * ct * kPC, kPC, s_dow, kPC, kC, lane);
+      mma16(q, s_kgt + 16 * ct * kPC, kPC, s_but, kPC, kC, lane);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) D[ct][r] = D[ct][r] * s_gam[16 * ct + 4 * lq + r] + a.scale * p[r] - q[r];
+    }
+  }
+  if (a.dh0 && vok)
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) a.dh0[((size_t)head * KT + 16 * ct + 4 * lq + r) * V + vc] = D[ct][r];
+}
+
+// ==================================================================== local gradients
+template <int KT>
+struct LocalLds {
+  static constexpr int PK = KT + 8, PG = KT + 4, PV = 128 + 8;
+  static constexpr int g = 0;                      // [64][PG] fp32 G (all phases)
+  static constexpr int bt = g + kC * PG * 4;       // [64] fp32 beta
+  static constexpr int db1 = bt + kC * 4;          // [64] fp32 Ut . W0
+  static constexpr int db2 = db1 + kC * 4;         // [4][64] fp32 partial sum_j -D Mr per wave? (row-owned)
+  static constexpr int lx = db2 + kC * 4;          // [4][KT] fp32 last-token terms per wave
+  static constexpr int lx2 = lx + 4 * KT * 4;      // [KT] fp32 Gam_C rowsum(dS h)
+  static constexpr int ph = lx2 + KT * 4;          // phase region
+  // phase 1
+  static constexpr int uu = ph;                    // [64][PV] U
+  static constexpr int ut = uu + kC * PV * 2;      // [64][PV] Ut
+  static constexpr int dO = ut + kC * PV * 2;      // [64][PV] dO
+  static constexpr int hs = dO + kC * PV * 2;      // [KT][PV] h, then dS
+  static constexpr int end1 = hs + KT * PV * 2;
+  // phase 2
+  static constexpr int f = ph;                     // [64][kPC] F
+  static constexpr int ft = f + kC * kPC * 2;      // [64][kPC] F^T
+  static constexpr int e = ft + kC * kPC * 2;      // [64][kPC] E
+  static constexpr int et = e + kC * kPC * 2;      // [64][kPC] E^T
+  static constexpr int wop = et + kC * kPC * 2;    // [4][KT][kPC] per-wave operand
+  static constexpr int end2 = wop + 4 * KT * kPC * 2;
+  // phase 3
+  static constexpr int dgs = ph;                   // [64][PG] fp32 dG
+  static constexpr int end3 = dgs + kC * PG * 4;
+  static constexpr int total = end1 > end2 ? (end1 > end3 ? end1 : end3) : (end2 > end3 ? end2 : end3);
+  static_assert(total <= 160 * 1024, "LDS");
+};
+
+template <int KT>
+__global__ __launch_bounds__(256) void local_kernel(BwdArgs a) {
+  using L = LocalLds<KT>;
+  using P = PB<KT>;
+  constexpr int PG = L::PG, PV = L::PV, NCT = KT / 16;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[L::total];
+  float* G = reinterpret_cast<float*>(lds + L::g);
+  float* sb = reinterpret_cast<float*>(lds + L::bt);
+  float* db1 = reinterpret_cast<float*>(lds + L::db1);
+  float* db2 = reinterpret_cast<float*>(lds + L::db2);
+  float* lx = reinterpret_cast<float*>(lds + L::lx);
+  float* lx2 = reinterpret_cast<float*>(lds + L::lx2);
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int lr = lane & 15, lq = lane >> 4;
+  const int item = blockIdx.x;
+  const int n = item % a.NT, head = item / a.NT;
+  const int b = head / a.HV, hv = head - b * a.HV, hh = hv / (a.HV / a.H);
+  const int V = a.V, T = a.T;
+  const int t0 = n * kC, nrow = min(kC, T - t0);
+  const size_t qrow = (size_t)a.H * KT, grow = (size_t)a.HV * KT;
+  const bf16* qb = a.q + ((size_t)b * T + t0) * qrow + (size_t)hh * KT;
+  const bf16* kb = a.k + ((size_t)b * T + t0) * qrow + (size_t)hh * KT;
+  const bf16* gb = a.g + ((size_t)b * T + t0) * grow + (size_t)hv * KT;
+  const unsigned char* blk = a.blocks + (size_t)item * P::bytes;
+  const size_t trow = ((size_t)head * a.NT + n) * kC;
+  const bf16* hsrc = a.h + ((size_t)head * a.NT + n) * KT * V;
+  const bf16* dsrc = a.dsn + ((size_t)head * a.NT + n) * KT * V;
+
+  // G (recomputed as in prep), beta
+  {
+    float* tot = reinterpret_cast<float*>(lds + L::ph);  // scratch before phase 1
+    for (int it = tid; it < 4 * KT; it += 256) {
+      const int wb = it / KT, c = it % KT;
+      float acc = 0.f;
+      for (int i = 0; i < 16; ++i) {
+        const int t = 16 * wb + i;
+        acc += t < nrow ? ldf(gb + (size_t)t * grow + c) : 0.f;
+        G[t * PG + c] = acc;
+      }
+      tot[wb * KT + c] = acc;
+    }
+    if (tid < kC) sb[tid] = reinterpret_cast<const float*>(blk + P::beta)[tid];
+    __syncthreads();
+    for (int it = tid; it < 4 * KT; it += 256) {
+      const int wb = it / KT, c = it % KT;
+      float pre = 0.f;
+      for (int j = 0; j < wb; ++j) pre += tot[j * KT + c];
+      for (int i = 0; i < 16; ++i) G[(16 * wb + i) * PG + c] += pre;
+    }
+    __syncthreads();
+  }
+
+  // ---------------- phase 1: products contracting over V
+  bf16* s_u = reinterpret_cast<bf16*>(lds + L::uu);
+  bf16* s_ut = reinterpret_cast<bf16*>(lds + L::ut);
+  bf16* s_do = reinterpret_cast<bf16*>(lds + L::dO);
+  bf16* s_hs = reinterpret_cast<bf16*>(lds + L::hs);
+  for (int u = tid; u < kC * (V / 8); u += 256) {
+    const int r = u / (V / 8), c8 = 8 * (u % (V / 8));
+    st8(s_u + r * PV + c8, ld8(a.u + (trow + r) * V + c8));
+    st8(s_ut + r * PV + c8, ld8(a.ut + (trow + r) * V + c8));
+    bf16x8 x{};
+    if (r < nrow) x = ld8(a.dout + (((size_t)b * T + t0 + r) * a.HV + hv) * V + c8);
+    st8(s_do + r * PV + c8, x);
+  }
+  for (int u = tid; u < KT * (V / 8); u += 256) {
+    const int r = u / (V / 8), c8 = 8 * (u % (V / 8));
+    st8(s_hs + r * PV + c8, ld8(hsrc + (size_t)r * V + c8));
+  }
+  // Gam_C rowsum(dS * h), per channel, straight from the workspace
+  for (int c = tid; c < KT; c += 256) {
+    float s = 0.f;
+    for (int v8 = 0; v8 < V; v8 += 8) {
+      const bf16x8 x = ld8(hsrc + (size_t)c * V + v8), y = ld8(dsrc + (size_t)c * V + v8);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s += static_cast<float>(x[e]) * static_cast<float>(y[e]);
+    }
+    lx2[c] = ex(G[(kC - 1) * PG + c]) * s;
+  }
+  __syncthreads();
+
+  const int rw = 16 * w, ew = 16 * w + 15;  // first and last token of this wave's block
+  f32x4 Dm[4], Fo[4];
+#pragma unroll
+  for (int J = 0; J < 4; ++J) {
+    Dm[J] = Fo[J] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (J <= w) {
+      mma16(Dm[J], s_ut + rw * PV, PV, s_u + 16 * J * PV, PV, V, lane);
+      mma16(Fo[J], s_do + rw * PV, PV, s_u + 16 * J * PV, PV, V, lane);
+    }
+  }
+  f32x4 adq[NCT], arow[NCT], acol[NCT];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+    adq[ct] = arow[ct] = acol[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    mma16(adq[ct], s_do + rw * PV, PV, s_hs + 16 * ct * PV, PV, V, lane);
+    mma16(arow[ct], s_ut + rw * PV, PV, s_hs + 16 * ct * PV, PV, V, lane);
+    const int c = 16 * ct + lr;
+    const float er = ex(G[rw * PG + c]);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      adq[ct][r] *= a.scale * er;                     // scale dO h^T, times exp(G_r)
+      arow[ct][r] *= -sb[rw + 4 * lq + r] * er;        // -(beta Ut) h^T, times exp(G_r)
+    }
+  }
+  __syncthreads();
+  for (int u = tid; u < KT * (V / 8); u += 256) {
+    const int r = u / (V / 8), c8 = 8 * (u % (V / 8));
+    st8(s_hs + r * PV + c8, ld8(dsrc + (size_t)r * V + c8));
+  }
+  // dbeta, first term: Ut_i . W0_i (4 threads per token)
+  {
+    const int i = tid >> 2, p = tid & 3;
+    float s = 0.f;
+    for (int v8 = 8 * p; v8 < V; v8 += 32) {
+      const bf16x8 x = ld8(s_ut + i * PV + v8), y = ld8(a.w0 + (trow + i) * V + v8);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s += static_cast<float>(x[e]) * static_cast<float>(y[e]);
+    }
+    s += __shfl_xor(s, 1);
+    s += __shfl_xor(s, 2);
+    if (p == 0) db1[i] = s;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+    f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
+    mma16(x, s_u + rw * PV, PV, s_hs + 16 * ct * PV, PV, V, lane);  // U dS^T
+    const int c = 16 * ct + lr;
+    const float gl = G[(kC - 1) * PG + c];
+    float part = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int j = rw + 4 * lq + r;
+      const float kv = j < nrow ? ldf(kb + (size_t)j * qrow + c) : 0.f;
+      part += kv * ex(gl - G[j * PG + c]) * x[r];  // last-token term of dG
+    }
+    part += __shfl_xor(part, 16);
+    part += __shfl_xor(part, 32);
+    if (lq == 0) lx[w * KT + c] = part;
+    const float f = ex(gl - G[ew * PG + c]);
+    acol[ct] = x * f;  // U dS^T times exp(G_C - G_ew); the output factor exp(G_ew - G_j) completes Gam_C/Gam_j
+  }
+  // dbeta, second term: sum_j (-Ut U^T)_ij Mr_ij, rows of this wave
+  {
+    const float* gmr = reinterpret_cast<const float*>(blk + P::mr);
+    float s[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int J = 0; J < 4; ++J)
+      if (J <= w)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = rw + 4 * lq + r, j = 16 * J + lr;
+          s[r] -= Dm[J][r] * gmr[i * kC + j];  // Mr is zero on and above the diagonal
+        }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float x = s[r];
+      x += __shfl_xor(x, 1);
+      x += __shfl_xor(x, 2);
+      x += __shfl_xor(x, 4);
+      x += __shfl_xor(x, 8);
+      if (lr == 0) db2[rw + 4 * lq + r] = x;
+    }
+  }
+  __syncthreads();  // phase 1 operands are dead
+
+  // ---------------- phase 2: F, E and the relative-decay products
+  bf16* s_f = reinterpret_cast<bf16*>(lds + L::f);
+  bf16* s_ft = reinterpret_cast<bf16*>(lds + L::ft);
+  bf16* s_e = reinterpret_cast<bf16*>(lds + L::e);
+  bf16* s_et = reinterpret_cast<bf16*>(lds + L::et);
+  bf16* s_op = reinterpret_cast<bf16*>(lds + L::wop) + w * KT * kPC;
+#pragma unroll
+  for (int J = 0; J < 4; ++J) {
+    const int j = 16 * J + lr;
+    f32x4 fv, evv;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = rw + 4 * lq + r;
+      fv[r] = j <= i ? a.scale * Fo[J][r] : 0.f;
+      evv[r] = j < i ? -sb[i] * Dm[J][r] : 0.f;
+      s_f[i * kPC + j] = static_cast<bf16>(fv[r]);
+      s_e[i * kPC + j] = static_cast<bf16>(evv[r]);
+    }
+    st4(s_ft + j * kPC + rw + 4 * lq, fv);
+    st4(s_et + j * kPC + rw + 4 * lq, evv);
+  }
+  __syncthreads();
+
+  // The scaled q / k operand goes in as a bf16 pair hi + lo (two products): the gradient terms
+  // of Aq and Mr enter dG once through each role with opposite signs and cancel in the
+  // reverse cumsum, which plain bf16 rounding of this operand (different in each role) would
+  // not preserve. F and E are rounded once and shared by both roles. Half the channels at a time.
+  constexpr int KH = KT / 2, NCH = NCT / 2;
+  bf16* s_hi = s_op;
+  bf16* s_lo = s_op + KH * kPC;
+  // role 0: row role against reference rw over tokens 0 .. ew, operand k_j exp(G_rw - G_j)
+  // role 1 / 2: column role against reference ew over tokens rw .. 63, operand
+  //             q_i exp(G_i - G_ew) (with F^T) / k_i exp(G_i - G_ew) (with E^T)
+  for (int role = 0; role < 3; ++role) {
+    const int first = role == 0 ? 0 : rw;
+    const int ntok = role == 0 ? 16 * (w + 1) : kC - rw;
+    const int ref = role == 0 ? rw : ew;
+    const bf16* src = role == 1 ? qb : kb;
+    for (int half = 0; half < 2; ++half) {
+      for (int u = lane; u < KH * (ntok / 8); u += 64) {
+        const int cl = u % KH, c = half * KH + cl, j8 = 8 * (u / KH);
+        bf16x8 xh, xl;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int j = first + j8 + e;
+          const float yv = j < nrow ? ldf(src + (size_t)j * qrow + c) : 0.f;
+          const float d = role == 0 ? G[ref * PG + c] - G[j * PG + c] : G[j * PG + c] - G[ref * PG + c];
+          const float x = yv * ex(d);
+          const bf16 hi = static_cast<bf16>(x);
+          xh[e] = hi;
+          xl[e] = static_cast<bf16>(x - static_cast<float>(hi));
+        }
+        st8(s_hi + cl * kPC + j8, xh);
+        st8(s_lo + cl * kPC + j8, xl);
+      }
+      __syncthreads();
+#pragma unroll
+      for (int cc = 0; cc < NCH; ++cc) {
+        const int ct = half * NCH + cc;
+        const bf16* bh = s_hi + 16 * cc * kPC;
+        const bf16* bl = s_lo + 16 * cc * kPC;
+        if (role == 0) {
+          mma16(adq[ct], s_f + rw * kPC, kPC, bh, kPC, ntok, lane);
+          mma16(adq[ct], s_f + rw * kPC, kPC, bl, kPC, ntok, lane);
+          mma16(arow[ct], s_e + rw * kPC, kPC, bh, kPC, ntok, lane);
+          mma16(arow[ct], s_e + rw * kPC, kPC, bl, kPC, ntok, lane);
+        } else {
+          const bf16* xa = (role == 1 ? s_ft : s_et) + rw * kPC + rw;
+          mma16(acol[ct], xa, kPC, bh, kPC, ntok, lane);
+          mma16(acol[ct], xa, kPC, bl, kPC, ntok, lane);
+        }
+      }
+      __syncthreads();
+    }
+  }
+
+  // ---------------- phase 3: output factors, dq, dk, dG, then dg by a reverse scan
+  float* dgs = reinterpret_cast<float*>(lds + L::dgs);
+  const int G_ = a.HV / a.H;
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+    const int c = 16 * ct + lr;
+    const float gr = G[rw * PG + c], ge = G[ew * PG + c];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = rw + 4 * lq + r;
+      const float gi = G[i * PG + c];
+      const float fr = ex(gi - gr), fc = ex(ge - gi);
+      const float dq = adq[ct][r] * fr;
+      const float dpos = arow[ct][r] * fr, dneg = acol[ct][r] * fc;
+      const float dk = dpos + dneg;
+      const bool ok = i < nrow;
+      const float qv = ok ? ldf(qb + (size_t)i * qrow + c) : 0.f;
+      const float kv = ok ? ldf(kb + (size_t)i * qrow + c) : 0.f;
+      dgs[i * PG + c] = qv * dq + kv * (dpos - dneg);
+      if (ok) {
+        const size_t t = (size_t)b * T + t0 + i;
+        if (G_ == 1) {
+          a.dq[(t * a.H + hh) * KT + c] = static_cast<bf16>(dq);
+          a.dk[(t * a.H + hh) * KT + c] = static_cast<bf16>(dk);
+        } else {
+          a.dq32[(t * a.HV + hv) * KT + c] = dq;
+          a.dk32[(t * a.HV + hv) * KT + c] = dk;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  for (int c = tid; c < KT; c += 256) {
+    float run = lx[c] + lx[KT + c] + lx[2 * KT + c] + lx[3 * KT + c] + lx2[c];
+    for (int i = kC - 1; i >= 0; --i) {
+      run += dgs[i * PG + c];
+      if (i < nrow) a.dg[(((size_t)b * T + t0 + i) * a.HV + hv) * KT + c] = static_cast<bf16>(run);
+    }
+  }
+  for (int u = tid; u < nrow * (V / 8); u += 256) {  // dv = beta Ut
+    const int i = u / (V / 8), c8 = 8 * (u % (V / 8));
+    const bf16x8 x = ld8(a.ut + (trow + i) * V + c8);
+    bf16x8 y;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] = static_cast<bf16>(sb[i] * static_cast<float>(x[e]));
+    st8(a.dv + (((size_t)b * T + t0 + i) * a.HV + hv) * V + c8, y);
+  }
+  if (tid < nrow) a.dbeta[((size_t)b * T + t0 + tid) * a.HV + hv] = static_cast<bf16>(db1[tid] + db2[tid]);
+}
+
+// dq, dk: sum of the G value heads of each q/k head (fp32 -> bf16)
+__global__ __launch_bounds__(256) void gva_reduce_kernel(const float* __restrict__ x32,
+                                                         bf16* __restrict__ out, size_t rows, int H,
+                                                         int G, int K) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;  // one output element
+  if (i >= rows * H * K) return;
+  const size_t row = i / ((size_t)H * K);
+  const int rem = (int)(i - row * H * K), h = rem / K, c = rem - h * K;
+  const float* src = x32 + (row * H * G + (size_t)h * G) * K + c;
+  float s = 0.f;
+  for (int j = 0; j < G; ++j) s += src[(size_t)j * K];
+  out[i] = static_cast<bf16>(s);
+}
+
+struct Layout {
+  size_t blocks, h, dsn, u, w0, ut, dq32, dk32, total;
+};
+
+Layout layout(int B, int T, int H, int HV, int K, int V) {
+  const int NT = (T + kC - 1) / kC;
+  const size_t heads = (size_t)B * HV;
+  auto al = [](size_t x) { return (x + 255) / 256 * 256; };
+  Layout l{};
+  size_t off = 0;
+  l.blocks = off; off += al(heads * NT * prep_block_bytes(K));
+  l.h = off;      off += al(heads * NT * (size_t)K * V * 2);
+  l.dsn = off;    off += al(heads * NT * (size_t)K * V * 2);
+  l.u = off;      off += al(heads * NT * kC * (size_t)V * 2);
+  l.w0 = off;     off += al(heads * NT * kC * (size_t)V * 2);
+  l.ut = off;     off += al(heads * NT * kC * (size_t)V * 2);
+  if (HV != H) {
+    l.dq32 = off; off += al((size_t)B * T * HV * K * 4);
+    l.dk32 = off; off += al((size_t)B * T * HV * K * 4);
+  }
+  l.total = off;
+  return l;
+}
+
+template <int KT>
+hipError_t launch_cfg(BwdArgs a, hipStream_t stream) {
+  const int items = a.B * a.HV * a.NT;
+  hipLaunchKernelGGL((prep_kernel<KT>), dim3(items), dim3(256), 0, stream, a);
+  constexpr int NW = 2;
+  const int sweeps = a.B * a.HV * ((a.V + 16 * NW - 1) / (16 * NW));
+  hipLaunchKernelGGL((fwd_sweep_kernel<KT, NW>), dim3(sweeps), dim3(64 * NW), 0, stream, a);
+  hipLaunchKernelGGL((rev_sweep_kernel<KT, NW>), dim3(sweeps), dim3(64 * NW), 0, stream, a);
+  hipLaunchKernelGGL((local_kernel<KT>), dim3(items), dim3(256), 0, stream, a);
+  if (a.HV != a.H) {
+    const size_t n = (size_t)a.B * a.T * a.H * KT;
+    const unsigned grid = (unsigned)((n + 255) / 256);
+    hipLaunchKernelGGL(gva_reduce_kernel, dim3(grid), dim3(256), 0, stream, a.dq32, a.dq,
+                       (size_t)a.B * a.T, a.H, a.HV / a.H, KT);
+    hipLaunchKernelGGL(gva_reduce_kernel, dim3(grid), dim3(256), 0, stream, a.dk32, a.dk,
+                       (size_t)a.B * a.T, a.H, a.HV / a.H, KT);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace bwd
+
+size_t bwd_workspace_bytes(int B, int T, int H, int HV, int K, int V) {
+  return bwd::layout(B, T, H, HV, K, V).total;
+}
+
+// Inputs validated by the C ABI: bf16, K in {32, 64, 128}, V % 16 == 0, V <= 128, workspace of
+// bwd_workspace_bytes, 256-byte aligned; q, k, v, g, dout 16-byte aligned.
+hipError_t launch_chunk_bwd(const void* q, const void* k, const void* v, const void* g,
+                            const void* beta, const float* s0, const void* dout, const float* dht,
+                            void* dq, void* dk, void* dv, void* dg, void* dbeta, float* dh0,
+                            int B, int T, int H, int HV, int K, int V, float scale,
+                            void* workspace, hipStream_t stream) {
+  using namespace bwd;
+  const Layout l = layout(B, T, H, HV, K, V);
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  BwdArgs a{};
+  a.q = static_cast<const bf16*>(q);
+  a.k = static_cast<const bf16*>(k);
+  a.v = static_cast<const bf16*>(v);
+  a.g = static_cast<const bf16*>(g);
+  a.beta = static_cast<const bf16*>(beta);
+  a.dout = static_cast<const bf16*>(dout);
+  a.s0 = s0;
+  a.dht = dht;
+  a.dq = static_cast<bf16*>(dq);
+  a.dk = static_cast<bf16*>(dk);
+  a.dv = static_cast<bf16*>(dv);
+  a.dg = static_cast<bf16*>(dg);
+  a.dbeta = static_cast<bf16*>(dbeta);
+  a.dh0 = dh0;
+  a.B = B; a.T = T; a.H = H; a.HV = HV; a.K = K; a.V = V;
+  a.NT = (T + kC - 1) / kC;
+  a.scale = scale;
+  a.blocks = ws + l.blocks;
+  a.h = reinterpret_cast<bf16*>(ws + l.h);
+  a.dsn = reinterpret_cast<bf16*>(ws + l.dsn);
+  a.u = reinterpret_cast<bf16*>(ws + l.u);
+  a.w0 = reinterpret_cast<bf16*>(ws + l.w0);
+  a.ut = reinterpret_cast<bf16*>(ws + l.ut);
+  a.dq32 = HV != H ? reinterpret_cast<float*>(ws + l.dq32) : nullptr;
+  a.dk32 = HV != H ? reinterpret_cast<float*>(ws + l.dk32) : nullptr;
+  if (K == 32) return launch_cfg<32>(a, stream);
+  if (K == 64) return launch_cfg<64>(a, stream);
+  if (K == 128) return launch_cfg<128>(a, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace kda

@@ -113,6 +113,41 @@ int kda_chunk_fwd_ex(const void* q, const void* k, const void* v, const void* g,
                      unsigned flags, void* stream);
 
 /*
+ * Chunked backward: the gradients of L = <o, dout> + <final_state, dht> with respect to
+ * every input of kda_chunk_fwd (K3 README, roadmap row L4: end-to-end backward of the
+ * chunked kernels, hand-written gradients dq, dk, dv, dg, dbeta as in row L1; key-
+ * constraints table: dq and dk are computed per value head and summed over the G = HV / H
+ * value heads of each q/k head, dv, dg, dbeta stay per value head).
+ *
+ *   q, k, v, g, beta, initial_state, scale, chunk_size   as for kda_chunk_fwd
+ *   dout           [B, T, HV, V]  dtype   gradient reaching o
+ *   dht            [B, HV, K, V]  float32 gradient reaching final_state, or NULL (zeros)
+ *   dq, dk         [B, T, H, K]   dtype out
+ *   dv             [B, T, HV, V]  dtype out
+ *   dg             [B, T, HV, K]  dtype out
+ *   dbeta          [B, T, HV]     dtype out
+ *   dh0            [B, HV, K, V]  float32 out (gradient reaching initial_state), or NULL
+ *   workspace      device memory of at least kda_chunk_bwd_workspace_size() bytes,
+ *                  256-byte aligned, owned by the caller and overwritten (per-chunk factors,
+ *                  the recomputed state entering each chunk, U, W0, the state gradient
+ *                  and T^T dU per chunk); calls sharing it must be ordered on one stream.
+ *                  NULL, too small or misaligned: KDA_ERR_INVALID.
+ * Outputs must not overlap inputs, the workspace or each other.
+ *
+ * Constraints: as for kda_chunk_fwd, and: bf16 only; K in {32, 64, 128}; V % 16 == 0 and
+ * V <= 128; q, k, v, g, dout, dv 16-byte aligned (else KDA_ERR_UNSUPPORTED).
+ */
+size_t kda_chunk_bwd_workspace_size(int B, int T, int H, int HV, int K, int V,
+                                    int chunk_size, int dtype);
+
+int kda_chunk_bwd(const void* q, const void* k, const void* v, const void* g,
+                  const void* beta, const float* initial_state, const void* dout,
+                  const float* dht, void* dq, void* dk, void* dv, void* dg, void* dbeta,
+                  float* dh0, int B, int T, int H, int HV, int K, int V, float scale,
+                  int chunk_size, int dtype, void* workspace, size_t workspace_bytes,
+                  void* stream);
+
+/*
  * One decode token for every (b, hv), state updated IN PLACE (K3 README, roadmap
  * row L6: recurrent decode against a [B, HV, K, V] state cache; the DM-KDAGQA-1.7B
  * model card's usage notes: cached generation costs one such step per token).

@@ -172,3 +172,46 @@ def test_recurrent_step_ex_rejects_invalid_arguments(lib, flags, kw, rc):
     assert lib.kda_recurrent_step_ex(a["q"], a["k"], a["v"], a["g"], a["beta"], a["state"],
                                      a["o"], a["B"], a["H"], a["HV"], a["K"], a["V"], a["scale"],
                                      a["dtype"], flags, None) == rc
+
+
+def _bwd(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, s0=None, do=FAKE, dht=None, dq=FAKE,
+             dk=FAKE, dv=FAKE, dg=FAKE, dbeta=FAKE, dh0=None, B=2, T=64, H=2, HV=4, K=64, V=64,
+             scale=0.125, chunk=64, dtype=1, ws=ctypes.c_void_p(0x100000), ws_bytes=1 << 40)
+    a.update(kw)
+    return lib.kda_chunk_bwd(a["q"], a["k"], a["v"], a["g"], a["beta"], a["s0"], a["do"],
+                             a["dht"], a["dq"], a["dk"], a["dv"], a["dg"], a["dbeta"], a["dh0"],
+                             a["B"], a["T"], a["H"], a["HV"], a["K"], a["V"], a["scale"],
+                             a["chunk"], a["dtype"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("bad,rc", [
+    (dict(q=None), kda.KDA_ERR_INVALID),
+    (dict(do=None), kda.KDA_ERR_INVALID),
+    (dict(dbeta=None), kda.KDA_ERR_INVALID),
+    (dict(T=72), kda.KDA_ERR_INVALID),                 # T % chunk != 0
+    (dict(HV=3), kda.KDA_ERR_INVALID),
+    (dict(scale=float("nan")), kda.KDA_ERR_INVALID),
+    (dict(ws=None), kda.KDA_ERR_INVALID),              # the backward always needs a workspace
+    (dict(ws_bytes=4096), kda.KDA_ERR_INVALID),
+    (dict(ws=ctypes.c_void_p(0x100010)), kda.KDA_ERR_INVALID),
+    (dict(dtype=0), kda.KDA_ERR_UNSUPPORTED),           # bf16 only
+    (dict(K=48), kda.KDA_ERR_UNSUPPORTED),
+    (dict(V=40), kda.KDA_ERR_UNSUPPORTED),
+    (dict(V=256), kda.KDA_ERR_UNSUPPORTED),
+    (dict(q=ctypes.c_void_p(0x1008)), kda.KDA_ERR_UNSUPPORTED),  # not 16-byte aligned
+])
+def test_chunk_bwd_rejects_invalid_arguments(lib, bad, rc):
+    assert _bwd(lib, **bad) == rc
+
+
+def test_bwd_workspace_size(lib):
+    ws = lib.kda_chunk_bwd_workspace_size
+    small = ws(1, 64, 1, 1, 64, 64, 64, 1)
+    assert small > 0 and small % 256 == 0
+    assert ws(2, 64, 1, 1, 64, 64, 64, 1) > small
+    assert ws(1, 72, 1, 1, 64, 64, 8, 1) > small     # a partial second 64-token chunk
+    assert ws(1, 64, 1, 2, 64, 64, 64, 1) > 2 * small  # GVA adds fp32 dq / dk buffers
+    assert ws(1, 64, 1, 1, 64, 64, 64, 0) == 0        # fp32: no backward
+    assert ws(1, 64, 1, 1, 48, 64, 64, 1) == 0
+    assert ws(1, 72, 1, 1, 64, 64, 64, 1) == 0        # T % chunk != 0

@@ -1,0 +1,104 @@
+"""GPU parity of kda_chunk_bwd against the fp64 oracle (oracle.recurrent_bwd, pinned to
+finite differences of the forward oracle).
+
+Inputs are bf16 (q, k unit-norm, gates in [-5, 0], beta in (0, 1)); do is standard
+normal, dht and the initial state N(0, 0.1^2)-ish. Each gradient is held to the bf16
+reading of the tolerance the forward uses: RMS(err) <= 2e-2 RMS(ref) with the per-row
+guard (tests/helpers.py). Shapes span several 64-token chunks, a ragged last chunk,
+GVA (HV > H), K in {32, 64, 128} and V < K; the full-size case is B4 T8192 H16 K=V=128
+with sampled heads."""
+
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_67_amd as kda
+from oracle import recurrent_bwd
+from synth import prefill_inputs
+from tests.helpers import assert_parity, log, to64
+
+pytestmark = pytest.mark.gpu
+
+NAMES = ("dq", "dk", "dv", "dg", "dbeta", "dh0")
+
+
+def _grad_inputs(B, T, H, HV, K, V, seed, gate="default", beta="default"):
+    inp = prefill_inputs(B, T, H, HV, K, V, "bf16", True, seed, gate=gate, beta=beta)
+    gen = torch.Generator().manual_seed(seed + 7)
+    inp["do"] = torch.randn((B, T, HV, V), generator=gen).to(torch.bfloat16)
+    inp["dht"] = 0.1 * torch.randn((B, HV, K, V), generator=gen)
+    return inp
+
+
+def _gpu_bwd(inp, chunk=64):
+    d = {n: (t.cuda() if isinstance(t, torch.Tensor) else t) for n, t in inp.items()}
+    out = kda.kda_chunk_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["do"], d["scale"],
+                            d["initial_state"], d["dht"], chunk)
+    torch.cuda.synchronize()
+    return out
+
+
+def _ref(inp):
+    return recurrent_bwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["scale"],
+                         inp["do"], inp["initial_state"], inp["dht"])
+
+
+def _check(got, ref, what=""):
+    for name, x, r in zip(NAMES, got, ref):
+        assert_parity(to64(x), r, torch.bfloat16, f"{what} {name}")
+
+
+@pytest.mark.parametrize("shape", [
+    dict(B=1, T=64, H=1, HV=1, K=32, V=32),
+    dict(B=2, T=128, H=2, HV=4, K=64, V=64),      # GVA, two chunks
+    dict(B=1, T=200, H=1, HV=2, K=64, V=48),      # ragged last chunk, V < K
+    dict(B=1, T=256, H=2, HV=2, K=128, V=128),
+    dict(B=2, T=96, H=1, HV=3, K=128, V=16),      # G = 3, one 16-column tile
+])
+def test_small_shapes(shape):
+    log(f"backward {shape}")
+    inp = _grad_inputs(**shape, seed=sum(shape.values()))
+    chunk = 64 if shape["T"] % 64 == 0 else 8  # kernels tile by 64 and mask the ragged tail
+    _check(_gpu_bwd(inp, chunk), _ref(inp), str(shape))
+
+
+@pytest.mark.parametrize("gate,beta", [("bound", "default"), ("zero", "large"), ("slow", "small")])
+def test_stress_gates(gate, beta):
+    log(f"backward stress gate={gate} beta={beta} (B1 T512 H=HV=2 K=V=128)")
+    inp = _grad_inputs(1, 512, 2, 2, 128, 128, 61, gate=gate, beta=beta)
+    _check(_gpu_bwd(inp), _ref(inp), f"{gate}/{beta}")
+
+
+def test_chunk_size_does_not_change_the_result():
+    inp = _grad_inputs(1, 256, 1, 2, 64, 64, 5)
+    a = _gpu_bwd(inp, 64)
+    for chunk in (16, 128):
+        b = _gpu_bwd(inp, chunk)
+        for name, x, y in zip(NAMES, a, b):
+            assert torch.equal(x, y), f"{name} differs at chunk {chunk}"
+
+
+def test_full_size_sampled_heads():
+    """B4 T8192 H16 K=V=128 (the prefill workload), two heads against the oracle."""
+    log("backward B4 T8192 H16 K=V=128 (sampled heads)")
+    inp = _grad_inputs(4, 8192, 16, 16, 128, 128, 1236)
+    got = _gpu_bwd(inp)
+    for b, hv in ((0, 0), (3, 11)):
+        one = {n: (t[b:b + 1, :, hv:hv + 1] if t.dim() >= 3 and n != "initial_state" and n != "dht"
+                   else t) for n, t in inp.items() if isinstance(t, torch.Tensor)}
+        one["initial_state"] = inp["initial_state"][b:b + 1, hv:hv + 1]
+        one["dht"] = inp["dht"][b:b + 1, hv:hv + 1]
+        one["scale"] = inp["scale"]
+        ref = _ref(one)
+        sub = [got[0][b:b + 1, :, hv:hv + 1], got[1][b:b + 1, :, hv:hv + 1],
+               got[2][b:b + 1, :, hv:hv + 1], got[3][b:b + 1, :, hv:hv + 1],
+               got[4][b:b + 1, :, hv:hv + 1], got[5][b:b + 1, hv:hv + 1]]
+        _check(sub, ref, f"({b},{hv})")
+
+
+def test_unsupported_shapes_raise():
+    inp = prefill_inputs(1, 64, 1, 1, 48, 32, "bf16", True, 3)
+    d = {n: (t.cuda() if isinstance(t, torch.Tensor) else t) for n, t in inp.items()}
+    do = torch.zeros_like(d["v"])
+    with pytest.raises(RuntimeError, match="UNSUPPORTED"):
+        kda.kda_chunk_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], do, d["scale"])
