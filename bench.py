@@ -5,7 +5,9 @@ B=4, T=8192, H=HV=16, K=V=128, bf16 inputs, fp32 state, chunk 64 (synthetic,
 seeded; the 16 x 128 head layout and 8,192-token context of the pages' KDA
 layers). `value` is prefill tokens/s (B*T per step). The decode step
 (kda_recurrent_step, 64 consecutive steps on a B=256, H=HV=16, K=V=128 fp32
-state cache) is timed in the same run and reported under "decode".
+state cache) is timed in the same run and reported under "decode", and the chunked
+backward (kda_chunk_bwd: dq, dk, dv, dg, dbeta, dh0 of the prefill workload for a
+seeded dO) under "backward".
 
 Timing uses HIP events recorded on the stream the kernels are launched on,
 bracketed by device synchronisation. One prefill call is two kernels on that
@@ -56,6 +58,17 @@ def prefill_algorithmic(B, T, H, HV, K, V, ib, state_in, state_out):
     byts += B * HV * K * V * 4 * (int(state_in) + int(state_out))
     flops = tok * HV * (C * (3 * K + 2 * V) + 6 * K * V + C * C / 3.0)
     return byts, flops
+
+
+def backward_algorithmic(B, T, H, HV, K, V, ib):
+    """Bytes of one backward call: q, k, v, g, beta, dO and the initial state read once;
+    dq, dk, dv, dg, dbeta and dh0 written once."""
+    qk = 2 * B * T * H * K * ib
+    per_v = B * T * HV * (V + K + 1 + V) * ib      # v, g, beta, dO
+    state = B * HV * K * V * 4
+    reads = qk + per_v + state
+    writes = qk + B * T * HV * (V + K + 1) * ib + state
+    return reads + writes
 
 
 def decode_algorithmic(B, H, HV, K, V, ib):
@@ -160,6 +173,8 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=8192)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--backward-steps", type=int, default=5)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -198,7 +213,7 @@ def main():
     achieved = byts / (avg_ms * 1e-3) / 1e9
     tflops = flops / (avg_ms * 1e-3) / 1e12
     traffic = measured_traffic()
-    del d, o, s
+    del o, s
     ceiling = copy_ceiling(torch)
     t_bound = max(flops / (MFMA_BF16_PEAK_TFS * 1e12), byts / (HBM_PEAK_GBS * 1e9))
 
@@ -285,6 +300,37 @@ def main():
                          "median_launch_ms": per_step[len(per_step) // 2]},
         }
         del dd, state, views
+
+    # ---------------- chunked backward on the prefill workload
+    if not args.no_backward:
+        log(f"bench: timing {args.backward_steps} backward calls on {PREFILL_WORKLOAD}")
+        gen = torch.Generator(device=dev).manual_seed(4321)
+        dout = torch.randn(d["v"].shape, generator=gen, device=dev).to(torch.bfloat16)
+
+        def backward():
+            return kda.kda_chunk_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], dout, d["scale"],
+                                     d["initial_state"], None, c["chunk"])
+
+        grads = backward()
+        torch.cuda.synchronize()
+        assert all(torch.isfinite(x.float()).all() for x in grads), "non-finite gradient"
+        del grads
+        b_avg, b_med, b_min = time_launches(backward, args.backward_steps, 1, torch)
+        bbytes = backward_algorithmic(c["B"], c["T"], c["H"], c["HV"], c["K"], c["V"], 2)
+        bgbs = bbytes / (b_avg * 1e-3) / 1e9
+        result["backward"] = {
+            "workload": PREFILL_WORKLOAD + ", seeded dO, gradients of every input and of the "
+                        "initial state",
+            "ms_per_call": b_avg, "median_ms": b_med, "min_ms": b_min,
+            "tokens_per_s": tokens / (b_avg * 1e-3),
+            "roofline": {"bound": "hbm", "achieved": bgbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": bgbs / HBM_PEAK_GBS,
+                         "kernel": "kda::bwd prep_kernel + fwd_sweep_kernel + rev_sweep_kernel + "
+                                   "local_kernel (one kda_chunk_bwd call)",
+                         "algorithmic_bytes_per_launch": bbytes},
+        }
+        del dout
+    del d
 
     # ---------------- oracle on the host
     if not args.no_cpu_baseline:

@@ -95,6 +95,95 @@ __device__ __forceinline__ void st4(void* p, f32x4 x) {
       bf16x4{static_cast<bf16>(x[0]), static_cast<bf16>(x[1]), static_cast<bf16>(x[2]), static_cast<bf16>(x[3])};
 }
 
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+// 16 bytes at byte offset off; zeros past the resource's range
+__device__ __forceinline__ bf16x8 bload8(__amdgpu_buffer_rsrc_t r, unsigned off) {
+  return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+// orders this wave's LDS writes before its later reads (and reads before later writes)
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// One chunk's q, k (bf16, [64][pk]) and g (as fp32 into G, [64][pg]) into LDS; rows past
+// nrow read as zeros. All loads are issued before the first store.
+template <int KT>
+__device__ __forceinline__ void stage_qkg(bf16* sq, bf16* sk, float* G, int pk, int pg,
+                                          const bf16* qb, const bf16* kb, const bf16* gb,
+                                          unsigned qrow, unsigned grow, int nrow, int tid) {
+  constexpr int PER = KT / 8, NU = kC * PER / 256;
+  const auto rq = rsrc(qb, ((unsigned)(nrow - 1) * qrow + KT) * 2);
+  const auto rk = rsrc(kb, ((unsigned)(nrow - 1) * qrow + KT) * 2);
+  const auto rg = rsrc(gb, ((unsigned)(nrow - 1) * grow + KT) * 2);
+  bf16x8 xq[NU], xk[NU], xg[NU];
+#pragma unroll
+  for (int e = 0; e < NU; ++e) {
+    const int u = tid + 256 * e, r = u / PER, c8 = 8 * (u % PER);
+    xq[e] = bload8(rq, (r * qrow + c8) * 2);
+    xk[e] = bload8(rk, (r * qrow + c8) * 2);
+    xg[e] = bload8(rg, (r * grow + c8) * 2);
+  }
+#pragma unroll
+  for (int e = 0; e < NU; ++e) {
+    const int u = tid + 256 * e, r = u / PER, c8 = 8 * (u % PER);
+    st8(sq + r * pk + c8, xq[e]);
+    st8(sk + r * pk + c8, xk[e]);
+#pragma unroll
+    for (int x = 0; x < 8; ++x) G[r * pg + c8 + x] = static_cast<float>(xg[e][x]);
+  }
+}
+
+// In-place inclusive cumsum of G over the 64 rows (columns < KT); tot: [4][KT] scratch.
+template <int KT>
+__device__ __forceinline__ void cumsum_rows(float* G, int pg, float* tot, int tid) {
+  __syncthreads();
+  for (int it = tid; it < 4 * KT; it += 256) {
+    const int wb = it / KT, c = it % KT;
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      acc += G[(16 * wb + i) * pg + c];
+      G[(16 * wb + i) * pg + c] = acc;
+    }
+    tot[wb * KT + c] = acc;
+  }
+  __syncthreads();
+  for (int it = tid; it < 4 * KT; it += 256) {
+    const int wb = it / KT, c = it % KT;
+    float pre = 0.f;
+    for (int j = 0; j < wb; ++j) pre += tot[j * KT + c];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) G[(16 * wb + i) * pg + c] += pre;
+  }
+  __syncthreads();
+}
+
+// acc += A B for A rows held in registers (af[s]: this lane's 8 values of k step s, zeros
+// past kk) and B given transposed in LDS (as mma16).
+__device__ __forceinline__ void mma_ra(f32x4& acc, const bf16x8* af, const bf16* bt, int ldb,
+                                       int kk, int lane) {
+  const int r = lane & 15, q8 = (lane >> 4) * 8;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    if (32 * s >= kk) break;
+    const bf16x8 bv = 32 * s + q8 < kk ? ld8(bt + r * ldb + 32 * s + q8) : bf16x8{};
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[s], bv, acc, 0, 0, 0);
+  }
+}
+
+// acc += A B in fp32 (v_mfma_f32_16x16x4_f32); A and B row-major in LDS.
+__device__ __forceinline__ void mma16_nn(f32x4& acc, const float* a, int lda, const float* b,
+                                         int ldb, int kk, int lane) {
+  const int r = lane & 15, q = lane >> 4;
+  for (int k0 = 0; k0 < kk; k0 += 4)
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[r * lda + k0 + q], b[(k0 + q) * ldb + r], acc, 0,
+                                               0, 0);
+}
+
 // ============================================================================ prep
 template <int KT>
 struct PrepLds {
@@ -102,13 +191,16 @@ struct PrepLds {
   static constexpr int g = 0;                      // [64][PG] fp32 G
   static constexpr int tot = g + kC * PG * 4;      // [4][KT] fp32 16-token block sums
   static constexpr int bt = tot + 4 * KT * 4;      // [64] fp32 beta
-  static constexpr int qs = bt + kC * 4;           // [64][PK] bf16 q exp(G - G_r), r own block
+  static constexpr int sq = bt + kC * 4;           // [64][PK] bf16 q
+  static constexpr int sk = sq + kC * PK * 2;      // [64][PK] bf16 k
+  static constexpr int qs = sk + kC * PK * 2;      // [64][PK] bf16 q exp(G - G_r), r own block
   static constexpr int ks = qs + kC * PK * 2;      // [64][PK] bf16 k exp(G - G_r)
   static constexpr int bop = ks + kC * PK * 2;     // [160][PK] bf16 k_j exp(G_rw - G_j), wave w
   static constexpr int end1 = bop + 160 * PK * 2;
   static constexpr int mr = qs;                    // [64][65] fp32 Mr (after the products)
   static constexpr int tf = mr + kC * 65 * 4;      // [64][65] fp32 T
-  static constexpr int end2 = tf + kC * 65 * 4;
+  static constexpr int scr = tf + kC * 65 * 4;     // [4][16][17] fp32 per-wave scratch
+  static constexpr int end2 = scr + 4 * 16 * 17 * 4;
   static constexpr int total = end1 > end2 ? end1 : end2;
   static_assert(total <= 160 * 1024, "LDS");
 };
@@ -120,58 +212,39 @@ __global__ __launch_bounds__(256) void prep_kernel(BwdArgs a) {
   constexpr int PK = L::PK, PG = L::PG;
   __shared__ __attribute__((aligned(16))) unsigned char lds[L::total];
   float* G = reinterpret_cast<float*>(lds + L::g);
-  float* tot = reinterpret_cast<float*>(lds + L::tot);
   float* sb = reinterpret_cast<float*>(lds + L::bt);
+  bf16* sq = reinterpret_cast<bf16*>(lds + L::sq);
+  bf16* sk = reinterpret_cast<bf16*>(lds + L::sk);
   bf16* qs = reinterpret_cast<bf16*>(lds + L::qs);
   bf16* ks = reinterpret_cast<bf16*>(lds + L::ks);
   bf16* bop = reinterpret_cast<bf16*>(lds + L::bop);
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int lr = lane & 15, lq = lane >> 4;
   const int item = blockIdx.x;
   const int n = item % a.NT, head = item / a.NT;
   const int b = head / a.HV, hv = head - b * a.HV, hh = hv / (a.HV / a.H);
   const int t0 = n * kC, nrow = min(kC, a.T - t0);
-  const size_t qrow = (size_t)a.H * KT, grow = (size_t)a.HV * KT;
+  const unsigned qrow = (unsigned)(a.H * KT), grow = (unsigned)(a.HV * KT);
   const bf16* qb = a.q + ((size_t)b * a.T + t0) * qrow + (size_t)hh * KT;
   const bf16* kb = a.k + ((size_t)b * a.T + t0) * qrow + (size_t)hh * KT;
   const bf16* gb = a.g + ((size_t)b * a.T + t0) * grow + (size_t)hv * KT;
   unsigned char* blk = a.blocks + (size_t)item * P::bytes;
 
-  // G: each (16-token block, channel) scanned by one thread, then block prefixes added
-  for (int it = tid; it < 4 * KT; it += 256) {
-    const int wb = it / KT, c = it % KT;
-    float acc = 0.f;
-    for (int i = 0; i < 16; ++i) {
-      const int t = 16 * wb + i;
-      acc += t < nrow ? ldf(gb + (size_t)t * grow + c) : 0.f;
-      G[t * PG + c] = acc;
-    }
-    tot[wb * KT + c] = acc;
-  }
+  stage_qkg<KT>(sq, sk, G, PK, PG, qb, kb, gb, qrow, grow, nrow, tid);
   if (tid < kC) {
     const float bv = tid < nrow ? ldf(a.beta + ((size_t)b * a.T + t0 + tid) * a.HV + hv) : 0.f;
     sb[tid] = bv;
     reinterpret_cast<float*>(blk + P::beta)[tid] = bv;
   }
-  __syncthreads();
-  for (int it = tid; it < 4 * KT; it += 256) {
-    const int wb = it / KT, c = it % KT;
-    float pre = 0.f;
-    for (int j = 0; j < wb; ++j) pre += tot[j * KT + c];
-    for (int i = 0; i < 16; ++i) G[(16 * wb + i) * PG + c] += pre;
-  }
-  __syncthreads();
+  cumsum_rows<KT>(G, PG, reinterpret_cast<float*>(lds + L::tot), tid);  // includes barriers
 
   // operands of the row-block-w products, built by wave w
   {
     const int r0 = 16 * w;
     for (int u = lane; u < 16 * (KT / 8); u += 64) {  // q, k of block w relative to its first token
       const int i = r0 + u / (KT / 8), c8 = 8 * (u % (KT / 8));
-      bf16x8 qv{}, kv{};
-      if (i < nrow) {
-        qv = ld8(qb + (size_t)i * qrow + c8);
-        kv = ld8(kb + (size_t)i * qrow + c8);
-      }
+      const bf16x8 qv = ld8(sq + i * PK + c8), kv = ld8(sk + i * PK + c8);
       bf16x8 qo, ko;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -185,8 +258,7 @@ __global__ __launch_bounds__(256) void prep_kernel(BwdArgs a) {
     bf16* bw = bop + 8 * w * (w + 1) * PK;  // rows 0 .. 16w + 15
     for (int u = lane; u < 16 * (w + 1) * (KT / 8); u += 64) {
       const int j = u / (KT / 8), c8 = 8 * (u % (KT / 8));
-      bf16x8 kv{};
-      if (j < nrow) kv = ld8(kb + (size_t)j * qrow + c8);
+      const bf16x8 kv = ld8(sk + j * PK + c8);
       bf16x8 ko;
 #pragma unroll
       for (int e = 0; e < 8; ++e)
@@ -194,12 +266,13 @@ __global__ __launch_bounds__(256) void prep_kernel(BwdArgs a) {
       st8(bw + j * PK + c8, ko);
     }
   }
-  __syncthreads();
+  wave_sync();
 
-  // Aq and Mr row block w; tiles J <= w
+  // Aq and Mr row block w; tiles J <= w (operands are this wave's own)
   f32x4 aq[4], mr[4];
   {
     const bf16* bw = bop + 8 * w * (w + 1) * PK;
+#pragma unroll
     for (int J = 0; J < 4; ++J) {
       aq[J] = mr[J] = f32x4{0.f, 0.f, 0.f, 0.f};
       if (J <= w) {
@@ -211,37 +284,60 @@ __global__ __launch_bounds__(256) void prep_kernel(BwdArgs a) {
   __syncthreads();  // qs / ks / bop are dead from here; mr / tf reuse them
   float* smr = reinterpret_cast<float*>(lds + L::mr);
   float* stf = reinterpret_cast<float*>(lds + L::tf);
+  float* scr = reinterpret_cast<float*>(lds + L::scr) + w * 16 * 17;
   {
-    const int col = lane & 15, rq = 4 * (lane >> 4);
     bf16* aqt = reinterpret_cast<bf16*>(blk + P::aqt);
     float* gmr = reinterpret_cast<float*>(blk + P::mr);
+#pragma unroll
     for (int J = 0; J < 4; ++J) {
-      const int j = 16 * J + col;
+      const int j = 16 * J + lr;
       f32x4 av = aq[J], mv = mr[J];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int i = 16 * w + rq + r;
+        const int i = 16 * w + 4 * lq + r;
         if (j > i) av[r] = 0.f;
         if (j >= i) mv[r] = 0.f;
         smr[i * 65 + j] = mv[r];
-        gmr[i * kC + j] = mv[r];
+        stf[i * 65 + j] = 0.f;
       }
-      st4(aqt + j * kC + 16 * w + rq, av);  // Aq^T row j, tokens i .. i+3
+      st4(aqt + j * kC + 16 * w + 4 * lq, av);  // Aq^T row j, tokens i .. i+3
+#pragma unroll
+      for (int r = 0; r < 4; ++r) gmr[(16 * w + 4 * lq + r) * kC + j] = mv[r];
+    }
+  }
+  wave_sync();
+  // T = (I + diag(beta) Mr)^-1. Diagonal 16 x 16 blocks by forward substitution (wave w owns
+  // block w; lane: column lr, partial sums over rows j = lq mod 4) ...
+  {
+    const int o = 16 * w;
+    for (int ii = 0; ii < 16; ++ii) {
+      float s = 0.f;
+      for (int jj = lr + ((lq - lr) & 3); jj < ii; jj += 4)  // jj >= lr, jj = lq mod 4
+        s += smr[(o + ii) * 65 + o + jj] * stf[(o + jj) * 65 + o + lr];
+      s += __shfl_xor(s, 16);
+      s += __shfl_xor(s, 32);
+      if (lq == 0) stf[(o + ii) * 65 + o + lr] = lr == ii ? 1.f : (lr < ii ? -sb[o + ii] * s : 0.f);
+      wave_sync();
     }
   }
   __syncthreads();
-
-  // T = (I + diag(beta) Mr)^-1 by forward substitution, one row at a time
-  {
-    const int c = tid >> 2, p = tid & 3;
-    for (int i = 0; i < kC; ++i) {
-      float s = 0.f;
-      for (int j = c + p; j < i; j += 4) s += smr[i * 65 + j] * stf[j * 65 + c];
-      s += __shfl_xor(s, 1);
-      s += __shfl_xor(s, 2);
-      if (p == 0) stf[i * 65 + c] = c == i ? 1.f : (c < i ? -sb[i] * s : 0.f);
-      __syncthreads();
+  // ... then block row I, column J = I - d for d = 1, 2, 3:
+  // T_IJ = -T_II sum_{J <= L < I} diag(beta_I) Mr_IL T_LJ, on fp32 MFMA
+  for (int d = 1; d < 4; ++d) {
+    const int I = d + w, J = w;
+    if (I < 4) {
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int Lb = J; Lb < I; ++Lb)
+        mma16_nn(acc, smr + 16 * I * 65 + 16 * Lb, 65, stf + 16 * Lb * 65 + 16 * J, 65, 16, lane);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) scr[(4 * lq + r) * 17 + lr] = -sb[16 * I + 4 * lq + r] * acc[r];
+      wave_sync();
+      f32x4 t = f32x4{0.f, 0.f, 0.f, 0.f};
+      mma16_nn(t, stf + 16 * I * 65 + 16 * I, 65, scr, 17, 16, lane);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) stf[(16 * I + 4 * lq + r) * 65 + 16 * J + lr] = t[r];
     }
+    __syncthreads();
   }
   // T, T^T (bf16)
   {
@@ -266,8 +362,7 @@ __global__ __launch_bounds__(256) void prep_kernel(BwdArgs a) {
     bf16* kc = reinterpret_cast<bf16*>(blk + P::kc);
     for (int u = tid; u < kC * KT / 8; u += 256) {
       const int i = u / (KT / 8), c8 = 8 * (u % (KT / 8));
-      bf16x8 kv{};
-      if (i < nrow) kv = ld8(kb + (size_t)i * qrow + c8);
+      const bf16x8 kv = ld8(sk + i * PK + c8);
       bf16x8 x, y;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -288,8 +383,8 @@ __global__ __launch_bounds__(256) void prep_kernel(BwdArgs a) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int i = i8 + e;
-        const float kv = i < nrow ? ldf(kb + (size_t)i * qrow + c) : 0.f;
-        const float qv = i < nrow ? ldf(qb + (size_t)i * qrow + c) : 0.f;
+        const float kv = static_cast<float>(sk[i * PK + c]);
+        const float qv = static_cast<float>(sq[i * PK + c]);
         const float gi = G[i * PG + c];
         x[e] = static_cast<bf16>(kv * ex(gl - gi));
         y[e] = static_cast<bf16>(qv * ex(gi));
@@ -302,20 +397,12 @@ __global__ __launch_bounds__(256) void prep_kernel(BwdArgs a) {
   }
 }
 
-// Copies rows x cols bf16 (cols a multiple of 8) from a dense global tile into LDS with pitch ld.
-__device__ __forceinline__ void copy_tile(bf16* dst, int ld, const bf16* src, int rows, int cols,
-                                          int tid, int nthreads) {
-  const int per = cols / 8;
-  for (int u = tid; u < rows * per; u += nthreads) {
-    const int r = u / per, c8 = 8 * (u % per);
-    st8(dst + r * ld + c8, ld8(src + (size_t)r * cols + c8));
-  }
-}
-
-// ==================================================================== forward sweep
+// ==================================================================== sweeps
 // One workgroup of NW waves per (b, hv, 16 NW-column V tile); wave w owns 16 columns and
-// keeps their state h (K x 16, fp32) in MFMA accumulators. Per chunk: store h, then
-// W0 = V - Kg h, U = T (beta W0), h <- Gam_C h + Kc^T U.
+// keeps their K x 16 state (forward: h; reverse: dS) in fp32 MFMA accumulators. The sibling
+// V tiles of a head sit on one XCD (dispatch is round-robin over 8), so the chunk's factor
+// tiles come from HBM once per head. Each chunk's tiles are loaded into registers while the
+// previous chunk computes, then written to LDS.
 template <int KT, int NW>
 struct SweepLds {
   static constexpr int PK = KT + 8, BV = 16 * NW, PV = BV + 8;
@@ -343,16 +430,45 @@ struct SweepLds {
   static constexpr int dut = dst + BV * PK * 2;         // [BV][kPC] dU^T
   static constexpr int but = dut + BV * kPC * 2;        // [BV][kPC] (beta Ut)^T
   static constexpr int rev_total = but + BV * kPC * 2;
-  static constexpr int total = fwd_total > rev_total ? fwd_total : rev_total;
-  static_assert(total <= 160 * 1024, "LDS");
+  static_assert(fwd_total <= 160 * 1024 && rev_total <= 160 * 1024, "LDS");
 };
+
+__device__ __forceinline__ void sweep_tile(int nvt, int nh, int& head, int& vt_idx) {
+  if (nh % 8 == 0) {  // sibling V tiles of a head on one XCD
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    head = (slot / nvt) * 8 + xcd;
+    vt_idx = slot % nvt;
+  } else {
+    head = blockIdx.x / nvt;
+    vt_idx = blockIdx.x % nvt;
+  }
+}
+
+// this wave's 16 columns of a K x 16 state, held transposed in LDS (st[v][c], pitch pk),
+// to dst[c][v] (row pitch V) with 16-byte stores; columns past V are dropped
+template <int KT>
+__device__ __forceinline__ void store_state_tile(bf16* dst, int V, int vcol0, const bf16* st, int pk,
+                                                 int lane) {
+#pragma unroll
+  for (int e = 0; e < KT * 2 / 64; ++e) {
+    const int u = lane + 64 * e, c = u >> 1, h8 = 8 * (u & 1);
+    if (vcol0 + h8 < V) {
+      bf16x8 x;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = st[(h8 + j) * pk + c];
+      st8(dst + (size_t)c * V + vcol0 + h8, x);
+    }
+  }
+}
 
 template <int KT, int NW>
 __global__ __launch_bounds__(64 * NW) void fwd_sweep_kernel(BwdArgs a) {
   using L = SweepLds<KT, NW>;
   using P = PB<KT>;
-  constexpr int PK = L::PK, BV = L::BV, PV = L::PV, NCT = KT / 16;
-  __shared__ __attribute__((aligned(16))) unsigned char lds[L::total];
+  constexpr int PK = L::PK, BV = L::BV, PV = L::PV, NCT = KT / 16, NTH = 64 * NW;
+  constexpr int N1 = kC * KT / 8 / NTH, N2 = KT * kC / 8 / NTH, N3 = kC * kC / 8 / NTH;
+  constexpr int NV = (kC * BV / 8 + NTH - 1) / NTH;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[L::fwd_total];
   bf16* s_kg = reinterpret_cast<bf16*>(lds + L::kg);
   bf16* s_kct = reinterpret_cast<bf16*>(lds + L::kct);
   bf16* s_tm = reinterpret_cast<bf16*>(lds + L::tm);
@@ -366,11 +482,13 @@ __global__ __launch_bounds__(64 * NW) void fwd_sweep_kernel(BwdArgs a) {
   bf16* s_uu = reinterpret_cast<bf16*>(lds + L::uu) + 16 * w * kPC;
 
   const int nvt = (a.V + BV - 1) / BV;
-  const int head = blockIdx.x / nvt, vt_idx = blockIdx.x % nvt;
+  int head, vt_idx;
+  sweep_tile(nvt, a.B * a.HV, head, vt_idx);
   const int b = head / a.HV, hv = head - b * a.HV;
   const int V = a.V, T = a.T;
   const int vc = vt_idx * BV + 16 * w + lr;  // this lane's column
   const bool vok = vc < V;
+  const unsigned vrow = (unsigned)(a.HV * V);
 
   f32x4 S[NCT];
 #pragma unroll
@@ -381,41 +499,64 @@ __global__ __launch_bounds__(64 * NW) void fwd_sweep_kernel(BwdArgs a) {
       S[ct][r] = (a.s0 && vok) ? a.s0[((size_t)head * KT + c) * V + vc] : 0.f;
     }
 
-  for (int n = 0; n < a.NT; ++n) {
-    const int t0 = n * kC, nrow = min(kC, T - t0);
+  bf16x8 p1[N1], p2[N2], p3[N3], pv[NV];
+  float pgam = 0.f, pbt = 0.f;
+  auto fetch = [&](int n) {
     const unsigned char* blk = a.blocks + ((size_t)head * a.NT + n) * P::bytes;
-    __syncthreads();
-    for (int u = tid; u < kC * KT / 8; u += 64 * NW) {
-      const int r = u / (KT / 8), c8 = 8 * (u % (KT / 8));
-      st8(s_kg + r * PK + c8, ld8(blk + P::kg + (r * KT + c8) * 2));
-    }
-    for (int u = tid; u < KT * kC / 8; u += 64 * NW) {
-      const int r = u / 8, c8 = 8 * (u % 8);
-      st8(s_kct + r * kPC + c8, ld8(blk + P::kct + (r * kC + c8) * 2));
-    }
-    for (int u = tid; u < kC * kC / 8; u += 64 * NW) {
-      const int r = u / 8, c8 = 8 * (u % 8);
-      st8(s_tm + r * kPC + c8, ld8(blk + P::tm + (r * kC + c8) * 2));
-    }
-    for (int u = tid; u < KT; u += 64 * NW) s_gam[u] = reinterpret_cast<const float*>(blk + P::gam)[u];
-    for (int u = tid; u < kC; u += 64 * NW) s_bt[u] = reinterpret_cast<const float*>(blk + P::beta)[u];
-    for (int u = tid; u < kC * BV / 8; u += 64 * NW) {  // v tile, zeros past T or V
-      const int r = u / (BV / 8), c8 = 8 * (u % (BV / 8));
-      const int col = vt_idx * BV + c8;
-      bf16x8 x{};
-      if (r < nrow && col < V) x = ld8(a.v + (((size_t)b * T + t0 + r) * a.HV + hv) * V + col);
-      st8(s_vt + r * PV + c8, x);
-    }
-    // h of this chunk: to the workspace (bf16, [K][V]) and transposed into LDS
-    bf16* hg = a.h + ((size_t)head * a.NT + n) * KT * V;
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      st4(s_ht + lr * PK + 16 * ct + 4 * lq, S[ct]);
-      if (vok)
+    for (int e = 0; e < N1; ++e) p1[e] = ld8(blk + P::kg + 16 * (tid + NTH * e));
 #pragma unroll
-        for (int r = 0; r < 4; ++r) hg[(size_t)(16 * ct + 4 * lq + r) * V + vc] = static_cast<bf16>(S[ct][r]);
+    for (int e = 0; e < N2; ++e) p2[e] = ld8(blk + P::kct + 16 * (tid + NTH * e));
+#pragma unroll
+    for (int e = 0; e < N3; ++e) p3[e] = ld8(blk + P::tm + 16 * (tid + NTH * e));
+    if (tid < KT) pgam = reinterpret_cast<const float*>(blk + P::gam)[tid];
+    if (tid < kC) pbt = reinterpret_cast<const float*>(blk + P::beta)[tid];
+    const int t0 = n * kC, nrow = min(kC, T - t0);
+    const auto rv = rsrc(a.v + ((size_t)b * T + t0) * vrow + (size_t)hv * V,
+                         ((unsigned)(nrow - 1) * vrow + V) * 2);
+#pragma unroll
+    for (int e = 0; e < NV; ++e) {
+      const int u = tid + NTH * e, r = u / (BV / 8), col = vt_idx * BV + 8 * (u % (BV / 8));
+      const unsigned off = (u < kC * BV / 8 && col < V) ? (r * vrow + col) * 2 : 0x80000000u;
+      pv[e] = bload8(rv, off);
     }
+  };
+  auto put = [&]() {
+#pragma unroll
+    for (int e = 0; e < N1; ++e) {
+      const int u = tid + NTH * e, r = u / (KT / 8), c8 = 8 * (u % (KT / 8));
+      st8(s_kg + r * PK + c8, p1[e]);
+    }
+#pragma unroll
+    for (int e = 0; e < N2; ++e) {
+      const int u = tid + NTH * e, r = u / 8, c8 = 8 * (u % 8);
+      st8(s_kct + r * kPC + c8, p2[e]);
+    }
+#pragma unroll
+    for (int e = 0; e < N3; ++e) {
+      const int u = tid + NTH * e, r = u / 8, c8 = 8 * (u % 8);
+      st8(s_tm + r * kPC + c8, p3[e]);
+    }
+    if (tid < KT) s_gam[tid] = pgam;
+    if (tid < kC) s_bt[tid] = pbt;
+#pragma unroll
+    for (int e = 0; e < NV; ++e) {
+      const int u = tid + NTH * e, r = u / (BV / 8), c8 = 8 * (u % (BV / 8));
+      if (u < kC * BV / 8) st8(s_vt + r * PV + c8, pv[e]);
+    }
+  };
+
+  fetch(0);
+  for (int n = 0; n < a.NT; ++n) {
     __syncthreads();
+    put();
+    // h of this chunk, transposed into this wave's LDS rows
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) st4(s_ht + lr * PK + 16 * ct + 4 * lq, S[ct]);
+    if (n + 1 < a.NT) fetch(n + 1);
+    __syncthreads();
+    store_state_tile<KT>(a.h + ((size_t)head * a.NT + n) * KT * V, V, vt_idx * BV + 16 * w, s_ht,
+                         PK, lane);
     // X = Kg h, W0 = V - X, Y = beta W0
     const size_t trow = ((size_t)head * a.NT + n) * kC;
 #pragma unroll
@@ -452,13 +593,14 @@ __global__ __launch_bounds__(64 * NW) void fwd_sweep_kernel(BwdArgs a) {
   }
 }
 
-// ==================================================================== reverse sweep
 template <int KT, int NW>
 __global__ __launch_bounds__(64 * NW) void rev_sweep_kernel(BwdArgs a) {
   using L = SweepLds<KT, NW>;
   using P = PB<KT>;
-  constexpr int PK = L::PK, BV = L::BV, NCT = KT / 16;
-  __shared__ __attribute__((aligned(16))) unsigned char lds[L::total];
+  constexpr int PK = L::PK, BV = L::BV, NCT = KT / 16, NTH = 64 * NW;
+  constexpr int N1 = kC * KT / 8 / NTH, N2 = KT * kC / 8 / NTH, N3 = kC * kC / 8 / NTH;
+  constexpr int ND = (kC * BV / 8 + NTH - 1) / NTH;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[L::rev_total];
   bf16* s_kc = reinterpret_cast<bf16*>(lds + L::kc);
   bf16* s_qgt = reinterpret_cast<bf16*>(lds + L::qgt);
   bf16* s_kgt = reinterpret_cast<bf16*>(lds + L::kgt);
@@ -475,11 +617,13 @@ __global__ __launch_bounds__(64 * NW) void rev_sweep_kernel(BwdArgs a) {
   bf16* s_dow = s_dot + 16 * w * kPC;
 
   const int nvt = (a.V + BV - 1) / BV;
-  const int head = blockIdx.x / nvt, vt_idx = blockIdx.x % nvt;
+  int head, vt_idx;
+  sweep_tile(nvt, a.B * a.HV, head, vt_idx);
   const int b = head / a.HV, hv = head - b * a.HV;
   const int V = a.V, T = a.T;
   const int vc = vt_idx * BV + 16 * w + lr;
   const bool vok = vc < V;
+  const unsigned vrow = (unsigned)(a.HV * V);
 
   f32x4 D[NCT];
 #pragma unroll
@@ -490,47 +634,74 @@ __global__ __launch_bounds__(64 * NW) void rev_sweep_kernel(BwdArgs a) {
       D[ct][r] = (a.dht && vok) ? a.dht[((size_t)head * KT + c) * V + vc] : 0.f;
     }
 
-  for (int n = a.NT - 1; n >= 0; --n) {
-    const int t0 = n * kC, nrow = min(kC, T - t0);
+  bf16x8 p1[N1], p2[N2], p3[N2], p4[N3], p5[N3], pd[ND];
+  float pgam = 0.f, pbt = 0.f;
+  auto fetch = [&](int n) {
     const unsigned char* blk = a.blocks + ((size_t)head * a.NT + n) * P::bytes;
+#pragma unroll
+    for (int e = 0; e < N1; ++e) p1[e] = ld8(blk + P::kc + 16 * (tid + NTH * e));
+#pragma unroll
+    for (int e = 0; e < N2; ++e) {
+      p2[e] = ld8(blk + P::qgt + 16 * (tid + NTH * e));
+      p3[e] = ld8(blk + P::kgt + 16 * (tid + NTH * e));
+    }
+#pragma unroll
+    for (int e = 0; e < N3; ++e) {
+      p4[e] = ld8(blk + P::tt + 16 * (tid + NTH * e));
+      p5[e] = ld8(blk + P::aqt + 16 * (tid + NTH * e));
+    }
+    if (tid < KT) pgam = reinterpret_cast<const float*>(blk + P::gam)[tid];
+    if (tid < kC) pbt = reinterpret_cast<const float*>(blk + P::beta)[tid];
+    const int t0 = n * kC, nrow = min(kC, T - t0);
+    const auto rd = rsrc(a.dout + ((size_t)b * T + t0) * vrow + (size_t)hv * V,
+                         ((unsigned)(nrow - 1) * vrow + V) * 2);
+#pragma unroll
+    for (int e = 0; e < ND; ++e) {
+      const int u = tid + NTH * e, r = u / (BV / 8), col = vt_idx * BV + 8 * (u % (BV / 8));
+      const unsigned off = (u < kC * BV / 8 && col < V) ? (r * vrow + col) * 2 : 0x80000000u;
+      pd[e] = bload8(rd, off);
+    }
+  };
+  auto put = [&]() {
+#pragma unroll
+    for (int e = 0; e < N1; ++e) {
+      const int u = tid + NTH * e, r = u / (KT / 8), c8 = 8 * (u % (KT / 8));
+      st8(s_kc + r * PK + c8, p1[e]);
+    }
+#pragma unroll
+    for (int e = 0; e < N2; ++e) {
+      const int u = tid + NTH * e, r = u / 8, c8 = 8 * (u % 8);
+      st8(s_qgt + r * kPC + c8, p2[e]);
+      st8(s_kgt + r * kPC + c8, p3[e]);
+    }
+#pragma unroll
+    for (int e = 0; e < N3; ++e) {
+      const int u = tid + NTH * e, r = u / 8, c8 = 8 * (u % 8);
+      st8(s_tt + r * kPC + c8, p4[e]);
+      st8(s_aqt + r * kPC + c8, p5[e]);
+    }
+    if (tid < KT) s_gam[tid] = pgam;
+    if (tid < kC) s_bt[tid] = pbt;
+#pragma unroll
+    for (int e = 0; e < ND; ++e) {  // dO tile, written transposed: dO^T[v][token]
+      const int u = tid + NTH * e, r = u / (BV / 8), c8 = 8 * (u % (BV / 8));
+      if (u < kC * BV / 8)
+#pragma unroll
+        for (int x = 0; x < 8; ++x) s_dot[(c8 + x) * kPC + r] = pd[e][x];
+    }
+  };
+
+  fetch(a.NT - 1);
+  for (int n = a.NT - 1; n >= 0; --n) {
     __syncthreads();
-    for (int u = tid; u < kC * KT / 8; u += 64 * NW) {
-      const int r = u / (KT / 8), c8 = 8 * (u % (KT / 8));
-      st8(s_kc + r * PK + c8, ld8(blk + P::kc + (r * KT + c8) * 2));
-    }
-    for (int u = tid; u < KT * kC / 8; u += 64 * NW) {
-      const int r = u / 8, c8 = 8 * (u % 8);
-      st8(s_qgt + r * kPC + c8, ld8(blk + P::qgt + (r * kC + c8) * 2));
-      st8(s_kgt + r * kPC + c8, ld8(blk + P::kgt + (r * kC + c8) * 2));
-    }
-    for (int u = tid; u < kC * kC / 8; u += 64 * NW) {
-      const int r = u / 8, c8 = 8 * (u % 8);
-      st8(s_tt + r * kPC + c8, ld8(blk + P::tt + (r * kC + c8) * 2));
-      st8(s_aqt + r * kPC + c8, ld8(blk + P::aqt + (r * kC + c8) * 2));
-    }
-    for (int u = tid; u < KT; u += 64 * NW) s_gam[u] = reinterpret_cast<const float*>(blk + P::gam)[u];
-    for (int u = tid; u < kC; u += 64 * NW) s_bt[u] = reinterpret_cast<const float*>(blk + P::beta)[u];
-    // dO^T of the tile: lane (lr, lq) of wave w reads tokens 4 lq .. + 3 (+16 I) of its column
+    put();
+    // dS reaching the state that leaves this chunk, transposed into this wave's LDS rows
 #pragma unroll
-    for (int I = 0; I < 4; ++I) {
-      bf16x4 x;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = 16 * I + 4 * lq + r;
-        x[r] = (i < nrow && vok) ? a.dout[(((size_t)b * T + t0 + i) * a.HV + hv) * V + vc] : static_cast<bf16>(0.f);
-      }
-      *reinterpret_cast<bf16x4*>(s_dow + lr * kPC + 16 * I + 4 * lq) = x;
-    }
-    // dS reaching the state that leaves this chunk: to the workspace, and transposed into LDS
-    bf16* dg_ = a.dsn + ((size_t)head * a.NT + n) * KT * V;
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      st4(s_dst + lr * PK + 16 * ct + 4 * lq, D[ct]);
-      if (vok)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) dg_[(size_t)(16 * ct + 4 * lq + r) * V + vc] = static_cast<bf16>(D[ct][r]);
-    }
+    for (int ct = 0; ct < NCT; ++ct) st4(s_dst + lr * PK + 16 * ct + 4 * lq, D[ct]);
+    if (n > 0) fetch(n - 1);
     __syncthreads();
+    store_state_tile<KT>(a.dsn + ((size_t)head * a.NT + n) * KT * V, V, vt_idx * BV + 16 * w,
+                         s_dst, PK, lane);
     // dU = scale Aq^T dO + Kc dS
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
@@ -539,7 +710,7 @@ __global__ __launch_bounds__(64 * NW) void rev_sweep_kernel(BwdArgs a) {
       mma16(q, s_kc + 16 * I * PK, PK, s_dst, PK, KT, lane);
       st4(s_dut + lr * kPC + 16 * I + 4 * lq, a.scale * p + q);
     }
-    // Ut = T^T dU; dv = beta Ut
+    // Ut = T^T dU; beta Ut
     const size_t trow = ((size_t)head * a.NT + n) * kC;
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
@@ -576,25 +747,26 @@ template <int KT>
 struct LocalLds {
   static constexpr int PK = KT + 8, PG = KT + 4, PV = 128 + 8;
   static constexpr int g = 0;                      // [64][PG] fp32 G (all phases)
-  static constexpr int bt = g + kC * PG * 4;       // [64] fp32 beta
+  static constexpr int sq = g + kC * PG * 4;       // [64][PK] bf16 q
+  static constexpr int sk = sq + kC * PK * 2;      // [64][PK] bf16 k
+  static constexpr int bt = sk + kC * PK * 2;      // [64] fp32 beta
   static constexpr int db1 = bt + kC * 4;          // [64] fp32 Ut . W0
-  static constexpr int db2 = db1 + kC * 4;         // [4][64] fp32 partial sum_j -D Mr per wave? (row-owned)
+  static constexpr int db2 = db1 + kC * 4;         // [64] fp32 sum_j -D Mr
   static constexpr int lx = db2 + kC * 4;          // [4][KT] fp32 last-token terms per wave
   static constexpr int lx2 = lx + 4 * KT * 4;      // [KT] fp32 Gam_C rowsum(dS h)
-  static constexpr int ph = lx2 + KT * 4;          // phase region
+  static constexpr int tot = lx2 + KT * 4;         // [4][KT] fp32 cumsum scratch
+  static constexpr int ph = tot + 4 * KT * 4;      // phase region
   // phase 1
   static constexpr int uu = ph;                    // [64][PV] U
-  static constexpr int ut = uu + kC * PV * 2;      // [64][PV] Ut
-  static constexpr int dO = ut + kC * PV * 2;      // [64][PV] dO
-  static constexpr int hs = dO + kC * PV * 2;      // [KT][PV] h, then dS
+  static constexpr int hs = uu + kC * PV * 2;      // [KT][PV] h, then dS
   static constexpr int end1 = hs + KT * PV * 2;
   // phase 2
   static constexpr int f = ph;                     // [64][kPC] F
   static constexpr int ft = f + kC * kPC * 2;      // [64][kPC] F^T
   static constexpr int e = ft + kC * kPC * 2;      // [64][kPC] E
   static constexpr int et = e + kC * kPC * 2;      // [64][kPC] E^T
-  static constexpr int wop = et + kC * kPC * 2;    // [4][KT][kPC] per-wave operand
-  static constexpr int end2 = wop + 4 * KT * kPC * 2;
+  static constexpr int wop = et + kC * kPC * 2;    // [4][64][kPC] per wave: 32 channels hi, 32 lo
+  static constexpr int end2 = wop + 4 * 64 * kPC * 2;
   // phase 3
   static constexpr int dgs = ph;                   // [64][PG] fp32 dG
   static constexpr int end3 = dgs + kC * PG * 4;
@@ -606,9 +778,11 @@ template <int KT>
 __global__ __launch_bounds__(256) void local_kernel(BwdArgs a) {
   using L = LocalLds<KT>;
   using P = PB<KT>;
-  constexpr int PG = L::PG, PV = L::PV, NCT = KT / 16;
+  constexpr int PK = L::PK, PG = L::PG, PV = L::PV, NCT = KT / 16;
   __shared__ __attribute__((aligned(16))) unsigned char lds[L::total];
   float* G = reinterpret_cast<float*>(lds + L::g);
+  bf16* sq = reinterpret_cast<bf16*>(lds + L::sq);
+  bf16* sk = reinterpret_cast<bf16*>(lds + L::sk);
   float* sb = reinterpret_cast<float*>(lds + L::bt);
   float* db1 = reinterpret_cast<float*>(lds + L::db1);
   float* db2 = reinterpret_cast<float*>(lds + L::db2);
@@ -622,7 +796,7 @@ __global__ __launch_bounds__(256) void local_kernel(BwdArgs a) {
   const int b = head / a.HV, hv = head - b * a.HV, hh = hv / (a.HV / a.H);
   const int V = a.V, T = a.T;
   const int t0 = n * kC, nrow = min(kC, T - t0);
-  const size_t qrow = (size_t)a.H * KT, grow = (size_t)a.HV * KT;
+  const unsigned qrow = (unsigned)(a.H * KT), grow = (unsigned)(a.HV * KT);
   const bf16* qb = a.q + ((size_t)b * T + t0) * qrow + (size_t)hh * KT;
   const bf16* kb = a.k + ((size_t)b * T + t0) * qrow + (size_t)hh * KT;
   const bf16* gb = a.g + ((size_t)b * T + t0) * grow + (size_t)hv * KT;
@@ -630,101 +804,113 @@ __global__ __launch_bounds__(256) void local_kernel(BwdArgs a) {
   const size_t trow = ((size_t)head * a.NT + n) * kC;
   const bf16* hsrc = a.h + ((size_t)head * a.NT + n) * KT * V;
   const bf16* dsrc = a.dsn + ((size_t)head * a.NT + n) * KT * V;
+  const int rw = 16 * w, ew = 16 * w + 15;  // first and last token of this wave's block
+  const unsigned vrow = (unsigned)(a.HV * V);
 
-  // G (recomputed as in prep), beta
+  // this wave's rows of dO and Ut (and W0) as MFMA A operands, straight from memory
+  bf16x8 fdo[4], fut[4], fw0[4];
   {
-    float* tot = reinterpret_cast<float*>(lds + L::ph);  // scratch before phase 1
-    for (int it = tid; it < 4 * KT; it += 256) {
-      const int wb = it / KT, c = it % KT;
-      float acc = 0.f;
-      for (int i = 0; i < 16; ++i) {
-        const int t = 16 * wb + i;
-        acc += t < nrow ? ldf(gb + (size_t)t * grow + c) : 0.f;
-        G[t * PG + c] = acc;
-      }
-      tot[wb * KT + c] = acc;
+    const auto rdo = rsrc(a.dout + ((size_t)b * T + t0) * vrow + (size_t)hv * V,
+                          ((unsigned)(nrow - 1) * vrow + V) * 2);
+    const int row = rw + lr;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int k0 = 32 * s + 8 * lq;
+      const bool ok = k0 < V;
+      fdo[s] = ok ? bload8(rdo, (row * vrow + k0) * 2) : bf16x8{};
+      fut[s] = ok ? ld8(a.ut + (trow + row) * V + k0) : bf16x8{};
+      fw0[s] = ok ? ld8(a.w0 + (trow + row) * V + k0) : bf16x8{};
     }
-    if (tid < kC) sb[tid] = reinterpret_cast<const float*>(blk + P::beta)[tid];
-    __syncthreads();
-    for (int it = tid; it < 4 * KT; it += 256) {
-      const int wb = it / KT, c = it % KT;
-      float pre = 0.f;
-      for (int j = 0; j < wb; ++j) pre += tot[j * KT + c];
-      for (int i = 0; i < 16; ++i) G[(16 * wb + i) * PG + c] += pre;
-    }
-    __syncthreads();
   }
-
+  stage_qkg<KT>(sq, sk, G, PK, PG, qb, kb, gb, qrow, grow, nrow, tid);
+  if (tid < kC) sb[tid] = reinterpret_cast<const float*>(blk + P::beta)[tid];
   // ---------------- phase 1: products contracting over V
   bf16* s_u = reinterpret_cast<bf16*>(lds + L::uu);
-  bf16* s_ut = reinterpret_cast<bf16*>(lds + L::ut);
-  bf16* s_do = reinterpret_cast<bf16*>(lds + L::dO);
   bf16* s_hs = reinterpret_cast<bf16*>(lds + L::hs);
-  for (int u = tid; u < kC * (V / 8); u += 256) {
-    const int r = u / (V / 8), c8 = 8 * (u % (V / 8));
-    st8(s_u + r * PV + c8, ld8(a.u + (trow + r) * V + c8));
-    st8(s_ut + r * PV + c8, ld8(a.ut + (trow + r) * V + c8));
-    bf16x8 x{};
-    if (r < nrow) x = ld8(a.dout + (((size_t)b * T + t0 + r) * a.HV + hv) * V + c8);
-    st8(s_do + r * PV + c8, x);
-  }
-  for (int u = tid; u < KT * (V / 8); u += 256) {
-    const int r = u / (V / 8), c8 = 8 * (u % (V / 8));
-    st8(s_hs + r * PV + c8, ld8(hsrc + (size_t)r * V + c8));
-  }
-  // Gam_C rowsum(dS * h), per channel, straight from the workspace
-  for (int c = tid; c < KT; c += 256) {
-    float s = 0.f;
-    for (int v8 = 0; v8 < V; v8 += 8) {
-      const bf16x8 x = ld8(hsrc + (size_t)c * V + v8), y = ld8(dsrc + (size_t)c * V + v8);
+  {
+    constexpr int NU = kC * 16 / 256, NH = KT * 16 / 256;  // 8-column pieces at V = 128
+    bf16x8 xu[NU], xh[NH];
+    const int per = V / 8;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) s += static_cast<float>(x[e]) * static_cast<float>(y[e]);
+    for (int e = 0; e < NU; ++e) {
+      const int u = tid + 256 * e, r = u / per, c8 = 8 * (u % per);
+      xu[e] = u < kC * per ? ld8(a.u + (trow + r) * V + c8) : bf16x8{};
     }
-    lx2[c] = ex(G[(kC - 1) * PG + c]) * s;
+#pragma unroll
+    for (int e = 0; e < NH; ++e) {
+      const int u = tid + 256 * e, r = u / per, c8 = 8 * (u % per);
+      xh[e] = u < KT * per ? ld8(hsrc + (size_t)r * V + c8) : bf16x8{};
+    }
+#pragma unroll
+    for (int e = 0; e < NU; ++e) {
+      const int u = tid + 256 * e, r = u / per, c8 = 8 * (u % per);
+      if (u < kC * per) st8(s_u + r * PV + c8, xu[e]);
+    }
+#pragma unroll
+    for (int e = 0; e < NH; ++e) {
+      const int u = tid + 256 * e, r = u / per, c8 = 8 * (u % per);
+      if (u < KT * per) st8(s_hs + r * PV + c8, xh[e]);
+    }
   }
-  __syncthreads();
+  cumsum_rows<KT>(G, PG, reinterpret_cast<float*>(lds + L::tot), tid);  // includes barriers
 
-  const int rw = 16 * w, ew = 16 * w + 15;  // first and last token of this wave's block
+  if (tid < KT) lx2[tid] = 0.f;  // Gam_C rowsum(dS * h), accumulated when dS arrives
+  // dbeta, first term: Ut_i . W0_i for this wave's rows
+  {
+    float s = 0.f;
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s += static_cast<float>(fut[x][e]) * static_cast<float>(fw0[x][e]);
+    s += __shfl_xor(s, 16);
+    s += __shfl_xor(s, 32);
+    if (lq == 0) db1[rw + lr] = s;
+  }
   f32x4 Dm[4], Fo[4];
 #pragma unroll
   for (int J = 0; J < 4; ++J) {
     Dm[J] = Fo[J] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (J <= w) {
-      mma16(Dm[J], s_ut + rw * PV, PV, s_u + 16 * J * PV, PV, V, lane);
-      mma16(Fo[J], s_do + rw * PV, PV, s_u + 16 * J * PV, PV, V, lane);
+      mma_ra(Dm[J], fut, s_u + 16 * J * PV, PV, V, lane);
+      mma_ra(Fo[J], fdo, s_u + 16 * J * PV, PV, V, lane);
     }
   }
   f32x4 adq[NCT], arow[NCT], acol[NCT];
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) {
-    adq[ct] = arow[ct] = acol[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-    mma16(adq[ct], s_do + rw * PV, PV, s_hs + 16 * ct * PV, PV, V, lane);
-    mma16(arow[ct], s_ut + rw * PV, PV, s_hs + 16 * ct * PV, PV, V, lane);
+    adq[ct] = arow[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    mma_ra(adq[ct], fdo, s_hs + 16 * ct * PV, PV, V, lane);
+    mma_ra(arow[ct], fut, s_hs + 16 * ct * PV, PV, V, lane);
     const int c = 16 * ct + lr;
     const float er = ex(G[rw * PG + c]);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      adq[ct][r] *= a.scale * er;                     // scale dO h^T, times exp(G_r)
-      arow[ct][r] *= -sb[rw + 4 * lq + r] * er;        // -(beta Ut) h^T, times exp(G_r)
+      adq[ct][r] *= a.scale * er;                 // scale dO h^T, times exp(G_rw)
+      arow[ct][r] *= -sb[rw + 4 * lq + r] * er;    // -(beta Ut) h^T, times exp(G_rw)
     }
   }
-  __syncthreads();
-  for (int u = tid; u < KT * (V / 8); u += 256) {
-    const int r = u / (V / 8), c8 = 8 * (u % (V / 8));
-    st8(s_hs + r * PV + c8, ld8(dsrc + (size_t)r * V + c8));
-  }
-  // dbeta, first term: Ut_i . W0_i (4 threads per token)
   {
-    const int i = tid >> 2, p = tid & 3;
-    float s = 0.f;
-    for (int v8 = 8 * p; v8 < V; v8 += 32) {
-      const bf16x8 x = ld8(s_ut + i * PV + v8), y = ld8(a.w0 + (trow + i) * V + v8);
+    constexpr int NH = KT * 16 / 256;
+    bf16x8 xh[NH];
+    const int per = V / 8;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) s += static_cast<float>(x[e]) * static_cast<float>(y[e]);
+    for (int e = 0; e < NH; ++e) {
+      const int u = tid + 256 * e, r = u / per, c8 = 8 * (u % per);
+      xh[e] = u < KT * per ? ld8(dsrc + (size_t)r * V + c8) : bf16x8{};
     }
-    s += __shfl_xor(s, 1);
-    s += __shfl_xor(s, 2);
-    if (p == 0) db1[i] = s;
+    __syncthreads();  // every wave is done with h
+#pragma unroll
+    for (int e = 0; e < NH; ++e) {
+      const int u = tid + 256 * e, r = u / per, c8 = 8 * (u % per);
+      if (u < KT * per) {
+        const bf16x8 hv8 = ld8(s_hs + r * PV + c8);
+        float sdot = 0.f;
+#pragma unroll
+        for (int x = 0; x < 8; ++x) sdot += static_cast<float>(hv8[x]) * static_cast<float>(xh[e][x]);
+        atomicAdd(lx2 + r, sdot);
+        st8(s_hs + r * PV + c8, xh[e]);
+      }
+    }
   }
   __syncthreads();
 #pragma unroll
@@ -737,14 +923,12 @@ __global__ __launch_bounds__(256) void local_kernel(BwdArgs a) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int j = rw + 4 * lq + r;
-      const float kv = j < nrow ? ldf(kb + (size_t)j * qrow + c) : 0.f;
-      part += kv * ex(gl - G[j * PG + c]) * x[r];  // last-token term of dG
+      part += static_cast<float>(sk[j * PK + c]) * ex(gl - G[j * PG + c]) * x[r];  // last-token term
     }
     part += __shfl_xor(part, 16);
     part += __shfl_xor(part, 32);
     if (lq == 0) lx[w * KT + c] = part;
-    const float f = ex(gl - G[ew * PG + c]);
-    acol[ct] = x * f;  // U dS^T times exp(G_C - G_ew); the output factor exp(G_ew - G_j) completes Gam_C/Gam_j
+    acol[ct] = x * ex(gl - G[ew * PG + c]);  // U dS^T exp(G_C - G_ew); exp(G_ew - G_j) follows
   }
   // dbeta, second term: sum_j (-Ut U^T)_ij Mr_ij, rows of this wave
   {
@@ -775,7 +959,6 @@ __global__ __launch_bounds__(256) void local_kernel(BwdArgs a) {
   bf16* s_ft = reinterpret_cast<bf16*>(lds + L::ft);
   bf16* s_e = reinterpret_cast<bf16*>(lds + L::e);
   bf16* s_et = reinterpret_cast<bf16*>(lds + L::et);
-  bf16* s_op = reinterpret_cast<bf16*>(lds + L::wop) + w * KT * kPC;
 #pragma unroll
   for (int J = 0; J < 4; ++J) {
     const int j = 16 * J + lr;
@@ -796,10 +979,10 @@ __global__ __launch_bounds__(256) void local_kernel(BwdArgs a) {
   // The scaled q / k operand goes in as a bf16 pair hi + lo (two products): the gradient terms
   // of Aq and Mr enter dG once through each role with opposite signs and cancel in the
   // reverse cumsum, which plain bf16 rounding of this operand (different in each role) would
-  // not preserve. F and E are rounded once and shared by both roles. Half the channels at a time.
-  constexpr int KH = KT / 2, NCH = NCT / 2;
-  bf16* s_hi = s_op;
-  bf16* s_lo = s_op + KH * kPC;
+  // not preserve. F and E are rounded once and shared by both roles. The operand is built by
+  // this wave alone, 32 channels at a time, in its own LDS slot.
+  bf16* s_hi = reinterpret_cast<bf16*>(lds + L::wop) + w * 64 * kPC;
+  bf16* s_lo = s_hi + 32 * kPC;
   // role 0: row role against reference rw over tokens 0 .. ew, operand k_j exp(G_rw - G_j)
   // role 1 / 2: column role against reference ew over tokens rw .. 63, operand
   //             q_i exp(G_i - G_ew) (with F^T) / k_i exp(G_i - G_ew) (with E^T)
@@ -807,17 +990,17 @@ __global__ __launch_bounds__(256) void local_kernel(BwdArgs a) {
     const int first = role == 0 ? 0 : rw;
     const int ntok = role == 0 ? 16 * (w + 1) : kC - rw;
     const int ref = role == 0 ? rw : ew;
-    const bf16* src = role == 1 ? qb : kb;
-    for (int half = 0; half < 2; ++half) {
-      for (int u = lane; u < KH * (ntok / 8); u += 64) {
-        const int cl = u % KH, c = half * KH + cl, j8 = 8 * (u / KH);
+    const bf16* src = role == 1 ? sq : sk;
+    for (int part = 0; part < KT / 32; ++part) {
+      for (int u = lane; u < 32 * (ntok / 8); u += 64) {
+        const int cl = u % 32, c = 32 * part + cl, j8 = 8 * (u / 32);
+        const float gref = G[ref * PG + c];
         bf16x8 xh, xl;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int j = first + j8 + e;
-          const float yv = j < nrow ? ldf(src + (size_t)j * qrow + c) : 0.f;
-          const float d = role == 0 ? G[ref * PG + c] - G[j * PG + c] : G[j * PG + c] - G[ref * PG + c];
-          const float x = yv * ex(d);
+          const float d = role == 0 ? gref - G[j * PG + c] : G[j * PG + c] - gref;
+          const float x = static_cast<float>(src[j * PK + c]) * ex(d);
           const bf16 hi = static_cast<bf16>(x);
           xh[e] = hi;
           xl[e] = static_cast<bf16>(x - static_cast<float>(hi));
@@ -825,10 +1008,10 @@ __global__ __launch_bounds__(256) void local_kernel(BwdArgs a) {
         st8(s_hi + cl * kPC + j8, xh);
         st8(s_lo + cl * kPC + j8, xl);
       }
-      __syncthreads();
+      wave_sync();
 #pragma unroll
-      for (int cc = 0; cc < NCH; ++cc) {
-        const int ct = half * NCH + cc;
+      for (int cc = 0; cc < 2; ++cc) {
+        const int ct = 2 * part + cc;
         const bf16* bh = s_hi + 16 * cc * kPC;
         const bf16* bl = s_lo + 16 * cc * kPC;
         if (role == 0) {
@@ -842,9 +1025,10 @@ __global__ __launch_bounds__(256) void local_kernel(BwdArgs a) {
           mma16(acol[ct], xa, kPC, bl, kPC, ntok, lane);
         }
       }
-      __syncthreads();
+      wave_sync();
     }
   }
+  __syncthreads();  // phase 2 operands are dead
 
   // ---------------- phase 3: output factors, dq, dk, dG, then dg by a reverse scan
   float* dgs = reinterpret_cast<float*>(lds + L::dgs);
@@ -861,11 +1045,10 @@ __global__ __launch_bounds__(256) void local_kernel(BwdArgs a) {
       const float dq = adq[ct][r] * fr;
       const float dpos = arow[ct][r] * fr, dneg = acol[ct][r] * fc;
       const float dk = dpos + dneg;
-      const bool ok = i < nrow;
-      const float qv = ok ? ldf(qb + (size_t)i * qrow + c) : 0.f;
-      const float kv = ok ? ldf(kb + (size_t)i * qrow + c) : 0.f;
+      const float qv = static_cast<float>(sq[i * PK + c]);
+      const float kv = static_cast<float>(sk[i * PK + c]);
       dgs[i * PG + c] = qv * dq + kv * (dpos - dneg);
-      if (ok) {
+      if (i < nrow) {
         const size_t t = (size_t)b * T + t0 + i;
         if (G_ == 1) {
           a.dq[(t * a.H + hh) * KT + c] = static_cast<bf16>(dq);
@@ -879,19 +1062,26 @@ __global__ __launch_bounds__(256) void local_kernel(BwdArgs a) {
   }
   __syncthreads();
   for (int c = tid; c < KT; c += 256) {
-    float run = lx[c] + lx[KT + c] + lx[2 * KT + c] + lx[3 * KT + c] + lx2[c];
+    float run = lx[c] + lx[KT + c] + lx[2 * KT + c] + lx[3 * KT + c] + ex(G[(kC - 1) * PG + c]) * lx2[c];
     for (int i = kC - 1; i >= 0; --i) {
       run += dgs[i * PG + c];
       if (i < nrow) a.dg[(((size_t)b * T + t0 + i) * a.HV + hv) * KT + c] = static_cast<bf16>(run);
     }
   }
-  for (int u = tid; u < nrow * (V / 8); u += 256) {  // dv = beta Ut
-    const int i = u / (V / 8), c8 = 8 * (u % (V / 8));
-    const bf16x8 x = ld8(a.ut + (trow + i) * V + c8);
-    bf16x8 y;
+  {  // dv = beta Ut, this wave's rows from the A fragments it holds
+    const int i = rw + lr;
+    if (i < nrow) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) y[e] = static_cast<bf16>(sb[i] * static_cast<float>(x[e]));
-    st8(a.dv + (((size_t)b * T + t0 + i) * a.HV + hv) * V + c8, y);
+      for (int x = 0; x < 4; ++x) {
+        const int k0 = 32 * x + 8 * lq;
+        if (k0 < V) {
+          bf16x8 y;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) y[e] = static_cast<bf16>(sb[i] * static_cast<float>(fut[x][e]));
+          st8(a.dv + (((size_t)b * T + t0 + i) * a.HV + hv) * V + k0, y);
+        }
+      }
+    }
   }
   if (tid < nrow) a.dbeta[((size_t)b * T + t0 + tid) * a.HV + hv] = static_cast<bf16>(db1[tid] + db2[tid]);
 }
