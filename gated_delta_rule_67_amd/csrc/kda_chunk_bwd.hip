@@ -110,38 +110,41 @@ __device__ __forceinline__ void wave_sync() {
 }
 
 // One chunk's q, k (bf16, [64][pk]) and g (as fp32 into G, [64][pg]) into LDS; rows past
-// nrow read as zeros. All loads are issued before the first store.
-template <int KT>
+// nrow read as zeros. All loads are issued before the first store. NTH threads.
+template <int KT, int NTH>
 __device__ __forceinline__ void stage_qkg(bf16* sq, bf16* sk, float* G, int pk, int pg,
                                           const bf16* qb, const bf16* kb, const bf16* gb,
                                           unsigned qrow, unsigned grow, int nrow, int tid) {
-  constexpr int PER = KT / 8, NU = kC * PER / 256;
+  constexpr int PER = KT / 8, NPC = kC * PER, NU = (NPC + NTH - 1) / NTH;
   const auto rq = rsrc(qb, ((unsigned)(nrow - 1) * qrow + KT) * 2);
   const auto rk = rsrc(kb, ((unsigned)(nrow - 1) * qrow + KT) * 2);
   const auto rg = rsrc(gb, ((unsigned)(nrow - 1) * grow + KT) * 2);
   bf16x8 xq[NU], xk[NU], xg[NU];
 #pragma unroll
   for (int e = 0; e < NU; ++e) {
-    const int u = tid + 256 * e, r = u / PER, c8 = 8 * (u % PER);
-    xq[e] = bload8(rq, (r * qrow + c8) * 2);
-    xk[e] = bload8(rk, (r * qrow + c8) * 2);
-    xg[e] = bload8(rg, (r * grow + c8) * 2);
+    const int u = tid + NTH * e, r = u / PER, c8 = 8 * (u % PER);
+    const unsigned off = u < NPC ? 0u : 0x80000000u;
+    xq[e] = bload8(rq, ((r * qrow + c8) * 2) | off);
+    xk[e] = bload8(rk, ((r * qrow + c8) * 2) | off);
+    xg[e] = bload8(rg, ((r * grow + c8) * 2) | off);
   }
 #pragma unroll
   for (int e = 0; e < NU; ++e) {
-    const int u = tid + 256 * e, r = u / PER, c8 = 8 * (u % PER);
-    st8(sq + r * pk + c8, xq[e]);
-    st8(sk + r * pk + c8, xk[e]);
+    const int u = tid + NTH * e, r = u / PER, c8 = 8 * (u % PER);
+    if (u < NPC) {
+      st8(sq + r * pk + c8, xq[e]);
+      st8(sk + r * pk + c8, xk[e]);
 #pragma unroll
-    for (int x = 0; x < 8; ++x) G[r * pg + c8 + x] = static_cast<float>(xg[e][x]);
+      for (int x = 0; x < 8; ++x) G[r * pg + c8 + x] = static_cast<float>(xg[e][x]);
+    }
   }
 }
 
 // In-place inclusive cumsum of G over the 64 rows (columns < KT); tot: [4][KT] scratch.
-template <int KT>
+template <int KT, int NTH>
 __device__ __forceinline__ void cumsum_rows(float* G, int pg, float* tot, int tid) {
   __syncthreads();
-  for (int it = tid; it < 4 * KT; it += 256) {
+  for (int it = tid; it < 4 * KT; it += NTH) {
     const int wb = it / KT, c = it % KT;
     float acc = 0.f;
 #pragma unroll
@@ -152,7 +155,7 @@ __device__ __forceinline__ void cumsum_rows(float* G, int pg, float* tot, int ti
     tot[wb * KT + c] = acc;
   }
   __syncthreads();
-  for (int it = tid; it < 4 * KT; it += 256) {
+  for (int it = tid; it < 4 * KT; it += NTH) {
     const int wb = it / KT, c = it % KT;
     float pre = 0.f;
     for (int j = 0; j < wb; ++j) pre += tot[j * KT + c];
@@ -231,13 +234,13 @@ __global__ __launch_bounds__(256) void prep_kernel(BwdArgs a) {
   const bf16* gb = a.g + ((size_t)b * a.T + t0) * grow + (size_t)hv * KT;
   unsigned char* blk = a.blocks + (size_t)item * P::bytes;
 
-  stage_qkg<KT>(sq, sk, G, PK, PG, qb, kb, gb, qrow, grow, nrow, tid);
+  stage_qkg<KT, 256>(sq, sk, G, PK, PG, qb, kb, gb, qrow, grow, nrow, tid);
   if (tid < kC) {
     const float bv = tid < nrow ? ldf(a.beta + ((size_t)b * a.T + t0 + tid) * a.HV + hv) : 0.f;
     sb[tid] = bv;
     reinterpret_cast<float*>(blk + P::beta)[tid] = bv;
   }
-  cumsum_rows<KT>(G, PG, reinterpret_cast<float*>(lds + L::tot), tid);  // includes barriers
+  cumsum_rows<KT, 256>(G, PG, reinterpret_cast<float*>(lds + L::tot), tid);  // includes barriers
 
   // operands of the row-block-w products, built by wave w
   {
@@ -743,6 +746,116 @@ __global__ __launch_bounds__(64 * NW) void rev_sweep_kernel(BwdArgs a) {
 }
 
 // ==================================================================== local gradients
+// acc += A B with A (row-major, lda) and B given transposed (bt[col][k], ldb) in LDS, KK a
+// compile-time multiple of 16.
+template <int KK>
+__device__ __forceinline__ void mmaK(f32x4& acc, const bf16* a, int lda, const bf16* bt, int ldb,
+                                     int lane) {
+  const int r = lane & 15, q8 = (lane >> 4) * 8;
+#pragma unroll
+  for (int k0 = 0; k0 < KK; k0 += 32) {
+    bf16x8 av{}, bv{};
+    if (k0 + 32 <= KK || q8 < KK - k0) {
+      av = ld8(a + r * lda + k0 + q8);
+      bv = ld8(bt + r * ldb + k0 + q8);
+    }
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc, 0, 0, 0);
+  }
+}
+
+// The relative-decay products of one wave's 16-token block W (rows rw .. rw + 15) over its
+// half of the key channels (ch), 16 channels (one output tile) at a time:
+//   row role against reference rw over tokens 0 .. rw + 15 with operand k_j exp(G_rw - G_j),
+//     into dq (with F) and the + part of dk (with E);
+//   column role against reference ew = rw + 15 over tokens rw .. 63 with operands
+//     q_i exp(G_i - G_ew) (with F^T) and k_i exp(G_i - G_ew) (with E^T), into the - part of dk.
+// The scaled q / k operand goes in as a bf16 pair hi + lo (two products): the gradient terms
+// of Aq and Mr enter dG once through each role with opposite signs and cancel in the
+// reverse cumsum, which plain bf16 rounding of this operand (different in each role) would
+// not preserve. F and E are rounded once and shared by both roles. The operand is built by
+// this wave alone in its own LDS slot ([16][kPC] hi, then lo).
+template <int KT, int W>
+__device__ __forceinline__ void rdp_products(f32x4* adq, f32x4* arow, f32x4* acol, unsigned char* lds,
+                                             int wslot, int of, int oft, int oe, int oet,
+                                             const float* G, const bf16* sq, const bf16* sk,
+                                             int ch, int lane) {
+  constexpr int PG = KT + 4, PK = KT + 8, rw = 16 * W, ew = rw + 15;
+  constexpr int NR = 16 * (W + 1), NC = kC - rw;  // tokens of the row / column role
+  constexpr int NP = KT / 32;                     // 16-channel parts per half
+  const bf16* s_f = reinterpret_cast<const bf16*>(lds + of) + rw * kPC;
+  const bf16* s_e = reinterpret_cast<const bf16*>(lds + oe) + rw * kPC;
+  const bf16* s_ft = reinterpret_cast<const bf16*>(lds + oft) + rw * kPC + rw;
+  const bf16* s_et = reinterpret_cast<const bf16*>(lds + oet) + rw * kPC + rw;
+  bf16* s_hi = reinterpret_cast<bf16*>(lds + wslot);
+  bf16* s_lo = s_hi + 16 * kPC;
+  const int cl = lane & 15, tg = lane >> 4;  // channel in the part, token-octet group
+#pragma unroll 1
+  for (int part = 0; part < NP; ++part) {
+    const int c = ch * (KT / 2) + 16 * part + cl;
+    {  // row role
+      const float gref = G[rw * PG + c];
+#pragma unroll
+      for (int j8 = 8 * tg; j8 < NR; j8 += 32) {
+        bf16x8 xh, xl;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int j = j8 + e;
+          const float x = static_cast<float>(sk[j * PK + c]) * ex(gref - G[j * PG + c]);
+          const bf16 hi = static_cast<bf16>(x);
+          xh[e] = hi;
+          xl[e] = static_cast<bf16>(x - static_cast<float>(hi));
+        }
+        st8(s_hi + cl * kPC + j8, xh);
+        st8(s_lo + cl * kPC + j8, xl);
+      }
+    }
+    wave_sync();
+    mmaK<NR>(adq[part], s_f, kPC, s_hi, kPC, lane);
+    mmaK<NR>(adq[part], s_f, kPC, s_lo, kPC, lane);
+    mmaK<NR>(arow[part], s_e, kPC, s_hi, kPC, lane);
+    mmaK<NR>(arow[part], s_e, kPC, s_lo, kPC, lane);
+    wave_sync();
+    {  // column role: operands q_i f_i, then k_i f_i, with f_i = exp(G_i - G_ew)
+      constexpr int NO = (NC / 8 + 3) / 4;  // octets per lane (some lanes have one less)
+      const float gref = G[ew * PG + c];
+      float f[NO][8];
+#pragma unroll
+      for (int t = 0; t < NO; ++t) {
+        const int j8 = 8 * tg + 32 * t;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[t][e] = j8 < NC ? ex(G[(rw + j8 + e) * PG + c] - gref) : 0.f;
+      }
+#pragma unroll
+      for (int pass = 0; pass < 2; ++pass) {
+        const bf16* src = pass == 0 ? sq : sk;
+#pragma unroll
+        for (int t = 0; t < NO; ++t) {
+          const int j8 = 8 * tg + 32 * t;
+          if (j8 < NC) {
+            bf16x8 xh, xl;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float x = static_cast<float>(src[(rw + j8 + e) * PK + c]) * f[t][e];
+              const bf16 hi = static_cast<bf16>(x);
+              xh[e] = hi;
+              xl[e] = static_cast<bf16>(x - static_cast<float>(hi));
+            }
+            st8(s_hi + cl * kPC + j8, xh);
+            st8(s_lo + cl * kPC + j8, xl);
+          }
+        }
+        wave_sync();
+        const bf16* xa = pass == 0 ? s_ft : s_et;
+        mmaK<NC>(acol[part], xa, kPC, s_hi, kPC, lane);
+        mmaK<NC>(acol[part], xa, kPC, s_lo, kPC, lane);
+        wave_sync();
+      }
+    }
+  }
+}
+
+constexpr int kLocalWaves = 8;
+
 template <int KT>
 struct LocalLds {
   static constexpr int PK = KT + 8, PG = KT + 4, PV = 128 + 8;
@@ -752,8 +865,8 @@ struct LocalLds {
   static constexpr int bt = sk + kC * PK * 2;      // [64] fp32 beta
   static constexpr int db1 = bt + kC * 4;          // [64] fp32 Ut . W0
   static constexpr int db2 = db1 + kC * 4;         // [64] fp32 sum_j -D Mr
-  static constexpr int lx = db2 + kC * 4;          // [4][KT] fp32 last-token terms per wave
-  static constexpr int lx2 = lx + 4 * KT * 4;      // [KT] fp32 Gam_C rowsum(dS h)
+  static constexpr int lx = db2 + kC * 4;          // [4][KT] fp32 last-token terms per block
+  static constexpr int lx2 = lx + 4 * KT * 4;      // [KT] fp32 rowsum(dS h)
   static constexpr int tot = lx2 + KT * 4;         // [4][KT] fp32 cumsum scratch
   static constexpr int ph = tot + 4 * KT * 4;      // phase region
   // phase 1
@@ -765,8 +878,8 @@ struct LocalLds {
   static constexpr int ft = f + kC * kPC * 2;      // [64][kPC] F^T
   static constexpr int e = ft + kC * kPC * 2;      // [64][kPC] E
   static constexpr int et = e + kC * kPC * 2;      // [64][kPC] E^T
-  static constexpr int wop = et + kC * kPC * 2;    // [4][64][kPC] per wave: 32 channels hi, 32 lo
-  static constexpr int end2 = wop + 4 * 64 * kPC * 2;
+  static constexpr int wop = et + kC * kPC * 2;    // [8][32][kPC] per wave: 16 channels hi, lo
+  static constexpr int end2 = wop + kLocalWaves * 32 * kPC * 2;
   // phase 3
   static constexpr int dgs = ph;                   // [64][PG] fp32 dG
   static constexpr int end3 = dgs + kC * PG * 4;
@@ -774,11 +887,14 @@ struct LocalLds {
   static_assert(total <= 160 * 1024, "LDS");
 };
 
+// One workgroup of 8 waves per (b, hv, chunk): waves w and w + 4 own token block w and split
+// its key channels (ch = 0: the first half, 1: the second).
 template <int KT>
-__global__ __launch_bounds__(256) void local_kernel(BwdArgs a) {
+__global__ __launch_bounds__(64 * kLocalWaves) void local_kernel(BwdArgs a) {
   using L = LocalLds<KT>;
   using P = PB<KT>;
-  constexpr int PK = L::PK, PG = L::PG, PV = L::PV, NCT = KT / 16;
+  constexpr int NTH = 64 * kLocalWaves;
+  constexpr int PK = L::PK, PG = L::PG, PV = L::PV, NCH = KT / 32;  // tiles per channel half
   __shared__ __attribute__((aligned(16))) unsigned char lds[L::total];
   float* G = reinterpret_cast<float*>(lds + L::g);
   bf16* sq = reinterpret_cast<bf16*>(lds + L::sq);
@@ -789,7 +905,8 @@ __global__ __launch_bounds__(256) void local_kernel(BwdArgs a) {
   float* lx = reinterpret_cast<float*>(lds + L::lx);
   float* lx2 = reinterpret_cast<float*>(lds + L::lx2);
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w8 = tid >> 6;
+  const int w = w8 & 3, ch = w8 >> 2;
   const int lr = lane & 15, lq = lane >> 4;
   const int item = blockIdx.x;
   const int n = item % a.NT, head = item / a.NT;
@@ -805,6 +922,7 @@ __global__ __launch_bounds__(256) void local_kernel(BwdArgs a) {
   const bf16* hsrc = a.h + ((size_t)head * a.NT + n) * KT * V;
   const bf16* dsrc = a.dsn + ((size_t)head * a.NT + n) * KT * V;
   const int rw = 16 * w, ew = 16 * w + 15;  // first and last token of this wave's block
+  const int c0 = ch * (KT / 2);             // first channel of this wave's half
   const unsigned vrow = (unsigned)(a.HV * V);
 
   // this wave's rows of dO and Ut (and W0) as MFMA A operands, straight from memory
@@ -819,44 +937,47 @@ __global__ __launch_bounds__(256) void local_kernel(BwdArgs a) {
       const bool ok = k0 < V;
       fdo[s] = ok ? bload8(rdo, (row * vrow + k0) * 2) : bf16x8{};
       fut[s] = ok ? ld8(a.ut + (trow + row) * V + k0) : bf16x8{};
-      fw0[s] = ok ? ld8(a.w0 + (trow + row) * V + k0) : bf16x8{};
+      fw0[s] = ok && ch == 0 ? ld8(a.w0 + (trow + row) * V + k0) : bf16x8{};
     }
   }
-  stage_qkg<KT>(sq, sk, G, PK, PG, qb, kb, gb, qrow, grow, nrow, tid);
-  if (tid < kC) sb[tid] = reinterpret_cast<const float*>(blk + P::beta)[tid];
+  stage_qkg<KT, NTH>(sq, sk, G, PK, PG, qb, kb, gb, qrow, grow, nrow, tid);
+  if (tid < kC) {
+    sb[tid] = reinterpret_cast<const float*>(blk + P::beta)[tid];
+    db2[tid] = 0.f;
+  }
+  if (tid < KT) lx2[tid] = 0.f;
   // ---------------- phase 1: products contracting over V
   bf16* s_u = reinterpret_cast<bf16*>(lds + L::uu);
   bf16* s_hs = reinterpret_cast<bf16*>(lds + L::hs);
   {
-    constexpr int NU = kC * 16 / 256, NH = KT * 16 / 256;  // 8-column pieces at V = 128
+    constexpr int NU = (kC * 16 + NTH - 1) / NTH, NH = (KT * 16 + NTH - 1) / NTH;
     bf16x8 xu[NU], xh[NH];
     const int per = V / 8;
 #pragma unroll
     for (int e = 0; e < NU; ++e) {
-      const int u = tid + 256 * e, r = u / per, c8 = 8 * (u % per);
+      const int u = tid + NTH * e, r = u / per, c8 = 8 * (u % per);
       xu[e] = u < kC * per ? ld8(a.u + (trow + r) * V + c8) : bf16x8{};
     }
 #pragma unroll
     for (int e = 0; e < NH; ++e) {
-      const int u = tid + 256 * e, r = u / per, c8 = 8 * (u % per);
+      const int u = tid + NTH * e, r = u / per, c8 = 8 * (u % per);
       xh[e] = u < KT * per ? ld8(hsrc + (size_t)r * V + c8) : bf16x8{};
     }
 #pragma unroll
     for (int e = 0; e < NU; ++e) {
-      const int u = tid + 256 * e, r = u / per, c8 = 8 * (u % per);
+      const int u = tid + NTH * e, r = u / per, c8 = 8 * (u % per);
       if (u < kC * per) st8(s_u + r * PV + c8, xu[e]);
     }
 #pragma unroll
     for (int e = 0; e < NH; ++e) {
-      const int u = tid + 256 * e, r = u / per, c8 = 8 * (u % per);
+      const int u = tid + NTH * e, r = u / per, c8 = 8 * (u % per);
       if (u < KT * per) st8(s_hs + r * PV + c8, xh[e]);
     }
   }
-  cumsum_rows<KT>(G, PG, reinterpret_cast<float*>(lds + L::tot), tid);  // includes barriers
+  cumsum_rows<KT, NTH>(G, PG, reinterpret_cast<float*>(lds + L::tot), tid);  // includes barriers
 
-  if (tid < KT) lx2[tid] = 0.f;  // Gam_C rowsum(dS * h), accumulated when dS arrives
-  // dbeta, first term: Ut_i . W0_i for this wave's rows
-  {
+  // dbeta, first term: Ut_i . W0_i for this block's rows (one wave of the pair)
+  if (ch == 0) {
     float s = 0.f;
 #pragma unroll
     for (int x = 0; x < 4; ++x)
@@ -866,42 +987,44 @@ __global__ __launch_bounds__(256) void local_kernel(BwdArgs a) {
     s += __shfl_xor(s, 32);
     if (lq == 0) db1[rw + lr] = s;
   }
-  f32x4 Dm[4], Fo[4];
+  // D = Ut U^T and Fo = dO U^T, tiles J <= w with J = ch mod 2
+  f32x4 Dm[2], Fo[2];
 #pragma unroll
-  for (int J = 0; J < 4; ++J) {
-    Dm[J] = Fo[J] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int jj = 0; jj < 2; ++jj) {
+    const int J = 2 * jj + ch;
+    Dm[jj] = Fo[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (J <= w) {
-      mma_ra(Dm[J], fut, s_u + 16 * J * PV, PV, V, lane);
-      mma_ra(Fo[J], fdo, s_u + 16 * J * PV, PV, V, lane);
+      mma_ra(Dm[jj], fut, s_u + 16 * J * PV, PV, V, lane);
+      mma_ra(Fo[jj], fdo, s_u + 16 * J * PV, PV, V, lane);
     }
   }
-  f32x4 adq[NCT], arow[NCT], acol[NCT];
+  f32x4 adq[NCH], arow[NCH], acol[NCH];
 #pragma unroll
-  for (int ct = 0; ct < NCT; ++ct) {
-    adq[ct] = arow[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-    mma_ra(adq[ct], fdo, s_hs + 16 * ct * PV, PV, V, lane);
-    mma_ra(arow[ct], fut, s_hs + 16 * ct * PV, PV, V, lane);
-    const int c = 16 * ct + lr;
+  for (int cc = 0; cc < NCH; ++cc) {
+    adq[cc] = arow[cc] = f32x4{0.f, 0.f, 0.f, 0.f};
+    mma_ra(adq[cc], fdo, s_hs + (c0 + 16 * cc) * PV, PV, V, lane);
+    mma_ra(arow[cc], fut, s_hs + (c0 + 16 * cc) * PV, PV, V, lane);
+    const int c = c0 + 16 * cc + lr;
     const float er = ex(G[rw * PG + c]);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      adq[ct][r] *= a.scale * er;                 // scale dO h^T, times exp(G_rw)
-      arow[ct][r] *= -sb[rw + 4 * lq + r] * er;    // -(beta Ut) h^T, times exp(G_rw)
+      adq[cc][r] *= a.scale * er;                 // scale dO h^T, times exp(G_rw)
+      arow[cc][r] *= -sb[rw + 4 * lq + r] * er;    // -(beta Ut) h^T, times exp(G_rw)
     }
   }
   {
-    constexpr int NH = KT * 16 / 256;
+    constexpr int NH = (KT * 16 + NTH - 1) / NTH;
     bf16x8 xh[NH];
     const int per = V / 8;
 #pragma unroll
     for (int e = 0; e < NH; ++e) {
-      const int u = tid + 256 * e, r = u / per, c8 = 8 * (u % per);
+      const int u = tid + NTH * e, r = u / per, c8 = 8 * (u % per);
       xh[e] = u < KT * per ? ld8(dsrc + (size_t)r * V + c8) : bf16x8{};
     }
     __syncthreads();  // every wave is done with h
 #pragma unroll
     for (int e = 0; e < NH; ++e) {
-      const int u = tid + 256 * e, r = u / per, c8 = 8 * (u % per);
+      const int u = tid + NTH * e, r = u / per, c8 = 8 * (u % per);
       if (u < KT * per) {
         const bf16x8 hv8 = ld8(s_hs + r * PV + c8);
         float sdot = 0.f;
@@ -914,10 +1037,10 @@ __global__ __launch_bounds__(256) void local_kernel(BwdArgs a) {
   }
   __syncthreads();
 #pragma unroll
-  for (int ct = 0; ct < NCT; ++ct) {
+  for (int cc = 0; cc < NCH; ++cc) {
     f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
-    mma16(x, s_u + rw * PV, PV, s_hs + 16 * ct * PV, PV, V, lane);  // U dS^T
-    const int c = 16 * ct + lr;
+    mma16(x, s_u + rw * PV, PV, s_hs + (c0 + 16 * cc) * PV, PV, V, lane);  // U dS^T
+    const int c = c0 + 16 * cc + lr;
     const float gl = G[(kC - 1) * PG + c];
     float part = 0.f;
 #pragma unroll
@@ -928,20 +1051,22 @@ __global__ __launch_bounds__(256) void local_kernel(BwdArgs a) {
     part += __shfl_xor(part, 16);
     part += __shfl_xor(part, 32);
     if (lq == 0) lx[w * KT + c] = part;
-    acol[ct] = x * ex(gl - G[ew * PG + c]);  // U dS^T exp(G_C - G_ew); exp(G_ew - G_j) follows
+    acol[cc] = x * ex(gl - G[ew * PG + c]);  // U dS^T exp(G_C - G_ew); exp(G_ew - G_j) follows
   }
-  // dbeta, second term: sum_j (-Ut U^T)_ij Mr_ij, rows of this wave
+  // dbeta, second term: sum_j (-Ut U^T)_ij Mr_ij over this wave's tiles J
   {
     const float* gmr = reinterpret_cast<const float*>(blk + P::mr);
     float s[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int J = 0; J < 4; ++J)
+    for (int jj = 0; jj < 2; ++jj) {
+      const int J = 2 * jj + ch;
       if (J <= w)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int i = rw + 4 * lq + r, j = 16 * J + lr;
-          s[r] -= Dm[J][r] * gmr[i * kC + j];  // Mr is zero on and above the diagonal
+          s[r] -= Dm[jj][r] * gmr[i * kC + j];  // Mr is zero on and above the diagonal
         }
+    }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       float x = s[r];
@@ -949,7 +1074,7 @@ __global__ __launch_bounds__(256) void local_kernel(BwdArgs a) {
       x += __shfl_xor(x, 2);
       x += __shfl_xor(x, 4);
       x += __shfl_xor(x, 8);
-      if (lr == 0) db2[rw + 4 * lq + r] = x;
+      if (lr == 0) atomicAdd(db2 + rw + 4 * lq + r, x);
     }
   }
   __syncthreads();  // phase 1 operands are dead
@@ -960,14 +1085,15 @@ __global__ __launch_bounds__(256) void local_kernel(BwdArgs a) {
   bf16* s_e = reinterpret_cast<bf16*>(lds + L::e);
   bf16* s_et = reinterpret_cast<bf16*>(lds + L::et);
 #pragma unroll
-  for (int J = 0; J < 4; ++J) {
+  for (int jj = 0; jj < 2; ++jj) {  // this wave's tiles J (zeros where J > w)
+    const int J = 2 * jj + ch;
     const int j = 16 * J + lr;
     f32x4 fv, evv;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int i = rw + 4 * lq + r;
-      fv[r] = j <= i ? a.scale * Fo[J][r] : 0.f;
-      evv[r] = j < i ? -sb[i] * Dm[J][r] : 0.f;
+      fv[r] = j <= i ? a.scale * Fo[jj][r] : 0.f;
+      evv[r] = j < i ? -sb[i] * Dm[jj][r] : 0.f;
       s_f[i * kPC + j] = static_cast<bf16>(fv[r]);
       s_e[i * kPC + j] = static_cast<bf16>(evv[r]);
     }
@@ -975,58 +1101,12 @@ __global__ __launch_bounds__(256) void local_kernel(BwdArgs a) {
     st4(s_et + j * kPC + rw + 4 * lq, evv);
   }
   __syncthreads();
-
-  // The scaled q / k operand goes in as a bf16 pair hi + lo (two products): the gradient terms
-  // of Aq and Mr enter dG once through each role with opposite signs and cancel in the
-  // reverse cumsum, which plain bf16 rounding of this operand (different in each role) would
-  // not preserve. F and E are rounded once and shared by both roles. The operand is built by
-  // this wave alone, 32 channels at a time, in its own LDS slot.
-  bf16* s_hi = reinterpret_cast<bf16*>(lds + L::wop) + w * 64 * kPC;
-  bf16* s_lo = s_hi + 32 * kPC;
-  // role 0: row role against reference rw over tokens 0 .. ew, operand k_j exp(G_rw - G_j)
-  // role 1 / 2: column role against reference ew over tokens rw .. 63, operand
-  //             q_i exp(G_i - G_ew) (with F^T) / k_i exp(G_i - G_ew) (with E^T)
-  for (int role = 0; role < 3; ++role) {
-    const int first = role == 0 ? 0 : rw;
-    const int ntok = role == 0 ? 16 * (w + 1) : kC - rw;
-    const int ref = role == 0 ? rw : ew;
-    const bf16* src = role == 1 ? sq : sk;
-    for (int part = 0; part < KT / 32; ++part) {
-      for (int u = lane; u < 32 * (ntok / 8); u += 64) {
-        const int cl = u % 32, c = 32 * part + cl, j8 = 8 * (u / 32);
-        const float gref = G[ref * PG + c];
-        bf16x8 xh, xl;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int j = first + j8 + e;
-          const float d = role == 0 ? gref - G[j * PG + c] : G[j * PG + c] - gref;
-          const float x = static_cast<float>(src[j * PK + c]) * ex(d);
-          const bf16 hi = static_cast<bf16>(x);
-          xh[e] = hi;
-          xl[e] = static_cast<bf16>(x - static_cast<float>(hi));
-        }
-        st8(s_hi + cl * kPC + j8, xh);
-        st8(s_lo + cl * kPC + j8, xl);
-      }
-      wave_sync();
-#pragma unroll
-      for (int cc = 0; cc < 2; ++cc) {
-        const int ct = 2 * part + cc;
-        const bf16* bh = s_hi + 16 * cc * kPC;
-        const bf16* bl = s_lo + 16 * cc * kPC;
-        if (role == 0) {
-          mma16(adq[ct], s_f + rw * kPC, kPC, bh, kPC, ntok, lane);
-          mma16(adq[ct], s_f + rw * kPC, kPC, bl, kPC, ntok, lane);
-          mma16(arow[ct], s_e + rw * kPC, kPC, bh, kPC, ntok, lane);
-          mma16(arow[ct], s_e + rw * kPC, kPC, bl, kPC, ntok, lane);
-        } else {
-          const bf16* xa = (role == 1 ? s_ft : s_et) + rw * kPC + rw;
-          mma16(acol[ct], xa, kPC, bh, kPC, ntok, lane);
-          mma16(acol[ct], xa, kPC, bl, kPC, ntok, lane);
-        }
-      }
-      wave_sync();
-    }
+  const int wslot = L::wop + w8 * 32 * kPC * 2;
+  switch (w) {
+    case 0: rdp_products<KT, 0>(adq, arow, acol, lds, wslot, L::f, L::ft, L::e, L::et, G, sq, sk, ch, lane); break;
+    case 1: rdp_products<KT, 1>(adq, arow, acol, lds, wslot, L::f, L::ft, L::e, L::et, G, sq, sk, ch, lane); break;
+    case 2: rdp_products<KT, 2>(adq, arow, acol, lds, wslot, L::f, L::ft, L::e, L::et, G, sq, sk, ch, lane); break;
+    default: rdp_products<KT, 3>(adq, arow, acol, lds, wslot, L::f, L::ft, L::e, L::et, G, sq, sk, ch, lane); break;
   }
   __syncthreads();  // phase 2 operands are dead
 
@@ -1034,16 +1114,16 @@ __global__ __launch_bounds__(256) void local_kernel(BwdArgs a) {
   float* dgs = reinterpret_cast<float*>(lds + L::dgs);
   const int G_ = a.HV / a.H;
 #pragma unroll
-  for (int ct = 0; ct < NCT; ++ct) {
-    const int c = 16 * ct + lr;
+  for (int cc = 0; cc < NCH; ++cc) {
+    const int c = c0 + 16 * cc + lr;
     const float gr = G[rw * PG + c], ge = G[ew * PG + c];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int i = rw + 4 * lq + r;
       const float gi = G[i * PG + c];
       const float fr = ex(gi - gr), fc = ex(ge - gi);
-      const float dq = adq[ct][r] * fr;
-      const float dpos = arow[ct][r] * fr, dneg = acol[ct][r] * fc;
+      const float dq = adq[cc][r] * fr;
+      const float dpos = arow[cc][r] * fr, dneg = acol[cc][r] * fc;
       const float dk = dpos + dneg;
       const float qv = static_cast<float>(sq[i * PK + c]);
       const float kv = static_cast<float>(sk[i * PK + c]);
@@ -1061,14 +1141,14 @@ __global__ __launch_bounds__(256) void local_kernel(BwdArgs a) {
     }
   }
   __syncthreads();
-  for (int c = tid; c < KT; c += 256) {
+  for (int c = tid; c < KT; c += NTH) {
     float run = lx[c] + lx[KT + c] + lx[2 * KT + c] + lx[3 * KT + c] + ex(G[(kC - 1) * PG + c]) * lx2[c];
     for (int i = kC - 1; i >= 0; --i) {
       run += dgs[i * PG + c];
       if (i < nrow) a.dg[(((size_t)b * T + t0 + i) * a.HV + hv) * KT + c] = static_cast<bf16>(run);
     }
   }
-  {  // dv = beta Ut, this wave's rows from the A fragments it holds
+  if (ch == 0) {  // dv = beta Ut, this block's rows from the A fragments the wave holds
     const int i = rw + lr;
     if (i < nrow) {
 #pragma unroll
@@ -1132,7 +1212,7 @@ hipError_t launch_cfg(BwdArgs a, hipStream_t stream) {
   const int sweeps = a.B * a.HV * ((a.V + 16 * NW - 1) / (16 * NW));
   hipLaunchKernelGGL((fwd_sweep_kernel<KT, NW>), dim3(sweeps), dim3(64 * NW), 0, stream, a);
   hipLaunchKernelGGL((rev_sweep_kernel<KT, NW>), dim3(sweeps), dim3(64 * NW), 0, stream, a);
-  hipLaunchKernelGGL((local_kernel<KT>), dim3(items), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((local_kernel<KT>), dim3(items), dim3(64 * kLocalWaves), 0, stream, a);
   if (a.HV != a.H) {
     const size_t n = (size_t)a.B * a.T * a.H * KT;
     const unsigned grid = (unsigned)((n + 255) / 256);
