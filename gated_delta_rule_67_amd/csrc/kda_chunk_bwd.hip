@@ -187,6 +187,23 @@ __device__ __forceinline__ void mma16_nn(f32x4& acc, const float* a, int lda, co
                                                0, 0);
 }
 
+// acc += A B with A (row-major, lda) and B given transposed (bt[col][k], ldb) in LDS, KK a
+// compile-time multiple of 16.
+template <int KK>
+__device__ __forceinline__ void mmaK(f32x4& acc, const bf16* a, int lda, const bf16* bt, int ldb,
+                                     int lane) {
+  const int r = lane & 15, q8 = (lane >> 4) * 8;
+#pragma unroll
+  for (int k0 = 0; k0 < KK; k0 += 32) {
+    bf16x8 av{}, bv{};
+    if (k0 + 32 <= KK || q8 < KK - k0) {
+      av = ld8(a + r * lda + k0 + q8);
+      bv = ld8(bt + r * ldb + k0 + q8);
+    }
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc, 0, 0, 0);
+  }
+}
+
 // ============================================================================ prep
 template <int KT>
 struct PrepLds {
@@ -279,8 +296,8 @@ __global__ __launch_bounds__(256) void prep_kernel(BwdArgs a) {
     for (int J = 0; J < 4; ++J) {
       aq[J] = mr[J] = f32x4{0.f, 0.f, 0.f, 0.f};
       if (J <= w) {
-        mma16(aq[J], qs + 16 * w * PK, PK, bw + 16 * J * PK, PK, KT, lane);
-        mma16(mr[J], ks + 16 * w * PK, PK, bw + 16 * J * PK, PK, KT, lane);
+        mmaK<KT>(aq[J], qs + 16 * w * PK, PK, bw + 16 * J * PK, PK, lane);
+        mmaK<KT>(mr[J], ks + 16 * w * PK, PK, bw + 16 * J * PK, PK, lane);
       }
     }
   }
@@ -558,14 +575,12 @@ __global__ __launch_bounds__(64 * NW) void fwd_sweep_kernel(BwdArgs a) {
     for (int ct = 0; ct < NCT; ++ct) st4(s_ht + lr * PK + 16 * ct + 4 * lq, S[ct]);
     if (n + 1 < a.NT) fetch(n + 1);
     __syncthreads();
-    store_state_tile<KT>(a.h + ((size_t)head * a.NT + n) * KT * V, V, vt_idx * BV + 16 * w, s_ht,
-                         PK, lane);
     // X = Kg h, W0 = V - X, Y = beta W0
     const size_t trow = ((size_t)head * a.NT + n) * kC;
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
       f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
-      mma16(x, s_kg + 16 * I * PK, PK, s_ht, PK, KT, lane);
+      mmaK<KT>(x, s_kg + 16 * I * PK, PK, s_ht, PK, lane);
       f32x4 w0, y;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -580,7 +595,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_sweep_kernel(BwdArgs a) {
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
       f32x4 uv = f32x4{0.f, 0.f, 0.f, 0.f};
-      mma16(uv, s_tm + 16 * I * kPC, kPC, s_yt, kPC, kC, lane);
+      mmaK<kC>(uv, s_tm + 16 * I * kPC, kPC, s_yt, kPC, lane);
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         if (vok) a.u[(trow + 16 * I + 4 * lq + r) * V + vc] = static_cast<bf16>(uv[r]);
@@ -591,8 +606,11 @@ __global__ __launch_bounds__(64 * NW) void fwd_sweep_kernel(BwdArgs a) {
     for (int ct = 0; ct < NCT; ++ct) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) S[ct][r] *= s_gam[16 * ct + 4 * lq + r];
-      mma16(S[ct], s_kct + 16 * ct * kPC, kPC, s_uu, kPC, kC, lane);
+      mmaK<kC>(S[ct], s_kct + 16 * ct * kPC, kPC, s_uu, kPC, lane);
     }
+    // h of this chunk to the workspace (its LDS copy is intact until the next chunk)
+    store_state_tile<KT>(a.h + ((size_t)head * a.NT + n) * KT * V, V, vt_idx * BV + 16 * w, s_ht,
+                         PK, lane);
   }
 }
 
@@ -703,14 +721,12 @@ __global__ __launch_bounds__(64 * NW) void rev_sweep_kernel(BwdArgs a) {
     for (int ct = 0; ct < NCT; ++ct) st4(s_dst + lr * PK + 16 * ct + 4 * lq, D[ct]);
     if (n > 0) fetch(n - 1);
     __syncthreads();
-    store_state_tile<KT>(a.dsn + ((size_t)head * a.NT + n) * KT * V, V, vt_idx * BV + 16 * w,
-                         s_dst, PK, lane);
     // dU = scale Aq^T dO + Kc dS
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
       f32x4 p = f32x4{0.f, 0.f, 0.f, 0.f}, q = f32x4{0.f, 0.f, 0.f, 0.f};
-      mma16(p, s_aqt + 16 * I * kPC, kPC, s_dow, kPC, kC, lane);
-      mma16(q, s_kc + 16 * I * PK, PK, s_dst, PK, KT, lane);
+      mmaK<kC>(p, s_aqt + 16 * I * kPC, kPC, s_dow, kPC, lane);
+      mmaK<KT>(q, s_kc + 16 * I * PK, PK, s_dst, PK, lane);
       st4(s_dut + lr * kPC + 16 * I + 4 * lq, a.scale * p + q);
     }
     // Ut = T^T dU; beta Ut
@@ -718,7 +734,7 @@ __global__ __launch_bounds__(64 * NW) void rev_sweep_kernel(BwdArgs a) {
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
       f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
-      mma16(x, s_tt + 16 * I * kPC, kPC, s_dut, kPC, kC, lane);
+      mmaK<kC>(x, s_tt + 16 * I * kPC, kPC, s_dut, kPC, lane);
       f32x4 y;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -732,11 +748,14 @@ __global__ __launch_bounds__(64 * NW) void rev_sweep_kernel(BwdArgs a) {
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
       f32x4 p = f32x4{0.f, 0.f, 0.f, 0.f}, q = f32x4{0.f, 0.f, 0.f, 0.f};
-      mma16(p, s_qgt + 16 * ct * kPC, kPC, s_dow, kPC, kC, lane);
-      mma16(q, s_kgt + 16 * ct * kPC, kPC, s_but, kPC, kC, lane);
+      mmaK<kC>(p, s_qgt + 16 * ct * kPC, kPC, s_dow, kPC, lane);
+      mmaK<kC>(q, s_kgt + 16 * ct * kPC, kPC, s_but, kPC, lane);
 #pragma unroll
       for (int r = 0; r < 4; ++r) D[ct][r] = D[ct][r] * s_gam[16 * ct + 4 * lq + r] + a.scale * p[r] - q[r];
     }
+    // dS of this chunk to the workspace (its LDS copy is intact until the next chunk)
+    store_state_tile<KT>(a.dsn + ((size_t)head * a.NT + n) * KT * V, V, vt_idx * BV + 16 * w,
+                         s_dst, PK, lane);
   }
   if (a.dh0 && vok)
 #pragma unroll
@@ -746,23 +765,6 @@ __global__ __launch_bounds__(64 * NW) void rev_sweep_kernel(BwdArgs a) {
 }
 
 // ==================================================================== local gradients
-// acc += A B with A (row-major, lda) and B given transposed (bt[col][k], ldb) in LDS, KK a
-// compile-time multiple of 16.
-template <int KK>
-__device__ __forceinline__ void mmaK(f32x4& acc, const bf16* a, int lda, const bf16* bt, int ldb,
-                                     int lane) {
-  const int r = lane & 15, q8 = (lane >> 4) * 8;
-#pragma unroll
-  for (int k0 = 0; k0 < KK; k0 += 32) {
-    bf16x8 av{}, bv{};
-    if (k0 + 32 <= KK || q8 < KK - k0) {
-      av = ld8(a + r * lda + k0 + q8);
-      bv = ld8(bt + r * ldb + k0 + q8);
-    }
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc, 0, 0, 0);
-  }
-}
-
 // The relative-decay products of one wave's 16-token block W (rows rw .. rw + 15) over its
 // half of the key channels (ch), 16 channels (one output tile) at a time:
 //   row role against reference rw over tokens 0 .. rw + 15 with operand k_j exp(G_rw - G_j),
@@ -1036,10 +1038,16 @@ __global__ __launch_bounds__(64 * kLocalWaves) void local_kernel(BwdArgs a) {
     }
   }
   __syncthreads();
+  bf16x8 fuu[4];  // this block's rows of U as A fragments
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    const int k0 = 32 * x + 8 * lq;
+    fuu[x] = k0 < V ? ld8(s_u + (rw + lr) * PV + k0) : bf16x8{};
+  }
 #pragma unroll
   for (int cc = 0; cc < NCH; ++cc) {
     f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
-    mma16(x, s_u + rw * PV, PV, s_hs + (c0 + 16 * cc) * PV, PV, V, lane);  // U dS^T
+    mma_ra(x, fuu, s_hs + (c0 + 16 * cc) * PV, PV, V, lane);  // U dS^T
     const int c = c0 + 16 * cc + lr;
     const float gl = G[(kC - 1) * PG + c];
     float part = 0.f;
