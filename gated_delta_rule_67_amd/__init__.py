@@ -24,7 +24,7 @@ import os
 
 import torch
 
-__all__ = ["kda_chunk_fwd", "kda_chunk_bwd", "kda_recurrent_step", "library", "library_path", "status_string",
+__all__ = ["kda_chunk_fwd", "kda_chunk_fwd_varlen", "kda_chunk_bwd", "kda_recurrent_step", "library", "library_path", "status_string",
            "KDA_OK", "KDA_ERR_INVALID", "KDA_ERR_UNSUPPORTED", "KDA_ERR_HIP",
            "KDA_FLAG_QK_L2NORM", "KDA_FLAG_BETA_SIGMOID"]
 
@@ -51,6 +51,11 @@ def library():
     lib.kda_chunk_fwd_ex.restype = i
     lib.kda_chunk_fwd_workspace_size.argtypes = [i] * 8
     lib.kda_chunk_fwd_workspace_size.restype = sz
+    lib.kda_chunk_fwd_varlen.argtypes = [vp] * 6 + [i] + [vp] * 3 + [i] * 5 + [f, i, vp, sz,
+                                                                            ctypes.c_uint, vp]
+    lib.kda_chunk_fwd_varlen.restype = i
+    lib.kda_chunk_fwd_varlen_workspace_size.argtypes = [i] * 7
+    lib.kda_chunk_fwd_varlen_workspace_size.restype = sz
     lib.kda_chunk_bwd.argtypes = [vp] * 14 + [i] * 6 + [f, i, i, vp, sz, vp]
     lib.kda_chunk_bwd.restype = i
     lib.kda_chunk_bwd_workspace_size.argtypes = [i] * 8
@@ -129,6 +134,51 @@ def kda_chunk_fwd(q, k, v, g, beta, scale=None, initial_state=None, output_final
                                   _flags(qk_l2norm, beta_sigmoid), ctypes.c_void_p(stream))
     _check(rc)
     return o, final
+
+
+def kda_chunk_fwd_varlen(q, k, v, g, beta, cu_seqlens, scale=None, initial_state=None,
+                         output_final_state=True, qk_l2norm=False, beta_sigmoid=False):
+    """Packed variable-length prefill (bf16). q, k [1,T,H,K] (or [T,H,K]); v [1,T,HV,V];
+    g [1,T,HV,K]; beta [1,T,HV]; cu_seqlens int32 [N+1] on the same device; initial_state
+    [N,HV,K,V] float32 or None. Returns (o shaped like v, final_state [N,HV,K,V] or None)."""
+    _require(q.is_cuda, "inputs must be on a GPU")
+    dev, dt = q.device, q.dtype
+    _require(dt in _DTYPE, f"unsupported dtype {dt}")
+    squeeze = q.dim() == 3
+    if not squeeze:
+        _require(q.shape[0] == 1, "packed inputs have batch size 1")
+        q, k, v, g, beta = q[0], k[0], v[0], g[0], beta[0]
+    T, H, K = q.shape
+    HV, V = v.shape[1], v.shape[2]
+    _require(k.shape == q.shape, "k must match q")
+    _require(v.shape[0] == T, "v must be [T, HV, V]")
+    _require(tuple(g.shape) == (T, HV, K), "g must be [T, HV, K]")
+    _require(tuple(beta.shape) == (T, HV), "beta must be [T, HV]")
+    _check_tensors([("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta)], dt, dev)
+    _require(cu_seqlens.is_cuda and cu_seqlens.device == dev, "cu_seqlens must be on the same GPU")
+    _require(cu_seqlens.dtype == torch.int32 and cu_seqlens.dim() == 1 and cu_seqlens.is_contiguous(),
+             "cu_seqlens must be a contiguous int32 vector")
+    N = cu_seqlens.numel() - 1
+    _require(N >= 1, "cu_seqlens needs at least two offsets")
+    if initial_state is not None:
+        _require(tuple(initial_state.shape) == (N, HV, K, V), "initial_state must be [N, HV, K, V]")
+        _check_tensors([("initial_state", initial_state)], torch.float32, dev)
+    if scale is None:
+        scale = 1.0 / math.sqrt(K)
+    lib = library()
+    o = torch.empty((T, HV, V), dtype=dt, device=dev)
+    final = torch.empty((N, HV, K, V), dtype=torch.float32, device=dev) if output_final_state else None
+    ws_bytes = lib.kda_chunk_fwd_varlen_workspace_size(N, T, H, HV, K, V, _DTYPE[dt])
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        rc = lib.kda_chunk_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                      _ptr(cu_seqlens), N, _ptr(initial_state), _ptr(final),
+                                      _ptr(o), T, H, HV, K, V, float(scale), _DTYPE[dt], _ptr(ws),
+                                      ws_bytes, _flags(qk_l2norm, beta_sigmoid),
+                                      ctypes.c_void_p(stream))
+    _check(rc)
+    return (o if squeeze else o.unsqueeze(0)), final
 
 
 def kda_chunk_bwd(q, k, v, g, beta, do, scale=None, initial_state=None, dht=None, chunk_size=64,

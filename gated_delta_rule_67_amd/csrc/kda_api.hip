@@ -15,6 +15,9 @@ hipError_t launch_prefill(const void*, const void*, const void*, const void*, co
                           void*, unsigned, hipStream_t);
 size_t wy_workspace_bytes(int B, int T, int HV, int K);
 size_t bwd_workspace_bytes(int B, int T, int H, int HV, int K, int V);
+size_t wy_varlen_workspace_bytes(int nseq, int T, int HV, int K);
+hipError_t launch_prefill_wy_varlen(const PrefillArgs& p, const int* cu_seqlens, void* workspace,
+                                    hipStream_t stream);
 hipError_t launch_chunk_bwd(const void*, const void*, const void*, const void*, const void*,
                             const float*, const void*, const float*, void*, void*, void*, void*,
                             void*, float*, int, int, int, int, int, int, float, void*,
@@ -105,6 +108,41 @@ int kda_chunk_fwd_ex(const void* q, const void* k, const void* v, const void* g,
                                            need ? workspace : nullptr, flags,
                                            static_cast<hipStream_t>(stream));
   if (e == hipErrorNotSupported) return KDA_ERR_UNSUPPORTED;  // flags, unaligned tensors
+  return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+// Packed sequences take the two-kernel path only: bf16, K % 8 == 0, V % 8 == 0.
+static bool varlen_shape(int K, int V, int dtype) {
+  return dtype == KDA_DTYPE_BF16 && K % 8 == 0 && V % 8 == 0;
+}
+
+size_t kda_chunk_fwd_varlen_workspace_size(int N, int T, int H, int HV, int K, int V, int dtype) {
+  if (!positive(T)) return 0;
+  if (check_common(N, H, HV, K, V, 1.f, dtype) != KDA_OK || !varlen_shape(K, V, dtype)) return 0;
+  return kda::wy_varlen_workspace_bytes(N, T, HV, K);
+}
+
+int kda_chunk_fwd_varlen(const void* q, const void* k, const void* v, const void* g,
+                         const void* beta, const int* cu_seqlens, int N,
+                         const float* initial_state, float* final_state, void* o, int T, int H,
+                         int HV, int K, int V, float scale, int dtype, void* workspace,
+                         size_t workspace_bytes, unsigned flags, void* stream) {
+  if (!q || !k || !v || !g || !beta || !o || !cu_seqlens) return KDA_ERR_INVALID;
+  if (flags & ~(unsigned)(KDA_FLAG_QK_L2NORM | KDA_FLAG_BETA_SIGMOID)) return KDA_ERR_INVALID;
+  if (!positive(T)) return KDA_ERR_INVALID;
+  const int rc = check_common(N, H, HV, K, V, scale, dtype);
+  if (rc != KDA_OK) return rc;
+  if (!varlen_shape(K, V, dtype)) return KDA_ERR_UNSUPPORTED;
+  if ((int64_t)HV * (T / 64 + (int64_t)N) > INT32_MAX) return KDA_ERR_UNSUPPORTED;
+  if ((int64_t)N * HV * ((V + 15) / 16) > INT32_MAX) return KDA_ERR_UNSUPPORTED;
+  const size_t need = kda::wy_varlen_workspace_bytes(N, T, HV, K);
+  if (!workspace || workspace_bytes < need) return KDA_ERR_INVALID;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0) return KDA_ERR_INVALID;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(g) || !aligned16(v)) return KDA_ERR_UNSUPPORTED;
+  kda::PrefillArgs a{q, k, v, g, beta, initial_state, final_state, o, N, T, H, HV, K, V, scale,
+                     1, 1, flags};
+  const hipError_t e = kda::launch_prefill_wy_varlen(a, cu_seqlens, workspace,
+                                                     static_cast<hipStream_t>(stream));
   return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 

@@ -126,8 +126,16 @@ __device__ __forceinline__ int tri_off(int row, int c) {
 
 struct WyArgs {
   PrefillArgs p;
-  unsigned char* ws;  // B * HV * NT blocks of Blk<KT>::bytes, (b, hv, chunk) order
-  int NT;             // chunks per sequence
+  unsigned char* ws;  // blocks of Blk<KT>::bytes: B * HV * NT in (b, hv, chunk) order, or, for
+                      // packed sequences, HV * NC in (hv, chunk of the packed list) order
+  int NT;             // chunks per sequence (fixed length)
+  // Packed variable-length sequences (else null): p.B sequences, sequence s = tokens
+  // cu[s] .. cu[s+1] - 1 of one packed batch row; its chunks are coff[s] .. coff[s+1] - 1 of
+  // the packed chunk list, chunk c = ctab[c] = {first token, rows}; NC bounds the chunk count.
+  const int* cu;
+  const int* coff;
+  const int2* ctab;
+  int NC;
 };
 
 // ================================================================ per-chunk factors
@@ -159,7 +167,7 @@ struct LdsA {
 // the 16-token block w; lane (lr, lq) holds token 16w + lr and, for k step s, channels
 // 32s + 8lq..+7. L2N: q and k are L2-normalised here (an instantiation of its own, so the
 // plain path keeps its register budget: two workgroups per CU).
-template <int KT, bool L2N>
+template <int KT, bool L2N, bool VARLEN>
 __global__ __launch_bounds__(256) void factors_kernel(WyArgs a) {
   using L = LdsA<KT>;
   using W = Blk<KT>;
@@ -184,7 +192,7 @@ __global__ __launch_bounds__(256) void factors_kernel(WyArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 15, lq = lane >> 4;
   const int K = p.K, T = p.T, NT = a.NT;
-  const int items = p.B * p.HV * NT;
+  const int items = VARLEN ? p.HV * a.NC : p.B * p.HV * NT;
   const int i_row = 16 * w + lr;  // the lane's token inside the chunk
 
   // Per-lane byte offsets of the 8 channels of each k step; channels >= K (K % 8 == 0) start
@@ -199,11 +207,26 @@ __global__ __launch_bounds__(256) void factors_kernel(WyArgs a) {
 
   bf16x8 rq[NKS], rk[NKS], rg[NKS];
   unsigned rbeta;
+  // tokens of item it: the first (row0, in the packed [B*T] token order) and how many
+  auto item_rows = [&](int it, int& hv, size_t& row0, int& nrow) {
+    if constexpr (VARLEN) {
+      hv = it / a.NC;
+      const int2 e = a.ctab[it - hv * a.NC];
+      row0 = (size_t)e.x;
+      nrow = e.y;
+    } else {
+      const int head = it / NT, n = it - head * NT;
+      const int b = head / p.HV;
+      hv = head - b * p.HV;
+      row0 = (size_t)b * T + n * kC;
+      nrow = min(kC, T - n * kC);
+    }
+  };
   auto prefetch = [&](int it) {
-    const int head = it / NT, n = it - head * NT;
-    const int b = head / p.HV, hv = head - b * p.HV, h = hv / (p.HV / p.H);
-    const int t0 = n * kC, nrow = min(kC, T - t0);
-    const size_t row0 = (size_t)b * T + t0;
+    int hv, nrow;
+    size_t row0;
+    item_rows(it, hv, row0, nrow);
+    const int h = hv / (p.HV / p.H);
     // ranges end at the last token of the sequence: later rows read as zeros
     const auto rq_ = make_rsrc(static_cast<const bf16*>(p.q) + (row0 * p.H + h) * K, (unsigned)(nrow * p.H * K * 2));
     const auto rk_ = make_rsrc(static_cast<const bf16*>(p.k) + (row0 * p.H + h) * K, (unsigned)(nrow * p.H * K * 2));
@@ -222,6 +245,10 @@ __global__ __launch_bounds__(256) void factors_kernel(WyArgs a) {
 
   for (int it = blockIdx.x; it < items; it += gridDim.x) {
     unsigned char* blk = a.ws + (size_t)it * W::bytes;
+    if (VARLEN && a.ctab[it % a.NC].y == 0) {  // past the packed list's last chunk: no block
+      if (it + (int)gridDim.x < items) prefetch(it + gridDim.x);
+      continue;
+    }
 
     // ---------------- in-block cumsum of g (log2 units): d = G_i - G_first, DPP row scan
     float d[NKS][8];
@@ -541,7 +568,7 @@ __device__ __forceinline__ void wait_vmem() {
 // perm32(rho)); the DMA waves stream the next chunk's factors into the other LDS buffer, so
 // the compute waves never wait on memory issue.
 
-template <int KT, int NW>
+template <int KT, int NW, bool VARLEN>
 __global__ __launch_bounds__(64 * (NW + kDmaWaves)) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void state_kernel(WyArgs a) {
   using W = Blk<KT>;
@@ -572,8 +599,21 @@ void state_kernel(WyArgs a) {
     vt_idx = blockIdx.x % nvt;
   }
   const int b = head / p.HV, hv = head - b * p.HV;
-  const int K = p.K, V = p.V, T = p.T, NT = a.NT;
-  const unsigned char* wsh = a.ws + (size_t)head * NT * W::bytes;
+  const int K = p.K, V = p.V;
+  // this sequence's tokens bos .. bos + len - 1 (packed order) and its NT chunk blocks
+  int bos, len, NT;
+  const unsigned char* wsh;
+  if constexpr (VARLEN) {
+    bos = a.cu[b];
+    len = a.cu[b + 1] - bos;
+    NT = a.coff[b + 1] - a.coff[b];
+    wsh = a.ws + ((size_t)hv * a.NC + a.coff[b]) * W::bytes;
+  } else {
+    bos = b * p.T;
+    len = p.T;
+    NT = a.NT;
+    wsh = a.ws + (size_t)head * NT * W::bytes;
+  }
 
   // Both roles pass the same barriers: one before each chunk. Before a buffer is read, the
   // DMA waves have waited for their loads into it; before it is refilled, every compute
@@ -597,8 +637,8 @@ void state_kernel(WyArgs a) {
     bf16x8 rvv[NPL];
     auto load_v = [&](int n) {  // n past the end re-reads the last chunk (no branch)
       n = min(n, NT - 1);
-      const int t0 = n * kC, nrow = min(kC, T - t0);
-      const auto rv_ = make_rsrc(static_cast<const bf16*>(p.v) + (((size_t)b * T + t0) * p.HV + hv) * V,
+      const int t0 = n * kC, nrow = min(kC, len - t0);
+      const auto rv_ = make_rsrc(static_cast<const bf16*>(p.v) + (((size_t)bos + t0) * p.HV + hv) * V,
                                  (unsigned)nrow * rowb);
 #pragma unroll
       for (int e = 0; e < NPL; ++e)
@@ -641,6 +681,7 @@ void state_kernel(WyArgs a) {
       load_v(n + 1);
       warm(n + 1);
     };
+    if (VARLEN && NT == 0) return;  // empty sequence
     load_v(0);
     fill(buf0, 0);
     for (int n = 0; n < NT; n += 2) {
@@ -674,7 +715,7 @@ void state_kernel(WyArgs a) {
   }
 
   auto step = [&](const unsigned char* bk, int n) {
-    const int t0 = n * kC, nrow = min(kC, T - t0);
+    const int t0 = n * kC, nrow = min(kC, len - t0);
     auto frag_q = [&](int tile, int J, int m) {  // rows of Q*Gam / K*Gam
       const int row = 16 * J + lr;
       return load8(bk + tile + (row * RQ + swz<RQ>(row, 4 * m + lq)) * 16);
@@ -761,7 +802,7 @@ void state_kernel(WyArgs a) {
     O[2] = mfma32(fa[3], ub[1], mfma32(fa[2], ub[0], P[2]));
     O[3] = mfma32(fa[5], ub[1], mfma32(fa[4], ub[0], P[3]));
     // stores go out before the state update so they drain under its products
-    const auto ro_ = make_rsrc(static_cast<const bf16*>(p.o) + (((size_t)b * T + t0) * p.HV + hv) * V,
+    const auto ro_ = make_rsrc(static_cast<const bf16*>(p.o) + (((size_t)bos + t0) * p.HV + hv) * V,
                                (unsigned)nrow * rowb);
 #pragma unroll
     for (int I = 0; I < 4; ++I)
@@ -794,18 +835,62 @@ void state_kernel(WyArgs a) {
   }
 }
 
+// Chunk tables of packed sequences (one workgroup). The offsets are clamped into [0, T] and
+// made non-decreasing, and the chunk count is capped at NC (an upper bound for any valid
+// offsets), so malformed offsets give wrong results, never accesses out of range.
+__global__ __launch_bounds__(256) void varlen_table_kernel(const int* __restrict__ cu_in, int nseq,
+                                                           int T, int NC, int* __restrict__ cu,
+                                                           int* __restrict__ coff,
+                                                           int2* __restrict__ ctab) {
+  if (threadIdx.x == 0) {
+    int prev = min(max(cu_in[0], 0), T), c = 0;
+    cu[0] = prev;
+    coff[0] = 0;
+    for (int s = 0; s < nseq; ++s) {
+      int e = min(max(cu_in[s + 1], prev), T);
+      int n = (e - prev + kC - 1) / kC;
+      if (c + n > NC) {
+        n = NC - c;
+        e = prev + n * kC < e ? prev + n * kC : e;
+      }
+      cu[s + 1] = e;
+      c += n;
+      coff[s + 1] = c;
+      prev = e;
+    }
+  }
+  __syncthreads();
+  for (int s = threadIdx.x; s < nseq; s += 256) {
+    const int bos = cu[s], eos = cu[s + 1], c0 = coff[s], c1 = coff[s + 1];
+    for (int c = c0; c < c1; ++c) {
+      const int t = bos + (c - c0) * kC;
+      ctab[c] = make_int2(t, min(kC, eos - t));
+    }
+  }
+  for (int c = coff[nseq] + threadIdx.x; c < NC; c += 256) ctab[c] = make_int2(0, 0);
+}
+
 template <int KT, int NW>
 hipError_t launch_cfg(const WyArgs& a, int cus, hipStream_t stream) {
-  const int items = a.p.B * a.p.HV * a.NT;
+  const int items = a.ctab ? a.p.HV * a.NC : a.p.B * a.p.HV * a.NT;
   const int grid_a = items < 2 * cus ? items : 2 * cus;
-  if (a.p.flags & kFlagQkL2norm)
-    hipLaunchKernelGGL((factors_kernel<KT, true>), dim3(grid_a), dim3(256), 0, stream, a);
+  const bool l2 = a.p.flags & kFlagQkL2norm, vl = a.ctab != nullptr;
+  if (l2 && vl)
+    hipLaunchKernelGGL((factors_kernel<KT, true, true>), dim3(grid_a), dim3(256), 0, stream, a);
+  else if (l2)
+    hipLaunchKernelGGL((factors_kernel<KT, true, false>), dim3(grid_a), dim3(256), 0, stream, a);
+  else if (vl)
+    hipLaunchKernelGGL((factors_kernel<KT, false, true>), dim3(grid_a), dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL((factors_kernel<KT, false>), dim3(grid_a), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((factors_kernel<KT, false, false>), dim3(grid_a), dim3(256), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nvt = (a.p.V + 16 * NW - 1) / (16 * NW);
-  hipLaunchKernelGGL((state_kernel<KT, NW>), dim3(a.p.B * a.p.HV * nvt), dim3(64 * (NW + kDmaWaves)), 0, stream, a);
+  const dim3 grid(a.p.B * a.p.HV * nvt), block(64 * (NW + kDmaWaves));
+  if (vl)
+    hipLaunchKernelGGL((state_kernel<KT, NW, true>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((state_kernel<KT, NW, false>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
@@ -817,12 +902,34 @@ size_t wy_workspace_bytes(int B, int T, int HV, int K) {
   return (size_t)B * HV * ((T + wy::kC - 1) / wy::kC) * wy::block_bytes(K);
 }
 
+namespace wy {
+struct VarlenLayout {
+  int NC;
+  size_t blocks, cu, coff, ctab, total;
+};
+VarlenLayout varlen_layout(int nseq, int T, int HV, int K) {
+  auto al = [](size_t x) { return (x + 255) / 256 * 256; };
+  VarlenLayout l{};
+  l.NC = T / kC + nseq;  // >= the sum over sequences of ceil(length / 64)
+  l.blocks = 0;
+  l.cu = al((size_t)HV * l.NC * block_bytes(K));
+  l.coff = l.cu + al((size_t)(nseq + 1) * 4);
+  l.ctab = l.coff + al((size_t)(nseq + 1) * 4);
+  l.total = l.ctab + al((size_t)l.NC * 8);
+  return l;
+}
+}  // namespace wy
+
+size_t wy_varlen_workspace_bytes(int nseq, int T, int HV, int K) {
+  return wy::varlen_layout(nseq, T, HV, K).total;
+}
+
 // bf16 inputs, K % 8 == 0, 16-byte aligned q/k/g, and a workspace of wy_workspace_bytes.
 // The state pass runs one workgroup per CU (double-buffered LDS); its V tile is the widest
 // of 16, 32 or 64 columns that still gives every CU a workgroup.
-hipError_t launch_prefill_wy(const PrefillArgs& p, void* workspace, hipStream_t stream) {
+static hipError_t launch_wy(const wy::WyArgs& a, hipStream_t stream) {
   using namespace wy;
-  WyArgs a{p, static_cast<unsigned char*>(workspace), (p.T + kC - 1) / kC};
+  const PrefillArgs& p = a.p;
   const int cus = device_cu_count();
   const int heads = p.B * p.HV;
   const int nw = p.V <= 16 ? 1 : (p.V <= 32 || heads * ((p.V + 31) / 32) <= cus) ? 2 : 4;
@@ -830,6 +937,31 @@ hipError_t launch_prefill_wy(const PrefillArgs& p, void* workspace, hipStream_t 
   if (p.K <= 64) return nw == 1 ? launch_cfg<64, 1>(a, cus, stream) : nw == 2 ? launch_cfg<64, 2>(a, cus, stream) : launch_cfg<64, 4>(a, cus, stream);
   if (p.K <= 128) return nw == 1 ? launch_cfg<128, 1>(a, cus, stream) : nw == 2 ? launch_cfg<128, 2>(a, cus, stream) : launch_cfg<128, 4>(a, cus, stream);
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_prefill_wy(const PrefillArgs& p, void* workspace, hipStream_t stream) {
+  using namespace wy;
+  const WyArgs a{p, static_cast<unsigned char*>(workspace), (p.T + kC - 1) / kC, nullptr, nullptr,
+                 nullptr, 0};
+  return launch_wy(a, stream);
+}
+
+// Packed sequences: p.B is the number of sequences, p.T the packed token count; cu_seqlens
+// (device, p.B + 1 offsets) is read by the table kernel only.
+hipError_t launch_prefill_wy_varlen(const PrefillArgs& p, const int* cu_seqlens, void* workspace,
+                                    hipStream_t stream) {
+  using namespace wy;
+  const VarlenLayout l = varlen_layout(p.B, p.T, p.HV, p.K);
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  int* cu = reinterpret_cast<int*>(ws + l.cu);
+  int* coff = reinterpret_cast<int*>(ws + l.coff);
+  int2* ctab = reinterpret_cast<int2*>(ws + l.ctab);
+  hipLaunchKernelGGL(varlen_table_kernel, dim3(1), dim3(256), 0, stream, cu_seqlens, p.B, p.T, l.NC,
+                     cu, coff, ctab);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const WyArgs a{p, ws + l.blocks, 0, cu, coff, ctab, l.NC};
+  return launch_wy(a, stream);
 }
 
 }  // namespace kda

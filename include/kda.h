@@ -113,6 +113,41 @@ int kda_chunk_fwd_ex(const void* q, const void* k, const void* v, const void* g,
                      unsigned flags, void* stream);
 
 /*
+ * Chunked prefill over N variable-length sequences packed along one token axis, each with
+ * its own state: sequence s is tokens cu_seqlens[s] .. cu_seqlens[s+1] - 1, and the state is
+ * reset to initial_state[s] at its first token. The DM-KDAGQA-1.7B-SD model card trains on
+ * packed 8,192-token sequences, and its usage notes point out that the KDA layers have no
+ * padding mask, so sequences of different lengths are batched this way rather than padded.
+ * Same arithmetic per sequence as kda_chunk_fwd_ex.
+ *
+ *   q, k           [T, H, K]      bf16 (the packed [1, T, H, K])
+ *   v              [T, HV, V]     bf16
+ *   g              [T, HV, K]     bf16
+ *   beta           [T, HV]        bf16
+ *   cu_seqlens     [N + 1]        int32 DEVICE memory, 0 <= cu_seqlens[0] <= ... <= cu_seqlens[N]
+ *                                 <= T (usually 0 and T); any length, zero included (an empty
+ *                                 sequence passes its state through). Offsets outside [0, T] or
+ *                                 decreasing are clamped (wrong results, no out-of-range access).
+ *   initial_state  [N, HV, K, V]  float32, or NULL for zeros
+ *   final_state    [N, HV, K, V]  float32 out, or NULL
+ *   o              [T, HV, V]     bf16 out (tokens outside [cu_seqlens[0], cu_seqlens[N]) untouched)
+ *   flags          as for kda_chunk_fwd_ex
+ *   workspace      device memory of at least kda_chunk_fwd_varlen_workspace_size() bytes,
+ *                  256-byte aligned, caller-owned, overwritten; NULL, too small or misaligned:
+ *                  KDA_ERR_INVALID.
+ *
+ * Constraints: N, T, H, HV, K, V >= 1; HV % H == 0; K, V <= 128; bf16 with K % 8 == 0,
+ * V % 8 == 0 and 16-byte aligned q, k, g, v (else KDA_ERR_UNSUPPORTED).
+ */
+size_t kda_chunk_fwd_varlen_workspace_size(int N, int T, int H, int HV, int K, int V, int dtype);
+
+int kda_chunk_fwd_varlen(const void* q, const void* k, const void* v, const void* g,
+                         const void* beta, const int* cu_seqlens, int N,
+                         const float* initial_state, float* final_state, void* o, int T, int H,
+                         int HV, int K, int V, float scale, int dtype, void* workspace,
+                         size_t workspace_bytes, unsigned flags, void* stream);
+
+/*
  * Chunked backward: the gradients of L = <o, dout> + <final_state, dht> with respect to
  * every input of kda_chunk_fwd (K3 README, roadmap row L4: end-to-end backward of the
  * chunked kernels, hand-written gradients dq, dk, dv, dg, dbeta as in row L1; key-

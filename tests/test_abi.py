@@ -30,6 +30,7 @@ def lib():
 def test_header_declares_the_boundary():
     names = _declared_functions()
     for required in ("kda_chunk_fwd", "kda_chunk_fwd_ex", "kda_chunk_fwd_workspace_size",
+                     "kda_chunk_fwd_varlen", "kda_chunk_fwd_varlen_workspace_size", "kda_chunk_bwd",
                      "kda_recurrent_step", "kda_recurrent_step_ex", "kda_status_string",
                      "kda_version"):
         assert required in names
@@ -215,3 +216,44 @@ def test_bwd_workspace_size(lib):
     assert ws(1, 64, 1, 1, 64, 64, 64, 0) == 0        # fp32: no backward
     assert ws(1, 64, 1, 1, 48, 64, 64, 1) == 0
     assert ws(1, 72, 1, 1, 64, 64, 64, 1) == 0        # T % chunk != 0
+
+
+def _varlen(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, cu=FAKE, N=2, s0=None, sT=None, o=FAKE,
+             T=128, H=2, HV=4, K=64, V=64, scale=0.125, dtype=1, ws=ctypes.c_void_p(0x100000),
+             ws_bytes=1 << 40, flags=0)
+    a.update(kw)
+    return lib.kda_chunk_fwd_varlen(a["q"], a["k"], a["v"], a["g"], a["beta"], a["cu"], a["N"],
+                                    a["s0"], a["sT"], a["o"], a["T"], a["H"], a["HV"], a["K"],
+                                    a["V"], a["scale"], a["dtype"], a["ws"], a["ws_bytes"],
+                                    a["flags"], None)
+
+
+@pytest.mark.parametrize("bad,rc", [
+    (dict(cu=None), kda.KDA_ERR_INVALID),
+    (dict(o=None), kda.KDA_ERR_INVALID),
+    (dict(N=0), kda.KDA_ERR_INVALID),
+    (dict(T=0), kda.KDA_ERR_INVALID),
+    (dict(HV=3), kda.KDA_ERR_INVALID),
+    (dict(flags=4), kda.KDA_ERR_INVALID),
+    (dict(ws=None), kda.KDA_ERR_INVALID),
+    (dict(ws_bytes=1024), kda.KDA_ERR_INVALID),
+    (dict(ws=ctypes.c_void_p(0x100080)), kda.KDA_ERR_INVALID),
+    (dict(dtype=0), kda.KDA_ERR_UNSUPPORTED),           # the two-kernel bf16 path only
+    (dict(K=60), kda.KDA_ERR_UNSUPPORTED),
+    (dict(V=36), kda.KDA_ERR_UNSUPPORTED),
+    (dict(K=256), kda.KDA_ERR_UNSUPPORTED),
+    (dict(g=ctypes.c_void_p(0x1004)), kda.KDA_ERR_UNSUPPORTED),
+])
+def test_chunk_fwd_varlen_rejects_invalid_arguments(lib, bad, rc):
+    assert _varlen(lib, **bad) == rc
+
+
+def test_varlen_workspace_size(lib):
+    ws = lib.kda_chunk_fwd_varlen_workspace_size
+    one = ws(1, 64, 1, 1, 64, 64, 1)
+    assert one > 0 and one % 256 == 0
+    assert ws(2, 64, 1, 1, 64, 64, 1) > one        # one more possible partial chunk
+    assert ws(1, 128, 1, 1, 64, 64, 1) > one
+    assert ws(1, 64, 1, 1, 64, 64, 0) == 0         # fp32: no varlen path
+    assert ws(1, 64, 1, 1, 60, 64, 1) == 0
