@@ -24,7 +24,8 @@ import os
 
 import torch
 
-__all__ = ["kda_chunk_fwd", "kda_chunk_fwd_varlen", "kda_chunk_bwd", "kda_recurrent_step", "library", "library_path", "status_string",
+__all__ = ["kda_chunk_fwd", "kda_chunk_fwd_varlen", "kda_chunk_bwd", "kda_recurrent_step",
+           "kda_recurrent_step_slots", "library", "library_path", "status_string",
            "KDA_OK", "KDA_ERR_INVALID", "KDA_ERR_UNSUPPORTED", "KDA_ERR_HIP",
            "KDA_FLAG_QK_L2NORM", "KDA_FLAG_BETA_SIGMOID"]
 
@@ -64,6 +65,8 @@ def library():
     lib.kda_recurrent_step.restype = i
     lib.kda_recurrent_step_ex.argtypes = [vp] * 7 + [i] * 5 + [f, i, ctypes.c_uint, vp]
     lib.kda_recurrent_step_ex.restype = i
+    lib.kda_recurrent_step_slots.argtypes = [vp] * 7 + [i, vp] + [i] * 5 + [f, i, ctypes.c_uint, vp]
+    lib.kda_recurrent_step_slots.restype = i
     lib.kda_status_string.argtypes = [i]
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_version.argtypes = []
@@ -250,5 +253,41 @@ def kda_recurrent_step(q, k, v, g, beta, state, scale=None, qk_l2norm=False, bet
                                        _ptr(state), _ptr(o), B, H, HV, K, V, float(scale),
                                        _DTYPE[dt], _flags(qk_l2norm, beta_sigmoid),
                                        ctypes.c_void_p(stream))
+    _check(rc)
+    return o
+
+
+def kda_recurrent_step_slots(q, k, v, g, beta, state_pool, slots, scale=None, qk_l2norm=False,
+                             beta_sigmoid=False):
+    """One decode token per request against a slot-indexed state pool. q, k [B,H,K];
+    v [B,HV,V]; g [B,HV,K]; beta [B,HV]; state_pool [num_slots,HV,K,V] float32 (updated in
+    place); slots int32 [B] (a slot outside [0, num_slots) gives o = 0 and no update).
+    Returns o [B,HV,V]."""
+    _require(q.is_cuda, "inputs must be on a GPU")
+    dev, dt = q.device, q.dtype
+    _require(dt in _DTYPE, f"unsupported dtype {dt}")
+    if q.dim() == 4:
+        q, k, v, g, beta = q[:, 0], k[:, 0], v[:, 0], g[:, 0], beta[:, 0]
+    B, H, K = q.shape
+    HV, V = v.shape[1], v.shape[2]
+    _require(k.shape == q.shape, "k must match q")
+    _require(tuple(g.shape) == (B, HV, K), "g must be [B, HV, K]")
+    _require(tuple(beta.shape) == (B, HV), "beta must be [B, HV]")
+    _require(state_pool.dim() == 4 and tuple(state_pool.shape[1:]) == (HV, K, V),
+             "state_pool must be [num_slots, HV, K, V]")
+    _check_tensors([("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta)], dt, dev)
+    _check_tensors([("state_pool", state_pool)], torch.float32, dev)
+    _require(slots.is_cuda and slots.device == dev and slots.dtype == torch.int32
+             and tuple(slots.shape) == (B,) and slots.is_contiguous(), "slots must be int32 [B] on the GPU")
+    if scale is None:
+        scale = 1.0 / math.sqrt(K)
+    lib = library()
+    o = torch.empty((B, HV, V), dtype=dt, device=dev)
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        rc = lib.kda_recurrent_step_slots(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                          _ptr(state_pool), _ptr(slots), state_pool.shape[0],
+                                          _ptr(o), B, H, HV, K, V, float(scale), _DTYPE[dt],
+                                          _flags(qk_l2norm, beta_sigmoid), ctypes.c_void_p(stream))
     _check(rc)
     return o

@@ -9,7 +9,8 @@
 namespace kda {
 template <typename Tin>
 hipError_t launch_decode(const void*, const void*, const void*, const void*, const void*, float*,
-                         void*, int, int, int, int, int, float, unsigned, hipStream_t);
+                         void*, int, int, int, int, int, float, unsigned, const int*, int,
+                         hipStream_t);
 hipError_t launch_prefill(const void*, const void*, const void*, const void*, const void*,
                           const float*, float*, void*, int, int, int, int, int, int, float, bool,
                           void*, unsigned, hipStream_t);
@@ -186,9 +187,10 @@ int kda_chunk_bwd(const void* q, const void* k, const void* v, const void* g, co
   return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
-int kda_recurrent_step_ex(const void* q, const void* k, const void* v, const void* g,
-                          const void* beta, float* state, void* o, int B, int H, int HV, int K,
-                          int V, float scale, int dtype, unsigned flags, void* stream) {
+static int recurrent_step(const void* q, const void* k, const void* v, const void* g,
+                          const void* beta, float* state, const int* slots, int nslots, void* o,
+                          int B, int H, int HV, int K, int V, float scale, int dtype,
+                          unsigned flags, void* stream) {
   if (!q || !k || !v || !g || !beta || !state || !o) return KDA_ERR_INVALID;
   if (flags & ~(unsigned)(KDA_FLAG_QK_L2NORM | KDA_FLAG_BETA_SIGMOID)) return KDA_ERR_INVALID;
   const int rc = check_common(B, H, HV, K, V, scale, dtype);
@@ -199,10 +201,26 @@ int kda_recurrent_step_ex(const void* q, const void* k, const void* v, const voi
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const hipError_t e = dtype == KDA_DTYPE_BF16
                            ? kda::launch_decode<kda::bf16>(q, k, v, g, beta, state, o, B, H, HV,
-                                                           K, V, scale, flags, s)
+                                                           K, V, scale, flags, slots, nslots, s)
                            : kda::launch_decode<float>(q, k, v, g, beta, state, o, B, H, HV, K,
-                                                       V, scale, flags, s);
+                                                       V, scale, flags, slots, nslots, s);
   return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+int kda_recurrent_step_ex(const void* q, const void* k, const void* v, const void* g,
+                          const void* beta, float* state, void* o, int B, int H, int HV, int K,
+                          int V, float scale, int dtype, unsigned flags, void* stream) {
+  return recurrent_step(q, k, v, g, beta, state, nullptr, 0, o, B, H, HV, K, V, scale, dtype,
+                        flags, stream);
+}
+
+int kda_recurrent_step_slots(const void* q, const void* k, const void* v, const void* g,
+                             const void* beta, float* state_pool, const int* slots,
+                             int num_slots, void* o, int B, int H, int HV, int K, int V,
+                             float scale, int dtype, unsigned flags, void* stream) {
+  if (!slots || num_slots < 1) return KDA_ERR_INVALID;
+  return recurrent_step(q, k, v, g, beta, state_pool, slots, num_slots, o, B, H, HV, K, V, scale,
+                        dtype, flags, stream);
 }
 
 int kda_recurrent_step(const void* q, const void* k, const void* v, const void* g,

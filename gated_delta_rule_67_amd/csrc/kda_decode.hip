@@ -24,11 +24,14 @@ namespace kda {
 constexpr int kDecodeThreads = 256;
 constexpr int kDecodeMaxRows = 16;  // K <= 128 with >= 8 row groups per workgroup
 
-template <typename Tin, int VSPLIT>
+// SLOTS: the state of row b is slot slots[b] of a [nslots, HV, K, V] pool (a serving cache);
+// a row whose slot is outside [0, nslots) writes zeros to o and leaves the pool alone.
+template <typename Tin, int VSPLIT, bool SLOTS>
 __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(
     const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
     const Tin* __restrict__ g, const Tin* __restrict__ beta, float* __restrict__ state,
-    Tin* __restrict__ o, int H, int HV, int K, int V, float scale, unsigned flags) {
+    Tin* __restrict__ o, int H, int HV, int K, int V, float scale, unsigned flags,
+    const int* __restrict__ slots, int nslots) {
   __shared__ float s_dec[128], s_k[128], s_q[128], s_v[128], s_u[128];
   __shared__ f32x4 s_pa[kDecodeThreads], s_pb[kDecodeThreads];
   __shared__ float s_qk, s_iq, s_ik;  // q.k (raw), scale/|q|, 1/|k| (norms only when asked)
@@ -47,7 +50,16 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(
   const int rg = t / nc;
   const bool active = rg < rgc;
 
-  float* S = state + (size_t)bh * K * V + v0 + 4 * c4;
+  size_t sbh = bh;  // this row's state among [*, HV] states
+  if constexpr (SLOTS) {
+    const int slot = slots[b];
+    if (slot < 0 || slot >= nslots) {  // uniform over the workgroup, before any barrier
+      if (t < vw) o[(size_t)bh * V + v0 + t] = from_f32<Tin>(0.f);
+      return;
+    }
+    sbh = (size_t)slot * HV + hv;
+  }
+  float* S = state + sbh * K * V + v0 + 4 * c4;
 
   // The per-head vectors go first, unconditionally (clamped index), so that one wait
   // covers them while the slab's loads below stay in flight.
@@ -141,11 +153,13 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(
   }
 }
 
-// Host-side launcher (called from the C ABI after validation).
+// Host-side launcher (called from the C ABI after validation). slots: null for a [B, HV, K, V]
+// state, else the per-row slots of a [nslots, HV, K, V] pool.
 template <typename Tin>
 hipError_t launch_decode(const void* q, const void* k, const void* v, const void* g,
                          const void* beta, float* state, void* o, int B, int H, int HV,
-                         int K, int V, float scale, unsigned flags, hipStream_t stream) {
+                         int K, int V, float scale, unsigned flags, const int* slots, int nslots,
+                         hipStream_t stream) {
   const Tin* q_ = static_cast<const Tin*>(q);
   const Tin* k_ = static_cast<const Tin*>(k);
   const Tin* v_ = static_cast<const Tin*>(v);
@@ -154,21 +168,31 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, const void
   Tin* o_ = static_cast<Tin*>(o);
   const int heads = B * HV;
   // Split V in two when that keeps >= 4 workgroups per CU-slot worth of work.
-  if (V % 8 == 0 && heads < 8192) {
-    hipLaunchKernelGGL((decode_step_kernel<Tin, 2>), dim3(heads * 2), dim3(kDecodeThreads), 0,
-                       stream, q_, k_, v_, g_, b_, state, o_, H, HV, K, V, scale, flags);
+  const bool split = V % 8 == 0 && heads < 8192;
+  const dim3 grid(split ? heads * 2 : heads), block(kDecodeThreads);
+  if (slots) {
+    if (split)
+      hipLaunchKernelGGL((decode_step_kernel<Tin, 2, true>), grid, block, 0, stream, q_, k_, v_, g_,
+                         b_, state, o_, H, HV, K, V, scale, flags, slots, nslots);
+    else
+      hipLaunchKernelGGL((decode_step_kernel<Tin, 1, true>), grid, block, 0, stream, q_, k_, v_, g_,
+                         b_, state, o_, H, HV, K, V, scale, flags, slots, nslots);
   } else {
-    hipLaunchKernelGGL((decode_step_kernel<Tin, 1>), dim3(heads), dim3(kDecodeThreads), 0, stream,
-                       q_, k_, v_, g_, b_, state, o_, H, HV, K, V, scale, flags);
+    if (split)
+      hipLaunchKernelGGL((decode_step_kernel<Tin, 2, false>), grid, block, 0, stream, q_, k_, v_, g_,
+                         b_, state, o_, H, HV, K, V, scale, flags, slots, nslots);
+    else
+      hipLaunchKernelGGL((decode_step_kernel<Tin, 1, false>), grid, block, 0, stream, q_, k_, v_, g_,
+                         b_, state, o_, H, HV, K, V, scale, flags, slots, nslots);
   }
   return hipGetLastError();
 }
 
 template hipError_t launch_decode<float>(const void*, const void*, const void*, const void*,
                                          const void*, float*, void*, int, int, int, int, int,
-                                         float, unsigned, hipStream_t);
+                                         float, unsigned, const int*, int, hipStream_t);
 template hipError_t launch_decode<bf16>(const void*, const void*, const void*, const void*,
                                         const void*, float*, void*, int, int, int, int, int,
-                                        float, unsigned, hipStream_t);
+                                        float, unsigned, const int*, int, hipStream_t);
 
 }  // namespace kda

@@ -214,6 +214,22 @@ const char* kda_status_string(int status);
 /* Library version string, e.g. "kda-gfx950 0.1". */
 const char* kda_version(void);
 
+/*
+ * One decode token per request against a slot-indexed state cache (serving with a pool of
+ * per-request states, continuous batching): request b reads and updates state slot slots[b]
+ * of state_pool [num_slots, HV, K, V] (float32) in place. A request whose slot is outside
+ * [0, num_slots) (padding, e.g. -1) gets o = 0 and changes no state. Slots of valid requests
+ * in one call must be distinct (two requests on one slot race). Otherwise as
+ * kda_recurrent_step_ex (K3 README, roadmap row L6: the [B, HV, K, V] decode state).
+ *
+ *   slots       [B] int32 DEVICE memory
+ *   num_slots   >= 1 (else KDA_ERR_INVALID); NULL slots: KDA_ERR_INVALID
+ */
+int kda_recurrent_step_slots(const void* q, const void* k, const void* v, const void* g,
+                             const void* beta, float* state_pool, const int* slots,
+                             int num_slots, void* o, int B, int H, int HV, int K, int V,
+                             float scale, int dtype, unsigned flags, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -31,6 +31,7 @@ def test_header_declares_the_boundary():
     names = _declared_functions()
     for required in ("kda_chunk_fwd", "kda_chunk_fwd_ex", "kda_chunk_fwd_workspace_size",
                      "kda_chunk_fwd_varlen", "kda_chunk_fwd_varlen_workspace_size", "kda_chunk_bwd",
+                     "kda_recurrent_step_slots",
                      "kda_recurrent_step", "kda_recurrent_step_ex", "kda_status_string",
                      "kda_version"):
         assert required in names
@@ -257,3 +258,20 @@ def test_varlen_workspace_size(lib):
     assert ws(1, 128, 1, 1, 64, 64, 1) > one
     assert ws(1, 64, 1, 1, 64, 64, 0) == 0         # fp32: no varlen path
     assert ws(1, 64, 1, 1, 60, 64, 1) == 0
+
+
+@pytest.mark.parametrize("bad,rc", [
+    (dict(slots=None), kda.KDA_ERR_INVALID),
+    (dict(num_slots=0), kda.KDA_ERR_INVALID),
+    (dict(state=None), kda.KDA_ERR_INVALID),
+    (dict(flags=8), kda.KDA_ERR_INVALID),
+    (dict(V=62), kda.KDA_ERR_UNSUPPORTED),
+])
+def test_recurrent_step_slots_rejects_invalid_arguments(lib, bad, rc):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, state=FAKE, slots=FAKE, num_slots=4,
+             o=FAKE, B=2, H=2, HV=4, K=64, V=64, scale=0.125, dtype=1, flags=0)
+    a.update(bad)
+    assert lib.kda_recurrent_step_slots(a["q"], a["k"], a["v"], a["g"], a["beta"], a["state"],
+                                        a["slots"], a["num_slots"], a["o"], a["B"], a["H"],
+                                        a["HV"], a["K"], a["V"], a["scale"], a["dtype"],
+                                        a["flags"], None) == rc

@@ -96,3 +96,44 @@ def test_decode_error_path_raises():
                                torch.zeros(2, 2, 8, dtype=torch.bfloat16, device="cuda"),
                                torch.zeros(2, 2, dtype=torch.bfloat16, device="cuda"),
                                torch.zeros(2, 2, 8, 62, device="cuda"))
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_decode_slot_pool(dtype):
+    """Requests on slots [7, 2, -1, 9] of a 10-slot pool for 3 steps: each valid request
+    against the oracle on its own slot; the padding request gives o = 0; other slots untouched."""
+    B, H, HV, K, V, NS, steps = 4, 2, 4, 64, 64, 10, 3
+    log(f"decode slot pool dtype={dtype} B={B} HV={HV} K=V={K} slots=10")
+    inp = decode_inputs(steps, B, H, HV, K, V, dtype, True, 404)
+    gen = torch.Generator().manual_seed(405)
+    pool0 = 0.1 * torch.randn((NS, HV, K, V), generator=gen)
+    slots = torch.tensor([7, 2, -1, 9], dtype=torch.int32)
+    pool = pool0.cuda().clone()
+    q, k, v, g, beta = (inp[n].cuda() for n in ("q", "k", "v", "g", "beta"))
+    outs = [kda.kda_recurrent_step_slots(q[t], k[t], v[t], g[t], beta[t], pool, slots.cuda(),
+                                         inp["scale"]) for t in range(steps)]
+    torch.cuda.synchronize()
+    G = HV // H
+    for b, slot in enumerate(slots.tolist()):
+        if slot < 0:
+            for t in range(steps):
+                assert torch.count_nonzero(outs[t][b]) == 0
+            continue
+        s_ref = to64(pool0[slot:slot + 1])
+        for t in range(steps):
+            o_ref, s_ref = decode_step(to64(inp["q"][t][b:b + 1]), to64(inp["k"][t][b:b + 1]),
+                                       to64(inp["v"][t][b:b + 1]), to64(inp["g"][t][b:b + 1]),
+                                       to64(inp["beta"][t][b:b + 1]), s_ref, inp["scale"])
+            og = to64(outs[t][b:b + 1])
+            if dtype == "fp32":
+                assert np.max(np.abs(og - o_ref)) <= 1e-5, f"request {b} step {t}"
+            else:
+                assert_parity(og, o_ref, torch.bfloat16, f"o request {b} step {t}")
+        sg = to64(pool[slot:slot + 1])
+        if dtype == "fp32":
+            assert np.max(np.abs(sg - s_ref)) <= 1e-5
+        else:
+            assert_parity(sg, s_ref, torch.bfloat16, f"slot {slot}")
+    for slot in set(range(NS)) - set(slots.tolist()):
+        assert torch.equal(pool[slot].cpu(), pool0[slot]), f"slot {slot} changed"
+    del G
