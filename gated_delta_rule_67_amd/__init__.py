@@ -24,7 +24,8 @@ import os
 
 import torch
 
-__all__ = ["kda_chunk_fwd", "kda_chunk_fwd_varlen", "kda_chunk_bwd", "kda_recurrent_step",
+__all__ = ["kda_chunk_fwd", "kda_chunk_fwd_varlen", "kda_chunk_bwd",
+           "kda_chunk_bwd_varlen", "kda_recurrent_step",
            "kda_recurrent_step_slots", "library", "library_path", "status_string",
            "KDA_OK", "KDA_ERR_INVALID", "KDA_ERR_UNSUPPORTED", "KDA_ERR_HIP",
            "KDA_FLAG_QK_L2NORM", "KDA_FLAG_BETA_SIGMOID"]
@@ -58,6 +59,10 @@ def library():
     lib.kda_chunk_fwd_varlen_workspace_size.argtypes = [i] * 7
     lib.kda_chunk_fwd_varlen_workspace_size.restype = sz
     lib.kda_chunk_bwd.argtypes = [vp] * 14 + [i] * 6 + [f, i, i, vp, sz, vp]
+    lib.kda_chunk_bwd_varlen.argtypes = [vp] * 6 + [i] + [vp] * 9 + [i] * 5 + [f, i, vp, sz, vp]
+    lib.kda_chunk_bwd_varlen.restype = i
+    lib.kda_chunk_bwd_varlen_workspace_size.argtypes = [i] * 7
+    lib.kda_chunk_bwd_varlen_workspace_size.restype = sz
     lib.kda_chunk_bwd.restype = i
     lib.kda_chunk_bwd_workspace_size.argtypes = [i] * 8
     lib.kda_chunk_bwd_workspace_size.restype = sz
@@ -224,6 +229,55 @@ def kda_chunk_bwd(q, k, v, g, beta, do, scale=None, initial_state=None, dht=None
                                ctypes.c_void_p(stream))
     _check(rc)
     return dq, dk, dv, dg, dbeta, dh0
+
+
+def kda_chunk_bwd_varlen(q, k, v, g, beta, do, cu_seqlens, scale=None, initial_state=None,
+                         dht=None, need_dh0=True):
+    """Gradients for kda_chunk_fwd_varlen's inputs (bf16, packed sequences). Token tensors
+    [1,T,...] (or [T,...]); cu_seqlens int32 [N+1]; initial_state, dht [N,HV,K,V] float32 or
+    None. Returns (dq, dk, dv, dg, dbeta shaped like their inputs, dh0 [N,HV,K,V] or None)."""
+    _require(q.is_cuda, "inputs must be on a GPU")
+    dev, dt = q.device, q.dtype
+    _require(dt in _DTYPE, f"unsupported dtype {dt}")
+    squeeze = q.dim() == 3
+    if not squeeze:
+        _require(q.shape[0] == 1, "packed inputs have batch size 1")
+        q, k, v, g, beta, do = q[0], k[0], v[0], g[0], beta[0], do[0]
+    T, H, K = q.shape
+    HV, V = v.shape[1], v.shape[2]
+    _require(k.shape == q.shape, "k must match q")
+    _require(tuple(v.shape) == (T, HV, V) and tuple(do.shape) == (T, HV, V), "v, do must be [T, HV, V]")
+    _require(tuple(g.shape) == (T, HV, K), "g must be [T, HV, K]")
+    _require(tuple(beta.shape) == (T, HV), "beta must be [T, HV]")
+    _check_tensors([("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("do", do)], dt, dev)
+    _require(cu_seqlens.is_cuda and cu_seqlens.device == dev and cu_seqlens.dtype == torch.int32
+             and cu_seqlens.dim() == 1 and cu_seqlens.is_contiguous(), "cu_seqlens must be int32 on the GPU")
+    N = cu_seqlens.numel() - 1
+    _require(N >= 1, "cu_seqlens needs at least two offsets")
+    for name, t in (("initial_state", initial_state), ("dht", dht)):
+        if t is not None:
+            _require(tuple(t.shape) == (N, HV, K, V), f"{name} must be [N, HV, K, V]")
+            _check_tensors([(name, t)], torch.float32, dev)
+    if scale is None:
+        scale = 1.0 / math.sqrt(K)
+    lib = library()
+    dq, dk = torch.empty_like(q), torch.empty_like(k)
+    dv, dg, dbeta = torch.empty_like(v), torch.empty_like(g), torch.empty_like(beta)
+    dh0 = torch.empty((N, HV, K, V), dtype=torch.float32, device=dev) if need_dh0 else None
+    ws_bytes = lib.kda_chunk_bwd_varlen_workspace_size(N, T, H, HV, K, V, _DTYPE[dt])
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        rc = lib.kda_chunk_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                      _ptr(cu_seqlens), N, _ptr(initial_state), _ptr(do),
+                                      _ptr(dht), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg),
+                                      _ptr(dbeta), _ptr(dh0), T, H, HV, K, V, float(scale),
+                                      _DTYPE[dt], _ptr(ws), ws_bytes, ctypes.c_void_p(stream))
+    _check(rc)
+    outs = (dq, dk, dv, dg, dbeta)
+    if not squeeze:
+        outs = tuple(x.unsqueeze(0) for x in outs)
+    return outs + (dh0,)
 
 
 def kda_recurrent_step(q, k, v, g, beta, state, scale=None, qk_l2norm=False, beta_sigmoid=False):

@@ -31,6 +31,7 @@
 // <= 1 except exp(G_r - G_j) for j in block r's own block and exp(G_i - G_e) for i in e's,
 // which stay below e^75 when g >= -5.
 #include "kda_device.h"
+#include "kda_varlen.h"
 
 namespace kda {
 namespace bwd {
@@ -63,7 +64,68 @@ struct BwdArgs {
   bf16* ut;               // [B*HV][NT*64][V]
   float* dq32;            // [B, T, HV, K] per value head (G > 1), else null
   float* dk32;
+  // Packed variable-length sequences (else null): B sequences over T packed tokens, tables as
+  // in kda_varlen.h; chunk slots are (hv, packed chunk), HV * NC of them.
+  const int* cu;
+  const int* coff;
+  const int2* ctab;
+  int NC;
 };
+
+// The chunk a prep / local item stands for: its value head, its first token in the packed
+// [B * T] token order, its rows (0: no chunk, the item does nothing), and its slot (the index
+// of its prep block and of its saved per-chunk tensors, which is the item itself).
+struct Chunk {
+  int hv, rows;
+  size_t row0, slot;
+};
+__device__ __forceinline__ Chunk item_chunk(const BwdArgs& a, int item) {
+  Chunk ch;
+  if (a.ctab) {
+    ch.hv = item / a.NC;
+    const int2 e = a.ctab[item - ch.hv * a.NC];
+    ch.row0 = (size_t)e.x;
+    ch.rows = e.y;
+  } else {
+    const int n = item % a.NT, head = item / a.NT, b = head / a.HV;
+    ch.hv = head - b * a.HV;
+    ch.row0 = (size_t)b * a.T + n * kC;
+    ch.rows = min(kC, a.T - n * kC);
+  }
+  ch.slot = (size_t)item;
+  return ch;
+}
+
+// The chunks of sequence (fixed length: batch row) s for value head hv, in order: chunk n
+// has slot slot0 + n; seq_rows gives its first token and rows.
+struct SeqChunks {
+  int nch, c0;
+  size_t slot0;
+};
+__device__ __forceinline__ SeqChunks seq_chunks(const BwdArgs& a, int s, int hv) {
+  SeqChunks q;
+  if (a.ctab) {
+    q.c0 = a.coff[s];
+    q.nch = a.coff[s + 1] - q.c0;
+    q.slot0 = (size_t)hv * a.NC + q.c0;
+  } else {
+    q.c0 = 0;
+    q.nch = a.NT;
+    q.slot0 = ((size_t)s * a.HV + hv) * a.NT;
+  }
+  return q;
+}
+__device__ __forceinline__ void seq_rows(const BwdArgs& a, const SeqChunks& q, int s, int n,
+                                         size_t& row0, int& rows) {
+  if (a.ctab) {
+    const int2 e = a.ctab[q.c0 + n];
+    row0 = (size_t)e.x;
+    rows = e.y;
+  } else {
+    row0 = (size_t)s * a.T + n * kC;
+    rows = min(kC, a.T - n * kC);
+  }
+}
 
 // One chunk's prep block (bytes).
 template <int KT>
@@ -241,19 +303,18 @@ __global__ __launch_bounds__(256) void prep_kernel(BwdArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int lr = lane & 15, lq = lane >> 4;
-  const int item = blockIdx.x;
-  const int n = item % a.NT, head = item / a.NT;
-  const int b = head / a.HV, hv = head - b * a.HV, hh = hv / (a.HV / a.H);
-  const int t0 = n * kC, nrow = min(kC, a.T - t0);
+  const Chunk ch = item_chunk(a, blockIdx.x);
+  if (ch.rows == 0) return;  // past the packed list's last chunk
+  const int hv = ch.hv, hh = hv / (a.HV / a.H), nrow = ch.rows;
   const unsigned qrow = (unsigned)(a.H * KT), grow = (unsigned)(a.HV * KT);
-  const bf16* qb = a.q + ((size_t)b * a.T + t0) * qrow + (size_t)hh * KT;
-  const bf16* kb = a.k + ((size_t)b * a.T + t0) * qrow + (size_t)hh * KT;
-  const bf16* gb = a.g + ((size_t)b * a.T + t0) * grow + (size_t)hv * KT;
-  unsigned char* blk = a.blocks + (size_t)item * P::bytes;
+  const bf16* qb = a.q + ch.row0 * qrow + (size_t)hh * KT;
+  const bf16* kb = a.k + ch.row0 * qrow + (size_t)hh * KT;
+  const bf16* gb = a.g + ch.row0 * grow + (size_t)hv * KT;
+  unsigned char* blk = a.blocks + ch.slot * P::bytes;
 
   stage_qkg<KT, 256>(sq, sk, G, PK, PG, qb, kb, gb, qrow, grow, nrow, tid);
   if (tid < kC) {
-    const float bv = tid < nrow ? ldf(a.beta + ((size_t)b * a.T + t0 + tid) * a.HV + hv) : 0.f;
+    const float bv = tid < nrow ? ldf(a.beta + (ch.row0 + tid) * a.HV + hv) : 0.f;
     sb[tid] = bv;
     reinterpret_cast<float*>(blk + P::beta)[tid] = bv;
   }
@@ -505,10 +566,11 @@ __global__ __launch_bounds__(64 * NW) void fwd_sweep_kernel(BwdArgs a) {
   int head, vt_idx;
   sweep_tile(nvt, a.B * a.HV, head, vt_idx);
   const int b = head / a.HV, hv = head - b * a.HV;
-  const int V = a.V, T = a.T;
+  const int V = a.V;
   const int vc = vt_idx * BV + 16 * w + lr;  // this lane's column
   const bool vok = vc < V;
   const unsigned vrow = (unsigned)(a.HV * V);
+  const SeqChunks sq_ = seq_chunks(a, b, hv);
 
   f32x4 S[NCT];
 #pragma unroll
@@ -522,7 +584,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_sweep_kernel(BwdArgs a) {
   bf16x8 p1[N1], p2[N2], p3[N3], pv[NV];
   float pgam = 0.f, pbt = 0.f;
   auto fetch = [&](int n) {
-    const unsigned char* blk = a.blocks + ((size_t)head * a.NT + n) * P::bytes;
+    const unsigned char* blk = a.blocks + (sq_.slot0 + n) * P::bytes;
 #pragma unroll
     for (int e = 0; e < N1; ++e) p1[e] = ld8(blk + P::kg + 16 * (tid + NTH * e));
 #pragma unroll
@@ -531,9 +593,10 @@ __global__ __launch_bounds__(64 * NW) void fwd_sweep_kernel(BwdArgs a) {
     for (int e = 0; e < N3; ++e) p3[e] = ld8(blk + P::tm + 16 * (tid + NTH * e));
     if (tid < KT) pgam = reinterpret_cast<const float*>(blk + P::gam)[tid];
     if (tid < kC) pbt = reinterpret_cast<const float*>(blk + P::beta)[tid];
-    const int t0 = n * kC, nrow = min(kC, T - t0);
-    const auto rv = rsrc(a.v + ((size_t)b * T + t0) * vrow + (size_t)hv * V,
-                         ((unsigned)(nrow - 1) * vrow + V) * 2);
+    size_t row0;
+    int nrow;
+    seq_rows(a, sq_, b, n, row0, nrow);
+    const auto rv = rsrc(a.v + row0 * vrow + (size_t)hv * V, ((unsigned)(nrow - 1) * vrow + V) * 2);
 #pragma unroll
     for (int e = 0; e < NV; ++e) {
       const int u = tid + NTH * e, r = u / (BV / 8), col = vt_idx * BV + 8 * (u % (BV / 8));
@@ -566,17 +629,18 @@ __global__ __launch_bounds__(64 * NW) void fwd_sweep_kernel(BwdArgs a) {
     }
   };
 
-  fetch(0);
-  for (int n = 0; n < a.NT; ++n) {
+  const int NT = sq_.nch;
+  if (NT > 0) fetch(0);
+  for (int n = 0; n < NT; ++n) {
     __syncthreads();
     put();
     // h of this chunk, transposed into this wave's LDS rows
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) st4(s_ht + lr * PK + 16 * ct + 4 * lq, S[ct]);
-    if (n + 1 < a.NT) fetch(n + 1);
+    if (n + 1 < NT) fetch(n + 1);
     __syncthreads();
     // X = Kg h, W0 = V - X, Y = beta W0
-    const size_t trow = ((size_t)head * a.NT + n) * kC;
+    const size_t trow = (sq_.slot0 + n) * kC;
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
       f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -609,8 +673,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_sweep_kernel(BwdArgs a) {
       mmaK<kC>(S[ct], s_kct + 16 * ct * kPC, kPC, s_uu, kPC, lane);
     }
     // h of this chunk to the workspace (its LDS copy is intact until the next chunk)
-    store_state_tile<KT>(a.h + ((size_t)head * a.NT + n) * KT * V, V, vt_idx * BV + 16 * w, s_ht,
-                         PK, lane);
+    store_state_tile<KT>(a.h + (sq_.slot0 + n) * KT * V, V, vt_idx * BV + 16 * w, s_ht, PK, lane);
   }
 }
 
@@ -641,10 +704,11 @@ __global__ __launch_bounds__(64 * NW) void rev_sweep_kernel(BwdArgs a) {
   int head, vt_idx;
   sweep_tile(nvt, a.B * a.HV, head, vt_idx);
   const int b = head / a.HV, hv = head - b * a.HV;
-  const int V = a.V, T = a.T;
+  const int V = a.V;
   const int vc = vt_idx * BV + 16 * w + lr;
   const bool vok = vc < V;
   const unsigned vrow = (unsigned)(a.HV * V);
+  const SeqChunks sq_ = seq_chunks(a, b, hv);
 
   f32x4 D[NCT];
 #pragma unroll
@@ -658,7 +722,7 @@ __global__ __launch_bounds__(64 * NW) void rev_sweep_kernel(BwdArgs a) {
   bf16x8 p1[N1], p2[N2], p3[N2], p4[N3], p5[N3], pd[ND];
   float pgam = 0.f, pbt = 0.f;
   auto fetch = [&](int n) {
-    const unsigned char* blk = a.blocks + ((size_t)head * a.NT + n) * P::bytes;
+    const unsigned char* blk = a.blocks + (sq_.slot0 + n) * P::bytes;
 #pragma unroll
     for (int e = 0; e < N1; ++e) p1[e] = ld8(blk + P::kc + 16 * (tid + NTH * e));
 #pragma unroll
@@ -673,9 +737,10 @@ __global__ __launch_bounds__(64 * NW) void rev_sweep_kernel(BwdArgs a) {
     }
     if (tid < KT) pgam = reinterpret_cast<const float*>(blk + P::gam)[tid];
     if (tid < kC) pbt = reinterpret_cast<const float*>(blk + P::beta)[tid];
-    const int t0 = n * kC, nrow = min(kC, T - t0);
-    const auto rd = rsrc(a.dout + ((size_t)b * T + t0) * vrow + (size_t)hv * V,
-                         ((unsigned)(nrow - 1) * vrow + V) * 2);
+    size_t row0;
+    int nrow;
+    seq_rows(a, sq_, b, n, row0, nrow);
+    const auto rd = rsrc(a.dout + row0 * vrow + (size_t)hv * V, ((unsigned)(nrow - 1) * vrow + V) * 2);
 #pragma unroll
     for (int e = 0; e < ND; ++e) {
       const int u = tid + NTH * e, r = u / (BV / 8), col = vt_idx * BV + 8 * (u % (BV / 8));
@@ -712,8 +777,9 @@ __global__ __launch_bounds__(64 * NW) void rev_sweep_kernel(BwdArgs a) {
     }
   };
 
-  fetch(a.NT - 1);
-  for (int n = a.NT - 1; n >= 0; --n) {
+  const int NT = sq_.nch;
+  if (NT > 0) fetch(NT - 1);
+  for (int n = NT - 1; n >= 0; --n) {
     __syncthreads();
     put();
     // dS reaching the state that leaves this chunk, transposed into this wave's LDS rows
@@ -730,7 +796,7 @@ __global__ __launch_bounds__(64 * NW) void rev_sweep_kernel(BwdArgs a) {
       st4(s_dut + lr * kPC + 16 * I + 4 * lq, a.scale * p + q);
     }
     // Ut = T^T dU; beta Ut
-    const size_t trow = ((size_t)head * a.NT + n) * kC;
+    const size_t trow = (sq_.slot0 + n) * kC;
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
       f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -754,8 +820,8 @@ __global__ __launch_bounds__(64 * NW) void rev_sweep_kernel(BwdArgs a) {
       for (int r = 0; r < 4; ++r) D[ct][r] = D[ct][r] * s_gam[16 * ct + 4 * lq + r] + a.scale * p[r] - q[r];
     }
     // dS of this chunk to the workspace (its LDS copy is intact until the next chunk)
-    store_state_tile<KT>(a.dsn + ((size_t)head * a.NT + n) * KT * V, V, vt_idx * BV + 16 * w,
-                         s_dst, PK, lane);
+    store_state_tile<KT>(a.dsn + (sq_.slot0 + n) * KT * V, V, vt_idx * BV + 16 * w, s_dst, PK,
+                         lane);
   }
   if (a.dh0 && vok)
 #pragma unroll
@@ -910,19 +976,19 @@ __global__ __launch_bounds__(64 * kLocalWaves) void local_kernel(BwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, w8 = tid >> 6;
   const int w = w8 & 3, ch = w8 >> 2;
   const int lr = lane & 15, lq = lane >> 4;
-  const int item = blockIdx.x;
-  const int n = item % a.NT, head = item / a.NT;
-  const int b = head / a.HV, hv = head - b * a.HV, hh = hv / (a.HV / a.H);
-  const int V = a.V, T = a.T;
-  const int t0 = n * kC, nrow = min(kC, T - t0);
+  const Chunk cr = item_chunk(a, blockIdx.x);
+  if (cr.rows == 0) return;  // past the packed list's last chunk
+  const int hv = cr.hv, hh = hv / (a.HV / a.H), nrow = cr.rows;
+  const int V = a.V;
+  const size_t row0 = cr.row0;  // first token of the chunk, packed [B * T] order
   const unsigned qrow = (unsigned)(a.H * KT), grow = (unsigned)(a.HV * KT);
-  const bf16* qb = a.q + ((size_t)b * T + t0) * qrow + (size_t)hh * KT;
-  const bf16* kb = a.k + ((size_t)b * T + t0) * qrow + (size_t)hh * KT;
-  const bf16* gb = a.g + ((size_t)b * T + t0) * grow + (size_t)hv * KT;
-  const unsigned char* blk = a.blocks + (size_t)item * P::bytes;
-  const size_t trow = ((size_t)head * a.NT + n) * kC;
-  const bf16* hsrc = a.h + ((size_t)head * a.NT + n) * KT * V;
-  const bf16* dsrc = a.dsn + ((size_t)head * a.NT + n) * KT * V;
+  const bf16* qb = a.q + row0 * qrow + (size_t)hh * KT;
+  const bf16* kb = a.k + row0 * qrow + (size_t)hh * KT;
+  const bf16* gb = a.g + row0 * grow + (size_t)hv * KT;
+  const unsigned char* blk = a.blocks + cr.slot * P::bytes;
+  const size_t trow = cr.slot * kC;
+  const bf16* hsrc = a.h + cr.slot * KT * V;
+  const bf16* dsrc = a.dsn + cr.slot * KT * V;
   const int rw = 16 * w, ew = 16 * w + 15;  // first and last token of this wave's block
   const int c0 = ch * (KT / 2);             // first channel of this wave's half
   const unsigned vrow = (unsigned)(a.HV * V);
@@ -930,8 +996,7 @@ __global__ __launch_bounds__(64 * kLocalWaves) void local_kernel(BwdArgs a) {
   // this wave's rows of dO and Ut (and W0) as MFMA A operands, straight from memory
   bf16x8 fdo[4], fut[4], fw0[4];
   {
-    const auto rdo = rsrc(a.dout + ((size_t)b * T + t0) * vrow + (size_t)hv * V,
-                          ((unsigned)(nrow - 1) * vrow + V) * 2);
+    const auto rdo = rsrc(a.dout + row0 * vrow + (size_t)hv * V, ((unsigned)(nrow - 1) * vrow + V) * 2);
     const int row = rw + lr;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -1137,7 +1202,7 @@ __global__ __launch_bounds__(64 * kLocalWaves) void local_kernel(BwdArgs a) {
       const float kv = static_cast<float>(sk[i * PK + c]);
       dgs[i * PG + c] = qv * dq + kv * (dpos - dneg);
       if (i < nrow) {
-        const size_t t = (size_t)b * T + t0 + i;
+        const size_t t = row0 + i;
         if (G_ == 1) {
           a.dq[(t * a.H + hh) * KT + c] = static_cast<bf16>(dq);
           a.dk[(t * a.H + hh) * KT + c] = static_cast<bf16>(dk);
@@ -1153,7 +1218,7 @@ __global__ __launch_bounds__(64 * kLocalWaves) void local_kernel(BwdArgs a) {
     float run = lx[c] + lx[KT + c] + lx[2 * KT + c] + lx[3 * KT + c] + ex(G[(kC - 1) * PG + c]) * lx2[c];
     for (int i = kC - 1; i >= 0; --i) {
       run += dgs[i * PG + c];
-      if (i < nrow) a.dg[(((size_t)b * T + t0 + i) * a.HV + hv) * KT + c] = static_cast<bf16>(run);
+      if (i < nrow) a.dg[((row0 + i) * a.HV + hv) * KT + c] = static_cast<bf16>(run);
     }
   }
   if (ch == 0) {  // dv = beta Ut, this block's rows from the A fragments the wave holds
@@ -1166,12 +1231,12 @@ __global__ __launch_bounds__(64 * kLocalWaves) void local_kernel(BwdArgs a) {
           bf16x8 y;
 #pragma unroll
           for (int e = 0; e < 8; ++e) y[e] = static_cast<bf16>(sb[i] * static_cast<float>(fut[x][e]));
-          st8(a.dv + (((size_t)b * T + t0 + i) * a.HV + hv) * V + k0, y);
+          st8(a.dv + ((row0 + i) * a.HV + hv) * V + k0, y);
         }
       }
     }
   }
-  if (tid < nrow) a.dbeta[((size_t)b * T + t0 + tid) * a.HV + hv] = static_cast<bf16>(db1[tid] + db2[tid]);
+  if (tid < nrow) a.dbeta[(row0 + tid) * a.HV + hv] = static_cast<bf16>(db1[tid] + db2[tid]);
 }
 
 // dq, dk: sum of the G value heads of each q/k head (fp32 -> bf16)
@@ -1189,32 +1254,47 @@ __global__ __launch_bounds__(256) void gva_reduce_kernel(const float* __restrict
 }
 
 struct Layout {
-  size_t blocks, h, dsn, u, w0, ut, dq32, dk32, total;
+  size_t blocks, h, dsn, u, w0, ut, dq32, dk32, cu, coff, ctab, total;
 };
 
-Layout layout(int B, int T, int H, int HV, int K, int V) {
-  const int NT = (T + kC - 1) / kC;
-  const size_t heads = (size_t)B * HV;
+// slots: chunk slots (B * HV * NT, or HV * NC when packed); rows: tokens (B * T); nseq: packed
+// sequences (0: fixed length).
+Layout layout(size_t slots, size_t rows, int H, int HV, int K, int V, int nseq, int NC) {
   auto al = [](size_t x) { return (x + 255) / 256 * 256; };
   Layout l{};
   size_t off = 0;
-  l.blocks = off; off += al(heads * NT * prep_block_bytes(K));
-  l.h = off;      off += al(heads * NT * (size_t)K * V * 2);
-  l.dsn = off;    off += al(heads * NT * (size_t)K * V * 2);
-  l.u = off;      off += al(heads * NT * kC * (size_t)V * 2);
-  l.w0 = off;     off += al(heads * NT * kC * (size_t)V * 2);
-  l.ut = off;     off += al(heads * NT * kC * (size_t)V * 2);
+  l.blocks = off; off += al(slots * prep_block_bytes(K));
+  l.h = off;      off += al(slots * (size_t)K * V * 2);
+  l.dsn = off;    off += al(slots * (size_t)K * V * 2);
+  l.u = off;      off += al(slots * kC * (size_t)V * 2);
+  l.w0 = off;     off += al(slots * kC * (size_t)V * 2);
+  l.ut = off;     off += al(slots * kC * (size_t)V * 2);
   if (HV != H) {
-    l.dq32 = off; off += al((size_t)B * T * HV * K * 4);
-    l.dk32 = off; off += al((size_t)B * T * HV * K * 4);
+    l.dq32 = off; off += al(rows * HV * K * 4);
+    l.dk32 = off; off += al(rows * HV * K * 4);
+  }
+  if (nseq > 0) {
+    l.cu = off;   off += al((size_t)(nseq + 1) * 4);
+    l.coff = off; off += al((size_t)(nseq + 1) * 4);
+    l.ctab = off; off += al((size_t)NC * 8);
   }
   l.total = off;
   return l;
 }
 
+Layout fixed_layout(int B, int T, int H, int HV, int K, int V) {
+  const size_t NT = (T + kC - 1) / kC;
+  return layout((size_t)B * HV * NT, (size_t)B * T, H, HV, K, V, 0, 0);
+}
+
+Layout varlen_layout(int nseq, int T, int H, int HV, int K, int V) {
+  const int NC = varlen_chunk_bound(nseq, T);
+  return layout((size_t)HV * NC, (size_t)T, H, HV, K, V, nseq, NC);
+}
+
 template <int KT>
 hipError_t launch_cfg(BwdArgs a, hipStream_t stream) {
-  const int items = a.B * a.HV * a.NT;
+  const int items = a.ctab ? a.HV * a.NC : a.B * a.HV * a.NT;
   hipLaunchKernelGGL((prep_kernel<KT>), dim3(items), dim3(256), 0, stream, a);
   constexpr int NW = 2;
   const int sweeps = a.B * a.HV * ((a.V + 16 * NW - 1) / (16 * NW));
@@ -1222,12 +1302,12 @@ hipError_t launch_cfg(BwdArgs a, hipStream_t stream) {
   hipLaunchKernelGGL((rev_sweep_kernel<KT, NW>), dim3(sweeps), dim3(64 * NW), 0, stream, a);
   hipLaunchKernelGGL((local_kernel<KT>), dim3(items), dim3(64 * kLocalWaves), 0, stream, a);
   if (a.HV != a.H) {
-    const size_t n = (size_t)a.B * a.T * a.H * KT;
-    const unsigned grid = (unsigned)((n + 255) / 256);
-    hipLaunchKernelGGL(gva_reduce_kernel, dim3(grid), dim3(256), 0, stream, a.dq32, a.dq,
-                       (size_t)a.B * a.T, a.H, a.HV / a.H, KT);
-    hipLaunchKernelGGL(gva_reduce_kernel, dim3(grid), dim3(256), 0, stream, a.dk32, a.dk,
-                       (size_t)a.B * a.T, a.H, a.HV / a.H, KT);
+    const size_t rows = a.ctab ? (size_t)a.T : (size_t)a.B * a.T;  // packed: one row of T tokens
+    const unsigned grid = (unsigned)((rows * a.H * KT + 255) / 256);
+    hipLaunchKernelGGL(gva_reduce_kernel, dim3(grid), dim3(256), 0, stream, a.dq32, a.dq, rows,
+                       a.H, a.HV / a.H, KT);
+    hipLaunchKernelGGL(gva_reduce_kernel, dim3(grid), dim3(256), 0, stream, a.dk32, a.dk, rows,
+                       a.H, a.HV / a.H, KT);
   }
   return hipGetLastError();
 }
@@ -1235,18 +1315,24 @@ hipError_t launch_cfg(BwdArgs a, hipStream_t stream) {
 }  // namespace bwd
 
 size_t bwd_workspace_bytes(int B, int T, int H, int HV, int K, int V) {
-  return bwd::layout(B, T, H, HV, K, V).total;
+  return bwd::fixed_layout(B, T, H, HV, K, V).total;
+}
+
+size_t bwd_varlen_workspace_bytes(int nseq, int T, int H, int HV, int K, int V) {
+  return bwd::varlen_layout(nseq, T, H, HV, K, V).total;
 }
 
 // Inputs validated by the C ABI: bf16, K in {32, 64, 128}, V % 16 == 0, V <= 128, workspace of
-// bwd_workspace_bytes, 256-byte aligned; q, k, v, g, dout 16-byte aligned.
+// bwd_workspace_bytes (or bwd_varlen_workspace_bytes with cu_seqlens), 256-byte aligned; q, k,
+// v, g, dout, dv 16-byte aligned. cu_seqlens (device, B + 1 offsets) non-null: B packed
+// sequences over T tokens.
 hipError_t launch_chunk_bwd(const void* q, const void* k, const void* v, const void* g,
-                            const void* beta, const float* s0, const void* dout, const float* dht,
-                            void* dq, void* dk, void* dv, void* dg, void* dbeta, float* dh0,
-                            int B, int T, int H, int HV, int K, int V, float scale,
-                            void* workspace, hipStream_t stream) {
+                            const void* beta, const int* cu_seqlens, const float* s0,
+                            const void* dout, const float* dht, void* dq, void* dk, void* dv,
+                            void* dg, void* dbeta, float* dh0, int B, int T, int H, int HV, int K,
+                            int V, float scale, void* workspace, hipStream_t stream) {
   using namespace bwd;
-  const Layout l = layout(B, T, H, HV, K, V);
+  const Layout l = cu_seqlens ? varlen_layout(B, T, H, HV, K, V) : fixed_layout(B, T, H, HV, K, V);
   unsigned char* ws = static_cast<unsigned char*>(workspace);
   BwdArgs a{};
   a.q = static_cast<const bf16*>(q);
@@ -1274,6 +1360,17 @@ hipError_t launch_chunk_bwd(const void* q, const void* k, const void* v, const v
   a.ut = reinterpret_cast<bf16*>(ws + l.ut);
   a.dq32 = HV != H ? reinterpret_cast<float*>(ws + l.dq32) : nullptr;
   a.dk32 = HV != H ? reinterpret_cast<float*>(ws + l.dk32) : nullptr;
+  if (cu_seqlens) {
+    a.NC = varlen_chunk_bound(B, T);
+    int* cu = reinterpret_cast<int*>(ws + l.cu);
+    int* coff = reinterpret_cast<int*>(ws + l.coff);
+    int2* ctab = reinterpret_cast<int2*>(ws + l.ctab);
+    hipLaunchKernelGGL(varlen_table_kernel, dim3(1), dim3(256), 0, stream, cu_seqlens, B, T, a.NC,
+                       cu, coff, ctab);
+    a.cu = cu;
+    a.coff = coff;
+    a.ctab = ctab;
+  }
   if (K == 32) return launch_cfg<32>(a, stream);
   if (K == 64) return launch_cfg<64>(a, stream);
   if (K == 128) return launch_cfg<128>(a, stream);

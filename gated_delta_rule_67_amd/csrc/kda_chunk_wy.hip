@@ -33,6 +33,7 @@
 // blocks use (x_i R_i).(k_j C_j); block I > J uses the column factor k_j C_j exp(G_rI - G_rJ);
 // Gam_i = exp(G_rI) R_i and Gam_C/Gam_j = exp(G_C - G_rJ) C_j.
 #include "kda_device.h"
+#include "kda_varlen.h"
 
 namespace kda {
 namespace wy {
@@ -833,41 +834,6 @@ void state_kernel(WyArgs a) {
         if (vok && c < K) sT[(size_t)c * V + vc] = S[ct][r];
       }
   }
-}
-
-// Chunk tables of packed sequences (one workgroup). The offsets are clamped into [0, T] and
-// made non-decreasing, and the chunk count is capped at NC (an upper bound for any valid
-// offsets), so malformed offsets give wrong results, never accesses out of range.
-__global__ __launch_bounds__(256) void varlen_table_kernel(const int* __restrict__ cu_in, int nseq,
-                                                           int T, int NC, int* __restrict__ cu,
-                                                           int* __restrict__ coff,
-                                                           int2* __restrict__ ctab) {
-  if (threadIdx.x == 0) {
-    int prev = min(max(cu_in[0], 0), T), c = 0;
-    cu[0] = prev;
-    coff[0] = 0;
-    for (int s = 0; s < nseq; ++s) {
-      int e = min(max(cu_in[s + 1], prev), T);
-      int n = (e - prev + kC - 1) / kC;
-      if (c + n > NC) {
-        n = NC - c;
-        e = prev + n * kC < e ? prev + n * kC : e;
-      }
-      cu[s + 1] = e;
-      c += n;
-      coff[s + 1] = c;
-      prev = e;
-    }
-  }
-  __syncthreads();
-  for (int s = threadIdx.x; s < nseq; s += 256) {
-    const int bos = cu[s], eos = cu[s + 1], c0 = coff[s], c1 = coff[s + 1];
-    for (int c = c0; c < c1; ++c) {
-      const int t = bos + (c - c0) * kC;
-      ctab[c] = make_int2(t, min(kC, eos - t));
-    }
-  }
-  for (int c = coff[nseq] + threadIdx.x; c < NC; c += 256) ctab[c] = make_int2(0, 0);
 }
 
 template <int KT, int NW>

@@ -183,6 +183,24 @@ int kda_chunk_bwd(const void* q, const void* k, const void* v, const void* g,
                   void* stream);
 
 /*
+ * kda_chunk_bwd for N packed variable-length sequences, each with its own state (the
+ * sequences of kda_chunk_fwd_varlen): tensors as kda_chunk_fwd_varlen's with the [T, ...]
+ * token axis (dq, dk [T, H, K]; dv [T, HV, V]; dg [T, HV, K]; dbeta [T, HV]); initial_state,
+ * dht and dh0 [N, HV, K, V] float32 (dht, dh0 optional); cu_seqlens as for
+ * kda_chunk_fwd_varlen. Gradients of tokens outside [cu_seqlens[0], cu_seqlens[N]) are left
+ * unspecified. Workspace of kda_chunk_bwd_varlen_workspace_size(). Constraints as
+ * kda_chunk_bwd.
+ */
+size_t kda_chunk_bwd_varlen_workspace_size(int N, int T, int H, int HV, int K, int V, int dtype);
+
+int kda_chunk_bwd_varlen(const void* q, const void* k, const void* v, const void* g,
+                         const void* beta, const int* cu_seqlens, int N,
+                         const float* initial_state, const void* dout, const float* dht,
+                         void* dq, void* dk, void* dv, void* dg, void* dbeta, float* dh0, int T,
+                         int H, int HV, int K, int V, float scale, int dtype, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/*
  * One decode token for every (b, hv), state updated IN PLACE (K3 README, roadmap
  * row L6: recurrent decode against a [B, HV, K, V] state cache; the DM-KDAGQA-1.7B
  * model card's usage notes: cached generation costs one such step per token).

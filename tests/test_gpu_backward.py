@@ -102,3 +102,57 @@ def test_unsupported_shapes_raise():
     do = torch.zeros_like(d["v"])
     with pytest.raises(RuntimeError, match="UNSUPPORTED"):
         kda.kda_chunk_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], do, d["scale"])
+
+
+def _packed_grad_inputs(lengths, H, HV, K, V, seed):
+    T = int(sum(lengths))
+    inp = _grad_inputs(1, T, H, HV, K, V, seed)
+    gen = torch.Generator().manual_seed(seed + 3)
+    N = len(lengths)
+    inp["initial_state"] = 0.1 * torch.randn((N, HV, K, V), generator=gen)
+    inp["dht"] = 0.1 * torch.randn((N, HV, K, V), generator=gen)
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lengths)]), dtype=torch.int32)
+    return inp, cu
+
+
+def _gpu_bwd_varlen(inp, cu):
+    d = {n: (t.cuda() if isinstance(t, torch.Tensor) else t) for n, t in inp.items()}
+    out = kda.kda_chunk_bwd_varlen(d["q"], d["k"], d["v"], d["g"], d["beta"], d["do"], cu.cuda(),
+                                   d["scale"], d["initial_state"], d["dht"])
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("lengths,H,HV,K,V", [
+    ([1, 63, 64, 65, 150, 0, 130], 1, 2, 64, 64),
+    ([200, 17], 2, 4, 128, 48),              # GVA
+])
+def test_packed_sequences(lengths, H, HV, K, V):
+    log(f"backward packed lengths={lengths} H={H} HV={HV} K={K} V={V}")
+    inp, cu = _packed_grad_inputs(lengths, H, HV, K, V, seed=len(lengths) * 7 + K)
+    got = _gpu_bwd_varlen(inp, cu)
+    for s in range(len(lengths)):
+        a, b = int(cu[s]), int(cu[s + 1])
+        if a == b:  # empty: the state gradient passes through
+            assert torch.equal(got[5][s].cpu(), inp["dht"][s]), f"sequence {s}"
+            continue
+        one = {n: inp[n][:, a:b] for n in ("q", "k", "v", "g", "beta", "do")}
+        one.update(scale=inp["scale"], initial_state=inp["initial_state"][s:s + 1],
+                   dht=inp["dht"][s:s + 1])
+        ref = _ref(one)
+        sub = [x[:, a:b] for x in got[:5]] + [got[5][s:s + 1]]
+        _check(sub, ref, f"sequence {s} ({b - a} tokens)")
+
+
+def test_packed_equal_lengths_match_the_batched_backward():
+    log("backward packed 3 x 192 tokens vs kda_chunk_bwd with B = 3 (GVA)")
+    B, T, H, HV, K, V = 3, 192, 2, 4, 64, 64
+    inp = _grad_inputs(B, T, H, HV, K, V, 88)
+    a = _gpu_bwd(inp)
+    packed = {n: inp[n].reshape((1, B * T) + tuple(inp[n].shape[2:]))
+              for n in ("q", "k", "v", "g", "beta", "do")}
+    packed.update(scale=inp["scale"], initial_state=inp["initial_state"], dht=inp["dht"])
+    cu = torch.arange(0, (B + 1) * T, T, dtype=torch.int32)
+    b = _gpu_bwd_varlen(packed, cu)
+    for name, x, y in zip(NAMES, a, b):
+        assert torch.equal(x, y.reshape(x.shape)), f"{name} differs"
