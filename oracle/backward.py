@@ -25,6 +25,11 @@ The gradient of the final state (``dht``) seeds dS; the one reaching the
 initial state is returned as ``dh0``. Forward states are recomputed from
 checkpoints every ``ckpt`` tokens, so memory stays at T/ckpt states.
 
+With ``qk_l2norm`` / ``beta_sigmoid`` (the input transforms of ``oracle.transforms``)
+the gradients are taken through the transforms by the chain rule: for
+``x_hat = x r`` with ``r = (sum x^2 + EPS)^(-1/2)``, ``dx = r (dx_hat - x_hat (x_hat . dx_hat))``;
+for ``beta = sigmoid(b)``, ``db = dbeta * beta (1 - beta)``.
+
 Pinned (tests/test_oracle_backward.py) against central finite differences of the
 forward oracle ``recurrent``, the pages' gradcheck (float64, eps 1e-6, atol 1e-4).
 """
@@ -32,6 +37,7 @@ forward oracle ``recurrent``, the pages' gradcheck (float64, eps 1e-6, atol 1e-4
 import numpy as np
 
 from .recurrent import _expand_heads, _f64
+from .transforms import EPS, l2_normalize, sigmoid
 
 
 def _step(q, k, v, g, beta, s_prev, scale):
@@ -43,13 +49,31 @@ def _step(q, k, v, g, beta, s_prev, scale):
     return s, a, u, s_new
 
 
-def recurrent_bwd(q, k, v, g, beta, scale, do, initial_state=None, dht=None, ckpt=64):
+def recurrent_bwd(q, k, v, g, beta, scale, do, initial_state=None, dht=None, ckpt=64,
+                  qk_l2norm=False, beta_sigmoid=False):
     """Gradients of L = sum(o * do) + sum(S_T * dht) with respect to every input.
 
     Shapes as in ``recurrent``; do [B, T, HV, V]; dht [B, HV, K, V] or None (zeros).
     Returns ``(dq [B,T,H,K], dk [B,T,H,K], dv [B,T,HV,V], dg [B,T,HV,K],
-    dbeta [B,T,HV], dh0 [B,HV,K,V])`` in float64.
+    dbeta [B,T,HV], dh0 [B,HV,K,V])`` in float64. ``qk_l2norm`` / ``beta_sigmoid``:
+    the forward applied those transforms (``recurrent``'s flags); the gradients are with
+    respect to the raw inputs.
     """
+    if qk_l2norm or beta_sigmoid:
+        q, k, beta = (_f64(a) for a in (q, k, beta))
+        qn = l2_normalize(q) if qk_l2norm else q
+        kn = l2_normalize(k) if qk_l2norm else k
+        bn = sigmoid(beta) if beta_sigmoid else beta
+        dq, dk, dv, dg, db, dh0 = recurrent_bwd(qn, kn, v, g, bn, scale, do, initial_state,
+                                                dht, ckpt)
+        if qk_l2norm:
+            def through_norm(x, xn, dxn):
+                r = 1.0 / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + EPS)
+                return r * (dxn - xn * np.sum(xn * dxn, axis=-1, keepdims=True))
+            dq, dk = through_norm(q, qn, dq), through_norm(k, kn, dk)
+        if beta_sigmoid:
+            db = db * bn * (1.0 - bn)
+        return dq, dk, dv, dg, db, dh0
     q, k, v, g, beta, do = (_f64(a) for a in (q, k, v, g, beta, do))
     b, t_len, h, kd = q.shape
     hv, vd = v.shape[2], v.shape[3]

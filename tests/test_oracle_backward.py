@@ -9,6 +9,9 @@
 * Independence of the checkpoint interval.
 * Sensitivity: an error of 1e-3 in any one gradient fails the finite-difference
   check, so the check is not vacuous.
+* Gradients through the in-operator transforms (q/k L2 normalisation, beta sigmoid):
+  every element against central differences of the forward oracle with the same
+  transforms, on raw q, k and beta logits.
 """
 
 import numpy as np
@@ -121,3 +124,32 @@ def test_finite_difference_check_catches_small_errors():
         idx = tuple(rng.integers(0, s) for s in x[name].shape)
         fd = _fd_element(x, scale, name, idx)
         assert abs(fd - (gr[name][idx] + 1e-3)) > ATOL  # a planted 1e-3 error shows
+
+
+def _loss_t(x, scale, flags):
+    o, s = recurrent(x["q"], x["k"], x["v"], x["g"], x["beta"], scale, x["initial_state"], **flags)
+    return float(np.sum(o * x["do"]) + np.sum(s * x["dht"]))
+
+
+@pytest.mark.parametrize("flags", [dict(qk_l2norm=True, beta_sigmoid=False),
+                                   dict(qk_l2norm=False, beta_sigmoid=True),
+                                   dict(qk_l2norm=True, beta_sigmoid=True)])
+def test_transformed_gradients_match_finite_differences(flags):
+    """Gradients through the in-operator transforms, element by element against central
+    differences of the forward oracle applying the same transforms (raw q, k; beta logits)."""
+    x, scale = _inputs(1, 5, 1, 2, 4, 3, seed=13)
+    rng = np.random.default_rng(14)
+    x["q"] = 3.0 * rng.standard_normal(x["q"].shape)
+    x["k"] = 0.5 * rng.standard_normal(x["k"].shape)
+    x["beta"] = 2.0 * rng.standard_normal(x["beta"].shape)
+    dq, dk, dv, dg, db, dh0 = recurrent_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], scale,
+                                            x["do"], x["initial_state"], x["dht"], **flags)
+    gr = {"q": dq, "k": dk, "v": dv, "g": dg, "beta": db, "initial_state": dh0}
+    for name in NAMES:
+        for idx in np.ndindex(x[name].shape):
+            xp = {n: a.copy() for n, a in x.items()}
+            xm = {n: a.copy() for n, a in x.items()}
+            xp[name][idx] += EPS
+            xm[name][idx] -= EPS
+            fd = (_loss_t(xp, scale, flags) - _loss_t(xm, scale, flags)) / (2 * EPS)
+            assert abs(fd - gr[name][idx]) <= ATOL, f"d{name}{idx}: {gr[name][idx]:.8f} vs {fd:.8f}"
