@@ -58,10 +58,15 @@ def library():
     lib.kda_chunk_fwd_varlen.restype = i
     lib.kda_chunk_fwd_varlen_workspace_size.argtypes = [i] * 7
     lib.kda_chunk_fwd_varlen_workspace_size.restype = sz
+    u = ctypes.c_uint
     lib.kda_chunk_bwd.argtypes = [vp] * 14 + [i] * 6 + [f, i, i, vp, sz, vp]
-    lib.kda_chunk_bwd_varlen.argtypes = [vp] * 6 + [i] + [vp] * 9 + [i] * 5 + [f, i, vp, sz, vp]
+    lib.kda_chunk_bwd_ex.argtypes = [vp] * 14 + [i] * 6 + [f, i, i, vp, sz, u, vp]
+    lib.kda_chunk_bwd_ex.restype = i
+    lib.kda_chunk_bwd_workspace_size_ex.argtypes = [i] * 8 + [u]
+    lib.kda_chunk_bwd_workspace_size_ex.restype = sz
+    lib.kda_chunk_bwd_varlen.argtypes = [vp] * 6 + [i] + [vp] * 9 + [i] * 5 + [f, i, vp, sz, u, vp]
     lib.kda_chunk_bwd_varlen.restype = i
-    lib.kda_chunk_bwd_varlen_workspace_size.argtypes = [i] * 7
+    lib.kda_chunk_bwd_varlen_workspace_size.argtypes = [i] * 7 + [u]
     lib.kda_chunk_bwd_varlen_workspace_size.restype = sz
     lib.kda_chunk_bwd.restype = i
     lib.kda_chunk_bwd_workspace_size.argtypes = [i] * 8
@@ -190,10 +195,12 @@ def kda_chunk_fwd_varlen(q, k, v, g, beta, cu_seqlens, scale=None, initial_state
 
 
 def kda_chunk_bwd(q, k, v, g, beta, do, scale=None, initial_state=None, dht=None, chunk_size=64,
-                  need_dh0=True):
+                  need_dh0=True, qk_l2norm=False, beta_sigmoid=False):
     """Gradients of <o, do> + <final_state, dht> for kda_chunk_fwd's inputs (bf16).
     Shapes as kda_chunk_fwd; do [B,T,HV,V]; dht [B,HV,K,V] float32 or None.
-    Returns (dq, dk, dv, dg, dbeta, dh0 or None); dh0 is float32 [B,HV,K,V]."""
+    Returns (dq, dk, dv, dg, dbeta, dh0 or None); dh0 is float32 [B,HV,K,V].
+    qk_l2norm / beta_sigmoid: the forward applied those transforms; gradients are for the
+    raw inputs."""
     _require(q.is_cuda, "inputs must be on a GPU")
     dev, dt = q.device, q.dtype
     _require(dt in _DTYPE, f"unsupported dtype {dt}")
@@ -218,21 +225,22 @@ def kda_chunk_bwd(q, k, v, g, beta, do, scale=None, initial_state=None, dht=None
     dg = torch.empty((B, T, HV, K), dtype=dt, device=dev)
     dbeta = torch.empty((B, T, HV), dtype=dt, device=dev)
     dh0 = torch.empty((B, HV, K, V), dtype=torch.float32, device=dev) if need_dh0 else None
-    ws_bytes = lib.kda_chunk_bwd_workspace_size(B, T, H, HV, K, V, chunk_size, _DTYPE[dt])
+    flags = _flags(qk_l2norm, beta_sigmoid)
+    ws_bytes = lib.kda_chunk_bwd_workspace_size_ex(B, T, H, HV, K, V, chunk_size, _DTYPE[dt], flags)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     with torch.cuda.device(dev):
         stream = torch.cuda.current_stream(dev).cuda_stream
-        rc = lib.kda_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-                               _ptr(initial_state), _ptr(do), _ptr(dht), _ptr(dq), _ptr(dk),
-                               _ptr(dv), _ptr(dg), _ptr(dbeta), _ptr(dh0), B, T, H, HV, K, V,
-                               float(scale), int(chunk_size), _DTYPE[dt], _ptr(ws), ws_bytes,
-                               ctypes.c_void_p(stream))
+        rc = lib.kda_chunk_bwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                  _ptr(initial_state), _ptr(do), _ptr(dht), _ptr(dq), _ptr(dk),
+                                  _ptr(dv), _ptr(dg), _ptr(dbeta), _ptr(dh0), B, T, H, HV, K, V,
+                                  float(scale), int(chunk_size), _DTYPE[dt], _ptr(ws), ws_bytes,
+                                  flags, ctypes.c_void_p(stream))
     _check(rc)
     return dq, dk, dv, dg, dbeta, dh0
 
 
 def kda_chunk_bwd_varlen(q, k, v, g, beta, do, cu_seqlens, scale=None, initial_state=None,
-                         dht=None, need_dh0=True):
+                         dht=None, need_dh0=True, qk_l2norm=False, beta_sigmoid=False):
     """Gradients for kda_chunk_fwd_varlen's inputs (bf16, packed sequences). Token tensors
     [1,T,...] (or [T,...]); cu_seqlens int32 [N+1]; initial_state, dht [N,HV,K,V] float32 or
     None. Returns (dq, dk, dv, dg, dbeta shaped like their inputs, dh0 [N,HV,K,V] or None)."""
@@ -264,7 +272,8 @@ def kda_chunk_bwd_varlen(q, k, v, g, beta, do, cu_seqlens, scale=None, initial_s
     dq, dk = torch.empty_like(q), torch.empty_like(k)
     dv, dg, dbeta = torch.empty_like(v), torch.empty_like(g), torch.empty_like(beta)
     dh0 = torch.empty((N, HV, K, V), dtype=torch.float32, device=dev) if need_dh0 else None
-    ws_bytes = lib.kda_chunk_bwd_varlen_workspace_size(N, T, H, HV, K, V, _DTYPE[dt])
+    flags = _flags(qk_l2norm, beta_sigmoid)
+    ws_bytes = lib.kda_chunk_bwd_varlen_workspace_size(N, T, H, HV, K, V, _DTYPE[dt], flags)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     with torch.cuda.device(dev):
         stream = torch.cuda.current_stream(dev).cuda_stream
@@ -272,7 +281,7 @@ def kda_chunk_bwd_varlen(q, k, v, g, beta, do, cu_seqlens, scale=None, initial_s
                                       _ptr(cu_seqlens), N, _ptr(initial_state), _ptr(do),
                                       _ptr(dht), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg),
                                       _ptr(dbeta), _ptr(dh0), T, H, HV, K, V, float(scale),
-                                      _DTYPE[dt], _ptr(ws), ws_bytes, ctypes.c_void_p(stream))
+                                      _DTYPE[dt], _ptr(ws), ws_bytes, flags, ctypes.c_void_p(stream))
     _check(rc)
     outs = (dq, dk, dv, dg, dbeta)
     if not squeeze:

@@ -15,15 +15,15 @@ hipError_t launch_prefill(const void*, const void*, const void*, const void*, co
                           const float*, float*, void*, int, int, int, int, int, int, float, bool,
                           void*, unsigned, hipStream_t);
 size_t wy_workspace_bytes(int B, int T, int HV, int K);
-size_t bwd_workspace_bytes(int B, int T, int H, int HV, int K, int V);
-size_t bwd_varlen_workspace_bytes(int nseq, int T, int H, int HV, int K, int V);
+size_t bwd_workspace_bytes(int B, int T, int H, int HV, int K, int V, unsigned flags);
+size_t bwd_varlen_workspace_bytes(int nseq, int T, int H, int HV, int K, int V, unsigned flags);
 size_t wy_varlen_workspace_bytes(int nseq, int T, int HV, int K);
 hipError_t launch_prefill_wy_varlen(const PrefillArgs& p, const int* cu_seqlens, void* workspace,
                                     hipStream_t stream);
 hipError_t launch_chunk_bwd(const void*, const void*, const void*, const void*, const void*,
                             const int*, const float*, const void*, const float*, void*, void*,
                             void*, void*, void*, float*, int, int, int, int, int, int, float,
-                            void*, hipStream_t);
+                            unsigned, void*, hipStream_t);
 }  // namespace kda
 
 namespace {
@@ -156,27 +156,37 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const void* g, co
                           scale, chunk_size, dtype, workspace, workspace_bytes, 0u, stream);
 }
 
-size_t kda_chunk_bwd_workspace_size(int B, int T, int H, int HV, int K, int V, int chunk_size,
-                                    int dtype) {
-  if (!positive(T) || !valid_chunk(T, chunk_size)) return 0;
-  if (check_common(B, H, HV, K, V, 1.f, dtype) != KDA_OK || !bwd_shape(K, V, dtype)) return 0;
-  return kda::bwd_workspace_bytes(B, T, H, HV, K, V);
+static bool valid_flags(unsigned flags) {
+  return (flags & ~(unsigned)(KDA_FLAG_QK_L2NORM | KDA_FLAG_BETA_SIGMOID)) == 0;
 }
 
-int kda_chunk_bwd(const void* q, const void* k, const void* v, const void* g, const void* beta,
-                  const float* initial_state, const void* dout, const float* dht, void* dq,
-                  void* dk, void* dv, void* dg, void* dbeta, float* dh0, int B, int T, int H,
-                  int HV, int K, int V, float scale, int chunk_size, int dtype, void* workspace,
-                  size_t workspace_bytes, void* stream) {
+size_t kda_chunk_bwd_workspace_size_ex(int B, int T, int H, int HV, int K, int V, int chunk_size,
+                                       int dtype, unsigned flags) {
+  if (!positive(T) || !valid_chunk(T, chunk_size) || !valid_flags(flags)) return 0;
+  if (check_common(B, H, HV, K, V, 1.f, dtype) != KDA_OK || !bwd_shape(K, V, dtype)) return 0;
+  return kda::bwd_workspace_bytes(B, T, H, HV, K, V, flags);
+}
+
+size_t kda_chunk_bwd_workspace_size(int B, int T, int H, int HV, int K, int V, int chunk_size,
+                                    int dtype) {
+  return kda_chunk_bwd_workspace_size_ex(B, T, H, HV, K, V, chunk_size, dtype, 0u);
+}
+
+int kda_chunk_bwd_ex(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                     const float* initial_state, const void* dout, const float* dht, void* dq,
+                     void* dk, void* dv, void* dg, void* dbeta, float* dh0, int B, int T, int H,
+                     int HV, int K, int V, float scale, int chunk_size, int dtype, void* workspace,
+                     size_t workspace_bytes, unsigned flags, void* stream) {
   if (!q || !k || !v || !g || !beta || !dout || !dq || !dk || !dv || !dg || !dbeta)
     return KDA_ERR_INVALID;
+  if (!valid_flags(flags)) return KDA_ERR_INVALID;
   if (!positive(T) || !valid_chunk(T, chunk_size)) return KDA_ERR_INVALID;
   const int rc = check_common(B, H, HV, K, V, scale, dtype);
   if (rc != KDA_OK) return rc;
   if (!bwd_shape(K, V, dtype)) return KDA_ERR_UNSUPPORTED;
   if ((int64_t)B * HV * ((T + 63) / 64) > INT32_MAX) return KDA_ERR_UNSUPPORTED;
   if ((int64_t)B * T * H * K / 256 > INT32_MAX) return KDA_ERR_UNSUPPORTED;
-  const size_t need = kda::bwd_workspace_bytes(B, T, H, HV, K, V);
+  const size_t need = kda::bwd_workspace_bytes(B, T, H, HV, K, V, flags);
   if (!workspace || workspace_bytes < need) return KDA_ERR_INVALID;
   if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0) return KDA_ERR_INVALID;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g) || !aligned16(dout) ||
@@ -184,14 +194,25 @@ int kda_chunk_bwd(const void* q, const void* k, const void* v, const void* g, co
     return KDA_ERR_UNSUPPORTED;
   const hipError_t e = kda::launch_chunk_bwd(q, k, v, g, beta, nullptr, initial_state, dout, dht,
                                              dq, dk, dv, dg, dbeta, dh0, B, T, H, HV, K, V, scale,
-                                             workspace, static_cast<hipStream_t>(stream));
+                                             flags, workspace, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
-size_t kda_chunk_bwd_varlen_workspace_size(int N, int T, int H, int HV, int K, int V, int dtype) {
-  if (!positive(T)) return 0;
+int kda_chunk_bwd(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                  const float* initial_state, const void* dout, const float* dht, void* dq,
+                  void* dk, void* dv, void* dg, void* dbeta, float* dh0, int B, int T, int H,
+                  int HV, int K, int V, float scale, int chunk_size, int dtype, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+  return kda_chunk_bwd_ex(q, k, v, g, beta, initial_state, dout, dht, dq, dk, dv, dg, dbeta, dh0,
+                          B, T, H, HV, K, V, scale, chunk_size, dtype, workspace, workspace_bytes,
+                          0u, stream);
+}
+
+size_t kda_chunk_bwd_varlen_workspace_size(int N, int T, int H, int HV, int K, int V, int dtype,
+                                           unsigned flags) {
+  if (!positive(T) || !valid_flags(flags)) return 0;
   if (check_common(N, H, HV, K, V, 1.f, dtype) != KDA_OK || !bwd_shape(K, V, dtype)) return 0;
-  return kda::bwd_varlen_workspace_bytes(N, T, H, HV, K, V);
+  return kda::bwd_varlen_workspace_bytes(N, T, H, HV, K, V, flags);
 }
 
 int kda_chunk_bwd_varlen(const void* q, const void* k, const void* v, const void* g,
@@ -199,16 +220,17 @@ int kda_chunk_bwd_varlen(const void* q, const void* k, const void* v, const void
                          const float* initial_state, const void* dout, const float* dht,
                          void* dq, void* dk, void* dv, void* dg, void* dbeta, float* dh0, int T,
                          int H, int HV, int K, int V, float scale, int dtype, void* workspace,
-                         size_t workspace_bytes, void* stream) {
+                         size_t workspace_bytes, unsigned flags, void* stream) {
   if (!q || !k || !v || !g || !beta || !cu_seqlens || !dout || !dq || !dk || !dv || !dg || !dbeta)
     return KDA_ERR_INVALID;
+  if (!valid_flags(flags)) return KDA_ERR_INVALID;
   if (!positive(T)) return KDA_ERR_INVALID;
   const int rc = check_common(N, H, HV, K, V, scale, dtype);
   if (rc != KDA_OK) return rc;
   if (!bwd_shape(K, V, dtype)) return KDA_ERR_UNSUPPORTED;
   if ((int64_t)HV * (T / 64 + (int64_t)N) > INT32_MAX) return KDA_ERR_UNSUPPORTED;
   if ((int64_t)T * H * K / 256 > INT32_MAX) return KDA_ERR_UNSUPPORTED;
-  const size_t need = kda::bwd_varlen_workspace_bytes(N, T, H, HV, K, V);
+  const size_t need = kda::bwd_varlen_workspace_bytes(N, T, H, HV, K, V, flags);
   if (!workspace || workspace_bytes < need) return KDA_ERR_INVALID;
   if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0) return KDA_ERR_INVALID;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g) || !aligned16(dout) ||
@@ -216,7 +238,8 @@ int kda_chunk_bwd_varlen(const void* q, const void* k, const void* v, const void
     return KDA_ERR_UNSUPPORTED;
   const hipError_t e = kda::launch_chunk_bwd(q, k, v, g, beta, cu_seqlens, initial_state, dout,
                                              dht, dq, dk, dv, dg, dbeta, dh0, N, T, H, HV, K, V,
-                                             scale, workspace, static_cast<hipStream_t>(stream));
+                                             scale, flags, workspace,
+                                             static_cast<hipStream_t>(stream));
   return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 

@@ -70,6 +70,7 @@ struct BwdArgs {
   const int* coff;
   const int2* ctab;
   int NC;
+  unsigned flags;  // kFlag* input transforms the forward applied (gradients go through them)
 };
 
 // The chunk a prep / local item stands for: its value head, its first token in the packed
@@ -227,6 +228,29 @@ __device__ __forceinline__ void cumsum_rows(float* G, int pg, float* tot, int ti
   __syncthreads();
 }
 
+// q and k rows in LDS (64 x KT bf16 each) to unit L2 norm over KT (x / sqrt(sum x^2 + eps)),
+// as the forward's q/k transform; NTH / 64 threads per row, all in one wave.
+template <int KT, int NTH>
+__device__ __forceinline__ void l2norm_rows(bf16* sq, bf16* sk, int pk, int tid) {
+  constexpr int TPR = NTH / kC, PER = KT / TPR;
+  const int r = tid / TPR, part = tid % TPR;
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    bf16* x = (m ? sk : sq) + r * pk + part * PER;
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const float v = static_cast<float>(x[e]);
+      ss += v * v;
+    }
+#pragma unroll
+    for (int o = 1; o < TPR; o <<= 1) ss += __shfl_xor(ss, o);
+    const float inv = rsqrtf(ss + kL2normEps);
+#pragma unroll
+    for (int e = 0; e < PER; ++e) x[e] = static_cast<bf16>(static_cast<float>(x[e]) * inv);
+  }
+}
+
 // acc += A B for A rows held in registers (af[s]: this lane's 8 values of k step s, zeros
 // past kk) and B given transposed in LDS (as mma16).
 __device__ __forceinline__ void mma_ra(f32x4& acc, const bf16x8* af, const bf16* bt, int ldb,
@@ -314,11 +338,16 @@ __global__ __launch_bounds__(256) void prep_kernel(BwdArgs a) {
 
   stage_qkg<KT, 256>(sq, sk, G, PK, PG, qb, kb, gb, qrow, grow, nrow, tid);
   if (tid < kC) {
-    const float bv = tid < nrow ? ldf(a.beta + (ch.row0 + tid) * a.HV + hv) : 0.f;
+    float bv = tid < nrow ? ldf(a.beta + (ch.row0 + tid) * a.HV + hv) : 0.f;
+    if ((a.flags & kFlagBetaSigmoid) && tid < nrow) bv = sigmoid_f32(bv);
     sb[tid] = bv;
     reinterpret_cast<float*>(blk + P::beta)[tid] = bv;
   }
   cumsum_rows<KT, 256>(G, PG, reinterpret_cast<float*>(lds + L::tot), tid);  // includes barriers
+  if (a.flags & kFlagQkL2norm) {
+    l2norm_rows<KT, 256>(sq, sk, PK, tid);
+    __syncthreads();
+  }
 
   // operands of the row-block-w products, built by wave w
   {
@@ -1042,6 +1071,10 @@ __global__ __launch_bounds__(64 * kLocalWaves) void local_kernel(BwdArgs a) {
     }
   }
   cumsum_rows<KT, NTH>(G, PG, reinterpret_cast<float*>(lds + L::tot), tid);  // includes barriers
+  if (a.flags & kFlagQkL2norm) {
+    l2norm_rows<KT, NTH>(sq, sk, PK, tid);
+    __syncthreads();
+  }
 
   // dbeta, first term: Ut_i . W0_i for this block's rows (one wave of the pair)
   if (ch == 0) {
@@ -1185,7 +1218,6 @@ __global__ __launch_bounds__(64 * kLocalWaves) void local_kernel(BwdArgs a) {
 
   // ---------------- phase 3: output factors, dq, dk, dG, then dg by a reverse scan
   float* dgs = reinterpret_cast<float*>(lds + L::dgs);
-  const int G_ = a.HV / a.H;
 #pragma unroll
   for (int cc = 0; cc < NCH; ++cc) {
     const int c = c0 + 16 * cc + lr;
@@ -1203,7 +1235,7 @@ __global__ __launch_bounds__(64 * kLocalWaves) void local_kernel(BwdArgs a) {
       dgs[i * PG + c] = qv * dq + kv * (dpos - dneg);
       if (i < nrow) {
         const size_t t = row0 + i;
-        if (G_ == 1) {
+        if (!a.dq32) {
           a.dq[(t * a.H + hh) * KT + c] = static_cast<bf16>(dq);
           a.dk[(t * a.H + hh) * KT + c] = static_cast<bf16>(dk);
         } else {
@@ -1236,7 +1268,11 @@ __global__ __launch_bounds__(64 * kLocalWaves) void local_kernel(BwdArgs a) {
       }
     }
   }
-  if (tid < nrow) a.dbeta[(row0 + tid) * a.HV + hv] = static_cast<bf16>(db1[tid] + db2[tid]);
+  if (tid < nrow) {
+    const float bt = sb[tid];  // beta as the recurrence used it
+    const float chain = (a.flags & kFlagBetaSigmoid) ? bt * (1.f - bt) : 1.f;
+    a.dbeta[(row0 + tid) * a.HV + hv] = static_cast<bf16>((db1[tid] + db2[tid]) * chain);
+  }
 }
 
 // dq, dk: sum of the G value heads of each q/k head (fp32 -> bf16)
@@ -1253,13 +1289,60 @@ __global__ __launch_bounds__(256) void gva_reduce_kernel(const float* __restrict
   out[i] = static_cast<bf16>(s);
 }
 
+// dq, dk through the q/k L2 normalisation: per (token, q/k head), the G value heads' fp32
+// gradients are summed into dx_hat, then dx = r (dx_hat - x_hat (x_hat . dx_hat)) with
+// r = (sum x^2 + eps)^(-1/2) and x_hat = x r. One wave per (token, head); K <= 128.
+__global__ __launch_bounds__(256) void qk_norm_bwd_kernel(const bf16* __restrict__ q,
+                                                          const bf16* __restrict__ k,
+                                                          const float* __restrict__ dq32,
+                                                          const float* __restrict__ dk32,
+                                                          bf16* __restrict__ dq,
+                                                          bf16* __restrict__ dk, size_t rows,
+                                                          int H, int G, int K) {
+  const size_t wid = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (wid >= rows * H) return;  // whole waves; this kernel has no barriers
+  const size_t row = wid / H;
+  const int h = (int)(wid - row * H);
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const bf16* x = pass ? k : q;
+    const float* d32 = pass ? dk32 : dq32;
+    bf16* out = pass ? dk : dq;
+    float xv[2], dv[2], ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int c = lane + 64 * j;
+      xv[j] = dv[j] = 0.f;
+      if (c < K) {
+        xv[j] = static_cast<float>(x[(row * H + h) * K + c]);
+        float sum = 0.f;
+        for (int gi = 0; gi < G; ++gi) sum += d32[((row * H + h) * G + gi) * K + c];
+        dv[j] = sum;
+      }
+      ss += xv[j] * xv[j];
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+    const float r = rsqrtf(ss + kL2normEps);
+    float dot = xv[0] * r * dv[0] + xv[1] * r * dv[1];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) dot += __shfl_xor(dot, o);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int c = lane + 64 * j;
+      if (c < K) out[(row * H + h) * K + c] = static_cast<bf16>(r * (dv[j] - xv[j] * r * dot));
+    }
+  }
+}
+
 struct Layout {
   size_t blocks, h, dsn, u, w0, ut, dq32, dk32, cu, coff, ctab, total;
 };
 
 // slots: chunk slots (B * HV * NT, or HV * NC when packed); rows: tokens (B * T); nseq: packed
 // sequences (0: fixed length).
-Layout layout(size_t slots, size_t rows, int H, int HV, int K, int V, int nseq, int NC) {
+Layout layout(size_t slots, size_t rows, bool need32, int K, int V, int HV, int nseq, int NC) {
   auto al = [](size_t x) { return (x + 255) / 256 * 256; };
   Layout l{};
   size_t off = 0;
@@ -1269,7 +1352,7 @@ Layout layout(size_t slots, size_t rows, int H, int HV, int K, int V, int nseq, 
   l.u = off;      off += al(slots * kC * (size_t)V * 2);
   l.w0 = off;     off += al(slots * kC * (size_t)V * 2);
   l.ut = off;     off += al(slots * kC * (size_t)V * 2);
-  if (HV != H) {
+  if (need32) {
     l.dq32 = off; off += al(rows * HV * K * 4);
     l.dk32 = off; off += al(rows * HV * K * 4);
   }
@@ -1282,14 +1365,17 @@ Layout layout(size_t slots, size_t rows, int H, int HV, int K, int V, int nseq, 
   return l;
 }
 
-Layout fixed_layout(int B, int T, int H, int HV, int K, int V) {
+// fp32 dq / dk per value head: to sum G > 1 value heads, or to go through the q/k L2 norm
+bool needs_fp32_dqk(int H, int HV, unsigned flags) { return HV != H || (flags & kFlagQkL2norm); }
+
+Layout fixed_layout(int B, int T, int H, int HV, int K, int V, unsigned flags) {
   const size_t NT = (T + kC - 1) / kC;
-  return layout((size_t)B * HV * NT, (size_t)B * T, H, HV, K, V, 0, 0);
+  return layout((size_t)B * HV * NT, (size_t)B * T, needs_fp32_dqk(H, HV, flags), K, V, HV, 0, 0);
 }
 
-Layout varlen_layout(int nseq, int T, int H, int HV, int K, int V) {
+Layout varlen_layout(int nseq, int T, int H, int HV, int K, int V, unsigned flags) {
   const int NC = varlen_chunk_bound(nseq, T);
-  return layout((size_t)HV * NC, (size_t)T, H, HV, K, V, nseq, NC);
+  return layout((size_t)HV * NC, (size_t)T, needs_fp32_dqk(H, HV, flags), K, V, HV, nseq, NC);
 }
 
 template <int KT>
@@ -1301,8 +1387,12 @@ hipError_t launch_cfg(BwdArgs a, hipStream_t stream) {
   hipLaunchKernelGGL((fwd_sweep_kernel<KT, NW>), dim3(sweeps), dim3(64 * NW), 0, stream, a);
   hipLaunchKernelGGL((rev_sweep_kernel<KT, NW>), dim3(sweeps), dim3(64 * NW), 0, stream, a);
   hipLaunchKernelGGL((local_kernel<KT>), dim3(items), dim3(64 * kLocalWaves), 0, stream, a);
-  if (a.HV != a.H) {
-    const size_t rows = a.ctab ? (size_t)a.T : (size_t)a.B * a.T;  // packed: one row of T tokens
+  const size_t rows = a.ctab ? (size_t)a.T : (size_t)a.B * a.T;  // packed: one row of T tokens
+  if (a.flags & kFlagQkL2norm) {
+    const unsigned grid = (unsigned)((rows * a.H + 3) / 4);
+    hipLaunchKernelGGL(qk_norm_bwd_kernel, dim3(grid), dim3(256), 0, stream, a.q, a.k, a.dq32,
+                       a.dk32, a.dq, a.dk, rows, a.H, a.HV / a.H, KT);
+  } else if (a.HV != a.H) {
     const unsigned grid = (unsigned)((rows * a.H * KT + 255) / 256);
     hipLaunchKernelGGL(gva_reduce_kernel, dim3(grid), dim3(256), 0, stream, a.dq32, a.dq, rows,
                        a.H, a.HV / a.H, KT);
@@ -1314,12 +1404,12 @@ hipError_t launch_cfg(BwdArgs a, hipStream_t stream) {
 
 }  // namespace bwd
 
-size_t bwd_workspace_bytes(int B, int T, int H, int HV, int K, int V) {
-  return bwd::fixed_layout(B, T, H, HV, K, V).total;
+size_t bwd_workspace_bytes(int B, int T, int H, int HV, int K, int V, unsigned flags) {
+  return bwd::fixed_layout(B, T, H, HV, K, V, flags).total;
 }
 
-size_t bwd_varlen_workspace_bytes(int nseq, int T, int H, int HV, int K, int V) {
-  return bwd::varlen_layout(nseq, T, H, HV, K, V).total;
+size_t bwd_varlen_workspace_bytes(int nseq, int T, int H, int HV, int K, int V, unsigned flags) {
+  return bwd::varlen_layout(nseq, T, H, HV, K, V, flags).total;
 }
 
 // Inputs validated by the C ABI: bf16, K in {32, 64, 128}, V % 16 == 0, V <= 128, workspace of
@@ -1330,9 +1420,11 @@ hipError_t launch_chunk_bwd(const void* q, const void* k, const void* v, const v
                             const void* beta, const int* cu_seqlens, const float* s0,
                             const void* dout, const float* dht, void* dq, void* dk, void* dv,
                             void* dg, void* dbeta, float* dh0, int B, int T, int H, int HV, int K,
-                            int V, float scale, void* workspace, hipStream_t stream) {
+                            int V, float scale, unsigned flags, void* workspace,
+                            hipStream_t stream) {
   using namespace bwd;
-  const Layout l = cu_seqlens ? varlen_layout(B, T, H, HV, K, V) : fixed_layout(B, T, H, HV, K, V);
+  const Layout l = cu_seqlens ? varlen_layout(B, T, H, HV, K, V, flags)
+                              : fixed_layout(B, T, H, HV, K, V, flags);
   unsigned char* ws = static_cast<unsigned char*>(workspace);
   BwdArgs a{};
   a.q = static_cast<const bf16*>(q);
@@ -1358,8 +1450,10 @@ hipError_t launch_chunk_bwd(const void* q, const void* k, const void* v, const v
   a.u = reinterpret_cast<bf16*>(ws + l.u);
   a.w0 = reinterpret_cast<bf16*>(ws + l.w0);
   a.ut = reinterpret_cast<bf16*>(ws + l.ut);
-  a.dq32 = HV != H ? reinterpret_cast<float*>(ws + l.dq32) : nullptr;
-  a.dk32 = HV != H ? reinterpret_cast<float*>(ws + l.dk32) : nullptr;
+  const bool f32 = needs_fp32_dqk(H, HV, flags);
+  a.dq32 = f32 ? reinterpret_cast<float*>(ws + l.dq32) : nullptr;
+  a.dk32 = f32 ? reinterpret_cast<float*>(ws + l.dk32) : nullptr;
+  a.flags = flags;
   if (cu_seqlens) {
     a.NC = varlen_chunk_bound(B, T);
     int* cu = reinterpret_cast<int*>(ws + l.cu);

@@ -183,22 +183,40 @@ int kda_chunk_bwd(const void* q, const void* k, const void* v, const void* g,
                   void* stream);
 
 /*
+ * kda_chunk_bwd for a forward that applied input transforms (kda_chunk_fwd_ex's flags):
+ * gradients are with respect to the raw q, k (before the L2 normalisation) and the raw beta
+ * (the logit before the sigmoid), by the chain rule through each transform. The workspace
+ * depends on the flags: kda_chunk_bwd_workspace_size_ex(). kda_chunk_bwd(...) is
+ * kda_chunk_bwd_ex(..., 0, stream). Invalid flag bits: KDA_ERR_INVALID.
+ */
+size_t kda_chunk_bwd_workspace_size_ex(int B, int T, int H, int HV, int K, int V,
+                                       int chunk_size, int dtype, unsigned flags);
+
+int kda_chunk_bwd_ex(const void* q, const void* k, const void* v, const void* g,
+                     const void* beta, const float* initial_state, const void* dout,
+                     const float* dht, void* dq, void* dk, void* dv, void* dg, void* dbeta,
+                     float* dh0, int B, int T, int H, int HV, int K, int V, float scale,
+                     int chunk_size, int dtype, void* workspace, size_t workspace_bytes,
+                     unsigned flags, void* stream);
+
+/*
  * kda_chunk_bwd for N packed variable-length sequences, each with its own state (the
  * sequences of kda_chunk_fwd_varlen): tensors as kda_chunk_fwd_varlen's with the [T, ...]
  * token axis (dq, dk [T, H, K]; dv [T, HV, V]; dg [T, HV, K]; dbeta [T, HV]); initial_state,
  * dht and dh0 [N, HV, K, V] float32 (dht, dh0 optional); cu_seqlens as for
  * kda_chunk_fwd_varlen. Gradients of tokens outside [cu_seqlens[0], cu_seqlens[N]) are left
- * unspecified. Workspace of kda_chunk_bwd_varlen_workspace_size(). Constraints as
- * kda_chunk_bwd.
+ * unspecified. flags as for kda_chunk_bwd_ex (the forward's transforms). Workspace of
+ * kda_chunk_bwd_varlen_workspace_size() for the same flags. Constraints as kda_chunk_bwd.
  */
-size_t kda_chunk_bwd_varlen_workspace_size(int N, int T, int H, int HV, int K, int V, int dtype);
+size_t kda_chunk_bwd_varlen_workspace_size(int N, int T, int H, int HV, int K, int V, int dtype,
+                                           unsigned flags);
 
 int kda_chunk_bwd_varlen(const void* q, const void* k, const void* v, const void* g,
                          const void* beta, const int* cu_seqlens, int N,
                          const float* initial_state, const void* dout, const float* dht,
                          void* dq, void* dk, void* dv, void* dg, void* dbeta, float* dh0, int T,
                          int H, int HV, int K, int V, float scale, int dtype, void* workspace,
-                         size_t workspace_bytes, void* stream);
+                         size_t workspace_bytes, unsigned flags, void* stream);
 
 /*
  * One decode token for every (b, hv), state updated IN PLACE (K3 README, roadmap

@@ -275,3 +275,13 @@ def test_recurrent_step_slots_rejects_invalid_arguments(lib, bad, rc):
                                         a["slots"], a["num_slots"], a["o"], a["B"], a["H"],
                                         a["HV"], a["K"], a["V"], a["scale"], a["dtype"],
                                         a["flags"], None) == rc
+
+
+def test_chunk_bwd_ex_rejects_unknown_flags(lib):
+    assert lib.kda_chunk_bwd_ex(FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, FAKE, FAKE, FAKE,
+                                FAKE, FAKE, None, 2, 64, 2, 4, 64, 64, 0.125, 64, 1,
+                                ctypes.c_void_p(0x100000), 1 << 40, 4, None) == kda.KDA_ERR_INVALID
+    assert lib.kda_chunk_bwd_workspace_size_ex(2, 64, 2, 4, 64, 64, 64, 1, 4) == 0
+    # the q/k normalisation needs fp32 per-value-head dq / dk even without GVA
+    assert (lib.kda_chunk_bwd_workspace_size_ex(1, 64, 1, 1, 64, 64, 64, 1, 1)
+            > lib.kda_chunk_bwd_workspace_size_ex(1, 64, 1, 1, 64, 64, 64, 1, 0))

@@ -156,3 +156,55 @@ def test_packed_equal_lengths_match_the_batched_backward():
     b = _gpu_bwd_varlen(packed, cu)
     for name, x, y in zip(NAMES, a, b):
         assert torch.equal(x, y.reshape(x.shape)), f"{name} differs"
+
+
+@pytest.mark.parametrize("flags", [dict(qk_l2norm=True, beta_sigmoid=True),
+                                   dict(qk_l2norm=True, beta_sigmoid=False),
+                                   dict(qk_l2norm=False, beta_sigmoid=True)])
+@pytest.mark.parametrize("shape", [dict(B=1, T=192, H=1, HV=1, K=128, V=128),
+                                   dict(B=2, T=128, H=2, HV=4, K=64, V=32)])
+def test_through_input_transforms(shape, flags):
+    """Raw q, k (norms far from 1) and beta logits; gradients for the raw inputs against the
+    oracle's chain rule through the same transforms."""
+    log(f"backward through transforms {flags} {shape}")
+    B, T, H, HV, K, V = (shape[n] for n in ("B", "T", "H", "HV", "K", "V"))
+    inp = prefill_inputs(B, T, H, HV, K, V, "bf16", True, 71 + K, raw_qk=flags["qk_l2norm"],
+                         beta="logit" if flags["beta_sigmoid"] else "default")
+    if flags["qk_l2norm"]:
+        inp["q"] = inp["q"] * 4.0
+    if flags["beta_sigmoid"]:
+        inp["beta"] = inp["beta"] * 3.0
+    gen = torch.Generator().manual_seed(72)
+    inp["do"] = torch.randn((B, T, HV, V), generator=gen).to(torch.bfloat16)
+    inp["dht"] = 0.1 * torch.randn((B, HV, K, V), generator=gen)
+    d = {n: (t.cuda() if isinstance(t, torch.Tensor) else t) for n, t in inp.items()}
+    got = kda.kda_chunk_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["do"], d["scale"],
+                            d["initial_state"], d["dht"], 64, **flags)
+    torch.cuda.synchronize()
+    ref = recurrent_bwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["scale"],
+                        inp["do"], inp["initial_state"], inp["dht"], **flags)
+    _check(got, ref, str(flags))
+
+
+def test_packed_sequences_through_input_transforms():
+    log("backward packed, q/k L2 norm and beta sigmoid")
+    flags = dict(qk_l2norm=True, beta_sigmoid=True)
+    lengths = [70, 1, 128]
+    T = sum(lengths)
+    inp = prefill_inputs(1, T, 1, 2, 64, 64, "bf16", True, 75, raw_qk=True, beta="logit")
+    gen = torch.Generator().manual_seed(76)
+    inp["do"] = torch.randn((1, T, 2, 64), generator=gen).to(torch.bfloat16)
+    inp["initial_state"] = 0.1 * torch.randn((3, 2, 64, 64), generator=gen)
+    inp["dht"] = 0.1 * torch.randn((3, 2, 64, 64), generator=gen)
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lengths)]), dtype=torch.int32)
+    d = {n: (t.cuda() if isinstance(t, torch.Tensor) else t) for n, t in inp.items()}
+    got = kda.kda_chunk_bwd_varlen(d["q"], d["k"], d["v"], d["g"], d["beta"], d["do"], cu.cuda(),
+                                   d["scale"], d["initial_state"], d["dht"], **flags)
+    torch.cuda.synchronize()
+    for s in range(3):
+        a, b = int(cu[s]), int(cu[s + 1])
+        one = {n: inp[n][:, a:b] for n in ("q", "k", "v", "g", "beta", "do")}
+        ref = recurrent_bwd(one["q"], one["k"], one["v"], one["g"], one["beta"], inp["scale"],
+                            one["do"], inp["initial_state"][s:s + 1], inp["dht"][s:s + 1], **flags)
+        sub = [x[:, a:b] for x in got[:5]] + [got[5][s:s + 1]]
+        _check(sub, ref, f"sequence {s}")
