@@ -104,22 +104,28 @@ def measured_traffic():
 
 
 def time_launches(fn, steps, warmup, torch):
-    """Average launch duration in ms over `steps` back-to-back launches (events on the
-    launch stream), plus per-launch median."""
+    """Average launch duration in ms over `steps` back-to-back launches, timed by two events on
+    the launch stream around all of them; then, in a second pass of `steps` launches with an
+    event after each, the per-launch median and minimum."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    avg = e0.elapsed_time(e1) / steps
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     ev[0].record(stream)
     for i in range(steps):
         fn()
         ev[i + 1].record(stream)
     torch.cuda.synchronize()
-    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
-    total = ev[0].elapsed_time(ev[steps])
-    per.sort()
-    return total / steps, per[len(per) // 2], per[0]
+    per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+    return avg, per[len(per) // 2], per[0]
 
 
 def copy_ceiling(torch, nbytes=1 << 30, reps=5):
@@ -168,7 +174,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--decode-reps", type=int, default=3)
     ap.add_argument("--cpu-tokens", type=int, default=8192)
     ap.add_argument("--no-cpu-baseline", action="store_true")
