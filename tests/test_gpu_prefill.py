@@ -212,3 +212,29 @@ def test_full_size_sampled_heads(name):
         ref_o, ref_s = recurrent(**head_slice(inp, b, hv, c["HV"] // c["H"]))
         assert_parity(to64(o[b:b + 1, :, hv:hv + 1]), ref_o, torch.bfloat16, f"o b={b} hv={hv}")
         assert_parity(to64(s[b:b + 1, hv:hv + 1]), ref_s, torch.bfloat16, f"state b={b} hv={hv}")
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_degenerate_inputs(dtype):
+    """beta = 0 exactly (no writes: the state only decays), the shortest sequence (T = 8,
+    chunk 8), q = 0 (o = 0 exactly) and a large initial state, each against the oracle."""
+    log(f"prefill degenerate cases {dtype}")
+    K = 64 if dtype == "bf16" else 32
+    # beta = 0: every token leaves the (decayed) state as it is
+    inp = prefill_inputs(1, 128, 2, 2, K, K, dtype, True, 91)
+    inp["beta"] = torch.zeros_like(inp["beta"])
+    _check_full(inp, dtype, what="beta=0")
+    # T = 8 with chunk 8 (the shortest sequence chunk_size allows; one-token sequences are
+    # covered by the packed entry point's tests)
+    _check_full(prefill_inputs(2, 8, 1, 2, K, K, dtype, True, 92), dtype, chunk=8, what="T=8")
+    # q = 0: o is exactly zero whatever the state
+    inp = prefill_inputs(1, 64, 1, 1, K, K, dtype, True, 93)
+    inp["q"] = torch.zeros_like(inp["q"])
+    o, s = _gpu_fwd(inp, chunk=64)
+    assert torch.count_nonzero(o) == 0
+    _, s_ref = recurrent(**inp)
+    assert_parity(to64(s), s_ref, DT[dtype], "state with q = 0")
+    # a large initial state (|S0| ~ 30)
+    inp = prefill_inputs(1, 64, 1, 2, K, K, dtype, True, 94)
+    inp["initial_state"] = inp["initial_state"] * 300.0
+    _check_full(inp, dtype, what="large state")
