@@ -311,11 +311,13 @@ struct PrepLds {
   static_assert(total <= 160 * 1024, "LDS");
 };
 
+// 8 waves: waves w and w + 4 own row block w; wave w builds q*exp(G - G_r) and the first half
+// of the shared k operand rows and computes Aq, wave w + 4 the k side and Mr.
 template <int KT>
-__global__ __launch_bounds__(256) void prep_kernel(BwdArgs a) {
+__global__ __launch_bounds__(512) void prep_kernel(BwdArgs a) {
   using L = PrepLds<KT>;
   using P = PB<KT>;
-  constexpr int PK = L::PK, PG = L::PG;
+  constexpr int PK = L::PK, PG = L::PG, NTH = 512;
   __shared__ __attribute__((aligned(16))) unsigned char lds[L::total];
   float* G = reinterpret_cast<float*>(lds + L::g);
   float* sb = reinterpret_cast<float*>(lds + L::bt);
@@ -325,7 +327,8 @@ __global__ __launch_bounds__(256) void prep_kernel(BwdArgs a) {
   bf16* ks = reinterpret_cast<bf16*>(lds + L::ks);
   bf16* bop = reinterpret_cast<bf16*>(lds + L::bop);
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w8 = tid >> 6;
+  const int w = w8 & 3, role = w8 >> 2;  // role 0: Aq side, 1: Mr side
   const int lr = lane & 15, lq = lane >> 4;
   const Chunk ch = item_chunk(a, blockIdx.x);
   if (ch.rows == 0) return;  // past the packed list's last chunk
@@ -336,38 +339,37 @@ __global__ __launch_bounds__(256) void prep_kernel(BwdArgs a) {
   const bf16* gb = a.g + ch.row0 * grow + (size_t)hv * KT;
   unsigned char* blk = a.blocks + ch.slot * P::bytes;
 
-  stage_qkg<KT, 256>(sq, sk, G, PK, PG, qb, kb, gb, qrow, grow, nrow, tid);
+  stage_qkg<KT, NTH>(sq, sk, G, PK, PG, qb, kb, gb, qrow, grow, nrow, tid);
   if (tid < kC) {
     float bv = tid < nrow ? ldf(a.beta + (ch.row0 + tid) * a.HV + hv) : 0.f;
     if ((a.flags & kFlagBetaSigmoid) && tid < nrow) bv = sigmoid_f32(bv);
     sb[tid] = bv;
     reinterpret_cast<float*>(blk + P::beta)[tid] = bv;
   }
-  cumsum_rows<KT, 256>(G, PG, reinterpret_cast<float*>(lds + L::tot), tid);  // includes barriers
+  cumsum_rows<KT, NTH>(G, PG, reinterpret_cast<float*>(lds + L::tot), tid);  // includes barriers
   if (a.flags & kFlagQkL2norm) {
-    l2norm_rows<KT, 256>(sq, sk, PK, tid);
+    l2norm_rows<KT, NTH>(sq, sk, PK, tid);
     __syncthreads();
   }
 
-  // operands of the row-block-w products, built by wave w
+  // operands of the row-block-w products
+  bf16* bw = bop + 8 * w * (w + 1) * PK;  // rows 0 .. 16w + 15, reference: first token of block w
   {
     const int r0 = 16 * w;
-    for (int u = lane; u < 16 * (KT / 8); u += 64) {  // q, k of block w relative to its first token
+    const bf16* src = role == 0 ? sq : sk;
+    bf16* dst = role == 0 ? qs : ks;
+    for (int u = lane; u < 16 * (KT / 8); u += 64) {  // q (k) of block w relative to its first token
       const int i = r0 + u / (KT / 8), c8 = 8 * (u % (KT / 8));
-      const bf16x8 qv = ld8(sq + i * PK + c8), kv = ld8(sk + i * PK + c8);
-      bf16x8 qo, ko;
+      const bf16x8 xv = ld8(src + i * PK + c8);
+      bf16x8 xo;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float f = ex(G[i * PG + c8 + e] - G[r0 * PG + c8 + e]);
-        qo[e] = static_cast<bf16>(static_cast<float>(qv[e]) * f);
-        ko[e] = static_cast<bf16>(static_cast<float>(kv[e]) * f);
-      }
-      st8(qs + i * PK + c8, qo);
-      st8(ks + i * PK + c8, ko);
+      for (int e = 0; e < 8; ++e)
+        xo[e] = static_cast<bf16>(static_cast<float>(xv[e]) * ex(G[i * PG + c8 + e] - G[r0 * PG + c8 + e]));
+      st8(dst + i * PK + c8, xo);
     }
-    bf16* bw = bop + 8 * w * (w + 1) * PK;  // rows 0 .. 16w + 15
-    for (int u = lane; u < 16 * (w + 1) * (KT / 8); u += 64) {
-      const int j = u / (KT / 8), c8 = 8 * (u % (KT / 8));
+    const int half = 8 * (w + 1);  // this role's half of the k operand rows
+    for (int u = lane; u < half * (KT / 8); u += 64) {
+      const int j = role * half + u / (KT / 8), c8 = 8 * (u % (KT / 8));
       const bf16x8 kv = ld8(sk + j * PK + c8);
       bf16x8 ko;
 #pragma unroll
@@ -376,49 +378,51 @@ __global__ __launch_bounds__(256) void prep_kernel(BwdArgs a) {
       st8(bw + j * PK + c8, ko);
     }
   }
-  wave_sync();
+  __syncthreads();
 
-  // Aq and Mr row block w; tiles J <= w (operands are this wave's own)
-  f32x4 aq[4], mr[4];
-  {
-    const bf16* bw = bop + 8 * w * (w + 1) * PK;
+  // Aq (role 0) or Mr (role 1), row block w; tiles J <= w
+  f32x4 acc[4];
 #pragma unroll
-    for (int J = 0; J < 4; ++J) {
-      aq[J] = mr[J] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (J <= w) {
-        mmaK<KT>(aq[J], qs + 16 * w * PK, PK, bw + 16 * J * PK, PK, lane);
-        mmaK<KT>(mr[J], ks + 16 * w * PK, PK, bw + 16 * J * PK, PK, lane);
-      }
-    }
+  for (int J = 0; J < 4; ++J) {
+    acc[J] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (J <= w) mmaK<KT>(acc[J], (role == 0 ? qs : ks) + 16 * w * PK, PK, bw + 16 * J * PK, PK, lane);
   }
   __syncthreads();  // qs / ks / bop are dead from here; mr / tf reuse them
   float* smr = reinterpret_cast<float*>(lds + L::mr);
   float* stf = reinterpret_cast<float*>(lds + L::tf);
   float* scr = reinterpret_cast<float*>(lds + L::scr) + w * 16 * 17;
-  {
+  if (role == 0) {
     bf16* aqt = reinterpret_cast<bf16*>(blk + P::aqt);
-    float* gmr = reinterpret_cast<float*>(blk + P::mr);
 #pragma unroll
     for (int J = 0; J < 4; ++J) {
       const int j = 16 * J + lr;
-      f32x4 av = aq[J], mv = mr[J];
+      f32x4 av = acc[J];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = 16 * w + 4 * lq + r;
         if (j > i) av[r] = 0.f;
-        if (j >= i) mv[r] = 0.f;
-        smr[i * 65 + j] = mv[r];
         stf[i * 65 + j] = 0.f;
       }
       st4(aqt + j * kC + 16 * w + 4 * lq, av);  // Aq^T row j, tokens i .. i+3
+    }
+  } else {
+    float* gmr = reinterpret_cast<float*>(blk + P::mr);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) gmr[(16 * w + 4 * lq + r) * kC + j] = mv[r];
+    for (int J = 0; J < 4; ++J) {
+      const int j = 16 * J + lr;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * w + 4 * lq + r;
+        const float mv = j < i ? acc[J][r] : 0.f;
+        smr[i * 65 + j] = mv;
+        gmr[i * kC + j] = mv;
+      }
     }
   }
-  wave_sync();
+  __syncthreads();
   // T = (I + diag(beta) Mr)^-1. Diagonal 16 x 16 blocks by forward substitution (wave w owns
   // block w; lane: column lr, partial sums over rows j = lq mod 4) ...
-  {
+  if (role == 0) {
     const int o = 16 * w;
     for (int ii = 0; ii < 16; ++ii) {
       float s = 0.f;
@@ -435,7 +439,7 @@ __global__ __launch_bounds__(256) void prep_kernel(BwdArgs a) {
   // T_IJ = -T_II sum_{J <= L < I} diag(beta_I) Mr_IL T_LJ, on fp32 MFMA
   for (int d = 1; d < 4; ++d) {
     const int I = d + w, J = w;
-    if (I < 4) {
+    if (role == 0 && I < 4) {
       f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
       for (int Lb = J; Lb < I; ++Lb)
         mma16_nn(acc, smr + 16 * I * 65 + 16 * Lb, 65, stf + 16 * Lb * 65 + 16 * J, 65, 16, lane);
@@ -453,7 +457,7 @@ __global__ __launch_bounds__(256) void prep_kernel(BwdArgs a) {
   {
     bf16* tm = reinterpret_cast<bf16*>(blk + P::tm);
     bf16* tt = reinterpret_cast<bf16*>(blk + P::tt);
-    for (int u = tid; u < kC * kC / 8; u += 256) {
+    for (int u = tid; u < kC * kC / 8; u += NTH) {
       const int row = u / 8, c8 = 8 * (u % 8);
       bf16x8 x, y;
 #pragma unroll
@@ -470,7 +474,7 @@ __global__ __launch_bounds__(256) void prep_kernel(BwdArgs a) {
   {
     bf16* kg = reinterpret_cast<bf16*>(blk + P::kg);
     bf16* kc = reinterpret_cast<bf16*>(blk + P::kc);
-    for (int u = tid; u < kC * KT / 8; u += 256) {
+    for (int u = tid; u < kC * KT / 8; u += NTH) {
       const int i = u / (KT / 8), c8 = 8 * (u % (KT / 8));
       const bf16x8 kv = ld8(sk + i * PK + c8);
       bf16x8 x, y;
@@ -486,7 +490,7 @@ __global__ __launch_bounds__(256) void prep_kernel(BwdArgs a) {
     bf16* kct = reinterpret_cast<bf16*>(blk + P::kct);
     bf16* qgt = reinterpret_cast<bf16*>(blk + P::qgt);
     bf16* kgt = reinterpret_cast<bf16*>(blk + P::kgt);
-    for (int u = tid; u < KT * kC / 8; u += 256) {
+    for (int u = tid; u < KT * kC / 8; u += NTH) {
       const int c = u % KT, i8 = 8 * (u / KT);
       bf16x8 x, y, z;
       const float gl = G[(kC - 1) * PG + c];
@@ -1381,7 +1385,7 @@ Layout varlen_layout(int nseq, int T, int H, int HV, int K, int V, unsigned flag
 template <int KT>
 hipError_t launch_cfg(BwdArgs a, hipStream_t stream) {
   const int items = a.ctab ? a.HV * a.NC : a.B * a.HV * a.NT;
-  hipLaunchKernelGGL((prep_kernel<KT>), dim3(items), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((prep_kernel<KT>), dim3(items), dim3(512), 0, stream, a);
   constexpr int NW = 2;
   const int sweeps = a.B * a.HV * ((a.V + 16 * NW - 1) / (16 * NW));
   hipLaunchKernelGGL((fwd_sweep_kernel<KT, NW>), dim3(sweeps), dim3(64 * NW), 0, stream, a);
