@@ -19,6 +19,9 @@ Three independent CPU formulations, all in float64 numpy:
   explicitly with K x K matrices. Only for tiny shapes.
 * ``recurrent_bwd``: gradients of O1 by reverse-mode differentiation of each
   token step, written out (K3 README roadmap rows L1/L4).
+* ``gate`` / ``gate_bwd``: the decay gate that produces g from the gate input,
+  A_log and dt_bias (standard and safe, K3 README roadmap row L5), and its
+  gradients.
 * ``transforms``: the optional in-operator input transforms (q/k L2
   normalisation, beta sigmoid) that ``recurrent`` / ``decode_step`` apply on
   request.
@@ -33,6 +36,7 @@ from .chunked import chunked, forward_substitution_inverse
 from .brute import brute
 from .transforms import l2_normalize, sigmoid
 from .backward import recurrent_bwd
+from .gate import gate, gate_bwd
 
 __all__ = [
     "decode_step",
@@ -43,4 +47,6 @@ __all__ = [
     "l2_normalize",
     "sigmoid",
     "recurrent_bwd",
+    "gate",
+    "gate_bwd",
 ]
