@@ -7,7 +7,8 @@ layers). `value` is prefill tokens/s (B*T per step). The decode step
 (kda_recurrent_step, 64 consecutive steps on a B=256, H=HV=16, K=V=128 fp32
 state cache) is timed in the same run and reported under "decode", and the chunked
 backward (kda_chunk_bwd: dq, dk, dv, dg, dbeta, dh0 of the prefill workload for a
-seeded dO) under "backward".
+seeded dO) under "backward", and the decay gate (kda_gate_fwd / kda_gate_bwd on the
+same layer's [B, T, HV, K] gate input) under "gate".
 
 Timing uses HIP events recorded on the stream the kernels are launched on,
 bracketed by device synchronisation. One prefill call is two kernels on that
@@ -69,6 +70,13 @@ def backward_algorithmic(B, T, H, HV, K, V, ib):
     reads = qk + per_v + state
     writes = qk + B * T * HV * (V + K + 1) * ib + state
     return reads + writes
+
+
+def gate_algorithmic(n, HV, K, ib=2):
+    """Bytes of the gate's calls over n elements: forward reads x and writes g; backward
+    reads x and dg and writes dx, plus the fp32 parameters and their gradients."""
+    params = HV * 4 + HV * K * 4
+    return 2 * n * ib + params, 3 * n * ib + 2 * params
 
 
 def decode_algorithmic(B, H, HV, K, V, ib):
@@ -180,6 +188,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-gate", action="store_true")
     ap.add_argument("--backward-steps", type=int, default=5)
     args = ap.parse_args()
     if args.gpus != 1:
@@ -336,6 +345,38 @@ def main():
                          "algorithmic_bytes_per_launch": bbytes},
         }
         del dout
+
+    # ---------------- decay gate (forward and backward) on the prefill layer's g shape
+    if not args.no_gate:
+        from synth import gate_inputs
+        log(f"bench: timing the decay gate on the {PREFILL_WORKLOAD} gate shape")
+        gi = gate_inputs(c["B"], c["T"], c["HV"], c["K"], "bf16", seed=4322)
+        gx, gA, gb, gdg = (gi[n].to(dev) for n in ("x", "A_log", "dt_bias", "dg"))
+        del gi
+        f_avg, f_med, f_min = time_launches(lambda: kda.kda_gate_fwd(gx, gA, gb, -5.0),
+                                            args.steps, args.warmup, torch)
+        r_avg, r_med, r_min = time_launches(lambda: kda.kda_gate_bwd(gx, gA, gb, gdg, -5.0),
+                                            args.steps, args.warmup, torch)
+        n = gx.numel()
+        fbytes, rbytes = gate_algorithmic(n, c["HV"], c["K"])
+        result["gate"] = {
+            "workload": f"safe gate (lower bound -5) on x [B={c['B']}, T={c['T']}, "
+                        f"HV={c['HV']}, K={c['K']}] bf16, A_log [HV] and dt_bias [HV, K] fp32",
+            "fwd": {"ms_per_call": f_avg, "median_ms": f_med, "min_ms": f_min,
+                    "roofline": {"bound": "hbm", "achieved": fbytes / (f_avg * 1e-3) / 1e9,
+                                 "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                 "frac": fbytes / (f_avg * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                 "kernel": "kda::gate::fwd_kernel<bf16>",
+                                 "algorithmic_bytes_per_launch": fbytes}},
+            "bwd": {"ms_per_call": r_avg, "median_ms": r_med, "min_ms": r_min,
+                    "roofline": {"bound": "hbm", "achieved": rbytes / (r_avg * 1e-3) / 1e9,
+                                 "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                 "frac": rbytes / (r_avg * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                 "kernel": "kda::gate::bwd_kernel<bf16> + reduce_kernel "
+                                           "(one kda_gate_bwd call)",
+                                 "algorithmic_bytes_per_launch": rbytes}},
+        }
+        del gx, gA, gb, gdg
     del d
 
     # ---------------- oracle on the host

@@ -13,6 +13,9 @@ Entry points (same names as the C ABI):
   -> (o, final_state)``
 * ``kda_recurrent_step(q, k, v, g, beta, state, scale=None, qk_l2norm=False,
   beta_sigmoid=False) -> o`` (updates ``state`` in place)
+* ``kda_gate_fwd(x, A_log, dt_bias=None, lower_bound=None) -> g`` and
+  ``kda_gate_bwd(x, A_log, dt_bias, dg, lower_bound=None) -> (dx, dA_log, ddt_bias)``:
+  the decay gate that produces g, and its backward
 
 ``qk_l2norm`` / ``beta_sigmoid`` ask the kernels to L2-normalise q and k and to
 apply the sigmoid to beta (``kda_chunk_fwd_ex`` / ``kda_recurrent_step_ex``).
@@ -26,7 +29,7 @@ import torch
 
 __all__ = ["kda_chunk_fwd", "kda_chunk_fwd_varlen", "kda_chunk_bwd",
            "kda_chunk_bwd_varlen", "kda_recurrent_step",
-           "kda_recurrent_step_slots", "library", "library_path", "status_string",
+           "kda_recurrent_step_slots", "kda_gate_fwd", "kda_gate_bwd", "library", "library_path", "status_string",
            "KDA_OK", "KDA_ERR_INVALID", "KDA_ERR_UNSUPPORTED", "KDA_ERR_HIP",
            "KDA_FLAG_QK_L2NORM", "KDA_FLAG_BETA_SIGMOID"]
 
@@ -77,6 +80,12 @@ def library():
     lib.kda_recurrent_step_ex.restype = i
     lib.kda_recurrent_step_slots.argtypes = [vp] * 7 + [i, vp] + [i] * 5 + [f, i, ctypes.c_uint, vp]
     lib.kda_recurrent_step_slots.restype = i
+    lib.kda_gate_fwd.argtypes = [vp] * 4 + [i] * 4 + [f, i, vp]
+    lib.kda_gate_fwd.restype = i
+    lib.kda_gate_bwd_workspace_size.argtypes = [i] * 5
+    lib.kda_gate_bwd_workspace_size.restype = sz
+    lib.kda_gate_bwd.argtypes = [vp] * 7 + [i] * 4 + [f, i, vp, sz, vp]
+    lib.kda_gate_bwd.restype = i
     lib.kda_status_string.argtypes = [i]
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_version.argtypes = []
@@ -354,3 +363,56 @@ def kda_recurrent_step_slots(q, k, v, g, beta, state_pool, slots, scale=None, qk
                                           _flags(qk_l2norm, beta_sigmoid), ctypes.c_void_p(stream))
     _check(rc)
     return o
+
+
+def _gate_args(x, A_log, dt_bias, lower_bound):
+    _require(x.is_cuda, "inputs must be on a GPU")
+    dev, dt = x.device, x.dtype
+    _require(dt in _DTYPE, f"unsupported dtype {dt}")
+    _require(x.dim() == 4, "x must be [B, T, HV, K]")
+    B, T, HV, K = x.shape
+    _check_tensors([("x", x)], dt, dev)
+    _require(tuple(A_log.shape) == (HV,), "A_log must be [HV]")
+    _check_tensors([("A_log", A_log)], torch.float32, dev)
+    if dt_bias is not None:
+        _require(dt_bias.numel() == HV * K, "dt_bias must be [HV, K]")
+        _check_tensors([("dt_bias", dt_bias)], torch.float32, dev)
+    lb = float("-inf") if lower_bound is None else float(lower_bound)
+    return dev, dt, B, T, HV, K, lb
+
+
+def kda_gate_fwd(x, A_log, dt_bias=None, lower_bound=None):
+    """The KDA decay gate: g = max(lower_bound, -exp(A_log[hv]) * softplus(x + dt_bias[hv]))
+    for x [B,T,HV,K] (bf16 or float32), A_log [HV] and dt_bias [HV,K] float32 (or None).
+    lower_bound None is the standard gate; a number <= 0 (the pages use -5) the safe gate.
+    Returns g shaped and typed like x."""
+    dev, dt, B, T, HV, K, lb = _gate_args(x, A_log, dt_bias, lower_bound)
+    lib = library()
+    g = torch.empty_like(x)
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        rc = lib.kda_gate_fwd(_ptr(x), _ptr(A_log), _ptr(dt_bias), _ptr(g), B, T, HV, K, lb,
+                              _DTYPE[dt], ctypes.c_void_p(stream))
+    _check(rc)
+    return g
+
+
+def kda_gate_bwd(x, A_log, dt_bias, dg, lower_bound=None):
+    """Backward of kda_gate_fwd for the gradient dg reaching g. Returns (dx like x,
+    dA_log [HV] float32, ddt_bias [HV,K] float32)."""
+    dev, dt, B, T, HV, K, lb = _gate_args(x, A_log, dt_bias, lower_bound)
+    _require(dg.shape == x.shape, "dg must match x")
+    _check_tensors([("dg", dg)], dt, dev)
+    lib = library()
+    dx = torch.empty_like(x)
+    dA_log = torch.empty((HV,), dtype=torch.float32, device=dev)
+    ddt_bias = torch.empty((HV, K), dtype=torch.float32, device=dev)
+    ws_bytes = lib.kda_gate_bwd_workspace_size(B, T, HV, K, _DTYPE[dt])
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        rc = lib.kda_gate_bwd(_ptr(x), _ptr(A_log), _ptr(dt_bias), _ptr(dg), _ptr(dx),
+                              _ptr(dA_log), _ptr(ddt_bias), B, T, HV, K, lb, _DTYPE[dt],
+                              _ptr(ws), ws_bytes, ctypes.c_void_p(stream))
+    _check(rc)
+    return dx, dA_log, ddt_bias

@@ -13,7 +13,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libkda.so")
 SOURCES = ["kda_api.hip", "kda_decode.hip", "kda_prefill.hip", "kda_chunk_bf16.hip",
-           "kda_chunk_wy.hip", "kda_chunk_bwd.hip"]
+           "kda_chunk_wy.hip", "kda_chunk_bwd.hip", "kda_gate.hip"]
 
 
 def hipcc():

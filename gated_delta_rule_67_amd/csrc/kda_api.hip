@@ -24,6 +24,14 @@ hipError_t launch_chunk_bwd(const void*, const void*, const void*, const void*, 
                             const int*, const float*, const void*, const float*, void*, void*,
                             void*, void*, void*, float*, int, int, int, int, int, int, float,
                             unsigned, void*, hipStream_t);
+size_t gate_bwd_workspace_bytes(int64_t rows, int HV, int K, bool bf);
+hipError_t launch_gate_fwd(const void* x, const float* A_log, const float* dt_bias, void* g,
+                           int64_t rows, int HV, int K, float lower_bound, bool bf,
+                           hipStream_t stream);
+hipError_t launch_gate_bwd(const void* x, const float* A_log, const float* dt_bias,
+                           const void* dg, void* dx, float* dA_log, float* ddt_bias,
+                           int64_t rows, int HV, int K, float lower_bound, bool bf,
+                           void* workspace, hipStream_t stream);
 }  // namespace kda
 
 namespace {
@@ -53,6 +61,16 @@ int check_common(int B, int H, int HV, int K, int V, float scale, int dtype) {
   if (!isfinite(scale)) return KDA_ERR_INVALID;
   if (dtype != KDA_DTYPE_F32 && dtype != KDA_DTYPE_BF16) return KDA_ERR_INVALID;
   if (K > kMaxDim || V > kMaxDim) return KDA_ERR_UNSUPPORTED;
+  return KDA_OK;
+}
+
+// Shapes and bounds both gate entry points accept: KDA_OK, or the status to return.
+int check_gate(int B, int T, int HV, int K, float lower_bound, int dtype) {
+  if (B < 0 || T < 0 || !positive(HV) || !positive(K)) return KDA_ERR_INVALID;
+  if (isnan(lower_bound) || lower_bound > 0.f) return KDA_ERR_INVALID;
+  if (dtype != KDA_DTYPE_F32 && dtype != KDA_DTYPE_BF16) return KDA_ERR_INVALID;
+  if (K % (dtype == KDA_DTYPE_BF16 ? 8 : 4) != 0) return KDA_ERR_UNSUPPORTED;
+  if ((int64_t)HV * K > (1 << 24)) return KDA_ERR_UNSUPPORTED;
   return KDA_OK;
 }
 
@@ -240,6 +258,44 @@ int kda_chunk_bwd_varlen(const void* q, const void* k, const void* v, const void
                                              dht, dq, dk, dv, dg, dbeta, dh0, N, T, H, HV, K, V,
                                              scale, flags, workspace,
                                              static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+int kda_gate_fwd(const void* x, const float* A_log, const float* dt_bias, void* g, int B, int T,
+                 int HV, int K, float lower_bound, int dtype, void* stream) {
+  // per-token tensors of an empty batch may be NULL (torch gives 0-element tensors no storage)
+  const bool empty = (int64_t)B * T == 0;
+  if (!A_log || (!empty && (!x || !g))) return KDA_ERR_INVALID;
+  const int rc = check_gate(B, T, HV, K, lower_bound, dtype);
+  if (rc != KDA_OK) return rc;
+  if (!aligned16(x) || !aligned16(g)) return KDA_ERR_UNSUPPORTED;
+  const hipError_t e = kda::launch_gate_fwd(x, A_log, dt_bias, g, (int64_t)B * T, HV, K,
+                                            lower_bound, dtype == KDA_DTYPE_BF16,
+                                            static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+size_t kda_gate_bwd_workspace_size(int B, int T, int HV, int K, int dtype) {
+  if (check_gate(B, T, HV, K, -INFINITY, dtype) != KDA_OK) return 0;
+  return kda::gate_bwd_workspace_bytes((int64_t)B * T, HV, K, dtype == KDA_DTYPE_BF16);
+}
+
+int kda_gate_bwd(const void* x, const float* A_log, const float* dt_bias, const void* dg,
+                 void* dx, float* dA_log, float* ddt_bias, int B, int T, int HV, int K,
+                 float lower_bound, int dtype, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+  const bool empty = (int64_t)B * T == 0;
+  if (!A_log || (!empty && (!x || !dg || !dx))) return KDA_ERR_INVALID;
+  const int rc = check_gate(B, T, HV, K, lower_bound, dtype);
+  if (rc != KDA_OK) return rc;
+  if (!aligned16(x) || !aligned16(dg) || !aligned16(dx)) return KDA_ERR_UNSUPPORTED;
+  const size_t need = kda_gate_bwd_workspace_size(B, T, HV, K, dtype);
+  if (need && (!workspace || workspace_bytes < need)) return KDA_ERR_INVALID;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0) return KDA_ERR_INVALID;
+  const hipError_t e = kda::launch_gate_bwd(x, A_log, dt_bias, dg, dx, dA_log, ddt_bias,
+                                            (int64_t)B * T, HV, K, lower_bound,
+                                            dtype == KDA_DTYPE_BF16, workspace,
+                                            static_cast<hipStream_t>(stream));
   return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 

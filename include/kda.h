@@ -266,6 +266,55 @@ int kda_recurrent_step_slots(const void* q, const void* k, const void* v, const 
                              int num_slots, void* o, int B, int H, int HV, int K, int V,
                              float scale, int dtype, unsigned flags, void* stream);
 
+/*
+ * The KDA decay gate: g from the gate projection (K3 README, roadmap row L5: the standard
+ * and the safe gate; key-constraints table, exp-underflow row: the gate path clamps g at a
+ * lower bound of -5 before it is applied; the DM-KDAGQA-1.7B-SD model card's Model table:
+ * a per-channel decay gate). The pages give no formula; the reading (the workloads' recipe
+ * g = max(-5, -softplus(x)) is this gate at A_log = 0, dt_bias = 0), per token, value head
+ * hv and key channel c, in float32:
+ *
+ *     z = x + dt_bias[hv, c]
+ *     g = max(lower_bound, -exp(A_log[hv]) * log(1 + exp(z)))
+ *
+ *   x         [B, T, HV, K]  dtype   gate input (the projection before the gate)
+ *   A_log     [HV]           float32 log of the per-head rate
+ *   dt_bias   [HV, K]        float32 per-channel bias, or NULL (zeros)
+ *   g         [B, T, HV, K]  dtype out (natural-log decay, <= 0), ready for kda_chunk_fwd /
+ *                            kda_recurrent_step; must not overlap x
+ *   lower_bound  -INFINITY: the standard gate (no clamp); finite and <= 0: the safe gate
+ *                (the pages use -5); NaN or > 0: KDA_ERR_INVALID
+ *
+ * Constraints: B, T >= 0 (B * T == 0: nothing to do, and x, g may be NULL); HV, K >= 1; K % 8 == 0 for bf16,
+ * K % 4 == 0 for float32, x and g 16-byte aligned, HV * K <= 2^24 (else KDA_ERR_UNSUPPORTED).
+ */
+int kda_gate_fwd(const void* x, const float* A_log, const float* dt_bias, void* g, int B, int T,
+                 int HV, int K, float lower_bound, int dtype, void* stream);
+
+/*
+ * Backward of kda_gate_fwd (K3 README, roadmap row L5: gradients of A_log, dt_bias and the
+ * gate input): for the gradient dg reaching g, with m = 1 where -exp(A_log) softplus(z) >=
+ * lower_bound and 0 where the clamp holds g,
+ *
+ *     dx             = dg * m * (-exp(A_log[hv])) * logistic(z)          [B, T, HV, K] dtype
+ *     ddt_bias[hv,c] = sum over (b, t) of dx                             [HV, K] float32
+ *     dA_log[hv]     = sum over (b, t, c) of dg * m * g_standard         [HV] float32
+ *
+ * dA_log and ddt_bias may be NULL (not returned); every other pointer is required (x, dg, dx
+ * may be NULL when B * T == 0; the sums are then zero). The sums
+ * are taken in a fixed order (bitwise reproducible for equal arguments). Outputs must not
+ * overlap inputs. workspace: device memory of kda_gate_bwd_workspace_size() bytes (per-block
+ * partial sums), 256-byte aligned, caller-owned, overwritten; NULL allowed only when that
+ * size is 0 (B * T == 0), else KDA_ERR_INVALID. Constraints as kda_gate_fwd; dg and dx
+ * 16-byte aligned.
+ */
+size_t kda_gate_bwd_workspace_size(int B, int T, int HV, int K, int dtype);
+
+int kda_gate_bwd(const void* x, const float* A_log, const float* dt_bias, const void* dg,
+                 void* dx, float* dA_log, float* ddt_bias, int B, int T, int HV, int K,
+                 float lower_bound, int dtype, void* workspace, size_t workspace_bytes,
+                 void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -10,6 +10,8 @@ Value distributions (the layer shapes and distributions of the five workloads):
 * beta ``[B, T, HV]``: ``sigmoid(N(0, 1))``;
 * initial state ``[B, HV, K, V]`` float32: ``0.1 * N(0, 1)`` or absent (zeros).
 
+``gate_inputs`` draws the decay gate's inputs (its docstring gives the recipe).
+
 Draw order is q, k, v, g, beta, state from one ``torch.Generator('cpu')``
 seeded with ``seed``; everything is computed in float32 and rounded to the
 workload dtype (round to nearest even for bfloat16). The gate and beta modes
@@ -110,6 +112,29 @@ def decode_inputs(steps, B, H, HV, K, V, dtype="bf16", init_state=True, seed=0,
     else:
         s0 = torch.zeros((B, HV, K, V), dtype=torch.float32)
     return dict(q=q, k=k, v=v, g=g, beta=b, state=s0, scale=1.0 / math.sqrt(K))
+
+
+def gate_inputs(B, T, HV, K, dtype="bf16", seed=0, x_std=1.0):
+    """Inputs of the decay gate and its backward, drawn in this order:
+
+    * x ``[B, T, HV, K]``: ``x_std * N(0, 1)`` (the gate projection), rounded to dtype;
+    * A_log ``[HV]`` float32: ``log(U(1, 16))`` per head;
+    * dt_bias ``[HV, K]`` float32: ``log(expm1(dt))`` with dt log-uniform in
+      [1e-3, 1e-1] (softplus(dt_bias) = dt), per channel;
+    * dg ``[B, T, HV, K]``: ``N(0, 1)``, rounded to dtype (the gradient reaching g).
+
+    The pages give no initialisation for A_log and dt_bias; these are the usual ranges of
+    per-head rates and per-channel time steps of decay gates."""
+    gen = torch.Generator("cpu").manual_seed(seed)
+    dt = DTYPES[dtype]
+    x = (x_std * torch.randn((B, T, HV, K), generator=gen, dtype=torch.float32)).to(dt)
+    a = 1.0 + 15.0 * torch.rand((HV,), generator=gen, dtype=torch.float64)
+    A_log = torch.log(a).float()
+    u = torch.rand((HV, K), generator=gen, dtype=torch.float64)
+    step = torch.exp(math.log(1e-3) + u * (math.log(1e-1) - math.log(1e-3)))
+    dt_bias = torch.log(torch.expm1(step)).float()
+    dg = torch.randn((B, T, HV, K), generator=gen, dtype=torch.float32).to(dt)
+    return dict(x=x, A_log=A_log, dt_bias=dt_bias, dg=dg)
 
 
 def workload_inputs(name, **overrides):

@@ -31,7 +31,8 @@ def test_header_declares_the_boundary():
     names = _declared_functions()
     for required in ("kda_chunk_fwd", "kda_chunk_fwd_ex", "kda_chunk_fwd_workspace_size",
                      "kda_chunk_fwd_varlen", "kda_chunk_fwd_varlen_workspace_size", "kda_chunk_bwd",
-                     "kda_recurrent_step_slots",
+                     "kda_recurrent_step_slots", "kda_gate_fwd", "kda_gate_bwd",
+                     "kda_gate_bwd_workspace_size",
                      "kda_recurrent_step", "kda_recurrent_step_ex", "kda_status_string",
                      "kda_version"):
         assert required in names
@@ -285,3 +286,72 @@ def test_chunk_bwd_ex_rejects_unknown_flags(lib):
     # the q/k normalisation needs fp32 per-value-head dq / dk even without GVA
     assert (lib.kda_chunk_bwd_workspace_size_ex(1, 64, 1, 1, 64, 64, 64, 1, 1)
             > lib.kda_chunk_bwd_workspace_size_ex(1, 64, 1, 1, 64, 64, 64, 1, 0))
+
+
+def _gate(lib, bwd=False, **kw):
+    a = dict(x=FAKE, A_log=FAKE, dt_bias=None, g=FAKE, dg=FAKE, dx=FAKE, B=2, T=64, HV=4, K=64,
+             lb=-5.0, dtype=1, ws=FAKE, ws_bytes=1 << 30)
+    a.update(kw)
+    if not bwd:
+        return lib.kda_gate_fwd(a["x"], a["A_log"], a["dt_bias"], a["g"], a["B"], a["T"], a["HV"],
+                                a["K"], a["lb"], a["dtype"], None)
+    return lib.kda_gate_bwd(a["x"], a["A_log"], a["dt_bias"], a["dg"], a["dx"], None, None,
+                            a["B"], a["T"], a["HV"], a["K"], a["lb"], a["dtype"], a["ws"],
+                            a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("bwd", [False, True])
+@pytest.mark.parametrize("bad,rc", [
+    (dict(x=None), kda.KDA_ERR_INVALID),
+    (dict(A_log=None), kda.KDA_ERR_INVALID),
+    (dict(B=-1), kda.KDA_ERR_INVALID),
+    (dict(HV=0), kda.KDA_ERR_INVALID),
+    (dict(K=0), kda.KDA_ERR_INVALID),
+    (dict(lb=float("nan")), kda.KDA_ERR_INVALID),
+    (dict(lb=0.5), kda.KDA_ERR_INVALID),          # a positive bound would make g grow the state
+    (dict(dtype=2), kda.KDA_ERR_INVALID),
+    (dict(K=12), kda.KDA_ERR_UNSUPPORTED),        # bf16 needs K % 8 == 0
+    (dict(K=6, dtype=0), kda.KDA_ERR_UNSUPPORTED),  # float32 needs K % 4 == 0
+    (dict(x=ctypes.c_void_p(0x1008)), kda.KDA_ERR_UNSUPPORTED),  # not 16-byte aligned
+])
+def test_gate_rejects_invalid_arguments(lib, bwd, bad, rc):
+    assert _gate(lib, bwd, **bad) == rc
+
+
+@pytest.mark.parametrize("bad,rc", [
+    (dict(g=None), kda.KDA_ERR_INVALID),
+])
+def test_gate_fwd_rejects_missing_output(lib, bad, rc):
+    assert _gate(lib, False, **bad) == rc
+
+
+@pytest.mark.parametrize("bad,rc", [
+    (dict(dg=None), kda.KDA_ERR_INVALID),
+    (dict(dx=None), kda.KDA_ERR_INVALID),
+    (dict(ws=None), kda.KDA_ERR_INVALID),
+    (dict(ws_bytes=1024), kda.KDA_ERR_INVALID),            # workspace too small
+    (dict(ws=ctypes.c_void_p(0x1010)), kda.KDA_ERR_INVALID),  # misaligned
+    (dict(dx=ctypes.c_void_p(0x1008)), kda.KDA_ERR_UNSUPPORTED),
+])
+def test_gate_bwd_rejects_invalid_arguments(lib, bad, rc):
+    assert _gate(lib, True, **bad) == rc
+
+
+def test_gate_empty_input_needs_no_launch(lib):
+    assert _gate(lib, False, B=0) == kda.KDA_OK
+    assert _gate(lib, False, T=0) == kda.KDA_OK
+
+
+def test_gate_bwd_workspace_size(lib):
+    ws = lib.kda_gate_bwd_workspace_size
+    assert ws(0, 64, 4, 64, 1) == 0
+    assert ws(2, 64, 0, 64, 1) == 0          # invalid arguments
+    assert ws(2, 64, 4, 12, 1) == 0          # unsupported K
+    big = ws(4, 8192, 16, 128, 1)
+    assert big % 256 == 0 and 0 < big <= 16 << 20   # partial sums stay small next to the tensors
+    assert ws(4, 8192, 16, 128, 0) > 0
+
+
+def test_gate_empty_input_accepts_null_token_tensors(lib):
+    assert _gate(lib, False, B=0, x=None, g=None) == kda.KDA_OK
+    assert _gate(lib, False, B=0, A_log=None) == kda.KDA_ERR_INVALID
