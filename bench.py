@@ -357,6 +357,13 @@ def main():
                                             args.steps, args.warmup, torch)
         r_avg, r_med, r_min = time_launches(lambda: kda.kda_gate_bwd(gx, gA, gb, gdg, -5.0),
                                             args.steps, args.warmup, torch)
+        # the gate fused into the prefill, against the gate then the prefill
+        fused = lambda: kda.kda_chunk_fwd_gated(d["q"], d["k"], d["v"], gx, gA, gb, d["beta"], -5.0,
+                                                d["scale"], d["initial_state"])
+        unfused = lambda: kda.kda_chunk_fwd(d["q"], d["k"], d["v"], kda.kda_gate_fwd(gx, gA, gb, -5.0),
+                                            d["beta"], d["scale"], d["initial_state"])
+        u_avg, u_med, _ = time_launches(unfused, args.steps, args.warmup, torch)
+        z_avg, z_med, _ = time_launches(fused, args.steps, args.warmup, torch)
         n = gx.numel()
         fbytes, rbytes = gate_algorithmic(n, c["HV"], c["K"])
         result["gate"] = {
@@ -375,6 +382,13 @@ def main():
                                  "kernel": "kda::gate::bwd_kernel<bf16> + reduce_kernel "
                                            "(one kda_gate_bwd call)",
                                  "algorithmic_bytes_per_launch": rbytes}},
+            "prefill_gated": {
+                "workload": PREFILL_WORKLOAD + " with g made by the safe gate from x",
+                "fused_ms": z_avg, "fused_median_ms": z_med,
+                "fused_tokens_per_s": tokens / (z_avg * 1e-3),
+                "gate_then_prefill_ms": u_avg, "gate_then_prefill_median_ms": u_med,
+                "kernel": "kda_chunk_fwd_gated (factors_kernel with the gate + state_kernel) "
+                          "against kda_gate_fwd + kda_chunk_fwd"},
         }
         del gx, gA, gb, gdg
     del d

@@ -16,6 +16,8 @@ Entry points (same names as the C ABI):
 * ``kda_gate_fwd(x, A_log, dt_bias=None, lower_bound=None) -> g`` and
   ``kda_gate_bwd(x, A_log, dt_bias, dg, lower_bound=None) -> (dx, dA_log, ddt_bias)``:
   the decay gate that produces g, and its backward
+* ``kda_chunk_fwd_gated`` / ``kda_recurrent_step_gated``: the prefill and the decode step
+  with that gate applied inside the kernels (the gate's input in place of g)
 
 ``qk_l2norm`` / ``beta_sigmoid`` ask the kernels to L2-normalise q and k and to
 apply the sigmoid to beta (``kda_chunk_fwd_ex`` / ``kda_recurrent_step_ex``).
@@ -29,7 +31,8 @@ import torch
 
 __all__ = ["kda_chunk_fwd", "kda_chunk_fwd_varlen", "kda_chunk_bwd",
            "kda_chunk_bwd_varlen", "kda_recurrent_step",
-           "kda_recurrent_step_slots", "kda_gate_fwd", "kda_gate_bwd", "library", "library_path", "status_string",
+           "kda_recurrent_step_slots", "kda_gate_fwd", "kda_gate_bwd",
+           "kda_chunk_fwd_gated", "kda_recurrent_step_gated", "library", "library_path", "status_string",
            "KDA_OK", "KDA_ERR_INVALID", "KDA_ERR_UNSUPPORTED", "KDA_ERR_HIP",
            "KDA_FLAG_QK_L2NORM", "KDA_FLAG_BETA_SIGMOID"]
 
@@ -86,6 +89,12 @@ def library():
     lib.kda_gate_bwd_workspace_size.restype = sz
     lib.kda_gate_bwd.argtypes = [vp] * 7 + [i] * 4 + [f, i, vp, sz, vp]
     lib.kda_gate_bwd.restype = i
+    lib.kda_chunk_fwd_gated.argtypes = [vp] * 6 + [f] + [vp] * 4 + [i] * 6 + [f, i, i, vp, sz,
+                                                                            ctypes.c_uint, vp]
+    lib.kda_chunk_fwd_gated.restype = i
+    lib.kda_recurrent_step_gated.argtypes = [vp] * 6 + [f] + [vp] * 3 + [i] * 5 + [f, i,
+                                                                                 ctypes.c_uint, vp]
+    lib.kda_recurrent_step_gated.restype = i
     lib.kda_status_string.argtypes = [i]
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_version.argtypes = []
@@ -416,3 +425,83 @@ def kda_gate_bwd(x, A_log, dt_bias, dg, lower_bound=None):
                               _ptr(ws), ws_bytes, ctypes.c_void_p(stream))
     _check(rc)
     return dx, dA_log, ddt_bias
+
+
+def _gate_params(A_log, dt_bias, lower_bound, HV, K, dev):
+    _require(tuple(A_log.shape) == (HV,), "A_log must be [HV]")
+    _check_tensors([("A_log", A_log)], torch.float32, dev)
+    if dt_bias is not None:
+        _require(dt_bias.numel() == HV * K, "dt_bias must be [HV, K]")
+        _check_tensors([("dt_bias", dt_bias)], torch.float32, dev)
+    return float("-inf") if lower_bound is None else float(lower_bound)
+
+
+def kda_chunk_fwd_gated(q, k, v, gate_x, A_log, dt_bias, beta, lower_bound=-5.0, scale=None,
+                        initial_state=None, output_final_state=True, chunk_size=64,
+                        qk_l2norm=False, beta_sigmoid=False):
+    """kda_chunk_fwd with the decay gate applied in the kernels: gate_x [B,T,HV,K] (bf16) is
+    the gate's input; g = max(lower_bound, -exp(A_log) softplus(gate_x + dt_bias)), rounded
+    to bf16 as kda_gate_fwd stores it. lower_bound None: the standard gate.
+    Returns (o, final_state)."""
+    _require(q.is_cuda, "inputs must be on a GPU")
+    dev, dt = q.device, q.dtype
+    _require(dt in _DTYPE, f"unsupported dtype {dt}")
+    B, T, H, K = q.shape
+    HV, V = v.shape[2], v.shape[3]
+    _require(k.shape == q.shape, "k must match q")
+    _require(tuple(v.shape[:2]) == (B, T), "v must be [B, T, HV, V]")
+    _require(tuple(gate_x.shape) == (B, T, HV, K), "gate_x must be [B, T, HV, K]")
+    _require(tuple(beta.shape) == (B, T, HV), "beta must be [B, T, HV]")
+    _check_tensors([("q", q), ("k", k), ("v", v), ("gate_x", gate_x), ("beta", beta)], dt, dev)
+    lb = _gate_params(A_log, dt_bias, lower_bound, HV, K, dev)
+    if initial_state is not None:
+        _require(tuple(initial_state.shape) == (B, HV, K, V), "initial_state must be [B, HV, K, V]")
+        _check_tensors([("initial_state", initial_state)], torch.float32, dev)
+    if scale is None:
+        scale = 1.0 / math.sqrt(K)
+    lib = library()
+    o = torch.empty((B, T, HV, V), dtype=dt, device=dev)
+    final = torch.empty((B, HV, K, V), dtype=torch.float32, device=dev) if output_final_state else None
+    ws_bytes = lib.kda_chunk_fwd_workspace_size(B, T, H, HV, K, V, chunk_size, _DTYPE[dt])
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        rc = lib.kda_chunk_fwd_gated(_ptr(q), _ptr(k), _ptr(v), _ptr(gate_x), _ptr(A_log),
+                                     _ptr(dt_bias), lb, _ptr(beta), _ptr(initial_state),
+                                     _ptr(final), _ptr(o), B, T, H, HV, K, V, float(scale),
+                                     int(chunk_size), _DTYPE[dt], _ptr(ws), ws_bytes,
+                                     _flags(qk_l2norm, beta_sigmoid), ctypes.c_void_p(stream))
+    _check(rc)
+    return o, final
+
+
+def kda_recurrent_step_gated(q, k, v, gate_x, A_log, dt_bias, beta, state, lower_bound=-5.0,
+                             scale=None, qk_l2norm=False, beta_sigmoid=False):
+    """kda_recurrent_step with the decay gate applied in the kernel: gate_x [B,HV,K] is the
+    gate's input (as kda_chunk_fwd_gated). Updates state in place; returns o [B,HV,V]."""
+    _require(q.is_cuda, "inputs must be on a GPU")
+    dev, dt = q.device, q.dtype
+    _require(dt in _DTYPE, f"unsupported dtype {dt}")
+    if q.dim() == 4:
+        q, k, v, gate_x, beta = q[:, 0], k[:, 0], v[:, 0], gate_x[:, 0], beta[:, 0]
+    B, H, K = q.shape
+    HV, V = v.shape[1], v.shape[2]
+    _require(k.shape == q.shape, "k must match q")
+    _require(tuple(gate_x.shape) == (B, HV, K), "gate_x must be [B, HV, K]")
+    _require(tuple(beta.shape) == (B, HV), "beta must be [B, HV]")
+    _require(tuple(state.shape) == (B, HV, K, V), "state must be [B, HV, K, V]")
+    _check_tensors([("q", q), ("k", k), ("v", v), ("gate_x", gate_x), ("beta", beta)], dt, dev)
+    _check_tensors([("state", state)], torch.float32, dev)
+    lb = _gate_params(A_log, dt_bias, lower_bound, HV, K, dev)
+    if scale is None:
+        scale = 1.0 / math.sqrt(K)
+    lib = library()
+    o = torch.empty((B, HV, V), dtype=dt, device=dev)
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        rc = lib.kda_recurrent_step_gated(_ptr(q), _ptr(k), _ptr(v), _ptr(gate_x), _ptr(A_log),
+                                          _ptr(dt_bias), lb, _ptr(beta), _ptr(state), _ptr(o), B,
+                                          H, HV, K, V, float(scale), _DTYPE[dt],
+                                          _flags(qk_l2norm, beta_sigmoid), ctypes.c_void_p(stream))
+    _check(rc)
+    return o

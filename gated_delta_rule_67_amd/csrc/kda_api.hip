@@ -10,10 +10,10 @@ namespace kda {
 template <typename Tin>
 hipError_t launch_decode(const void*, const void*, const void*, const void*, const void*, float*,
                          void*, int, int, int, int, int, float, unsigned, const int*, int,
-                         hipStream_t);
+                         const float*, const float*, float, hipStream_t);
 hipError_t launch_prefill(const void*, const void*, const void*, const void*, const void*,
                           const float*, float*, void*, int, int, int, int, int, int, float, bool,
-                          void*, unsigned, hipStream_t);
+                          void*, unsigned, const float*, const float*, float, hipStream_t);
 size_t wy_workspace_bytes(int B, int T, int HV, int K);
 size_t bwd_workspace_bytes(int B, int T, int H, int HV, int K, int V, unsigned flags);
 size_t bwd_varlen_workspace_bytes(int nseq, int T, int H, int HV, int K, int V, unsigned flags);
@@ -100,13 +100,14 @@ size_t kda_chunk_fwd_workspace_size(int B, int T, int H, int HV, int K, int V, i
   return kda::wy_workspace_bytes(B, T, HV, K);
 }
 
-int kda_chunk_fwd_ex(const void* q, const void* k, const void* v, const void* g,
-                     const void* beta, const float* initial_state, float* final_state, void* o,
-                     int B, int T, int H, int HV, int K, int V, float scale, int chunk_size,
-                     int dtype, void* workspace, size_t workspace_bytes, unsigned flags,
-                     void* stream) {
+static int chunk_fwd(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                     const float* initial_state, float* final_state, void* o, int B, int T, int H,
+                     int HV, int K, int V, float scale, int chunk_size, int dtype, void* workspace,
+                     size_t workspace_bytes, unsigned flags, const float* A_log,
+                     const float* dt_bias, float gate_lb, void* stream) {
   if (!q || !k || !v || !g || !beta || !o) return KDA_ERR_INVALID;
-  if (flags & ~(unsigned)(KDA_FLAG_QK_L2NORM | KDA_FLAG_BETA_SIGMOID)) return KDA_ERR_INVALID;
+  if (flags & ~(unsigned)(KDA_FLAG_QK_L2NORM | KDA_FLAG_BETA_SIGMOID | kda::kFlagGate))
+    return KDA_ERR_INVALID;
   if (!positive(T)) return KDA_ERR_INVALID;
   if (chunk_size != 8 && chunk_size != 16 && chunk_size != 32 && chunk_size != 64 &&
       chunk_size != 128)
@@ -121,14 +122,49 @@ int kda_chunk_fwd_ex(const void* q, const void* k, const void* v, const void* g,
   const size_t need = kda_chunk_fwd_workspace_size(B, T, H, HV, K, V, chunk_size, dtype);
   if (workspace && workspace_bytes < need) return KDA_ERR_INVALID;
   if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0) return KDA_ERR_INVALID;
-  // The input transforms are applied by the factors kernel of the two-kernel path only.
+  // The input transforms and the gate are applied by the factors kernel of the two-kernel
+  // path only.
   if (flags && (need == 0 || !workspace)) return KDA_ERR_UNSUPPORTED;
   const hipError_t e = kda::launch_prefill(q, k, v, g, beta, initial_state, final_state, o, B, T,
                                            H, HV, K, V, scale, dtype == KDA_DTYPE_BF16,
-                                           need ? workspace : nullptr, flags,
-                                           static_cast<hipStream_t>(stream));
+                                           need ? workspace : nullptr, flags, A_log, dt_bias,
+                                           gate_lb, static_cast<hipStream_t>(stream));
   if (e == hipErrorNotSupported) return KDA_ERR_UNSUPPORTED;  // flags, unaligned tensors
   return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+int kda_chunk_fwd_ex(const void* q, const void* k, const void* v, const void* g,
+                     const void* beta, const float* initial_state, float* final_state, void* o,
+                     int B, int T, int H, int HV, int K, int V, float scale, int chunk_size,
+                     int dtype, void* workspace, size_t workspace_bytes, unsigned flags,
+                     void* stream) {
+  if (flags & ~(unsigned)(KDA_FLAG_QK_L2NORM | KDA_FLAG_BETA_SIGMOID)) return KDA_ERR_INVALID;
+  return chunk_fwd(q, k, v, g, beta, initial_state, final_state, o, B, T, H, HV, K, V, scale,
+                   chunk_size, dtype, workspace, workspace_bytes, flags, nullptr, nullptr, 0.f,
+                   stream);
+}
+
+// The gate's own parameters: A_log required, dt_bias optional and 16-byte aligned, the bound
+// -inf or finite <= 0.
+static int check_gate_params(const float* A_log, const float* dt_bias, float lower_bound) {
+  if (!A_log) return KDA_ERR_INVALID;
+  if (isnan(lower_bound) || lower_bound > 0.f) return KDA_ERR_INVALID;
+  if (!aligned16(dt_bias)) return KDA_ERR_UNSUPPORTED;
+  return KDA_OK;
+}
+
+int kda_chunk_fwd_gated(const void* q, const void* k, const void* v, const void* gate_x,
+                        const float* A_log, const float* dt_bias, float lower_bound,
+                        const void* beta, const float* initial_state, float* final_state,
+                        void* o, int B, int T, int H, int HV, int K, int V, float scale,
+                        int chunk_size, int dtype, void* workspace, size_t workspace_bytes,
+                        unsigned flags, void* stream) {
+  if (flags & ~(unsigned)(KDA_FLAG_QK_L2NORM | KDA_FLAG_BETA_SIGMOID)) return KDA_ERR_INVALID;
+  const int rc = check_gate_params(A_log, dt_bias, lower_bound);
+  if (rc != KDA_OK) return rc;
+  return chunk_fwd(q, k, v, gate_x, beta, initial_state, final_state, o, B, T, H, HV, K, V, scale,
+                   chunk_size, dtype, workspace, workspace_bytes, flags | kda::kFlagGate, A_log,
+                   dt_bias, lower_bound, stream);
 }
 
 // Packed sequences take the two-kernel path only: bf16, K % 8 == 0, V % 8 == 0.
@@ -302,9 +338,11 @@ int kda_gate_bwd(const void* x, const float* A_log, const float* dt_bias, const 
 static int recurrent_step(const void* q, const void* k, const void* v, const void* g,
                           const void* beta, float* state, const int* slots, int nslots, void* o,
                           int B, int H, int HV, int K, int V, float scale, int dtype,
-                          unsigned flags, void* stream) {
+                          unsigned flags, const float* A_log, const float* dt_bias, float gate_lb,
+                          void* stream) {
   if (!q || !k || !v || !g || !beta || !state || !o) return KDA_ERR_INVALID;
-  if (flags & ~(unsigned)(KDA_FLAG_QK_L2NORM | KDA_FLAG_BETA_SIGMOID)) return KDA_ERR_INVALID;
+  if (flags & ~(unsigned)(KDA_FLAG_QK_L2NORM | KDA_FLAG_BETA_SIGMOID | kda::kFlagGate))
+    return KDA_ERR_INVALID;
   const int rc = check_common(B, H, HV, K, V, scale, dtype);
   if (rc != KDA_OK) return rc;
   if (V % 4 != 0) return KDA_ERR_UNSUPPORTED;
@@ -313,17 +351,31 @@ static int recurrent_step(const void* q, const void* k, const void* v, const voi
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const hipError_t e = dtype == KDA_DTYPE_BF16
                            ? kda::launch_decode<kda::bf16>(q, k, v, g, beta, state, o, B, H, HV,
-                                                           K, V, scale, flags, slots, nslots, s)
+                                                           K, V, scale, flags, slots, nslots,
+                                                           A_log, dt_bias, gate_lb, s)
                            : kda::launch_decode<float>(q, k, v, g, beta, state, o, B, H, HV, K,
-                                                       V, scale, flags, slots, nslots, s);
+                                                       V, scale, flags, slots, nslots, A_log,
+                                                       dt_bias, gate_lb, s);
   return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
 int kda_recurrent_step_ex(const void* q, const void* k, const void* v, const void* g,
                           const void* beta, float* state, void* o, int B, int H, int HV, int K,
                           int V, float scale, int dtype, unsigned flags, void* stream) {
+  if (flags & ~(unsigned)(KDA_FLAG_QK_L2NORM | KDA_FLAG_BETA_SIGMOID)) return KDA_ERR_INVALID;
   return recurrent_step(q, k, v, g, beta, state, nullptr, 0, o, B, H, HV, K, V, scale, dtype,
-                        flags, stream);
+                        flags, nullptr, nullptr, 0.f, stream);
+}
+
+int kda_recurrent_step_gated(const void* q, const void* k, const void* v, const void* gate_x,
+                             const float* A_log, const float* dt_bias, float lower_bound,
+                             const void* beta, float* state, void* o, int B, int H, int HV, int K,
+                             int V, float scale, int dtype, unsigned flags, void* stream) {
+  if (flags & ~(unsigned)(KDA_FLAG_QK_L2NORM | KDA_FLAG_BETA_SIGMOID)) return KDA_ERR_INVALID;
+  const int rc = check_gate_params(A_log, dt_bias, lower_bound);
+  if (rc != KDA_OK) return rc;
+  return recurrent_step(q, k, v, gate_x, beta, state, nullptr, 0, o, B, H, HV, K, V, scale, dtype,
+                        flags | kda::kFlagGate, A_log, dt_bias, lower_bound, stream);
 }
 
 int kda_recurrent_step_slots(const void* q, const void* k, const void* v, const void* g,
@@ -331,8 +383,9 @@ int kda_recurrent_step_slots(const void* q, const void* k, const void* v, const 
                              int num_slots, void* o, int B, int H, int HV, int K, int V,
                              float scale, int dtype, unsigned flags, void* stream) {
   if (!slots || num_slots < 1) return KDA_ERR_INVALID;
+  if (flags & ~(unsigned)(KDA_FLAG_QK_L2NORM | KDA_FLAG_BETA_SIGMOID)) return KDA_ERR_INVALID;
   return recurrent_step(q, k, v, g, beta, state_pool, slots, num_slots, o, B, H, HV, K, V, scale,
-                        dtype, flags, stream);
+                        dtype, flags, nullptr, nullptr, 0.f, stream);
 }
 
 int kda_recurrent_step(const void* q, const void* k, const void* v, const void* g,

@@ -167,8 +167,10 @@ struct LdsA {
 // gridDim.x (the next item's q, k, g are loaded while the current one finishes). Wave w owns
 // the 16-token block w; lane (lr, lq) holds token 16w + lr and, for k step s, channels
 // 32s + 8lq..+7. L2N: q and k are L2-normalised here (an instantiation of its own, so the
-// plain path keeps its register budget: two workgroups per CU).
-template <int KT, bool L2N, bool VARLEN>
+// plain path keeps its register budget: two workgroups per CU). GATE: the g input holds the
+// gate's input x, and the decay gate (gate_value, rounded to bf16 as the standalone gate
+// stores it) turns it into g before anything else reads it.
+template <int KT, bool L2N, bool VARLEN, bool GATE = false>
 __global__ __launch_bounds__(256) void factors_kernel(WyArgs a) {
   using L = LdsA<KT>;
   using W = Blk<KT>;
@@ -249,6 +251,30 @@ __global__ __launch_bounds__(256) void factors_kernel(WyArgs a) {
     if (VARLEN && a.ctab[it % a.NC].y == 0) {  // past the packed list's last chunk: no block
       if (it + (int)gridDim.x < items) prefetch(it + gridDim.x);
       continue;
+    }
+    if constexpr (GATE) {
+      // rows past the chunk's last token stay zero tokens (g = 0), channels >= K stay zero
+      int ghv, gnrow;
+      size_t grow0;
+      item_rows(it, ghv, grow0, gnrow);
+      const float na = -expf(p.A_log[ghv]);
+      const float* brow = p.dt_bias ? p.dt_bias + (size_t)ghv * K : nullptr;
+#pragma unroll
+      for (int s = 0; s < NKS; ++s) {
+        const int c = 32 * s + 8 * lq;
+        if (c < K && i_row < gnrow) {
+          f32x4 b0 = {0.f, 0.f, 0.f, 0.f}, b1 = {0.f, 0.f, 0.f, 0.f};
+          if (brow) {
+            b0 = *reinterpret_cast<const f32x4*>(brow + c);
+            b1 = *reinterpret_cast<const f32x4*>(brow + c + 4);
+          }
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            rg[s][e] = from_f32<bf16>(gate_value(to_f32(rg[s][e]), e < 4 ? b0[e] : b1[e - 4], na, p.gate_lb));
+        } else {
+          rg[s] = bf16x8{};
+        }
+      }
     }
 
     // ---------------- in-block cumsum of g (log2 units): d = G_i - G_first, DPP row scan
@@ -841,7 +867,12 @@ hipError_t launch_cfg(const WyArgs& a, int cus, hipStream_t stream) {
   const int items = a.ctab ? a.p.HV * a.NC : a.p.B * a.p.HV * a.NT;
   const int grid_a = items < 2 * cus ? items : 2 * cus;
   const bool l2 = a.p.flags & kFlagQkL2norm, vl = a.ctab != nullptr;
-  if (l2 && vl)
+  const bool gt = a.p.flags & kFlagGate;  // fixed-length sequences only (the C ABI's check)
+  if (gt && l2)
+    hipLaunchKernelGGL((factors_kernel<KT, true, false, true>), dim3(grid_a), dim3(256), 0, stream, a);
+  else if (gt)
+    hipLaunchKernelGGL((factors_kernel<KT, false, false, true>), dim3(grid_a), dim3(256), 0, stream, a);
+  else if (l2 && vl)
     hipLaunchKernelGGL((factors_kernel<KT, true, true>), dim3(grid_a), dim3(256), 0, stream, a);
   else if (l2)
     hipLaunchKernelGGL((factors_kernel<KT, true, false>), dim3(grid_a), dim3(256), 0, stream, a);

@@ -26,12 +26,21 @@ constexpr int kDecodeMaxRows = 16;  // K <= 128 with >= 8 row groups per workgro
 
 // SLOTS: the state of row b is slot slots[b] of a [nslots, HV, K, V] pool (a serving cache);
 // a row whose slot is outside [0, nslots) writes zeros to o and leaves the pool alone.
-template <typename Tin, int VSPLIT, bool SLOTS>
+// The decay gate's parameters for GATE instantiations (g then holds the gate input).
+struct DecodeGate {
+  const float* A_log;
+  const float* dt_bias;
+  float lower_bound;
+};
+
+// GATE: g holds the gate's input; the decay gate (gate_value, rounded to the input type as
+// the standalone gate stores it) turns it into g.
+template <typename Tin, int VSPLIT, bool SLOTS, bool GATE>
 __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(
     const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
     const Tin* __restrict__ g, const Tin* __restrict__ beta, float* __restrict__ state,
     Tin* __restrict__ o, int H, int HV, int K, int V, float scale, unsigned flags,
-    const int* __restrict__ slots, int nslots) {
+    const int* __restrict__ slots, int nslots, DecodeGate gate) {
   __shared__ float s_dec[128], s_k[128], s_q[128], s_v[128], s_u[128];
   __shared__ f32x4 s_pa[kDecodeThreads], s_pb[kDecodeThreads];
   __shared__ float s_qk, s_iq, s_ik;  // q.k (raw), scale/|q|, 1/|k| (norms only when asked)
@@ -70,6 +79,11 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(
   const Tin xg = g[g_off + tk], xk = k[qk_off + tk], xq = q[qk_off + tk];
   const Tin xv = v[(size_t)bh * V + v0 + tv];
   const Tin xb = beta[bh];
+  float gbias = 0.f, gna = 0.f;  // the lane channel's dt_bias and -exp(A_log[hv])
+  if constexpr (GATE) {
+    gbias = gate.dt_bias ? gate.dt_bias[(size_t)hv * K + tk] : 0.f;
+    gna = -expf(gate.A_log[hv]);
+  }
 
   // Then the whole slab: it is the critical resource.
   f32x4 s[kDecodeMaxRows];
@@ -83,7 +97,9 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(
   }
 
   if (t < K) {
-    s_dec[t] = fast_exp2(to_f32(xg) * kLog2e);
+    float gl = to_f32(xg);
+    if constexpr (GATE) gl = to_f32(from_f32<Tin>(gate_value(gl, gbias, gna, gate.lower_bound)));
+    s_dec[t] = fast_exp2(gl * kLog2e);
     s_k[t] = to_f32(xk);
     s_q[t] = to_f32(xq);
   }
@@ -159,6 +175,7 @@ template <typename Tin>
 hipError_t launch_decode(const void* q, const void* k, const void* v, const void* g,
                          const void* beta, float* state, void* o, int B, int H, int HV,
                          int K, int V, float scale, unsigned flags, const int* slots, int nslots,
+                         const float* A_log, const float* dt_bias, float gate_lb,
                          hipStream_t stream) {
   const Tin* q_ = static_cast<const Tin*>(q);
   const Tin* k_ = static_cast<const Tin*>(k);
@@ -170,29 +187,29 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, const void
   // Split V in two when that keeps >= 4 workgroups per CU-slot worth of work.
   const bool split = V % 8 == 0 && heads < 8192;
   const dim3 grid(split ? heads * 2 : heads), block(kDecodeThreads);
-  if (slots) {
-    if (split)
-      hipLaunchKernelGGL((decode_step_kernel<Tin, 2, true>), grid, block, 0, stream, q_, k_, v_, g_,
-                         b_, state, o_, H, HV, K, V, scale, flags, slots, nslots);
-    else
-      hipLaunchKernelGGL((decode_step_kernel<Tin, 1, true>), grid, block, 0, stream, q_, k_, v_, g_,
-                         b_, state, o_, H, HV, K, V, scale, flags, slots, nslots);
+  const DecodeGate gate{A_log, dt_bias, gate_lb};
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, grid, block, 0, stream, q_, k_, v_, g_, b_, state, o_, H, HV, K, V,
+                       scale, flags, slots, nslots, gate);
+  };
+  const bool gt = flags & kFlagGate;
+  if (gt) {
+    if (slots) split ? go(decode_step_kernel<Tin, 2, true, true>) : go(decode_step_kernel<Tin, 1, true, true>);
+    else split ? go(decode_step_kernel<Tin, 2, false, true>) : go(decode_step_kernel<Tin, 1, false, true>);
   } else {
-    if (split)
-      hipLaunchKernelGGL((decode_step_kernel<Tin, 2, false>), grid, block, 0, stream, q_, k_, v_, g_,
-                         b_, state, o_, H, HV, K, V, scale, flags, slots, nslots);
-    else
-      hipLaunchKernelGGL((decode_step_kernel<Tin, 1, false>), grid, block, 0, stream, q_, k_, v_, g_,
-                         b_, state, o_, H, HV, K, V, scale, flags, slots, nslots);
+    if (slots) split ? go(decode_step_kernel<Tin, 2, true, false>) : go(decode_step_kernel<Tin, 1, true, false>);
+    else split ? go(decode_step_kernel<Tin, 2, false, false>) : go(decode_step_kernel<Tin, 1, false, false>);
   }
   return hipGetLastError();
 }
 
 template hipError_t launch_decode<float>(const void*, const void*, const void*, const void*,
                                          const void*, float*, void*, int, int, int, int, int,
-                                         float, unsigned, const int*, int, hipStream_t);
+                                         float, unsigned, const int*, int, const float*,
+                                         const float*, float, hipStream_t);
 template hipError_t launch_decode<bf16>(const void*, const void*, const void*, const void*,
                                         const void*, float*, void*, int, int, int, int, int,
-                                        float, unsigned, const int*, int, hipStream_t);
+                                        float, unsigned, const int*, int, const float*,
+                                        const float*, float, hipStream_t);
 
 }  // namespace kda

@@ -43,6 +43,46 @@ constexpr float kL2normEps = 1e-6f;
 
 __device__ __forceinline__ float sigmoid_f32(float x) { return 1.f / (1.f + fast_exp2(-x * kLog2e)); }
 
+// ---- The KDA decay gate (K3 README, roadmap row L5; key-constraints table, exp-underflow row):
+// g = max(lower_bound, -exp(A_log) * softplus(x + dt_bias)). One definition serves the
+// standalone gate kernels and the kernels that apply the gate to their g input, with FP
+// contraction off so that every caller rounds identically (a fused gate then equals the
+// standalone gate followed by the operator, bit for bit).
+constexpr unsigned kFlagGate = 4u;  // internal: g holds the gate input (gated entry points)
+constexpr float kLn2 = 0.6931471805599453f;
+
+// log(1 + e) for e in [0, 1] on the transcendental unit, with Goldberg's correction
+// log1p(e) = log(u) * e / (u - 1), u = fl(1 + e): it cancels the rounding of 1 + e, so the
+// result keeps a few-ulp relative accuracy however small e is (u == 1: log1p(e) = e).
+__device__ __forceinline__ float log1p_unit(float e) {
+#pragma clang fp contract(off)
+  const float u = 1.f + e;
+  const float d = u - 1.f;
+  return d == 0.f ? e : __builtin_amdgcn_logf(u) * kLn2 * (e * __builtin_amdgcn_rcpf(d));
+}
+
+// softplus(z) = max(z, 0) + log1p(e^-|z|); relative error ~1e-6 for z > -87, where e^z
+// leaves the float32 normal range (below it the result flushes to 0, an absolute error
+// under 1e-37). Also returns e = e^-|z|, which the logistic reuses.
+__device__ __forceinline__ float softplus_f32(float z, float& e) {
+#pragma clang fp contract(off)
+  e = fast_exp2(-fabsf(z) * kLog2e);
+  return fmaxf(z, 0.f) + log1p_unit(e);
+}
+
+// logistic(z) from e = e^-|z|.
+__device__ __forceinline__ float logistic_from(float z, float e) {
+  const float r = __builtin_amdgcn_rcpf(1.f + e);
+  return z >= 0.f ? r : e * r;
+}
+
+// The gate's value for input x, channel bias and neg_rate = -exp(A_log).
+__device__ __forceinline__ float gate_value(float x, float bias, float neg_rate, float lower_bound) {
+#pragma clang fp contract(off)
+  float e;
+  return fmaxf(neg_rate * softplus_f32(x + bias, e), lower_bound);
+}
+
 // Arguments of one chunked-prefill launch (validated by the C ABI).
 struct PrefillArgs {
   const void* q;
@@ -57,6 +97,10 @@ struct PrefillArgs {
   float scale;
   int vec_qkg, vec_v;
   unsigned flags;  // kFlag* input transforms (two-kernel bf16 path only)
+  // kFlagGate: g is the gate input x; A_log [HV], dt_bias [HV, K] (or null), bound
+  const float* A_log;
+  const float* dt_bias;
+  float gate_lb;
 };
 
 }  // namespace kda

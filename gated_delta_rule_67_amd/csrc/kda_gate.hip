@@ -35,31 +35,7 @@ template <typename T> struct Vec;
 template <> struct Vec<bf16> { static constexpr int n = 8; typedef bf16x8 type; };
 template <> struct Vec<float> { static constexpr int n = 4; typedef f32x4 type; };
 
-constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kRows = 4;  // rows whose loads a thread issues before computing any of them
-
-// log(1 + e) for e in [0, 1] on the transcendental unit, with Goldberg's correction
-// log1p(e) = log(u) * e / (u - 1), u = fl(1 + e): it cancels the rounding of 1 + e, so the
-// result keeps a few-ulp relative accuracy however small e is (u == 1: log1p(e) = e).
-__device__ __forceinline__ float log1p_unit(float e) {
-  const float u = 1.f + e;
-  const float d = u - 1.f;
-  return d == 0.f ? e : __builtin_amdgcn_logf(u) * kLn2 * (e * __builtin_amdgcn_rcpf(d));
-}
-
-// softplus(z) = max(z, 0) + log1p(e^-|z|); relative error ~1e-6 for z > -87, where e^z
-// leaves the float32 normal range (below it the result flushes to 0, an absolute error
-// under 1e-37). Also returns e = e^-|z| for the logistic.
-__device__ __forceinline__ float softplus_f32(float z, float& e) {
-  e = fast_exp2(-fabsf(z) * kLog2e);
-  return fmaxf(z, 0.f) + log1p_unit(e);
-}
-
-// logistic(z) from e = e^-|z|.
-__device__ __forceinline__ float logistic_from(float z, float e) {
-  const float r = __builtin_amdgcn_rcpf(1.f + e);
-  return z >= 0.f ? r : e * r;
-}
 
 struct Grid {
   int ncv;      // column vectors per row (HV*K / VEC)
@@ -108,9 +84,7 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(const T* __restrict__ x,
     vec_t gv;
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
-      float ez;
-      const float s = na * softplus_f32(to_f32(xv[e]) + bias[e], ez);
-      gv[e] = from_f32<T>(fmaxf(s, lower_bound));
+      gv[e] = from_f32<T>(gate_value(to_f32(xv[e]), bias[e], na, lower_bound));
     }
     *out = gv;  // cached: a prefill that consumes g may find it in the last-level cache
   };

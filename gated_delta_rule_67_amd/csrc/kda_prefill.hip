@@ -477,8 +477,10 @@ hipError_t launch_prefill_wy(const PrefillArgs& a, void* workspace, hipStream_t 
 hipError_t launch_prefill(const void* q, const void* k, const void* v, const void* g,
                           const void* beta, const float* s0, float* sT, void* o, int B, int T,
                           int H, int HV, int K, int V, float scale, bool bf16_inputs,
-                          void* workspace, unsigned flags, hipStream_t stream) {
-  PrefillArgs a{q, k, v, g, beta, s0, sT, o, B, T, H, HV, K, V, scale, 0, 0, flags};
+                          void* workspace, unsigned flags, const float* A_log,
+                          const float* dt_bias, float gate_lb, hipStream_t stream) {
+  PrefillArgs a{q, k, v, g, beta, s0, sT, o, B, T, H, HV, K, V, scale, 0, 0, flags,
+                A_log, dt_bias, gate_lb};
   const int vw = bf16_inputs ? 8 : 4;
   a.vec_qkg = (K % vw == 0) && aligned16(q) && aligned16(k) && aligned16(g);
   a.vec_v = (V % vw == 0) && aligned16(v);

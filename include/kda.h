@@ -315,6 +315,39 @@ int kda_gate_bwd(const void* x, const float* A_log, const float* dt_bias, const 
                  float lower_bound, int dtype, void* workspace, size_t workspace_bytes,
                  void* stream);
 
+/*
+ * kda_chunk_fwd_ex with the decay gate applied inside the operator (the gate of
+ * kda_gate_fwd; K3 README, roadmap row L5: gate fusion): gate_x [B, T, HV, K] (dtype) holds
+ * the gate's input in place of g, and the kernels turn it into g = max(lower_bound,
+ * -exp(A_log[hv]) * softplus(x + dt_bias[hv, c])), rounded to dtype exactly as
+ * kda_gate_fwd stores it, before any other step. The result equals kda_gate_fwd followed by
+ * kda_chunk_fwd_ex bit for bit, without writing g to memory and reading it back.
+ *
+ *   A_log, dt_bias, lower_bound   as for kda_gate_fwd (dt_bias may be NULL; when given it
+ *                                 must be 16-byte aligned, else KDA_ERR_UNSUPPORTED)
+ *   everything else               as for kda_chunk_fwd_ex (flags: the input transforms)
+ *
+ * Needs the two-kernel path (bf16, K % 8 == 0, V % 8 == 0, 16-byte aligned q, k, gate_x, v,
+ * a workspace of kda_chunk_fwd_workspace_size() bytes); elsewhere KDA_ERR_UNSUPPORTED.
+ */
+int kda_chunk_fwd_gated(const void* q, const void* k, const void* v, const void* gate_x,
+                        const float* A_log, const float* dt_bias, float lower_bound,
+                        const void* beta, const float* initial_state, float* final_state,
+                        void* o, int B, int T, int H, int HV, int K, int V, float scale,
+                        int chunk_size, int dtype, void* workspace, size_t workspace_bytes,
+                        unsigned flags, void* stream);
+
+/*
+ * kda_recurrent_step_ex with the decay gate applied inside the step: gate_x [B, HV, K]
+ * (dtype) in place of g, turned into g as kda_chunk_fwd_gated does (rounded to dtype as
+ * kda_gate_fwd stores it). Equals kda_gate_fwd followed by kda_recurrent_step_ex bit for bit.
+ * A_log, dt_bias, lower_bound as for kda_chunk_fwd_gated; the rest as kda_recurrent_step_ex.
+ */
+int kda_recurrent_step_gated(const void* q, const void* k, const void* v, const void* gate_x,
+                             const float* A_log, const float* dt_bias, float lower_bound,
+                             const void* beta, float* state, void* o, int B, int H, int HV, int K,
+                             int V, float scale, int dtype, unsigned flags, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

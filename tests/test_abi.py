@@ -355,3 +355,56 @@ def test_gate_bwd_workspace_size(lib):
 def test_gate_empty_input_accepts_null_token_tensors(lib):
     assert _gate(lib, False, B=0, x=None, g=None) == kda.KDA_OK
     assert _gate(lib, False, B=0, A_log=None) == kda.KDA_ERR_INVALID
+
+
+def _gated_chunk(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, x=FAKE, A_log=FAKE, dt_bias=None, lb=-5.0, beta=FAKE,
+             s0=None, sT=None, o=FAKE, B=2, T=128, H=2, HV=4, K=64, V=64, scale=0.125, chunk=64,
+             dtype=1, ws=FAKE, ws_bytes=1 << 30, flags=0)
+    a.update(kw)
+    return lib.kda_chunk_fwd_gated(a["q"], a["k"], a["v"], a["x"], a["A_log"], a["dt_bias"],
+                                   a["lb"], a["beta"], a["s0"], a["sT"], a["o"], a["B"], a["T"],
+                                   a["H"], a["HV"], a["K"], a["V"], a["scale"], a["chunk"],
+                                   a["dtype"], a["ws"], a["ws_bytes"], a["flags"], None)
+
+
+def _gated_step(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, x=FAKE, A_log=FAKE, dt_bias=None, lb=-5.0, beta=FAKE,
+             state=FAKE, o=FAKE, B=2, H=2, HV=4, K=64, V=64, scale=0.125, dtype=1, flags=0)
+    a.update(kw)
+    return lib.kda_recurrent_step_gated(a["q"], a["k"], a["v"], a["x"], a["A_log"], a["dt_bias"],
+                                        a["lb"], a["beta"], a["state"], a["o"], a["B"], a["H"],
+                                        a["HV"], a["K"], a["V"], a["scale"], a["dtype"],
+                                        a["flags"], None)
+
+
+@pytest.mark.parametrize("call", [_gated_chunk, _gated_step])
+@pytest.mark.parametrize("bad,rc", [
+    (dict(A_log=None), kda.KDA_ERR_INVALID),
+    (dict(x=None), kda.KDA_ERR_INVALID),
+    (dict(lb=float("nan")), kda.KDA_ERR_INVALID),
+    (dict(lb=1.0), kda.KDA_ERR_INVALID),
+    (dict(flags=4), kda.KDA_ERR_INVALID),                       # not a caller flag
+    (dict(dt_bias=ctypes.c_void_p(0x1004)), kda.KDA_ERR_UNSUPPORTED),  # misaligned bias
+    (dict(scale=float("nan")), kda.KDA_ERR_INVALID),
+])
+def test_gated_entry_points_reject_invalid_arguments(lib, call, bad, rc):
+    assert call(lib, **bad) == rc
+
+
+@pytest.mark.parametrize("bad,rc", [
+    (dict(ws=None), kda.KDA_ERR_UNSUPPORTED),      # the gate needs the two-kernel path
+    (dict(dtype=0, K=32, V=32), kda.KDA_ERR_UNSUPPORTED),
+    (dict(K=60), kda.KDA_ERR_UNSUPPORTED),
+    (dict(T=100), kda.KDA_ERR_INVALID),            # T % chunk_size != 0
+])
+def test_gated_chunk_needs_the_two_kernel_path(lib, bad, rc):
+    assert _gated_chunk(lib, **bad) == rc
+
+
+def test_ex_entry_points_reject_the_internal_gate_flag(lib):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, state=FAKE, o=FAKE)
+    assert lib.kda_recurrent_step_ex(a["q"], a["k"], a["v"], a["g"], a["beta"], a["state"],
+                                     a["o"], 2, 2, 4, 64, 64, 0.125, 1, 4, None) == kda.KDA_ERR_INVALID
+    assert lib.kda_chunk_fwd_ex(FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, 2, 128, 2, 4, 64,
+                                64, 0.125, 64, 1, FAKE, 1 << 30, 4, None) == kda.KDA_ERR_INVALID

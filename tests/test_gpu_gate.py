@@ -156,3 +156,83 @@ def test_gate_feeds_the_prefill():
     o_ref, s_ref = recurrent(**ref_in)
     assert_parity(to64(o), o_ref, torch.bfloat16, "o")
     assert_parity(to64(s), s_ref, torch.bfloat16, "state")
+
+
+def _gated_prefill_case(B, T, H, HV, K, V, chunk, seed, lb=-5.0, init=True, l2=False, x_std=1.0,
+                        bias=True):
+    from synth import prefill_inputs
+    from tests.helpers import gpu
+
+    dev = torch.device("cuda")
+    inp = prefill_inputs(B, T, H, HV, K, V, "bf16", init, seed=seed, raw_qk=l2)
+    gd = gate_inputs(B, T, HV, K, "bf16", seed + 1, x_std)
+    d = gpu(inp)
+    x, A = gd["x"].to(dev), gd["A_log"].to(dev)
+    bias_t = gd["dt_bias"].to(dev) if bias else None
+    log(f"gated prefill B={B} T={T} H={H} HV={HV} K={K} V={V} chunk={chunk} lb={lb} l2={l2} seed={seed}")
+    o_f, s_f = kda.kda_chunk_fwd_gated(d["q"], d["k"], d["v"], x, A, bias_t, d["beta"], lb,
+                                       inp["scale"], d["initial_state"], chunk_size=chunk,
+                                       qk_l2norm=l2)
+    g = kda.kda_gate_fwd(x, A, bias_t, lb)
+    o_u, s_u = kda.kda_chunk_fwd(d["q"], d["k"], d["v"], g, d["beta"], inp["scale"],
+                                 d["initial_state"], chunk_size=chunk, qk_l2norm=l2)
+    torch.cuda.synchronize()
+    return inp, gd, (o_f, s_f), (o_u, s_u), g
+
+
+@pytest.mark.parametrize("case", [
+    dict(B=2, T=512, H=4, HV=8, K=64, V=64, chunk=64, seed=30),              # GVA, the pages' fused-test shape
+    dict(B=1, T=208, H=2, HV=2, K=128, V=128, chunk=16, seed=31, x_std=3.0),  # ragged last tile
+    dict(B=2, T=192, H=2, HV=2, K=32, V=48, chunk=32, seed=32, lb=None, init=False),
+    dict(B=1, T=256, H=2, HV=4, K=64, V=64, chunk=64, seed=33, l2=True, bias=False),
+])
+def test_gated_prefill_equals_gate_then_prefill(case):
+    """The fused gate changes nothing but where g is made: bit-identical to kda_gate_fwd
+    followed by kda_chunk_fwd, and within the prefill's bf16 criterion of the oracle."""
+    from oracle import recurrent
+    from tests.helpers import assert_parity
+
+    inp, gd, (o_f, s_f), (o_u, s_u), g = _gated_prefill_case(**case)
+    assert torch.equal(o_f, o_u), "fused o differs from gate + prefill"
+    assert torch.equal(s_f, s_u), "fused state differs from gate + prefill"
+    lb = case.get("lb", -5.0)
+    b64 = to64(gd["dt_bias"]) if case.get("bias", True) else None
+    g_ref = gate(to64(gd["x"]), to64(gd["A_log"]), b64, lb)
+    ref_in = dict(inp, g=torch.from_numpy(g_ref).to(torch.bfloat16))
+    o_ref, s_ref = recurrent(**ref_in, qk_l2norm=case.get("l2", False))
+    assert_parity(to64(o_f), o_ref, torch.bfloat16, "o")
+    assert_parity(to64(s_f), s_ref, torch.bfloat16, "state")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_gated_decode_equals_gate_then_decode(dtype):
+    from oracle import decode_step
+    from synth import decode_inputs
+    from tests.helpers import assert_parity
+
+    dev = torch.device("cuda")
+    steps, B, H, HV, K, V = 3, 8, 2, 4, 128, 128
+    dec = decode_inputs(steps, B, H, HV, K, V, dtype, True, seed=34)
+    gd = gate_inputs(steps, B, HV, K, dtype, 35, 2.0)  # [steps, B, HV, K] gate inputs
+    A, bias_t = gd["A_log"].to(dev), gd["dt_bias"].to(dev)
+    s_f = dec["state"].to(dev).clone()
+    s_u = s_f.clone()
+    s_ref = dec["state"].double().numpy()
+    for t in range(steps):
+        args = [dec[n][t].to(dev) for n in ("q", "k", "v")]
+        x = gd["x"][t].to(dev)
+        beta = dec["beta"][t].to(dev)
+        o_f = kda.kda_recurrent_step_gated(*args, x, A, bias_t, beta, s_f, -5.0, dec["scale"])
+        g = kda.kda_gate_fwd(x.unsqueeze(1), A, bias_t, -5.0)[:, 0]
+        o_u = kda.kda_recurrent_step(*args, g, beta, s_u, dec["scale"])
+        torch.cuda.synchronize()
+        assert torch.equal(o_f, o_u) and torch.equal(s_f, s_u), f"step {t}: fused != gate + step"
+        g_ref = gate(to64(gd["x"][t]), to64(gd["A_log"]), to64(gd["dt_bias"]), -5.0)
+        g_in = torch.from_numpy(g_ref).to(dec["q"].dtype)
+        o_ref, s_ref = decode_step(dec["q"][t], dec["k"][t], dec["v"][t], g_in, dec["beta"][t],
+                                   s_ref, dec["scale"])
+        dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+        if dt == torch.float32:
+            assert np.abs(to64(o_f) - o_ref).max() <= 1e-5
+        else:
+            assert_parity(to64(o_f), o_ref, dt, f"step {t} o")
