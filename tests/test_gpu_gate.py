@@ -236,3 +236,35 @@ def test_gated_decode_equals_gate_then_decode(dtype):
             assert np.abs(to64(o_f) - o_ref).max() <= 1e-5
         else:
             assert_parity(to64(o_f), o_ref, dt, f"step {t} o")
+
+
+def test_training_chain_through_the_gate():
+    """The gate's gradients through the whole operator, as training takes them:
+    kda_gate_fwd -> kda_chunk_bwd (dg) -> kda_gate_bwd, against the oracle's chain
+    (recurrent_bwd's dg for the bf16 g the operator reads, then gate_bwd). bf16 reading of
+    the tolerance, as for the other gradients."""
+    from oracle import recurrent_bwd
+    from synth import prefill_inputs
+    from tests.helpers import assert_parity, gpu
+
+    dev = torch.device("cuda")
+    B, T, H, HV, K, V = 2, 192, 2, 4, 64, 64
+    inp = prefill_inputs(B, T, H, HV, K, V, "bf16", True, seed=40)
+    gd = _off_kink(gate_inputs(B, T, HV, K, "bf16", 41, 2.0), -5.0)
+    do = torch.randn((B, T, HV, V), generator=torch.Generator().manual_seed(42)).to(torch.bfloat16)
+    d = gpu(inp)
+    x, A, bias_t = gd["x"].to(dev), gd["A_log"].to(dev), gd["dt_bias"].to(dev)
+    log(f"gate -> chunk bwd -> gate bwd, B={B} T={T} H={H} HV={HV} K={K} V={V}")
+    g = kda.kda_gate_fwd(x, A, bias_t, -5.0)
+    grads = kda.kda_chunk_bwd(d["q"], d["k"], d["v"], g, d["beta"], do.to(dev), inp["scale"],
+                              d["initial_state"], None, 64)
+    dx, dA, db = kda.kda_gate_bwd(x, A, bias_t, grads[3], -5.0)
+    torch.cuda.synchronize()
+    x64, A64, b64 = to64(gd["x"]), to64(gd["A_log"]), to64(gd["dt_bias"])
+    g_in = torch.from_numpy(gate(x64, A64, b64, -5.0)).to(torch.bfloat16)
+    refs = recurrent_bwd(inp["q"], inp["k"], inp["v"], g_in, inp["beta"], inp["scale"], do,
+                         inp["initial_state"])
+    dx_ref, dA_ref, db_ref = gate_bwd(x64, A64, b64, refs[3], -5.0)
+    assert_parity(to64(dx), dx_ref, torch.bfloat16, "dx")
+    assert_parity(to64(db), db_ref, torch.bfloat16, "ddt_bias")
+    assert_parity(to64(dA)[None], dA_ref[None], torch.bfloat16, "dA_log")
