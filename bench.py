@@ -189,6 +189,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-gate", action="store_true")
+    ap.add_argument("--no-segmented", action="store_true")
     ap.add_argument("--backward-steps", type=int, default=5)
     args = ap.parse_args()
     if args.gpus != 1:
@@ -345,6 +346,36 @@ def main():
                          "algorithmic_bytes_per_launch": bbytes},
         }
         del dout
+
+    # ---------------- few heads, long sequence: the segmented prefill against the plain path
+    if not args.no_segmented:
+        from synth import prefill_inputs
+        result["few_heads"] = []
+        for (fb, ft, fh) in ((1, 32768, 4), (1, 32768, 16)):
+            log(f"bench: few heads B={fb} T={ft} H=HV={fh}")
+            fi = prefill_inputs(fb, ft, fh, fh, 128, 128, "bf16", True, seed=4323)
+            fd = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in fi.items()}
+            del fi
+            segs = kda.library().kda_chunk_fwd_workspace_size(fb, ft, fh, fh, 128, 128, 64, 1)
+            auto = lambda: kda.kda_chunk_fwd(fd["q"], fd["k"], fd["v"], fd["g"], fd["beta"],
+                                             fd["scale"], fd["initial_state"])
+            plain = lambda: kda.kda_chunk_fwd_segmented(fd["q"], fd["k"], fd["v"], fd["g"],
+                                                        fd["beta"], 1, fd["scale"],
+                                                        fd["initial_state"])
+            a_avg, a_med, _ = time_launches(auto, args.steps, args.warmup, torch)
+            p_avg, p_med, _ = time_launches(plain, args.steps, args.warmup, torch)
+            fbytes, _ = prefill_algorithmic(fb, ft, fh, fh, 128, 128, 2, True, True)
+            result["few_heads"].append({
+                "workload": f"KDA chunked prefill B={fb} T={ft} H=HV={fh} K=V=128 bf16, "
+                            "initial state N(0, 0.1)",
+                "default_ms": a_avg, "default_median_ms": a_med,
+                "default_tokens_per_s": fb * ft / (a_avg * 1e-3),
+                "default_roofline_frac": fbytes / (a_avg * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                "plain_two_kernel_ms": p_avg, "plain_two_kernel_median_ms": p_med,
+                "workspace_bytes": segs,
+                "kernel": "kda_chunk_fwd (segmented when few heads) against "
+                          "kda_chunk_fwd_segmented(segments=1)"})
+            del fd
 
     # ---------------- decay gate (forward and backward) on the prefill layer's g shape
     if not args.no_gate:

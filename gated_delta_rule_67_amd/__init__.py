@@ -18,6 +18,8 @@ Entry points (same names as the C ABI):
   the decay gate that produces g, and its backward
 * ``kda_chunk_fwd_gated`` / ``kda_recurrent_step_gated``: the prefill and the decode step
   with that gate applied inside the kernels (the gate's input in place of g)
+* ``kda_chunk_fwd_segmented(q, k, v, g, beta, segments, ...)``: the prefill over segments
+  of each sequence composed by a scan (for few heads)
 
 ``qk_l2norm`` / ``beta_sigmoid`` ask the kernels to L2-normalise q and k and to
 apply the sigmoid to beta (``kda_chunk_fwd_ex`` / ``kda_recurrent_step_ex``).
@@ -32,7 +34,8 @@ import torch
 __all__ = ["kda_chunk_fwd", "kda_chunk_fwd_varlen", "kda_chunk_bwd",
            "kda_chunk_bwd_varlen", "kda_recurrent_step",
            "kda_recurrent_step_slots", "kda_gate_fwd", "kda_gate_bwd",
-           "kda_chunk_fwd_gated", "kda_recurrent_step_gated", "library", "library_path", "status_string",
+           "kda_chunk_fwd_gated", "kda_recurrent_step_gated", "kda_chunk_fwd_segmented",
+           "library", "library_path", "status_string",
            "KDA_OK", "KDA_ERR_INVALID", "KDA_ERR_UNSUPPORTED", "KDA_ERR_HIP",
            "KDA_FLAG_QK_L2NORM", "KDA_FLAG_BETA_SIGMOID"]
 
@@ -95,6 +98,10 @@ def library():
     lib.kda_recurrent_step_gated.argtypes = [vp] * 6 + [f] + [vp] * 3 + [i] * 5 + [f, i,
                                                                                  ctypes.c_uint, vp]
     lib.kda_recurrent_step_gated.restype = i
+    lib.kda_chunk_fwd_segmented.argtypes = [vp] * 8 + [i] * 6 + [f, i, i, vp, sz, ctypes.c_uint, vp]
+    lib.kda_chunk_fwd_segmented.restype = i
+    lib.kda_chunk_fwd_segmented_workspace_size.argtypes = [i] * 8
+    lib.kda_chunk_fwd_segmented_workspace_size.restype = sz
     lib.kda_status_string.argtypes = [i]
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_version.argtypes = []
@@ -505,3 +512,40 @@ def kda_recurrent_step_gated(q, k, v, gate_x, A_log, dt_bias, beta, state, lower
                                           _flags(qk_l2norm, beta_sigmoid), ctypes.c_void_p(stream))
     _check(rc)
     return o
+
+
+def kda_chunk_fwd_segmented(q, k, v, g, beta, segments, scale=None, initial_state=None,
+                            output_final_state=True, qk_l2norm=False, beta_sigmoid=False):
+    """kda_chunk_fwd over `segments` equal segments of each sequence, composed by a scan of the
+    segments' affine state maps (bf16; T % (64 * segments) == 0). kda_chunk_fwd takes this
+    route by itself when it pays; this entry point chooses the segment count explicitly.
+    Returns (o, final_state)."""
+    _require(q.is_cuda, "inputs must be on a GPU")
+    dev, dt = q.device, q.dtype
+    _require(dt in _DTYPE, f"unsupported dtype {dt}")
+    B, T, H, K = q.shape
+    HV, V = v.shape[2], v.shape[3]
+    _require(k.shape == q.shape, "k must match q")
+    _require(tuple(v.shape[:2]) == (B, T), "v must be [B, T, HV, V]")
+    _require(tuple(g.shape) == (B, T, HV, K), "g must be [B, T, HV, K]")
+    _require(tuple(beta.shape) == (B, T, HV), "beta must be [B, T, HV]")
+    _check_tensors([("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta)], dt, dev)
+    if initial_state is not None:
+        _require(tuple(initial_state.shape) == (B, HV, K, V), "initial_state must be [B, HV, K, V]")
+        _check_tensors([("initial_state", initial_state)], torch.float32, dev)
+    if scale is None:
+        scale = 1.0 / math.sqrt(K)
+    lib = library()
+    o = torch.empty((B, T, HV, V), dtype=dt, device=dev)
+    final = torch.empty((B, HV, K, V), dtype=torch.float32, device=dev) if output_final_state else None
+    ws_bytes = lib.kda_chunk_fwd_segmented_workspace_size(B, T, H, HV, K, V, int(segments), _DTYPE[dt])
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        rc = lib.kda_chunk_fwd_segmented(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                         _ptr(initial_state), _ptr(final), _ptr(o), B, T, H, HV,
+                                         K, V, float(scale), int(segments), _DTYPE[dt], _ptr(ws),
+                                         ws_bytes, _flags(qk_l2norm, beta_sigmoid),
+                                         ctypes.c_void_p(stream))
+    _check(rc)
+    return o, final

@@ -18,6 +18,12 @@ size_t wy_workspace_bytes(int B, int T, int HV, int K);
 size_t bwd_workspace_bytes(int B, int T, int H, int HV, int K, int V, unsigned flags);
 size_t bwd_varlen_workspace_bytes(int nseq, int T, int H, int HV, int K, int V, unsigned flags);
 size_t wy_varlen_workspace_bytes(int nseq, int T, int HV, int K);
+size_t wy_segmented_workspace_bytes(int B, int T, int HV, int K, int V, int P);
+int wy_segments(int B, int T, int HV, int V, int cus);
+int device_cu_count();
+hipError_t launch_prefill_wy(const PrefillArgs& p, void* workspace, hipStream_t stream);
+hipError_t launch_prefill_wy_segmented(const PrefillArgs& p, int P, void* workspace,
+                                       hipStream_t stream);
 hipError_t launch_prefill_wy_varlen(const PrefillArgs& p, const int* cu_seqlens, void* workspace,
                                     hipStream_t stream);
 hipError_t launch_chunk_bwd(const void*, const void*, const void*, const void*, const void*,
@@ -97,7 +103,43 @@ size_t kda_chunk_fwd_workspace_size(int B, int T, int H, int HV, int K, int V, i
   if (chunk_size < 1 || !positive(T)) return 0;
   if (check_common(B, H, HV, K, V, 1.f, dtype) != KDA_OK) return 0;
   if (dtype != KDA_DTYPE_BF16 || K % 8 != 0 || V % 8 != 0) return 0;
-  return kda::wy_workspace_bytes(B, T, HV, K);
+  // with few heads the call runs over segments of the sequence (kda_chunk_fwd_segmented)
+  const int P = kda::wy_segments(B, T, HV, V, kda::device_cu_count());
+  return P > 1 ? kda::wy_segmented_workspace_bytes(B, T, HV, K, V, P)
+               : kda::wy_workspace_bytes(B, T, HV, K);
+}
+
+size_t kda_chunk_fwd_segmented_workspace_size(int B, int T, int H, int HV, int K, int V,
+                                              int segments, int dtype) {
+  if (segments < 1 || !positive(T) || T % (64 * segments) != 0) return 0;
+  if (check_common(B, H, HV, K, V, 1.f, dtype) != KDA_OK) return 0;
+  if (dtype != KDA_DTYPE_BF16 || K % 8 != 0 || V % 8 != 0) return 0;
+  return segments > 1 ? kda::wy_segmented_workspace_bytes(B, T, HV, K, V, segments)
+                      : kda::wy_workspace_bytes(B, T, HV, K);
+}
+
+int kda_chunk_fwd_segmented(const void* q, const void* k, const void* v, const void* g,
+                            const void* beta, const float* initial_state, float* final_state,
+                            void* o, int B, int T, int H, int HV, int K, int V, float scale,
+                            int segments, int dtype, void* workspace, size_t workspace_bytes,
+                            unsigned flags, void* stream) {
+  if (!q || !k || !v || !g || !beta || !o) return KDA_ERR_INVALID;
+  if (flags & ~(unsigned)(KDA_FLAG_QK_L2NORM | KDA_FLAG_BETA_SIGMOID)) return KDA_ERR_INVALID;
+  if (!positive(T) || segments < 1 || T % (64 * segments) != 0) return KDA_ERR_INVALID;
+  const int rc = check_common(B, H, HV, K, V, scale, dtype);
+  if (rc != KDA_OK) return rc;
+  if (dtype != KDA_DTYPE_BF16 || K % 8 != 0 || V % 8 != 0) return KDA_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(g) || !aligned16(v)) return KDA_ERR_UNSUPPORTED;
+  if ((int64_t)B * segments * HV * ((T / segments + 63) / 64) > INT32_MAX) return KDA_ERR_UNSUPPORTED;
+  const size_t need = kda_chunk_fwd_segmented_workspace_size(B, T, H, HV, K, V, segments, dtype);
+  if (!workspace || workspace_bytes < need) return KDA_ERR_INVALID;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0) return KDA_ERR_INVALID;
+  kda::PrefillArgs a{q, k, v, g, beta, initial_state, final_state, o, B, T, H, HV, K, V, scale,
+                     1, 1, flags};
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = segments > 1 ? kda::launch_prefill_wy_segmented(a, segments, workspace, s)
+                                    : kda::launch_prefill_wy(a, workspace, s);
+  return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
 static int chunk_fwd(const void* q, const void* k, const void* v, const void* g, const void* beta,

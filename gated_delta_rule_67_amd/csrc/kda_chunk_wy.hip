@@ -666,7 +666,7 @@ void state_kernel(WyArgs a) {
       n = min(n, NT - 1);
       const int t0 = n * kC, nrow = min(kC, len - t0);
       const auto rv_ = make_rsrc(static_cast<const bf16*>(p.v) + (((size_t)bos + t0) * p.HV + hv) * V,
-                                 (unsigned)nrow * rowb);
+                                 p.v ? (unsigned)nrow * rowb : 0u);  // no v: zeros
 #pragma unroll
       for (int e = 0; e < NPL; ++e)
         rvv[e] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rv_, voff[e], 0, 0));
@@ -830,7 +830,7 @@ void state_kernel(WyArgs a) {
     O[3] = mfma32(fa[5], ub[1], mfma32(fa[4], ub[0], P[3]));
     // stores go out before the state update so they drain under its products
     const auto ro_ = make_rsrc(static_cast<const bf16*>(p.o) + (((size_t)bos + t0) * p.HV + hv) * V,
-                               (unsigned)nrow * rowb);
+                               p.o ? (unsigned)nrow * rowb : 0u);  // no o: stores dropped
 #pragma unroll
     for (int I = 0; I < 4; ++I)
 #pragma unroll
@@ -862,8 +862,8 @@ void state_kernel(WyArgs a) {
   }
 }
 
-template <int KT, int NW>
-hipError_t launch_cfg(const WyArgs& a, int cus, hipStream_t stream) {
+template <int KT>
+hipError_t launch_factors(const WyArgs& a, int cus, hipStream_t stream) {
   const int items = a.ctab ? a.p.HV * a.NC : a.p.B * a.p.HV * a.NT;
   const int grid_a = items < 2 * cus ? items : 2 * cus;
   const bool l2 = a.p.flags & kFlagQkL2norm, vl = a.ctab != nullptr;
@@ -880,8 +880,12 @@ hipError_t launch_cfg(const WyArgs& a, int cus, hipStream_t stream) {
     hipLaunchKernelGGL((factors_kernel<KT, false, true>), dim3(grid_a), dim3(256), 0, stream, a);
   else
     hipLaunchKernelGGL((factors_kernel<KT, false, false>), dim3(grid_a), dim3(256), 0, stream, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  return hipGetLastError();
+}
+
+template <int KT, int NW>
+hipError_t launch_state(const WyArgs& a, hipStream_t stream) {
+  const bool vl = a.ctab != nullptr;
   const int nvt = (a.p.V + 16 * NW - 1) / (16 * NW);
   const dim3 grid(a.p.B * a.p.HV * nvt), block(64 * (NW + kDmaWaves));
   if (vl)
@@ -889,6 +893,70 @@ hipError_t launch_cfg(const WyArgs& a, int cus, hipStream_t stream) {
   else
     hipLaunchKernelGGL((state_kernel<KT, NW, false>), grid, block, 0, stream, a);
   return hipGetLastError();
+}
+
+// Segmented prefill (a chunk scan over the sequence, for few heads): each sequence is cut into
+// P equal segments, which is the same memory viewed as P times the batch. Per segment, the
+// state leaving it is an affine map of the state entering it, S_out = A S_in + Bm (A: K x K).
+// The scan below composes the maps in segment order: S_in[0] = S0, S_in[p+1] = A_p S_in[p] +
+// Bm_p; the last value is the sequence's final state. One workgroup per (b, hv, 16-column tile);
+// the state tile lives in LDS, a thread owns one state row and 8 of the tile's columns.
+__global__ __launch_bounds__(256) void segment_scan_kernel(const float* __restrict__ Am,
+                                                           const float* __restrict__ Bm,
+                                                           const float* s0, float* __restrict__ Sin,
+                                                           float* sT, int P, int HV, int K, int V) {
+  __shared__ float sS[128][17];
+  const int ntile = (V + 15) / 16;
+  const int tile = blockIdx.x % ntile, bh = blockIdx.x / ntile;
+  const int b = bh / HV, hv = bh - b * HV;
+  const int t = threadIdx.x, c = t >> 1, j0 = (t & 1) * 8, col0 = tile * 16;
+  for (int i = t; i < K * 16; i += 256) {
+    const int r = i >> 4, j = i & 15;
+    sS[r][j] = (s0 && col0 + j < V) ? s0[((size_t)bh * K + r) * V + col0 + j] : 0.f;
+  }
+  __syncthreads();
+  for (int p = 0; p < P; ++p) {
+    const size_t seg = (size_t)(b * P + p) * HV + hv;
+    float acc[8];
+    if (c < K) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int col = col0 + j0 + j;
+        if (col < V) Sin[(seg * K + c) * V + col] = sS[c][j0 + j];
+        acc[j] = col < V ? Bm[(seg * K + c) * V + col] : 0.f;
+      }
+      const float* arow = Am + (seg * K + c) * K;
+      for (int k = 0; k < K; k += 4) {
+        const f32x4 a4 = *reinterpret_cast<const f32x4*>(arow + k);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) acc[j] += a4[e] * sS[k + e][j0 + j];
+      }
+    }
+    __syncthreads();
+    if (c < K) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) sS[c][j0 + j] = acc[j];
+    }
+    __syncthreads();
+  }
+  if (sT && c < K) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int col = col0 + j0 + j;
+      if (col < V) sT[((size_t)bh * K + c) * V + col] = sS[c][j0 + j];
+    }
+  }
+}
+
+// n identity matrices of K x K (the state entering each segment when its map A is traced).
+__global__ __launch_bounds__(256) void eye_kernel(float* __restrict__ out, size_t n, int K) {
+  const size_t total = n * K * K;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (size_t)gridDim.x * 256) {
+    const int e = (int)(i % ((size_t)K * K));
+    out[i] = (e / K == e % K) ? 1.f : 0.f;
+  }
 }
 
 }  // namespace wy
@@ -924,16 +992,108 @@ size_t wy_varlen_workspace_bytes(int nseq, int T, int HV, int K) {
 // bf16 inputs, K % 8 == 0, 16-byte aligned q/k/g, and a workspace of wy_workspace_bytes.
 // The state pass runs one workgroup per CU (double-buffered LDS); its V tile is the widest
 // of 16, 32 or 64 columns that still gives every CU a workgroup.
-static hipError_t launch_wy(const wy::WyArgs& a, hipStream_t stream) {
+static hipError_t launch_state_any(const wy::WyArgs& a, int cus, hipStream_t stream) {
   using namespace wy;
   const PrefillArgs& p = a.p;
-  const int cus = device_cu_count();
   const int heads = p.B * p.HV;
   const int nw = p.V <= 16 ? 1 : (p.V <= 32 || heads * ((p.V + 31) / 32) <= cus) ? 2 : 4;
-  if (p.K <= 32) return nw == 1 ? launch_cfg<32, 1>(a, cus, stream) : nw == 2 ? launch_cfg<32, 2>(a, cus, stream) : launch_cfg<32, 4>(a, cus, stream);
-  if (p.K <= 64) return nw == 1 ? launch_cfg<64, 1>(a, cus, stream) : nw == 2 ? launch_cfg<64, 2>(a, cus, stream) : launch_cfg<64, 4>(a, cus, stream);
-  if (p.K <= 128) return nw == 1 ? launch_cfg<128, 1>(a, cus, stream) : nw == 2 ? launch_cfg<128, 2>(a, cus, stream) : launch_cfg<128, 4>(a, cus, stream);
+  if (p.K <= 32) return nw == 1 ? launch_state<32, 1>(a, stream) : nw == 2 ? launch_state<32, 2>(a, stream) : launch_state<32, 4>(a, stream);
+  if (p.K <= 64) return nw == 1 ? launch_state<64, 1>(a, stream) : nw == 2 ? launch_state<64, 2>(a, stream) : launch_state<64, 4>(a, stream);
+  if (p.K <= 128) return nw == 1 ? launch_state<128, 1>(a, stream) : nw == 2 ? launch_state<128, 2>(a, stream) : launch_state<128, 4>(a, stream);
   return hipErrorInvalidValue;
+}
+
+static hipError_t launch_factors_any(const wy::WyArgs& a, int cus, hipStream_t stream) {
+  using namespace wy;
+  if (a.p.K <= 32) return launch_factors<32>(a, cus, stream);
+  if (a.p.K <= 64) return launch_factors<64>(a, cus, stream);
+  if (a.p.K <= 128) return launch_factors<128>(a, cus, stream);
+  return hipErrorInvalidValue;
+}
+
+static hipError_t launch_wy(const wy::WyArgs& a, hipStream_t stream) {
+  const int cus = device_cu_count();
+  const hipError_t e = launch_factors_any(a, cus, stream);
+  return e != hipSuccess ? e : launch_state_any(a, cus, stream);
+}
+
+namespace wy {
+// Workspace of the segmented prefill: the factor blocks of the B * P segment-sequences, then
+// per segment the maps A [K x K] and Bm [K x V] and the entering states S_in [K x V], fp32.
+struct SegLayout {
+  size_t blocks, am, bm, sin, total;
+};
+SegLayout seg_layout(int B, int T, int HV, int K, int V, int P) {
+  auto al = [](size_t x) { return (x + 255) / 256 * 256; };
+  const size_t heads = (size_t)B * P * HV;
+  SegLayout l{};
+  l.blocks = 0;
+  l.am = al(wy_workspace_bytes(B * P, T / P, HV, K));
+  l.bm = l.am + al(heads * K * K * 4);
+  l.sin = l.bm + al(heads * K * V * 4);
+  l.total = l.sin + al(heads * K * V * 4);
+  return l;
+}
+}  // namespace wy
+
+// Segments for a fixed-length bf16 prefill on this device: P > 1 cuts each sequence into P
+// segments (P a power of two, T % (64 P) == 0, at least 4 chunks per segment) when the state
+// pass would otherwise leave most CUs idle. The segmented path runs three state passes (the
+// maps Bm and A, then the outputs), so it pays only from P >= 4: it is used then, else P = 1.
+int wy_segments(int B, int T, int HV, int V, int cus) {
+  const int units = B * HV * ((V + 31) / 32);  // state-pass workgroups at 32 columns each
+  if (units * 4 > cus) return 1;
+  int P = 1;
+  while (2 * P * units <= cus && T % (64 * 2 * P) == 0 && T / (64 * 2 * P) >= 4) P *= 2;
+  return P >= 4 ? P : 1;
+}
+
+size_t wy_segmented_workspace_bytes(int B, int T, int HV, int K, int V, int P) {
+  return wy::seg_layout(B, T, HV, K, V, P).total;
+}
+
+// The segmented prefill (P > 1, T % (64 P) == 0): factors once for all segments, then the
+// state pass three times over the B * P segment-sequences: Bm (zero entering state, v, no
+// outputs), A (identity entering state, v = 0, V = K columns, no outputs), and, after the scan
+// has made every segment's entering state, the outputs from those states.
+hipError_t launch_prefill_wy_segmented(const PrefillArgs& p, int P, void* workspace,
+                                       hipStream_t stream) {
+  using namespace wy;
+  const SegLayout l = seg_layout(p.B, p.T, p.HV, p.K, p.V, P);
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  float* Am = reinterpret_cast<float*>(ws + l.am);
+  float* Bm = reinterpret_cast<float*>(ws + l.bm);
+  float* Sin = reinterpret_cast<float*>(ws + l.sin);
+  const int cus = device_cu_count();
+  PrefillArgs ps = p;
+  ps.B = p.B * P;
+  ps.T = p.T / P;
+  WyArgs a{ps, ws + l.blocks, (ps.T + kC - 1) / kC, nullptr, nullptr, nullptr, 0};
+  hipError_t e = launch_factors_any(a, cus, stream);
+  if (e != hipSuccess) return e;
+  WyArgs ab = a;  // Bm: the state leaving each segment from a zero entering state
+  ab.p.s0 = nullptr;
+  ab.p.sT = Bm;
+  ab.p.o = nullptr;
+  if ((e = launch_state_any(ab, cus, stream)) != hipSuccess) return e;
+  const size_t nmat = (size_t)ps.B * p.HV;
+  hipLaunchKernelGGL(eye_kernel, dim3(1024), dim3(256), 0, stream, Am, nmat, p.K);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  WyArgs aa = a;  // A: the map of the entering state (identity in, v = 0, K columns)
+  aa.p.V = p.K;
+  aa.p.v = nullptr;
+  aa.p.s0 = Am;
+  aa.p.sT = Am;
+  aa.p.o = nullptr;
+  if ((e = launch_state_any(aa, cus, stream)) != hipSuccess) return e;
+  const int ntile = (p.V + 15) / 16;
+  hipLaunchKernelGGL(segment_scan_kernel, dim3(p.B * p.HV * ntile), dim3(256), 0, stream, Am, Bm,
+                     p.s0, Sin, p.sT, P, p.HV, p.K, p.V);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  WyArgs ao = a;  // the outputs from each segment's entering state
+  ao.p.s0 = Sin;
+  ao.p.sT = nullptr;
+  return launch_state_any(ao, cus, stream);
 }
 
 hipError_t launch_prefill_wy(const PrefillArgs& p, void* workspace, hipStream_t stream) {

@@ -472,6 +472,10 @@ static inline bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_prefill_wy(const PrefillArgs& a, void* workspace, hipStream_t stream);
+hipError_t launch_prefill_wy_segmented(const PrefillArgs& a, int P, void* workspace,
+                                       hipStream_t stream);
+int wy_segments(int B, int T, int HV, int V, int cus);
+int device_cu_count();
 
 // Returns hipErrorInvalidValue for shapes this build does not instantiate.
 hipError_t launch_prefill(const void* q, const void* k, const void* v, const void* g,
@@ -484,8 +488,14 @@ hipError_t launch_prefill(const void* q, const void* k, const void* v, const voi
   const int vw = bf16_inputs ? 8 : 4;
   a.vec_qkg = (K % vw == 0) && aligned16(q) && aligned16(k) && aligned16(g);
   a.vec_v = (V % vw == 0) && aligned16(v);
-  // With a workspace (sized by the caller), bf16 runs as per-chunk factors + state pass.
-  if (bf16_inputs && a.vec_qkg && a.vec_v && workspace) return launch_prefill_wy(a, workspace, stream);
+  // With a workspace (sized by the caller), bf16 runs as per-chunk factors + state pass; with
+  // few heads, over segments of the sequence composed by a scan (wy_segments decides, as the
+  // workspace size did).
+  if (bf16_inputs && a.vec_qkg && a.vec_v && workspace) {
+    const int P = wy_segments(B, T, HV, V, device_cu_count());
+    return P > 1 ? launch_prefill_wy_segmented(a, P, workspace, stream)
+                 : launch_prefill_wy(a, workspace, stream);
+  }
   // the input transforms exist only in the two-kernel path
   if (flags) return hipErrorNotSupported;
   // The bf16 kernel addresses each batch's tensors through 32-bit buffer offsets.

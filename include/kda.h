@@ -89,8 +89,9 @@ typedef enum {
  * KDA_ERR_UNSUPPORTED); float32 needs K <= 64 (else KDA_ERR_UNSUPPORTED).
  */
 /* Bytes of workspace the two-kernel path uses for these arguments: one block per
- * (b, hv, 64-token chunk) for bf16 with K % 8 == 0 and V % 8 == 0, else 0 (also 0 for
- * arguments kda_chunk_fwd would reject). */
+ * (b, hv, 64-token chunk) for bf16 with K % 8 == 0 and V % 8 == 0, plus the segment maps
+ * when few heads make the call run over segments on the current device
+ * (kda_chunk_fwd_segmented); else 0 (also 0 for arguments kda_chunk_fwd would reject). */
 size_t kda_chunk_fwd_workspace_size(int B, int T, int H, int HV, int K, int V,
                                     int chunk_size, int dtype);
 
@@ -347,6 +348,40 @@ int kda_recurrent_step_gated(const void* q, const void* k, const void* v, const 
                              const float* A_log, const float* dt_bias, float lower_bound,
                              const void* beta, float* state, void* o, int B, int H, int HV, int K,
                              int V, float scale, int dtype, unsigned flags, void* stream);
+
+/*
+ * Chunked prefill over segments of each sequence, for few heads (a chunk scan inside one
+ * GPU). The state pass of kda_chunk_fwd is sequential over a sequence's chunks, so B * HV
+ * heads keep only a few CUs busy when B * HV is small. This cuts every sequence into
+ * `segments` equal parts and runs them side by side: the state leaving a segment is an affine
+ * map of the state entering it, S_out = A S_in + Bm (K3 README, roadmap row L2, step 4: the
+ * state passed between chunks, composed over a segment's chunks), so one pass over all
+ * segments gives every Bm (zero entering state), one more gives every A (identity entering
+ * state, v = 0), a scan composes them in segment order into each segment's entering state and
+ * the final state, and a last pass makes o from those entering states. Same arithmetic per
+ * chunk as kda_chunk_fwd_ex's two-kernel path; the result differs from it by rounding only.
+ * kda_chunk_fwd / kda_chunk_fwd_ex / kda_chunk_fwd_gated take this route by themselves when it
+ * pays on the current device (four or more segments fit the CUs), and size their workspace
+ * for it.
+ *
+ *   segments     >= 1, T % (64 * segments) == 0 (else KDA_ERR_INVALID); 1 is the plain
+ *                two-kernel path
+ *   workspace    device memory of kda_chunk_fwd_segmented_workspace_size() bytes, 256-byte
+ *                aligned, caller-owned, overwritten; NULL or too small: KDA_ERR_INVALID
+ *   the rest     as for kda_chunk_fwd_ex (flags: the input transforms); initial_state and
+ *                final_state may be the same buffer
+ *
+ * Constraints: bf16, K % 8 == 0, V % 8 == 0, 16-byte aligned q, k, g, v (else
+ * KDA_ERR_UNSUPPORTED); otherwise as for kda_chunk_fwd.
+ */
+size_t kda_chunk_fwd_segmented_workspace_size(int B, int T, int H, int HV, int K, int V,
+                                              int segments, int dtype);
+
+int kda_chunk_fwd_segmented(const void* q, const void* k, const void* v, const void* g,
+                            const void* beta, const float* initial_state, float* final_state,
+                            void* o, int B, int T, int H, int HV, int K, int V, float scale,
+                            int segments, int dtype, void* workspace, size_t workspace_bytes,
+                            unsigned flags, void* stream);
 
 #ifdef __cplusplus
 }

@@ -408,3 +408,42 @@ def test_ex_entry_points_reject_the_internal_gate_flag(lib):
                                      a["o"], 2, 2, 4, 64, 64, 0.125, 1, 4, None) == kda.KDA_ERR_INVALID
     assert lib.kda_chunk_fwd_ex(FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, 2, 128, 2, 4, 64,
                                 64, 0.125, 64, 1, FAKE, 1 << 30, 4, None) == kda.KDA_ERR_INVALID
+
+
+def _segmented(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, s0=None, sT=None, o=FAKE, B=1, T=1024,
+             H=2, HV=2, K=128, V=128, scale=0.125, segments=4, dtype=1, ws=FAKE, ws_bytes=1 << 30,
+             flags=0)
+    a.update(kw)
+    return lib.kda_chunk_fwd_segmented(a["q"], a["k"], a["v"], a["g"], a["beta"], a["s0"], a["sT"],
+                                       a["o"], a["B"], a["T"], a["H"], a["HV"], a["K"], a["V"],
+                                       a["scale"], a["segments"], a["dtype"], a["ws"],
+                                       a["ws_bytes"], a["flags"], None)
+
+
+@pytest.mark.parametrize("bad,rc", [
+    (dict(q=None), kda.KDA_ERR_INVALID),
+    (dict(segments=0), kda.KDA_ERR_INVALID),
+    (dict(segments=3), kda.KDA_ERR_INVALID),       # 1024 is not a multiple of 64 * 3
+    (dict(T=1000), kda.KDA_ERR_INVALID),
+    (dict(ws=None), kda.KDA_ERR_INVALID),
+    (dict(ws_bytes=4096), kda.KDA_ERR_INVALID),
+    (dict(ws=ctypes.c_void_p(0x1010)), kda.KDA_ERR_INVALID),
+    (dict(flags=4), kda.KDA_ERR_INVALID),
+    (dict(dtype=0, K=64, V=64), kda.KDA_ERR_UNSUPPORTED),
+    (dict(K=60), kda.KDA_ERR_UNSUPPORTED),
+    (dict(g=ctypes.c_void_p(0x1008)), kda.KDA_ERR_UNSUPPORTED),
+])
+def test_segmented_rejects_invalid_arguments(lib, bad, rc):
+    assert _segmented(lib, **bad) == rc
+
+
+def test_segmented_workspace_sizes(lib):
+    ws = lib.kda_chunk_fwd_segmented_workspace_size
+    plain = ws(1, 4096, 2, 2, 128, 128, 1, 1)
+    assert plain == 1 * 2 * (4096 // 64) * lib.kda_chunk_fwd_workspace_size(1, 64, 1, 1, 128, 128, 64, 1)
+    seg = ws(1, 4096, 2, 2, 128, 128, 16, 1)
+    # the same factor blocks plus, per segment and head, A (K x K), Bm and S_in (K x V) in fp32
+    assert seg == plain + 3 * 16 * 2 * 128 * 128 * 4
+    assert ws(1, 4096, 2, 2, 128, 128, 3, 1) == 0     # 4096 is not a multiple of 64 * 3
+    assert ws(1, 4096, 2, 2, 128, 128, 16, 0) == 0    # bf16 only
