@@ -351,7 +351,7 @@ def main():
     if not args.no_segmented:
         from synth import prefill_inputs
         result["few_heads"] = []
-        for (fb, ft, fh) in ((1, 32768, 4), (1, 32768, 16)):
+        for (fb, ft, fh) in ((1, 32768, 4), (1, 32768, 8)):
             log(f"bench: few heads B={fb} T={ft} H=HV={fh}")
             fi = prefill_inputs(fb, ft, fh, fh, 128, 128, "bf16", True, seed=4323)
             fd = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in fi.items()}

@@ -899,55 +899,102 @@ hipError_t launch_state(const WyArgs& a, hipStream_t stream) {
 // P equal segments, which is the same memory viewed as P times the batch. Per segment, the
 // state leaving it is an affine map of the state entering it, S_out = A S_in + Bm (A: K x K).
 // The scan below composes the maps in segment order: S_in[0] = S0, S_in[p+1] = A_p S_in[p] +
-// Bm_p; the last value is the sequence's final state. One workgroup per (b, hv, 16-column tile);
-// the state tile lives in LDS, a thread owns one state row and 8 of the tile's columns.
+// Bm_p; the last value is the sequence's final state.
+//
+// One workgroup of 4 waves per (b, hv, 16-column tile). The products run on fp32 MFMA
+// (v_mfma_f32_16x16x4_f32) with the contraction index permuted so that lane group q = l / 16
+// covers k = NS q .. NS q + NS - 1 (NS = KT / 4): every wave keeps the whole K x 16 state tile
+// in registers as B operands (lane (q, j) holds column j's rows NS q ..), and a lane's A operands
+// are NS consecutive floats of one row of A_p, loaded as 16-byte pieces. Wave w computes the
+// row blocks w, w + 4, ...; the new rows meet in LDS once per step and come back as B operands.
+template <int KT>
 __global__ __launch_bounds__(256) void segment_scan_kernel(const float* __restrict__ Am,
                                                            const float* __restrict__ Bm,
                                                            const float* s0, float* __restrict__ Sin,
                                                            float* sT, int P, int HV, int K, int V) {
-  __shared__ float sS[128][17];
+  constexpr int NS = KT / 4;    // k steps of one product (4 per MFMA, one per lane group)
+  constexpr int NRB = KT / 16;  // row blocks of the state tile
+  __shared__ float sS[KT][17];
   const int ntile = (V + 15) / 16;
   const int tile = blockIdx.x % ntile, bh = blockIdx.x / ntile;
   const int b = bh / HV, hv = bh - b * HV;
-  const int t = threadIdx.x, c = t >> 1, j0 = (t & 1) * 8, col0 = tile * 16;
-  for (int i = t; i < K * 16; i += 256) {
-    const int r = i >> 4, j = i & 15;
-    sS[r][j] = (s0 && col0 + j < V) ? s0[((size_t)bh * K + r) * V + col0 + j] : 0.f;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int j = lane & 15, q = lane >> 4;
+  const int col = tile * 16 + j;
+  // Every access below is a buffer access with its whole offset in the lane's register and a
+  // range of one matrix: rows >= K fall past the range and columns >= V start at kOutOfRange,
+  // so they read zeros and their stores are dropped, without a branch (branches around each
+  // access made the compiler wait for all memory operations before each one).
+  const unsigned kv = (unsigned)K * V * 4, kk = (unsigned)K * K * 4;
+  const unsigned vrow = (unsigned)V * 4;
+  const unsigned lcol = col < V ? (unsigned)col * 4 : kOutOfRange;
+  auto mat_kv = [&](const float* base, size_t m) { return make_rsrc(base + m * K * V, kv); };
+
+  float Sb[NS];  // B operands: S[NS q + s][col]
+  {
+    const auto r0 = mat_kv(s0, bh);
+#pragma unroll
+    for (int st = 0; st < NS; ++st)
+      Sb[st] = s0 ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                  r0, lcol + (unsigned)(NS * q + st) * vrow, 0, 0))
+                  : 0.f;
   }
-  __syncthreads();
+  // rows NS q .. of column col go out from the wave whose index is q (each row once)
+  auto store_rows = [&](float* dst, size_t m) {
+    const auto rd = mat_kv(dst, m);
+    const unsigned base = w == q ? lcol : kOutOfRange;
+#pragma unroll
+    for (int st = 0; st < NS; ++st)
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, Sb[st]), rd,
+                                            base + (unsigned)(NS * q + st) * vrow, 0, 0);
+  };
+  // A and Bm of this wave's next (step, row block) item load while the current one multiplies:
+  // neither depends on the state.
+  const int nmine = w < NRB ? (NRB - 1 - w) / 4 + 1 : 0;  // row blocks w, w + 4, ...
+  auto load_item = [&](int pp, int rb, f32x4 (&a4)[NS / 4], f32x4& bm) {
+    const size_t seg = (size_t)(b * P + pp) * HV + hv;
+    const auto rb_ = mat_kv(Bm, seg);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      bm[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                            rb_, lcol + (unsigned)(16 * rb + 4 * q + i) * vrow, 0, 0));
+    const auto ra = make_rsrc(Am + seg * K * K, kk);
+    const int row = 16 * rb + j;
+#pragma unroll
+    for (int m = 0; m < NS / 4; ++m) {
+      const int k = NS * q + 4 * m;  // K % 8 == 0: a piece is wholly inside or outside
+      const unsigned off = (row < K && k < K) ? (unsigned)(row * K + k) * 4 : kOutOfRange;
+      a4[m] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0));
+    }
+  };
+  f32x4 a_cur[NS / 4], a_nxt[NS / 4], bm_cur, bm_nxt;
+  if (nmine > 0) load_item(0, w, a_cur, bm_cur);
   for (int p = 0; p < P; ++p) {
-    const size_t seg = (size_t)(b * P + p) * HV + hv;
-    float acc[8];
-    if (c < K) {
+    store_rows(Sin, (size_t)(b * P + p) * HV + hv);
+    for (int i = 0; i < nmine; ++i) {
+      const int rb = w + 4 * i;
+      const int np = i + 1 < nmine ? p : p + 1, ni = i + 1 < nmine ? i + 1 : 0;
+      if (np < P) load_item(np, w + 4 * ni, a_nxt, bm_nxt);
+      // four independent accumulator chains (k steps st = 4 m + e go to chain e)
+      f32x4 acc[4] = {bm_cur, f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f},
+                      f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int col = col0 + j0 + j;
-        if (col < V) Sin[(seg * K + c) * V + col] = sS[c][j0 + j];
-        acc[j] = col < V ? Bm[(seg * K + c) * V + col] : 0.f;
-      }
-      const float* arow = Am + (seg * K + c) * K;
-      for (int k = 0; k < K; k += 4) {
-        const f32x4 a4 = *reinterpret_cast<const f32x4*>(arow + k);
+      for (int st = 0; st < NS; ++st)
+        acc[st & 3] = __builtin_amdgcn_mfma_f32_16x16x4f32(a_cur[st >> 2][st & 3], Sb[st],
+                                                           acc[st & 3], 0, 0, 0);
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
+      for (int r = 0; r < 4; ++r)
+        sS[16 * rb + 4 * q + r][j] = (acc[0][r] + acc[1][r]) + (acc[2][r] + acc[3][r]);
 #pragma unroll
-          for (int j = 0; j < 8; ++j) acc[j] += a4[e] * sS[k + e][j0 + j];
-      }
+      for (int m = 0; m < NS / 4; ++m) a_cur[m] = a_nxt[m];
+      bm_cur = bm_nxt;
     }
-    __syncthreads();
-    if (c < K) {
+    lds_barrier();
 #pragma unroll
-      for (int j = 0; j < 8; ++j) sS[c][j0 + j] = acc[j];
-    }
-    __syncthreads();
+    for (int st = 0; st < NS; ++st) Sb[st] = sS[NS * q + st][j];
+    lds_barrier();
   }
-  if (sT && c < K) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int col = col0 + j0 + j;
-      if (col < V) sT[((size_t)bh * K + c) * V + col] = sS[c][j0 + j];
-    }
-  }
+  if (sT) store_rows(sT, bh);
 }
 
 // n identity matrices of K x K (the state entering each segment when its map A is traced).
@@ -1039,13 +1086,15 @@ SegLayout seg_layout(int B, int T, int HV, int K, int V, int P) {
 // Segments for a fixed-length bf16 prefill on this device: P > 1 cuts each sequence into P
 // segments (P a power of two, T % (64 P) == 0, at least 4 chunks per segment) when the state
 // pass would otherwise leave most CUs idle. The segmented path runs three state passes (the
-// maps Bm and A, then the outputs), so it pays only from P >= 4: it is used then, else P = 1.
+// maps Bm and A, then the outputs) and a scan, so it pays only from P >= 8 (measured: P = 4 at
+// B1 T32768 H16 ties with the plain path, P = 16 at H4 is 2.7 times faster): it is used then,
+// else P = 1.
 int wy_segments(int B, int T, int HV, int V, int cus) {
   const int units = B * HV * ((V + 31) / 32);  // state-pass workgroups at 32 columns each
-  if (units * 4 > cus) return 1;
+  if (units * 8 > cus) return 1;
   int P = 1;
   while (2 * P * units <= cus && T % (64 * 2 * P) == 0 && T / (64 * 2 * P) >= 4) P *= 2;
-  return P >= 4 ? P : 1;
+  return P >= 8 ? P : 1;
 }
 
 size_t wy_segmented_workspace_bytes(int B, int T, int HV, int K, int V, int P) {
@@ -1087,8 +1136,13 @@ hipError_t launch_prefill_wy_segmented(const PrefillArgs& p, int P, void* worksp
   aa.p.o = nullptr;
   if ((e = launch_state_any(aa, cus, stream)) != hipSuccess) return e;
   const int ntile = (p.V + 15) / 16;
-  hipLaunchKernelGGL(segment_scan_kernel, dim3(p.B * p.HV * ntile), dim3(256), 0, stream, Am, Bm,
-                     p.s0, Sin, p.sT, P, p.HV, p.K, p.V);
+  auto scan = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, dim3(p.B * p.HV * ntile), dim3(256), 0, stream, Am, Bm, p.s0, Sin,
+                       p.sT, P, p.HV, p.K, p.V);
+  };
+  if (p.K <= 32) scan(segment_scan_kernel<32>);
+  else if (p.K <= 64) scan(segment_scan_kernel<64>);
+  else scan(segment_scan_kernel<128>);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   WyArgs ao = a;  // the outputs from each segment's entering state
   ao.p.s0 = Sin;

@@ -361,7 +361,7 @@ int kda_recurrent_step_gated(const void* q, const void* k, const void* v, const 
  * the final state, and a last pass makes o from those entering states. Same arithmetic per
  * chunk as kda_chunk_fwd_ex's two-kernel path; the result differs from it by rounding only.
  * kda_chunk_fwd / kda_chunk_fwd_ex / kda_chunk_fwd_gated take this route by themselves when it
- * pays on the current device (four or more segments fit the CUs), and size their workspace
+ * pays on the current device (eight or more segments fit the CUs), and size their workspace
  * for it.
  *
  *   segments     >= 1, T % (64 * segments) == 0 (else KDA_ERR_INVALID); 1 is the plain
