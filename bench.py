@@ -36,7 +36,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFS = 2516.6     # MI355X dense bf16 MFMA, published (no sparsity)
 METRIC = "KDA prefill tokens/s + MFMA util (H=16,K=V=128,T=8192); decode state HBM GB/s"
-PREFILL_KERNELS = ["kda::wy::factors_kernel<128, false, false>", "kda::wy::state_kernel<128, 2, false>"]
+PREFILL_KERNELS = ["kda::wy::factors_kernel<128, false, false, false>", "kda::wy::state_kernel<128, 2, false>"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_traffic.json")
 MEASURED_SOURCES = ["kda_chunk_wy.hip", "kda_device.h"]
 PREFILL_WORKLOAD = "prefill-B4-T8192-H16-K128"
