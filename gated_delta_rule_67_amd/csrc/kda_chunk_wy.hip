@@ -582,6 +582,21 @@ __device__ __forceinline__ void dma_block(unsigned char* dst, const unsigned cha
   }
 }
 
+// One wave copies a whole chunk block into LDS (1 KB per instruction, lane-contiguous).
+template <int KT>
+__device__ __forceinline__ void dma_block_all(unsigned char* dst, const unsigned char* src, int lane) {
+  constexpr int NB = Blk<KT>::bytes / 1024;
+  const __amdgpu_buffer_rsrc_t r = make_rsrc(src, Blk<KT>::bytes);
+  const unsigned voff = 16u * lane;
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+#if __HIP_DEVICE_COMPILE__  // device-only builtin (LDS address space)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(dst + 1024 * j), 16,
+                                              voff, 1024 * j, 0, 0);
+#endif
+  }
+}
+
 // s_waitcnt vmcnt(N) (expcnt and lgkmcnt left unconstrained)
 template <int N>
 __device__ __forceinline__ void wait_vmem() {
@@ -646,8 +661,96 @@ void state_kernel(WyArgs a) {
   // DMA waves have waited for their loads into it; before it is refilled, every compute
   // wave has passed the barrier that follows its last read.
   const unsigned rowb = (unsigned)(p.HV * V * 2);  // bytes between consecutive tokens of v / o
-  if (wv >= NW) {
-    // DMA waves: the factors by LDS DMA; the v tile by range-checked loads (zeros past T
+  // Two DMA schedules. With one workgroup per CU (NW <= 2 at the grids that choose it), each DMA
+  // wave owns one buffer and its look-ahead loads get two intervals (measured: 421-436 us
+  // against 457-465 us at B4 T8192 H16). With NW = 4 (grids of more than one round) the two
+  // waves split every block, which measured faster there (2.42 ms against 2.53 ms at B1
+  // T32768 H96).
+  constexpr bool kAltDma = NW <= 2;
+  if (kAltDma && wv >= NW) {
+    // DMA waves (NW <= 2). Wave pw owns LDS buffer pw and fills it with the chunks n = pw (mod 2): the
+    // factors by LDS DMA, the v tile by range-checked loads (zeros past T or V), written
+    // transposed so a compute lane reads 4 consecutive tokens at once. A wave issues the v
+    // loads and the L2 warm-up of its next chunk right after its fill, two intervals before
+    // it waits on them (vmcnt counts in order, so a wait for the DMA also waits for every
+    // older load: with one shared look-ahead interval, each interval lasted a memory round
+    // trip even with no factor DMA at all).
+    // v tile: 64 rows x BV/8 pieces of 8 columns; lane takes pieces lane + 64 e (V % 8 == 0,
+    // so a piece is wholly inside or outside the row)
+    const int pw = wv - NW;
+    constexpr int PPR = BV / 8;  // pieces per row
+    constexpr int NPL = PPR;     // pieces per lane: 64 rows x PPR pieces over 64 lanes
+    unsigned voff[NPL];
+#pragma unroll
+    for (int e = 0; e < NPL; ++e) {
+      const int pc = lane + 64 * e, row = pc / PPR, c8 = pc % PPR;
+      const int col = vt_idx * BV + 8 * c8;
+      voff[e] = col < V ? (unsigned)(col * 2) + (unsigned)row * rowb : kOutOfRange;
+    }
+    bf16x8 rvv[NPL];
+    auto load_v = [&](int n) {  // n past the end re-reads the last chunk (no branch)
+      n = min(n, NT - 1);
+      const int t0 = n * kC, nrow = min(kC, len - t0);
+      const auto rv_ = make_rsrc(static_cast<const bf16*>(p.v) + (((size_t)bos + t0) * p.HV + hv) * V,
+                                 p.v ? (unsigned)nrow * rowb : 0u);  // no v: zeros
+#pragma unroll
+      for (int e = 0; e < NPL; ++e)
+        rvv[e] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rv_, voff[e], 0, 0));
+    };
+    auto store_v = [&](unsigned char* dst) {
+      bf16* vt = reinterpret_cast<bf16*>(dst + VT);
+#pragma unroll
+      for (int e = 0; e < NPL; ++e) {
+        const int pc = lane + 64 * e, row = pc / PPR, c8 = pc % PPR;
+#pragma unroll
+        for (int x = 0; x < 8; ++x) vt[(8 * c8 + x) * PV + row] = rvv[e][x];
+      }
+    };
+    // L2 warm-up of the wave's next chunk: the sibling workgroups of a head (V tiles) split
+    // each block's 1 KB rows, so the block comes from HBM once and the DMA two intervals later
+    // hits L2. The loaded values are not used; their registers are consumed just before the
+    // next reuse.
+    constexpr int NB = W::bytes / 1024;
+    constexpr int NPF = (NB * NW + 7) / 8;  // rows per workgroup when V tiles cover 128 columns
+    u32x4 pf[NPF];
+#pragma unroll
+    for (int i = 0; i < NPF; ++i) pf[i] = u32x4{0u, 0u, 0u, 0u};
+    const int pf_row0 = vt_idx * NPF;
+    auto warm = [&](int n) {  // n past the end re-reads the last block (no branch)
+      const unsigned char* src = wsh + (size_t)min(n, NT - 1) * W::bytes + 16 * lane;
+#pragma unroll
+      for (int i = 0; i < NPF; ++i) {
+        asm volatile("" ::"v"(pf[i]));
+        pf[i] = *reinterpret_cast<const u32x4*>(src + 1024 * ((pf_row0 + i) % NB));
+      }
+    };
+    // chunk n into dst (its v tile was loaded two intervals earlier); then v and the L2
+    // warm-up of chunk n + 2 go out and stay in flight across two barriers
+    auto fill = [&](unsigned char* dst, int n) {
+      dma_block_all<KT>(dst, wsh + (size_t)n * W::bytes, lane);
+      wait_vmem<0>();
+      store_v(dst);
+      load_v(n + 2);
+      warm(n + 2);
+    };
+    if (VARLEN && NT == 0) return;  // empty sequence
+    load_v(pw);
+    warm(pw);
+    if (pw == 0) fill(buf0, 0);
+    for (int n = 0; n < NT; n += 2) {
+      lds_barrier();
+      if (pw == 1 && n + 1 < NT) fill(buf1, n + 1);
+      if (n + 1 >= NT) break;
+      lds_barrier();
+      if (pw == 0 && n + 2 < NT) fill(buf0, n + 2);
+    }
+#pragma unroll
+    for (int i = 0; i < NPF; ++i) asm volatile("" ::"v"(pf[i]));
+    return;
+  }
+
+  if (!kAltDma && wv >= NW) {
+    // DMA waves (NW > 2): the factors by LDS DMA; the v tile by range-checked loads (zeros past T
     // or V), written transposed so a compute lane reads 4 consecutive tokens at once.
     // v tile: 64 rows x BV/8 pieces of 8 columns; lane pl takes pieces pl + 128 e (V % 8 == 0,
     // so a piece is wholly inside or outside the row)
