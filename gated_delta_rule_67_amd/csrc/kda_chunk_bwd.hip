@@ -158,6 +158,8 @@ __device__ __forceinline__ void st4(void* p, f32x4 x) {
       bf16x4{static_cast<bf16>(x[0]), static_cast<bf16>(x[1]), static_cast<bf16>(x[2]), static_cast<bf16>(x[3])};
 }
 
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, unsigned bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
 }
@@ -560,19 +562,42 @@ __device__ __forceinline__ void sweep_tile(int nvt, int nh, int& head, int& vt_i
 
 // this wave's 16 columns of a K x 16 state, held transposed in LDS (st[v][c], pitch pk),
 // to dst[c][v] (row pitch V) with 16-byte stores; columns past V are dropped
-template <int KT>
+// BRANCH_FREE: buffer stores with the column check in the offset, never behind a branch. In
+// the forward sweep that lets the loop wait only for its own loads (the compiler cannot count
+// stores behind branches across the loop, and vmcnt counts them in order with the loads):
+// 448 -> 357-363 us at B4 T8192 H16. The reverse sweep measured slower with it (568 -> 600+ us)
+// and keeps the branch.
+template <int KT, bool BRANCH_FREE>
 __device__ __forceinline__ void store_state_tile(bf16* dst, int V, int vcol0, const bf16* st, int pk,
                                                  int lane) {
+  if constexpr (BRANCH_FREE) {
+    const auto r = rsrc(dst, (unsigned)KT * V * 2);
 #pragma unroll
-  for (int e = 0; e < KT * 2 / 64; ++e) {
-    const int u = lane + 64 * e, c = u >> 1, h8 = 8 * (u & 1);
-    if (vcol0 + h8 < V) {
+    for (int e = 0; e < KT * 2 / 64; ++e) {
+      const int u = lane + 64 * e, c = u >> 1, h8 = 8 * (u & 1);
       bf16x8 x;
 #pragma unroll
       for (int j = 0; j < 8; ++j) x[j] = st[(h8 + j) * pk + c];
-      st8(dst + (size_t)c * V + vcol0 + h8, x);
+      const unsigned off = vcol0 + h8 < V ? (unsigned)(c * V + vcol0 + h8) * 2 : 0x80000000u;
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), r, off, 0, 0);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < KT * 2 / 64; ++e) {
+      const int u = lane + 64 * e, c = u >> 1, h8 = 8 * (u & 1);
+      if (vcol0 + h8 < V) {
+        bf16x8 x;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = st[(h8 + j) * pk + c];
+        st8(dst + (size_t)c * V + vcol0 + h8, x);
+      }
     }
   }
+}
+
+// One bf16 into a chunk's [rows][V] tile by a buffer store (offset 0x80000000: dropped).
+__device__ __forceinline__ void bstore1(bf16 x, __amdgpu_buffer_rsrc_t r, unsigned off) {
+  __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, x), r, off, 0, 0);
 }
 
 template <int KT, int NW>
@@ -624,8 +649,10 @@ __global__ __launch_bounds__(64 * NW) void fwd_sweep_kernel(BwdArgs a) {
     for (int e = 0; e < N2; ++e) p2[e] = ld8(blk + P::kct + 16 * (tid + NTH * e));
 #pragma unroll
     for (int e = 0; e < N3; ++e) p3[e] = ld8(blk + P::tm + 16 * (tid + NTH * e));
-    if (tid < KT) pgam = reinterpret_cast<const float*>(blk + P::gam)[tid];
-    if (tid < kC) pbt = reinterpret_cast<const float*>(blk + P::beta)[tid];
+    // unconditional (clamped) loads: in branches the compiler sank them below the chunk's
+    // stores, and the wait for them then waited for every store (vmcnt counts in order)
+    pgam = reinterpret_cast<const float*>(blk + P::gam)[tid < KT ? tid : KT - 1];
+    pbt = reinterpret_cast<const float*>(blk + P::beta)[tid < kC ? tid : kC - 1];
     size_t row0;
     int nrow;
     seq_rows(a, sq_, b, n, row0, nrow);
@@ -674,6 +701,10 @@ __global__ __launch_bounds__(64 * NW) void fwd_sweep_kernel(BwdArgs a) {
     __syncthreads();
     // X = Kg h, W0 = V - X, Y = beta W0
     const size_t trow = (sq_.slot0 + n) * kC;
+    // W0 and U rows of this chunk: buffer stores, never behind a branch (columns >= V dropped)
+    const auto rw0 = rsrc(a.w0 + trow * V, (unsigned)kC * V * 2);
+    const auto ru = rsrc(a.u + trow * V, (unsigned)kC * V * 2);
+    const unsigned lane_off = vok ? (unsigned)(4 * lq * V + vc) * 2 : 0x80000000u;
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
       f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -684,7 +715,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_sweep_kernel(BwdArgs a) {
         const int i = 16 * I + 4 * lq + r;
         w0[r] = static_cast<float>(s_vt[i * PV + 16 * w + lr]) - x[r];
         y[r] = s_bt[i] * w0[r];
-        if (vok) a.w0[(trow + i) * V + vc] = static_cast<bf16>(w0[r]);
+        bstore1(static_cast<bf16>(w0[r]), rw0, lane_off + (unsigned)((16 * I + r) * V) * 2);
       }
       st4(s_yt + lr * kPC + 16 * I + 4 * lq, y);
     }
@@ -695,7 +726,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_sweep_kernel(BwdArgs a) {
       mmaK<kC>(uv, s_tm + 16 * I * kPC, kPC, s_yt, kPC, lane);
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        if (vok) a.u[(trow + 16 * I + 4 * lq + r) * V + vc] = static_cast<bf16>(uv[r]);
+        bstore1(static_cast<bf16>(uv[r]), ru, lane_off + (unsigned)((16 * I + r) * V) * 2);
       st4(s_uu + lr * kPC + 16 * I + 4 * lq, uv);
     }
     // h <- Gam_C h + Kc^T U
@@ -706,7 +737,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_sweep_kernel(BwdArgs a) {
       mmaK<kC>(S[ct], s_kct + 16 * ct * kPC, kPC, s_uu, kPC, lane);
     }
     // h of this chunk to the workspace (its LDS copy is intact until the next chunk)
-    store_state_tile<KT>(a.h + (sq_.slot0 + n) * KT * V, V, vt_idx * BV + 16 * w, s_ht, PK, lane);
+    store_state_tile<KT, true>(a.h + (sq_.slot0 + n) * KT * V, V, vt_idx * BV + 16 * w, s_ht, PK, lane);
   }
 }
 
@@ -853,7 +884,7 @@ __global__ __launch_bounds__(64 * NW) void rev_sweep_kernel(BwdArgs a) {
       for (int r = 0; r < 4; ++r) D[ct][r] = D[ct][r] * s_gam[16 * ct + 4 * lq + r] + a.scale * p[r] - q[r];
     }
     // dS of this chunk to the workspace (its LDS copy is intact until the next chunk)
-    store_state_tile<KT>(a.dsn + (sq_.slot0 + n) * KT * V, V, vt_idx * BV + 16 * w, s_dst, PK,
+    store_state_tile<KT, false>(a.dsn + (sq_.slot0 + n) * KT * V, V, vt_idx * BV + 16 * w, s_dst, PK,
                          lane);
   }
   if (a.dh0 && vok)
