@@ -154,9 +154,13 @@ def copy_ceiling(torch, nbytes=1 << 30, reps=5):
     return 2 * nbytes / (ms * 1e-3) / 1e9
 
 
-def cpu_baseline(tokens):
+def cpu_baseline(tokens, gpu_out=None):
     """The fp64 oracle on the first `tokens` tokens of the prefill workload (all batches and
-    heads), single-threaded, on this host."""
+    heads), single-threaded, on this host. With gpu_out = (o, final_state) of the timed GPU
+    call on the whole workload (CPU tensors) and the whole workload timed, the oracle's result
+    also checks that call: RMS(err) <= 2e-2 RMS(ref) over each tensor and every row within
+    2e-2 (RMS_row(ref) + RMS(ref)), the bf16 reading the parity tests use."""
+    import numpy as np
     from oracle import recurrent
     from synth import workload_inputs
 
@@ -168,14 +172,27 @@ def cpu_baseline(tokens):
     except ImportError:  # pragma: no cover
         limiter = None
     t0 = time.perf_counter()
-    recurrent(**sl)
+    o_ref, s_ref = recurrent(**sl)
     dt = time.perf_counter() - t0
     if limiter is not None:
         limiter.restore_original_limits()
     B = inp["q"].shape[0]
-    return dict(value=B * tokens / dt, unit="tokens/s", cores=1, kind="oracle",
-                sample=f"first {tokens} of the 8192 tokens of the prefill workload, all B=4 x 16 heads "
-                       f"({B * tokens} tokens, {dt:.1f} s, numpy float64, one thread)")
+    out = dict(value=B * tokens / dt, unit="tokens/s", cores=1, kind="oracle",
+               sample=f"first {tokens} of the 8192 tokens of the prefill workload, all B=4 x 16 heads "
+                      f"({B * tokens} tokens, {dt:.1f} s, numpy float64, one thread)")
+    if gpu_out is not None and tokens == inp["q"].shape[1]:
+        checks = {}
+        for name, got, ref in (("o", gpu_out[0], o_ref), ("final_state", gpu_out[1], s_ref)):
+            got = got.double().numpy()
+            err = got - ref
+            rms = float(np.sqrt(np.mean(ref ** 2)))
+            rel = float(np.sqrt(np.mean(err ** 2))) / rms
+            row = float(np.max(np.sqrt(np.mean(err ** 2, axis=-1)) /
+                               (np.sqrt(np.mean(ref ** 2, axis=-1)) + rms)))
+            checks[name] = {"rms_err_over_rms": rel, "worst_row": row,
+                            "pass": bool(rel <= 2e-2 and row <= 2e-2)}
+        out["parity_of_timed_call"] = checks
+    return out
 
 
 def main():
@@ -221,6 +238,7 @@ def main():
     o, s = prefill()
     torch.cuda.synchronize()
     assert torch.isfinite(o.float()).all() and torch.isfinite(s).all(), "non-finite prefill output"
+    checked = (o.cpu(), s.cpu()) if not args.no_cpu_baseline else None  # judged by the oracle leg
     log(f"bench: timing {args.steps} prefill steps after {args.warmup} warmup")
     avg_ms, med_ms, min_ms = time_launches(prefill, args.steps, args.warmup, torch)
     tokens = c["B"] * c["T"]
@@ -427,7 +445,7 @@ def main():
     # ---------------- oracle on the host
     if not args.no_cpu_baseline:
         log(f"bench: timing the CPU oracle on {args.cpu_tokens} tokens")
-        result["cpu_baseline"] = cpu_baseline(args.cpu_tokens)
+        result["cpu_baseline"] = cpu_baseline(args.cpu_tokens, checked)
 
     print(json.dumps(result), flush=True)
 
