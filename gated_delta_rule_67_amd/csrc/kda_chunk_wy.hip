@@ -423,7 +423,13 @@ __global__ __launch_bounds__(256) void factors_kernel(WyArgs a) {
       }
     }
     const float brow = (p.flags & kFlagBetaSigmoid) ? sigmoid_f32(bits_to_f32(rbeta)) : bits_to_f32(rbeta);
-    if (lq == 0) *reinterpret_cast<float*>(blk + W::beta + i_row * 4) = brow;
+    // Block stores that depend on the lane or the wave are buffer stores with the condition in
+    // the offset (kOutOfRange: dropped), never behind a branch: the compiler can then count
+    // them across the item loop, and the next item's wait for its prefetched inputs does not
+    // also wait for this item's stores (vmcnt counts loads and stores in order).
+    const auto rblk = make_rsrc(blk, W::bytes);
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, brow), rblk,
+                                          lq == 0 ? (unsigned)(W::beta + i_row * 4) : kOutOfRange, 0, 0);
     // this item's raw inputs are consumed: fetch the next item's
     if (it + (int)gridDim.x < items) prefetch(it + gridDim.x);
     lds_barrier();
@@ -463,9 +469,10 @@ __global__ __launch_bounds__(256) void factors_kernel(WyArgs a) {
         }
       }
 #pragma unroll
-      for (int m = 0; m < 2; ++m)
-        if (m == 0 || w >= 2)  // rows of tokens 0..31 keep only the first 32-token step
-          *reinterpret_cast<bf16x8*>(blk + W::aq + tri_off(i_row, 4 * m + lq)) = cat8(qv[2 * m], qv[2 * m + 1]);
+      for (int m = 0; m < 2; ++m)  // rows of tokens 0..31 keep only the first 32-token step
+        __builtin_amdgcn_raw_buffer_store_b128(
+            __builtin_bit_cast(u32x4, cat8(qv[2 * m], qv[2 * m + 1])), rblk,
+            (m == 0 || w >= 2) ? (unsigned)(W::aq + tri_off(i_row, 4 * m + lq)) : kOutOfRange, 0, 0);
     }
     lds_barrier();
 
@@ -543,18 +550,22 @@ __global__ __launch_bounds__(256) void factors_kernel(WyArgs a) {
     for (int rep = 0; rep < 2; ++rep) {
       const int task = tid + 256 * rep, i = task >> 3, c8 = task & 7;
       const int m = c8 >> 2, q = c8 & 3, I = i >> 4;
-      if (i >= 32 || m == 0) {
-        const bf16x4 lo = (2 * m <= I) ? load4(tT + i * PC + 32 * m + 4 * q) : bf16x4{};
-        const bf16x4 hi = (2 * m + 1 <= I) ? load4(tT + i * PC + 32 * m + 16 + 4 * q) : bf16x4{};
-        *reinterpret_cast<bf16x8*>(blk + W::t + tri_off(i, c8)) = cat8(lo, hi);
-      }
+      const bf16x4 lo = (2 * m <= I) ? load4(tT + i * PC + 32 * m + 4 * q) : bf16x4{};
+      const bf16x4 hi = (2 * m + 1 <= I) ? load4(tT + i * PC + 32 * m + 16 + 4 * q) : bf16x4{};
+      __builtin_amdgcn_raw_buffer_store_b128(
+          __builtin_bit_cast(u32x4, cat8(lo, hi)), rblk,
+          (i >= 32 || m == 0) ? (unsigned)(W::t + tri_off(i, c8)) : kOutOfRange, 0, 0);
     }
 #pragma unroll
     for (int rep = 0; rep < KT / 32; ++rep) {  // row rho holds channel perm32(rho)
       const int task = tid + 256 * rep, rho = task >> 3, c8 = task & 7;
       *reinterpret_cast<bf16x8*>(blk + W::kdt + (rho * 8 + swz<8>(rho, c8)) * 16) = load8(tKdT + perm32(rho) * PC + 8 * c8);
     }
-    if (tid < KT / 4) *reinterpret_cast<f32x4*>(blk + W::gam + tid * 16) = load4f(sGam + perm32(4 * tid));
+    {
+      const int tg = tid < KT / 4 ? tid : KT / 4 - 1;  // lanes past K/4 read a valid entry, store nothing
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, load4f(sGam + perm32(4 * tg))), rblk,
+                                             tid < KT / 4 ? (unsigned)(W::gam + tid * 16) : kOutOfRange, 0, 0);
+    }
     lds_barrier();  // the next item's scan writes over T
   }
 }
