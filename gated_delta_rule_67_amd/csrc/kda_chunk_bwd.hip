@@ -1057,7 +1057,12 @@ __global__ __launch_bounds__(64 * kLocalWaves) void local_kernel(BwdArgs a) {
   const int c0 = ch * (KT / 2);             // first channel of this wave's half
   const unsigned vrow = (unsigned)(a.HV * V);
 
-  // this wave's rows of dO and Ut (and W0) as MFMA A operands, straight from memory
+  // this wave's rows of dO and Ut (and W0) as MFMA A operands, straight from memory. Every
+  // global read of this kernel is a buffer load with its condition in the offset (out of range
+  // reads zeros): behind branches, each group of loads got a wait of its own, and the item paid
+  // several memory round trips in a row.
+  const auto rut = rsrc(a.ut + trow * V, (unsigned)kC * V * 2);
+  const auto rw0 = rsrc(a.w0 + trow * V, (unsigned)kC * V * 2);
   bf16x8 fdo[4], fut[4], fw0[4];
   {
     const auto rdo = rsrc(a.dout + row0 * vrow + (size_t)hv * V, ((unsigned)(nrow - 1) * vrow + V) * 2);
@@ -1066,9 +1071,9 @@ __global__ __launch_bounds__(64 * kLocalWaves) void local_kernel(BwdArgs a) {
     for (int s = 0; s < 4; ++s) {
       const int k0 = 32 * s + 8 * lq;
       const bool ok = k0 < V;
-      fdo[s] = ok ? bload8(rdo, (row * vrow + k0) * 2) : bf16x8{};
-      fut[s] = ok ? ld8(a.ut + (trow + row) * V + k0) : bf16x8{};
-      fw0[s] = ok && ch == 0 ? ld8(a.w0 + (trow + row) * V + k0) : bf16x8{};
+      fdo[s] = bload8(rdo, ok ? (row * vrow + k0) * 2 : 0x80000000u);
+      fut[s] = bload8(rut, ok ? (unsigned)(row * V + k0) * 2 : 0x80000000u);
+      fw0[s] = bload8(rw0, ok && ch == 0 ? (unsigned)(row * V + k0) * 2 : 0x80000000u);
     }
   }
   stage_qkg<KT, NTH>(sq, sk, G, PK, PG, qb, kb, gb, qrow, grow, nrow, tid);
@@ -1084,15 +1089,17 @@ __global__ __launch_bounds__(64 * kLocalWaves) void local_kernel(BwdArgs a) {
     constexpr int NU = (kC * 16 + NTH - 1) / NTH, NH = (KT * 16 + NTH - 1) / NTH;
     bf16x8 xu[NU], xh[NH];
     const int per = V / 8;
+    const auto ru = rsrc(a.u + trow * V, (unsigned)kC * V * 2);
+    const auto rh = rsrc(hsrc, (unsigned)KT * V * 2);
 #pragma unroll
     for (int e = 0; e < NU; ++e) {
       const int u = tid + NTH * e, r = u / per, c8 = 8 * (u % per);
-      xu[e] = u < kC * per ? ld8(a.u + (trow + r) * V + c8) : bf16x8{};
+      xu[e] = bload8(ru, u < kC * per ? (unsigned)(r * V + c8) * 2 : 0x80000000u);
     }
 #pragma unroll
     for (int e = 0; e < NH; ++e) {
       const int u = tid + NTH * e, r = u / per, c8 = 8 * (u % per);
-      xh[e] = u < KT * per ? ld8(hsrc + (size_t)r * V + c8) : bf16x8{};
+      xh[e] = bload8(rh, u < KT * per ? (unsigned)(r * V + c8) * 2 : 0x80000000u);
     }
 #pragma unroll
     for (int e = 0; e < NU; ++e) {
@@ -1151,10 +1158,11 @@ __global__ __launch_bounds__(64 * kLocalWaves) void local_kernel(BwdArgs a) {
     constexpr int NH = (KT * 16 + NTH - 1) / NTH;
     bf16x8 xh[NH];
     const int per = V / 8;
+    const auto rds = rsrc(dsrc, (unsigned)KT * V * 2);
 #pragma unroll
     for (int e = 0; e < NH; ++e) {
       const int u = tid + NTH * e, r = u / per, c8 = 8 * (u % per);
-      xh[e] = u < KT * per ? ld8(dsrc + (size_t)r * V + c8) : bf16x8{};
+      xh[e] = bload8(rds, u < KT * per ? (unsigned)(r * V + c8) * 2 : 0x80000000u);
     }
     __syncthreads();  // every wave is done with h
 #pragma unroll
