@@ -199,7 +199,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--decode-reps", type=int, default=3)
     ap.add_argument("--cpu-tokens", type=int, default=8192)
     ap.add_argument("--no-cpu-baseline", action="store_true")
