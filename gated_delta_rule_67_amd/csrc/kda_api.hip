@@ -88,7 +88,7 @@ const char* kda_status_string(int status) {
   switch (status) {
     case KDA_OK: return "KDA_OK";
     case KDA_ERR_INVALID: return "KDA_ERR_INVALID: invalid argument (null pointer, dims, chunk size or scale)";
-    case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED: valid shape with no kernel in this build";
+    case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED: valid shape with no kernel in this library";
     case KDA_ERR_HIP: return "KDA_ERR_HIP: the HIP runtime reported an error at launch";
     default: return "KDA: unknown status";
   }

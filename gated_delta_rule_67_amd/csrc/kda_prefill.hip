@@ -477,7 +477,7 @@ hipError_t launch_prefill_wy_segmented(const PrefillArgs& a, int P, void* worksp
 int wy_segments(int B, int T, int HV, int V, int cus);
 int device_cu_count();
 
-// Returns hipErrorInvalidValue for shapes this build does not instantiate.
+// Returns hipErrorInvalidValue for shapes the library does not instantiate.
 hipError_t launch_prefill(const void* q, const void* k, const void* v, const void* g,
                           const void* beta, const float* s0, float* sT, void* o, int B, int T,
                           int H, int HV, int K, int V, float scale, bool bf16_inputs,

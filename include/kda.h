@@ -42,7 +42,7 @@ extern "C" {
 typedef enum {
   KDA_OK = 0,
   KDA_ERR_INVALID = -1,     /* null required pointer, bad dims, bad chunk size, non-finite scale */
-  KDA_ERR_UNSUPPORTED = -2, /* valid arguments this build has no kernel for (e.g. K or V > 128) */
+  KDA_ERR_UNSUPPORTED = -2, /* valid arguments the library has no kernel for (e.g. K or V > 128) */
   KDA_ERR_HIP = -3          /* the HIP runtime reported an error at launch */
 } kda_status;
 
