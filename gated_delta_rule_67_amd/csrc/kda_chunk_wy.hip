@@ -423,13 +423,7 @@ __global__ __launch_bounds__(256) void factors_kernel(WyArgs a) {
       }
     }
     const float brow = (p.flags & kFlagBetaSigmoid) ? sigmoid_f32(bits_to_f32(rbeta)) : bits_to_f32(rbeta);
-    // Block stores that depend on the lane or the wave are buffer stores with the condition in
-    // the offset (kOutOfRange: dropped), never behind a branch: the compiler can then count
-    // them across the item loop, and the next item's wait for its prefetched inputs does not
-    // also wait for this item's stores (vmcnt counts loads and stores in order).
-    const auto rblk = make_rsrc(blk, W::bytes);
-    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, brow), rblk,
-                                          lq == 0 ? (unsigned)(W::beta + i_row * 4) : kOutOfRange, 0, 0);
+    if (lq == 0) *reinterpret_cast<float*>(blk + W::beta + i_row * 4) = brow;
     // this item's raw inputs are consumed: fetch the next item's
     if (it + (int)gridDim.x < items) prefetch(it + gridDim.x);
     lds_barrier();
@@ -469,10 +463,9 @@ __global__ __launch_bounds__(256) void factors_kernel(WyArgs a) {
         }
       }
 #pragma unroll
-      for (int m = 0; m < 2; ++m)  // rows of tokens 0..31 keep only the first 32-token step
-        __builtin_amdgcn_raw_buffer_store_b128(
-            __builtin_bit_cast(u32x4, cat8(qv[2 * m], qv[2 * m + 1])), rblk,
-            (m == 0 || w >= 2) ? (unsigned)(W::aq + tri_off(i_row, 4 * m + lq)) : kOutOfRange, 0, 0);
+      for (int m = 0; m < 2; ++m)
+        if (m == 0 || w >= 2)  // rows of tokens 0..31 keep only the first 32-token step
+          *reinterpret_cast<bf16x8*>(blk + W::aq + tri_off(i_row, 4 * m + lq)) = cat8(qv[2 * m], qv[2 * m + 1]);
     }
     lds_barrier();
 
@@ -550,22 +543,18 @@ __global__ __launch_bounds__(256) void factors_kernel(WyArgs a) {
     for (int rep = 0; rep < 2; ++rep) {
       const int task = tid + 256 * rep, i = task >> 3, c8 = task & 7;
       const int m = c8 >> 2, q = c8 & 3, I = i >> 4;
-      const bf16x4 lo = (2 * m <= I) ? load4(tT + i * PC + 32 * m + 4 * q) : bf16x4{};
-      const bf16x4 hi = (2 * m + 1 <= I) ? load4(tT + i * PC + 32 * m + 16 + 4 * q) : bf16x4{};
-      __builtin_amdgcn_raw_buffer_store_b128(
-          __builtin_bit_cast(u32x4, cat8(lo, hi)), rblk,
-          (i >= 32 || m == 0) ? (unsigned)(W::t + tri_off(i, c8)) : kOutOfRange, 0, 0);
+      if (i >= 32 || m == 0) {
+        const bf16x4 lo = (2 * m <= I) ? load4(tT + i * PC + 32 * m + 4 * q) : bf16x4{};
+        const bf16x4 hi = (2 * m + 1 <= I) ? load4(tT + i * PC + 32 * m + 16 + 4 * q) : bf16x4{};
+        *reinterpret_cast<bf16x8*>(blk + W::t + tri_off(i, c8)) = cat8(lo, hi);
+      }
     }
 #pragma unroll
     for (int rep = 0; rep < KT / 32; ++rep) {  // row rho holds channel perm32(rho)
       const int task = tid + 256 * rep, rho = task >> 3, c8 = task & 7;
       *reinterpret_cast<bf16x8*>(blk + W::kdt + (rho * 8 + swz<8>(rho, c8)) * 16) = load8(tKdT + perm32(rho) * PC + 8 * c8);
     }
-    {
-      const int tg = tid < KT / 4 ? tid : KT / 4 - 1;  // lanes past K/4 read a valid entry, store nothing
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, load4f(sGam + perm32(4 * tg))), rblk,
-                                             tid < KT / 4 ? (unsigned)(W::gam + tid * 16) : kOutOfRange, 0, 0);
-    }
+    if (tid < KT / 4) *reinterpret_cast<f32x4*>(blk + W::gam + tid * 16) = load4f(sGam + perm32(4 * tid));
     lds_barrier();  // the next item's scan writes over T
   }
 }
@@ -590,21 +579,6 @@ __device__ __forceinline__ void dma_block(unsigned char* dst, const unsigned cha
                                                 voff, 1024 * kDmaWaves * i, 0, 0);
 #endif
     }
-  }
-}
-
-// One wave copies a whole chunk block into LDS (1 KB per instruction, lane-contiguous).
-template <int KT>
-__device__ __forceinline__ void dma_block_all(unsigned char* dst, const unsigned char* src, int lane) {
-  constexpr int NB = Blk<KT>::bytes / 1024;
-  const __amdgpu_buffer_rsrc_t r = make_rsrc(src, Blk<KT>::bytes);
-  const unsigned voff = 16u * lane;
-#pragma unroll
-  for (int j = 0; j < NB; ++j) {
-#if __HIP_DEVICE_COMPILE__  // device-only builtin (LDS address space)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(dst + 1024 * j), 16,
-                                              voff, 1024 * j, 0, 0);
-#endif
   }
 }
 
@@ -672,96 +646,8 @@ void state_kernel(WyArgs a) {
   // DMA waves have waited for their loads into it; before it is refilled, every compute
   // wave has passed the barrier that follows its last read.
   const unsigned rowb = (unsigned)(p.HV * V * 2);  // bytes between consecutive tokens of v / o
-  // Two DMA schedules. With one workgroup per CU (NW <= 2 at the grids that choose it), each DMA
-  // wave owns one buffer and its look-ahead loads get two intervals (measured: 421-436 us
-  // against 457-465 us at B4 T8192 H16). With NW = 4 (grids of more than one round) the two
-  // waves split every block, which measured faster there (2.42 ms against 2.53 ms at B1
-  // T32768 H96).
-  constexpr bool kAltDma = NW <= 2;
-  if (kAltDma && wv >= NW) {
-    // DMA waves (NW <= 2). Wave pw owns LDS buffer pw and fills it with the chunks n = pw (mod 2): the
-    // factors by LDS DMA, the v tile by range-checked loads (zeros past T or V), written
-    // transposed so a compute lane reads 4 consecutive tokens at once. A wave issues the v
-    // loads and the L2 warm-up of its next chunk right after its fill, two intervals before
-    // it waits on them (vmcnt counts in order, so a wait for the DMA also waits for every
-    // older load: with one shared look-ahead interval, each interval lasted a memory round
-    // trip even with no factor DMA at all).
-    // v tile: 64 rows x BV/8 pieces of 8 columns; lane takes pieces lane + 64 e (V % 8 == 0,
-    // so a piece is wholly inside or outside the row)
-    const int pw = wv - NW;
-    constexpr int PPR = BV / 8;  // pieces per row
-    constexpr int NPL = PPR;     // pieces per lane: 64 rows x PPR pieces over 64 lanes
-    unsigned voff[NPL];
-#pragma unroll
-    for (int e = 0; e < NPL; ++e) {
-      const int pc = lane + 64 * e, row = pc / PPR, c8 = pc % PPR;
-      const int col = vt_idx * BV + 8 * c8;
-      voff[e] = col < V ? (unsigned)(col * 2) + (unsigned)row * rowb : kOutOfRange;
-    }
-    bf16x8 rvv[NPL];
-    auto load_v = [&](int n) {  // n past the end re-reads the last chunk (no branch)
-      n = min(n, NT - 1);
-      const int t0 = n * kC, nrow = min(kC, len - t0);
-      const auto rv_ = make_rsrc(static_cast<const bf16*>(p.v) + (((size_t)bos + t0) * p.HV + hv) * V,
-                                 p.v ? (unsigned)nrow * rowb : 0u);  // no v: zeros
-#pragma unroll
-      for (int e = 0; e < NPL; ++e)
-        rvv[e] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rv_, voff[e], 0, 0));
-    };
-    auto store_v = [&](unsigned char* dst) {
-      bf16* vt = reinterpret_cast<bf16*>(dst + VT);
-#pragma unroll
-      for (int e = 0; e < NPL; ++e) {
-        const int pc = lane + 64 * e, row = pc / PPR, c8 = pc % PPR;
-#pragma unroll
-        for (int x = 0; x < 8; ++x) vt[(8 * c8 + x) * PV + row] = rvv[e][x];
-      }
-    };
-    // L2 warm-up of the wave's next chunk: the sibling workgroups of a head (V tiles) split
-    // each block's 1 KB rows, so the block comes from HBM once and the DMA two intervals later
-    // hits L2. The loaded values are not used; their registers are consumed just before the
-    // next reuse.
-    constexpr int NB = W::bytes / 1024;
-    constexpr int NPF = (NB * NW + 7) / 8;  // rows per workgroup when V tiles cover 128 columns
-    u32x4 pf[NPF];
-#pragma unroll
-    for (int i = 0; i < NPF; ++i) pf[i] = u32x4{0u, 0u, 0u, 0u};
-    const int pf_row0 = vt_idx * NPF;
-    auto warm = [&](int n) {  // n past the end re-reads the last block (no branch)
-      const unsigned char* src = wsh + (size_t)min(n, NT - 1) * W::bytes + 16 * lane;
-#pragma unroll
-      for (int i = 0; i < NPF; ++i) {
-        asm volatile("" ::"v"(pf[i]));
-        pf[i] = *reinterpret_cast<const u32x4*>(src + 1024 * ((pf_row0 + i) % NB));
-      }
-    };
-    // chunk n into dst (its v tile was loaded two intervals earlier); then v and the L2
-    // warm-up of chunk n + 2 go out and stay in flight across two barriers
-    auto fill = [&](unsigned char* dst, int n) {
-      dma_block_all<KT>(dst, wsh + (size_t)n * W::bytes, lane);
-      wait_vmem<0>();
-      store_v(dst);
-      load_v(n + 2);
-      warm(n + 2);
-    };
-    if (VARLEN && NT == 0) return;  // empty sequence
-    load_v(pw);
-    warm(pw);
-    if (pw == 0) fill(buf0, 0);
-    for (int n = 0; n < NT; n += 2) {
-      lds_barrier();
-      if (pw == 1 && n + 1 < NT) fill(buf1, n + 1);
-      if (n + 1 >= NT) break;
-      lds_barrier();
-      if (pw == 0 && n + 2 < NT) fill(buf0, n + 2);
-    }
-#pragma unroll
-    for (int i = 0; i < NPF; ++i) asm volatile("" ::"v"(pf[i]));
-    return;
-  }
-
-  if (!kAltDma && wv >= NW) {
-    // DMA waves (NW > 2): the factors by LDS DMA; the v tile by range-checked loads (zeros past T
+  if (wv >= NW) {
+    // DMA waves: the factors by LDS DMA; the v tile by range-checked loads (zeros past T
     // or V), written transposed so a compute lane reads 4 consecutive tokens at once.
     // v tile: 64 rows x BV/8 pieces of 8 columns; lane pl takes pieces pl + 128 e (V % 8 == 0,
     // so a piece is wholly inside or outside the row)
