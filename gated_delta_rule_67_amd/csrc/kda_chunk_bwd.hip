@@ -175,34 +175,47 @@ __device__ __forceinline__ void wave_sync() {
 }
 
 // One chunk's q, k (bf16, [64][pk]) and g (as fp32 into G, [64][pg]) into LDS; rows past
-// nrow read as zeros. All loads are issued before the first store. NTH threads.
+// nrow read as zeros. QkgTile::load issues every load of this thread's pieces, QkgTile::store
+// writes them to LDS, so a caller can issue more loads in between. NTH threads.
+template <int KT, int NTH>
+struct QkgTile {
+  static constexpr int PER = KT / 8, NPC = kC * PER, NU = (NPC + NTH - 1) / NTH;
+  bf16x8 xq[NU], xk[NU], xg[NU];
+  __device__ __forceinline__ void load(const bf16* qb, const bf16* kb, const bf16* gb,
+                                       unsigned qrow, unsigned grow, int nrow, int tid) {
+    const auto rq = rsrc(qb, ((unsigned)(nrow - 1) * qrow + KT) * 2);
+    const auto rk = rsrc(kb, ((unsigned)(nrow - 1) * qrow + KT) * 2);
+    const auto rg = rsrc(gb, ((unsigned)(nrow - 1) * grow + KT) * 2);
+#pragma unroll
+    for (int e = 0; e < NU; ++e) {
+      const int u = tid + NTH * e, r = u / PER, c8 = 8 * (u % PER);
+      const unsigned off = u < NPC ? 0u : 0x80000000u;
+      xq[e] = bload8(rq, ((r * qrow + c8) * 2) | off);
+      xk[e] = bload8(rk, ((r * qrow + c8) * 2) | off);
+      xg[e] = bload8(rg, ((r * grow + c8) * 2) | off);
+    }
+  }
+  __device__ __forceinline__ void store(bf16* sq, bf16* sk, float* G, int pk, int pg, int tid) const {
+#pragma unroll
+    for (int e = 0; e < NU; ++e) {
+      const int u = tid + NTH * e, r = u / PER, c8 = 8 * (u % PER);
+      if (u < NPC) {
+        st8(sq + r * pk + c8, xq[e]);
+        st8(sk + r * pk + c8, xk[e]);
+#pragma unroll
+        for (int x = 0; x < 8; ++x) G[r * pg + c8 + x] = static_cast<float>(xg[e][x]);
+      }
+    }
+  }
+};
+
 template <int KT, int NTH>
 __device__ __forceinline__ void stage_qkg(bf16* sq, bf16* sk, float* G, int pk, int pg,
                                           const bf16* qb, const bf16* kb, const bf16* gb,
                                           unsigned qrow, unsigned grow, int nrow, int tid) {
-  constexpr int PER = KT / 8, NPC = kC * PER, NU = (NPC + NTH - 1) / NTH;
-  const auto rq = rsrc(qb, ((unsigned)(nrow - 1) * qrow + KT) * 2);
-  const auto rk = rsrc(kb, ((unsigned)(nrow - 1) * qrow + KT) * 2);
-  const auto rg = rsrc(gb, ((unsigned)(nrow - 1) * grow + KT) * 2);
-  bf16x8 xq[NU], xk[NU], xg[NU];
-#pragma unroll
-  for (int e = 0; e < NU; ++e) {
-    const int u = tid + NTH * e, r = u / PER, c8 = 8 * (u % PER);
-    const unsigned off = u < NPC ? 0u : 0x80000000u;
-    xq[e] = bload8(rq, ((r * qrow + c8) * 2) | off);
-    xk[e] = bload8(rk, ((r * qrow + c8) * 2) | off);
-    xg[e] = bload8(rg, ((r * grow + c8) * 2) | off);
-  }
-#pragma unroll
-  for (int e = 0; e < NU; ++e) {
-    const int u = tid + NTH * e, r = u / PER, c8 = 8 * (u % PER);
-    if (u < NPC) {
-      st8(sq + r * pk + c8, xq[e]);
-      st8(sk + r * pk + c8, xk[e]);
-#pragma unroll
-      for (int x = 0; x < 8; ++x) G[r * pg + c8 + x] = static_cast<float>(xg[e][x]);
-    }
-  }
+  QkgTile<KT, NTH> t;
+  t.load(qb, kb, gb, qrow, grow, nrow, tid);
+  t.store(sq, sk, G, pk, pg, tid);
 }
 
 // In-place inclusive cumsum of G over the 64 rows (columns < KT); tot: [4][KT] scratch.
@@ -1076,21 +1089,20 @@ __global__ __launch_bounds__(64 * kLocalWaves) void local_kernel(BwdArgs a) {
       fw0[s] = bload8(rw0, ok && ch == 0 ? (unsigned)(row * V + k0) * 2 : 0x80000000u);
     }
   }
-  stage_qkg<KT, NTH>(sq, sk, G, PK, PG, qb, kb, gb, qrow, grow, nrow, tid);
-  if (tid < kC) {
-    sb[tid] = reinterpret_cast<const float*>(blk + P::beta)[tid];
-    db2[tid] = 0.f;
-  }
-  if (tid < KT) lx2[tid] = 0.f;
-  // ---------------- phase 1: products contracting over V
-  bf16* s_u = reinterpret_cast<bf16*>(lds + L::uu);
-  bf16* s_hs = reinterpret_cast<bf16*>(lds + L::hs);
+  // beta, q, k, g, U, h, dS and this lane's Mr entries: all issued before the first is used,
+  // so the item waits for memory about once
+  const float bload = __builtin_bit_cast(
+      float, __builtin_amdgcn_raw_buffer_load_b32(rsrc(blk + P::beta, kC * 4),
+                                                  tid < kC ? (unsigned)tid * 4 : 0x80000000u, 0, 0));
+  QkgTile<KT, NTH> qkg;
+  qkg.load(qb, kb, gb, qrow, grow, nrow, tid);
+  constexpr int NU = (kC * 16 + NTH - 1) / NTH, NH = (KT * 16 + NTH - 1) / NTH;
+  const int per = V / 8;
+  bf16x8 xu[NU], xh[NH], xds[NH];
   {
-    constexpr int NU = (kC * 16 + NTH - 1) / NTH, NH = (KT * 16 + NTH - 1) / NTH;
-    bf16x8 xu[NU], xh[NH];
-    const int per = V / 8;
     const auto ru = rsrc(a.u + trow * V, (unsigned)kC * V * 2);
     const auto rh = rsrc(hsrc, (unsigned)KT * V * 2);
+    const auto rds = rsrc(dsrc, (unsigned)KT * V * 2);
 #pragma unroll
     for (int e = 0; e < NU; ++e) {
       const int u = tid + NTH * e, r = u / per, c8 = 8 * (u % per);
@@ -1101,6 +1113,35 @@ __global__ __launch_bounds__(64 * kLocalWaves) void local_kernel(BwdArgs a) {
       const int u = tid + NTH * e, r = u / per, c8 = 8 * (u % per);
       xh[e] = bload8(rh, u < KT * per ? (unsigned)(r * V + c8) * 2 : 0x80000000u);
     }
+#pragma unroll
+    for (int e = 0; e < NH; ++e) {
+      const int u = tid + NTH * e, r = u / per, c8 = 8 * (u % per);
+      xds[e] = bload8(rds, u < KT * per ? (unsigned)(r * V + c8) * 2 : 0x80000000u);
+    }
+  }
+  float mrv[2][4];  // Mr[rw + 4 lq + r][16 J + lr] for this wave's tiles J = 2 jj + ch <= w
+  {
+    const auto rmr = rsrc(blk + P::mr, kC * kC * 4);
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = rw + 4 * lq + r, j = 16 * (2 * jj + ch) + lr;
+        mrv[jj][r] = __builtin_bit_cast(
+            float, __builtin_amdgcn_raw_buffer_load_b32(
+                       rmr, 2 * jj + ch <= w ? (unsigned)(i * kC + j) * 4 : 0x80000000u, 0, 0));
+      }
+  }
+  qkg.store(sq, sk, G, PK, PG, tid);
+  if (tid < kC) {
+    sb[tid] = bload;
+    db2[tid] = 0.f;
+  }
+  if (tid < KT) lx2[tid] = 0.f;
+  // ---------------- phase 1: products contracting over V
+  bf16* s_u = reinterpret_cast<bf16*>(lds + L::uu);
+  bf16* s_hs = reinterpret_cast<bf16*>(lds + L::hs);
+  {
 #pragma unroll
     for (int e = 0; e < NU; ++e) {
       const int u = tid + NTH * e, r = u / per, c8 = 8 * (u % per);
@@ -1155,15 +1196,6 @@ __global__ __launch_bounds__(64 * kLocalWaves) void local_kernel(BwdArgs a) {
     }
   }
   {
-    constexpr int NH = (KT * 16 + NTH - 1) / NTH;
-    bf16x8 xh[NH];
-    const int per = V / 8;
-    const auto rds = rsrc(dsrc, (unsigned)KT * V * 2);
-#pragma unroll
-    for (int e = 0; e < NH; ++e) {
-      const int u = tid + NTH * e, r = u / per, c8 = 8 * (u % per);
-      xh[e] = bload8(rds, u < KT * per ? (unsigned)(r * V + c8) * 2 : 0x80000000u);
-    }
     __syncthreads();  // every wave is done with h
 #pragma unroll
     for (int e = 0; e < NH; ++e) {
@@ -1172,9 +1204,9 @@ __global__ __launch_bounds__(64 * kLocalWaves) void local_kernel(BwdArgs a) {
         const bf16x8 hv8 = ld8(s_hs + r * PV + c8);
         float sdot = 0.f;
 #pragma unroll
-        for (int x = 0; x < 8; ++x) sdot += static_cast<float>(hv8[x]) * static_cast<float>(xh[e][x]);
+        for (int x = 0; x < 8; ++x) sdot += static_cast<float>(hv8[x]) * static_cast<float>(xds[e][x]);
         atomicAdd(lx2 + r, sdot);
-        st8(s_hs + r * PV + c8, xh[e]);
+        st8(s_hs + r * PV + c8, xds[e]);
       }
     }
   }
@@ -1204,18 +1236,12 @@ __global__ __launch_bounds__(64 * kLocalWaves) void local_kernel(BwdArgs a) {
   }
   // dbeta, second term: sum_j (-Ut U^T)_ij Mr_ij over this wave's tiles J
   {
-    const float* gmr = reinterpret_cast<const float*>(blk + P::mr);
     float s[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-      const int J = 2 * jj + ch;
-      if (J <= w)
+    for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int i = rw + 4 * lq + r, j = 16 * J + lr;
-          s[r] -= Dm[jj][r] * gmr[i * kC + j];  // Mr is zero on and above the diagonal
-        }
-    }
+      for (int r = 0; r < 4; ++r)  // Mr is zero on and above the diagonal; Dm, mrv 0 for J > w
+        s[r] -= Dm[jj][r] * mrv[jj][r];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       float x = s[r];
