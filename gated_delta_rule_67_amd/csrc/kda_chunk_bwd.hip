@@ -1196,18 +1196,27 @@ __global__ __launch_bounds__(64 * kLocalWaves) void local_kernel(BwdArgs a) {
     }
   }
   {
+    // rowsum(dS * h): the per pieces of a row sit on per consecutive lanes; when per is a
+    // power of two they are summed by shuffles and stored once, else added atomically
+    const bool pow2 = (per & (per - 1)) == 0;
     __syncthreads();  // every wave is done with h
 #pragma unroll
     for (int e = 0; e < NH; ++e) {
       const int u = tid + NTH * e, r = u / per, c8 = 8 * (u % per);
-      if (u < KT * per) {
+      const bool in = u < KT * per;
+      float sdot = 0.f;
+      if (in) {
         const bf16x8 hv8 = ld8(s_hs + r * PV + c8);
-        float sdot = 0.f;
 #pragma unroll
         for (int x = 0; x < 8; ++x) sdot += static_cast<float>(hv8[x]) * static_cast<float>(xds[e][x]);
-        atomicAdd(lx2 + r, sdot);
-        st8(s_hs + r * PV + c8, xds[e]);
       }
+      if (pow2) {
+        for (int o = 1; o < per; o <<= 1) sdot += __shfl_xor(sdot, o);
+        if (in && c8 == 0) lx2[r] = sdot;
+      } else if (in) {
+        atomicAdd(lx2 + r, sdot);
+      }
+      if (in) st8(s_hs + r * PV + c8, xds[e]);
     }
   }
   __syncthreads();
@@ -1315,11 +1324,26 @@ __global__ __launch_bounds__(64 * kLocalWaves) void local_kernel(BwdArgs a) {
     }
   }
   __syncthreads();
-  for (int c = tid; c < KT; c += NTH) {
-    float run = lx[c] + lx[KT + c] + lx[2 * KT + c] + lx[3 * KT + c] + ex(G[(kC - 1) * PG + c]) * lx2[c];
-    for (int i = kC - 1; i >= 0; --i) {
-      run += dgs[i * PG + c];
-      if (i < nrow) a.dg[((row0 + i) * a.HV + hv) * KT + c] = static_cast<bf16>(run);
+  // dg = reverse cumsum of dG over the chunk, in four 16-row segments: segment sums first,
+  // then each segment's scan starts from the sums of the segments after it
+  static_assert(4 * KT <= NTH, "one thread per segment and channel");
+  float* segs = reinterpret_cast<float*>(lds + L::tot);  // [4][KT]
+  const int sc = tid % KT, sp = tid / KT;
+  if (tid < 4 * KT) {
+    float bsum = 0.f;
+#pragma unroll
+    for (int i = 15; i >= 0; --i) bsum += dgs[(16 * sp + i) * PG + sc];
+    segs[sp * KT + sc] = bsum;
+  }
+  __syncthreads();
+  if (tid < 4 * KT) {
+    float run = lx[sc] + lx[KT + sc] + lx[2 * KT + sc] + lx[3 * KT + sc] + ex(G[(kC - 1) * PG + sc]) * lx2[sc];
+    for (int p = 3; p > sp; --p) run += segs[p * KT + sc];
+#pragma unroll
+    for (int i = 15; i >= 0; --i) {
+      const int row = 16 * sp + i;
+      run += dgs[row * PG + sc];
+      if (row < nrow) a.dg[((row0 + row) * a.HV + hv) * KT + sc] = static_cast<bf16>(run);
     }
   }
   if (ch == 0) {  // dv = beta Ut, this block's rows from the A fragments the wave holds
