@@ -934,7 +934,7 @@ __device__ __forceinline__ void rdp_products(f32x4* adq, f32x4* arow, f32x4* aco
   bf16* s_hi = reinterpret_cast<bf16*>(lds + wslot);
   bf16* s_lo = s_hi + 16 * kPC;
   const int cl = lane & 15, tg = lane >> 4;  // channel in the part, token-octet group
-#pragma unroll 1
+#pragma unroll
   for (int part = 0; part < NP; ++part) {
     const int c = ch * (KT / 2) + 16 * part + cl;
     {  // row role
@@ -955,14 +955,20 @@ __device__ __forceinline__ void rdp_products(f32x4* adq, f32x4* arow, f32x4* aco
       }
     }
     wave_sync();
-    mmaK<NR>(adq[part], s_f, kPC, s_hi, kPC, lane);
-    mmaK<NR>(adq[part], s_f, kPC, s_lo, kPC, lane);
-    mmaK<NR>(arow[part], s_e, kPC, s_hi, kPC, lane);
-    mmaK<NR>(arow[part], s_e, kPC, s_lo, kPC, lane);
+    {
+      f32x4 xq = adq[part], xr = arow[part];  // one indexed move each way per part
+      mmaK<NR>(xq, s_f, kPC, s_hi, kPC, lane);
+      mmaK<NR>(xq, s_f, kPC, s_lo, kPC, lane);
+      mmaK<NR>(xr, s_e, kPC, s_hi, kPC, lane);
+      mmaK<NR>(xr, s_e, kPC, s_lo, kPC, lane);
+      adq[part] = xq;
+      arow[part] = xr;
+    }
     wave_sync();
     {  // column role: operands q_i f_i, then k_i f_i, with f_i = exp(G_i - G_ew)
       constexpr int NO = (NC / 8 + 3) / 4;  // octets per lane (some lanes have one less)
       const float gref = G[ew * PG + c];
+      f32x4 xc = acol[part];
       float f[NO][8];
 #pragma unroll
       for (int t = 0; t < NO; ++t) {
@@ -991,10 +997,11 @@ __device__ __forceinline__ void rdp_products(f32x4* adq, f32x4* arow, f32x4* aco
         }
         wave_sync();
         const bf16* xa = pass == 0 ? s_ft : s_et;
-        mmaK<NC>(acol[part], xa, kPC, s_hi, kPC, lane);
-        mmaK<NC>(acol[part], xa, kPC, s_lo, kPC, lane);
+        mmaK<NC>(xc, xa, kPC, s_hi, kPC, lane);
+        mmaK<NC>(xc, xa, kPC, s_lo, kPC, lane);
         wave_sync();
       }
+      acol[part] = xc;
     }
   }
 }
