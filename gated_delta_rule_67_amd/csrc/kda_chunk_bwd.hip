@@ -326,8 +326,8 @@ struct PrepLds {
   static_assert(total <= 160 * 1024, "LDS");
 };
 
-// 8 waves: waves w and w + 4 own row block w; wave w builds q*exp(G - G_r) and the first half
-// of the shared k operand rows and computes Aq, wave w + 4 the k side and Mr.
+// 8 waves: two waves own each row block w; the Aq-side wave builds q*exp(G - G_r) and the
+// first half of the shared k operand rows and computes Aq, the Mr-side wave the k side and Mr.
 template <int KT>
 __global__ __launch_bounds__(512) void prep_kernel(BwdArgs a) {
   using L = PrepLds<KT>;
@@ -343,7 +343,9 @@ __global__ __launch_bounds__(512) void prep_kernel(BwdArgs a) {
   bf16* bop = reinterpret_cast<bf16*>(lds + L::bop);
 
   const int tid = threadIdx.x, lane = tid & 63, w8 = tid >> 6;
-  const int w = w8 & 3, role = w8 >> 2;  // role 0: Aq side, 1: Mr side
+  // role 0: Aq side, 1: Mr side. Waves w8 and w8 + 4 share a SIMD; the second takes block
+  // 3 - w8, so every SIMD holds one large and one small row block (work grows with w)
+  const int role = w8 >> 2, w = role == 0 ? w8 : 7 - w8;
   const int lr = lane & 15, lq = lane >> 4;
   const Chunk ch = item_chunk(a, blockIdx.x);
   if (ch.rows == 0) return;  // past the packed list's last chunk
@@ -1039,8 +1041,8 @@ struct LocalLds {
   static_assert(total <= 160 * 1024, "LDS");
 };
 
-// One workgroup of 8 waves per (b, hv, chunk): waves w and w + 4 own token block w and split
-// its key channels (ch = 0: the first half, 1: the second).
+// One workgroup of 8 waves per (b, hv, chunk): two waves own each token block w and split its
+// key channels (ch = 0: the first half, 1: the second).
 template <int KT>
 __global__ __launch_bounds__(64 * kLocalWaves) void local_kernel(BwdArgs a) {
   using L = LocalLds<KT>;
@@ -1058,7 +1060,9 @@ __global__ __launch_bounds__(64 * kLocalWaves) void local_kernel(BwdArgs a) {
   float* lx2 = reinterpret_cast<float*>(lds + L::lx2);
 
   const int tid = threadIdx.x, lane = tid & 63, w8 = tid >> 6;
-  const int w = w8 & 3, ch = w8 >> 2;
+  // waves w8 and w8 + 4 share a SIMD; the second takes block 3 - w8, so every SIMD holds one
+  // large and one small share of the relative-decay products
+  const int ch = w8 >> 2, w = ch == 0 ? w8 : 7 - w8;
   const int lr = lane & 15, lq = lane >> 4;
   const Chunk cr = item_chunk(a, blockIdx.x);
   if (cr.rows == 0) return;  // past the packed list's last chunk
