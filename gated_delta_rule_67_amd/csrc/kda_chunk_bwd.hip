@@ -209,15 +209,6 @@ struct QkgTile {
   }
 };
 
-template <int KT, int NTH>
-__device__ __forceinline__ void stage_qkg(bf16* sq, bf16* sk, float* G, int pk, int pg,
-                                          const bf16* qb, const bf16* kb, const bf16* gb,
-                                          unsigned qrow, unsigned grow, int nrow, int tid) {
-  QkgTile<KT, NTH> t;
-  t.load(qb, kb, gb, qrow, grow, nrow, tid);
-  t.store(sq, sk, G, pk, pg, tid);
-}
-
 // In-place inclusive cumsum of G over the 64 rows (columns < KT); tot: [4][KT] scratch.
 template <int KT, int NTH>
 __device__ __forceinline__ void cumsum_rows(float* G, int pg, float* tot, int tid) {
@@ -356,9 +347,15 @@ __global__ __launch_bounds__(512) void prep_kernel(BwdArgs a) {
   const bf16* gb = a.g + ch.row0 * grow + (size_t)hv * KT;
   unsigned char* blk = a.blocks + ch.slot * P::bytes;
 
-  stage_qkg<KT, NTH>(sq, sk, G, PK, PG, qb, kb, gb, qrow, grow, nrow, tid);
+  // q, k, g and beta all in flight before the first is stored (beta reads 0 past nrow)
+  QkgTile<KT, NTH> qkg;
+  qkg.load(qb, kb, gb, qrow, grow, nrow, tid);
+  const unsigned short braw = __builtin_amdgcn_raw_buffer_load_b16(
+      rsrc(a.beta + ch.row0 * a.HV + hv, (unsigned)nrow * a.HV * 2),
+      tid < nrow ? (unsigned)(tid * a.HV) * 2 : 0x80000000u, 0, 0);
+  qkg.store(sq, sk, G, PK, PG, tid);
   if (tid < kC) {
-    float bv = tid < nrow ? ldf(a.beta + (ch.row0 + tid) * a.HV + hv) : 0.f;
+    float bv = static_cast<float>(__builtin_bit_cast(bf16, braw));
     if ((a.flags & kFlagBetaSigmoid) && tid < nrow) bv = sigmoid_f32(bv);
     sb[tid] = bv;
     reinterpret_cast<float*>(blk + P::beta)[tid] = bv;
