@@ -18,6 +18,10 @@ prices the call's algorithmic bytes (q, k, v, g, beta read once, o and the final
 state written once) against MI355X's 8 TB/s HBM3E peak; the decode object prices
 its algorithmic bytes (state read + write, plus the token vectors) the same way.
 A 1 GiB device copy is timed in the same run as the measured HBM ceiling.
+The decode steps and the gate calls, whose kernels take 50-90 us, are issued
+through the C ABI with their outputs allocated up front (checked bit for bit
+against the Python binding first), so that the host's per-call work in the
+binding does not leave gaps between the timed kernels.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -134,6 +138,38 @@ def time_launches(fn, steps, warmup, torch):
     torch.cuda.synchronize()
     per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
     return avg, per[len(per) // 2], per[0]
+
+
+def gate_abi_calls(kda, x, A_log, dt_bias, dg, lower_bound, torch):
+    """kda_gate_fwd and kda_gate_bwd called through the C ABI with their outputs and workspace
+    allocated once. The kernels take about 50 and 90 us; the Python binding's per-call checks
+    and allocations take about as long, so timing back-to-back calls through it would measure
+    the host. Each caller returns the status; the first calls are checked here, and their
+    outputs are compared with the binding's, bit for bit."""
+    import ctypes
+    lib = kda.library()
+    B, T, HV, K = x.shape
+    dt = kda._DTYPE[x.dtype]
+    g = torch.empty_like(x)
+    dx = torch.empty_like(x)
+    dA = torch.empty((HV,), dtype=torch.float32, device=x.device)
+    db = torch.empty((HV, K), dtype=torch.float32, device=x.device)
+    ws_bytes = lib.kda_gate_bwd_workspace_size(B, T, HV, K, dt)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=x.device)
+    p = lambda t: ctypes.c_void_p(t.data_ptr())
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    fwd_args = (p(x), p(A_log), p(dt_bias), p(g), B, T, HV, K, float(lower_bound), dt, stream)
+    bwd_args = (p(x), p(A_log), p(dt_bias), p(dg), p(dx), p(dA), p(db), B, T, HV, K,
+                float(lower_bound), dt, p(ws), ws_bytes, stream)
+    fwd = lambda: lib.kda_gate_fwd(*fwd_args)
+    bwd = lambda: lib.kda_gate_bwd(*bwd_args)
+    assert fwd() == kda.KDA_OK and bwd() == kda.KDA_OK, "gate entry points failed"
+    ref_g = kda.kda_gate_fwd(x, A_log, dt_bias, lower_bound)
+    ref_dx, ref_dA, ref_db = kda.kda_gate_bwd(x, A_log, dt_bias, dg, lower_bound)
+    torch.cuda.synchronize()
+    assert torch.equal(g, ref_g) and torch.equal(dx, ref_dx), "C ABI and binding differ"
+    assert torch.equal(dA, ref_dA) and torch.equal(db, ref_db), "C ABI and binding differ"
+    return fwd, bwd
 
 
 def copy_ceiling(torch, nbytes=1 << 30, reps=5):
@@ -298,26 +334,57 @@ def main():
         state = dd["state"].clone()
         steps = c3["steps"]
         views = [[dd[n][t] for n in ("q", "k", "v", "g", "beta")] for t in range(steps)]
+        # the steps go through the C ABI with every o allocated up front: a step's kernel
+        # takes about 80 us, close to what the binding's per-call checks and allocation cost
+        # the host, so calls through the binding would leave gaps between the kernels
+        import ctypes
+        lib = kda.library()
+        outs = [torch.empty_like(dd["v"][t]) for t in range(steps)]
+        p = lambda t: ctypes.c_void_p(t.data_ptr())
+        stream = torch.cuda.current_stream()
+        sp = ctypes.c_void_p(stream.cuda_stream)
+        B3, H3, K3 = dd["q"][0].shape
+        HV3, V3 = dd["v"][0].shape[1], dd["v"][0].shape[2]
+        step_args = [tuple(p(x) for x in views[t]) + (p(state), p(outs[t]), B3, H3, HV3, K3, V3,
+                                                      float(dd["scale"]), kda._DTYPE[dd["q"].dtype], sp)
+                     for t in range(steps)]
 
         def one(t):
-            return kda.kda_recurrent_step(*views[t], state, dd["scale"])
+            return lib.kda_recurrent_step(*step_args[t])
 
-        for t in range(3):  # warm-up on a scratch copy of the state
+        # warm-up on a scratch copy of the state; the C ABI's first step matches the binding's
+        assert one(0) == kda.KDA_OK, "kda_recurrent_step failed"
+        state.copy_(dd["state"])
+        one(0)
+        s_abi, o_abi = state.clone(), outs[0].clone()
+        state.copy_(dd["state"])
+        o_ref = kda.kda_recurrent_step(*views[0], state, dd["scale"])
+        torch.cuda.synchronize()
+        assert torch.equal(o_abi, o_ref) and torch.equal(s_abi, state), "C ABI and binding differ"
+        del s_abi, o_abi, o_ref
+        for t in range(3):
             one(t)
         per_step = []
         totals = []
-        stream = torch.cuda.current_stream()
-        for _ in range(args.decode_reps):
+        for _ in range(args.decode_reps):  # 64 steps between two events
             state.copy_(dd["state"])
             torch.cuda.synchronize()
-            ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
-            ev[0].record(stream)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
             for t in range(steps):
                 one(t)
-                ev[t + 1].record(stream)
+            e1.record(stream)
             torch.cuda.synchronize()
-            per_step += [ev[t].elapsed_time(ev[t + 1]) for t in range(steps)]
-            totals.append(ev[0].elapsed_time(ev[steps]))
+            totals.append(e0.elapsed_time(e1))
+        state.copy_(dd["state"])  # per-step durations: one more pass, an event after each step
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        ev[0].record(stream)
+        for t in range(steps):
+            one(t)
+            ev[t + 1].record(stream)
+        torch.cuda.synchronize()
+        per_step = [ev[t].elapsed_time(ev[t + 1]) for t in range(steps)]
         step_ms = min(totals) / steps
         dbytes = decode_algorithmic(c3["B"], c3["H"], c3["HV"], c3["K"], c3["V"], 2)
         gbs = dbytes / (step_ms * 1e-3) / 1e9
@@ -333,7 +400,7 @@ def main():
                          "algorithmic_bytes_per_launch": dbytes,
                          "median_launch_ms": per_step[len(per_step) // 2]},
         }
-        del dd, state, views
+        del dd, state, views, outs, step_args
 
     # ---------------- chunked backward on the prefill workload
     if not args.no_backward:
@@ -402,10 +469,9 @@ def main():
         gi = gate_inputs(c["B"], c["T"], c["HV"], c["K"], "bf16", seed=4322)
         gx, gA, gb, gdg = (gi[n].to(dev) for n in ("x", "A_log", "dt_bias", "dg"))
         del gi
-        f_avg, f_med, f_min = time_launches(lambda: kda.kda_gate_fwd(gx, gA, gb, -5.0),
-                                            args.steps, args.warmup, torch)
-        r_avg, r_med, r_min = time_launches(lambda: kda.kda_gate_bwd(gx, gA, gb, gdg, -5.0),
-                                            args.steps, args.warmup, torch)
+        gate_fwd, gate_bwd = gate_abi_calls(kda, gx, gA, gb, gdg, -5.0, torch)
+        f_avg, f_med, f_min = time_launches(gate_fwd, args.steps, args.warmup, torch)
+        r_avg, r_med, r_min = time_launches(gate_bwd, args.steps, args.warmup, torch)
         # the gate fused into the prefill, against the gate then the prefill
         fused = lambda: kda.kda_chunk_fwd_gated(d["q"], d["k"], d["v"], gx, gA, gb, d["beta"], -5.0,
                                                 d["scale"], d["initial_state"])
