@@ -447,6 +447,48 @@ __global__ __launch_bounds__(512) void prep_kernel(BwdArgs a) {
       if (lq == 0) stf[(o + ii) * 65 + o + lr] = lr == ii ? 1.f : (lr < ii ? -sb[o + ii] * s : 0.f);
       wave_sync();
     }
+  } else {
+    // meanwhile the Mr-side waves write the tiles that need only q, k and G: Gam_C,
+    // K*Gam, K*Gam_C/Gam (natural), their transposes and (Q*Gam)^T
+    constexpr int NT1 = NTH / 2;
+    const int t1 = tid - NT1;
+    if (t1 < KT) reinterpret_cast<float*>(blk + P::gam)[t1] = ex(G[(kC - 1) * PG + t1]);
+    bf16* kg = reinterpret_cast<bf16*>(blk + P::kg);
+    bf16* kc = reinterpret_cast<bf16*>(blk + P::kc);
+    for (int u = t1; u < kC * KT / 8; u += NT1) {
+      const int i = u / (KT / 8), c8 = 8 * (u % (KT / 8));
+      const bf16x8 kv = ld8(sk + i * PK + c8);
+      bf16x8 x, y;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float gi = G[i * PG + c8 + e], gl = G[(kC - 1) * PG + c8 + e];
+        x[e] = static_cast<bf16>(static_cast<float>(kv[e]) * ex(gi));
+        y[e] = static_cast<bf16>(static_cast<float>(kv[e]) * ex(gl - gi));
+      }
+      st8(kg + i * KT + c8, x);
+      st8(kc + i * KT + c8, y);
+    }
+    bf16* kct = reinterpret_cast<bf16*>(blk + P::kct);
+    bf16* qgt = reinterpret_cast<bf16*>(blk + P::qgt);
+    bf16* kgt = reinterpret_cast<bf16*>(blk + P::kgt);
+    for (int u = t1; u < KT * kC / 8; u += NT1) {
+      const int c = u % KT, i8 = 8 * (u / KT);
+      bf16x8 x, y, z;
+      const float gl = G[(kC - 1) * PG + c];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int i = i8 + e;
+        const float kv = static_cast<float>(sk[i * PK + c]);
+        const float qv = static_cast<float>(sq[i * PK + c]);
+        const float gi = G[i * PG + c];
+        x[e] = static_cast<bf16>(kv * ex(gl - gi));
+        y[e] = static_cast<bf16>(qv * ex(gi));
+        z[e] = static_cast<bf16>(kv * ex(gi));
+      }
+      st8(kct + c * kC + i8, x);
+      st8(qgt + c * kC + i8, y);
+      st8(kgt + c * kC + i8, z);
+    }
   }
   __syncthreads();
   // ... then block row I, column J = I - d for d = 1, 2, 3:
@@ -481,46 +523,6 @@ __global__ __launch_bounds__(512) void prep_kernel(BwdArgs a) {
       }
       st8(tm + row * kC + c8, x);
       st8(tt + row * kC + c8, y);
-    }
-  }
-  // Gam_C; K*Gam, K*Gam_C/Gam (natural); their transposes and (Q*Gam)^T
-  if (tid < KT) reinterpret_cast<float*>(blk + P::gam)[tid] = ex(G[(kC - 1) * PG + tid]);
-  {
-    bf16* kg = reinterpret_cast<bf16*>(blk + P::kg);
-    bf16* kc = reinterpret_cast<bf16*>(blk + P::kc);
-    for (int u = tid; u < kC * KT / 8; u += NTH) {
-      const int i = u / (KT / 8), c8 = 8 * (u % (KT / 8));
-      const bf16x8 kv = ld8(sk + i * PK + c8);
-      bf16x8 x, y;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float gi = G[i * PG + c8 + e], gl = G[(kC - 1) * PG + c8 + e];
-        x[e] = static_cast<bf16>(static_cast<float>(kv[e]) * ex(gi));
-        y[e] = static_cast<bf16>(static_cast<float>(kv[e]) * ex(gl - gi));
-      }
-      st8(kg + i * KT + c8, x);
-      st8(kc + i * KT + c8, y);
-    }
-    bf16* kct = reinterpret_cast<bf16*>(blk + P::kct);
-    bf16* qgt = reinterpret_cast<bf16*>(blk + P::qgt);
-    bf16* kgt = reinterpret_cast<bf16*>(blk + P::kgt);
-    for (int u = tid; u < KT * kC / 8; u += NTH) {
-      const int c = u % KT, i8 = 8 * (u / KT);
-      bf16x8 x, y, z;
-      const float gl = G[(kC - 1) * PG + c];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int i = i8 + e;
-        const float kv = static_cast<float>(sk[i * PK + c]);
-        const float qv = static_cast<float>(sq[i * PK + c]);
-        const float gi = G[i * PG + c];
-        x[e] = static_cast<bf16>(kv * ex(gl - gi));
-        y[e] = static_cast<bf16>(qv * ex(gi));
-        z[e] = static_cast<bf16>(kv * ex(gi));
-      }
-      st8(kct + c * kC + i8, x);
-      st8(qgt + c * kC + i8, y);
-      st8(kgt + c * kC + i8, z);
     }
   }
 }
