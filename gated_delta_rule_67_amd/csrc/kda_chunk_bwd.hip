@@ -434,19 +434,28 @@ __global__ __launch_bounds__(512) void prep_kernel(BwdArgs a) {
     }
   }
   __syncthreads();
-  // T = (I + diag(beta) Mr)^-1. Diagonal 16 x 16 blocks by forward substitution (wave w owns
-  // block w; lane: column lr, partial sums over rows j = lq mod 4) ...
+  // T = (I + diag(beta) Mr)^-1. Diagonal 16 x 16 blocks by forward substitution in
+  // registers (wave w owns block w; lane: column lr, rows 4 lq + r, with its rows of
+  // diag(beta) Mr): step k takes the finished row k of T from the lanes that hold it and
+  // subtracts (beta Mr)[i][k] T[k][j] from every row i (zero for i <= k, Mr strictly lower) ...
   if (role == 0) {
     const int o = 16 * w;
-    for (int ii = 0; ii < 16; ++ii) {
-      float s = 0.f;
-      for (int jj = lr + ((lq - lr) & 3); jj < ii; jj += 4)  // jj >= lr, jj = lq mod 4
-        s += smr[(o + ii) * 65 + o + jj] * stf[(o + jj) * 65 + o + lr];
-      s += __shfl_xor(s, 16);
-      s += __shfl_xor(s, 32);
-      if (lq == 0) stf[(o + ii) * 65 + o + lr] = lr == ii ? 1.f : (lr < ii ? -sb[o + ii] * s : 0.f);
-      wave_sync();
+    float tc[4], mrow[4][16];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = o + 4 * lq + r;
+      tc[r] = 4 * lq + r == lr ? 1.f : 0.f;
+#pragma unroll
+      for (int c = 0; c < 16; ++c) mrow[r][c] = sb[i] * smr[i * 65 + o + c];
     }
+#pragma unroll
+    for (int kk = 0; kk < 15; ++kk) {
+      const float tk = __shfl(tc[kk & 3], (kk >> 2) * 16 + lr);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) tc[r] -= mrow[r][kk] * tk;
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) stf[(o + 4 * lq + r) * 65 + o + lr] = tc[r];
   } else {
     // meanwhile the Mr-side waves write the tiles that need only q, k and G: Gam_C,
     // K*Gam, K*Gam_C/Gam (natural), their transposes and (Q*Gam)^T
