@@ -1044,7 +1044,9 @@ struct LocalLds {
   static constexpr int end2 = wop + kLocalWaves * 32 * kPC * 2;
   // phase 3
   static constexpr int dgs = ph;                   // [64][PG] fp32 dG
-  static constexpr int end3 = dgs + kC * PG * 4;
+  static constexpr int dqs = dgs + kC * PG * 4;    // [64][PK] bf16 dq (per q/k head)
+  static constexpr int dks = dqs + kC * PK * 2;    // [64][PK] bf16 dk
+  static constexpr int end3 = dks + kC * PK * 2;
   static constexpr int total = end1 > end2 ? (end1 > end3 ? end1 : end3) : (end2 > end3 ? end2 : end3);
   static_assert(total <= 160 * 1024, "LDS");
 };
@@ -1315,6 +1317,8 @@ __global__ __launch_bounds__(64 * kLocalWaves) void local_kernel(BwdArgs a) {
 
   // ---------------- phase 3: output factors, dq, dk, dG, then dg by a reverse scan
   float* dgs = reinterpret_cast<float*>(lds + L::dgs);
+  bf16* sdq = reinterpret_cast<bf16*>(lds + L::dqs);
+  bf16* sdk = reinterpret_cast<bf16*>(lds + L::dks);
 #pragma unroll
   for (int cc = 0; cc < NCH; ++cc) {
     const int c = c0 + 16 * cc + lr;
@@ -1330,19 +1334,27 @@ __global__ __launch_bounds__(64 * kLocalWaves) void local_kernel(BwdArgs a) {
       const float qv = static_cast<float>(sq[i * PK + c]);
       const float kv = static_cast<float>(sk[i * PK + c]);
       dgs[i * PG + c] = qv * dq + kv * (dpos - dneg);
-      if (i < nrow) {
+      if (!a.dq32) {  // bf16 rows go out below as 16-byte pieces
+        sdq[i * PK + c] = static_cast<bf16>(dq);
+        sdk[i * PK + c] = static_cast<bf16>(dk);
+      } else if (i < nrow) {
         const size_t t = row0 + i;
-        if (!a.dq32) {
-          a.dq[(t * a.H + hh) * KT + c] = static_cast<bf16>(dq);
-          a.dk[(t * a.H + hh) * KT + c] = static_cast<bf16>(dk);
-        } else {
-          a.dq32[(t * a.HV + hv) * KT + c] = dq;
-          a.dk32[(t * a.HV + hv) * KT + c] = dk;
-        }
+        a.dq32[(t * a.HV + hv) * KT + c] = dq;
+        a.dk32[(t * a.HV + hv) * KT + c] = dk;
       }
     }
   }
   __syncthreads();
+  if (!a.dq32) {
+    for (int u = tid; u < kC * (KT / 8); u += NTH) {
+      const int i = u / (KT / 8), c8 = 8 * (u % (KT / 8));
+      if (i < nrow) {
+        const size_t o = ((row0 + i) * a.H + hh) * KT + c8;
+        st8(a.dq + o, ld8(sdq + i * PK + c8));
+        st8(a.dk + o, ld8(sdk + i * PK + c8));
+      }
+    }
+  }
   // dg = reverse cumsum of dG over the chunk, in four 16-row segments: segment sums first,
   // then each segment's scan starts from the sums of the segments after it
   static_assert(4 * KT <= NTH, "one thread per segment and channel");
