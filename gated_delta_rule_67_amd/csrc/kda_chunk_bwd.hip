@@ -822,8 +822,9 @@ __global__ __launch_bounds__(64 * NW) void rev_sweep_kernel(BwdArgs a) {
       p4[e] = ld8(blk + P::tt + 16 * (tid + NTH * e));
       p5[e] = ld8(blk + P::aqt + 16 * (tid + NTH * e));
     }
-    if (tid < KT) pgam = reinterpret_cast<const float*>(blk + P::gam)[tid];
-    if (tid < kC) pbt = reinterpret_cast<const float*>(blk + P::beta)[tid];
+    // unconditional (clamped) loads: in branches the compiler sank them below the chunk's stores
+    pgam = reinterpret_cast<const float*>(blk + P::gam)[min(tid, KT - 1)];
+    pbt = reinterpret_cast<const float*>(blk + P::beta)[min(tid, kC - 1)];
     size_t row0;
     int nrow;
     seq_rows(a, sq_, b, n, row0, nrow);
