@@ -286,7 +286,7 @@ int kda_chunk_bwd_ex(const void* q, const void* k, const void* v, const void* g,
   if (!workspace || workspace_bytes < need) return KDA_ERR_INVALID;
   if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0) return KDA_ERR_INVALID;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g) || !aligned16(dout) ||
-      !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+      !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(dg))
     return KDA_ERR_UNSUPPORTED;
   const hipError_t e = kda::launch_chunk_bwd(q, k, v, g, beta, nullptr, initial_state, dout, dht,
                                              dq, dk, dv, dg, dbeta, dh0, B, T, H, HV, K, V, scale,
@@ -330,7 +330,7 @@ int kda_chunk_bwd_varlen(const void* q, const void* k, const void* v, const void
   if (!workspace || workspace_bytes < need) return KDA_ERR_INVALID;
   if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0) return KDA_ERR_INVALID;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g) || !aligned16(dout) ||
-      !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+      !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(dg))
     return KDA_ERR_UNSUPPORTED;
   const hipError_t e = kda::launch_chunk_bwd(q, k, v, g, beta, cu_seqlens, initial_state, dout,
                                              dht, dq, dk, dv, dg, dbeta, dh0, N, T, H, HV, K, V,

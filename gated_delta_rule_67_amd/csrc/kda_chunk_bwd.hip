@@ -1360,6 +1360,7 @@ __global__ __launch_bounds__(64 * kLocalWaves) void local_kernel(BwdArgs a) {
   // then each segment's scan starts from the sums of the segments after it
   static_assert(4 * KT <= NTH, "one thread per segment and channel");
   float* segs = reinterpret_cast<float*>(lds + L::tot);  // [4][KT]
+  bf16* sdg = sdq;  // dg in bf16; the dq rows were written out before the barrier below
   const int sc = tid % KT, sp = tid / KT;
   if (tid < 4 * KT) {
     float bsum = 0.f;
@@ -1375,8 +1376,13 @@ __global__ __launch_bounds__(64 * kLocalWaves) void local_kernel(BwdArgs a) {
     for (int i = 15; i >= 0; --i) {
       const int row = 16 * sp + i;
       run += dgs[row * PG + sc];
-      if (row < nrow) a.dg[((row0 + row) * a.HV + hv) * KT + sc] = static_cast<bf16>(run);
+      sdg[row * PK + sc] = static_cast<bf16>(run);
     }
+  }
+  __syncthreads();
+  for (int u = tid; u < kC * (KT / 8); u += NTH) {  // dg rows as 16-byte pieces
+    const int i = u / (KT / 8), c8 = 8 * (u % (KT / 8));
+    if (i < nrow) st8(a.dg + ((row0 + i) * a.HV + hv) * KT + c8, ld8(sdg + i * PK + c8));
   }
   if (ch == 0) {  // dv = beta Ut, this block's rows from the A fragments the wave holds
     const int i = rw + lr;

@@ -171,7 +171,7 @@ int kda_chunk_fwd_varlen(const void* q, const void* k, const void* v, const void
  * Outputs must not overlap inputs, the workspace or each other.
  *
  * Constraints: as for kda_chunk_fwd, and: bf16 only; K in {32, 64, 128}; V % 16 == 0 and
- * V <= 128; q, k, v, g, dout, dq, dk, dv 16-byte aligned (else KDA_ERR_UNSUPPORTED).
+ * V <= 128; q, k, v, g, dout, dq, dk, dv, dg 16-byte aligned (else KDA_ERR_UNSUPPORTED).
  */
 size_t kda_chunk_bwd_workspace_size(int B, int T, int H, int HV, int K, int V,
                                     int chunk_size, int dtype);

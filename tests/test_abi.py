@@ -205,6 +205,7 @@ def _bwd(lib, **kw):
     (dict(q=ctypes.c_void_p(0x1008)), kda.KDA_ERR_UNSUPPORTED),  # not 16-byte aligned
     (dict(dq=ctypes.c_void_p(0x1008)), kda.KDA_ERR_UNSUPPORTED),  # dq, dk: 16-byte row stores
     (dict(dk=ctypes.c_void_p(0x1002)), kda.KDA_ERR_UNSUPPORTED),
+    (dict(dg=ctypes.c_void_p(0x1004)), kda.KDA_ERR_UNSUPPORTED),
 ])
 def test_chunk_bwd_rejects_invalid_arguments(lib, bad, rc):
     assert _bwd(lib, **bad) == rc
