@@ -51,36 +51,37 @@ __device__ __forceinline__ float sigmoid_f32(float x) { return 1.f / (1.f + fast
 constexpr unsigned kFlagGate = 4u;  // internal: g holds the gate input (gated entry points)
 constexpr float kLn2 = 0.6931471805599453f;
 
-// log(1 + e) for e in [0, 1] on the transcendental unit, with Goldberg's correction
-// log1p(e) = log(u) * e / (u - 1), u = fl(1 + e): it cancels the rounding of 1 + e, so the
-// result keeps a few-ulp relative accuracy however small e is (u == 1: log1p(e) = e).
-__device__ __forceinline__ float log1p_unit(float e) {
+// log(1 + e) for e in [0, 1] on the transcendental unit, given r = 1 / u for u = fl(1 + e).
+// With d = (u - 1) - e the rounding of 1 + e (computed exactly: u - 1 is exact, and d is a
+// difference of two floats that share their upper bits), log(1 + e) = log(u - d) =
+// log(u) - d / u + O(d^2), and d^2 < 2^-48: the result keeps the accuracy of log(u) however
+// small e is (u == 1: d = -e and the result is e). The logistic reuses r.
+__device__ __forceinline__ float log1p_unit(float e, float r) {
 #pragma clang fp contract(off)
   const float u = 1.f + e;
-  const float d = u - 1.f;
-  return d == 0.f ? e : __builtin_amdgcn_logf(u) * kLn2 * (e * __builtin_amdgcn_rcpf(d));
+  return __builtin_amdgcn_logf(u) * kLn2 - ((u - 1.f) - e) * r;
 }
 
 // softplus(z) = max(z, 0) + log1p(e^-|z|); relative error ~1e-6 for z > -87, where e^z
 // leaves the float32 normal range (below it the result flushes to 0, an absolute error
-// under 1e-37). Also returns e = e^-|z|, which the logistic reuses.
-__device__ __forceinline__ float softplus_f32(float z, float& e) {
+// under 1e-37). Also returns e = e^-|z| and r = 1 / (1 + e), which the logistic reuses.
+__device__ __forceinline__ float softplus_f32(float z, float& e, float& r) {
 #pragma clang fp contract(off)
   e = fast_exp2(-fabsf(z) * kLog2e);
-  return fmaxf(z, 0.f) + log1p_unit(e);
+  r = __builtin_amdgcn_rcpf(1.f + e);
+  return fmaxf(z, 0.f) + log1p_unit(e, r);
 }
 
-// logistic(z) from e = e^-|z|.
-__device__ __forceinline__ float logistic_from(float z, float e) {
-  const float r = __builtin_amdgcn_rcpf(1.f + e);
+// logistic(z) from e = e^-|z| and r = 1 / (1 + e).
+__device__ __forceinline__ float logistic_from(float z, float e, float r) {
   return z >= 0.f ? r : e * r;
 }
 
 // The gate's value for input x, channel bias and neg_rate = -exp(A_log).
 __device__ __forceinline__ float gate_value(float x, float bias, float neg_rate, float lower_bound) {
 #pragma clang fp contract(off)
-  float e;
-  return fmaxf(neg_rate * softplus_f32(x + bias, e), lower_bound);
+  float e, r;
+  return fmaxf(neg_rate * softplus_f32(x + bias, e, r), lower_bound);
 }
 
 // Arguments of one chunked-prefill launch (validated by the C ABI).

@@ -144,10 +144,10 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
         const float z = to_f32(xv[e]) + bias[e];
-        float ez;
-        const float gs = na * softplus_f32(z, ez);
+        float ez, rz;
+        const float gs = na * softplus_f32(z, ez, rz);
         const float d = gs >= lower_bound ? to_f32(gv[e]) : 0.f;
-        const float d_x = d * na * logistic_from(z, ez);
+        const float d_x = d * na * logistic_from(z, ez, rz);
         dv[e] = from_f32<T>(d_x);
         sb[e] += d_x;
         sa += d * gs;
