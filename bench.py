@@ -274,7 +274,7 @@ def main():
     o, s = prefill()
     torch.cuda.synchronize()
     assert torch.isfinite(o.float()).all() and torch.isfinite(s).all(), "non-finite prefill output"
-    checked = (o.cpu(), s.cpu()) if not args.no_cpu_baseline else None  # judged by the oracle leg
+    checked = (o.cpu(), s.cpu()) if not args.no_cpu_baseline else None  # checked by the oracle leg
     log(f"bench: timing {args.steps} prefill steps after {args.warmup} warmup")
     avg_ms, med_ms, min_ms = time_launches(prefill, args.steps, args.warmup, torch)
     tokens = c["B"] * c["T"]
