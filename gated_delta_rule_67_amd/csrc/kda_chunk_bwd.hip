@@ -1035,7 +1035,8 @@ struct LocalLds {
   // phase 1
   static constexpr int uu = ph;                    // [64][PV] U
   static constexpr int hs = uu + kC * PV * 2;      // [KT][PV] h, then dS
-  static constexpr int end1 = hs + KT * PV * 2;
+  static constexpr int lxp = hs + KT * PV * 2;     // [KT][16] fp32 rowsum(dS h) pieces
+  static constexpr int end1 = lxp + KT * 16 * 4;
   // phase 2
   static constexpr int f = ph;                     // [64][kPC] F
   static constexpr int ft = f + kC * kPC * 2;      // [64][kPC] F^T
@@ -1119,7 +1120,9 @@ __global__ __launch_bounds__(64 * kLocalWaves) void local_kernel(BwdArgs a) {
   QkgTile<KT, NTH> qkg;
   qkg.load(qb, kb, gb, qrow, grow, nrow, tid);
   constexpr int NU = (kC * 16 + NTH - 1) / NTH, NH = (KT * 16 + NTH - 1) / NTH;
-  const int per = V / 8;
+  const int per = V / 8;  // 16-byte pieces per row of U, h, dS (V <= 128: at most 16)
+  const bool pow2 = (per & (per - 1)) == 0;
+  float* lxp = reinterpret_cast<float*>(lds + L::lxp);
   bf16x8 xu[NU], xh[NH], xds[NH];
   {
     const auto ru = rsrc(a.u + trow * V, (unsigned)kC * V * 2);
@@ -1219,8 +1222,8 @@ __global__ __launch_bounds__(64 * kLocalWaves) void local_kernel(BwdArgs a) {
   }
   {
     // rowsum(dS * h): the per pieces of a row sit on per consecutive lanes; when per is a
-    // power of two they are summed by shuffles and stored once, else added atomically
-    const bool pow2 = (per & (per - 1)) == 0;
+    // power of two they are summed by shuffles and stored once, else each piece is kept in
+    // LDS and the row is summed below in a fixed order
     __syncthreads();  // every wave is done with h
 #pragma unroll
     for (int e = 0; e < NH; ++e) {
@@ -1236,12 +1239,17 @@ __global__ __launch_bounds__(64 * kLocalWaves) void local_kernel(BwdArgs a) {
         for (int o = 1; o < per; o <<= 1) sdot += __shfl_xor(sdot, o);
         if (in && c8 == 0) lx2[r] = sdot;
       } else if (in) {
-        atomicAdd(lx2 + r, sdot);
+        lxp[r * 16 + c8 / 8] = sdot;
       }
       if (in) st8(s_hs + r * PV + c8, xds[e]);
     }
   }
   __syncthreads();
+  if (!pow2 && tid < KT) {
+    float sum = 0.f;
+    for (int p = 0; p < per; ++p) sum += lxp[tid * 16 + p];
+    lx2[tid] = sum;
+  }
   bf16x8 fuu[4];  // this block's rows of U as A fragments
 #pragma unroll
   for (int x = 0; x < 4; ++x) {
