@@ -150,7 +150,9 @@ size_t prep_block_bytes(int K) {
 }
 
 __device__ __forceinline__ float ldf(const bf16* p) { return static_cast<float>(*p); }
-__device__ __forceinline__ float ex(float x) { return fast_exp2(x * kLog2e); }
+// e^x for x a difference of in-chunk cumulative gates; G is staged in log2 units (g log2 e, a
+// linear scaling that the cumsum keeps), so this is 2^x
+__device__ __forceinline__ float ex(float x) { return fast_exp2(x); }
 __device__ __forceinline__ bf16x8 ld8(const void* p) { return *reinterpret_cast<const bf16x8*>(p); }
 __device__ __forceinline__ void st8(void* p, bf16x8 x) { *reinterpret_cast<bf16x8*>(p) = x; }
 __device__ __forceinline__ void st4(void* p, f32x4 x) {
@@ -174,7 +176,7 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// One chunk's q, k (bf16, [64][pk]) and g (as fp32 into G, [64][pg]) into LDS; rows past
+// One chunk's q, k (bf16, [64][pk]) and g (as fp32 g log2 e into G, [64][pg]) into LDS; rows past
 // nrow read as zeros. QkgTile::load issues every load of this thread's pieces, QkgTile::store
 // writes them to LDS, so a caller can issue more loads in between. NTH threads.
 template <int KT, int NTH>
@@ -203,7 +205,7 @@ struct QkgTile {
         st8(sq + r * pk + c8, xq[e]);
         st8(sk + r * pk + c8, xk[e]);
 #pragma unroll
-        for (int x = 0; x < 8; ++x) G[r * pg + c8 + x] = static_cast<float>(xg[e][x]);
+        for (int x = 0; x < 8; ++x) G[r * pg + c8 + x] = static_cast<float>(xg[e][x]) * kLog2e;
       }
     }
   }
