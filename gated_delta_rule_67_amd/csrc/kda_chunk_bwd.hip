@@ -34,6 +34,9 @@
 #include "kda_varlen.h"
 
 namespace kda {
+
+int device_cu_count();
+
 namespace bwd {
 
 constexpr int kC = 64;
@@ -340,21 +343,31 @@ __global__ __launch_bounds__(512) void prep_kernel(BwdArgs a) {
   // 3 - w8, so every SIMD holds one large and one small row block (work grows with w)
   const int role = w8 >> 2, w = role == 0 ? w8 : 7 - w8;
   const int lr = lane & 15, lq = lane >> 4;
-  const Chunk ch = item_chunk(a, blockIdx.x);
-  if (ch.rows == 0) return;  // past the packed list's last chunk
-  const int hv = ch.hv, hh = hv / (a.HV / a.H), nrow = ch.rows;
   const unsigned qrow = (unsigned)(a.H * KT), grow = (unsigned)(a.HV * KT);
-  const bf16* qb = a.q + ch.row0 * qrow + (size_t)hh * KT;
-  const bf16* kb = a.k + ch.row0 * qrow + (size_t)hh * KT;
-  const bf16* gb = a.g + ch.row0 * grow + (size_t)hv * KT;
+  const int items = a.ctab ? a.HV * a.NC : a.B * a.HV * a.NT;
+  // K = 128 (149 KB of LDS, one workgroup per CU) runs persistent: the workgroup walks items
+  // blockIdx.x, + gridDim.x, ... and loads the next item's q, k, g and beta while the current
+  // one computes. Smaller K fit two workgroups per CU and launch one per item, without the
+  // cross-item prefetch (whose registers would cost them that second workgroup). Every
+  // branch below is uniform.
+  constexpr bool kPersist = KT == 128;
+  QkgTile<KT, NTH> qkg;
+  unsigned short braw = 0;
+  auto issue = [&](int item) {  // q, k, g and beta of an item (beta reads 0 past its rows)
+    const Chunk c = item_chunk(a, item);
+    if (c.rows == 0) return;
+    const int chh = c.hv / (a.HV / a.H);
+    qkg.load(a.q + c.row0 * qrow + (size_t)chh * KT, a.k + c.row0 * qrow + (size_t)chh * KT,
+             a.g + c.row0 * grow + (size_t)c.hv * KT, qrow, grow, c.rows, tid);
+    braw = __builtin_amdgcn_raw_buffer_load_b16(
+        rsrc(a.beta + c.row0 * a.HV + c.hv, (unsigned)c.rows * a.HV * 2),
+        tid < c.rows ? (unsigned)(tid * a.HV) * 2 : 0x80000000u, 0, 0);
+  };
+  // one item's work; q, k, g and beta are in qkg / braw when it starts
+  auto body = [&](const Chunk& ch, int item) {
+  const int nrow = ch.rows;
   unsigned char* blk = a.blocks + ch.slot * P::bytes;
 
-  // q, k, g and beta all in flight before the first is stored (beta reads 0 past nrow)
-  QkgTile<KT, NTH> qkg;
-  qkg.load(qb, kb, gb, qrow, grow, nrow, tid);
-  const unsigned short braw = __builtin_amdgcn_raw_buffer_load_b16(
-      rsrc(a.beta + ch.row0 * a.HV + hv, (unsigned)nrow * a.HV * 2),
-      tid < nrow ? (unsigned)(tid * a.HV) * 2 : 0x80000000u, 0, 0);
   qkg.store(sq, sk, G, PK, PG, tid);
   if (tid < kC) {
     float bv = static_cast<float>(__builtin_bit_cast(bf16, braw));
@@ -362,6 +375,8 @@ __global__ __launch_bounds__(512) void prep_kernel(BwdArgs a) {
     sb[tid] = bv;
     reinterpret_cast<float*>(blk + P::beta)[tid] = bv;
   }
+  if constexpr (kPersist)  // its registers are free again: the next item's loads go out
+    if (item + (int)gridDim.x < items) issue(item + gridDim.x);
   cumsum_rows<KT, NTH>(G, PG, reinterpret_cast<float*>(lds + L::tot), tid);  // includes barriers
   if (a.flags & kFlagQkL2norm) {
     l2norm_rows<KT, NTH>(sq, sk, PK, tid);
@@ -535,6 +550,24 @@ __global__ __launch_bounds__(512) void prep_kernel(BwdArgs a) {
       st8(tm + row * kC + c8, x);
       st8(tt + row * kC + c8, y);
     }
+  }
+  };
+  if constexpr (kPersist) {
+    if ((int)blockIdx.x < items) issue(blockIdx.x);
+    for (int item = blockIdx.x; item < items; item += gridDim.x) {
+      const Chunk ch = item_chunk(a, item);
+      if (ch.rows == 0) {  // past the packed list's last chunk
+        if (item + (int)gridDim.x < items) issue(item + gridDim.x);
+        continue;
+      }
+      body(ch, item);
+      __syncthreads();  // the next item's staging overwrites this item's LDS
+    }
+  } else {
+    const Chunk ch = item_chunk(a, blockIdx.x);
+    if (ch.rows == 0) return;  // past the packed list's last chunk
+    issue(blockIdx.x);
+    body(ch, blockIdx.x);
   }
 }
 
@@ -1522,7 +1555,9 @@ Layout varlen_layout(int nseq, int T, int H, int HV, int K, int V, unsigned flag
 template <int KT>
 hipError_t launch_cfg(BwdArgs a, hipStream_t stream) {
   const int items = a.ctab ? a.HV * a.NC : a.B * a.HV * a.NT;
-  hipLaunchKernelGGL((prep_kernel<KT>), dim3(items), dim3(512), 0, stream, a);
+  const int cus = device_cu_count();  // K = 128: persistent, one workgroup per CU (its LDS)
+  const int pgrid = (KT == 128 && items > cus) ? cus : items;
+  hipLaunchKernelGGL((prep_kernel<KT>), dim3(pgrid), dim3(512), 0, stream, a);
   constexpr int NW = 2;
   const int sweeps = a.B * a.HV * ((a.V + 16 * NW - 1) / (16 * NW));
   hipLaunchKernelGGL((fwd_sweep_kernel<KT, NW>), dim3(sweeps), dim3(64 * NW), 0, stream, a);
