@@ -20,6 +20,9 @@ Entry points (same names as the C ABI):
   with that gate applied inside the kernels (the gate's input in place of g)
 * ``kda_chunk_fwd_segmented(q, k, v, g, beta, segments, ...)``: the prefill over segments
   of each sequence composed by a scan (for few heads)
+* ``kda_chunk_fwd_noalloc(q, k, v, g, beta, o, final_state=None, ...)``: the prefill into
+  caller-provided outputs, with the workspace taken from the library's fixed per-device
+  scratch array (no device allocation anywhere in the call)
 
 ``qk_l2norm`` / ``beta_sigmoid`` ask the kernels to L2-normalise q and k and to
 apply the sigmoid to beta (``kda_chunk_fwd_ex`` / ``kda_recurrent_step_ex``).
@@ -35,11 +38,12 @@ __all__ = ["kda_chunk_fwd", "kda_chunk_fwd_varlen", "kda_chunk_bwd",
            "kda_chunk_bwd_varlen", "kda_recurrent_step",
            "kda_recurrent_step_slots", "kda_gate_fwd", "kda_gate_bwd",
            "kda_chunk_fwd_gated", "kda_recurrent_step_gated", "kda_chunk_fwd_segmented",
-           "library", "library_path", "status_string",
-           "KDA_OK", "KDA_ERR_INVALID", "KDA_ERR_UNSUPPORTED", "KDA_ERR_HIP",
+           "kda_chunk_fwd_noalloc", "NOALLOC_SCRATCH_BYTES", "library", "library_path", "status_string",
+           "KDA_OK", "KDA_ERR_INVALID", "KDA_ERR_UNSUPPORTED", "KDA_ERR_HIP", "KDA_ERR_SCRATCH",
            "KDA_FLAG_QK_L2NORM", "KDA_FLAG_BETA_SIGMOID"]
 
-KDA_OK, KDA_ERR_INVALID, KDA_ERR_UNSUPPORTED, KDA_ERR_HIP = 0, -1, -2, -3
+KDA_OK, KDA_ERR_INVALID, KDA_ERR_UNSUPPORTED, KDA_ERR_HIP, KDA_ERR_SCRATCH = 0, -1, -2, -3, -4
+NOALLOC_SCRATCH_BYTES = 64 << 20  # KDA_NOALLOC_SCRATCH_BYTES
 KDA_FLAG_QK_L2NORM, KDA_FLAG_BETA_SIGMOID = 1, 2
 _DTYPE = {torch.float32: 0, torch.bfloat16: 1}
 
@@ -102,6 +106,8 @@ def library():
     lib.kda_chunk_fwd_segmented.restype = i
     lib.kda_chunk_fwd_segmented_workspace_size.argtypes = [i] * 8
     lib.kda_chunk_fwd_segmented_workspace_size.restype = sz
+    lib.kda_chunk_fwd_noalloc.argtypes = [vp] * 8 + [i] * 6 + [f, i, i, ctypes.c_uint, vp]
+    lib.kda_chunk_fwd_noalloc.restype = i
     lib.kda_status_string.argtypes = [i]
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_version.argtypes = []
@@ -549,3 +555,37 @@ def kda_chunk_fwd_segmented(q, k, v, g, beta, segments, scale=None, initial_stat
                                          ctypes.c_void_p(stream))
     _check(rc)
     return o, final
+
+
+def kda_chunk_fwd_noalloc(q, k, v, g, beta, o, final_state=None, scale=None, initial_state=None,
+                          chunk_size=64, qk_l2norm=False, beta_sigmoid=False):
+    """kda_chunk_fwd writing into the caller's o [B,T,HV,V] (and final_state [B,HV,K,V]
+    float32, or None), with no device allocation: the library's fixed per-device scratch
+    array serves as the workspace (calls overlapping on one GPU race on it). Raises on
+    KDA_ERR_SCRATCH when the shape needs more than NOALLOC_SCRATCH_BYTES. Returns o."""
+    _require(q.is_cuda, "inputs must be on a GPU")
+    dev, dt = q.device, q.dtype
+    _require(dt in _DTYPE, f"unsupported dtype {dt}")
+    B, T, H, K = q.shape
+    HV, V = v.shape[2], v.shape[3]
+    _require(k.shape == q.shape, "k must match q")
+    _require(tuple(v.shape[:2]) == (B, T), "v must be [B, T, HV, V]")
+    _require(tuple(g.shape) == (B, T, HV, K), "g must be [B, T, HV, K]")
+    _require(tuple(beta.shape) == (B, T, HV), "beta must be [B, T, HV]")
+    _require(tuple(o.shape) == (B, T, HV, V), "o must be [B, T, HV, V]")
+    _check_tensors([("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("o", o)], dt, dev)
+    for name, st in (("initial_state", initial_state), ("final_state", final_state)):
+        if st is not None:
+            _require(tuple(st.shape) == (B, HV, K, V), f"{name} must be [B, HV, K, V]")
+            _check_tensors([(name, st)], torch.float32, dev)
+    if scale is None:
+        scale = 1.0 / math.sqrt(K)
+    lib = library()
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        rc = lib.kda_chunk_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                       _ptr(initial_state), _ptr(final_state), _ptr(o), B, T, H,
+                                       HV, K, V, float(scale), int(chunk_size), _DTYPE[dt],
+                                       _flags(qk_l2norm, beta_sigmoid), ctypes.c_void_p(stream))
+    _check(rc)
+    return o

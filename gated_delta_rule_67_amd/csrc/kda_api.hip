@@ -3,6 +3,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "../../include/kda.h"
 #include "kda_device.h"
 
@@ -13,7 +15,7 @@ hipError_t launch_decode(const void*, const void*, const void*, const void*, con
                          const float*, const float*, float, hipStream_t);
 hipError_t launch_prefill(const void*, const void*, const void*, const void*, const void*,
                           const float*, float*, void*, int, int, int, int, int, int, float, bool,
-                          void*, unsigned, const float*, const float*, float, hipStream_t);
+                          void*, unsigned, const float*, const float*, float, int, hipStream_t);
 size_t wy_workspace_bytes(int B, int T, int HV, int K);
 size_t bwd_workspace_bytes(int B, int T, int H, int HV, int K, int V, unsigned flags);
 size_t bwd_varlen_workspace_bytes(int nseq, int T, int H, int HV, int K, int V, unsigned flags);
@@ -90,6 +92,9 @@ const char* kda_status_string(int status) {
     case KDA_ERR_INVALID: return "KDA_ERR_INVALID: invalid argument (null pointer, dims, chunk size or scale)";
     case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED: valid shape with no kernel in this library";
     case KDA_ERR_HIP: return "KDA_ERR_HIP: the HIP runtime reported an error at launch";
+    case KDA_ERR_SCRATCH:
+      return "KDA_ERR_SCRATCH: the call needs more scratch than the allocation-free entry point's "
+             "fixed per-device array holds (KDA_NOALLOC_SCRATCH_BYTES)";
     default: return "KDA: unknown status";
   }
 }
@@ -142,11 +147,19 @@ int kda_chunk_fwd_segmented(const void* q, const void* k, const void* v, const v
   return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
+// Workspace of the plain two-kernel path (no segments) for these arguments, or 0 where the
+// call takes a path without workspace.
+static size_t plain_workspace_size(int B, int T, int H, int HV, int K, int V, int dtype) {
+  if (!positive(T) || check_common(B, H, HV, K, V, 1.f, dtype) != KDA_OK) return 0;
+  if (dtype != KDA_DTYPE_BF16 || K % 8 != 0 || V % 8 != 0) return 0;
+  return kda::wy_workspace_bytes(B, T, HV, K);
+}
+
 static int chunk_fwd(const void* q, const void* k, const void* v, const void* g, const void* beta,
                      const float* initial_state, float* final_state, void* o, int B, int T, int H,
                      int HV, int K, int V, float scale, int chunk_size, int dtype, void* workspace,
                      size_t workspace_bytes, unsigned flags, const float* A_log,
-                     const float* dt_bias, float gate_lb, void* stream) {
+                     const float* dt_bias, float gate_lb, int segments, void* stream) {
   if (!q || !k || !v || !g || !beta || !o) return KDA_ERR_INVALID;
   if (flags & ~(unsigned)(KDA_FLAG_QK_L2NORM | KDA_FLAG_BETA_SIGMOID | kda::kFlagGate))
     return KDA_ERR_INVALID;
@@ -160,8 +173,10 @@ static int chunk_fwd(const void* q, const void* k, const void* v, const void* g,
   if (dtype == KDA_DTYPE_F32 && K > 64) return KDA_ERR_UNSUPPORTED;
   if ((int64_t)B * HV * ((V + 15) / 16) > INT32_MAX) return KDA_ERR_UNSUPPORTED;
   if ((int64_t)B * HV * ((T + 63) / 64) > INT32_MAX) return KDA_ERR_UNSUPPORTED;
-  // A workspace, when given, must hold what kda_chunk_fwd_workspace_size asks for.
-  const size_t need = kda_chunk_fwd_workspace_size(B, T, H, HV, K, V, chunk_size, dtype);
+  // A workspace, when given, must hold what kda_chunk_fwd_workspace_size asks for (segments
+  // == 1: what the plain two-kernel path needs).
+  const size_t need = segments == 1 ? plain_workspace_size(B, T, H, HV, K, V, dtype)
+                                    : kda_chunk_fwd_workspace_size(B, T, H, HV, K, V, chunk_size, dtype);
   if (workspace && workspace_bytes < need) return KDA_ERR_INVALID;
   if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0) return KDA_ERR_INVALID;
   // The input transforms and the gate are applied by the factors kernel of the two-kernel
@@ -170,7 +185,7 @@ static int chunk_fwd(const void* q, const void* k, const void* v, const void* g,
   const hipError_t e = kda::launch_prefill(q, k, v, g, beta, initial_state, final_state, o, B, T,
                                            H, HV, K, V, scale, dtype == KDA_DTYPE_BF16,
                                            need ? workspace : nullptr, flags, A_log, dt_bias,
-                                           gate_lb, static_cast<hipStream_t>(stream));
+                                           gate_lb, segments, static_cast<hipStream_t>(stream));
   if (e == hipErrorNotSupported) return KDA_ERR_UNSUPPORTED;  // flags, unaligned tensors
   return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
@@ -182,7 +197,7 @@ int kda_chunk_fwd_ex(const void* q, const void* k, const void* v, const void* g,
                      void* stream) {
   if (flags & ~(unsigned)(KDA_FLAG_QK_L2NORM | KDA_FLAG_BETA_SIGMOID)) return KDA_ERR_INVALID;
   return chunk_fwd(q, k, v, g, beta, initial_state, final_state, o, B, T, H, HV, K, V, scale,
-                   chunk_size, dtype, workspace, workspace_bytes, flags, nullptr, nullptr, 0.f,
+                   chunk_size, dtype, workspace, workspace_bytes, flags, nullptr, nullptr, 0.f, 0,
                    stream);
 }
 
@@ -206,7 +221,7 @@ int kda_chunk_fwd_gated(const void* q, const void* k, const void* v, const void*
   if (rc != KDA_OK) return rc;
   return chunk_fwd(q, k, v, gate_x, beta, initial_state, final_state, o, B, T, H, HV, K, V, scale,
                    chunk_size, dtype, workspace, workspace_bytes, flags | kda::kFlagGate, A_log,
-                   dt_bias, lower_bound, stream);
+                   dt_bias, lower_bound, 0, stream);
 }
 
 // Packed sequences take the two-kernel path only: bf16, K % 8 == 0, V % 8 == 0.
@@ -435,6 +450,60 @@ int kda_recurrent_step(const void* q, const void* k, const void* v, const void* 
                        int V, float scale, int dtype, void* stream) {
   return kda_recurrent_step_ex(q, k, v, g, beta, state, o, B, H, HV, K, V, scale, dtype, 0u,
                                stream);
+}
+
+// ---- Allocation-free prefill. `scratch` stands in for the caller's workspace: one fixed
+// array per GPU (the code object holds it on every device it is loaded on, until the process
+// ends). Host code never uses the name `scratch` as an address: its device address, which
+// differs per device, is taken once per device with hipGetSymbolAddress (that device
+// current) and kept in scratch_addr.
+static __device__ __align__(256) unsigned char scratch[KDA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void*> scratch_addr[kMaxDevices];
+
+// The scratch array's address on the current device (KDA_OK), or the status to return.
+int current_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return KDA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return KDA_ERR_UNSUPPORTED;
+  void* p = scratch_addr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return KDA_ERR_HIP;
+    scratch_addr[dev].store(p, std::memory_order_release);  // two first calls store the same value
+  }
+  *out = p;
+  return KDA_OK;
+}
+}  // namespace
+
+int kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const void* g,
+                          const void* beta, const float* initial_state, float* final_state,
+                          void* o, int B, int T, int H, int HV, int K, int V, float scale,
+                          int chunk_size, int dtype, unsigned flags, void* stream) {
+  if (!q || !k || !v || !g || !beta || !o) return KDA_ERR_INVALID;
+  if (flags & ~(unsigned)(KDA_FLAG_QK_L2NORM | KDA_FLAG_BETA_SIGMOID)) return KDA_ERR_INVALID;
+  if (!positive(T) || !valid_chunk(T, chunk_size)) return KDA_ERR_INVALID;
+  const int rc = check_common(B, H, HV, K, V, scale, dtype);
+  if (rc != KDA_OK) return rc;
+  // The path kda_chunk_fwd_ex would take with a workspace; when its workspace (the segmented
+  // route's, with few heads) exceeds the array, the plain two-kernel path, if that fits.
+  size_t need = kda_chunk_fwd_workspace_size(B, T, H, HV, K, V, chunk_size, dtype);
+  int segments = 0;
+  if (need > KDA_NOALLOC_SCRATCH_BYTES) {
+    need = plain_workspace_size(B, T, H, HV, K, V, dtype);
+    segments = 1;
+    if (need > KDA_NOALLOC_SCRATCH_BYTES) return KDA_ERR_SCRATCH;
+  }
+  void* ws = nullptr;
+  if (need > 0) {  // paths without workspace use no scratch either
+    const int sc = current_scratch(&ws);
+    if (sc != KDA_OK) return sc;
+  }
+  return chunk_fwd(q, k, v, g, beta, initial_state, final_state, o, B, T, H, HV, K, V, scale,
+                   chunk_size, dtype, ws, ws ? (size_t)KDA_NOALLOC_SCRATCH_BYTES : 0, flags,
+                   nullptr, nullptr, 0.f, segments, stream);
 }
 
 }  // extern "C"

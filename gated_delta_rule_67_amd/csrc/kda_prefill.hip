@@ -482,7 +482,7 @@ hipError_t launch_prefill(const void* q, const void* k, const void* v, const voi
                           const void* beta, const float* s0, float* sT, void* o, int B, int T,
                           int H, int HV, int K, int V, float scale, bool bf16_inputs,
                           void* workspace, unsigned flags, const float* A_log,
-                          const float* dt_bias, float gate_lb, hipStream_t stream) {
+                          const float* dt_bias, float gate_lb, int segments, hipStream_t stream) {
   PrefillArgs a{q, k, v, g, beta, s0, sT, o, B, T, H, HV, K, V, scale, 0, 0, flags,
                 A_log, dt_bias, gate_lb};
   const int vw = bf16_inputs ? 8 : 4;
@@ -490,9 +490,9 @@ hipError_t launch_prefill(const void* q, const void* k, const void* v, const voi
   a.vec_v = (V % vw == 0) && aligned16(v);
   // With a workspace (sized by the caller), bf16 runs as per-chunk factors + state pass; with
   // few heads, over segments of the sequence composed by a scan (wy_segments decides, as the
-  // workspace size did).
+  // workspace size did, unless the caller fixed `segments`: 1 is the plain two-kernel path).
   if (bf16_inputs && a.vec_qkg && a.vec_v && workspace) {
-    const int P = wy_segments(B, T, HV, V, device_cu_count());
+    const int P = segments > 0 ? segments : wy_segments(B, T, HV, V, device_cu_count());
     return P > 1 ? launch_prefill_wy_segmented(a, P, workspace, stream)
                  : launch_prefill_wy(a, workspace, stream);
   }

@@ -25,7 +25,8 @@
  *   - beta is used as given (already in (0, 1)); one value per (token, value head).
  *   - `stream` is a hipStream_t (NULL = the null stream). Work is enqueued
  *     asynchronously; the library never synchronises and keeps no device
- *     allocations or mutable global state (re-entrant, thread-safe).
+ *     allocations or mutable global state (re-entrant, thread-safe), with one
+ *     exception: kda_chunk_fwd_noalloc's fixed scratch array per device (see there).
  *   - The caller owns every buffer. Arguments are validated before any launch;
  *     on a nonzero return nothing was enqueued. Faults inside a kernel surface at
  *     the caller's next synchronisation. No C++ exception crosses this ABI.
@@ -43,7 +44,9 @@ typedef enum {
   KDA_OK = 0,
   KDA_ERR_INVALID = -1,     /* null required pointer, bad dims, bad chunk size, non-finite scale */
   KDA_ERR_UNSUPPORTED = -2, /* valid arguments the library has no kernel for (e.g. K or V > 128) */
-  KDA_ERR_HIP = -3          /* the HIP runtime reported an error at launch */
+  KDA_ERR_HIP = -3,         /* the HIP runtime reported an error at launch */
+  KDA_ERR_SCRATCH = -4      /* kda_chunk_fwd_noalloc: the call needs more scratch than
+                               KDA_NOALLOC_SCRATCH_BYTES */
 } kda_status;
 
 typedef enum { KDA_DTYPE_F32 = 0, KDA_DTYPE_BF16 = 1 } kda_dtype;
@@ -382,6 +385,31 @@ int kda_chunk_fwd_segmented(const void* q, const void* k, const void* v, const v
                             void* o, int B, int T, int H, int HV, int K, int V, float scale,
                             int segments, int dtype, void* workspace, size_t workspace_bytes,
                             unsigned flags, void* stream);
+
+/*
+ * For callers that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc. kda_chunk_fwd_ex without a workspace
+ * argument and without any allocation: the two-kernel path's workspace is a fixed array of
+ * KDA_NOALLOC_SCRATCH_BYTES that the library's code object holds on every GPU it is loaded
+ * on, until the process ends (its address on the current device is looked up once per
+ * device). Same arguments, arithmetic and results as kda_chunk_fwd_ex with a workspace of
+ * kda_chunk_fwd_workspace_size() bytes, bit for bit: when that size exceeds the array (the
+ * segmented route for few heads), the plain two-kernel path is taken if its own workspace
+ * fits, else the call returns KDA_ERR_SCRATCH before anything is enqueued. Calls whose path
+ * needs no workspace (float32, K % 8 != 0, ...) run as kda_chunk_fwd_ex without one.
+ *
+ * The current device must be the device of `stream` (as for torch's current stream). Every
+ * call on a GPU shares that GPU's array: calls that overlap on one GPU (two streams, two
+ * threads, a graph replayed while another call runs) race on it and give wrong results.
+ * Calls ordered on one stream are safe; nothing in the array needs clearing between them
+ * (each call writes every byte it reads).
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+int kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const void* g,
+                          const void* beta, const float* initial_state, float* final_state,
+                          void* o, int B, int T, int H, int HV, int K, int V, float scale,
+                          int chunk_size, int dtype, unsigned flags, void* stream);
 
 #ifdef __cplusplus
 }

@@ -450,3 +450,34 @@ def test_segmented_workspace_sizes(lib):
     assert seg == plain + 3 * 16 * 2 * 128 * 128 * 4
     assert ws(1, 4096, 2, 2, 128, 128, 3, 1) == 0     # 4096 is not a multiple of 64 * 3
     assert ws(1, 4096, 2, 2, 128, 128, 16, 0) == 0    # bf16 only
+
+
+def _noalloc(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, s0=None, sT=None, o=FAKE, B=2, T=64, H=2,
+             HV=4, K=64, V=64, scale=0.125, chunk=64, dtype=1, flags=0)
+    a.update(kw)
+    return lib.kda_chunk_fwd_noalloc(a["q"], a["k"], a["v"], a["g"], a["beta"], a["s0"], a["sT"],
+                                     a["o"], a["B"], a["T"], a["H"], a["HV"], a["K"], a["V"],
+                                     a["scale"], a["chunk"], a["dtype"], a["flags"], None)
+
+
+def test_noalloc_scratch_constant_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define KDA_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == kda.NOALLOC_SCRATCH_BYTES
+    assert re.search(r"KDA_ERR_SCRATCH = (-\d+)", text).group(1) == str(kda.KDA_ERR_SCRATCH)
+
+
+@pytest.mark.parametrize("bad,rc", [
+    (dict(q=None), -1), (dict(o=None), -1), (dict(T=0), -1), (dict(chunk=48), -1),
+    (dict(T=100), -1), (dict(HV=3), -1), (dict(scale=float("nan")), -1), (dict(flags=4), -1),
+    (dict(K=256), -2),
+    # B4 T8192 H16 K=V=128 needs 512 MB of workspace: more than the fixed array, rejected
+    # before any HIP call
+    (dict(B=4, T=8192, H=16, HV=16, K=128, V=128), -4),
+    # B1 T32768 H4 would take the segmented route (140 MB) and its plain path needs 128 MB
+    (dict(B=1, T=32768, H=4, HV=4, K=128, V=128), -4),
+])
+def test_noalloc_rejects_before_any_launch(lib, bad, rc):
+    assert _noalloc(lib, **bad) == rc
+    assert "scratch" in kda.status_string(kda.KDA_ERR_SCRATCH)
