@@ -29,9 +29,12 @@
 // (and (K*Gam_C/Gam)^T row rho, Gam_C[rho] belong to channel perm32(rho)).
 //
 // Decay factors (factors_kernel): with r the first token of a 16-token block,
-// d_i = G_i - G_r <= 0, R_i = 2^(d log2 e) <= 1 and C_i = 1/R_i <= e^75 (g >= -5). Diagonal
-// blocks use (x_i R_i).(k_j C_j); block I > J uses the column factor k_j C_j exp(G_rI - G_rJ);
-// Gam_i = exp(G_rI) R_i and Gam_C/Gam_j = exp(G_C - G_rJ) C_j.
+// d_i = G_i - G_r <= 0, R_i = 2^(d log2 e) <= 1 and C_i = 1/R_i <= 2^kSpanLim while the block's
+// span is at most kSpanLim (log2 units). Diagonal blocks use (x_i R_i).(k_j C_j); block I > J
+// uses the column factor k_j C_j exp(G_rI - G_rJ); Gam_i = exp(G_rI) R_i and
+// Gam_C/Gam_j = exp(G_C - G_rJ) C_j. A block with a wider span (g far below the safe gate's
+// -5) computes its diagonal tiles pair by pair (direct_diag) and its column factors as one
+// exponential of a difference <= 0 each, so the factors are exact for any g <= 0.
 #include "kda_device.h"
 #include "kda_varlen.h"
 
@@ -55,7 +58,8 @@ struct Blk {
   static constexpr int aq = t + kTri;           // Aq, the same layout
   static constexpr int gam = aq + kTri;         // [KT] fp32 Gam_C, rows permuted
   static constexpr int beta = gam + KT * 4;     // [64] fp32 beta
-  static constexpr int used = beta + kC * 4;
+  static constexpr int flag = beta + kC * 4;    // [4] bytes: block w's span exceeds kSpanLim
+  static constexpr int used = flag + 4;
   static constexpr int bytes = (used + 1023) / 1024 * 1024;
 };
 
@@ -150,7 +154,9 @@ struct LdsA {
   static constexpr int tE = d15 + 4 * KT * 4;          // [4][KT] fp32 exp(G at block start)
   static constexpr int tF = tE + 4 * KT * 4;           // [4][KT] fp32 exp(G_C - G at block start)
   static constexpr int tFo = tF + 4 * KT * 4;          // [6][KT] fp32 exp(G_rI - G_rJ), I > J
-  static constexpr int end1 = tFo + 6 * KT * 4;
+  static constexpr int lgr = tFo + 6 * KT * 4;         // [4][KT] fp32 G at block start (log2 units)
+  static constexpr int lrun = lgr + 4 * KT * 4;        // [KT] fp32 G_C (log2 units)
+  static constexpr int end1 = lrun + KT * 4;
   // phase 2: M .. copy-out (same bytes)
   static constexpr int m = 0;                          // [64][PM] fp32 M
   static constexpr int t = m + kC * PM * 4;            // [64][PC] bf16 T
@@ -170,7 +176,15 @@ struct LdsA {
 // plain path keeps its register budget: two workgroups per CU). GATE: the g input holds the
 // gate's input x, and the decay gate (gate_value, rounded to bf16 as the standalone gate
 // stores it) turns it into g before anything else reads it.
-template <int KT, bool L2N, bool VARLEN, bool GATE = false>
+//
+// EXACT = false is the launch every call makes. A 16-token block whose decay span exceeds
+// kSpanLim (possible only for g well below the safe gate's -5) cannot use the factored
+// diagonal: its wave marks the item in the block's flag bytes (Blk::flag, one per wave) and
+// leaves garbage. EXACT = true, launched right after, reads those flags and recomputes only
+// the marked items, with the wide blocks' diagonal tiles pair by pair (direct_diag) and
+// their column factors as exponentials of differences <= 0. Being its own instantiation,
+// the exact route costs the common one no registers.
+template <int KT, bool L2N, bool VARLEN, bool GATE = false, bool EXACT = false>
 __global__ __launch_bounds__(256) void factors_kernel(WyArgs a) {
   using L = LdsA<KT>;
   using W = Blk<KT>;
@@ -185,6 +199,8 @@ __global__ __launch_bounds__(256) void factors_kernel(WyArgs a) {
   float* sE = reinterpret_cast<float*>(lds + L::tE);
   float* sF = reinterpret_cast<float*>(lds + L::tF);
   float* sFo = reinterpret_cast<float*>(lds + L::tFo);
+  float* sLg = reinterpret_cast<float*>(lds + L::lgr);
+  float* sRun = reinterpret_cast<float*>(lds + L::lrun);
   float* sM = reinterpret_cast<float*>(lds + L::m);
   bf16* tT = reinterpret_cast<bf16*>(lds + L::t);
   bf16* tTT = reinterpret_cast<bf16*>(lds + L::tt);
@@ -244,14 +260,10 @@ __global__ __launch_bounds__(256) void factors_kernel(WyArgs a) {
     rbeta = buf_load1(rb_, (unsigned)(i_row * p.HV * 2));
   };
 
-  if ((int)blockIdx.x < items) prefetch(blockIdx.x);
-
-  for (int it = blockIdx.x; it < items; it += gridDim.x) {
+  // One item; its q, k, g and beta are in registers when it starts. `next` (or -1) is the
+  // item whose inputs it loads once its own are consumed.
+  auto body = [&](int it, int next) {
     unsigned char* blk = a.ws + (size_t)it * W::bytes;
-    if (VARLEN && a.ctab[it % a.NC].y == 0) {  // past the packed list's last chunk: no block
-      if (it + (int)gridDim.x < items) prefetch(it + gridDim.x);
-      continue;
-    }
     if constexpr (GATE) {
       // rows past the chunk's last token stay zero tokens (g = 0), channels >= K stay zero
       int ghv, gnrow;
@@ -335,9 +347,11 @@ __global__ __launch_bounds__(256) void factors_kernel(WyArgs a) {
       for (int J = 0; J < 4; ++J) {
         sE[J * KT + c] = fast_exp2(gr[J]);
         sF[J * KT + c] = fast_exp2(run - gr[J]);
+        sLg[J * KT + c] = gr[J];
 #pragma unroll
         for (int I = J + 1; I < 4; ++I) sFo[pair_index(I, J) * KT + c] = fast_exp2(gr[I] - gr[J]);
       }
+      sRun[c] = run;
       sGam[c] = fast_exp2(run);
     }
     lds_barrier();
@@ -372,6 +386,60 @@ __global__ __launch_bounds__(256) void factors_kernel(WyArgs a) {
     f32x4 aK[3], aQ[3], aKd = {0.f, 0.f, 0.f, 0.f}, aQd = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int J = 0; J < 3; ++J) aK[J] = aQ[J] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // block w's span (d is monotone in the token for g <= 0; every lane's values are checked)
+    bool wide_l = false;
+#pragma unroll
+    for (int s = 0; s < NKS; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) wide_l |= !(fabsf(d[s][e]) <= kSpanLim);
+    const bool wide = wave_any(wide_l);
+    if constexpr (!EXACT)  // the exact launch redoes the item if any of its blocks is wide
+      if (lane == 0) blk[W::flag + w] = wide ? 1 : 0;
+    if (EXACT && wide) {
+      // wide span: every factor as one exponential of a difference <= 0; the diagonal tiles
+      // pair by pair
+#pragma unroll
+      for (int s = 0; s < NKS; ++s) {
+        const int cA = 32 * s + 8 * lq, cB = cA + 4;
+        const f32x4 e0 = load4f(sE + w * KT + cA), e1 = load4f(sE + w * KT + cB);
+        const f32x4 l0 = load4f(sLg + w * KT + cA), l1 = load4f(sLg + w * KT + cB);
+        const f32x4 u0 = load4f(sRun + cA), u1 = load4f(sRun + cB);
+        bf16x8 QG, KG;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float E = e < 4 ? e0[e] : e1[e - 4];
+          const float gw = e < 4 ? l0[e] : l1[e - 4];  // G at block w's first token
+          const float gc = e < 4 ? u0[e] : u1[e - 4];  // G_C
+          const float R = fast_exp2(d[s][e]);
+          const float qv = to_f32(rq[s][e]) * inv_q, kv = to_f32(rk[s][e]) * inv_k;
+          const float qr = qv * R, kr = kv * R;
+          QR[s][e] = static_cast<bf16>(qr);
+          KR[s][e] = static_cast<bf16>(kr);
+          QG[e] = static_cast<bf16>(qr * E);
+          KG[e] = static_cast<bf16>(kr * E);
+          tKdT[(cA + e) * PC + perm32(i_row)] = static_cast<bf16>(kv * fast_exp2((gc - gw) - d[s][e]));
+        }
+        const int qk_off = (i_row * (KT / 8) + swz<KT / 8>(i_row, 4 * s + lq)) * 16;
+        *reinterpret_cast<bf16x8*>(blk + W::qg + qk_off) = QG;
+        *reinterpret_cast<bf16x8*>(blk + W::kg + qk_off) = KG;
+#pragma unroll
+        for (int I = 1; I < 4; ++I) {
+          if (I > w) {
+            const int pi = pair_index(I, w);
+            const f32x4 h0 = load4f(sLg + I * KT + cA), h1 = load4f(sLg + I * KT + cB);
+            bf16x8 kco;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float gI = e < 4 ? h0[e] : h1[e - 4];
+              const float gw = e < 4 ? l0[e] : l1[e - 4];
+              kco[e] = static_cast<bf16>(to_f32(rk[s][e]) * inv_k * fast_exp2((gI - gw) - d[s][e]));
+            }
+            *reinterpret_cast<bf16x8*>(tKCo + (pi * 16 + lr) * PK + 32 * s + 8 * lq) = kco;
+          }
+        }
+      }
+      direct_diag<NKS>(d, rq, rk, inv_q, inv_k, lq, aKd, aQd);
+    } else {
 #pragma unroll
     for (int s = 0; s < NKS; ++s) {
       const int cA = 32 * s + 8 * lq, cB = cA + 4;  // channels of elements 0..3 and 4..7
@@ -422,10 +490,11 @@ __global__ __launch_bounds__(256) void factors_kernel(WyArgs a) {
         }
       }
     }
+    }
     const float brow = (p.flags & kFlagBetaSigmoid) ? sigmoid_f32(bits_to_f32(rbeta)) : bits_to_f32(rbeta);
     if (lq == 0) *reinterpret_cast<float*>(blk + W::beta + i_row * 4) = brow;
     // this item's raw inputs are consumed: fetch the next item's
-    if (it + (int)gridDim.x < items) prefetch(it + gridDim.x);
+    if (next >= 0) prefetch(next);
     lds_barrier();
 
     // ---------------- off-diagonal Akk^T / Aq^T tiles (J < w): column factors of block J
@@ -556,6 +625,38 @@ __global__ __launch_bounds__(256) void factors_kernel(WyArgs a) {
     }
     if (tid < KT / 4) *reinterpret_cast<f32x4*>(blk + W::gam + tid * 16) = load4f(sGam + perm32(4 * tid));
     lds_barrier();  // the next item's scan writes over T
+  };
+
+  if constexpr (!EXACT) {
+    if ((int)blockIdx.x < items) prefetch(blockIdx.x);
+    for (int it = blockIdx.x; it < items; it += gridDim.x) {
+      const int next = it + (int)gridDim.x < items ? it + (int)gridDim.x : -1;
+      if (VARLEN && a.ctab[it % a.NC].y == 0) {  // past the packed list's last chunk: no block
+        if (next >= 0) prefetch(next);
+        continue;
+      }
+      body(it, next);
+    }
+  } else {
+    // this workgroup's items (blockIdx.x + m gridDim.x), 256 flags read at once per batch
+    __shared__ unsigned sFlag[256];
+    const int stride = gridDim.x;
+    for (int base = blockIdx.x; base < items; base += 256 * stride) {
+      const int mine = base + tid * stride;
+      unsigned f = 0u;
+      if (mine < items && !(VARLEN && a.ctab[mine % a.NC].y == 0))
+        f = *reinterpret_cast<const unsigned*>(a.ws + (size_t)mine * W::bytes + W::flag);
+      sFlag[tid] = f;
+      lds_barrier();
+      for (int m = 0; m < 256; ++m) {
+        const int it = base + m * stride;
+        if (it >= items) break;
+        if (sFlag[m] == 0u) continue;
+        prefetch(it);
+        body(it, -1);
+      }
+      lds_barrier();  // the next batch rewrites sFlag
+    }
   }
 }
 
@@ -862,24 +963,32 @@ void state_kernel(WyArgs a) {
   }
 }
 
+template <int KT, bool EXACT>
+static void launch_factors_pass(const WyArgs& a, int grid, hipStream_t stream) {
+  const bool l2 = a.p.flags & kFlagQkL2norm, vl = a.ctab != nullptr;
+  const bool gt = a.p.flags & kFlagGate;  // fixed-length sequences only (the C ABI's check)
+  if (gt && l2)
+    hipLaunchKernelGGL((factors_kernel<KT, true, false, true, EXACT>), dim3(grid), dim3(256), 0, stream, a);
+  else if (gt)
+    hipLaunchKernelGGL((factors_kernel<KT, false, false, true, EXACT>), dim3(grid), dim3(256), 0, stream, a);
+  else if (l2 && vl)
+    hipLaunchKernelGGL((factors_kernel<KT, true, true, false, EXACT>), dim3(grid), dim3(256), 0, stream, a);
+  else if (l2)
+    hipLaunchKernelGGL((factors_kernel<KT, true, false, false, EXACT>), dim3(grid), dim3(256), 0, stream, a);
+  else if (vl)
+    hipLaunchKernelGGL((factors_kernel<KT, false, true, false, EXACT>), dim3(grid), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((factors_kernel<KT, false, false, false, EXACT>), dim3(grid), dim3(256), 0, stream, a);
+}
+
+// The factors of every item, then the exact pass over the items whose blocks were too wide
+// for the factored diagonal (it exits at once when there are none).
 template <int KT>
 hipError_t launch_factors(const WyArgs& a, int cus, hipStream_t stream) {
   const int items = a.ctab ? a.p.HV * a.NC : a.p.B * a.p.HV * a.NT;
   const int grid_a = items < 2 * cus ? items : 2 * cus;
-  const bool l2 = a.p.flags & kFlagQkL2norm, vl = a.ctab != nullptr;
-  const bool gt = a.p.flags & kFlagGate;  // fixed-length sequences only (the C ABI's check)
-  if (gt && l2)
-    hipLaunchKernelGGL((factors_kernel<KT, true, false, true>), dim3(grid_a), dim3(256), 0, stream, a);
-  else if (gt)
-    hipLaunchKernelGGL((factors_kernel<KT, false, false, true>), dim3(grid_a), dim3(256), 0, stream, a);
-  else if (l2 && vl)
-    hipLaunchKernelGGL((factors_kernel<KT, true, true>), dim3(grid_a), dim3(256), 0, stream, a);
-  else if (l2)
-    hipLaunchKernelGGL((factors_kernel<KT, true, false>), dim3(grid_a), dim3(256), 0, stream, a);
-  else if (vl)
-    hipLaunchKernelGGL((factors_kernel<KT, false, true>), dim3(grid_a), dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL((factors_kernel<KT, false, false>), dim3(grid_a), dim3(256), 0, stream, a);
+  launch_factors_pass<KT, false>(a, grid_a, stream);
+  launch_factors_pass<KT, true>(a, grid_a, stream);
   return hipGetLastError();
 }
 

@@ -23,9 +23,71 @@ template <> __device__ __forceinline__ float from_f32<float>(float x) { return x
 // float -> bfloat16 rounds to nearest even (v_cvt_pk_bf16_f32 on gfx950).
 template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return static_cast<bf16>(x); }
 
-// 2^x on the transcendental unit (v_exp_f32). Inputs here are <= 0 or bounded by
-// +75*log2(e), so the result is finite; denormal results may flush to zero.
+// 2^x on the transcendental unit (v_exp_f32). Callers keep x <= kSpanLim (a block's
+// decay span, see below) or x <= 0, so the result is finite; denormal results may flush to
+// zero.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---- Relative decay inside one 16-token block.
+// The chunk kernels factor exp(G_i - G_j) (j <= i, G the in-chunk cumsum of g) through the
+// block's first token r: 2^(d_i) * 2^(-d_j) with d = (G - G_r) log2 e <= 0. Both factors stay
+// in the float range while the block's span -d (at its last token) is at most kSpanLim; a
+// factor exp(G_rI - G_rJ) <= 1 between blocks that underflows then hides a term below
+// 2^(kSpanLim - 126) = 2^-30 of |q||k|. A block whose span is wider (any g, the standard
+// gate's included, can produce one) takes every pair's decay inside it as one exponential
+// of d_i - d_j <= 0 (direct_diag), and the factors it builds for other blocks as one
+// exponential of a difference <= 0 as well, which is exact for any g <= 0.
+constexpr float kSpanLim = 96.f;
+
+// The diagonal tiles of one 16-token block computed term by term, for a block whose span
+// exceeds kSpanLim. Lane (lr, lq) holds token i = lr of the block and the channels of its NS
+// k steps (NS x 8 values): rq / rk its raw q / k values, which inv_q / inv_k scale (the
+// optional L2 normalisation; 1 otherwise), d its in-block cumsum of g (log2 units). Returns,
+// in the accumulator layout of a 16 x 16 tile with rows j and columns i (lane: column lr,
+// rows 4 lq + r), the sums over the wave's channels
+//   ak[r] = sum_c k_j[c] k_i[c] 2^(d_i[c] - d_j[c]),   aq[r] = the same with q_i,
+// for j = 4 lq + r; entries with j > i are unspecified (callers mask them). Column token j's
+// values come from lane (j, lq) of the same row; the loop over j is not unrolled, so the
+// path adds few live registers to its kernel.
+template <int NS>
+__device__ __forceinline__ void direct_diag(const float (&d)[NS][8], const bf16x8 (&rq)[NS],
+                                            const bf16x8 (&rk)[NS], float inv_q, float inv_k,
+                                            int lq, f32x4& ak, f32x4& aq) {
+  const int row0 = (__lane_id() & 48);
+#pragma nounroll
+  for (int j = 0; j < 16; ++j) {
+    float sk = 0.f, sq = 0.f;
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        // each lane scales its own token's values (inv_* belong to the lane's token)
+        const float kv = static_cast<float>(rk[s][e]) * inv_k;
+        // j > i gives a positive exponent, possibly inf: those sums are never read
+        const float w = __shfl(kv, row0 | j) * fast_exp2(d[s][e] - __shfl(d[s][e], row0 | j));
+        sk = fmaf(kv, w, sk);
+        sq = fmaf(static_cast<float>(rq[s][e]) * inv_q, w, sq);
+      }
+    sk += __shfl_xor(sk, 16);  // the four lanes (lq) that hold token i's channels
+    sq += __shfl_xor(sq, 16);
+    sk += __shfl_xor(sk, 32);
+    sq += __shfl_xor(sq, 32);
+    if (lq == (j >> 2)) {
+      const int r = j & 3;
+      ak[0] = r == 0 ? sk : ak[0];
+      ak[1] = r == 1 ? sk : ak[1];
+      ak[2] = r == 2 ? sk : ak[2];
+      ak[3] = r == 3 ? sk : ak[3];
+      aq[0] = r == 0 ? sq : aq[0];
+      aq[1] = r == 1 ? sq : aq[1];
+      aq[2] = r == 2 ? sq : aq[2];
+      aq[3] = r == 3 ? sq : aq[3];
+    }
+  }
+}
+
+// True on every lane when any lane's v is true.
+__device__ __forceinline__ bool wave_any(bool v) { return __builtin_amdgcn_ballot_w64(v) != 0; }
 
 // Workgroup barrier for LDS traffic only: waits for this wave's LDS operations, not for
 // its outstanding global loads or stores (a plain __syncthreads() also drains those, which

@@ -15,7 +15,8 @@ Value distributions (the layer shapes and distributions of the five workloads):
 Draw order is q, k, v, g, beta, state from one ``torch.Generator('cpu')``
 seeded with ``seed``; everything is computed in float32 and rounded to the
 workload dtype (round to nearest even for bfloat16). The gate and beta modes
-are stress variants used for parity only.
+are stress variants used for parity only; "const:<v>" and "mixed" reach decays far
+below the safe gate's -5 (the standard gate has no lower bound).
 """
 
 import math
@@ -56,6 +57,13 @@ def _gate(shape, gen, mode):
         return torch.zeros(shape)
     if mode == "bound":
         return torch.full(shape, -5.0)
+    if mode.startswith("const:"):  # every g equal to one value, e.g. "const:-20"
+        return torch.full(shape, float(mode[6:]))
+    if mode == "mixed":
+        # the default gate, except that about one token in 64 (per value head, all channels)
+        # decays 40 times faster: chunks then mix blocks of both kinds of decay span
+        fast = torch.rand(shape[:-1] + (1,), generator=gen) < 1.0 / 64.0
+        return torch.where(fast, -40.0 * F.softplus(x), torch.clamp(-F.softplus(x), min=-5.0))
     raise ValueError(mode)
 
 

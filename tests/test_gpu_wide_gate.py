@@ -1,0 +1,126 @@
+"""GPU parity of the chunked paths when g leaves the safe gate's range (g < -5).
+
+The K3 README's roadmap row L5 has a standard gate next to the safe one; the standard gate
+has no lower bound, and any caller may pass g below -5. Within a 16-token block the chunk
+kernels factor the relative decay through the block's first token, which covers a decay
+span of up to 2^96 (about 66 nats); wider blocks take a term-by-term route (exact for any
+g <= 0). These tests cover:
+
+* constant g = -8, -20 and -100 (every block wide);
+* the standard gate (lower_bound = -inf) applied inside the prefill on a wide gate input
+  (x ~ 3 N(0, 1)), B1 T1024 HV16 K128;
+* "mixed" g: the default gate with about one token in 64 decaying 40 times faster, so that
+  chunks mix blocks of both routes;
+* the segmented route (few heads) and packed sequences with wide g.
+
+Each is checked against the float64 oracle at the bf16 criterion (tests/helpers.py)."""
+
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_67_amd as kda
+from oracle import gate, recurrent
+from synth import gate_inputs, prefill_inputs
+from tests.helpers import assert_parity, gpu, log, to64
+
+pytestmark = pytest.mark.gpu
+
+
+def _fwd_case(B, T, H, HV, K, V, gate_mode, seed, chunk=64, workspace=True):
+    inp = prefill_inputs(B, T, H, HV, K, V, "bf16", True, seed, gate=gate_mode)
+    d = gpu(inp)
+    o, s = kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["scale"],
+                             d["initial_state"], chunk_size=chunk)
+    torch.cuda.synchronize()
+    ref_o, ref_s = recurrent(**inp)
+    assert_parity(to64(o), ref_o, torch.bfloat16, f"o ({gate_mode})")
+    assert_parity(to64(s), ref_s, torch.bfloat16, f"state ({gate_mode})")
+
+
+@pytest.mark.parametrize("gate_mode", ["const:-8", "const:-20", "const:-100", "mixed"])
+def test_two_kernel_prefill_wide_decay(gate_mode):
+    log(f"two-kernel prefill B1 T1024 H16 K128 g={gate_mode}")
+    _fwd_case(1, 1024, 16, 16, 128, 128, gate_mode, seed=301)
+
+
+@pytest.mark.parametrize("shape", [
+    dict(B=2, T=200, H=2, HV=4, K=64, V=64),   # GVA, ragged last chunk
+    dict(B=1, T=136, H=1, HV=3, K=32, V=32),
+])
+def test_two_kernel_prefill_wide_decay_small_k(shape):
+    for mode in ("const:-20", "mixed"):
+        log(f"two-kernel prefill {shape} g={mode}")
+        _fwd_case(**shape, gate_mode=mode, seed=302, chunk=8)
+
+
+def test_standard_gate_inside_the_prefill():
+    """kda_chunk_fwd_gated with lower_bound = -inf (the standard gate) on x ~ 3 N(0, 1): the
+    oracle applies its own gate (float64, then rounded to bf16 as the kernel stores g)."""
+    B, T, H, HV, K, V = 1, 1024, 16, 16, 128, 128
+    log("standard gate inside the prefill, B1 T1024 HV16 K128, x ~ 3 N(0, 1)")
+    inp = prefill_inputs(B, T, H, HV, K, V, "bf16", True, seed=303)
+    gi = gate_inputs(B, T, HV, K, "bf16", seed=304, x_std=3.0)
+    g_ref = gate(gi["x"].double().numpy(), gi["A_log"].double().numpy(),
+                 gi["dt_bias"].double().numpy(), None)
+    wide = float(np.mean(g_ref < -5.0))
+    log(f"    share of g below -5: {wide:.3f}, min g {g_ref.min():.1f}")
+    assert wide > 0.05
+    d = gpu(inp)
+    o, s = kda.kda_chunk_fwd_gated(d["q"], d["k"], d["v"], gi["x"].cuda(), gi["A_log"].cuda(),
+                                   gi["dt_bias"].cuda(), d["beta"], None, d["scale"],
+                                   d["initial_state"])
+    torch.cuda.synchronize()
+    ref_o, ref_s = recurrent(**dict(inp, g=torch.from_numpy(g_ref).to(torch.bfloat16)))
+    assert_parity(to64(o), ref_o, torch.bfloat16, "o")
+    assert_parity(to64(s), ref_s, torch.bfloat16, "state")
+
+
+@pytest.mark.parametrize("gate_mode", ["const:-20", "mixed"])
+def test_segmented_prefill_wide_decay(gate_mode):
+    log(f"segmented prefill B1 T4096 H4 K128 g={gate_mode}")
+    inp = prefill_inputs(1, 4096, 4, 4, 128, 128, "bf16", True, 305, gate=gate_mode)
+    d = gpu(inp)
+    o, s = kda.kda_chunk_fwd_segmented(d["q"], d["k"], d["v"], d["g"], d["beta"], 16,
+                                       d["scale"], d["initial_state"])
+    torch.cuda.synchronize()
+    ref_o, ref_s = recurrent(**inp)
+    assert_parity(to64(o), ref_o, torch.bfloat16, "o")
+    assert_parity(to64(s), ref_s, torch.bfloat16, "state")
+
+
+def test_packed_sequences_wide_decay():
+    lengths = [70, 0, 200, 33]
+    log(f"packed sequences {lengths} g=mixed and const:-20")
+    for mode, seed in (("mixed", 306), ("const:-20", 307)):
+        T = sum(lengths)
+        inp = prefill_inputs(1, T, 2, 4, 64, 64, "bf16", True, seed, gate=mode)
+        gen = torch.Generator().manual_seed(seed + 1)
+        s0 = 0.1 * torch.randn((len(lengths), 4, 64, 64), generator=gen)
+        cu = torch.tensor(np.concatenate([[0], np.cumsum(lengths)]), dtype=torch.int32)
+        d = gpu(inp)
+        o, sT = kda.kda_chunk_fwd_varlen(d["q"], d["k"], d["v"], d["g"], d["beta"], cu.cuda(),
+                                         d["scale"], s0.cuda(), True)
+        torch.cuda.synchronize()
+        for sq in range(len(lengths)):
+            a, b = int(cu[sq]), int(cu[sq + 1])
+            if a == b:
+                continue
+            one = {n: inp[n][:, a:b] for n in ("q", "k", "v", "g", "beta")}
+            ref_o, ref_s = recurrent(**one, scale=inp["scale"], initial_state=s0[sq:sq + 1])
+            assert_parity(to64(o[:, a:b]), ref_o, torch.bfloat16, f"o of sequence {sq} ({mode})")
+            assert_parity(to64(sT[sq:sq + 1]), ref_s, torch.bfloat16, f"state of sequence {sq}")
+
+
+@pytest.mark.parametrize("gate_mode", ["const:-20", "mixed"])
+def test_two_kernel_prefill_wide_decay_with_l2norm(gate_mode):
+    """The in-kernel q/k L2 normalisation on the wide route: every token's own norm."""
+    log(f"two-kernel prefill with q/k L2-norm, B1 T256 H2 HV4 K64, g={gate_mode}")
+    inp = prefill_inputs(1, 256, 2, 4, 64, 64, "bf16", True, 308, gate=gate_mode, raw_qk=True)
+    d = gpu(inp)
+    o, s = kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["scale"],
+                             d["initial_state"], qk_l2norm=True)
+    torch.cuda.synchronize()
+    ref_o, ref_s = recurrent(**inp, qk_l2norm=True)
+    assert_parity(to64(o), ref_o, torch.bfloat16, "o")
+    assert_parity(to64(s), ref_s, torch.bfloat16, "state")
