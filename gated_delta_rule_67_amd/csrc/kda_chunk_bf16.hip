@@ -24,10 +24,13 @@
 // half of P. Only the tiles other waves need go through LDS.
 //
 // Decay factors: with r the first token of a block, d_i = G_i - G_r <= 0,
-// R_i = 2^(d log2 e) <= 1 and C_i = 1/R_i <= e^75 (g >= -5). Diagonal blocks use
-// (x_i R_i).(k_j C_j); block I > J uses the column factor k_j C_j exp(G_rI - G_rJ);
-// Gam_i = exp(G_rI) R_i and Gam_C/Gam_j = exp(G_C - G_rJ) C_j. The per-(block,
-// channel) constants come from a small table built once per chunk.
+// R_i = 2^(d log2 e) <= 1 and C_i = 1/R_i <= 2^kSpanLim while the block's span is within
+// kSpanLim (log2 units). Diagonal blocks use (x_i R_i).(k_j C_j); block I > J uses the column
+// factor k_j C_j exp(G_rI - G_rJ); Gam_i = exp(G_rI) R_i and Gam_C/Gam_j = exp(G_C - G_rJ) C_j.
+// The per-(block, channel) constants come from a small table built once per chunk. A wave
+// whose channels of its block span more (g far below the safe gate's -5) builds its
+// column factors as one exponential of a difference <= 0 each and its diagonal partial
+// tiles pair by pair (direct_diag), which is exact for any g <= 0.
 #include "kda_device.h"
 
 namespace kda {
@@ -52,10 +55,12 @@ struct Lds {
   static constexpr int tE = d15 + 4 * KT * 4;              // [4][KT] fp32 exp(G at block start)
   static constexpr int tF = tE + 4 * KT * 4;               // [4][KT] fp32 exp(G_C - G at block start)
   static constexpr int tFo = tF + 4 * KT * 4;              // [6][KT] fp32 exp(G_rI - G_rJ), I > J
+  static constexpr int lgr = tFo + 6 * KT * 4;             // [4][KT] fp32 G at block start (log2 units)
+  static constexpr int lrun = lgr + 4 * KT * 4;            // [KT]    fp32 G_C (log2 units)
   // partial-sum tiles (fp32, 1 KB each): per block pair 2(b+1) + 2 NVT tiles
   static constexpr int part = 0;
   static constexpr int nPart = 2 * 10 + 8 * NVT;
-  static constexpr int endX = (tFo + 6 * KT * 4) > nPart * 1024 ? (tFo + 6 * KT * 4) : nPart * 1024;
+  static constexpr int endX = (lrun + KT * 4) > nPart * 1024 ? (lrun + KT * 4) : nPart * 1024;
   // ---- live across the chunk
   static constexpr int kdt = endX;                         // [KT][PC]    bf16 (K*Gam_C/Gam)^T
   static constexpr int st = kdt + KT * PC * 2;             // [BV][PK]    bf16 S^T
@@ -143,6 +148,8 @@ __global__ __launch_bounds__(kThreads) void kernel(PrefillArgs p) {
   float* sE = reinterpret_cast<float*>(lds + L::tE);
   float* sF = reinterpret_cast<float*>(lds + L::tF);
   float* sFo = reinterpret_cast<float*>(lds + L::tFo);
+  float* sLg = reinterpret_cast<float*>(lds + L::lgr);
+  float* sRun = reinterpret_cast<float*>(lds + L::lrun);
   f32x4* sPart = reinterpret_cast<f32x4*>(lds + L::part);
   bf16* tKdT = reinterpret_cast<bf16*>(lds + L::kdt);
   bf16* tST = reinterpret_cast<bf16*>(lds + L::st);
@@ -305,7 +312,9 @@ __global__ __launch_bounds__(kThreads) void kernel(PrefillArgs p) {
         sF[J * KT + c] = fast_exp2(run - gr[J]);
 #pragma unroll
         for (int I = J + 1; I < 4; ++I) sFo[pair_index(I, J) * KT + c] = fast_exp2(gr[I] - gr[J]);
+        sLg[J * KT + c] = gr[J];
       }
+      sRun[c] = run;
       sGam[c] = fast_exp2(run);
     }
     lds_barrier();
@@ -322,6 +331,55 @@ __global__ __launch_bounds__(kThreads) void kernel(PrefillArgs p) {
     aKd = aQd = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int vt = 0; vt < NVT; ++vt) aX[vt] = aP[vt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // this wave's channels of block w: span within kSpanLim, or the exact route
+    bool wide_l = false;
+#pragma unroll
+    for (int sl = 0; sl < NKH; ++sl)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) wide_l |= !(fabsf(d[sl][e]) <= kSpanLim);
+    if (wave_any(wide_l)) {
+#pragma unroll
+      for (int sl = 0; sl < NKH; ++sl) {
+        const int s = hf * NKH + sl;
+        if (s < NKS) {
+          const int c0 = 32 * s + 8 * lq;
+          bf16x8 sf[NVT];
+#pragma unroll
+          for (int vt = 0; vt < NVT; ++vt) sf[vt] = load8(tST + (vt * 16 + lr) * PK + c0);
+          bf16x8 QG, KG;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float gw = sLg[w * KT + c0 + e];  // G at block w's first token
+            const float R = fast_exp2(d[sl][e]);
+            const float qv = to_f32(rq[sl][e]), kv = to_f32(rk[sl][e]);
+            const float qr = qv * R, kr = kv * R;
+            QR[sl][e] = static_cast<bf16>(qr);
+            KR[sl][e] = static_cast<bf16>(kr);
+            QG[e] = static_cast<bf16>(qr * sE[w * KT + c0 + e]);
+            KG[e] = static_cast<bf16>(kr * sE[w * KT + c0 + e]);
+            tKdT[(c0 + e) * PC + 16 * w + lr] = static_cast<bf16>(kv * fast_exp2((sRun[c0 + e] - gw) - d[sl][e]));
+          }
+#pragma unroll
+          for (int vt = 0; vt < NVT; ++vt) {
+            aX[vt] = mfma32(KG, sf[vt], aX[vt]);
+            aP[vt] = mfma32(QG, sf[vt], aP[vt]);
+          }
+#pragma unroll
+          for (int I = 1; I < 4; ++I) {
+            if (I > w) {
+              const int pi = pair_index(I, w);
+              bf16x8 kco;
+#pragma unroll
+              for (int e = 0; e < 8; ++e)
+                kco[e] = static_cast<bf16>(to_f32(rk[sl][e]) *
+                                           fast_exp2((sLg[I * KT + c0 + e] - sLg[w * KT + c0 + e]) - d[sl][e]));
+              *reinterpret_cast<bf16x8*>(tKCo + (pi * 16 + lr) * PK + c0) = kco;
+            }
+          }
+        }
+      }
+      direct_diag<NKH>(d, rq, rk, 1.f, 1.f, lq, aKd, aQd);
+    } else {
 #pragma unroll
     for (int sl = 0; sl < NKH; ++sl) {
       const int s = hf * NKH + sl;
@@ -371,6 +429,7 @@ __global__ __launch_bounds__(kThreads) void kernel(PrefillArgs p) {
           }
         }
       }
+    }
     }
     lds_barrier();
 

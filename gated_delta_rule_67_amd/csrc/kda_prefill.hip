@@ -15,10 +15,13 @@
 //   S_next  = diag(Gam_C) S + (K * Gam_C/Gam)^T U
 //
 // Relative decay without overflow: within a 16-token block I with first token r,
-// R_i = exp(G_i - G_r) <= 1 and C_i = 1/R_i <= exp(5*15) (g >= -5), so diagonal
-// blocks use (x_i R_i).(k_j C_j) and off-diagonal blocks (I > J) use the column
-// factor k_j C_j exp(G_rI - G_rJ) <= |k_j|. Two exp2 per token-channel; every
-// other decay factor is a product with a per-(block, channel) constant.
+// R_i = exp(G_i - G_r) <= 1 and C_i = 1/R_i <= 2^kSpanLim while the block's decay span is
+// within kSpanLim (log2 units), so diagonal blocks use (x_i R_i).(k_j C_j) and off-diagonal
+// blocks (I > J) use the column factor k_j C_j exp(G_rI - G_rJ) <= |k_j|. Two exp2 per
+// token-channel; every other decay factor is a product with a per-(block, channel)
+// constant. A block with a wider span (g far below the safe gate's -5) takes its column
+// factors as one exponential of a difference <= 0 each, and its diagonal tiles are
+// recomputed term by term after the first MFMA stage, which is exact for any g <= 0.
 //
 // Work layout: one workgroup (4 waves) per (b, hv, 16/32-column V tile); the
 // V-independent part of each chunk is recomputed per V tile. All contractions
@@ -70,7 +73,8 @@ struct Lds {
   static constexpr int gam = beta + kChunk * 4;        // [KT] fp32 exp(G_C)
   static constexpr int tot = gam + KT * 4;             // [4][KT] fp32 block sums (log2 units)
   static constexpr int first = tot + 4 * KT * 4;       // [4][KT] fp32 first g of each block
-  static constexpr int total = first + 4 * KT * 4;
+  static constexpr int wide = first + 4 * KT * 4;      // [4] int: block's span exceeds kSpanLim
+  static constexpr int total = wide + 4 * 4;
   static_assert(total <= 160 * 1024, "LDS budget");
 };
 
@@ -134,6 +138,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs p)
   float* sGam = reinterpret_cast<float*>(lds + L::gam);
   float* sTot = reinterpret_cast<float*>(lds + L::tot);
   float* sFirst = reinterpret_cast<float*>(lds + L::first);
+  int* sWide = reinterpret_cast<int*>(lds + L::wide);
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int lr = lane & 15, lq = lane >> 4;
@@ -206,6 +211,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs p)
     load_tile<CT>(tG, PK, gg + (size_t)t0 * sg, sg, nrow, KT, K, p.vec_qkg);
     load_tile<CT>(tV, BV, gv + (size_t)t0 * sv, sv, nrow, BV, vvalid, p.vec_v);
     if (tid < kChunk) sBeta[tid] = tid < nrow ? to_f32(gb[(size_t)(t0 + tid) * p.HV]) : 0.f;
+    if (tid < 4) sWide[tid] = 0;
     __syncthreads();
 
     // ---------------- in-block cumsum of g (log2 units), per channel pair
@@ -224,6 +230,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs p)
       sTot[fb * KT + c0 + 1] = a1;
       sFirst[fb * KT + c0] = Lc[0][0];
       sFirst[fb * KT + c0 + 1] = Lc[0][1];
+      if (!(fabsf(a0 - Lc[0][0]) <= kSpanLim && fabsf(a1 - Lc[0][1]) <= kSpanLim)) sWide[fb] = 1;
     }
     __syncthreads();
 
@@ -253,6 +260,9 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs p)
         sGam[c0] = fast_exp2(gc[0]);
         sGam[c0 + 1] = fast_exp2(gc[1]);
       }
+      // a wave that holds any channel of a wide block builds every column factor as one
+      // exponential of a difference <= 0
+      const bool wlog = wave_any(sWide[fb] != 0);
       CT kd[2][16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
@@ -271,12 +281,13 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs p)
           okc[e] = from_f32<CT>(kc);
           oqg[e] = from_f32<CT>(qr * eI[e]);
           okg[e] = from_f32<CT>(kr * eI[e]);
-          kd[e][i] = from_f32<CT>(kc * fI[e]);
+          kd[e][i] = from_f32<CT>(wlog ? kv * fast_exp2((gc[e] - gr[fb][e]) - d) : kc * fI[e]);
 #pragma unroll
           for (int J = 0; J < 4; ++J) {
             if (J > fb) {
               const int pidx = J * (J - 1) / 2 + fb;
-              tKCo[(pidx * 16 + i) * PK + c0 + e] = from_f32<CT>(kc * fo[J][e]);
+              tKCo[(pidx * 16 + i) * PK + c0 + e] =
+                  from_f32<CT>(wlog ? kv * fast_exp2((gr[J][e] - gr[fb][e]) - d) : kc * fo[J][e]);
             }
           }
         }
@@ -316,6 +327,60 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs p)
       mma16(accP[vt], tQG + (wave * 16) * PK, PK, tST + (vt * 16) * PK, PK, KT, lane);
     }
     __syncthreads();  // region A is dead from here on; region C reuses it
+
+    // Blocks whose span exceeds kSpanLim: their diagonal tiles again, term by term, from the
+    // block's q, k and g re-read (L2-resident) and staged at the start of the dead region A.
+    if (sWide[0] | sWide[1] | sWide[2] | sWide[3]) {
+      CT* wq = reinterpret_cast<CT*>(lds);                   // [16][PK] q
+      CT* wk = wq + 16 * PK;                                  // [16][PK] k
+      float* wd = reinterpret_cast<float*>(wk + 16 * PK);     // [16][KT] in-block cumsum of g
+      for (int I = 0; I < 4; ++I) {
+        if (sWide[I] == 0) continue;
+        for (int idx = tid; idx < 16 * KT; idx += kPrefillThreads) {
+          const int row = idx / KT, c = idx - row * KT, tok = I * 16 + row;
+          const bool ok = tok < nrow && c < K;
+          wq[row * PK + c] = ok ? gq[(size_t)(t0 + tok) * sqk + c] : CT{};
+          wk[row * PK + c] = ok ? gk[(size_t)(t0 + tok) * sqk + c] : CT{};
+        }
+        if (tid < KT) {
+          float run = 0.f;
+          for (int row = 0; row < 16; ++row) {
+            const int tok = I * 16 + row;
+            const float gv = (tok < nrow && tid < K) ? to_f32(gg[(size_t)(t0 + tok) * sg + tid]) * kLog2e : 0.f;
+            run = row == 0 ? 0.f : run + gv;
+            wd[row * KT + tid] = run;
+          }
+        }
+        __syncthreads();
+        // the wave holding tile (I, I) of the first stage: lane column j = lr, rows 4 lq + r
+        const int didx = I * (I + 1) / 2 + I, dn = didx / 4;
+        if (wave == didx % 4) {
+          f32x4 ak = {0.f, 0.f, 0.f, 0.f}, aqd = {0.f, 0.f, 0.f, 0.f};
+          for (int c = 0; c < KT; ++c) {
+            const float kj = to_f32(wk[lr * PK + c]), dj = wd[lr * KT + c];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int i = lq * 4 + r;
+              // j > i gives a positive exponent, possibly inf: those entries are masked
+              const float f = kj * fast_exp2(wd[i * KT + c] - dj);
+              ak[r] = fmaf(to_f32(wk[i * PK + c]), f, ak[r]);
+              aqd[r] = fmaf(to_f32(wq[i * PK + c]), f, aqd[r]);
+            }
+          }
+          if (dn == 0) {
+            accK[0] = ak;
+            accQ[0] = aqd;
+          } else if (dn == 1) {
+            accK[1] = ak;
+            accQ[1] = aqd;
+          } else {
+            accK[2] = ak;
+            accQ[2] = aqd;
+          }
+        }
+        __syncthreads();
+      }
+    }
 
     // zero T and T^T (their upper blocks must read as zero)
     for (int idx = tid; idx < 2 * kChunk * PC; idx += kPrefillThreads) tT[idx] = CT{};

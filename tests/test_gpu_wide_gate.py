@@ -124,3 +124,40 @@ def test_two_kernel_prefill_wide_decay_with_l2norm(gate_mode):
     ref_o, ref_s = recurrent(**inp, qk_l2norm=True)
     assert_parity(to64(o), ref_o, torch.bfloat16, "o")
     assert_parity(to64(s), ref_s, torch.bfloat16, "state")
+
+
+def _abi_fwd_null_workspace(d, o, s_out, dtype_code, chunk):
+    """kda_chunk_fwd through the C ABI with a NULL workspace (the single fused kernel for
+    bf16, the LDS-staged kernel for float32 and unaligned shapes)."""
+    import ctypes
+    p = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else None
+    B, T, H, K = d["q"].shape
+    HV, V = d["v"].shape[2], d["v"].shape[3]
+    rc = kda.library().kda_chunk_fwd(p(d["q"]), p(d["k"]), p(d["v"]), p(d["g"]), p(d["beta"]),
+                                     p(d["initial_state"]), p(s_out), p(o), B, T, H, HV, K, V,
+                                     float(d["scale"]), chunk, dtype_code, None, 0, None)
+    torch.cuda.synchronize()
+    return rc
+
+
+@pytest.mark.parametrize("case", [
+    dict(B=1, T=1024, H=16, HV=16, K=128, V=128, dtype="bf16", chunk=64),  # fused kernel
+    dict(B=2, T=200, H=2, HV=4, K=64, V=48, dtype="bf16", chunk=8),        # fused, ragged
+    dict(B=1, T=136, H=1, HV=3, K=36, V=32, dtype="bf16", chunk=8),        # LDS-staged (K % 8 != 0)
+    dict(B=2, T=16, H=2, HV=4, K=8, V=8, dtype="fp32", chunk=8),           # the tiny fp32 workload's shape
+    dict(B=1, T=256, H=2, HV=4, K=64, V=64, dtype="fp32", chunk=64),       # fp32, K = 64
+])
+@pytest.mark.parametrize("gate_mode", ["const:-20", "mixed"])
+def test_kernels_without_workspace_wide_decay(case, gate_mode):
+    dt = {"bf16": torch.bfloat16, "fp32": torch.float32}[case["dtype"]]
+    shape = {k: case[k] for k in ("B", "T", "H", "HV", "K", "V")}
+    log(f"prefill without workspace {shape} {case['dtype']} g={gate_mode}")
+    inp = prefill_inputs(**shape, dtype=case["dtype"], init_state=True, seed=309, gate=gate_mode)
+    d = gpu(inp)
+    o = torch.full(d["v"].shape, float("nan"), dtype=dt, device="cuda")
+    s = torch.full(d["initial_state"].shape, float("nan"), dtype=torch.float32, device="cuda")
+    assert _abi_fwd_null_workspace(d, o, s, 1 if case["dtype"] == "bf16" else 0,
+                                   case["chunk"]) == kda.KDA_OK
+    ref_o, ref_s = recurrent(**inp)
+    assert_parity(to64(o), ref_o, dt, f"o ({gate_mode})")
+    assert_parity(to64(s), ref_s, dt, f"state ({gate_mode})")
