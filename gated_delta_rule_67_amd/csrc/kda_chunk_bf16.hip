@@ -28,7 +28,7 @@
 // kSpanLim (log2 units). Diagonal blocks use (x_i R_i).(k_j C_j); block I > J uses the column
 // factor k_j C_j exp(G_rI - G_rJ); Gam_i = exp(G_rI) R_i and Gam_C/Gam_j = exp(G_C - G_rJ) C_j.
 // The per-(block, channel) constants come from a small table built once per chunk. A wave
-// whose channels of its block span more (g far below the safe gate's -5) builds its
+// whose channels of its block span more (a mean decay below about -4.4 per token) builds its
 // column factors as one exponential of a difference <= 0 each and its diagonal partial
 // tiles pair by pair (direct_diag), which is exact for any g <= 0.
 #include "kda_device.h"

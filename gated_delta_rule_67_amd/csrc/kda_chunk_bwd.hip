@@ -29,7 +29,10 @@
 // last, exp(G_i - G_j) = exp(G_i - G_r) exp(G_r - G_j) for an output row in block I (r of I),
 // or exp(G_i - G_e) exp(G_e - G_j) for an output column in block J (e of J). Every factor is
 // <= 1 except exp(G_r - G_j) for j in block r's own block and exp(G_i - G_e) for i in e's,
-// which stay below e^75 when g >= -5.
+// which stay below 2^kSpanLim while the block's decay span does. A block with a wider span
+// (a mean decay below about -4.4 per token) leaves those factors out of its products and adds the
+// terms with both tokens inside it one by one (exp of a difference <= 0 each), which is
+// exact for any g <= 0.
 #include "kda_device.h"
 #include "kda_varlen.h"
 
@@ -417,6 +420,29 @@ __global__ __launch_bounds__(512) void prep_kernel(BwdArgs a) {
   for (int J = 0; J < 4; ++J) {
     acc[J] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (J <= w) mmaK<KT>(acc[J], (role == 0 ? qs : ks) + 16 * w * PK, PK, bw + 16 * J * PK, PK, lane);
+  }
+  // block w wider than kSpanLim: its diagonal tile term by term (lane: column j = 16 w + lr,
+  // rows i = 16 w + 4 lq + r; entries j > i are masked below)
+  {
+    bool wl = false;
+    for (int c = lane; c < KT; c += 64) wl |= !(fabsf(G[(16 * w + 15) * PG + c] - G[16 * w * PG + c]) <= kSpanLim);
+    if (wave_any(wl)) {
+      const bf16* xs = role == 0 ? sq : sk;
+      const int j = 16 * w + lr;
+      f32x4 dir = {0.f, 0.f, 0.f, 0.f};
+      for (int c = 0; c < KT; ++c) {
+        const float kj = static_cast<float>(sk[j * PK + c]), gj = G[j * PG + c];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = 16 * w + 4 * lq + r;
+          dir[r] = fmaf(static_cast<float>(xs[i * PK + c]) * kj, ex(G[i * PG + c] - gj), dir[r]);
+        }
+      }
+      if (w == 0) acc[0] = dir;
+      else if (w == 1) acc[1] = dir;
+      else if (w == 2) acc[2] = dir;
+      else acc[3] = dir;
+    }
   }
   __syncthreads();  // qs / ks / bop are dead from here; mr / tf reuse them
   float* smr = reinterpret_cast<float*>(lds + L::mr);
@@ -965,11 +991,13 @@ __global__ __launch_bounds__(64 * NW) void rev_sweep_kernel(BwdArgs a) {
 // reverse cumsum, which plain bf16 rounding of this operand (different in each role) would
 // not preserve. F and E are rounded once and shared by both roles. The operand is built by
 // this wave alone in its own LDS slot ([16][kPC] hi, then lo).
+// wide: block W's span exceeds kSpanLim; its own tokens' operand rows are left out (zero) and
+// their terms are added one by one (diag_terms).
 template <int KT, int W>
 __device__ __forceinline__ void rdp_products(f32x4* adq, f32x4* arow, f32x4* acol, unsigned char* lds,
                                              int wslot, int of, int oft, int oe, int oet,
                                              const float* G, const bf16* sq, const bf16* sk,
-                                             int ch, int lane) {
+                                             int ch, int lane, bool wide) {
   constexpr int PG = KT + 4, PK = KT + 8, rw = 16 * W, ew = rw + 15;
   constexpr int NR = 16 * (W + 1), NC = kC - rw;  // tokens of the row / column role
   constexpr int NP = KT / 32;                     // 16-channel parts per half
@@ -991,7 +1019,7 @@ __device__ __forceinline__ void rdp_products(f32x4* adq, f32x4* arow, f32x4* aco
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int j = j8 + e;
-          const float x = static_cast<float>(sk[j * PK + c]) * ex(gref - G[j * PG + c]);
+          const float x = (wide && j >= rw) ? 0.f : static_cast<float>(sk[j * PK + c]) * ex(gref - G[j * PG + c]);
           const bf16 hi = static_cast<bf16>(x);
           xh[e] = hi;
           xl[e] = static_cast<bf16>(x - static_cast<float>(hi));
@@ -1020,7 +1048,8 @@ __device__ __forceinline__ void rdp_products(f32x4* adq, f32x4* arow, f32x4* aco
       for (int t = 0; t < NO; ++t) {
         const int j8 = 8 * tg + 32 * t;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) f[t][e] = j8 < NC ? ex(G[(rw + j8 + e) * PG + c] - gref) : 0.f;
+        for (int e = 0; e < 8; ++e)
+          f[t][e] = (j8 < NC && !(wide && j8 + e < 16)) ? ex(G[(rw + j8 + e) * PG + c] - gref) : 0.f;
       }
 #pragma unroll
       for (int pass = 0; pass < 2; ++pass) {
@@ -1066,7 +1095,8 @@ struct LocalLds {
   static constexpr int lx = db2 + kC * 4;          // [4][KT] fp32 last-token terms per block
   static constexpr int lx2 = lx + 4 * KT * 4;      // [KT] fp32 rowsum(dS h)
   static constexpr int tot = lx2 + KT * 4;         // [4][KT] fp32 cumsum scratch
-  static constexpr int ph = tot + 4 * KT * 4;      // phase region
+  static constexpr int fdg = tot + 4 * KT * 4;     // [64] fp32 F_tt (as F is stored, bf16)
+  static constexpr int ph = fdg + kC * 4;          // phase region
   // phase 1
   static constexpr int uu = ph;                    // [64][PV] U
   static constexpr int hs = uu + kC * PV * 2;      // [KT][PV] h, then dS
@@ -1105,6 +1135,7 @@ __global__ __launch_bounds__(64 * kLocalWaves) void local_kernel(BwdArgs a) {
   float* db2 = reinterpret_cast<float*>(lds + L::db2);
   float* lx = reinterpret_cast<float*>(lds + L::lx);
   float* lx2 = reinterpret_cast<float*>(lds + L::lx2);
+  float* fdg = reinterpret_cast<float*>(lds + L::fdg);
 
   const int tid = threadIdx.x, lane = tid & 63, w8 = tid >> 6;
   // waves w8 and w8 + 4 share a SIMD; the second takes block 3 - w8, so every SIMD holds one
@@ -1291,12 +1322,20 @@ __global__ __launch_bounds__(64 * kLocalWaves) void local_kernel(BwdArgs a) {
     const int k0 = 32 * x + 8 * lq;
     fuu[x] = k0 < V ? ld8(s_u + (rw + lr) * PV + k0) : bf16x8{};
   }
+  // The term of the chunk's last token (j = 63) in U dS^T enters dG at that token with + (the
+  // last-token sum) and - (through dk's column role): its factor exp(G_C - G_j) is 1 and
+  // depends on no g, so it is left out of both and goes to dk alone (xlast), which keeps dg
+  // free of that cancellation when the decays are extreme.
+  float xlast[NCH];
 #pragma unroll
   for (int cc = 0; cc < NCH; ++cc) {
     f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
     mma_ra(x, fuu, s_hs + (c0 + 16 * cc) * PV, PV, V, lane);  // U dS^T
     const int c = c0 + 16 * cc + lr;
     const float gl = G[(kC - 1) * PG + c];
+    const bool lastrow = w == 3 && lq == 3;  // row r = 3 of this lane is token 63
+    xlast[cc] = lastrow ? x[3] : 0.f;
+    if (lastrow) x[3] = 0.f;
     float part = 0.f;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -1344,18 +1383,57 @@ __global__ __launch_bounds__(64 * kLocalWaves) void local_kernel(BwdArgs a) {
       fv[r] = j <= i ? a.scale * Fo[jj][r] : 0.f;
       evv[r] = j < i ? -sb[i] * Dm[jj][r] : 0.f;
       s_f[i * kPC + j] = static_cast<bf16>(fv[r]);
+      if (j == i) fdg[i] = static_cast<float>(static_cast<bf16>(fv[r]));
       s_e[i * kPC + j] = static_cast<bf16>(evv[r]);
     }
     st4(s_ft + j * kPC + rw + 4 * lq, fv);
     st4(s_et + j * kPC + rw + 4 * lq, evv);
   }
   __syncthreads();
+  // this wave's channels of block w: span within kSpanLim, or its diagonal terms one by one
+  bool wide_l = false;
+  for (int c = c0 + lane; c < c0 + KT / 2; c += 64)
+    wide_l |= !(fabsf(G[ew * PG + c] - G[rw * PG + c]) <= kSpanLim);
+  const bool wide = wave_any(wide_l);
   const int wslot = L::wop + w8 * 32 * kPC * 2;
   switch (w) {
-    case 0: rdp_products<KT, 0>(adq, arow, acol, lds, wslot, L::f, L::ft, L::e, L::et, G, sq, sk, ch, lane); break;
-    case 1: rdp_products<KT, 1>(adq, arow, acol, lds, wslot, L::f, L::ft, L::e, L::et, G, sq, sk, ch, lane); break;
-    case 2: rdp_products<KT, 2>(adq, arow, acol, lds, wslot, L::f, L::ft, L::e, L::et, G, sq, sk, ch, lane); break;
-    default: rdp_products<KT, 3>(adq, arow, acol, lds, wslot, L::f, L::ft, L::e, L::et, G, sq, sk, ch, lane); break;
+    case 0: rdp_products<KT, 0>(adq, arow, acol, lds, wslot, L::f, L::ft, L::e, L::et, G, sq, sk, ch, lane, wide); break;
+    case 1: rdp_products<KT, 1>(adq, arow, acol, lds, wslot, L::f, L::ft, L::e, L::et, G, sq, sk, ch, lane, wide); break;
+    case 2: rdp_products<KT, 2>(adq, arow, acol, lds, wslot, L::f, L::ft, L::e, L::et, G, sq, sk, ch, lane, wide); break;
+    default: rdp_products<KT, 3>(adq, arow, acol, lds, wslot, L::f, L::ft, L::e, L::et, G, sq, sk, ch, lane, wide); break;
+  }
+  // A wide block's terms with both tokens inside it, for the lane's outputs (token
+  // t = rw + 4 lq + r, channel c0 + 16 cc + lr): F and E are zero outside their triangles, so
+  // one factor exp(-|G_t - G_j|) serves both orders.
+  //   dq_t += sum_j F_tj k_j e^(G_t - G_j),   dpos_t += sum_j E_tj k_j e^(G_t - G_j),
+  //   dneg_t += sum_j (F_jt q_j + E_jt k_j) e^(G_j - G_t)
+  // The pair j = t (F_tt q_t k_t, factor 1) enters dG with both signs; it is left out here and
+  // added to dq and dk alone in phase 3, so that dG holds no cancelling terms of that size.
+  float xdq[NCH][4], xdp[NCH][4], xdn[NCH][4];
+#pragma unroll
+  for (int cc = 0; cc < NCH; ++cc)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) xdq[cc][r] = xdp[cc][r] = xdn[cc][r] = 0.f;
+  if (wide) {
+#pragma unroll
+    for (int cc = 0; cc < NCH; ++cc) {
+      const int c = c0 + 16 * cc + lr;
+      for (int jj = 0; jj < 16; ++jj) {
+        const int j = rw + jj;
+        const float gj = G[j * PG + c];
+        const float kj = static_cast<float>(sk[j * PK + c]), qj = static_cast<float>(sq[j * PK + c]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = rw + 4 * lq + r;
+          const float f = j == t ? 0.f : ex(-fabsf(G[t * PG + c] - gj));
+          const float fkj = f * kj;
+          xdq[cc][r] = fmaf(static_cast<float>(s_f[t * kPC + j]), fkj, xdq[cc][r]);
+          xdp[cc][r] = fmaf(static_cast<float>(s_e[t * kPC + j]), fkj, xdp[cc][r]);
+          xdn[cc][r] = fmaf(static_cast<float>(s_f[j * kPC + t]) * qj + static_cast<float>(s_e[j * kPC + t]) * kj,
+                            f, xdn[cc][r]);
+        }
+      }
+    }
   }
   __syncthreads();  // phase 2 operands are dead
 
@@ -1372,12 +1450,15 @@ __global__ __launch_bounds__(64 * kLocalWaves) void local_kernel(BwdArgs a) {
       const int i = rw + 4 * lq + r;
       const float gi = G[i * PG + c];
       const float fr = ex(gi - gr), fc = ex(ge - gi);
-      const float dq = adq[cc][r] * fr;
-      const float dpos = arow[cc][r] * fr, dneg = acol[cc][r] * fc;
-      const float dk = dpos + dneg;
       const float qv = static_cast<float>(sq[i * PK + c]);
       const float kv = static_cast<float>(sk[i * PK + c]);
-      dgs[i * PG + c] = qv * dq + kv * (dpos - dneg);
+      const float dqg = fmaf(adq[cc][r], fr, xdq[cc][r]);  // the parts that enter dG
+      const float dpos = fmaf(arow[cc][r], fr, xdp[cc][r]), dneg = fmaf(acol[cc][r], fc, xdn[cc][r]);
+      dgs[i * PG + c] = qv * dqg + kv * (dpos - dneg);
+      // the self pair (wide blocks) and the last token's U dS^T term: outputs only
+      const float fs = wide ? fdg[i] : 0.f;
+      const float dq = fmaf(fs, kv, dqg);
+      const float dk = dpos + fmaf(fs, qv, dneg) + (r == 3 ? xlast[cc] : 0.f);
       if (!a.dq32) {  // bf16 rows go out below as 16-byte pieces
         sdq[i * PK + c] = static_cast<bf16>(dq);
         sdk[i * PK + c] = static_cast<bf16>(dk);

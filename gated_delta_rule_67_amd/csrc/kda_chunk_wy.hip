@@ -32,9 +32,11 @@
 // d_i = G_i - G_r <= 0, R_i = 2^(d log2 e) <= 1 and C_i = 1/R_i <= 2^kSpanLim while the block's
 // span is at most kSpanLim (log2 units). Diagonal blocks use (x_i R_i).(k_j C_j); block I > J
 // uses the column factor k_j C_j exp(G_rI - G_rJ); Gam_i = exp(G_rI) R_i and
-// Gam_C/Gam_j = exp(G_C - G_rJ) C_j. A block with a wider span (g far below the safe gate's
-// -5) computes its diagonal tiles pair by pair (direct_diag) and its column factors as one
-// exponential of a difference <= 0 each, so the factors are exact for any g <= 0.
+// Gam_C/Gam_j = exp(G_C - G_rJ) C_j. A block with a wider span (a mean decay below about
+// -4.4 per token across it: the safe gate's -5 held for 16 tokens, or the standard gate's
+// unbounded values) computes its diagonal tiles pair by pair (direct_diag) and its column
+// factors as one exponential of a difference <= 0 each, so the factors are exact for any
+// g <= 0.
 #include "kda_device.h"
 #include "kda_varlen.h"
 
@@ -178,7 +180,7 @@ struct LdsA {
 // stores it) turns it into g before anything else reads it.
 //
 // EXACT = false is the launch every call makes. A 16-token block whose decay span exceeds
-// kSpanLim (possible only for g well below the safe gate's -5) cannot use the factored
+// kSpanLim (a mean decay below about -4.4 per token across the block) cannot use the factored
 // diagonal: its wave marks the item in the block's flag bytes (Blk::flag, one per wave) and
 // leaves garbage. EXACT = true, launched right after, reads those flags and recomputes only
 // the marked items, with the wide blocks' diagonal tiles pair by pair (direct_diag) and

@@ -19,7 +19,7 @@
 // within kSpanLim (log2 units), so diagonal blocks use (x_i R_i).(k_j C_j) and off-diagonal
 // blocks (I > J) use the column factor k_j C_j exp(G_rI - G_rJ) <= |k_j|. Two exp2 per
 // token-channel; every other decay factor is a product with a per-(block, channel)
-// constant. A block with a wider span (g far below the safe gate's -5) takes its column
+// constant. A block with a wider span (a mean decay below about -4.4 per token) takes its column
 // factors as one exponential of a difference <= 0 each, and its diagonal tiles are
 // recomputed term by term after the first MFMA stage, which is exact for any g <= 0.
 //

@@ -19,9 +19,11 @@
  *     tensors are dense, contiguous, row-major in the shapes given below.
  *   - q, k, v, g, beta and o share one element type `dtype` (float32 or bfloat16);
  *     states are always float32. o is written in `dtype` (round to nearest even).
- *   - g is the natural-log decay as given; kernels neither clamp nor transform it.
- *     Precondition for kda_chunk_fwd's accuracy: -5 <= g <= 0 (the pages' safe-gate
- *     lower bound); values below -5 are not detected.
+ *   - g is the natural-log decay as given (g <= 0); kernels neither clamp nor transform
+ *     it. Every entry point is exact for any g <= 0, the standard gate's unbounded values
+ *     included (not only the safe gate's -5 <= g <= 0): a 16-token block whose decay span
+ *     exceeds 2^96 (a mean g below about -4.4 across it) takes a term-by-term route for
+ *     the relative decays inside it, slower but exact.
  *   - beta is used as given (already in (0, 1)); one value per (token, value head).
  *   - `stream` is a hipStream_t (NULL = the null stream). Work is enqueued
  *     asynchronously; the library never synchronises and keeps no device
@@ -67,7 +69,7 @@ typedef enum {
  *
  *   q, k           [B, T, H, K]   dtype
  *   v              [B, T, HV, V]  dtype
- *   g              [B, T, HV, K]  dtype   natural-log decay, -5 <= g <= 0
+ *   g              [B, T, HV, K]  dtype   natural-log decay, g <= 0
  *   beta           [B, T, HV]     dtype
  *   initial_state  [B, HV, K, V]  float32, or NULL for zeros
  *   final_state    [B, HV, K, V]  float32 out, or NULL (not returned); may equal

@@ -161,3 +161,55 @@ def test_kernels_without_workspace_wide_decay(case, gate_mode):
     ref_o, ref_s = recurrent(**inp)
     assert_parity(to64(o), ref_o, dt, f"o ({gate_mode})")
     assert_parity(to64(s), ref_s, dt, f"state ({gate_mode})")
+
+
+# ------------------------------------------------------------------ backward
+
+GRADS = ("dq", "dk", "dv", "dg", "dbeta", "dh0")
+
+
+def _bwd_case(inp, seed, chunk=64, what=""):
+    from oracle import recurrent_bwd
+    gen = torch.Generator().manual_seed(seed)
+    B, T, HV, V = inp["v"].shape
+    K = inp["q"].shape[-1]
+    inp = dict(inp, do=torch.randn((B, T, HV, V), generator=gen).to(torch.bfloat16),
+               dht=0.1 * torch.randn((B, HV, K, V), generator=gen))
+    d = gpu(inp)
+    got = kda.kda_chunk_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["do"], d["scale"],
+                            d["initial_state"], d["dht"], chunk)
+    torch.cuda.synchronize()
+    ref = recurrent_bwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["scale"],
+                        inp["do"], inp["initial_state"], inp["dht"])
+    for name, x, r in zip(GRADS, got, ref):
+        assert_parity(to64(x), r, torch.bfloat16, f"{what} {name}")
+
+
+@pytest.mark.parametrize("gate_mode", ["const:-8", "const:-20"])
+def test_backward_constant_wide_decay(gate_mode):
+    log(f"backward B1 T1024 H16 K128 g={gate_mode}")
+    inp = prefill_inputs(1, 1024, 16, 16, 128, 128, "bf16", True, 310, gate=gate_mode)
+    _bwd_case(inp, 311, what=gate_mode)
+
+
+@pytest.mark.parametrize("shape", [
+    dict(B=1, T=512, H=4, HV=4, K=128, V=128),
+    dict(B=2, T=200, H=2, HV=4, K=64, V=48),   # GVA, ragged last chunk
+    dict(B=1, T=128, H=1, HV=2, K=32, V=32),
+])
+def test_backward_mixed_decay(shape):
+    log(f"backward {shape} g=mixed")
+    inp = prefill_inputs(**shape, dtype="bf16", init_state=True, seed=312, gate="mixed")
+    _bwd_case(inp, 313, chunk=64 if shape["T"] % 64 == 0 else 8, what="mixed")
+
+
+def test_backward_standard_gate_values():
+    """The backward on g made by the standard gate (no lower bound) from x ~ 3 N(0, 1)."""
+    B, T, H, HV, K, V = 1, 1024, 16, 16, 128, 128
+    log("backward on standard-gate g, B1 T1024 HV16 K128, x ~ 3 N(0, 1)")
+    inp = prefill_inputs(B, T, H, HV, K, V, "bf16", True, seed=314)
+    gi = gate_inputs(B, T, HV, K, "bf16", seed=315, x_std=3.0)
+    g_ref = gate(gi["x"].double().numpy(), gi["A_log"].double().numpy(),
+                 gi["dt_bias"].double().numpy(), None)
+    inp["g"] = torch.from_numpy(g_ref).to(torch.bfloat16)
+    _bwd_case(inp, 316, what="standard gate")
