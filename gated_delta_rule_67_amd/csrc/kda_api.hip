@@ -21,7 +21,7 @@ size_t bwd_workspace_bytes(int B, int T, int H, int HV, int K, int V, unsigned f
 size_t bwd_varlen_workspace_bytes(int nseq, int T, int H, int HV, int K, int V, unsigned flags);
 size_t wy_varlen_workspace_bytes(int nseq, int T, int HV, int K);
 size_t wy_segmented_workspace_bytes(int B, int T, int HV, int K, int V, int P);
-int wy_segments(int B, int T, int HV, int V, int cus);
+int wy_segments(int B, int T, int HV, int V);
 int device_cu_count();
 hipError_t launch_prefill_wy(const PrefillArgs& p, void* workspace, hipStream_t stream);
 hipError_t launch_prefill_wy_segmented(const PrefillArgs& p, int P, void* workspace,
@@ -109,7 +109,7 @@ size_t kda_chunk_fwd_workspace_size(int B, int T, int H, int HV, int K, int V, i
   if (check_common(B, H, HV, K, V, 1.f, dtype) != KDA_OK) return 0;
   if (dtype != KDA_DTYPE_BF16 || K % 8 != 0 || V % 8 != 0) return 0;
   // with few heads the call runs over segments of the sequence (kda_chunk_fwd_segmented)
-  const int P = kda::wy_segments(B, T, HV, V, kda::device_cu_count());
+  const int P = kda::wy_segments(B, T, HV, V);
   return P > 1 ? kda::wy_segmented_workspace_bytes(B, T, HV, K, V, P)
                : kda::wy_workspace_bytes(B, T, HV, K);
 }

@@ -31,6 +31,8 @@
 // whose channels of its block span more (a mean decay below about -4.4 per token) builds its
 // column factors as one exponential of a difference <= 0 each and its diagonal partial
 // tiles pair by pair (direct_diag), which is exact for any g <= 0.
+#include <atomic>
+
 #include "kda_device.h"
 
 namespace kda {
@@ -692,16 +694,18 @@ hipError_t launch_cfg(const PrefillArgs& a, hipStream_t stream) {
 }  // namespace chunk_bf16
 
 // Number of compute units of the current device (queried once per device).
+// CUs of the current device, for launch grids. The count is cached per device in atomics
+// (relaxed: two first calls store the same value), so concurrent first calls do not race.
 int device_cu_count() {
-  static int cached[64] = {0};
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cached[dev] = n;
+    cached[dev].store(n, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return n;
 }
 
 // bf16 inputs with K % 8 == 0 and 16-byte aligned q/k/g rows. One workgroup per CU at a

@@ -1194,13 +1194,16 @@ SegLayout seg_layout(int B, int T, int HV, int K, int V, int P) {
 }
 }  // namespace wy
 
-// Segments for a fixed-length bf16 prefill on this device: P > 1 cuts each sequence into P
-// segments (P a power of two, T % (64 P) == 0, at least 4 chunks per segment) when the state
-// pass would otherwise leave most CUs idle. The segmented path runs three state passes (the
-// maps Bm and A, then the outputs) and a scan, so it pays only from P >= 8 (measured: P = 4 at
-// B1 T32768 H16 ties with the plain path, P = 16 at H4 is 2.7 times faster): it is used then,
-// else P = 1.
-int wy_segments(int B, int T, int HV, int V, int cus) {
+// Segments for a fixed-length bf16 prefill: P > 1 cuts each sequence into P segments (P a
+// power of two, T % (64 P) == 0, at least 4 chunks per segment) when the state pass would
+// otherwise leave most CUs idle. The segmented path runs three state passes (the maps Bm and A,
+// then the outputs) and a scan, so it pays only from P >= 8 (measured: P = 4 at B1 T32768 H16
+// ties with the plain path, P = 16 at H4 is 2.7 times faster): it is used then, else P = 1.
+// The choice is a function of the arguments alone, taken for a full gfx950 chip (256 CUs),
+// so the workspace size a caller queries and the launch agree whatever device is current.
+constexpr int kSegmentCus = 256;
+int wy_segments(int B, int T, int HV, int V) {
+  const int cus = kSegmentCus;
   const int units = B * HV * ((V + 31) / 32);  // state-pass workgroups at 32 columns each
   if (units * 8 > cus) return 1;
   int P = 1;

@@ -539,7 +539,7 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_prefill_wy(const PrefillArgs& a, void* workspace, hipStream_t stream);
 hipError_t launch_prefill_wy_segmented(const PrefillArgs& a, int P, void* workspace,
                                        hipStream_t stream);
-int wy_segments(int B, int T, int HV, int V, int cus);
+int wy_segments(int B, int T, int HV, int V);
 int device_cu_count();
 
 // Returns hipErrorInvalidValue for shapes the library does not instantiate.
@@ -557,7 +557,7 @@ hipError_t launch_prefill(const void* q, const void* k, const void* v, const voi
   // few heads, over segments of the sequence composed by a scan (wy_segments decides, as the
   // workspace size did, unless the caller fixed `segments`: 1 is the plain two-kernel path).
   if (bf16_inputs && a.vec_qkg && a.vec_v && workspace) {
-    const int P = segments > 0 ? segments : wy_segments(B, T, HV, V, device_cu_count());
+    const int P = segments > 0 ? segments : wy_segments(B, T, HV, V);
     return P > 1 ? launch_prefill_wy_segmented(a, P, workspace, stream)
                  : launch_prefill_wy(a, workspace, stream);
   }

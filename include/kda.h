@@ -27,8 +27,10 @@
  *   - beta is used as given (already in (0, 1)); one value per (token, value head).
  *   - `stream` is a hipStream_t (NULL = the null stream). Work is enqueued
  *     asynchronously; the library never synchronises and keeps no device
- *     allocations or mutable global state (re-entrant, thread-safe), with one
- *     exception: kda_chunk_fwd_noalloc's fixed scratch array per device (see there).
+ *     allocations or mutable global state (re-entrant, thread-safe), with two
+ *     exceptions: each device's CU count is cached once (atomically), and
+ *     kda_chunk_fwd_noalloc keeps a fixed scratch array per device (see there).
+ *     Workspace sizes are functions of the arguments alone.
  *   - The caller owns every buffer. Arguments are validated before any launch;
  *     on a nonzero return nothing was enqueued. Faults inside a kernel surface at
  *     the caller's next synchronisation. No C++ exception crosses this ABI.
@@ -95,8 +97,9 @@ typedef enum {
  */
 /* Bytes of workspace the two-kernel path uses for these arguments: one block per
  * (b, hv, 64-token chunk) for bf16 with K % 8 == 0 and V % 8 == 0, plus the segment maps
- * when few heads make the call run over segments on the current device
- * (kda_chunk_fwd_segmented); else 0 (also 0 for arguments kda_chunk_fwd would reject). */
+ * when few heads make the call run over segments (kda_chunk_fwd_segmented; the choice depends
+ * on the arguments only, not on the current device); else 0 (also 0 for arguments
+ * kda_chunk_fwd would reject). */
 size_t kda_chunk_fwd_workspace_size(int B, int T, int H, int HV, int K, int V,
                                     int chunk_size, int dtype);
 
@@ -366,7 +369,7 @@ int kda_recurrent_step_gated(const void* q, const void* k, const void* v, const 
  * the final state, and a last pass makes o from those entering states. Same arithmetic per
  * chunk as kda_chunk_fwd_ex's two-kernel path; the result differs from it by rounding only.
  * kda_chunk_fwd / kda_chunk_fwd_ex / kda_chunk_fwd_gated take this route by themselves when it
- * pays on the current device (eight or more segments fit the CUs), and size their workspace
+ * pays (eight or more segments fit a full chip's 256 CUs), and size their workspace
  * for it.
  *
  *   segments     >= 1, T % (64 * segments) == 0 (else KDA_ERR_INVALID); 1 is the plain
