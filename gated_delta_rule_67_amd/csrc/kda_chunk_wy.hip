@@ -61,7 +61,9 @@ struct Blk {
   static constexpr int gam = aq + kTri;         // [KT] fp32 Gam_C, rows permuted
   static constexpr int beta = gam + KT * 4;     // [64] fp32 beta
   static constexpr int flag = beta + kC * 4;    // [4] bytes: block w's span exceeds kSpanLim
-  static constexpr int used = flag + 4;
+  static constexpr int summ = flag + 4;         // [4] bytes (block of a workgroup's first item):
+                                                // wave w met a wide block in any of its items
+  static constexpr int used = summ + 4;
   static constexpr int bytes = (used + 1023) / 1024 * 1024;
 };
 
@@ -264,6 +266,7 @@ __global__ __launch_bounds__(256) void factors_kernel(WyArgs a) {
 
   // One item; its q, k, g and beta are in registers when it starts. `next` (or -1) is the
   // item whose inputs it loads once its own are consumed.
+  bool any_wide = false;  // this wave met a wide block (fast launch)
   auto body = [&](int it, int next) {
     unsigned char* blk = a.ws + (size_t)it * W::bytes;
     if constexpr (GATE) {
@@ -395,8 +398,10 @@ __global__ __launch_bounds__(256) void factors_kernel(WyArgs a) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) wide_l |= !(fabsf(d[s][e]) <= kSpanLim);
     const bool wide = wave_any(wide_l);
-    if constexpr (!EXACT)  // the exact launch redoes the item if any of its blocks is wide
+    if constexpr (!EXACT) {  // the exact launch redoes the item if any of its blocks is wide
       if (lane == 0) blk[W::flag + w] = wide ? 1 : 0;
+      any_wide |= wide;
+    }
     if (EXACT && wide) {
       // wide span: every factor as one exponential of a difference <= 0; the diagonal tiles
       // pair by pair
@@ -639,7 +644,10 @@ __global__ __launch_bounds__(256) void factors_kernel(WyArgs a) {
       }
       body(it, next);
     }
+    // the summary the exact launch reads first (the grid is the same in both launches)
+    if (lane == 0) a.ws[(size_t)blockIdx.x * W::bytes + W::summ + w] = any_wide ? 1 : 0;
   } else {
+    if (*reinterpret_cast<const unsigned*>(a.ws + (size_t)blockIdx.x * W::bytes + W::summ) == 0u) return;
     // this workgroup's items (blockIdx.x + m gridDim.x), 256 flags read at once per batch
     __shared__ unsigned sFlag[256];
     const int stride = gridDim.x;
@@ -664,7 +672,7 @@ __global__ __launch_bounds__(256) void factors_kernel(WyArgs a) {
 
 // ================================================================ sequential state pass
 
-constexpr int kDmaWaves = 2;
+constexpr int kDmaWaves = 4;
 
 // Wave pw of the DMA waves copies rows pw, pw + kDmaWaves, ... (1 KB each) of a block into
 // dst; lane l moves bytes 16l..16l+15 of a row (buffer DMA: the row offset is a scalar).
@@ -699,7 +707,7 @@ __device__ __forceinline__ void wait_vmem() {
 // the compute waves never wait on memory issue.
 
 template <int KT, int NW, bool VARLEN>
-__global__ __launch_bounds__(64 * (NW + kDmaWaves)) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(64 * (NW + kDmaWaves)) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void state_kernel(WyArgs a) {
   using W = Blk<KT>;
   constexpr int RQ = KT / 8;
@@ -752,17 +760,17 @@ void state_kernel(WyArgs a) {
   if (wv >= NW) {
     // DMA waves: the factors by LDS DMA; the v tile by range-checked loads (zeros past T
     // or V), written transposed so a compute lane reads 4 consecutive tokens at once.
-    // v tile: 64 rows x BV/8 pieces of 8 columns; lane pl takes pieces pl + 128 e (V % 8 == 0,
-    // so a piece is wholly inside or outside the row)
-    const int pw = wv - NW, pl = 64 * pw + lane;  // 128 lanes
-    constexpr int NPL = BV / 16;                      // pieces per lane
+    // v tile: 64 rows x BV/8 pieces of 8 columns; lane pl takes pieces pl + 64 kDmaWaves e
+    // (V % 8 == 0, so a piece is wholly inside or outside the row)
+    const int pw = wv - NW, pl = 64 * pw + lane;
+    constexpr int NPL = (BV / 8 + kDmaWaves - 1) / kDmaWaves;  // pieces per lane
     constexpr int PPR = BV / 8;                       // pieces per row
     unsigned voff[NPL];
 #pragma unroll
     for (int e = 0; e < NPL; ++e) {
-      const int pc = pl + 128 * e, row = pc / PPR, c8 = pc % PPR;
+      const int pc = pl + 64 * kDmaWaves * e, row = pc / PPR, c8 = pc % PPR;
       const int col = vt_idx * BV + 8 * c8;
-      voff[e] = col < V ? (unsigned)(col * 2) + (unsigned)row * rowb : kOutOfRange;
+      voff[e] = (col < V && row < kC) ? (unsigned)(col * 2) + (unsigned)row * rowb : kOutOfRange;
     }
     bf16x8 rvv[NPL];
     auto load_v = [&](int n) {  // n past the end re-reads the last chunk (no branch)
@@ -778,9 +786,10 @@ void state_kernel(WyArgs a) {
       bf16* vt = reinterpret_cast<bf16*>(dst + VT);
 #pragma unroll
       for (int e = 0; e < NPL; ++e) {
-        const int pc = pl + 128 * e, row = pc / PPR, c8 = pc % PPR;
+        const int pc = pl + 64 * kDmaWaves * e, row = pc / PPR, c8 = pc % PPR;
+        if (row < kC)
 #pragma unroll
-        for (int x = 0; x < 8; ++x) vt[(8 * c8 + x) * PV + row] = rvv[e][x];
+          for (int x = 0; x < 8; ++x) vt[(8 * c8 + x) * PV + row] = rvv[e][x];
       }
     };
     // L2 warm-up one chunk further ahead: the sibling workgroups of a head (V tiles) split
@@ -789,7 +798,7 @@ void state_kernel(WyArgs a) {
     // are issued after the wait for the DMA (vmcnt is in order), so they stay in flight
     // across the barrier; their registers are consumed just before the next reuse.
     constexpr int NB = W::bytes / 1024;
-    constexpr int NPF = (NB * NW + 15) / 16;  // rows per wave when V tiles cover 128 columns
+    constexpr int NPF = (NB * NW + 8 * kDmaWaves - 1) / (8 * kDmaWaves);  // rows per wave, 128 columns
     u32x4 pf[NPF];
 #pragma unroll
     for (int i = 0; i < NPF; ++i) pf[i] = u32x4{0u, 0u, 0u, 0u};
