@@ -63,7 +63,9 @@ struct Blk {
   static constexpr int flag = beta + kC * 4;    // [4] bytes: block w's span exceeds kSpanLim
   static constexpr int summ = flag + 4;         // [4] bytes (block of a workgroup's first item):
                                                 // wave w met a wide block in any of its items
-  static constexpr int used = summ + 4;
+  static constexpr int aql = flag + 16;         // [64][16] bf16 Aq - bf16(Aq) on the diagonal
+                                                // 16 x 16 tiles (row i: tile i / 16)
+  static constexpr int used = aql + kC * 16 * 2;
   static constexpr int bytes = (used + 1023) / 1024 * 1024;
 };
 
@@ -188,8 +190,8 @@ struct LdsA {
 // the marked items, with the wide blocks' diagonal tiles pair by pair (direct_diag) and
 // their column factors as exponentials of differences <= 0. Being its own instantiation,
 // the exact route costs the common one no registers.
-template <int KT, bool L2N, bool VARLEN, bool GATE = false, bool EXACT = false>
-__global__ __launch_bounds__(256) void factors_kernel(WyArgs a) {
+template <int KT, bool L2N, bool VARLEN, bool GATE, bool EXACT>
+__device__ __forceinline__ void factors_body(const WyArgs& a) {
   using L = LdsA<KT>;
   using W = Blk<KT>;
   constexpr int PK = L::PK, PC = L::PC, PM = L::PM;
@@ -465,7 +467,7 @@ __global__ __launch_bounds__(256) void factors_kernel(WyArgs a) {
         }
       }
       float kc[8];
-      bf16x8 KC, QG, KG;
+      bf16x8 KC, QG, KG, KCl, QRl;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float E = e < 4 ? e0[e] : e1[e - 4];
@@ -477,6 +479,8 @@ __global__ __launch_bounds__(256) void factors_kernel(WyArgs a) {
         QR[s][e] = static_cast<bf16>(qr);
         KR[s][e] = static_cast<bf16>(kr);
         KC[e] = static_cast<bf16>(kc[e]);
+        QRl[e] = static_cast<bf16>(qr - to_f32(QR[s][e]));
+        KCl[e] = static_cast<bf16>(kc[e] - to_f32(KC[e]));
         QG[e] = static_cast<bf16>(qr * E);
         KG[e] = static_cast<bf16>(kr * E);
         tKdT[(cA + e) * PC + perm32(i_row)] = static_cast<bf16>(kc[e] * F);
@@ -485,7 +489,11 @@ __global__ __launch_bounds__(256) void factors_kernel(WyArgs a) {
       *reinterpret_cast<bf16x8*>(blk + W::qg + qk_off) = QG;
       *reinterpret_cast<bf16x8*>(blk + W::kg + qk_off) = KG;
       aKd = mfma32(KC, KR[s], aKd);
+      // the diagonal Aq tile with both operands as bf16 pairs (the lo x lo term, ~2^-16 of
+      // the sum, is left out): its entries are the intra-chunk attention's largest
       aQd = mfma32(KC, QR[s], aQd);
+      aQd = mfma32(KCl, QR[s], aQd);
+      aQd = mfma32(KC, QRl, aQd);
 #pragma unroll
       for (int I = 1; I < 4; ++I) {
         if (I > w) {
@@ -536,6 +544,13 @@ __global__ __launch_bounds__(256) void factors_kernel(WyArgs a) {
             qv[J][r] = static_cast<bf16>((j <= i_row) ? aqv[r] : 0.f);
           }
           *reinterpret_cast<f32x4*>(sM + i_row * PM + 16 * J + 4 * lq) = mv;
+          if (J == w) {  // the diagonal tile's rounding residual
+            bf16x4 lo;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              lo[r] = static_cast<bf16>((16 * J + 4 * lq + r <= i_row) ? aqv[r] - to_f32(qv[J][r]) : 0.f);
+            *reinterpret_cast<bf16x4*>(blk + W::aql + (i_row * 16 + 4 * lq) * 2) = lo;
+          }
         }
       }
 #pragma unroll
@@ -668,6 +683,18 @@ __global__ __launch_bounds__(256) void factors_kernel(WyArgs a) {
       lds_barrier();  // the next batch rewrites sFlag
     }
   }
+}
+
+// The launch every call makes, held to two waves per SIMD (two workgroups per CU); and the
+// exact pass, which has the registers of one wave per SIMD for its pairwise diagonal.
+template <int KT, bool L2N, bool VARLEN, bool GATE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void factors_kernel(WyArgs a) {
+  factors_body<KT, L2N, VARLEN, GATE, false>(a);
+}
+
+template <int KT, bool L2N, bool VARLEN, bool GATE>
+__global__ __launch_bounds__(256) void factors_exact_kernel(WyArgs a) {
+  factors_body<KT, L2N, VARLEN, GATE, true>(a);
 }
 
 // ================================================================ sequential state pass
@@ -901,20 +928,25 @@ void state_kernel(WyArgs a) {
         P[J] = mfma32(fx[m & 1][4 + J], sb, P[J]);
       }
     }
-    // beta (V - X), bf16, as B operands of the 32-token steps
-    bf16x8 yb[2];
+    // beta (V - X) as bf16 pairs (hi + lo), B operands of the 32-token steps
+    bf16x8 yb[2], yl[2];
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
-      bf16x4 y[2];
+      bf16x4 y[2], z[2];
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
         const int J = 2 * m + h2;
         const f32x4 bt = load4f(bk + W::beta + (16 * J + 4 * lq) * 4);
         const bf16x4 vv = load4(bk + VT + ((16 * wv + lr) * PV + 16 * J + 4 * lq) * 2);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) y[h2][r] = static_cast<bf16>(bt[r] * (to_f32(vv[r]) - X[J][r]));
+        for (int r = 0; r < 4; ++r) {
+          const float yv = bt[r] * (to_f32(vv[r]) - X[J][r]);
+          y[h2][r] = static_cast<bf16>(yv);
+          z[h2][r] = static_cast<bf16>(yv - to_f32(y[h2][r]));
+        }
       }
       yb[m] = cat8(y[0], y[1]);
+      yl[m] = cat8(z[0], z[1]);
     }
     // (K*Gam_C/Gam)^T fragments and Gam_C for the state update, loaded under U and O
     bf16x8 fk[NCT][2];
@@ -926,20 +958,43 @@ void state_kernel(WyArgs a) {
       gm[ct] = load4f(bk + W::gam + (16 * ct + 4 * lq) * 4);
     }
     // U = T (beta Y); T is lower block-triangular, so block I needs 32-token steps m <= I/2
+    const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
     f32x4 U[4];
-    U[0] = mfma32(ft[0], yb[0], f32x4{0.f, 0.f, 0.f, 0.f});
-    U[1] = mfma32(ft[1], yb[0], f32x4{0.f, 0.f, 0.f, 0.f});
-    U[2] = mfma32(ft[3], yb[1], mfma32(ft[2], yb[0], f32x4{0.f, 0.f, 0.f, 0.f}));
-    U[3] = mfma32(ft[5], yb[1], mfma32(ft[4], yb[0], f32x4{0.f, 0.f, 0.f, 0.f}));
-    bf16x8 ub[2];
+    U[0] = mfma32(ft[0], yl[0], mfma32(ft[0], yb[0], z4));
+    U[1] = mfma32(ft[1], yl[0], mfma32(ft[1], yb[0], z4));
+    U[2] = mfma32(ft[3], yl[1], mfma32(ft[3], yb[1], mfma32(ft[2], yl[0], mfma32(ft[2], yb[0], z4))));
+    U[3] = mfma32(ft[5], yl[1], mfma32(ft[5], yb[1], mfma32(ft[4], yl[0], mfma32(ft[4], yb[0], z4))));
+    // U as bf16 pairs too: the hi and lo parts are both B operands below
+    bf16x8 ub[2], ul[2];
 #pragma unroll
-    for (int m = 0; m < 2; ++m) ub[m] = cat8(cvt4(U[2 * m]), cvt4(U[2 * m + 1]));
-    // O = scale (P + Aq U)
+    for (int m = 0; m < 2; ++m) {
+      const bf16x4 h0 = cvt4(U[2 * m]), h1 = cvt4(U[2 * m + 1]);
+      bf16x4 l0, l1;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        l0[r] = static_cast<bf16>(U[2 * m][r] - to_f32(h0[r]));
+        l1[r] = static_cast<bf16>(U[2 * m + 1][r] - to_f32(h1[r]));
+      }
+      ub[m] = cat8(h0, h1);
+      ul[m] = cat8(l0, l1);
+    }
+    // O = scale (P + Aq U), Aq's diagonal tiles with their residual (Blk::aql). In the A
+    // fragment of step I/2, element e of lane (lr, lq) is token 16 (e >> 2) + 4 lq + (e & 3)
+    // of the step (the order of the U operand), so block I's diagonal tile fills elements
+    // 4 (I & 1) .. + 3 of every lane and the other four are zero.
+    bf16x8 fl[4];
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+      const bf16x4 t = load4(bk + W::aql + ((16 * I + lr) * 16 + 4 * lq) * 2);
+      fl[I] = (I & 1) ? cat8(bf16x4{}, t) : cat8(t, bf16x4{});
+    }
     f32x4 O[4];
-    O[0] = mfma32(fa[0], ub[0], P[0]);
-    O[1] = mfma32(fa[1], ub[0], P[1]);
-    O[2] = mfma32(fa[3], ub[1], mfma32(fa[2], ub[0], P[2]));
-    O[3] = mfma32(fa[5], ub[1], mfma32(fa[4], ub[0], P[3]));
+    O[0] = mfma32(fl[0], ub[0], mfma32(fa[0], ul[0], mfma32(fa[0], ub[0], P[0])));
+    O[1] = mfma32(fl[1], ub[0], mfma32(fa[1], ul[0], mfma32(fa[1], ub[0], P[1])));
+    O[2] = mfma32(fl[2], ub[1], mfma32(fa[3], ul[1], mfma32(fa[3], ub[1],
+           mfma32(fa[2], ul[0], mfma32(fa[2], ub[0], P[2])))));
+    O[3] = mfma32(fl[3], ub[1], mfma32(fa[5], ul[1], mfma32(fa[5], ub[1],
+           mfma32(fa[4], ul[0], mfma32(fa[4], ub[0], P[3])))));
     // stores go out before the state update so they drain under its products
     const auto ro_ = make_rsrc(static_cast<const bf16*>(p.o) + (((size_t)bos + t0) * p.HV + hv) * V,
                                p.o ? (unsigned)nrow * rowb : 0u);  // no o: stores dropped
@@ -951,7 +1006,9 @@ void state_kernel(WyArgs a) {
                                               ro_, vlane, (16 * I + r) * rowb, 0);
     // S = diag(Gam_C) S + (K*Gam_C/Gam)^T U
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) S[ct] = mfma32(fk[ct][1], ub[1], mfma32(fk[ct][0], ub[0], S[ct] * gm[ct]));
+    for (int ct = 0; ct < NCT; ++ct)
+      S[ct] = mfma32(fk[ct][1], ul[1], mfma32(fk[ct][1], ub[1],
+              mfma32(fk[ct][0], ul[0], mfma32(fk[ct][0], ub[0], S[ct] * gm[ct]))));
   };
 
   for (int n = 0; n < NT; n += 2) {
@@ -978,18 +1035,26 @@ template <int KT, bool EXACT>
 static void launch_factors_pass(const WyArgs& a, int grid, hipStream_t stream) {
   const bool l2 = a.p.flags & kFlagQkL2norm, vl = a.ctab != nullptr;
   const bool gt = a.p.flags & kFlagGate;  // fixed-length sequences only (the C ABI's check)
+#define KDA_FACTORS(L2, VL, GT)                                                                   \
+  do {                                                                                            \
+    if (EXACT)                                                                                    \
+      hipLaunchKernelGGL((factors_exact_kernel<KT, L2, VL, GT>), dim3(grid), dim3(256), 0, stream, a); \
+    else                                                                                          \
+      hipLaunchKernelGGL((factors_kernel<KT, L2, VL, GT>), dim3(grid), dim3(256), 0, stream, a);  \
+  } while (0)
   if (gt && l2)
-    hipLaunchKernelGGL((factors_kernel<KT, true, false, true, EXACT>), dim3(grid), dim3(256), 0, stream, a);
+    KDA_FACTORS(true, false, true);
   else if (gt)
-    hipLaunchKernelGGL((factors_kernel<KT, false, false, true, EXACT>), dim3(grid), dim3(256), 0, stream, a);
+    KDA_FACTORS(false, false, true);
   else if (l2 && vl)
-    hipLaunchKernelGGL((factors_kernel<KT, true, true, false, EXACT>), dim3(grid), dim3(256), 0, stream, a);
+    KDA_FACTORS(true, true, false);
   else if (l2)
-    hipLaunchKernelGGL((factors_kernel<KT, true, false, false, EXACT>), dim3(grid), dim3(256), 0, stream, a);
+    KDA_FACTORS(true, false, false);
   else if (vl)
-    hipLaunchKernelGGL((factors_kernel<KT, false, true, false, EXACT>), dim3(grid), dim3(256), 0, stream, a);
+    KDA_FACTORS(false, true, false);
   else
-    hipLaunchKernelGGL((factors_kernel<KT, false, false, false, EXACT>), dim3(grid), dim3(256), 0, stream, a);
+    KDA_FACTORS(false, false, false);
+#undef KDA_FACTORS
 }
 
 // The factors of every item, then the exact pass over the items whose blocks were too wide

@@ -12,12 +12,15 @@ import torch
 #   (b) so that no localised fault hides in the global figure, every row r along the
 #       last axis (one token of one value head for o; one key row of one state)
 #       satisfies RMS_r(err) <= 2e-2 x (RMS_r(ref) + RMS(ref)).
-#   A per-element max-abs bound is not used for bf16: dot products whose bf16-rounded
-#   terms cancel have an error set by the terms, not by the (small) result, and storing
-#   o in bf16 alone moves outliers beyond 10 x RMS by more than 2e-2 x RMS. The
-#   max |err| / RMS figure is logged for reference.
+#   (c) per element, |err| <= 2e-2 x RMS(ref) + 2^-8 x |ref| (elem=True, the default):
+#       the 2^-8 |ref| term is bf16's unit roundoff, so storing an exact result in bf16
+#       always passes (at ratio <= 1), and the rest of the kernel's error has to stay
+#       under what is left. Callers turn it off, with the reason at the call, for the
+#       gradients and for the paths and inputs that do not meet it; the figure is
+#       logged for every bf16 comparison.
 FP32_ATOL = 1e-4
 BF16_REL = 2e-2
+BF16_UNIT = 2.0 ** -8
 
 
 def log(msg):
@@ -29,8 +32,16 @@ def to64(t):
     return t.detach().to("cpu").double().numpy()
 
 
-def assert_parity(out, ref, dtype, what):
-    """dtype: the input dtype of the workload (float32 or bfloat16)."""
+def elem_ratio(err, ref, rms):
+    """max over elements of |err| / (2e-2 RMS(ref) + 2^-8 |ref|) (0 for an all-zero ref)."""
+    if rms == 0:
+        return 0.0 if not np.any(err) else float("inf")
+    return float(np.max(np.abs(err) / (BF16_REL * rms + BF16_UNIT * np.abs(ref))))
+
+
+def assert_parity(out, ref, dtype, what, elem=True):
+    """dtype: the input dtype of the workload (float32 or bfloat16). elem: also assert the
+    per-element bound (c) for bfloat16."""
     out = np.asarray(out, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     assert out.shape == ref.shape, (out.shape, ref.shape)
@@ -47,11 +58,16 @@ def assert_parity(out, ref, dtype, what):
     row_ref = np.sqrt(np.mean(ref ** 2, axis=-1))
     row_err = np.sqrt(np.mean(err ** 2, axis=-1))
     row_ratio = float(np.max(row_err / (row_ref + rms))) if rms > 0 else float(row_err.max())
+    ratio = elem_ratio(err, ref, rms)
     log(f"    {what}: rms err / rms = {rms_err / max(rms, 1e-300):.2e}, worst row "
-        f"{row_ratio:.2e}, max |err| / rms = {np.abs(err).max() / max(rms, 1e-300):.2e}")
+        f"{row_ratio:.2e}, max |err| / rms = {np.abs(err).max() / max(rms, 1e-300):.2e}, "
+        f"per-element bound ratio {ratio:.3f}{'' if elem else ' (not asserted)'}")
     assert rms_err <= BF16_REL * rms, f"{what}: rms err {rms_err:.3e} > {BF16_REL} * rms {rms:.3e}"
     assert np.all(row_err <= BF16_REL * (row_ref + rms)), \
         f"{what}: a row's rms err exceeds 2e-2 x (row rms + rms): worst ratio {row_ratio:.3e}"
+    if elem:
+        assert ratio <= 1.0, \
+            f"{what}: |err| > 2e-2 RMS(ref) + 2^-8 |ref| at some element (worst ratio {ratio:.3f})"
     return rms_err / max(rms, 1e-300)
 
 

@@ -55,9 +55,10 @@ def test_workspace_size(lib):
     ws = lib.kda_chunk_fwd_workspace_size
     per = ws(1, 64, 1, 1, 128, 128, 64, 1)  # one (b, hv, 64-token chunk) block, K = 128
     # the block holds Q*Gam, K*Gam, (K*Gam_C/Gam)^T (64 x 128 bf16 each), the lower block
-    # triangles of T and Aq (rows 0..31 x 32 and rows 32..63 x 64, bf16), Gam_C (128 fp32) and
-    # beta (64 fp32), in whole kilobytes
-    need = 3 * 64 * 128 * 2 + 2 * (32 * 32 + 32 * 64) * 2 + 128 * 4 + 64 * 4
+    # triangles of T and Aq (rows 0..31 x 32 and rows 32..63 x 64, bf16), Gam_C (128 fp32),
+    # beta (64 fp32) and the residual of Aq's four diagonal 16 x 16 tiles (64 x 16 bf16), in
+    # whole kilobytes
+    need = 3 * 64 * 128 * 2 + 2 * (32 * 32 + 32 * 64) * 2 + 128 * 4 + 64 * 4 + 64 * 16 * 2
     assert need <= per < need + 1024 and per % 1024 == 0
     assert ws(4, 8192, 16, 16, 128, 128, 64, 1) == 4 * 16 * 128 * per
     assert ws(2, 65, 4, 8, 128, 64, 1, 1) == 2 * 8 * 2 * per     # a partial last chunk counts

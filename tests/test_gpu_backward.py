@@ -45,7 +45,8 @@ def _ref(inp):
 
 def _check(got, ref, what=""):
     for name, x, r in zip(NAMES, got, ref):
-        assert_parity(to64(x), r, torch.bfloat16, f"{what} {name}")
+        # gradients: the RMS and row criteria (the per-element bound is for the forward)
+        assert_parity(to64(x), r, torch.bfloat16, f"{what} {name}", elem=False)
 
 
 @pytest.mark.parametrize("shape", [

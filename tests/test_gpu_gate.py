@@ -265,6 +265,7 @@ def test_training_chain_through_the_gate():
     refs = recurrent_bwd(inp["q"], inp["k"], inp["v"], g_in, inp["beta"], inp["scale"], do,
                          inp["initial_state"])
     dx_ref, dA_ref, db_ref = gate_bwd(x64, A64, b64, refs[3], -5.0)
-    assert_parity(to64(dx), dx_ref, torch.bfloat16, "dx")
-    assert_parity(to64(db), db_ref, torch.bfloat16, "ddt_bias")
-    assert_parity(to64(dA)[None], dA_ref[None], torch.bfloat16, "dA_log")
+    # gradients: the RMS and row criteria (the per-element bound is for the forward)
+    assert_parity(to64(dx), dx_ref, torch.bfloat16, "dx", elem=False)
+    assert_parity(to64(db), db_ref, torch.bfloat16, "ddt_bias", elem=False)
+    assert_parity(to64(dA)[None], dA_ref[None], torch.bfloat16, "dA_log", elem=False)

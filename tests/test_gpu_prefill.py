@@ -3,8 +3,9 @@
 Small workloads are compared element by element in full; the full-size workloads
 (B4 T8192 H16 K=V=128 and B1 T32768 H96 K=V=128) run in the configuration the bench
 times and are compared on sampled heads, which the oracle computes one by one.
-Tolerances: float32 inputs 1e-4 max-abs; bf16 inputs 2e-2 x RMS(reference), on o and
-on the final state."""
+Tolerances: float32 inputs 1e-4 max-abs; bf16 inputs 2e-2 x RMS(reference) on o and on
+the final state, every row within 2e-2 (row RMS + RMS), and every element within
+2e-2 RMS + 2^-8 |ref| (bf16's unit roundoff) except where a test says why not."""
 
 import ctypes
 
@@ -30,11 +31,11 @@ def _gpu_fwd(inp, chunk=64):
     return o, s
 
 
-def _check_full(inp, dtype, chunk=64, what=""):
+def _check_full(inp, dtype, chunk=64, what="", elem=True):
     o, s = _gpu_fwd(inp, chunk)
     o_ref, s_ref = recurrent(**inp)
-    assert_parity(to64(o), o_ref, DT[dtype], f"{what} o")
-    assert_parity(to64(s), s_ref, DT[dtype], f"{what} state")
+    assert_parity(to64(o), o_ref, DT[dtype], f"{what} o", elem=elem)
+    assert_parity(to64(s), s_ref, DT[dtype], f"{what} state", elem=elem)
 
 
 def test_tiny_fp32():
@@ -64,7 +65,8 @@ def test_gva_bf16():
 def test_small_shapes(shape, dtype):
     log(f"prefill small {shape} {dtype}")
     inp = prefill_inputs(**shape, dtype=dtype, init_state=True, seed=sum(shape.values()))
-    _check_full(inp, dtype, chunk=8, what=str(shape))
+    # V % 8 != 0 takes the fused kernel, which rounds every operand once (no hi + lo pairs)
+    _check_full(inp, dtype, chunk=8, what=str(shape), elem=shape["V"] % 8 == 0)
 
 
 @pytest.mark.parametrize("gate,beta", [("slow", "default"), ("zero", "default"),
@@ -74,10 +76,14 @@ def test_stress_gates(gate, beta):
     log(f"prefill stress gate={gate} beta={beta} (B1 T1024 H=HV=16 K=V=128 bf16)")
     inp = prefill_inputs(1, 1024, 16, 16, 128, 128, "bf16", True, 77, gate=gate, beta=beta)
     o, s = _gpu_fwd(inp)
+    # beta ~ 1e-3 with the default decay: o is the initial state's readout (Q*Gam) S for a
+    # few tokens and ~0 after, so RMS(o) is far below those tokens' terms and one bf16
+    # rounding of Q*Gam and of S there exceeds 2e-2 RMS; the per-element bound is logged
+    elem = beta != "small"
     for hv in (0, 7, 15):
         ref_o, ref_s = recurrent(**head_slice(inp, 0, hv, 1))
-        assert_parity(to64(o[:, :, hv:hv + 1]), ref_o, torch.bfloat16, f"o head {hv}")
-        assert_parity(to64(s[:, hv:hv + 1]), ref_s, torch.bfloat16, f"state head {hv}")
+        assert_parity(to64(o[:, :, hv:hv + 1]), ref_o, torch.bfloat16, f"o head {hv}", elem=elem)
+        assert_parity(to64(s[:, hv:hv + 1]), ref_s, torch.bfloat16, f"state head {hv}", elem=elem)
 
 
 def test_zero_input_leaves_state_unchanged():
@@ -159,8 +165,9 @@ def test_in_place_state_and_poisoned_output(workspace):
     o = torch.full(d["v"].shape, float("nan"), dtype=torch.bfloat16, device="cuda")
     assert _abi_fwd(d, state, state, o, workspace) == kda.KDA_OK
     ref_o, ref_s = recurrent(**inp)
-    assert_parity(to64(o), ref_o, torch.bfloat16, "o")
-    assert_parity(to64(state), ref_s, torch.bfloat16, "state")
+    # the fused kernel (no workspace) rounds every operand once: no per-element bound
+    assert_parity(to64(o), ref_o, torch.bfloat16, "o", elem=workspace)
+    assert_parity(to64(state), ref_s, torch.bfloat16, "state", elem=workspace)
 
 
 @pytest.mark.parametrize("shape", [
@@ -177,8 +184,9 @@ def test_fused_and_factored_paths(shape):
         o = torch.empty_like(d["v"])
         s = torch.empty_like(d["initial_state"])
         assert _abi_fwd(d, d["initial_state"], s, o, workspace, chunk=8) == kda.KDA_OK
-        assert_parity(to64(o), ref_o, torch.bfloat16, f"o workspace={workspace}")
-        assert_parity(to64(s), ref_s, torch.bfloat16, f"state workspace={workspace}")
+        # the fused kernel (no workspace) rounds every operand once: no per-element bound
+        assert_parity(to64(o), ref_o, torch.bfloat16, f"o workspace={workspace}", elem=workspace)
+        assert_parity(to64(s), ref_s, torch.bfloat16, f"state workspace={workspace}", elem=workspace)
 
 
 def test_no_initial_state_and_no_final_state():
@@ -223,7 +231,9 @@ def test_degenerate_inputs(dtype):
     # beta = 0: every token leaves the (decayed) state as it is
     inp = prefill_inputs(1, 128, 2, 2, K, K, dtype, True, 91)
     inp["beta"] = torch.zeros_like(inp["beta"])
-    _check_full(inp, dtype, what="beta=0")
+    # o is the decayed initial state's readout alone, largest at the first tokens: one bf16
+    # rounding of Q*Gam and of S there exceeds 2e-2 RMS(o); the per-element bound is logged
+    _check_full(inp, dtype, what="beta=0", elem=False)
     # T = 8 with chunk 8 (the shortest sequence chunk_size allows; one-token sequences are
     # covered by the packed entry point's tests)
     _check_full(prefill_inputs(2, 8, 1, 2, K, K, dtype, True, 92), dtype, chunk=8, what="T=8")
@@ -237,7 +247,9 @@ def test_degenerate_inputs(dtype):
     # a large initial state (|S0| ~ 30)
     inp = prefill_inputs(1, 64, 1, 2, K, K, dtype, True, 94)
     inp["initial_state"] = inp["initial_state"] * 300.0
-    _check_full(inp, dtype, what="large state")
+    # o = (Q*Gam) S + Aq U with both terms ~30x the result (the delta rule removes what the
+    # state predicts): bf16 rounding of the terms exceeds the bound; logged, not asserted
+    _check_full(inp, dtype, what="large state", elem=False)
 
 
 @pytest.mark.parametrize("shape", [dict(B=2, T=512, H=2, HV=4, K=128, V=128),   # two kernels
