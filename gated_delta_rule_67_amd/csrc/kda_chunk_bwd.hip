@@ -33,6 +33,8 @@
 // (a mean decay below about -4.4 per token) leaves those factors out of its products and adds the
 // terms with both tokens inside it one by one (exp of a difference <= 0 each), which is
 // exact for any g <= 0.
+#include <atomic>
+
 #include "kda_device.h"
 #include "kda_varlen.h"
 
@@ -628,9 +630,10 @@ struct SweepLds {
   static constexpr int dot = rbt + kC * 4;              // [BV][kPC] dO^T
   static constexpr int dst = dot + BV * kPC * 2;        // [BV][PK] dS^T
   static constexpr int dut = dst + BV * PK * 2;         // [BV][kPC] dU^T
-  static constexpr int but = dut + BV * kPC * 2;        // [BV][kPC] (beta Ut)^T
-  static constexpr int rev_total = but + BV * kPC * 2;
-  static_assert(fwd_total <= 160 * 1024 && rev_total <= 160 * 1024, "LDS");
+  // (beta Ut)^T takes dO^T's bytes once dO's last product has read them, which keeps the two
+  // sweeps within one CU's LDS together (68,864 + 91,392 B at K = 128): they run side by side
+  static constexpr int rev_total = dut + BV * kPC * 2;
+  static_assert(fwd_total + rev_total <= 160 * 1024, "the two sweeps side by side on one CU");
 };
 
 __device__ __forceinline__ void sweep_tile(int nvt, int nh, int& head, int& vt_idx) {
@@ -845,8 +848,8 @@ __global__ __launch_bounds__(64 * NW) void rev_sweep_kernel(BwdArgs a) {
   const int lr = lane & 15, lq = lane >> 4;
   bf16* s_dst = reinterpret_cast<bf16*>(lds + L::dst) + 16 * w * PK;
   bf16* s_dut = reinterpret_cast<bf16*>(lds + L::dut) + 16 * w * kPC;
-  bf16* s_but = reinterpret_cast<bf16*>(lds + L::but) + 16 * w * kPC;
   bf16* s_dow = s_dot + 16 * w * kPC;
+  bf16* s_but = s_dow;  // written after the last read of this wave's dO^T rows
 
   const int nvt = (a.V + BV - 1) / BV;
   int head, vt_idx;
@@ -944,6 +947,14 @@ __global__ __launch_bounds__(64 * NW) void rev_sweep_kernel(BwdArgs a) {
       mmaK<KT>(q, s_kc + 16 * I * PK, PK, s_dst, PK, lane);
       st4(s_dut + lr * kPC + 16 * I + 4 * lq, a.scale * p + q);
     }
+    // dS <- Gam_C dS + scale Qg^T dO (dO^T's last read; the LDS copy of dS stays for the store)
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      f32x4 p = f32x4{0.f, 0.f, 0.f, 0.f};
+      mmaK<kC>(p, s_qgt + 16 * ct * kPC, kPC, s_dow, kPC, lane);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) D[ct][r] = D[ct][r] * s_gam[16 * ct + 4 * lq + r] + a.scale * p[r];
+    }
     // Ut = T^T dU; beta Ut
     const size_t trow = (sq_.slot0 + n) * kC;
 #pragma unroll
@@ -959,14 +970,13 @@ __global__ __launch_bounds__(64 * NW) void rev_sweep_kernel(BwdArgs a) {
       }
       st4(s_but + lr * kPC + 16 * I + 4 * lq, y);
     }
-    // dS <- Gam_C dS + scale Qg^T dO - Kg^T (beta Ut)
+    // dS <- dS - Kg^T (beta Ut)
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
-      f32x4 p = f32x4{0.f, 0.f, 0.f, 0.f}, q = f32x4{0.f, 0.f, 0.f, 0.f};
-      mmaK<kC>(p, s_qgt + 16 * ct * kPC, kPC, s_dow, kPC, lane);
+      f32x4 q = f32x4{0.f, 0.f, 0.f, 0.f};
       mmaK<kC>(q, s_kgt + 16 * ct * kPC, kPC, s_but, kPC, lane);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) D[ct][r] = D[ct][r] * s_gam[16 * ct + 4 * lq + r] + a.scale * p[r] - q[r];
+      for (int r = 0; r < 4; ++r) D[ct][r] -= q[r];
     }
     // dS of this chunk to the workspace (its LDS copy is intact until the next chunk)
     store_state_tile<KT, false>(a.dsn + (sq_.slot0 + n) * KT * V, V, vt_idx * BV + 16 * w, s_dst, PK,
@@ -1633,6 +1643,35 @@ Layout varlen_layout(int nseq, int T, int H, int HV, int K, int V, unsigned flag
   return layout((size_t)HV * NC, (size_t)T, needs_fp32_dqk(H, HV, flags), K, V, HV, nseq, NC);
 }
 
+// The stream the forward sweep runs on, beside the reverse sweep on the caller's stream: the
+// two read only prep's blocks (and their own inputs), not each other's outputs, and each
+// leaves most of a CU idle. One non-blocking stream per device, at the default priority, made
+// on the first call on that device and kept until the process ends.
+constexpr int kMaxSideDevices = 64;
+std::atomic<hipStream_t> side_streams[kMaxSideDevices];
+
+hipError_t side_stream(hipStream_t* out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxSideDevices) return hipErrorInvalidDevice;
+  hipStream_t s = side_streams[dev].load(std::memory_order_acquire);
+  if (s == nullptr) {
+    hipStream_t made = nullptr;
+    e = hipStreamCreateWithFlags(&made, hipStreamNonBlocking);
+    if (e != hipSuccess) return e;
+    hipStream_t expected = nullptr;
+    if (side_streams[dev].compare_exchange_strong(expected, made, std::memory_order_acq_rel)) {
+      s = made;
+    } else {  // another thread made one first
+      (void)hipStreamDestroy(made);
+      s = expected;
+    }
+  }
+  *out = s;
+  return hipSuccess;
+}
+
 template <int KT>
 hipError_t launch_cfg(BwdArgs a, hipStream_t stream) {
   const int items = a.ctab ? a.HV * a.NC : a.B * a.HV * a.NT;
@@ -1641,8 +1680,26 @@ hipError_t launch_cfg(BwdArgs a, hipStream_t stream) {
   hipLaunchKernelGGL((prep_kernel<KT>), dim3(pgrid), dim3(512), 0, stream, a);
   constexpr int NW = 2;
   const int sweeps = a.B * a.HV * ((a.V + 16 * NW - 1) / (16 * NW));
-  hipLaunchKernelGGL((fwd_sweep_kernel<KT, NW>), dim3(sweeps), dim3(64 * NW), 0, stream, a);
-  hipLaunchKernelGGL((rev_sweep_kernel<KT, NW>), dim3(sweeps), dim3(64 * NW), 0, stream, a);
+  // fork: the forward sweep on the side stream once prep is done; join before local
+  hipStream_t side = nullptr;
+  hipEvent_t forked = nullptr, joined = nullptr;
+  hipError_t e = side_stream(&side);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&forked, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&joined, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventRecord(forked, stream);
+  if (e == hipSuccess) e = hipStreamWaitEvent(side, forked, 0);
+  if (e == hipSuccess) {
+    hipLaunchKernelGGL((fwd_sweep_kernel<KT, NW>), dim3(sweeps), dim3(64 * NW), 0, side, a);
+    e = hipEventRecord(joined, side);
+  }
+  if (e == hipSuccess) {
+    hipLaunchKernelGGL((rev_sweep_kernel<KT, NW>), dim3(sweeps), dim3(64 * NW), 0, stream, a);
+    e = hipStreamWaitEvent(stream, joined, 0);
+  }
+  // released once their work is done
+  if (forked) (void)hipEventDestroy(forked);
+  if (joined) (void)hipEventDestroy(joined);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL((local_kernel<KT>), dim3(items), dim3(64 * kLocalWaves), 0, stream, a);
   const size_t rows = a.ctab ? (size_t)a.T : (size_t)a.B * a.T;  // packed: one row of T tokens
   if (a.flags & kFlagQkL2norm) {

@@ -27,10 +27,14 @@
  *   - beta is used as given (already in (0, 1)); one value per (token, value head).
  *   - `stream` is a hipStream_t (NULL = the null stream). Work is enqueued
  *     asynchronously; the library never synchronises and keeps no device
- *     allocations or mutable global state (re-entrant, thread-safe), with two
- *     exceptions: each device's CU count is cached once (atomically), and
- *     kda_chunk_fwd_noalloc keeps a fixed scratch array per device (see there).
- *     Workspace sizes are functions of the arguments alone.
+ *     allocations or mutable global state (re-entrant, thread-safe), with three
+ *     exceptions: each device's CU count is cached once (atomically);
+ *     kda_chunk_fwd_noalloc keeps a fixed scratch array per device (see there); and
+ *     the chunked backward forks one of its kernels onto a second stream of the
+ *     device (non-blocking, default priority, made once per device, atomically, and
+ *     kept until the process ends), joined back by events recorded per call, so its
+ *     work is still ordered after what `stream` held before the call and before what
+ *     follows it. Workspace sizes are functions of the arguments alone.
  *   - The caller owns every buffer. Arguments are validated before any launch;
  *     on a nonzero return nothing was enqueued. Faults inside a kernel surface at
  *     the caller's next synchronisation. No C++ exception crosses this ABI.
