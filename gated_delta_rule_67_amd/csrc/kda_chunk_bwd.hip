@@ -306,6 +306,27 @@ __device__ __forceinline__ void mmaK(f32x4& acc, const bf16* a, int lda, const b
   }
 }
 
+// The B fragments of one 16-column operand (contraction index contiguous, rows of pitch
+// ldb), loaded once for all the products of a step that share them; and the product that
+// takes them from registers (A fragments from LDS as in mmaK).
+template <int KK>
+__device__ __forceinline__ void load_b(bf16x8* bf, const bf16* bt, int ldb, int lane) {
+  const int r = lane & 15, q8 = (lane >> 4) * 8;
+#pragma unroll
+  for (int k0 = 0; k0 < KK; k0 += 32)
+    bf[k0 / 32] = (k0 + 32 <= KK || q8 < KK - k0) ? ld8(bt + r * ldb + k0 + q8) : bf16x8{};
+}
+
+template <int KK>
+__device__ __forceinline__ void mmaKb(f32x4& acc, const bf16* a, int lda, const bf16x8* bf, int lane) {
+  const int r = lane & 15, q8 = (lane >> 4) * 8;
+#pragma unroll
+  for (int k0 = 0; k0 < KK; k0 += 32) {
+    const bf16x8 av = (k0 + 32 <= KK || q8 < KK - k0) ? ld8(a + r * lda + k0 + q8) : bf16x8{};
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bf[k0 / 32], acc, 0, 0, 0);
+  }
+}
+
 // ============================================================================ prep
 template <int KT>
 struct PrepLds {
@@ -792,10 +813,12 @@ __global__ __launch_bounds__(64 * NW) void fwd_sweep_kernel(BwdArgs a) {
     const auto rw0 = rsrc(a.w0 + trow * V, (unsigned)kC * V * 2);
     const auto ru = rsrc(a.u + trow * V, (unsigned)kC * V * 2);
     const unsigned lane_off = vok ? (unsigned)(4 * lq * V + vc) * 2 : 0x80000000u;
+    bf16x8 bh[KT / 32];
+    load_b<KT>(bh, s_ht, PK, lane);
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
       f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
-      mmaK<KT>(x, s_kg + 16 * I * PK, PK, s_ht, PK, lane);
+      mmaKb<KT>(x, s_kg + 16 * I * PK, PK, bh, lane);
       f32x4 w0, y;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -807,21 +830,25 @@ __global__ __launch_bounds__(64 * NW) void fwd_sweep_kernel(BwdArgs a) {
       st4(s_yt + lr * kPC + 16 * I + 4 * lq, y);
     }
     // U = T Y
+    bf16x8 by[kC / 32];
+    load_b<kC>(by, s_yt, kPC, lane);
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
       f32x4 uv = f32x4{0.f, 0.f, 0.f, 0.f};
-      mmaK<kC>(uv, s_tm + 16 * I * kPC, kPC, s_yt, kPC, lane);
+      mmaKb<kC>(uv, s_tm + 16 * I * kPC, kPC, by, lane);
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         bstore1(static_cast<bf16>(uv[r]), ru, lane_off + (unsigned)((16 * I + r) * V) * 2);
       st4(s_uu + lr * kPC + 16 * I + 4 * lq, uv);
     }
     // h <- Gam_C h + Kc^T U
+    bf16x8 bu[kC / 32];
+    load_b<kC>(bu, s_uu, kPC, lane);
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) S[ct][r] *= s_gam[16 * ct + 4 * lq + r];
-      mmaK<kC>(S[ct], s_kct + 16 * ct * kPC, kPC, s_uu, kPC, lane);
+      mmaKb<kC>(S[ct], s_kct + 16 * ct * kPC, kPC, bu, lane);
     }
     // h of this chunk to the workspace (its LDS copy is intact until the next chunk)
     store_state_tile<KT, true>(a.h + (sq_.slot0 + n) * KT * V, V, vt_idx * BV + 16 * w, s_ht, PK, lane);
@@ -940,27 +967,32 @@ __global__ __launch_bounds__(64 * NW) void rev_sweep_kernel(BwdArgs a) {
     if (n > 0) fetch(n - 1);
     __syncthreads();
     // dU = scale Aq^T dO + Kc dS
+    bf16x8 bdo[kC / 32], bds[KT / 32];
+    load_b<kC>(bdo, s_dow, kPC, lane);
+    load_b<KT>(bds, s_dst, PK, lane);
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
       f32x4 p = f32x4{0.f, 0.f, 0.f, 0.f}, q = f32x4{0.f, 0.f, 0.f, 0.f};
-      mmaK<kC>(p, s_aqt + 16 * I * kPC, kPC, s_dow, kPC, lane);
-      mmaK<KT>(q, s_kc + 16 * I * PK, PK, s_dst, PK, lane);
+      mmaKb<kC>(p, s_aqt + 16 * I * kPC, kPC, bdo, lane);
+      mmaKb<KT>(q, s_kc + 16 * I * PK, PK, bds, lane);
       st4(s_dut + lr * kPC + 16 * I + 4 * lq, a.scale * p + q);
     }
     // dS <- Gam_C dS + scale Qg^T dO (dO^T's last read; the LDS copy of dS stays for the store)
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
       f32x4 p = f32x4{0.f, 0.f, 0.f, 0.f};
-      mmaK<kC>(p, s_qgt + 16 * ct * kPC, kPC, s_dow, kPC, lane);
+      mmaKb<kC>(p, s_qgt + 16 * ct * kPC, kPC, bdo, lane);
 #pragma unroll
       for (int r = 0; r < 4; ++r) D[ct][r] = D[ct][r] * s_gam[16 * ct + 4 * lq + r] + a.scale * p[r];
     }
     // Ut = T^T dU; beta Ut
     const size_t trow = (sq_.slot0 + n) * kC;
+    bf16x8 bdu[kC / 32];
+    load_b<kC>(bdu, s_dut, kPC, lane);
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
       f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
-      mmaK<kC>(x, s_tt + 16 * I * kPC, kPC, s_dut, kPC, lane);
+      mmaKb<kC>(x, s_tt + 16 * I * kPC, kPC, bdu, lane);
       f32x4 y;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -971,10 +1003,12 @@ __global__ __launch_bounds__(64 * NW) void rev_sweep_kernel(BwdArgs a) {
       st4(s_but + lr * kPC + 16 * I + 4 * lq, y);
     }
     // dS <- dS - Kg^T (beta Ut)
+    bf16x8 bbu[kC / 32];
+    load_b<kC>(bbu, s_but, kPC, lane);
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
       f32x4 q = f32x4{0.f, 0.f, 0.f, 0.f};
-      mmaK<kC>(q, s_kgt + 16 * ct * kPC, kPC, s_but, kPC, lane);
+      mmaKb<kC>(q, s_kgt + 16 * ct * kPC, kPC, bbu, lane);
 #pragma unroll
       for (int r = 0; r < 4; ++r) D[ct][r] -= q[r];
     }
