@@ -203,7 +203,7 @@ def copy_ceiling(torch, nbytes=1 << 30, reps=20):
     Run first, it also brings the clocks up before the prefill is timed."""
     src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
     dst = torch.empty_like(src)
-    for _ in range(20):
+    for _ in range(50):  # about 20 ms of copies: the clocks' ramp on a fresh box
         dst.copy_(src)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
