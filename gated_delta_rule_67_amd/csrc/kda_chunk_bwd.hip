@@ -1033,92 +1033,111 @@ __global__ __launch_bounds__(64 * NW) void rev_sweep_kernel(BwdArgs a) {
 // The scaled q / k operand goes in as a bf16 pair hi + lo (two products): the gradient terms
 // of Aq and Mr enter dG once through each role with opposite signs and cancel in the
 // reverse cumsum, which plain bf16 rounding of this operand (different in each role) would
-// not preserve. F and E are rounded once and shared by both roles. The operand is built by
-// this wave alone in its own LDS slot ([16][kPC] hi, then lo).
+// not preserve. F and E are rounded once and shared by both roles. Lane (cl, tg) builds the
+// operand's tokens 8 tg + 32 s .. + 7 of channel cl, which is exactly its B fragment of k step
+// s, so the operand stays in registers; the A fragments (this block's rows of F and E, of F^T
+// and E^T) are the same for every channel part and are loaded once.
 // wide: block W's span exceeds kSpanLim; its own tokens' operand rows are left out (zero) and
 // their terms are added one by one (diag_terms).
 template <int KT, int W>
-__device__ __forceinline__ void rdp_products(f32x4* adq, f32x4* arow, f32x4* acol, unsigned char* lds,
-                                             int wslot, int of, int oft, int oe, int oet,
+__device__ __forceinline__ void rdp_products(f32x4* adq, f32x4* arow, f32x4* acol, const unsigned char* lds,
+                                             int of, int oft, int oe, int oet,
                                              const float* G, const bf16* sq, const bf16* sk,
                                              int ch, int lane, bool wide) {
   constexpr int PG = KT + 4, PK = KT + 8, rw = 16 * W, ew = rw + 15;
   constexpr int NR = 16 * (W + 1), NC = kC - rw;  // tokens of the row / column role
+  constexpr int SR = (NR + 31) / 32, SC = (NC + 31) / 32;  // their k steps of 32 tokens
   constexpr int NP = KT / 32;                     // 16-channel parts per half
-  const bf16* s_f = reinterpret_cast<const bf16*>(lds + of) + rw * kPC;
-  const bf16* s_e = reinterpret_cast<const bf16*>(lds + oe) + rw * kPC;
-  const bf16* s_ft = reinterpret_cast<const bf16*>(lds + oft) + rw * kPC + rw;
-  const bf16* s_et = reinterpret_cast<const bf16*>(lds + oet) + rw * kPC + rw;
-  bf16* s_hi = reinterpret_cast<bf16*>(lds + wslot);
-  bf16* s_lo = s_hi + 16 * kPC;
-  const int cl = lane & 15, tg = lane >> 4;  // channel in the part, token-octet group
+  const int cl = lane & 15, tg = lane >> 4, q8 = 8 * tg;  // channel in the part, token octet
+  bf16x8 af[SR], ae[SR], aft[SC], aet[SC];  // zeros past the role's tokens
+  {
+    const bf16* s_f = reinterpret_cast<const bf16*>(lds + of) + (rw + cl) * kPC;
+    const bf16* s_e = reinterpret_cast<const bf16*>(lds + oe) + (rw + cl) * kPC;
+    const bf16* s_ft = reinterpret_cast<const bf16*>(lds + oft) + (rw + cl) * kPC + rw;
+    const bf16* s_et = reinterpret_cast<const bf16*>(lds + oet) + (rw + cl) * kPC + rw;
+#pragma unroll
+    for (int s = 0; s < SR; ++s) {
+      const bool ok = 32 * s + q8 < NR;
+      af[s] = ok ? ld8(s_f + 32 * s + q8) : bf16x8{};
+      ae[s] = ok ? ld8(s_e + 32 * s + q8) : bf16x8{};
+    }
+#pragma unroll
+    for (int s = 0; s < SC; ++s) {
+      const bool ok = 32 * s + q8 < NC;
+      aft[s] = ok ? ld8(s_ft + 32 * s + q8) : bf16x8{};
+      aet[s] = ok ? ld8(s_et + 32 * s + q8) : bf16x8{};
+    }
+  }
+  auto mfma = [](const bf16x8& x, const bf16x8& y, f32x4 acc) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, y, acc, 0, 0, 0);
+  };
 #pragma unroll
   for (int part = 0; part < NP; ++part) {
     const int c = ch * (KT / 2) + 16 * part + cl;
-    {  // row role
+    {  // row role: operand k_j exp(G_rw - G_j) over tokens 0 .. rw + 15
       const float gref = G[rw * PG + c];
+      bf16x8 bh[SR], bl[SR];
 #pragma unroll
-      for (int j8 = 8 * tg; j8 < NR; j8 += 32) {
-        bf16x8 xh, xl;
+      for (int s = 0; s < SR; ++s) {
+        const int j8 = 32 * s + q8;
+        bh[s] = bl[s] = bf16x8{};
+        if (j8 < NR) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int j = j8 + e;
-          const float x = (wide && j >= rw) ? 0.f : static_cast<float>(sk[j * PK + c]) * ex(gref - G[j * PG + c]);
-          const bf16 hi = static_cast<bf16>(x);
-          xh[e] = hi;
-          xl[e] = static_cast<bf16>(x - static_cast<float>(hi));
+          for (int e = 0; e < 8; ++e) {
+            const int j = j8 + e;
+            const float x = (wide && j >= rw) ? 0.f : static_cast<float>(sk[j * PK + c]) * ex(gref - G[j * PG + c]);
+            const bf16 hi = static_cast<bf16>(x);
+            bh[s][e] = hi;
+            bl[s][e] = static_cast<bf16>(x - static_cast<float>(hi));
+          }
         }
-        st8(s_hi + cl * kPC + j8, xh);
-        st8(s_lo + cl * kPC + j8, xl);
       }
-    }
-    wave_sync();
-    {
       f32x4 xq = adq[part], xr = arow[part];  // one indexed move each way per part
-      mmaK<NR>(xq, s_f, kPC, s_hi, kPC, lane);
-      mmaK<NR>(xq, s_f, kPC, s_lo, kPC, lane);
-      mmaK<NR>(xr, s_e, kPC, s_hi, kPC, lane);
-      mmaK<NR>(xr, s_e, kPC, s_lo, kPC, lane);
+#pragma unroll
+      for (int s = 0; s < SR; ++s) xq = mfma(af[s], bh[s], xq);
+#pragma unroll
+      for (int s = 0; s < SR; ++s) xq = mfma(af[s], bl[s], xq);
+#pragma unroll
+      for (int s = 0; s < SR; ++s) xr = mfma(ae[s], bh[s], xr);
+#pragma unroll
+      for (int s = 0; s < SR; ++s) xr = mfma(ae[s], bl[s], xr);
       adq[part] = xq;
       arow[part] = xr;
     }
-    wave_sync();
-    {  // column role: operands q_i f_i, then k_i f_i, with f_i = exp(G_i - G_ew)
-      constexpr int NO = (NC / 8 + 3) / 4;  // octets per lane (some lanes have one less)
+    {  // column role: operands q_i f_i, then k_i f_i, with f_i = exp(G_i - G_ew), i >= rw
       const float gref = G[ew * PG + c];
       f32x4 xc = acol[part];
-      float f[NO][8];
+      float f[SC][8];
 #pragma unroll
-      for (int t = 0; t < NO; ++t) {
-        const int j8 = 8 * tg + 32 * t;
+      for (int s = 0; s < SC; ++s) {
+        const int j8 = 32 * s + q8;
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          f[t][e] = (j8 < NC && !(wide && j8 + e < 16)) ? ex(G[(rw + j8 + e) * PG + c] - gref) : 0.f;
+          f[s][e] = (j8 < NC && !(wide && j8 + e < 16)) ? ex(G[(rw + j8 + e) * PG + c] - gref) : 0.f;
       }
 #pragma unroll
       for (int pass = 0; pass < 2; ++pass) {
         const bf16* src = pass == 0 ? sq : sk;
+        bf16x8 bh[SC], bl[SC];
 #pragma unroll
-        for (int t = 0; t < NO; ++t) {
-          const int j8 = 8 * tg + 32 * t;
+        for (int s = 0; s < SC; ++s) {
+          const int j8 = 32 * s + q8;
+          bh[s] = bl[s] = bf16x8{};
           if (j8 < NC) {
-            bf16x8 xh, xl;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-              const float x = static_cast<float>(src[(rw + j8 + e) * PK + c]) * f[t][e];
+              const float x = static_cast<float>(src[(rw + j8 + e) * PK + c]) * f[s][e];
               const bf16 hi = static_cast<bf16>(x);
-              xh[e] = hi;
-              xl[e] = static_cast<bf16>(x - static_cast<float>(hi));
+              bh[s][e] = hi;
+              bl[s][e] = static_cast<bf16>(x - static_cast<float>(hi));
             }
-            st8(s_hi + cl * kPC + j8, xh);
-            st8(s_lo + cl * kPC + j8, xl);
           }
         }
-        wave_sync();
-        const bf16* xa = pass == 0 ? s_ft : s_et;
-        mmaK<NC>(xc, xa, kPC, s_hi, kPC, lane);
-        mmaK<NC>(xc, xa, kPC, s_lo, kPC, lane);
-        wave_sync();
+        const bf16x8* xa = pass == 0 ? aft : aet;
+#pragma unroll
+        for (int s = 0; s < SC; ++s) xc = mfma(xa[s], bh[s], xc);
+#pragma unroll
+        for (int s = 0; s < SC; ++s) xc = mfma(xa[s], bl[s], xc);
       }
       acol[part] = xc;
     }
@@ -1151,8 +1170,7 @@ struct LocalLds {
   static constexpr int ft = f + kC * kPC * 2;      // [64][kPC] F^T
   static constexpr int e = ft + kC * kPC * 2;      // [64][kPC] E
   static constexpr int et = e + kC * kPC * 2;      // [64][kPC] E^T
-  static constexpr int wop = et + kC * kPC * 2;    // [8][32][kPC] per wave: 16 channels hi, lo
-  static constexpr int end2 = wop + kLocalWaves * 32 * kPC * 2;
+  static constexpr int end2 = et + kC * kPC * 2;
   // phase 3
   static constexpr int dgs = ph;                   // [64][PG] fp32 dG
   static constexpr int dqs = dgs + kC * PG * 4;    // [64][PK] bf16 dq (per q/k head)
@@ -1439,12 +1457,11 @@ __global__ __launch_bounds__(64 * kLocalWaves) void local_kernel(BwdArgs a) {
   for (int c = c0 + lane; c < c0 + KT / 2; c += 64)
     wide_l |= !(fabsf(G[ew * PG + c] - G[rw * PG + c]) <= kSpanLim);
   const bool wide = wave_any(wide_l);
-  const int wslot = L::wop + w8 * 32 * kPC * 2;
   switch (w) {
-    case 0: rdp_products<KT, 0>(adq, arow, acol, lds, wslot, L::f, L::ft, L::e, L::et, G, sq, sk, ch, lane, wide); break;
-    case 1: rdp_products<KT, 1>(adq, arow, acol, lds, wslot, L::f, L::ft, L::e, L::et, G, sq, sk, ch, lane, wide); break;
-    case 2: rdp_products<KT, 2>(adq, arow, acol, lds, wslot, L::f, L::ft, L::e, L::et, G, sq, sk, ch, lane, wide); break;
-    default: rdp_products<KT, 3>(adq, arow, acol, lds, wslot, L::f, L::ft, L::e, L::et, G, sq, sk, ch, lane, wide); break;
+    case 0: rdp_products<KT, 0>(adq, arow, acol, lds, L::f, L::ft, L::e, L::et, G, sq, sk, ch, lane, wide); break;
+    case 1: rdp_products<KT, 1>(adq, arow, acol, lds, L::f, L::ft, L::e, L::et, G, sq, sk, ch, lane, wide); break;
+    case 2: rdp_products<KT, 2>(adq, arow, acol, lds, L::f, L::ft, L::e, L::et, G, sq, sk, ch, lane, wide); break;
+    default: rdp_products<KT, 3>(adq, arow, acol, lds, L::f, L::ft, L::e, L::et, G, sq, sk, ch, lane, wide); break;
   }
   // A wide block's terms with both tokens inside it, for the lane's outputs (token
   // t = rw + 4 lq + r, channel c0 + 16 cc + lr): F and E are zero outside their triangles, so
