@@ -280,6 +280,20 @@ __device__ __forceinline__ void mma_ra(f32x4& acc, const bf16x8* af, const bf16*
   }
 }
 
+// acc0 += A0 B and acc1 += A1 B for two A operands in registers (as mma_ra) and one B given
+// transposed in LDS, whose fragments are loaded once for both products.
+__device__ __forceinline__ void mma_ra2(f32x4& acc0, const bf16x8* a0, f32x4& acc1, const bf16x8* a1,
+                                        const bf16* bt, int ldb, int kk, int lane) {
+  const int r = lane & 15, q8 = (lane >> 4) * 8;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    if (32 * s >= kk) break;
+    const bf16x8 bv = 32 * s + q8 < kk ? ld8(bt + r * ldb + 32 * s + q8) : bf16x8{};
+    acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0[s], bv, acc0, 0, 0, 0);
+    acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1[s], bv, acc1, 0, 0, 0);
+  }
+}
+
 // acc += A B in fp32 (v_mfma_f32_16x16x4_f32); A and B row-major in LDS.
 __device__ __forceinline__ void mma16_nn(f32x4& acc, const float* a, int lda, const float* b,
                                          int ldb, int kk, int lane) {
@@ -1329,17 +1343,13 @@ __global__ __launch_bounds__(64 * kLocalWaves) void local_kernel(BwdArgs a) {
   for (int jj = 0; jj < 2; ++jj) {
     const int J = 2 * jj + ch;
     Dm[jj] = Fo[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (J <= w) {
-      mma_ra(Dm[jj], fut, s_u + 16 * J * PV, PV, V, lane);
-      mma_ra(Fo[jj], fdo, s_u + 16 * J * PV, PV, V, lane);
-    }
+    if (J <= w) mma_ra2(Dm[jj], fut, Fo[jj], fdo, s_u + 16 * J * PV, PV, V, lane);
   }
   f32x4 adq[NCH], arow[NCH], acol[NCH];
 #pragma unroll
   for (int cc = 0; cc < NCH; ++cc) {
     adq[cc] = arow[cc] = f32x4{0.f, 0.f, 0.f, 0.f};
-    mma_ra(adq[cc], fdo, s_hs + (c0 + 16 * cc) * PV, PV, V, lane);
-    mma_ra(arow[cc], fut, s_hs + (c0 + 16 * cc) * PV, PV, V, lane);
+    mma_ra2(adq[cc], fdo, arow[cc], fut, s_hs + (c0 + 16 * cc) * PV, PV, V, lane);
     const int c = c0 + 16 * cc + lr;
     const float er = ex(G[rw * PG + c]);
 #pragma unroll
