@@ -341,6 +341,30 @@ __device__ __forceinline__ void mmaKb(f32x4& acc, const bf16* a, int lda, const 
   }
 }
 
+// Row order of a tile held in MFMA accumulators so that two adjacent 16-row tiles, side by
+// side, are the B fragment of one 32-deep k step: accumulator row 32m + 16h + 4q + r holds
+// index 32m + 8q + 4h + r. A product whose output rows are in this order reads its A rows in
+// it (row perm32(16 I + lr) for tile I).
+__device__ __forceinline__ int perm32(int y) {
+  return (y & ~31) | ((y & 12) << 1) | ((y & 16) >> 2) | (y & 3);
+}
+// The B fragment (bf16) of k step s from accumulator tiles 2s (lo) and 2s + 1 (hi).
+__device__ __forceinline__ bf16x8 frag2(f32x4 lo, f32x4 hi) {
+  return bf16x8{static_cast<bf16>(lo[0]), static_cast<bf16>(lo[1]), static_cast<bf16>(lo[2]),
+                static_cast<bf16>(lo[3]), static_cast<bf16>(hi[0]), static_cast<bf16>(hi[1]),
+                static_cast<bf16>(hi[2]), static_cast<bf16>(hi[3])};
+}
+// mmaKb with this lane's A row given by a pointer (rows gathered in any order).
+template <int KK>
+__device__ __forceinline__ void mmaKr(f32x4& acc, const bf16* arow, const bf16x8* bf, int lane) {
+  const int q8 = (lane >> 4) * 8;
+#pragma unroll
+  for (int k0 = 0; k0 < KK; k0 += 32) {
+    const bf16x8 av = (k0 + 32 <= KK || q8 < KK - k0) ? ld8(arow + k0 + q8) : bf16x8{};
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bf[k0 / 32], acc, 0, 0, 0);
+  }
+}
+
 // ============================================================================ prep
 template <int KT>
 struct PrepLds {
@@ -663,11 +687,9 @@ struct SweepLds {
   static constexpr int rgam = aqt + kC * kPC * 2;       // [KT] fp32
   static constexpr int rbt = rgam + KT * 4;             // [64] fp32
   static constexpr int dot = rbt + kC * 4;              // [BV][kPC] dO^T
-  static constexpr int dst = dot + BV * kPC * 2;        // [BV][PK] dS^T
-  static constexpr int dut = dst + BV * PK * 2;         // [BV][kPC] dU^T
-  // (beta Ut)^T takes dO^T's bytes once dO's last product has read them, which keeps the two
-  // sweeps within one CU's LDS together (68,864 + 91,392 B at K = 128): they run side by side
-  static constexpr int rev_total = dut + BV * kPC * 2;
+  static constexpr int dst = dot + BV * kPC * 2;        // [BV][PK] dS^T (for the workspace store)
+  // the two sweeps fit in one CU's LDS together: they run side by side
+  static constexpr int rev_total = dst + BV * PK * 2;
   static_assert(fwd_total + rev_total <= 160 * 1024, "the two sweeps side by side on one CU");
 };
 
@@ -888,9 +910,7 @@ __global__ __launch_bounds__(64 * NW) void rev_sweep_kernel(BwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int lr = lane & 15, lq = lane >> 4;
   bf16* s_dst = reinterpret_cast<bf16*>(lds + L::dst) + 16 * w * PK;
-  bf16* s_dut = reinterpret_cast<bf16*>(lds + L::dut) + 16 * w * kPC;
   bf16* s_dow = s_dot + 16 * w * kPC;
-  bf16* s_but = s_dow;  // written after the last read of this wave's dO^T rows
 
   const int nvt = (a.V + BV - 1) / BV;
   int head, vt_idx;
@@ -902,12 +922,16 @@ __global__ __launch_bounds__(64 * NW) void rev_sweep_kernel(BwdArgs a) {
   const unsigned vrow = (unsigned)(a.HV * V);
   const SeqChunks sq_ = seq_chunks(a, b, hv);
 
+  // dS in accumulators, rows in perm32 order (row 16 ct + 4 lq + r holds channel
+  // perm32(16 ct + 4 lq + r)); so are dU's and beta Ut's token rows. Each product's result is
+  // then, two tiles side by side, the B fragment of the next one, and the chain
+  // dS -> dU -> Ut -> dS takes no LDS round trip.
   f32x4 D[NCT];
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int c = 16 * ct + 4 * lq + r;
+      const int c = perm32(16 * ct + 4 * lq + r);
       D[ct][r] = (a.dht && vok) ? a.dht[((size_t)head * KT + c) * V + vc] : 0.f;
     }
 
@@ -975,54 +999,60 @@ __global__ __launch_bounds__(64 * NW) void rev_sweep_kernel(BwdArgs a) {
   for (int n = NT - 1; n >= 0; --n) {
     __syncthreads();
     put();
-    // dS reaching the state that leaves this chunk, transposed into this wave's LDS rows
+    // dS reaching the state that leaves this chunk, transposed into this wave's LDS rows, for
+    // the workspace store at the end of the step (tile ct's 4 rows are 4 consecutive channels)
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) st4(s_dst + lr * PK + 16 * ct + 4 * lq, D[ct]);
+    for (int ct = 0; ct < NCT; ++ct) st4(s_dst + lr * PK + 32 * (ct >> 1) + 8 * lq + 4 * (ct & 1), D[ct]);
     if (n > 0) fetch(n - 1);
     __syncthreads();
-    // dU = scale Aq^T dO + Kc dS
     bf16x8 bdo[kC / 32], bds[KT / 32];
     load_b<kC>(bdo, s_dow, kPC, lane);
-    load_b<KT>(bds, s_dst, PK, lane);
+#pragma unroll
+    for (int s2 = 0; s2 < KT / 32; ++s2) bds[s2] = frag2(D[2 * s2], D[2 * s2 + 1]);
+    // dU = scale Aq^T dO + Kc dS (token rows in perm32 order)
+    f32x4 dU[4];
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
+      const int row = perm32(16 * I + lr);
       f32x4 p = f32x4{0.f, 0.f, 0.f, 0.f}, q = f32x4{0.f, 0.f, 0.f, 0.f};
-      mmaKb<kC>(p, s_aqt + 16 * I * kPC, kPC, bdo, lane);
-      mmaKb<KT>(q, s_kc + 16 * I * PK, PK, bds, lane);
-      st4(s_dut + lr * kPC + 16 * I + 4 * lq, a.scale * p + q);
+      mmaKr<kC>(p, s_aqt + row * kPC, bdo, lane);
+      mmaKr<KT>(q, s_kc + row * PK, bds, lane);
+      dU[I] = a.scale * p + q;
     }
-    // dS <- Gam_C dS + scale Qg^T dO (dO^T's last read; the LDS copy of dS stays for the store)
+    // dS <- Gam_C dS + scale Qg^T dO (dO^T's last read)
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
       f32x4 p = f32x4{0.f, 0.f, 0.f, 0.f};
-      mmaKb<kC>(p, s_qgt + 16 * ct * kPC, kPC, bdo, lane);
+      mmaKr<kC>(p, s_qgt + perm32(16 * ct + lr) * kPC, bdo, lane);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) D[ct][r] = D[ct][r] * s_gam[16 * ct + 4 * lq + r] + a.scale * p[r];
+      for (int r = 0; r < 4; ++r)
+        D[ct][r] = D[ct][r] * s_gam[perm32(16 * ct + 4 * lq + r)] + a.scale * p[r];
     }
     // Ut = T^T dU; beta Ut
     const size_t trow = (sq_.slot0 + n) * kC;
     bf16x8 bdu[kC / 32];
-    load_b<kC>(bdu, s_dut, kPC, lane);
+#pragma unroll
+    for (int s2 = 0; s2 < kC / 32; ++s2) bdu[s2] = frag2(dU[2 * s2], dU[2 * s2 + 1]);
+    f32x4 bu[4];
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
       f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
-      mmaKb<kC>(x, s_tt + 16 * I * kPC, kPC, bdu, lane);
-      f32x4 y;
+      mmaKr<kC>(x, s_tt + perm32(16 * I + lr) * kPC, bdu, lane);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int i = 16 * I + 4 * lq + r;
-        y[r] = s_bt[i] * x[r];
+        const int i = perm32(16 * I + 4 * lq + r);
+        bu[I][r] = s_bt[i] * x[r];
         if (vok) a.ut[(trow + i) * V + vc] = static_cast<bf16>(x[r]);
       }
-      st4(s_but + lr * kPC + 16 * I + 4 * lq, y);
     }
     // dS <- dS - Kg^T (beta Ut)
     bf16x8 bbu[kC / 32];
-    load_b<kC>(bbu, s_but, kPC, lane);
+#pragma unroll
+    for (int s2 = 0; s2 < kC / 32; ++s2) bbu[s2] = frag2(bu[2 * s2], bu[2 * s2 + 1]);
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
       f32x4 q = f32x4{0.f, 0.f, 0.f, 0.f};
-      mmaKb<kC>(q, s_kgt + 16 * ct * kPC, kPC, bbu, lane);
+      mmaKr<kC>(q, s_kgt + perm32(16 * ct + lr) * kPC, bbu, lane);
 #pragma unroll
       for (int r = 0; r < 4; ++r) D[ct][r] -= q[r];
     }
@@ -1034,7 +1064,8 @@ __global__ __launch_bounds__(64 * NW) void rev_sweep_kernel(BwdArgs a) {
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) a.dh0[((size_t)head * KT + 16 * ct + 4 * lq + r) * V + vc] = D[ct][r];
+      for (int r = 0; r < 4; ++r)
+        a.dh0[((size_t)head * KT + perm32(16 * ct + 4 * lq + r)) * V + vc] = D[ct][r];
 }
 
 // ==================================================================== local gradients
