@@ -674,10 +674,8 @@ struct SweepLds {
   static constexpr int gam = tm + kC * kPC * 2;         // [KT] fp32
   static constexpr int bt = gam + KT * 4;               // [64] fp32
   static constexpr int vt = bt + kC * 4;                // [64][PV] v tile
-  static constexpr int ht = vt + kC * PV * 2;           // [BV][PK] h^T
-  static constexpr int yt = ht + BV * PK * 2;           // [BV][kPC] (beta W0)^T
-  static constexpr int uu = yt + BV * kPC * 2;          // [BV][kPC] U^T
-  static constexpr int fwd_total = uu + BV * kPC * 2;
+  static constexpr int ht = vt + kC * PV * 2;           // [BV][PK] h^T (for the workspace store)
+  static constexpr int fwd_total = ht + BV * PK * 2;
   // reverse sweep
   static constexpr int kc = 0;                          // [64][PK]
   static constexpr int qgt = kc + kC * PK * 2;          // [KT][kPC]
@@ -761,8 +759,6 @@ __global__ __launch_bounds__(64 * NW) void fwd_sweep_kernel(BwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int lr = lane & 15, lq = lane >> 4;
   bf16* s_ht = reinterpret_cast<bf16*>(lds + L::ht) + 16 * w * PK;
-  bf16* s_yt = reinterpret_cast<bf16*>(lds + L::yt) + 16 * w * kPC;
-  bf16* s_uu = reinterpret_cast<bf16*>(lds + L::uu) + 16 * w * kPC;
 
   const int nvt = (a.V + BV - 1) / BV;
   int head, vt_idx;
@@ -774,12 +770,16 @@ __global__ __launch_bounds__(64 * NW) void fwd_sweep_kernel(BwdArgs a) {
   const unsigned vrow = (unsigned)(a.HV * V);
   const SeqChunks sq_ = seq_chunks(a, b, hv);
 
+  // h in accumulators, rows in perm32 order (row 16 ct + 4 lq + r holds channel
+  // perm32(16 ct + 4 lq + r)); so are X's, Y's and U's token rows. Each product's result is
+  // then, two tiles side by side, the B fragment of the next one, and the chain
+  // h -> X -> Y -> U -> h takes no LDS round trip.
   f32x4 S[NCT];
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int c = 16 * ct + 4 * lq + r;
+      const int c = perm32(16 * ct + 4 * lq + r);
       S[ct][r] = (a.s0 && vok) ? a.s0[((size_t)head * KT + c) * V + vc] : 0.f;
     }
 
@@ -838,53 +838,59 @@ __global__ __launch_bounds__(64 * NW) void fwd_sweep_kernel(BwdArgs a) {
   for (int n = 0; n < NT; ++n) {
     __syncthreads();
     put();
-    // h of this chunk, transposed into this wave's LDS rows
+    // h of this chunk, transposed into this wave's LDS rows, for the workspace store at the end
+    // of the step (tile ct's 4 rows are 4 consecutive channels)
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) st4(s_ht + lr * PK + 16 * ct + 4 * lq, S[ct]);
+    for (int ct = 0; ct < NCT; ++ct) st4(s_ht + lr * PK + 32 * (ct >> 1) + 8 * lq + 4 * (ct & 1), S[ct]);
     if (n + 1 < NT) fetch(n + 1);
     __syncthreads();
     // X = Kg h, W0 = V - X, Y = beta W0
     const size_t trow = (sq_.slot0 + n) * kC;
-    // W0 and U rows of this chunk: buffer stores, never behind a branch (columns >= V dropped)
+    // W0 and U rows of this chunk: buffer stores, never behind a branch (columns >= V dropped);
+    // the lane's token rows perm32(16 I + 4 lq + r) = 32 (I >> 1) + 4 (I & 1) + r + 8 lq
     const auto rw0 = rsrc(a.w0 + trow * V, (unsigned)kC * V * 2);
     const auto ru = rsrc(a.u + trow * V, (unsigned)kC * V * 2);
-    const unsigned lane_off = vok ? (unsigned)(4 * lq * V + vc) * 2 : 0x80000000u;
+    const unsigned lane_off = vok ? (unsigned)(8 * lq * V + vc) * 2 : 0x80000000u;
     bf16x8 bh[KT / 32];
-    load_b<KT>(bh, s_ht, PK, lane);
+#pragma unroll
+    for (int s2 = 0; s2 < KT / 32; ++s2) bh[s2] = frag2(S[2 * s2], S[2 * s2 + 1]);
+    f32x4 yv[4];
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
       f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
-      mmaKb<KT>(x, s_kg + 16 * I * PK, PK, bh, lane);
-      f32x4 w0, y;
+      mmaKr<KT>(x, s_kg + perm32(16 * I + lr) * PK, bh, lane);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int i = 16 * I + 4 * lq + r;
-        w0[r] = static_cast<float>(s_vt[i * PV + 16 * w + lr]) - x[r];
-        y[r] = s_bt[i] * w0[r];
-        bstore1(static_cast<bf16>(w0[r]), rw0, lane_off + (unsigned)((16 * I + r) * V) * 2);
+        const int i = perm32(16 * I + 4 * lq + r), ir = 32 * (I >> 1) + 4 * (I & 1) + r;
+        const float w0 = static_cast<float>(s_vt[i * PV + 16 * w + lr]) - x[r];
+        yv[I][r] = s_bt[i] * w0;
+        bstore1(static_cast<bf16>(w0), rw0, lane_off + (unsigned)(ir * V) * 2);
       }
-      st4(s_yt + lr * kPC + 16 * I + 4 * lq, y);
     }
     // U = T Y
     bf16x8 by[kC / 32];
-    load_b<kC>(by, s_yt, kPC, lane);
+#pragma unroll
+    for (int s2 = 0; s2 < kC / 32; ++s2) by[s2] = frag2(yv[2 * s2], yv[2 * s2 + 1]);
+    f32x4 uv[4];
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
-      f32x4 uv = f32x4{0.f, 0.f, 0.f, 0.f};
-      mmaKb<kC>(uv, s_tm + 16 * I * kPC, kPC, by, lane);
+      uv[I] = f32x4{0.f, 0.f, 0.f, 0.f};
+      mmaKr<kC>(uv[I], s_tm + perm32(16 * I + lr) * kPC, by, lane);
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        bstore1(static_cast<bf16>(uv[r]), ru, lane_off + (unsigned)((16 * I + r) * V) * 2);
-      st4(s_uu + lr * kPC + 16 * I + 4 * lq, uv);
+      for (int r = 0; r < 4; ++r) {
+        const int ir = 32 * (I >> 1) + 4 * (I & 1) + r;
+        bstore1(static_cast<bf16>(uv[I][r]), ru, lane_off + (unsigned)(ir * V) * 2);
+      }
     }
     // h <- Gam_C h + Kc^T U
     bf16x8 bu[kC / 32];
-    load_b<kC>(bu, s_uu, kPC, lane);
+#pragma unroll
+    for (int s2 = 0; s2 < kC / 32; ++s2) bu[s2] = frag2(uv[2 * s2], uv[2 * s2 + 1]);
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) S[ct][r] *= s_gam[16 * ct + 4 * lq + r];
-      mmaKb<kC>(S[ct], s_kct + 16 * ct * kPC, kPC, bu, lane);
+      for (int r = 0; r < 4; ++r) S[ct][r] *= s_gam[perm32(16 * ct + 4 * lq + r)];
+      mmaKr<kC>(S[ct], s_kct + perm32(16 * ct + lr) * kPC, bu, lane);
     }
     // h of this chunk to the workspace (its LDS copy is intact until the next chunk)
     store_state_tile<KT, true>(a.h + (sq_.slot0 + n) * KT * V, V, vt_idx * BV + 16 * w, s_ht, PK, lane);
