@@ -703,37 +703,23 @@ __device__ __forceinline__ void sweep_tile(int nvt, int nh, int& head, int& vt_i
 }
 
 // this wave's 16 columns of a K x 16 state, held transposed in LDS (st[v][c], pitch pk),
-// to dst[c][v] (row pitch V) with 16-byte stores; columns past V are dropped
-// BRANCH_FREE: buffer stores with the column check in the offset, never behind a branch. In
-// the forward sweep that lets the loop wait only for its own loads (the compiler cannot count
-// stores behind branches across the loop, and vmcnt counts them in order with the loads):
-// 448 -> 357-363 us at B4 T8192 H16. The reverse sweep measured slower with it (568 -> 600+ us)
-// and keeps the branch.
-template <int KT, bool BRANCH_FREE>
+// to dst[c][v] (row pitch V) with 16-byte buffer stores; columns past V are dropped by the
+// offset, never behind a branch. That lets the loop wait only for its own loads (the compiler
+// cannot count stores behind branches across the loop, and vmcnt counts them in order with the
+// loads): the forward sweep went from 448 to 357-363 us at B4 T8192 H16, and the reverse
+// sweep, once its Ut rows were buffer stores too, took 90 us off the backward's call.
+template <int KT>
 __device__ __forceinline__ void store_state_tile(bf16* dst, int V, int vcol0, const bf16* st, int pk,
                                                  int lane) {
-  if constexpr (BRANCH_FREE) {
-    const auto r = rsrc(dst, (unsigned)KT * V * 2);
+  const auto r = rsrc(dst, (unsigned)KT * V * 2);
 #pragma unroll
-    for (int e = 0; e < KT * 2 / 64; ++e) {
-      const int u = lane + 64 * e, c = u >> 1, h8 = 8 * (u & 1);
-      bf16x8 x;
+  for (int e = 0; e < KT * 2 / 64; ++e) {
+    const int u = lane + 64 * e, c = u >> 1, h8 = 8 * (u & 1);
+    bf16x8 x;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) x[j] = st[(h8 + j) * pk + c];
-      const unsigned off = vcol0 + h8 < V ? (unsigned)(c * V + vcol0 + h8) * 2 : 0x80000000u;
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), r, off, 0, 0);
-    }
-  } else {
-#pragma unroll
-    for (int e = 0; e < KT * 2 / 64; ++e) {
-      const int u = lane + 64 * e, c = u >> 1, h8 = 8 * (u & 1);
-      if (vcol0 + h8 < V) {
-        bf16x8 x;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) x[j] = st[(h8 + j) * pk + c];
-        st8(dst + (size_t)c * V + vcol0 + h8, x);
-      }
-    }
+    for (int j = 0; j < 8; ++j) x[j] = st[(h8 + j) * pk + c];
+    const unsigned off = vcol0 + h8 < V ? (unsigned)(c * V + vcol0 + h8) * 2 : 0x80000000u;
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), r, off, 0, 0);
   }
 }
 
@@ -893,7 +879,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_sweep_kernel(BwdArgs a) {
       mmaKr<kC>(S[ct], s_kct + perm32(16 * ct + lr) * kPC, bu, lane);
     }
     // h of this chunk to the workspace (its LDS copy is intact until the next chunk)
-    store_state_tile<KT, true>(a.h + (sq_.slot0 + n) * KT * V, V, vt_idx * BV + 16 * w, s_ht, PK, lane);
+    store_state_tile<KT>(a.h + (sq_.slot0 + n) * KT * V, V, vt_idx * BV + 16 * w, s_ht, PK, lane);
   }
 }
 
@@ -1036,6 +1022,8 @@ __global__ __launch_bounds__(64 * NW) void rev_sweep_kernel(BwdArgs a) {
     }
     // Ut = T^T dU; beta Ut
     const size_t trow = (sq_.slot0 + n) * kC;
+    const auto rut = rsrc(a.ut + trow * V, (unsigned)kC * V * 2);
+    const unsigned lane_off = vok ? (unsigned)(8 * lq * V + vc) * 2 : 0x80000000u;
     bf16x8 bdu[kC / 32];
 #pragma unroll
     for (int s2 = 0; s2 < kC / 32; ++s2) bdu[s2] = frag2(dU[2 * s2], dU[2 * s2 + 1]);
@@ -1046,9 +1034,9 @@ __global__ __launch_bounds__(64 * NW) void rev_sweep_kernel(BwdArgs a) {
       mmaKr<kC>(x, s_tt + perm32(16 * I + lr) * kPC, bdu, lane);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int i = perm32(16 * I + 4 * lq + r);
+        const int i = perm32(16 * I + 4 * lq + r), ir = 32 * (I >> 1) + 4 * (I & 1) + r;
         bu[I][r] = s_bt[i] * x[r];
-        if (vok) a.ut[(trow + i) * V + vc] = static_cast<bf16>(x[r]);
+        bstore1(static_cast<bf16>(x[r]), rut, lane_off + (unsigned)(ir * V) * 2);
       }
     }
     // dS <- dS - Kg^T (beta Ut)
@@ -1063,7 +1051,7 @@ __global__ __launch_bounds__(64 * NW) void rev_sweep_kernel(BwdArgs a) {
       for (int r = 0; r < 4; ++r) D[ct][r] -= q[r];
     }
     // dS of this chunk to the workspace (its LDS copy is intact until the next chunk)
-    store_state_tile<KT, false>(a.dsn + (sq_.slot0 + n) * KT * V, V, vt_idx * BV + 16 * w, s_dst, PK,
+    store_state_tile<KT>(a.dsn + (sq_.slot0 + n) * KT * V, V, vt_idx * BV + 16 * w, s_dst, PK,
                          lane);
   }
   if (a.dh0 && vok)
