@@ -341,6 +341,28 @@ __device__ __forceinline__ void mmaKb(f32x4& acc, const bf16* a, int lda, const 
   }
 }
 
+// Cross-lane sums within a row of 16 lanes in VALU (DPP) instead of LDS-routed shuffles; they
+// add in the order of the xor butterfly they replace, so the sums are the same bits.
+template <int CTRL>
+__device__ __forceinline__ float dppf(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+// sum over aligned groups of n lanes (n = 1, 2, 4, 8 or 16, uniform), in every lane of the group:
+// xor 1 and xor 2 by quad permutes, then the half-row and row mirrors, which pair the same
+// group sums as xor 4 and xor 8 once each quad (half row) holds one value
+__device__ __forceinline__ float group_sum(float v, int n) {
+  if (n > 1) v += dppf<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+  if (n > 2) v += dppf<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+  if (n > 4) v += dppf<0x141>(v);  // row_half_mirror
+  if (n > 8) v += dppf<0x140>(v);  // row_mirror
+  return v;
+}
+// sum over lanes l, l ^ 16, l ^ 32 and l ^ 48, in every lane
+__device__ __forceinline__ float rows_sum(float v) {
+  v += __shfl_xor(v, 16);
+  return v + __shfl_xor(v, 32);
+}
+
 // Row order of a tile held in MFMA accumulators so that two adjacent 16-row tiles, side by
 // side, are the B fragment of one 32-deep k step: accumulator row 32m + 16h + 4q + r holds
 // index 32m + 8q + 4h + r. A product whose output rows are in this order reads its A rows in
@@ -1358,8 +1380,7 @@ __global__ __launch_bounds__(64 * kLocalWaves) void local_kernel(BwdArgs a) {
     for (int x = 0; x < 4; ++x)
 #pragma unroll
       for (int e = 0; e < 8; ++e) s += static_cast<float>(fut[x][e]) * static_cast<float>(fw0[x][e]);
-    s += __shfl_xor(s, 16);
-    s += __shfl_xor(s, 32);
+    s = rows_sum(s);
     if (lq == 0) db1[rw + lr] = s;
   }
   // D = Ut U^T and Fo = dO U^T, tiles J <= w with J = ch mod 2
@@ -1399,7 +1420,7 @@ __global__ __launch_bounds__(64 * kLocalWaves) void local_kernel(BwdArgs a) {
         for (int x = 0; x < 8; ++x) sdot += static_cast<float>(hv8[x]) * static_cast<float>(xds[e][x]);
       }
       if (pow2) {
-        for (int o = 1; o < per; o <<= 1) sdot += __shfl_xor(sdot, o);
+        sdot = group_sum(sdot, per);
         if (in && c8 == 0) lx2[r] = sdot;
       } else if (in) {
         lxp[r * 16 + c8 / 8] = sdot;
@@ -1439,8 +1460,7 @@ __global__ __launch_bounds__(64 * kLocalWaves) void local_kernel(BwdArgs a) {
       const int j = rw + 4 * lq + r;
       part += static_cast<float>(sk[j * PK + c]) * ex(gl - G[j * PG + c]) * x[r];  // last-token term
     }
-    part += __shfl_xor(part, 16);
-    part += __shfl_xor(part, 32);
+    part = rows_sum(part);
     if (lq == 0) lx[w * KT + c] = part;
     acol[cc] = x * ex(gl - G[ew * PG + c]);  // U dS^T exp(G_C - G_ew); exp(G_ew - G_j) follows
   }
@@ -1454,11 +1474,7 @@ __global__ __launch_bounds__(64 * kLocalWaves) void local_kernel(BwdArgs a) {
         s[r] -= Dm[jj][r] * mrv[jj][r];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      float x = s[r];
-      x += __shfl_xor(x, 1);
-      x += __shfl_xor(x, 2);
-      x += __shfl_xor(x, 4);
-      x += __shfl_xor(x, 8);
+      const float x = group_sum(s[r], 16);
       if (lr == 0) atomicAdd(db2 + rw + 4 * lq + r, x);
     }
   }
