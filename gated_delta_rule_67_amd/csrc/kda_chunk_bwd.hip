@@ -1084,8 +1084,8 @@ __global__ __launch_bounds__(64 * NW) void rev_sweep_kernel(BwdArgs a) {
 }
 
 // ==================================================================== local gradients
-// The relative-decay products of one wave's 16-token block W (rows rw .. rw + 15) over its
-// half of the key channels (ch), 16 channels (one output tile) at a time:
+// The relative-decay products of one wave's 16-token block W (rows rw .. rw + 15) over the
+// workgroup's NP x 16 key channels, 16 channels (one output tile) at a time:
 //   row role against reference rw over tokens 0 .. rw + 15 with operand k_j exp(G_rw - G_j),
 //     into dq (with F) and the + part of dk (with E);
 //   column role against reference ew = rw + 15 over tokens rw .. 63 with operands
@@ -1099,15 +1099,14 @@ __global__ __launch_bounds__(64 * NW) void rev_sweep_kernel(BwdArgs a) {
 // and E^T) are the same for every channel part and are loaded once.
 // wide: block W's span exceeds kSpanLim; its own tokens' operand rows are left out (zero) and
 // their terms are added one by one (diag_terms).
-template <int KT, int W>
+template <int NP, int PG, int PK, int W>
 __device__ __forceinline__ void rdp_products(f32x4* adq, f32x4* arow, f32x4* acol, const unsigned char* lds,
                                              int of, int oft, int oe, int oet,
                                              const float* G, const bf16* sq, const bf16* sk,
-                                             int ch, int lane, bool wide) {
-  constexpr int PG = KT + 4, PK = KT + 8, rw = 16 * W, ew = rw + 15;
+                                             int lane, bool wide) {
+  constexpr int rw = 16 * W, ew = rw + 15;
   constexpr int NR = 16 * (W + 1), NC = kC - rw;  // tokens of the row / column role
   constexpr int SR = (NR + 31) / 32, SC = (NC + 31) / 32;  // their k steps of 32 tokens
-  constexpr int NP = KT / 32;                     // 16-channel parts per half
   const int cl = lane & 15, tg = lane >> 4, q8 = 8 * tg;  // channel in the part, token octet
   bf16x8 af[SR], ae[SR], aft[SC], aet[SC];  // zeros past the role's tokens
   {
@@ -1133,7 +1132,7 @@ __device__ __forceinline__ void rdp_products(f32x4* adq, f32x4* arow, f32x4* aco
   };
 #pragma unroll
   for (int part = 0; part < NP; ++part) {
-    const int c = ch * (KT / 2) + 16 * part + cl;
+    const int c = 16 * part + cl;  // channel in the workgroup's LDS rows
     {  // row role: operand k_j exp(G_rw - G_j) over tokens 0 .. rw + 15
       const float gref = G[rw * PG + c];
       bf16x8 bh[SR], bl[SR];
@@ -1204,27 +1203,30 @@ __device__ __forceinline__ void rdp_products(f32x4* adq, f32x4* arow, f32x4* aco
   }
 }
 
-constexpr int kLocalWaves = 8;
+constexpr int kLocalWaves = 4;
 
+// One workgroup holds one half of the key channels of a chunk (KH = KT / 2): 78 KB at K = 128,
+// so two workgroups share a CU and one's memory waits and barriers overlap the other's work.
 template <int KT>
 struct LocalLds {
-  static constexpr int PK = KT + 8, PG = KT + 4, PV = 128 + 8;
+  static constexpr int KH = KT / 2;                // key channels of the workgroup
+  static constexpr int PK = KH + 8, PG = KH + 4, PV = 128 + 8;
   static constexpr int g = 0;                      // [64][PG] fp32 G (all phases)
   static constexpr int sq = g + kC * PG * 4;       // [64][PK] bf16 q
   static constexpr int sk = sq + kC * PK * 2;      // [64][PK] bf16 k
   static constexpr int bt = sk + kC * PK * 2;      // [64] fp32 beta
   static constexpr int db1 = bt + kC * 4;          // [64] fp32 Ut . W0
   static constexpr int db2 = db1 + kC * 4;         // [64] fp32 sum_j -D Mr
-  static constexpr int lx = db2 + kC * 4;          // [4][KT] fp32 last-token terms per block
-  static constexpr int lx2 = lx + 4 * KT * 4;      // [KT] fp32 rowsum(dS h)
-  static constexpr int tot = lx2 + KT * 4;         // [4][KT] fp32 cumsum scratch
-  static constexpr int fdg = tot + 4 * KT * 4;     // [64] fp32 F_tt (as F is stored, bf16)
+  static constexpr int lx = db2 + kC * 4;          // [4][KH] fp32 last-token terms per block
+  static constexpr int lx2 = lx + 4 * KH * 4;      // [KH] fp32 rowsum(dS h)
+  static constexpr int tot = lx2 + KH * 4;         // [4][KH] fp32 cumsum scratch
+  static constexpr int fdg = tot + 4 * KH * 4;     // [64] fp32 F_tt (as F is stored, bf16)
   static constexpr int ph = fdg + kC * 4;          // phase region
   // phase 1
   static constexpr int uu = ph;                    // [64][PV] U
-  static constexpr int hs = uu + kC * PV * 2;      // [KT][PV] h, then dS
-  static constexpr int lxp = hs + KT * PV * 2;     // [KT][16] fp32 rowsum(dS h) pieces
-  static constexpr int end1 = lxp + KT * 16 * 4;
+  static constexpr int hs = uu + kC * PV * 2;      // [KH][PV] h, then dS (the half's rows)
+  static constexpr int lxp = hs + KH * PV * 2;     // [KH][16] fp32 rowsum(dS h) pieces
+  static constexpr int end1 = lxp + KH * 16 * 4;
   // phase 2
   static constexpr int f = ph;                     // [64][kPC] F
   static constexpr int ft = f + kC * kPC * 2;      // [64][kPC] F^T
@@ -1237,17 +1239,58 @@ struct LocalLds {
   static constexpr int dks = dqs + kC * PK * 2;    // [64][PK] bf16 dk
   static constexpr int end3 = dks + kC * PK * 2;
   static constexpr int total = end1 > end2 ? (end1 > end3 ? end1 : end3) : (end2 > end3 ? end2 : end3);
-  static_assert(total <= 160 * 1024, "LDS");
+  static_assert(total <= 80 * 1024, "two workgroups per CU");
 };
 
-// One workgroup of 8 waves per (b, hv, chunk): two waves own each token block w and split its
-// key channels (ch = 0: the first half, 1: the second).
+// q and k rows in LDS (64 x KH bf16 each: this workgroup's channels c0 .. c0 + KH - 1) to unit L2
+// norm over all KT channels, as the forward's q/k transform: the squares of the other half
+// come from memory (qo, ko: that half's channel 0 of the chunk's first row; rows past nrow read
+// zeros). NTH / 64 threads per row, all in one wave.
+template <int KH, int NTH>
+__device__ __forceinline__ void l2norm_half(bf16* sq, bf16* sk, int pk, const bf16* qo, const bf16* ko,
+                                            unsigned qrow, int nrow, int tid) {
+  constexpr int TPR = NTH / kC, PER = KH / TPR;
+  static_assert(PER == 4 || PER % 8 == 0, "channels per thread");
+  const int r = tid / TPR, part = tid % TPR;
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    bf16* x = (m ? sk : sq) + r * pk + part * PER;
+    const auto ro = rsrc(m ? ko : qo, ((unsigned)(nrow - 1) * qrow + KH) * 2);
+    const unsigned off = (r * qrow + part * PER) * 2;
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const float v = static_cast<float>(x[e]);
+      ss += v * v;
+    }
+    if constexpr (PER == 4) {
+      const auto y = __builtin_bit_cast(bf16x4, __builtin_amdgcn_raw_buffer_load_b64(ro, off, 0, 0));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ss += static_cast<float>(y[e]) * static_cast<float>(y[e]);
+    } else {
+#pragma unroll
+      for (int p8 = 0; p8 < PER / 8; ++p8) {
+        const bf16x8 y = bload8(ro, off + 16 * p8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss += static_cast<float>(y[e]) * static_cast<float>(y[e]);
+      }
+    }
+    ss = group_sum(ss, TPR);
+    const float inv = rsqrtf(ss + kL2normEps);
+#pragma unroll
+    for (int e = 0; e < PER; ++e) x[e] = static_cast<bf16>(static_cast<float>(x[e]) * inv);
+  }
+}
+
+// Two workgroups of 4 waves per (b, hv, chunk): workgroup 2 n + ch takes item n's key channels
+// c0 = ch KH .. c0 + KH - 1, wave w its 16-token block. Both halves build F and E (products
+// contracting over V); the first half also computes dbeta and dv.
 template <int KT>
 __global__ __launch_bounds__(64 * kLocalWaves) void local_kernel(BwdArgs a) {
   using L = LocalLds<KT>;
   using P = PB<KT>;
-  constexpr int NTH = 64 * kLocalWaves;
-  constexpr int PK = L::PK, PG = L::PG, PV = L::PV, NCH = KT / 32;  // tiles per channel half
+  constexpr int NTH = 64 * kLocalWaves, KH = L::KH;
+  constexpr int PK = L::PK, PG = L::PG, PV = L::PV, NCH = KH / 16;  // 16-channel tiles
   __shared__ __attribute__((aligned(16))) unsigned char lds[L::total];
   float* G = reinterpret_cast<float*>(lds + L::g);
   bf16* sq = reinterpret_cast<bf16*>(lds + L::sq);
@@ -1259,26 +1302,27 @@ __global__ __launch_bounds__(64 * kLocalWaves) void local_kernel(BwdArgs a) {
   float* lx2 = reinterpret_cast<float*>(lds + L::lx2);
   float* fdg = reinterpret_cast<float*>(lds + L::fdg);
 
-  const int tid = threadIdx.x, lane = tid & 63, w8 = tid >> 6;
-  // waves w8 and w8 + 4 share a SIMD; the second takes block 3 - w8, so every SIMD holds one
-  // large and one small share of the relative-decay products
-  const int ch = w8 >> 2, w = ch == 0 ? w8 : 7 - w8;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int ch = blockIdx.x & 1;
+  // the second half's workgroups take the blocks in reverse order, so two workgroups on one
+  // CU tend to pair a large and a small share of the relative-decay products on each SIMD
+  const int w = ch == 0 ? wv : 3 - wv;
   const int lr = lane & 15, lq = lane >> 4;
-  const Chunk cr = item_chunk(a, blockIdx.x);
+  const Chunk cr = item_chunk(a, blockIdx.x >> 1);
   if (cr.rows == 0) return;  // past the packed list's last chunk
   const int hv = cr.hv, hh = hv / (a.HV / a.H), nrow = cr.rows;
   const int V = a.V;
   const size_t row0 = cr.row0;  // first token of the chunk, packed [B * T] order
+  const int c0 = ch * KH;       // first key channel of this workgroup
   const unsigned qrow = (unsigned)(a.H * KT), grow = (unsigned)(a.HV * KT);
   const bf16* qb = a.q + row0 * qrow + (size_t)hh * KT;
   const bf16* kb = a.k + row0 * qrow + (size_t)hh * KT;
   const bf16* gb = a.g + row0 * grow + (size_t)hv * KT;
   const unsigned char* blk = a.blocks + cr.slot * P::bytes;
   const size_t trow = cr.slot * kC;
-  const bf16* hsrc = a.h + cr.slot * KT * V;
-  const bf16* dsrc = a.dsn + cr.slot * KT * V;
+  const bf16* hsrc = a.h + cr.slot * KT * V + (size_t)c0 * V;
+  const bf16* dsrc = a.dsn + cr.slot * KT * V + (size_t)c0 * V;
   const int rw = 16 * w, ew = 16 * w + 15;  // first and last token of this wave's block
-  const int c0 = ch * (KT / 2);             // first channel of this wave's half
   const unsigned vrow = (unsigned)(a.HV * V);
 
   // this wave's rows of dO and Ut (and W0) as MFMA A operands, straight from memory. Every
@@ -1305,17 +1349,17 @@ __global__ __launch_bounds__(64 * kLocalWaves) void local_kernel(BwdArgs a) {
   const float bload = __builtin_bit_cast(
       float, __builtin_amdgcn_raw_buffer_load_b32(rsrc(blk + P::beta, kC * 4),
                                                   tid < kC ? (unsigned)tid * 4 : 0x80000000u, 0, 0));
-  QkgTile<KT, NTH> qkg;
-  qkg.load(qb, kb, gb, qrow, grow, nrow, tid);
-  constexpr int NU = (kC * 16 + NTH - 1) / NTH, NH = (KT * 16 + NTH - 1) / NTH;
+  QkgTile<KH, NTH> qkg;
+  qkg.load(qb + c0, kb + c0, gb + c0, qrow, grow, nrow, tid);
+  constexpr int NU = (kC * 16 + NTH - 1) / NTH, NH = (KH * 16 + NTH - 1) / NTH;
   const int per = V / 8;  // 16-byte pieces per row of U, h, dS (V <= 128: at most 16)
   const bool pow2 = (per & (per - 1)) == 0;
   float* lxp = reinterpret_cast<float*>(lds + L::lxp);
   bf16x8 xu[NU], xh[NH], xds[NH];
   {
     const auto ru = rsrc(a.u + trow * V, (unsigned)kC * V * 2);
-    const auto rh = rsrc(hsrc, (unsigned)KT * V * 2);
-    const auto rds = rsrc(dsrc, (unsigned)KT * V * 2);
+    const auto rh = rsrc(hsrc, (unsigned)KH * V * 2);
+    const auto rds = rsrc(dsrc, (unsigned)KH * V * 2);
 #pragma unroll
     for (int e = 0; e < NU; ++e) {
       const int u = tid + NTH * e, r = u / per, c8 = 8 * (u % per);
@@ -1324,33 +1368,30 @@ __global__ __launch_bounds__(64 * kLocalWaves) void local_kernel(BwdArgs a) {
 #pragma unroll
     for (int e = 0; e < NH; ++e) {
       const int u = tid + NTH * e, r = u / per, c8 = 8 * (u % per);
-      xh[e] = bload8(rh, u < KT * per ? (unsigned)(r * V + c8) * 2 : 0x80000000u);
+      xh[e] = bload8(rh, u < KH * per ? (unsigned)(r * V + c8) * 2 : 0x80000000u);
     }
 #pragma unroll
     for (int e = 0; e < NH; ++e) {
       const int u = tid + NTH * e, r = u / per, c8 = 8 * (u % per);
-      xds[e] = bload8(rds, u < KT * per ? (unsigned)(r * V + c8) * 2 : 0x80000000u);
+      xds[e] = bload8(rds, u < KH * per ? (unsigned)(r * V + c8) * 2 : 0x80000000u);
     }
   }
-  float mrv[2][4];  // Mr[rw + 4 lq + r][16 J + lr] for this wave's tiles J = 2 jj + ch <= w
+  float mrv[4][4];  // Mr[rw + 4 lq + r][16 J + lr] for tiles J <= w (first half only)
   {
     const auto rmr = rsrc(blk + P::mr, kC * kC * 4);
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj)
+    for (int J = 0; J < 4; ++J)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int i = rw + 4 * lq + r, j = 16 * (2 * jj + ch) + lr;
-        mrv[jj][r] = __builtin_bit_cast(
+        const int i = rw + 4 * lq + r, j = 16 * J + lr;
+        mrv[J][r] = __builtin_bit_cast(
             float, __builtin_amdgcn_raw_buffer_load_b32(
-                       rmr, 2 * jj + ch <= w ? (unsigned)(i * kC + j) * 4 : 0x80000000u, 0, 0));
+                       rmr, ch == 0 && J <= w ? (unsigned)(i * kC + j) * 4 : 0x80000000u, 0, 0));
       }
   }
   qkg.store(sq, sk, G, PK, PG, tid);
-  if (tid < kC) {
-    sb[tid] = bload;
-    db2[tid] = 0.f;
-  }
-  if (tid < KT) lx2[tid] = 0.f;
+  if (tid < kC) sb[tid] = bload;
+  if (tid < KH) lx2[tid] = 0.f;
   // ---------------- phase 1: products contracting over V
   bf16* s_u = reinterpret_cast<bf16*>(lds + L::uu);
   bf16* s_hs = reinterpret_cast<bf16*>(lds + L::hs);
@@ -1363,16 +1404,16 @@ __global__ __launch_bounds__(64 * kLocalWaves) void local_kernel(BwdArgs a) {
 #pragma unroll
     for (int e = 0; e < NH; ++e) {
       const int u = tid + NTH * e, r = u / per, c8 = 8 * (u % per);
-      if (u < KT * per) st8(s_hs + r * PV + c8, xh[e]);
+      if (u < KH * per) st8(s_hs + r * PV + c8, xh[e]);
     }
   }
-  cumsum_rows<KT, NTH>(G, PG, reinterpret_cast<float*>(lds + L::tot), tid);  // includes barriers
+  cumsum_rows<KH, NTH>(G, PG, reinterpret_cast<float*>(lds + L::tot), tid);  // includes barriers
   if (a.flags & kFlagQkL2norm) {
-    l2norm_rows<KT, NTH>(sq, sk, PK, tid);
+    l2norm_half<KH, NTH>(sq, sk, PK, qb + (KH - c0), kb + (KH - c0), qrow, nrow, tid);
     __syncthreads();
   }
 
-  // dbeta, first term: Ut_i . W0_i for this block's rows (one wave of the pair)
+  // dbeta, first term: Ut_i . W0_i for this block's rows (first half)
   if (ch == 0) {
     float s = 0.f;
 #pragma unroll
@@ -1382,20 +1423,19 @@ __global__ __launch_bounds__(64 * kLocalWaves) void local_kernel(BwdArgs a) {
     s = rows_sum(s);
     if (lq == 0) db1[rw + lr] = s;
   }
-  // D = Ut U^T and Fo = dO U^T, tiles J <= w with J = ch mod 2
-  f32x4 Dm[2], Fo[2];
+  // D = Ut U^T and Fo = dO U^T, tiles J <= w
+  f32x4 Dm[4], Fo[4];
 #pragma unroll
-  for (int jj = 0; jj < 2; ++jj) {
-    const int J = 2 * jj + ch;
-    Dm[jj] = Fo[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (J <= w) mma_ra2(Dm[jj], fut, Fo[jj], fdo, s_u + 16 * J * PV, PV, V, lane);
+  for (int J = 0; J < 4; ++J) {
+    Dm[J] = Fo[J] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (J <= w) mma_ra2(Dm[J], fut, Fo[J], fdo, s_u + 16 * J * PV, PV, V, lane);
   }
   f32x4 adq[NCH], arow[NCH], acol[NCH];
 #pragma unroll
   for (int cc = 0; cc < NCH; ++cc) {
     adq[cc] = arow[cc] = f32x4{0.f, 0.f, 0.f, 0.f};
-    mma_ra2(adq[cc], fdo, arow[cc], fut, s_hs + (c0 + 16 * cc) * PV, PV, V, lane);
-    const int c = c0 + 16 * cc + lr;
+    mma_ra2(adq[cc], fdo, arow[cc], fut, s_hs + 16 * cc * PV, PV, V, lane);
+    const int c = 16 * cc + lr;
     const float er = ex(G[rw * PG + c]);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -1405,13 +1445,13 @@ __global__ __launch_bounds__(64 * kLocalWaves) void local_kernel(BwdArgs a) {
   }
   {
     // rowsum(dS * h): the per pieces of a row sit on per consecutive lanes; when per is a
-    // power of two they are summed by shuffles and stored once, else each piece is kept in
+    // power of two they are summed across lanes and stored once, else each piece is kept in
     // LDS and the row is summed below in a fixed order
     __syncthreads();  // every wave is done with h
 #pragma unroll
     for (int e = 0; e < NH; ++e) {
       const int u = tid + NTH * e, r = u / per, c8 = 8 * (u % per);
-      const bool in = u < KT * per;
+      const bool in = u < KH * per;
       float sdot = 0.f;
       if (in) {
         const bf16x8 hv8 = ld8(s_hs + r * PV + c8);
@@ -1428,7 +1468,7 @@ __global__ __launch_bounds__(64 * kLocalWaves) void local_kernel(BwdArgs a) {
     }
   }
   __syncthreads();
-  if (!pow2 && tid < KT) {
+  if (!pow2 && tid < KH) {
     float sum = 0.f;
     for (int p = 0; p < per; ++p) sum += lxp[tid * 16 + p];
     lx2[tid] = sum;
@@ -1447,8 +1487,8 @@ __global__ __launch_bounds__(64 * kLocalWaves) void local_kernel(BwdArgs a) {
 #pragma unroll
   for (int cc = 0; cc < NCH; ++cc) {
     f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
-    mma_ra(x, fuu, s_hs + (c0 + 16 * cc) * PV, PV, V, lane);  // U dS^T
-    const int c = c0 + 16 * cc + lr;
+    mma_ra(x, fuu, s_hs + 16 * cc * PV, PV, V, lane);  // U dS^T
+    const int c = 16 * cc + lr;
     const float gl = G[(kC - 1) * PG + c];
     const bool lastrow = w == 3 && lq == 3;  // row r = 3 of this lane is token 63
     xlast[cc] = lastrow ? x[3] : 0.f;
@@ -1460,21 +1500,21 @@ __global__ __launch_bounds__(64 * kLocalWaves) void local_kernel(BwdArgs a) {
       part += static_cast<float>(sk[j * PK + c]) * ex(gl - G[j * PG + c]) * x[r];  // last-token term
     }
     part = rows_sum(part);
-    if (lq == 0) lx[w * KT + c] = part;
+    if (lq == 0) lx[w * KH + c] = part;
     acol[cc] = x * ex(gl - G[ew * PG + c]);  // U dS^T exp(G_C - G_ew); exp(G_ew - G_j) follows
   }
-  // dbeta, second term: sum_j (-Ut U^T)_ij Mr_ij over this wave's tiles J
-  {
+  // dbeta, second term: sum_j (-Ut U^T)_ij Mr_ij over the tiles J <= w (first half)
+  if (ch == 0) {
     float s[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj)
+    for (int J = 0; J < 4; ++J)
 #pragma unroll
       for (int r = 0; r < 4; ++r)  // Mr is zero on and above the diagonal; Dm, mrv 0 for J > w
-        s[r] -= Dm[jj][r] * mrv[jj][r];
+        s[r] -= Dm[J][r] * mrv[J][r];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float x = group_sum(s[r], 16);
-      if (lr == 0) atomicAdd(db2 + rw + 4 * lq + r, x);
+      if (lr == 0) db2[rw + 4 * lq + r] = x;
     }
   }
   __syncthreads();  // phase 1 operands are dead
@@ -1485,15 +1525,14 @@ __global__ __launch_bounds__(64 * kLocalWaves) void local_kernel(BwdArgs a) {
   bf16* s_e = reinterpret_cast<bf16*>(lds + L::e);
   bf16* s_et = reinterpret_cast<bf16*>(lds + L::et);
 #pragma unroll
-  for (int jj = 0; jj < 2; ++jj) {  // this wave's tiles J (zeros where J > w)
-    const int J = 2 * jj + ch;
+  for (int J = 0; J < 4; ++J) {  // this block's tiles J (zeros where J > w)
     const int j = 16 * J + lr;
     f32x4 fv, evv;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int i = rw + 4 * lq + r;
-      fv[r] = j <= i ? a.scale * Fo[jj][r] : 0.f;
-      evv[r] = j < i ? -sb[i] * Dm[jj][r] : 0.f;
+      fv[r] = j <= i ? a.scale * Fo[J][r] : 0.f;
+      evv[r] = j < i ? -sb[i] * Dm[J][r] : 0.f;
       s_f[i * kPC + j] = static_cast<bf16>(fv[r]);
       if (j == i) fdg[i] = static_cast<float>(static_cast<bf16>(fv[r]));
       s_e[i * kPC + j] = static_cast<bf16>(evv[r]);
@@ -1504,14 +1543,13 @@ __global__ __launch_bounds__(64 * kLocalWaves) void local_kernel(BwdArgs a) {
   __syncthreads();
   // this wave's channels of block w: span within kSpanLim, or its diagonal terms one by one
   bool wide_l = false;
-  for (int c = c0 + lane; c < c0 + KT / 2; c += 64)
-    wide_l |= !(fabsf(G[ew * PG + c] - G[rw * PG + c]) <= kSpanLim);
+  for (int c = lane; c < KH; c += 64) wide_l |= !(fabsf(G[ew * PG + c] - G[rw * PG + c]) <= kSpanLim);
   const bool wide = wave_any(wide_l);
   switch (w) {
-    case 0: rdp_products<KT, 0>(adq, arow, acol, lds, L::f, L::ft, L::e, L::et, G, sq, sk, ch, lane, wide); break;
-    case 1: rdp_products<KT, 1>(adq, arow, acol, lds, L::f, L::ft, L::e, L::et, G, sq, sk, ch, lane, wide); break;
-    case 2: rdp_products<KT, 2>(adq, arow, acol, lds, L::f, L::ft, L::e, L::et, G, sq, sk, ch, lane, wide); break;
-    default: rdp_products<KT, 3>(adq, arow, acol, lds, L::f, L::ft, L::e, L::et, G, sq, sk, ch, lane, wide); break;
+    case 0: rdp_products<NCH, PG, PK, 0>(adq, arow, acol, lds, L::f, L::ft, L::e, L::et, G, sq, sk, lane, wide); break;
+    case 1: rdp_products<NCH, PG, PK, 1>(adq, arow, acol, lds, L::f, L::ft, L::e, L::et, G, sq, sk, lane, wide); break;
+    case 2: rdp_products<NCH, PG, PK, 2>(adq, arow, acol, lds, L::f, L::ft, L::e, L::et, G, sq, sk, lane, wide); break;
+    default: rdp_products<NCH, PG, PK, 3>(adq, arow, acol, lds, L::f, L::ft, L::e, L::et, G, sq, sk, lane, wide); break;
   }
   // A wide block's terms with both tokens inside it, for the lane's outputs (token
   // t = rw + 4 lq + r, channel c0 + 16 cc + lr): F and E are zero outside their triangles, so
@@ -1528,7 +1566,7 @@ __global__ __launch_bounds__(64 * kLocalWaves) void local_kernel(BwdArgs a) {
   if (wide) {
 #pragma unroll
     for (int cc = 0; cc < NCH; ++cc) {
-      const int c = c0 + 16 * cc + lr;
+      const int c = 16 * cc + lr;
       for (int jj = 0; jj < 16; ++jj) {
         const int j = rw + jj;
         const float gj = G[j * PG + c];
@@ -1554,7 +1592,7 @@ __global__ __launch_bounds__(64 * kLocalWaves) void local_kernel(BwdArgs a) {
   bf16* sdk = reinterpret_cast<bf16*>(lds + L::dks);
 #pragma unroll
   for (int cc = 0; cc < NCH; ++cc) {
-    const int c = c0 + 16 * cc + lr;
+    const int c = 16 * cc + lr;
     const float gr = G[rw * PG + c], ge = G[ew * PG + c];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -1575,17 +1613,17 @@ __global__ __launch_bounds__(64 * kLocalWaves) void local_kernel(BwdArgs a) {
         sdk[i * PK + c] = static_cast<bf16>(dk);
       } else if (i < nrow) {
         const size_t t = row0 + i;
-        a.dq32[(t * a.HV + hv) * KT + c] = dq;
-        a.dk32[(t * a.HV + hv) * KT + c] = dk;
+        a.dq32[(t * a.HV + hv) * KT + c0 + c] = dq;
+        a.dk32[(t * a.HV + hv) * KT + c0 + c] = dk;
       }
     }
   }
   __syncthreads();
   if (!a.dq32) {
-    for (int u = tid; u < kC * (KT / 8); u += NTH) {
-      const int i = u / (KT / 8), c8 = 8 * (u % (KT / 8));
+    for (int u = tid; u < kC * (KH / 8); u += NTH) {
+      const int i = u / (KH / 8), c8 = 8 * (u % (KH / 8));
       if (i < nrow) {
-        const size_t o = ((row0 + i) * a.H + hh) * KT + c8;
+        const size_t o = ((row0 + i) * a.H + hh) * KT + c0 + c8;
         st8(a.dq + o, ld8(sdq + i * PK + c8));
         st8(a.dk + o, ld8(sdk + i * PK + c8));
       }
@@ -1593,20 +1631,20 @@ __global__ __launch_bounds__(64 * kLocalWaves) void local_kernel(BwdArgs a) {
   }
   // dg = reverse cumsum of dG over the chunk, in four 16-row segments: segment sums first,
   // then each segment's scan starts from the sums of the segments after it
-  static_assert(4 * KT <= NTH, "one thread per segment and channel");
-  float* segs = reinterpret_cast<float*>(lds + L::tot);  // [4][KT]
+  static_assert(4 * KH <= NTH, "one thread per segment and channel");
+  float* segs = reinterpret_cast<float*>(lds + L::tot);  // [4][KH]
   bf16* sdg = sdq;  // dg in bf16; the dq rows were written out before the barrier below
-  const int sc = tid % KT, sp = tid / KT;
-  if (tid < 4 * KT) {
+  const int sc = tid % KH, sp = tid / KH;
+  if (tid < 4 * KH) {
     float bsum = 0.f;
 #pragma unroll
     for (int i = 15; i >= 0; --i) bsum += dgs[(16 * sp + i) * PG + sc];
-    segs[sp * KT + sc] = bsum;
+    segs[sp * KH + sc] = bsum;
   }
   __syncthreads();
-  if (tid < 4 * KT) {
-    float run = lx[sc] + lx[KT + sc] + lx[2 * KT + sc] + lx[3 * KT + sc] + ex(G[(kC - 1) * PG + sc]) * lx2[sc];
-    for (int p = 3; p > sp; --p) run += segs[p * KT + sc];
+  if (tid < 4 * KH) {
+    float run = lx[sc] + lx[KH + sc] + lx[2 * KH + sc] + lx[3 * KH + sc] + ex(G[(kC - 1) * PG + sc]) * lx2[sc];
+    for (int p = 3; p > sp; --p) run += segs[p * KH + sc];
 #pragma unroll
     for (int i = 15; i >= 0; --i) {
       const int row = 16 * sp + i;
@@ -1615,9 +1653,9 @@ __global__ __launch_bounds__(64 * kLocalWaves) void local_kernel(BwdArgs a) {
     }
   }
   __syncthreads();
-  for (int u = tid; u < kC * (KT / 8); u += NTH) {  // dg rows as 16-byte pieces
-    const int i = u / (KT / 8), c8 = 8 * (u % (KT / 8));
-    if (i < nrow) st8(a.dg + ((row0 + i) * a.HV + hv) * KT + c8, ld8(sdg + i * PK + c8));
+  for (int u = tid; u < kC * (KH / 8); u += NTH) {  // dg rows as 16-byte pieces
+    const int i = u / (KH / 8), c8 = 8 * (u % (KH / 8));
+    if (i < nrow) st8(a.dg + ((row0 + i) * a.HV + hv) * KT + c0 + c8, ld8(sdg + i * PK + c8));
   }
   if (ch == 0) {  // dv = beta Ut, this block's rows from the A fragments the wave holds
     const int i = rw + lr;
@@ -1633,11 +1671,11 @@ __global__ __launch_bounds__(64 * kLocalWaves) void local_kernel(BwdArgs a) {
         }
       }
     }
-  }
-  if (tid < nrow) {
-    const float bt = sb[tid];  // beta as the recurrence used it
-    const float chain = (a.flags & kFlagBetaSigmoid) ? bt * (1.f - bt) : 1.f;
-    a.dbeta[(row0 + tid) * a.HV + hv] = static_cast<bf16>((db1[tid] + db2[tid]) * chain);
+    if (tid < nrow) {
+      const float bt = sb[tid];  // beta as the recurrence used it
+      const float chain = (a.flags & kFlagBetaSigmoid) ? bt * (1.f - bt) : 1.f;
+      a.dbeta[(row0 + tid) * a.HV + hv] = static_cast<bf16>((db1[tid] + db2[tid]) * chain);
+    }
   }
 }
 
@@ -1804,7 +1842,7 @@ hipError_t launch_cfg(BwdArgs a, hipStream_t stream) {
   if (forked) (void)hipEventDestroy(forked);
   if (joined) (void)hipEventDestroy(joined);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((local_kernel<KT>), dim3(items), dim3(64 * kLocalWaves), 0, stream, a);
+  hipLaunchKernelGGL((local_kernel<KT>), dim3(2 * items), dim3(64 * kLocalWaves), 0, stream, a);
   const size_t rows = a.ctab ? (size_t)a.T : (size_t)a.B * a.T;  // packed: one row of T tokens
   if (a.flags & kFlagQkL2norm) {
     const unsigned grid = (unsigned)((rows * a.H + 3) / 4);
