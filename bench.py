@@ -395,7 +395,7 @@ def main():
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-gate", action="store_true")
     ap.add_argument("--no-segmented", action="store_true")
-    ap.add_argument("--backward-steps", type=int, default=5)
+    ap.add_argument("--backward-steps", type=int, default=20)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -651,7 +651,7 @@ def main():
             h: [grads[i][h[0], :, h[1]].cpu() for i in range(5)] + [grads[5][h[0], h[1]].cpu()]
             for h in samples["backward"]}
         del grads
-        b_avg, b_med, b_min = time_launches(backward, args.backward_steps, 1, torch)
+        b_avg, b_med, b_min = time_launches(backward, args.backward_steps, 10, torch)
         bbytes = backward_algorithmic(c["B"], c["T"], c["H"], c["HV"], c["K"], c["V"], 2)
         bgbs = bbytes / (b_avg * 1e-3) / 1e9
         result["backward"] = {
