@@ -85,13 +85,18 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(
     gna = -expf(gate.A_log[hv]);
   }
 
-  // Then the whole slab: it is the critical resource.
+  // Then the whole slab: it is the critical resource. Loads and stores of the state are
+  // streaming (non-temporal): in a model each layer's cache is stepped once per token, with
+  // the other layers' caches in between, so nothing of it is left in cache for the next step
+  // and caching it only evicts other data. Over 4 caches stepped in turn (1.07 GB): 94.9 us per
+  // step against 101.5 with cached loads; on one cache stepped back to back, where cached loads
+  // re-read part of the previous step from the last-level cache, 93.5 against 79.
   f32x4 s[kDecodeMaxRows];
 #pragma unroll
   for (int i = 0; i < kDecodeMaxRows; ++i) {
     const int r = rg + i * rgc;
     if (active && r < K)
-      s[i] = *reinterpret_cast<const f32x4*>(S + (size_t)r * V);
+      s[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(S + (size_t)r * V));
     else
       s[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
