@@ -79,11 +79,15 @@ struct BwdArgs {
   const int2* ctab;
   int NC;
   unsigned flags;  // kFlag* input transforms the forward applied (gradients go through them)
+  // Fixed-length sequences only: the window of chunks c_lo .. c_lo + c_n - 1 of every
+  // sequence that a reverse-sweep or local launch covers (c_n = 0: all NT chunks).
+  int c_lo, c_n;
 };
 
 // The chunk a prep / local item stands for: its value head, its first token in the packed
 // [B * T] token order, its rows (0: no chunk, the item does nothing), and its slot (the index
-// of its prep block and of its saved per-chunk tensors, which is the item itself).
+// of its prep block and of its saved per-chunk tensors: the item itself, except in a local
+// launch over a window of chunks).
 struct Chunk {
   int hv, rows;
   size_t row0, slot;
@@ -95,13 +99,15 @@ __device__ __forceinline__ Chunk item_chunk(const BwdArgs& a, int item) {
     const int2 e = a.ctab[item - ch.hv * a.NC];
     ch.row0 = (size_t)e.x;
     ch.rows = e.y;
+    ch.slot = (size_t)item;
   } else {
-    const int n = item % a.NT, head = item / a.NT, b = head / a.HV;
+    const int w = a.c_n > 0 ? a.c_n : a.NT;  // the launch's window of chunks per sequence
+    const int n = a.c_lo + item % w, head = item / w, b = head / a.HV;
     ch.hv = head - b * a.HV;
     ch.row0 = (size_t)b * a.T + n * kC;
     ch.rows = min(kC, a.T - n * kC);
+    ch.slot = (size_t)head * a.NT + n;
   }
-  ch.slot = (size_t)item;
   return ch;
 }
 
@@ -1007,16 +1013,18 @@ __global__ __launch_bounds__(64 * NW) void rev_sweep_kernel(BwdArgs a) {
     }
   };
 
-  const int NT = sq_.nch;
-  if (NT > 0) fetch(NT - 1);
-  for (int n = NT - 1; n >= 0; --n) {
+  // chunks lo .. hi - 1 of the sequence, last first (a window when the call is split)
+  const int lo = (a.c_n > 0 && !a.ctab) ? a.c_lo : 0;
+  const int hi = (a.c_n > 0 && !a.ctab) ? a.c_lo + a.c_n : sq_.nch;
+  if (hi > lo) fetch(hi - 1);
+  for (int n = hi - 1; n >= lo; --n) {
     __syncthreads();
     put();
     // dS reaching the state that leaves this chunk, transposed into this wave's LDS rows, for
     // the workspace store at the end of the step (tile ct's 4 rows are 4 consecutive channels)
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) st4(s_dst + lr * PK + 32 * (ct >> 1) + 8 * lq + 4 * (ct & 1), D[ct]);
-    if (n > 0) fetch(n - 1);
+    if (n > lo) fetch(n - 1);
     __syncthreads();
     bf16x8 bdo[kC / 32], bds[KT / 32];
     load_b<kC>(bdo, s_dow, kPC, lane);
@@ -1741,12 +1749,13 @@ __global__ __launch_bounds__(256) void qk_norm_bwd_kernel(const bf16* __restrict
 }
 
 struct Layout {
-  size_t blocks, h, dsn, u, w0, ut, dq32, dk32, cu, coff, ctab, total;
+  size_t blocks, h, dsn, u, w0, ut, dq32, dk32, cu, coff, ctab, bnd, total;
 };
 
 // slots: chunk slots (B * HV * NT, or HV * NC when packed); rows: tokens (B * T); nseq: packed
 // sequences (0: fixed length).
-Layout layout(size_t slots, size_t rows, bool need32, int K, int V, int HV, int nseq, int NC) {
+Layout layout(size_t slots, size_t rows, bool need32, int K, int V, int HV, int nseq, int NC,
+              size_t bnd_states) {
   auto al = [](size_t x) { return (x + 255) / 256 * 256; };
   Layout l{};
   size_t off = 0;
@@ -1764,6 +1773,8 @@ Layout layout(size_t slots, size_t rows, bool need32, int K, int V, int HV, int 
     l.cu = off;   off += al((size_t)(nseq + 1) * 4);
     l.coff = off; off += al((size_t)(nseq + 1) * 4);
     l.ctab = off; off += al((size_t)NC * 8);
+  } else {        // fp32 gradient of the state between the two reverse-sweep launches
+    l.bnd = off;  off += al(bnd_states * (size_t)K * V * 4);
   }
   l.total = off;
   return l;
@@ -1774,12 +1785,13 @@ bool needs_fp32_dqk(int H, int HV, unsigned flags) { return HV != H || (flags & 
 
 Layout fixed_layout(int B, int T, int H, int HV, int K, int V, unsigned flags) {
   const size_t NT = (T + kC - 1) / kC;
-  return layout((size_t)B * HV * NT, (size_t)B * T, needs_fp32_dqk(H, HV, flags), K, V, HV, 0, 0);
+  return layout((size_t)B * HV * NT, (size_t)B * T, needs_fp32_dqk(H, HV, flags), K, V, HV, 0, 0,
+                (size_t)B * HV);
 }
 
 Layout varlen_layout(int nseq, int T, int H, int HV, int K, int V, unsigned flags) {
   const int NC = varlen_chunk_bound(nseq, T);
-  return layout((size_t)HV * NC, (size_t)T, needs_fp32_dqk(H, HV, flags), K, V, HV, nseq, NC);
+  return layout((size_t)HV * NC, (size_t)T, needs_fp32_dqk(H, HV, flags), K, V, HV, nseq, NC, 0);
 }
 
 // The stream the forward sweep runs on, beside the reverse sweep on the caller's stream: the
@@ -1812,7 +1824,7 @@ hipError_t side_stream(hipStream_t* out) {
 }
 
 template <int KT>
-hipError_t launch_cfg(BwdArgs a, hipStream_t stream) {
+hipError_t launch_cfg(BwdArgs a, float* bnd, hipStream_t stream) {
   const int items = a.ctab ? a.HV * a.NC : a.B * a.HV * a.NT;
   const int cus = device_cu_count();  // K = 128: persistent, one workgroup per CU (its LDS)
   const int pgrid = (KT == 128 && items > cus) ? cus : items;
@@ -1822,27 +1834,61 @@ hipError_t launch_cfg(BwdArgs a, hipStream_t stream) {
   // workgroups per CU, one of each sweep: 1.99 -> 1.91 ms per call)
   constexpr int NW = 4;
   const int sweeps = a.B * a.HV * ((a.V + 16 * NW - 1) / (16 * NW));
-  // fork: the forward sweep on the side stream once prep is done; join before local
+  // The forward sweep runs on the side stream once prep is done. Fixed-length calls split the
+  // reverse sweep at chunk s: its first launch carries dS from the last chunk down to s and
+  // leaves the state's gradient there in `bnd`, the second goes on from it. The local kernel
+  // of chunks s .. NT - 1 needs only the forward sweep and the first launch, so it runs on the
+  // side stream while the second launch holds half the CUs; chunks 0 .. s - 1 follow on the
+  // caller's stream, which joins the side stream at the end.
+  const bool split = !a.ctab && a.NT >= 4 && bnd != nullptr;
+  const int s = a.NT / 2;
   hipStream_t side = nullptr;
-  hipEvent_t forked = nullptr, joined = nullptr;
+  hipEvent_t forked = nullptr, fwd_done = nullptr, rev_hi = nullptr, joined = nullptr;
   hipError_t e = side_stream(&side);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&forked, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&fwd_done, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&rev_hi, hipEventDisableTiming);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&joined, hipEventDisableTiming);
   if (e == hipSuccess) e = hipEventRecord(forked, stream);
   if (e == hipSuccess) e = hipStreamWaitEvent(side, forked, 0);
   if (e == hipSuccess) {
     hipLaunchKernelGGL((fwd_sweep_kernel<KT, NW>), dim3(sweeps), dim3(64 * NW), 0, side, a);
-    e = hipEventRecord(joined, side);
+    e = hipEventRecord(fwd_done, side);
   }
-  if (e == hipSuccess) {
+  if (e == hipSuccess && split) {
+    BwdArgs ra = a, rb = a, la = a, lb = a;
+    ra.c_lo = s, ra.c_n = a.NT - s, ra.dh0 = bnd;  // dht as given
+    rb.c_lo = 0, rb.c_n = s, rb.dht = bnd;         // dh0 as given
+    la.c_lo = s, la.c_n = a.NT - s;
+    lb.c_lo = 0, lb.c_n = s;
+    hipLaunchKernelGGL((rev_sweep_kernel<KT, NW>), dim3(sweeps), dim3(64 * NW), 0, stream, ra);
+    e = hipEventRecord(rev_hi, stream);
+    if (e == hipSuccess) {
+      hipLaunchKernelGGL((rev_sweep_kernel<KT, NW>), dim3(sweeps), dim3(64 * NW), 0, stream, rb);
+      e = hipStreamWaitEvent(side, rev_hi, 0);
+    }
+    if (e == hipSuccess) {
+      hipLaunchKernelGGL((local_kernel<KT>), dim3(2 * a.B * a.HV * (a.NT - s)), dim3(64 * kLocalWaves), 0,
+                         side, la);
+      e = hipEventRecord(joined, side);
+    }
+    if (e == hipSuccess) e = hipStreamWaitEvent(stream, fwd_done, 0);
+    if (e == hipSuccess) {
+      hipLaunchKernelGGL((local_kernel<KT>), dim3(2 * a.B * a.HV * s), dim3(64 * kLocalWaves), 0, stream, lb);
+      e = hipStreamWaitEvent(stream, joined, 0);
+    }
+  } else if (e == hipSuccess) {
     hipLaunchKernelGGL((rev_sweep_kernel<KT, NW>), dim3(sweeps), dim3(64 * NW), 0, stream, a);
-    e = hipStreamWaitEvent(stream, joined, 0);
+    e = hipStreamWaitEvent(stream, fwd_done, 0);
+    if (e == hipSuccess)
+      hipLaunchKernelGGL((local_kernel<KT>), dim3(2 * items), dim3(64 * kLocalWaves), 0, stream, a);
   }
   // released once their work is done
   if (forked) (void)hipEventDestroy(forked);
+  if (fwd_done) (void)hipEventDestroy(fwd_done);
+  if (rev_hi) (void)hipEventDestroy(rev_hi);
   if (joined) (void)hipEventDestroy(joined);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((local_kernel<KT>), dim3(2 * items), dim3(64 * kLocalWaves), 0, stream, a);
   const size_t rows = a.ctab ? (size_t)a.T : (size_t)a.B * a.T;  // packed: one row of T tokens
   if (a.flags & kFlagQkL2norm) {
     const unsigned grid = (unsigned)((rows * a.H + 3) / 4);
@@ -1921,9 +1967,10 @@ hipError_t launch_chunk_bwd(const void* q, const void* k, const void* v, const v
     a.coff = coff;
     a.ctab = ctab;
   }
-  if (K == 32) return launch_cfg<32>(a, stream);
-  if (K == 64) return launch_cfg<64>(a, stream);
-  if (K == 128) return launch_cfg<128>(a, stream);
+  float* bnd = cu_seqlens ? nullptr : reinterpret_cast<float*>(ws + l.bnd);
+  if (K == 32) return launch_cfg<32>(a, bnd, stream);
+  if (K == 64) return launch_cfg<64>(a, bnd, stream);
+  if (K == 128) return launch_cfg<128>(a, bnd, stream);
   return hipErrorInvalidValue;
 }
 
