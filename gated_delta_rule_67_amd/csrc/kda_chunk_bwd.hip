@@ -327,24 +327,13 @@ __device__ __forceinline__ void mmaK(f32x4& acc, const bf16* a, int lda, const b
 }
 
 // The B fragments of one 16-column operand (contraction index contiguous, rows of pitch
-// ldb), loaded once for all the products of a step that share them; and the product that
-// takes them from registers (A fragments from LDS as in mmaK).
+// ldb), loaded once for all the products of a step that share them.
 template <int KK>
 __device__ __forceinline__ void load_b(bf16x8* bf, const bf16* bt, int ldb, int lane) {
   const int r = lane & 15, q8 = (lane >> 4) * 8;
 #pragma unroll
   for (int k0 = 0; k0 < KK; k0 += 32)
     bf[k0 / 32] = (k0 + 32 <= KK || q8 < KK - k0) ? ld8(bt + r * ldb + k0 + q8) : bf16x8{};
-}
-
-template <int KK>
-__device__ __forceinline__ void mmaKb(f32x4& acc, const bf16* a, int lda, const bf16x8* bf, int lane) {
-  const int r = lane & 15, q8 = (lane >> 4) * 8;
-#pragma unroll
-  for (int k0 = 0; k0 < KK; k0 += 32) {
-    const bf16x8 av = (k0 + 32 <= KK || q8 < KK - k0) ? ld8(a + r * lda + k0 + q8) : bf16x8{};
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bf[k0 / 32], acc, 0, 0, 0);
-  }
 }
 
 // Cross-lane sums within a row of 16 lanes in VALU (DPP) instead of LDS-routed shuffles; they
@@ -382,7 +371,8 @@ __device__ __forceinline__ bf16x8 frag2(f32x4 lo, f32x4 hi) {
                 static_cast<bf16>(lo[3]), static_cast<bf16>(hi[0]), static_cast<bf16>(hi[1]),
                 static_cast<bf16>(hi[2]), static_cast<bf16>(hi[3])};
 }
-// mmaKb with this lane's A row given by a pointer (rows gathered in any order).
+// acc += A B with B fragments in registers (as load_b gives them) and this lane's A row given
+// by a pointer (rows gathered in any order).
 template <int KK>
 __device__ __forceinline__ void mmaKr(f32x4& acc, const bf16* arow, const bf16x8* bf, int lane) {
   const int q8 = (lane >> 4) * 8;
