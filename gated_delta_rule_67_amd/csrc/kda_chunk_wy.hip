@@ -720,6 +720,20 @@ __device__ __forceinline__ void dma_block(unsigned char* dst, const unsigned cha
   }
 }
 
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+
+// Four bf16 by the LDS transpose load (ds_read_b64_tr_b16): in each 16-lane group, lane l
+// receives element l % 4 of the 8-byte pieces addressed by lanes 4e + l / 4, e = 0 .. 3.
+__device__ __forceinline__ bf16x4 load_tr4(lds_u8* p) {
+#if __HIP_DEVICE_COMPILE__
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p));
+#else
+  (void)p;
+  return bf16x4{};
+#endif
+}
+
 // s_waitcnt vmcnt(N) (expcnt and lgkmcnt left unconstrained)
 template <int N>
 __device__ __forceinline__ void wait_vmem() {
@@ -742,9 +756,10 @@ void state_kernel(WyArgs a) {
   constexpr int BV = 16 * NW;
   const PrefillArgs& p = a.p;
 
-  // per buffer: the chunk's factors, then v^T of the V tile ([BV][64 + 8] bf16)
-  constexpr int PV = kC + 8;
-  constexpr int VT = W::bytes, BUF = W::bytes + BV * PV * 2;
+  // per buffer: the chunk's factors, then the v tile in token order ([64][BV + 8] bf16), which
+  // the compute waves read four tokens of a column at a time with the LDS transpose load
+  constexpr int PVN = BV + 8;
+  constexpr int VT = W::bytes, BUF = W::bytes + kC * PVN * 2;
   __shared__ __attribute__((aligned(1024))) unsigned char buf0[BUF];
   __shared__ __attribute__((aligned(1024))) unsigned char buf1[BUF];
 
@@ -786,7 +801,7 @@ void state_kernel(WyArgs a) {
   const unsigned rowb = (unsigned)(p.HV * V * 2);  // bytes between consecutive tokens of v / o
   if (wv >= NW) {
     // DMA waves: the factors by LDS DMA; the v tile by range-checked loads (zeros past T
-    // or V), written transposed so a compute lane reads 4 consecutive tokens at once.
+    // or V), stored as loaded (16 bytes: 8 columns of a token).
     // v tile: 64 rows x BV/8 pieces of 8 columns; lane pl takes pieces pl + 64 kDmaWaves e
     // (V % 8 == 0, so a piece is wholly inside or outside the row)
     const int pw = wv - NW, pl = 64 * pw + lane;
@@ -814,9 +829,7 @@ void state_kernel(WyArgs a) {
 #pragma unroll
       for (int e = 0; e < NPL; ++e) {
         const int pc = pl + 64 * kDmaWaves * e, row = pc / PPR, c8 = pc % PPR;
-        if (row < kC)
-#pragma unroll
-          for (int x = 0; x < 8; ++x) vt[(8 * c8 + x) * PV + row] = rvv[e][x];
+        if (row < kC) *reinterpret_cast<bf16x8*>(vt + row * PVN + 8 * c8) = rvv[e];
       }
     };
     // L2 warm-up one chunk further ahead: the sibling workgroups of a head (V tiles) split
@@ -880,7 +893,7 @@ void state_kernel(WyArgs a) {
       }
   }
 
-  auto step = [&](const unsigned char* bk, int n) {
+  auto step = [&](const unsigned char* bk, lds_u8* bkl, int n) {
     const int t0 = n * kC, nrow = min(kC, len - t0);
     auto frag_q = [&](int tile, int J, int m) {  // rows of Q*Gam / K*Gam
       const int row = 16 * J + lr;
@@ -937,7 +950,9 @@ void state_kernel(WyArgs a) {
       for (int h2 = 0; h2 < 2; ++h2) {
         const int J = 2 * m + h2;
         const f32x4 bt = load4f(bk + W::beta + (16 * J + 4 * lq) * 4);
-        const bf16x4 vv = load4(bk + VT + ((16 * wv + lr) * PV + 16 * J + 4 * lq) * 2);
+        // tokens 16J + 4lq .. + 3 of column 16 wv + lr: in each 16-lane group, lane lr gives
+        // the address of token 16J + 4lq + lr / 4, columns 16 wv + 4 (lr % 4) .. + 3
+        const bf16x4 vv = load_tr4(bkl + VT + ((16 * J + 4 * lq + (lr >> 2)) * PVN + 16 * wv + 4 * (lr & 3)) * 2);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const float yv = bt[r] * (to_f32(vv[r]) - X[J][r]);
@@ -1011,12 +1026,19 @@ void state_kernel(WyArgs a) {
               mfma32(fk[ct][0], ul[0], mfma32(fk[ct][0], ub[0], S[ct] * gm[ct]))));
   };
 
+#if __HIP_DEVICE_COMPILE__
+  lds_u8* const lb0 = (lds_u8*)buf0;
+  lds_u8* const lb1 = (lds_u8*)buf1;
+#else
+  lds_u8* const lb0 = nullptr;
+  lds_u8* const lb1 = nullptr;
+#endif
   for (int n = 0; n < NT; n += 2) {
     lds_barrier();
-    step(buf0, n);
+    step(buf0, lb0, n);
     if (n + 1 >= NT) break;
     lds_barrier();
-    step(buf1, n + 1);
+    step(buf1, lb1, n + 1);
   }
 
   if (p.sT) {
