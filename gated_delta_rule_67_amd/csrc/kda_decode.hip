@@ -13,10 +13,8 @@
 //
 // The step is HBM-bound (~1 flop per state byte): one workgroup streams one
 // (b, hv[, V half]) state slab through registers exactly once, with 16-byte
-// coalesced accesses along V. State loads use the default cache policy and stores
-// are non-temporal: over consecutive steps on the same cache, the loads that hit the
-// 256 MB last-level cache are worth more than the stores there (measured: 87 us vs
-// 95 us per step with both non-temporal, for the 268 MB state of B=256, H=16, K=V=128).
+// coalesced accesses along V. State loads and stores are both streaming (non-temporal);
+// the reasons and measurements are at the loads below.
 #include "kda_device.h"
 
 namespace kda {
@@ -189,8 +187,11 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, const void
   const Tin* b_ = static_cast<const Tin*>(beta);
   Tin* o_ = static_cast<Tin*>(o);
   const int heads = B * HV;
-  // Split V in two when that keeps >= 4 workgroups per CU-slot worth of work.
-  const bool split = V % 8 == 0 && heads < 8192;
+  // Split V in two only for few heads (under 8 workgroups per CU on 256 CUs), where the extra
+  // workgroups shorten the step's latency. With many heads a workgroup per (b, hv) streams
+  // more bytes per wave: 92 us per step against 94.6 split, at B = 256, H = 16, K = V = 128
+  // over 4 caches in turn (128 threads per workgroup: 99 us).
+  const bool split = V % 8 == 0 && heads < 2048;
   const dim3 grid(split ? heads * 2 : heads), block(kDecodeThreads);
   const DecodeGate gate{A_log, dt_bias, gate_lb};
   auto go = [&](auto kernel) {
