@@ -37,6 +37,8 @@
 // unbounded values) computes its diagonal tiles pair by pair (direct_diag) and its column
 // factors as one exponential of a difference <= 0 each, so the factors are exact for any
 // g <= 0.
+#include <type_traits>
+
 #include "kda_device.h"
 #include "kda_varlen.h"
 
@@ -1108,19 +1110,22 @@ hipError_t launch_state(const WyArgs& a, hipStream_t stream) {
 // The scan below composes the maps in segment order: S_in[0] = S0, S_in[p+1] = A_p S_in[p] +
 // Bm_p; the last value is the sequence's final state.
 //
-// One workgroup of 4 waves per (b, hv, 16-column tile). The products run on fp32 MFMA
+// One workgroup of KT / 16 waves per (b, hv, 16-column tile). The products run on fp32 MFMA
 // (v_mfma_f32_16x16x4_f32) with the contraction index permuted so that lane group q = l / 16
 // covers k = NS q .. NS q + NS - 1 (NS = KT / 4): every wave keeps the whole K x 16 state tile
 // in registers as B operands (lane (q, j) holds column j's rows NS q ..), and a lane's A operands
-// are NS consecutive floats of one row of A_p, loaded as 16-byte pieces. Wave w computes the
-// row blocks w, w + 4, ...; the new rows meet in LDS once per step and come back as B operands.
+// are NS consecutive floats of one row of A_p, loaded as 16-byte pieces. Wave w computes row
+// block w; the new rows meet in LDS once per step and come back as B operands. A wave's rows of
+// A_(p+2) and Bm_(p+2) load during step p: they do not depend on the state, and two steps of
+// products hide their latency (with four waves of two row blocks each and the next block's
+// rows loaded one block ahead, a step took about 3.8 us at K = 128).
 template <int KT>
-__global__ __launch_bounds__(256) void segment_scan_kernel(const float* __restrict__ Am,
-                                                           const float* __restrict__ Bm,
-                                                           const float* s0, float* __restrict__ Sin,
-                                                           float* sT, int P, int HV, int K, int V) {
+__global__ __launch_bounds__(4 * KT) void segment_scan_kernel(const float* __restrict__ Am,
+                                                              const float* __restrict__ Bm,
+                                                              const float* s0, float* __restrict__ Sin,
+                                                              float* sT, int P, int HV, int K, int V) {
   constexpr int NS = KT / 4;    // k steps of one product (4 per MFMA, one per lane group)
-  constexpr int NRB = KT / 16;  // row blocks of the state tile
+  constexpr int NRB = KT / 16;  // row blocks of the state tile, one per wave
   __shared__ float sS[KT][17];
   const int ntile = (V + 15) / 16;
   const int tile = blockIdx.x % ntile, bh = blockIdx.x / ntile;
@@ -1146,27 +1151,24 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(const float* __restri
                                                   r0, lcol + (unsigned)(NS * q + st) * vrow, 0, 0))
                   : 0.f;
   }
-  // rows NS q .. of column col go out from the wave whose index is q (each row once)
+  // rows NS q .. of column col go out from wave q % NRB (each row once)
   auto store_rows = [&](float* dst, size_t m) {
     const auto rd = mat_kv(dst, m);
-    const unsigned base = w == q ? lcol : kOutOfRange;
+    const unsigned base = w == q % NRB ? lcol : kOutOfRange;
 #pragma unroll
     for (int st = 0; st < NS; ++st)
       __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, Sb[st]), rd,
                                             base + (unsigned)(NS * q + st) * vrow, 0, 0);
   };
-  // A and Bm of this wave's next (step, row block) item load while the current one multiplies:
-  // neither depends on the state.
-  const int nmine = w < NRB ? (NRB - 1 - w) / 4 + 1 : 0;  // row blocks w, w + 4, ...
-  auto load_item = [&](int pp, int rb, f32x4 (&a4)[NS / 4], f32x4& bm) {
+  const int row = 16 * w + j;  // this lane's row of A_p
+  auto load_step = [&](int pp, f32x4 (&a4)[NS / 4], f32x4& bm) {
     const size_t seg = (size_t)(b * P + pp) * HV + hv;
     const auto rb_ = mat_kv(Bm, seg);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       bm[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                            rb_, lcol + (unsigned)(16 * rb + 4 * q + i) * vrow, 0, 0));
+                                            rb_, lcol + (unsigned)(16 * w + 4 * q + i) * vrow, 0, 0));
     const auto ra = make_rsrc(Am + seg * K * K, kk);
-    const int row = 16 * rb + j;
 #pragma unroll
     for (int m = 0; m < NS / 4; ++m) {
       const int k = NS * q + 4 * m;  // K % 8 == 0: a piece is wholly inside or outside
@@ -1174,34 +1176,49 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(const float* __restri
       a4[m] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0));
     }
   };
-  f32x4 a_cur[NS / 4], a_nxt[NS / 4], bm_cur, bm_nxt;
-  if (nmine > 0) load_item(0, w, a_cur, bm_cur);
-  for (int p = 0; p < P; ++p) {
-    store_rows(Sin, (size_t)(b * P + p) * HV + hv);
-    for (int i = 0; i < nmine; ++i) {
-      const int rb = w + 4 * i;
-      const int np = i + 1 < nmine ? p : p + 1, ni = i + 1 < nmine ? i + 1 : 0;
-      if (np < P) load_item(np, w + 4 * ni, a_nxt, bm_nxt);
-      // four independent accumulator chains (k steps st = 4 m + e go to chain e)
-      f32x4 acc[4] = {bm_cur, f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f},
-                      f32x4{0.f, 0.f, 0.f, 0.f}};
+  // three register sets rotate: step p computes with set p % 3 while sets (p + 1) % 3 and
+  // (p + 2) % 3 are in flight
+  f32x4 a3[3][NS / 4], bm3[3];
+  // past the last segment the loads re-read it: every step issues the same memory operations
+  load_step(0, a3[0], bm3[0]);
+  load_step(min(1, P - 1), a3[1], bm3[1]);
+  // the entering state of segment 0; each later one (and the final state) goes out from the
+  // step that computes it, four rows per lane, so a step issues few memory operations and the
+  // loads of two steps ahead stay within the counter's reach
+  store_rows(Sin, (size_t)(b * P) * HV + hv);
+  auto step = [&](auto S_, int p) {
+    constexpr int c = decltype(S_)::value;
+    load_step(min(p + 2, P - 1), a3[(c + 2) % 3], bm3[(c + 2) % 3]);
+    // four independent accumulator chains (k steps st = 4 m + e go to chain e)
+    f32x4 acc[4] = {bm3[c], f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f},
+                    f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-      for (int st = 0; st < NS; ++st)
-        acc[st & 3] = __builtin_amdgcn_mfma_f32_16x16x4f32(a_cur[st >> 2][st & 3], Sb[st],
-                                                           acc[st & 3], 0, 0, 0);
+    for (int st = 0; st < NS; ++st)
+      acc[st & 3] = __builtin_amdgcn_mfma_f32_16x16x4f32(a3[c][st >> 2][st & 3], Sb[st],
+                                                         acc[st & 3], 0, 0, 0);
+    float* dst = p + 1 < P ? Sin : sT;
+    const size_t m = p + 1 < P ? (size_t)(b * P + p + 1) * HV + hv : (size_t)bh;
+    const auto rd = mat_kv(dst, m);
+    const unsigned base = dst ? lcol : kOutOfRange;  // no final state asked: stores dropped
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        sS[16 * rb + 4 * q + r][j] = (acc[0][r] + acc[1][r]) + (acc[2][r] + acc[3][r]);
-#pragma unroll
-      for (int m = 0; m < NS / 4; ++m) a_cur[m] = a_nxt[m];
-      bm_cur = bm_nxt;
+    for (int r = 0; r < 4; ++r) {
+      const float x = (acc[0][r] + acc[1][r]) + (acc[2][r] + acc[3][r]);
+      sS[16 * w + 4 * q + r][j] = x;
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, x), rd,
+                                            base + (unsigned)(16 * w + 4 * q + r) * vrow, 0, 0);
     }
     lds_barrier();
 #pragma unroll
     for (int st = 0; st < NS; ++st) Sb[st] = sS[NS * q + st][j];
     lds_barrier();
+  };
+  for (int p = 0; p < P; p += 3) {
+    step(std::integral_constant<int, 0>{}, p);
+    if (p + 1 >= P) break;
+    step(std::integral_constant<int, 1>{}, p + 1);
+    if (p + 2 >= P) break;
+    step(std::integral_constant<int, 2>{}, p + 2);
   }
-  if (sT) store_rows(sT, bh);
 }
 
 // n identity matrices of K x K (the state entering each segment when its map A is traced).
@@ -1346,13 +1363,13 @@ hipError_t launch_prefill_wy_segmented(const PrefillArgs& p, int P, void* worksp
   aa.p.o = nullptr;
   if ((e = launch_state_any(aa, cus, stream)) != hipSuccess) return e;
   const int ntile = (p.V + 15) / 16;
-  auto scan = [&](auto kernel) {
-    hipLaunchKernelGGL(kernel, dim3(p.B * p.HV * ntile), dim3(256), 0, stream, Am, Bm, p.s0, Sin,
+  auto scan = [&](auto kernel, int threads) {
+    hipLaunchKernelGGL(kernel, dim3(p.B * p.HV * ntile), dim3(threads), 0, stream, Am, Bm, p.s0, Sin,
                        p.sT, P, p.HV, p.K, p.V);
   };
-  if (p.K <= 32) scan(segment_scan_kernel<32>);
-  else if (p.K <= 64) scan(segment_scan_kernel<64>);
-  else scan(segment_scan_kernel<128>);
+  if (p.K <= 32) scan(segment_scan_kernel<32>, 4 * 32);
+  else if (p.K <= 64) scan(segment_scan_kernel<64>, 4 * 64);
+  else scan(segment_scan_kernel<128>, 4 * 128);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   WyArgs ao = a;  // the outputs from each segment's entering state
   ao.p.s0 = Sin;

@@ -91,10 +91,15 @@ __device__ __forceinline__ bool wave_any(bool v) { return __builtin_amdgcn_ballo
 
 // Workgroup barrier for LDS traffic only: waits for this wave's LDS operations, not for
 // its outstanding global loads or stores (a plain __syncthreads() also drains those, which
-// would expose every prefetch and every output store).
+// would expose every prefetch and every output store). The empty asm statements with a memory
+// clobber keep the compiler from moving any memory access across the barrier: the fences alone
+// order nothing for plain accesses, and LDS reads between two barriers were once sunk below the
+// second one, into the next loop iteration, where other waves had already rewritten the data.
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
