@@ -186,7 +186,9 @@ __device__ __forceinline__ bf16x8 bload8(__amdgpu_buffer_rsrc_t r, unsigned off)
 // orders this wave's LDS writes before its later reads (and reads before later writes)
 __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  asm volatile("" ::: "memory");  // no memory access crosses the barrier (see lds_barrier)
   __builtin_amdgcn_wave_barrier();
+  asm volatile("" ::: "memory");
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
