@@ -230,7 +230,7 @@ struct QkgTile {
 // In-place inclusive cumsum of G over the 64 rows (columns < KT); tot: [4][KT] scratch.
 template <int KT, int NTH>
 __device__ __forceinline__ void cumsum_rows(float* G, int pg, float* tot, int tid) {
-  __syncthreads();
+  block_barrier();
   for (int it = tid; it < 4 * KT; it += NTH) {
     const int wb = it / KT, c = it % KT;
     float acc = 0.f;
@@ -241,7 +241,7 @@ __device__ __forceinline__ void cumsum_rows(float* G, int pg, float* tot, int ti
     }
     tot[wb * KT + c] = acc;
   }
-  __syncthreads();
+  block_barrier();
   for (int it = tid; it < 4 * KT; it += NTH) {
     const int wb = it / KT, c = it % KT;
     float pre = 0.f;
@@ -249,7 +249,7 @@ __device__ __forceinline__ void cumsum_rows(float* G, int pg, float* tot, int ti
 #pragma unroll
     for (int i = 0; i < 16; ++i) G[(16 * wb + i) * pg + c] += pre;
   }
-  __syncthreads();
+  block_barrier();
 }
 
 // q and k rows in LDS (64 x KT bf16 each) to unit L2 norm over KT (x / sqrt(sum x^2 + eps)),
@@ -464,7 +464,7 @@ __global__ __launch_bounds__(512) void prep_kernel(BwdArgs a) {
   cumsum_rows<KT, NTH>(G, PG, reinterpret_cast<float*>(lds + L::tot), tid);  // includes barriers
   if (a.flags & kFlagQkL2norm) {
     l2norm_rows<KT, NTH>(sq, sk, PK, tid);
-    __syncthreads();
+    block_barrier();
   }
 
   // operands of the row-block-w products
@@ -493,7 +493,7 @@ __global__ __launch_bounds__(512) void prep_kernel(BwdArgs a) {
       st8(bw + j * PK + c8, ko);
     }
   }
-  __syncthreads();
+  block_barrier();
 
   // Aq (role 0) or Mr (role 1), row block w; tiles J <= w
   f32x4 acc[4];
@@ -525,7 +525,7 @@ __global__ __launch_bounds__(512) void prep_kernel(BwdArgs a) {
       else acc[3] = dir;
     }
   }
-  __syncthreads();  // qs / ks / bop are dead from here; mr / tf reuse them
+  block_barrier();  // qs / ks / bop are dead from here; mr / tf reuse them
   float* smr = reinterpret_cast<float*>(lds + L::mr);
   float* stf = reinterpret_cast<float*>(lds + L::tf);
   float* scr = reinterpret_cast<float*>(lds + L::scr) + w * 16 * 17;
@@ -557,7 +557,7 @@ __global__ __launch_bounds__(512) void prep_kernel(BwdArgs a) {
       }
     }
   }
-  __syncthreads();
+  block_barrier();
   // T = (I + diag(beta) Mr)^-1. Diagonal 16 x 16 blocks by forward substitution in
   // registers (wave w owns block w; lane: column lr, rows 4 lq + r, with its rows of
   // diag(beta) Mr): step k takes the finished row k of T from the lanes that hold it and
@@ -623,7 +623,7 @@ __global__ __launch_bounds__(512) void prep_kernel(BwdArgs a) {
       st8(kgt + c * kC + i8, z);
     }
   }
-  __syncthreads();
+  block_barrier();
   // ... then block row I, column J = I - d for d = 1, 2, 3:
   // T_IJ = -T_II sum_{J <= L < I} diag(beta_I) Mr_IL T_LJ, on fp32 MFMA
   for (int d = 1; d < 4; ++d) {
@@ -640,7 +640,7 @@ __global__ __launch_bounds__(512) void prep_kernel(BwdArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) stf[(16 * I + 4 * lq + r) * 65 + 16 * J + lr] = t[r];
     }
-    __syncthreads();
+    block_barrier();
   }
   // T, T^T (bf16)
   {
@@ -668,7 +668,7 @@ __global__ __launch_bounds__(512) void prep_kernel(BwdArgs a) {
         continue;
       }
       body(ch, item);
-      __syncthreads();  // the next item's staging overwrites this item's LDS
+      block_barrier();  // the next item's staging overwrites this item's LDS
     }
   } else {
     const Chunk ch = item_chunk(a, blockIdx.x);
@@ -841,14 +841,14 @@ __global__ __launch_bounds__(64 * NW) void fwd_sweep_kernel(BwdArgs a) {
   const int NT = sq_.nch;
   if (NT > 0) fetch(0);
   for (int n = 0; n < NT; ++n) {
-    __syncthreads();
+    block_barrier();
     put();
     // h of this chunk, transposed into this wave's LDS rows, for the workspace store at the end
     // of the step (tile ct's 4 rows are 4 consecutive channels)
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) st4(s_ht + lr * PK + 32 * (ct >> 1) + 8 * lq + 4 * (ct & 1), S[ct]);
     if (n + 1 < NT) fetch(n + 1);
-    __syncthreads();
+    block_barrier();
     // X = Kg h, W0 = V - X, Y = beta W0
     const size_t trow = (sq_.slot0 + n) * kC;
     // W0 and U rows of this chunk: buffer stores, never behind a branch (columns >= V dropped);
@@ -1010,14 +1010,14 @@ __global__ __launch_bounds__(64 * NW) void rev_sweep_kernel(BwdArgs a) {
   const int hi = (a.c_n > 0 && !a.ctab) ? a.c_lo + a.c_n : sq_.nch;
   if (hi > lo) fetch(hi - 1);
   for (int n = hi - 1; n >= lo; --n) {
-    __syncthreads();
+    block_barrier();
     put();
     // dS reaching the state that leaves this chunk, transposed into this wave's LDS rows, for
     // the workspace store at the end of the step (tile ct's 4 rows are 4 consecutive channels)
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) st4(s_dst + lr * PK + 32 * (ct >> 1) + 8 * lq + 4 * (ct & 1), D[ct]);
     if (n > lo) fetch(n - 1);
-    __syncthreads();
+    block_barrier();
     bf16x8 bdo[kC / 32], bds[KT / 32];
     load_b<kC>(bdo, s_dow, kPC, lane);
 #pragma unroll
@@ -1410,7 +1410,7 @@ __global__ __launch_bounds__(64 * kLocalWaves) void local_kernel(BwdArgs a) {
   cumsum_rows<KH, NTH>(G, PG, reinterpret_cast<float*>(lds + L::tot), tid);  // includes barriers
   if (a.flags & kFlagQkL2norm) {
     l2norm_half<KH, NTH>(sq, sk, PK, qb + (KH - c0), kb + (KH - c0), qrow, nrow, tid);
-    __syncthreads();
+    block_barrier();
   }
 
   // dbeta, first term: Ut_i . W0_i for this block's rows (first half)
@@ -1447,7 +1447,7 @@ __global__ __launch_bounds__(64 * kLocalWaves) void local_kernel(BwdArgs a) {
     // rowsum(dS * h): the per pieces of a row sit on per consecutive lanes; when per is a
     // power of two they are summed across lanes and stored once, else each piece is kept in
     // LDS and the row is summed below in a fixed order
-    __syncthreads();  // every wave is done with h
+    block_barrier();  // every wave is done with h
 #pragma unroll
     for (int e = 0; e < NH; ++e) {
       const int u = tid + NTH * e, r = u / per, c8 = 8 * (u % per);
@@ -1467,7 +1467,7 @@ __global__ __launch_bounds__(64 * kLocalWaves) void local_kernel(BwdArgs a) {
       if (in) st8(s_hs + r * PV + c8, xds[e]);
     }
   }
-  __syncthreads();
+  block_barrier();
   if (!pow2 && tid < KH) {
     float sum = 0.f;
     for (int p = 0; p < per; ++p) sum += lxp[tid * 16 + p];
@@ -1517,7 +1517,7 @@ __global__ __launch_bounds__(64 * kLocalWaves) void local_kernel(BwdArgs a) {
       if (lr == 0) db2[rw + 4 * lq + r] = x;
     }
   }
-  __syncthreads();  // phase 1 operands are dead
+  block_barrier();  // phase 1 operands are dead
 
   // ---------------- phase 2: F, E and the relative-decay products
   bf16* s_f = reinterpret_cast<bf16*>(lds + L::f);
@@ -1540,7 +1540,7 @@ __global__ __launch_bounds__(64 * kLocalWaves) void local_kernel(BwdArgs a) {
     st4(s_ft + j * kPC + rw + 4 * lq, fv);
     st4(s_et + j * kPC + rw + 4 * lq, evv);
   }
-  __syncthreads();
+  block_barrier();
   // this wave's channels of block w: span within kSpanLim, or its diagonal terms one by one
   bool wide_l = false;
   for (int c = lane; c < KH; c += 64) wide_l |= !(fabsf(G[ew * PG + c] - G[rw * PG + c]) <= kSpanLim);
@@ -1584,7 +1584,7 @@ __global__ __launch_bounds__(64 * kLocalWaves) void local_kernel(BwdArgs a) {
       }
     }
   }
-  __syncthreads();  // phase 2 operands are dead
+  block_barrier();  // phase 2 operands are dead
 
   // ---------------- phase 3: output factors, dq, dk, dG, then dg by a reverse scan
   float* dgs = reinterpret_cast<float*>(lds + L::dgs);
@@ -1618,7 +1618,7 @@ __global__ __launch_bounds__(64 * kLocalWaves) void local_kernel(BwdArgs a) {
       }
     }
   }
-  __syncthreads();
+  block_barrier();
   if (!a.dq32) {
     for (int u = tid; u < kC * (KH / 8); u += NTH) {
       const int i = u / (KH / 8), c8 = 8 * (u % (KH / 8));
@@ -1641,7 +1641,7 @@ __global__ __launch_bounds__(64 * kLocalWaves) void local_kernel(BwdArgs a) {
     for (int i = 15; i >= 0; --i) bsum += dgs[(16 * sp + i) * PG + sc];
     segs[sp * KH + sc] = bsum;
   }
-  __syncthreads();
+  block_barrier();
   if (tid < 4 * KH) {
     float run = lx[sc] + lx[KH + sc] + lx[2 * KH + sc] + lx[3 * KH + sc] + ex(G[(kC - 1) * PG + sc]) * lx2[sc];
     for (int p = 3; p > sp; --p) run += segs[p * KH + sc];
@@ -1652,7 +1652,7 @@ __global__ __launch_bounds__(64 * kLocalWaves) void local_kernel(BwdArgs a) {
       sdg[row * PK + sc] = static_cast<bf16>(run);
     }
   }
-  __syncthreads();
+  block_barrier();
   for (int u = tid; u < kC * (KH / 8); u += NTH) {  // dg rows as 16-byte pieces
     const int i = u / (KH / 8), c8 = 8 * (u % (KH / 8));
     if (i < nrow) st8(a.dg + ((row0 + i) * a.HV + hv) * KT + c0 + c8, ld8(sdg + i * PK + c8));

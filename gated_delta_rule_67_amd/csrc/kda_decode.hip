@@ -108,7 +108,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(
   }
   if (t < vw) s_v[t] = to_f32(xv);
   const float bt = (flags & kFlagBetaSigmoid) ? sigmoid_f32(to_f32(xb)) : to_f32(xb);
-  __syncthreads();
+  block_barrier();
 
   if (t < 64) {  // q . k and the squared norms, one wave
     float p = 0.f, nq = 0.f, nk = 0.f;
@@ -145,7 +145,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(
     s_pa[rg * nc + c4] = pa;
     s_pb[rg * nc + c4] = pb;
   }
-  __syncthreads();
+  block_barrier();
 
   if (t < vw) {
     const int cc = t >> 2, e = t & 3;
@@ -159,7 +159,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(
     s_u[t] = ik * u;  // the state update writes (k / |k|) u^T
     o[(size_t)bh * V + v0 + t] = from_f32<Tin>(iq * bq + iq * ik * s_qk * u);
   }
-  __syncthreads();
+  block_barrier();
 
   if (active) {
     const f32x4 u4 = {s_u[4 * c4], s_u[4 * c4 + 1], s_u[4 * c4 + 2], s_u[4 * c4 + 3]};

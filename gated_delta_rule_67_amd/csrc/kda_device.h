@@ -89,6 +89,18 @@ __device__ __forceinline__ void direct_diag(const float (&d)[NS][8], const bf16x
 // True on every lane when any lane's v is true.
 __device__ __forceinline__ bool wave_any(bool v) { return __builtin_amdgcn_ballot_w64(v) != 0; }
 
+// Workgroup barrier with the memory ordering of __syncthreads(), plus empty asm statements with
+// a memory clobber on each side of s_barrier, so that the compiler moves no memory access across
+// it: with __syncthreads() alone, LDS reads between two barriers of a loop were seen sunk below
+// the second one, into the next iteration, where other waves had already rewritten the data.
+__device__ __forceinline__ void block_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
 // Workgroup barrier for LDS traffic only: waits for this wave's LDS operations, not for
 // its outstanding global loads or stores (a plain __syncthreads() also drains those, which
 // would expose every prefetch and every output store). The empty asm statements with a memory

@@ -175,7 +175,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(
 #pragma unroll
   for (int e = 0; e < VEC; ++e) s_b[slice][e][lane] = sb[e];
   s_a[slice][lane] = sa;
-  __syncthreads();
+  block_barrier();
   if (slice == 0 && active) {
     float* pbr = pb + (int64_t)blockIdx.y * ld + col;
 #pragma unroll
@@ -225,7 +225,7 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(const float* __restric
       for (; j < nrb; j += kSlices) s += pb[(int64_t)j * ld + col];
     }
     red[t] = s;
-    __syncthreads();
+    block_barrier();
     if (slice == 0 && col < ld) {
       float tot = 0.f;
       for (int i = 0; i < kSlices; ++i) tot += red[i * kRedCols + c];
@@ -250,10 +250,10 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(const float* __restric
     }
     for (; i < n; i += kThreads) s += at(i);
     red[t] = s;
-    __syncthreads();
+    block_barrier();
     for (int w = kThreads / 2; w > 0; w >>= 1) {
       if (t < w) red[t] += red[t + w];
-      __syncthreads();
+      block_barrier();
     }
     if (t == 0 && dA_log) dA_log[hv] = red[0];
   }

@@ -212,7 +212,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs p)
     load_tile<CT>(tV, BV, gv + (size_t)t0 * sv, sv, nrow, BV, vvalid, p.vec_v);
     if (tid < kChunk) sBeta[tid] = tid < nrow ? to_f32(gb[(size_t)(t0 + tid) * p.HV]) : 0.f;
     if (tid < 4) sWide[tid] = 0;
-    __syncthreads();
+    block_barrier();
 
     // ---------------- in-block cumsum of g (log2 units), per channel pair
     float Lc[16][2];
@@ -232,7 +232,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs p)
       sFirst[fb * KT + c0 + 1] = Lc[0][1];
       if (!(fabsf(a0 - Lc[0][0]) <= kSpanLim && fabsf(a1 - Lc[0][1]) <= kSpanLim)) sWide[fb] = 1;
     }
-    __syncthreads();
+    block_barrier();
 
     // ---------------- decay factors and operand tiles
     if (fact) {
@@ -302,7 +302,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs p)
 #pragma unroll
         for (int i = 0; i < 16; ++i) tKdT[(c0 + e) * PC + fb * 16 + i] = kd[e][i];
     }
-    __syncthreads();
+    block_barrier();
 
     // ---------------- stage 1 MFMA: Akk, Aq (lower tiles), X = (K*Gam) S, P = (Q*Gam) S
     f32x4 accK[3], accQ[3], accX[NVT], accP[NVT];
@@ -326,7 +326,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs p)
       mma16(accX[vt], tKG + (wave * 16) * PK, PK, tST + (vt * 16) * PK, PK, KT, lane);
       mma16(accP[vt], tQG + (wave * 16) * PK, PK, tST + (vt * 16) * PK, PK, KT, lane);
     }
-    __syncthreads();  // region A is dead from here on; region C reuses it
+    block_barrier();  // region A is dead from here on; region C reuses it
 
     // Blocks whose span exceeds kSpanLim: their diagonal tiles again, term by term, from the
     // block's q, k and g re-read (L2-resident) and staged at the start of the dead region A.
@@ -351,7 +351,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs p)
             wd[row * KT + tid] = run;
           }
         }
-        __syncthreads();
+        block_barrier();
         // the wave holding tile (I, I) of the first stage: lane column j = lr, rows 4 lq + r
         const int didx = I * (I + 1) / 2 + I, dn = didx / 4;
         if (wave == didx % 4) {
@@ -378,7 +378,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs p)
             accQ[2] = aqd;
           }
         }
-        __syncthreads();
+        block_barrier();
       }
     }
 
@@ -408,7 +408,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs p)
         tBY[vc * PC + i] = from_f32<CT>(sBeta[i] * (to_f32(tV[i * BV + vc]) - accX[vt][r]));
       }
     }
-    __syncthreads();
+    block_barrier();
 
     // ---------------- solve T = (I + M)^-1: diagonal 16x16 blocks by forward substitution
     if (wave == 0) {
@@ -428,7 +428,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs p)
         tTT[(Ib * 16 + j) * PC + Ib * 16 + i] = from_f32<CT>(tv[i]);
       }
     }
-    __syncthreads();
+    block_barrier();
 
     // level A: T[I][I-1] = -T[I][I] M[I][I-1] T[I-1][I-1] for I = 1, 3
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -439,7 +439,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs p)
 #pragma unroll
       for (int r = 0; r < 4; ++r) tZ[(wave * 16 + lr) * PC + lq * 4 + r] = from_f32<CT>(acc[r]);
     }
-    __syncthreads();
+    block_barrier();
     if (wave < 2) {
       const int I = wave == 0 ? 1 : 3;
       acc = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -451,7 +451,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs p)
         tTT[j * PC + i] = from_f32<CT>(-acc[r]);
       }
     }
-    __syncthreads();
+    block_barrier();
 
     // level B: T[23][01] = -T[23][23] M[23][01] T[01][01]
     {
@@ -461,7 +461,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs p)
 #pragma unroll
       for (int r = 0; r < 4; ++r) tZ[(J * 16 + lr) * PC + (I - 2) * 16 + lq * 4 + r] = from_f32<CT>(acc[r]);
     }
-    __syncthreads();
+    block_barrier();
     {
       const int I = 2 + (wave >> 1), J = wave & 1;
       acc = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -469,7 +469,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs p)
 #pragma unroll
       for (int r = 0; r < 4; ++r) tT[(I * 16 + lq * 4 + r) * PC + J * 16 + lr] = from_f32<CT>(-acc[r]);
     }
-    __syncthreads();
+    block_barrier();
 
     // ---------------- U = T (beta Y), rows of block `wave`
 #pragma unroll
@@ -479,7 +479,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs p)
 #pragma unroll
       for (int r = 0; r < 4; ++r) tUT[(vt * 16 + lr) * PC + wave * 16 + lq * 4 + r] = from_f32<CT>(acc[r]);
     }
-    __syncthreads();
+    block_barrier();
 
     // ---------------- O = scale (P + Aq U), store
 #pragma unroll
@@ -507,7 +507,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs p)
         for (int r = 0; r < 4; ++r) tST[(vt * 16 + lr) * PK + ct * 16 + lq * 4 + r] = from_f32<CT>(S[n][r]);
       }
     }
-    __syncthreads();
+    block_barrier();
   }
 
   if (p.sT) {

@@ -35,7 +35,7 @@ __global__ __launch_bounds__(256) void varlen_table_kernel(const int* __restrict
       prev = e;
     }
   }
-  __syncthreads();
+  block_barrier();
   for (int s = threadIdx.x; s < nseq; s += 256) {
     const int bos = cu[s], eos = cu[s + 1], c0 = coff[s], c1 = coff[s + 1];
     for (int c = c0; c < c1; ++c) {
