@@ -1119,11 +1119,23 @@ hipError_t launch_state(const WyArgs& a, hipStream_t stream) {
 // A_(p+2) and Bm_(p+2) load during step p: they do not depend on the state, and two steps of
 // products hide their latency (with four waves of two row blocks each and the next block's
 // rows loaded one block ahead, a step took about 3.8 us at K = 128).
-template <int KT>
+template <int I, int N, class F>
+__device__ __forceinline__ void unroll_steps(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    unroll_steps<I + 1, N>(f);
+  }
+}
+
+// PF > 0: the scan for exactly PF segments, unrolled whole, so that the compiler counts every
+// step's outstanding memory operations exactly (in the loop, its merge at the loop head made it
+// wait for loads issued one step earlier); PF = 0: any P, in a loop.
+template <int KT, int PF>
 __global__ __launch_bounds__(4 * KT) void segment_scan_kernel(const float* __restrict__ Am,
                                                               const float* __restrict__ Bm,
                                                               const float* s0, float* __restrict__ Sin,
-                                                              float* sT, int P, int HV, int K, int V) {
+                                                              float* sT, int Pn, int HV, int K, int V) {
+  const int P = PF > 0 ? PF : Pn;
   constexpr int NS = KT / 4;    // k steps of one product (4 per MFMA, one per lane group)
   constexpr int NRB = KT / 16;  // row blocks of the state tile, one per wave
   __shared__ float sS[KT][17];
@@ -1212,12 +1224,19 @@ __global__ __launch_bounds__(4 * KT) void segment_scan_kernel(const float* __res
     for (int st = 0; st < NS; ++st) Sb[st] = sS[NS * q + st][j];
     lds_barrier();
   };
-  for (int p = 0; p < P; p += 3) {
-    step(std::integral_constant<int, 0>{}, p);
-    if (p + 1 >= P) break;
-    step(std::integral_constant<int, 1>{}, p + 1);
-    if (p + 2 >= P) break;
-    step(std::integral_constant<int, 2>{}, p + 2);
+  if constexpr (PF > 0) {
+    unroll_steps<0, PF>([&](auto I_) {
+      constexpr int i = decltype(I_)::value;
+      step(std::integral_constant<int, i % 3>{}, i);
+    });
+  } else {
+    for (int p = 0; p < P; p += 3) {
+      step(std::integral_constant<int, 0>{}, p);
+      if (p + 1 >= P) break;
+      step(std::integral_constant<int, 1>{}, p + 1);
+      if (p + 2 >= P) break;
+      step(std::integral_constant<int, 2>{}, p + 2);
+    }
   }
 }
 
@@ -1367,9 +1386,17 @@ hipError_t launch_prefill_wy_segmented(const PrefillArgs& p, int P, void* worksp
     hipLaunchKernelGGL(kernel, dim3(p.B * p.HV * ntile), dim3(threads), 0, stream, Am, Bm, p.s0, Sin,
                        p.sT, P, p.HV, p.K, p.V);
   };
-  if (p.K <= 32) scan(segment_scan_kernel<32>, 4 * 32);
-  else if (p.K <= 64) scan(segment_scan_kernel<64>, 4 * 64);
-  else scan(segment_scan_kernel<128>, 4 * 128);
+  // the segment counts the automatic route picks have unrolled instantiations
+  auto scan_k = [&](auto kt) {
+    constexpr int KT = decltype(kt)::value;
+    if (P == 8) scan(segment_scan_kernel<KT, 8>, 4 * KT);
+    else if (P == 16) scan(segment_scan_kernel<KT, 16>, 4 * KT);
+    else if (P == 32) scan(segment_scan_kernel<KT, 32>, 4 * KT);
+    else scan(segment_scan_kernel<KT, 0>, 4 * KT);
+  };
+  if (p.K <= 32) scan_k(std::integral_constant<int, 32>{});
+  else if (p.K <= 64) scan_k(std::integral_constant<int, 64>{});
+  else scan_k(std::integral_constant<int, 128>{});
   if ((e = hipGetLastError()) != hipSuccess) return e;
   WyArgs ao = a;  // the outputs from each segment's entering state
   ao.p.s0 = Sin;
