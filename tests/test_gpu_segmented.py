@@ -4,8 +4,9 @@ that route for few heads) against the fp64 oracle.
 The segmented path composes per-segment affine state maps in a scan, so it differs from the
 plain two-kernel path by rounding only; it is held to the same bf16 reading of the tolerance
 (RMS(err) <= 2e-2 RMS(ref) with the per-row guard). Shapes cover one chunk per segment, a
-segment count that is not a power of two, GVA, K < V and K > V, an initial state updated in
-place, the input transforms, the fused gate, and a 32,768-token sequence on four heads."""
+segment count that is not a power of two, GVA, K < V and K > V, the scan's unrolled segment
+counts (8, 16, 32) and its loop, an initial state updated in place, the input transforms, the
+fused gate, and a 32,768-token sequence on four heads."""
 
 import numpy as np
 import pytest
@@ -31,6 +32,8 @@ def _check(o, s, inp, **kw):
     dict(B=1, T=768, H=1, HV=1, K=32, V=48, segments=3),     # 3 segments of 4 chunks, V > K
     dict(B=1, T=512, H=1, HV=2, K=128, V=64, segments=2),
     dict(B=1, T=256, H=1, HV=1, K=64, V=64, segments=1),     # the plain path
+    dict(B=1, T=4096, H=1, HV=1, K=128, V=128, segments=32),  # the scan unrolled for 32
+    dict(B=1, T=2048, H=1, HV=2, K=32, V=32, segments=16),    # ... for 16, at K = 32
 ])
 def test_segmented_matches_oracle(case):
     seg = case.pop("segments")
