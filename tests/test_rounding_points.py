@@ -160,3 +160,19 @@ def test_small_beta_readout_breaks_the_bound_through_qg_and_s():
     assert h.ratios(("qg",))[0] > 1.0 and h.ratios(("s_p",))[0] > 1.0
     rest = tuple(p for p in KERNEL_POINTS if p not in ("qg", "s_p"))
     assert h.ratios(rest)[0] <= 1.0
+
+
+def test_short_keys_slow_gate_off_diagonal_aq_sets_the_excess():
+    # K = 32, V = 64, slow gate, 2,048 tokens: o's per-element figure comes near the bound on
+    # the GPU. The emulation puts it there too, and the off-diagonal Aq points (the operands of
+    # its products and the stored tiles, rounded once) are what takes the excess: without them
+    # the rest stay where they are at K = 128.
+    case = dict(B=1, T=2048, H=1, HV=2, K=32, V=64)
+    inp = prefill_inputs(**case, dtype="bf16", init_state=True, seed=sum(case.values()) + 16,
+                         gate="slow")
+    h = Head(inp, 0)
+    assert h.ratios(KERNEL_POINTS)[0] > 0.9
+    alone = {p: h.ratios((p,))[0] for p in KERNEL_POINTS}
+    assert max(alone, key=alone.get) == "aq_ops_off"
+    rest = tuple(p for p in KERNEL_POINTS if p not in ("aq_ops_off", "aq_off"))
+    assert h.ratios(rest)[0] <= 0.8
