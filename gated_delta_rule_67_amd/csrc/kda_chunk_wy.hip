@@ -149,6 +149,10 @@ struct WyArgs {
   const int* coff;
   const int2* ctab;
   int NC;
+  // Columns of v and o (0: p.V). With 0 < vw < p.V the state is wider than v: its columns vw ..
+  // p.V - 1 take v = 0 and write no o (the segmented path traces a segment's maps A and Bm in
+  // one pass over the state [Bm | A]).
+  int vw = 0;
 };
 
 // ================================================================ per-chunk factors
@@ -781,7 +785,7 @@ void state_kernel(WyArgs a) {
     vt_idx = blockIdx.x % nvt;
   }
   const int b = head / p.HV, hv = head - b * p.HV;
-  const int K = p.K, V = p.V;
+  const int K = p.K, V = p.V, VW = a.vw > 0 ? a.vw : V;
   // this sequence's tokens bos .. bos + len - 1 (packed order) and its NT chunk blocks
   int bos, len, NT;
   const unsigned char* wsh;
@@ -800,7 +804,7 @@ void state_kernel(WyArgs a) {
   // Both roles pass the same barriers: one before each chunk. Before a buffer is read, the
   // DMA waves have waited for their loads into it; before it is refilled, every compute
   // wave has passed the barrier that follows its last read.
-  const unsigned rowb = (unsigned)(p.HV * V * 2);  // bytes between consecutive tokens of v / o
+  const unsigned rowb = (unsigned)(p.HV * VW * 2);  // bytes between consecutive tokens of v / o
   if (wv >= NW) {
     // DMA waves: the factors by LDS DMA; the v tile by range-checked loads (zeros past T
     // or V), stored as loaded (16 bytes: 8 columns of a token).
@@ -814,13 +818,13 @@ void state_kernel(WyArgs a) {
     for (int e = 0; e < NPL; ++e) {
       const int pc = pl + 64 * kDmaWaves * e, row = pc / PPR, c8 = pc % PPR;
       const int col = vt_idx * BV + 8 * c8;
-      voff[e] = (col < V && row < kC) ? (unsigned)(col * 2) + (unsigned)row * rowb : kOutOfRange;
+      voff[e] = (col < VW && row < kC) ? (unsigned)(col * 2) + (unsigned)row * rowb : kOutOfRange;
     }
     bf16x8 rvv[NPL];
     auto load_v = [&](int n) {  // n past the end re-reads the last chunk (no branch)
       n = min(n, NT - 1);
       const int t0 = n * kC, nrow = min(kC, len - t0);
-      const auto rv_ = make_rsrc(static_cast<const bf16*>(p.v) + (((size_t)bos + t0) * p.HV + hv) * V,
+      const auto rv_ = make_rsrc(static_cast<const bf16*>(p.v) + (((size_t)bos + t0) * p.HV + hv) * VW,
                                  p.v ? (unsigned)nrow * rowb : 0u);  // no v: zeros
 #pragma unroll
       for (int e = 0; e < NPL; ++e)
@@ -879,9 +883,9 @@ void state_kernel(WyArgs a) {
 
   const int vc = vt_idx * BV + 16 * wv + lr;  // the lane's V column
   const bool vok = vc < V;
-  // lane part of an o offset (column, rows 4lq); columns >= V start out of range. The row
+  // lane part of an o offset (column, rows 4lq); columns >= VW start out of range. The row
   // part (16I + r) * rowb goes in the scalar offset.
-  const unsigned vlane = vok ? (unsigned)(vc * 2) + 4u * lq * rowb : kOutOfRange;
+  const unsigned vlane = vc < VW ? (unsigned)(vc * 2) + 4u * lq * rowb : kOutOfRange;
 
   f32x4 S[NCT];
   {
@@ -1013,7 +1017,7 @@ void state_kernel(WyArgs a) {
     O[3] = mfma32(fl[3], ub[1], mfma32(fa[5], ul[1], mfma32(fa[5], ub[1],
            mfma32(fa[4], ul[0], mfma32(fa[4], ub[0], P[3])))));
     // stores go out before the state update so they drain under its products
-    const auto ro_ = make_rsrc(static_cast<const bf16*>(p.o) + (((size_t)bos + t0) * p.HV + hv) * V,
+    const auto ro_ = make_rsrc(static_cast<const bf16*>(p.o) + (((size_t)bos + t0) * p.HV + hv) * VW,
                                p.o ? (unsigned)nrow * rowb : 0u);  // no o: stores dropped
 #pragma unroll
     for (int I = 0; I < 4; ++I)
@@ -1130,9 +1134,9 @@ __device__ __forceinline__ void unroll_steps(F&& f) {
 // PF > 0: the scan for exactly PF segments, unrolled whole, so that the compiler counts every
 // step's outstanding memory operations exactly (in the loop, its merge at the loop head made it
 // wait for loads issued one step earlier); PF = 0: any P, in a loop.
+// The maps of segment m are one K x (V + K) matrix [Bm | A] at Mp + m K (V + K).
 template <int KT, int PF>
-__global__ __launch_bounds__(4 * KT) void segment_scan_kernel(const float* __restrict__ Am,
-                                                              const float* __restrict__ Bm,
+__global__ __launch_bounds__(4 * KT) void segment_scan_kernel(const float* __restrict__ Mp,
                                                               const float* s0, float* __restrict__ Sin,
                                                               float* sT, int Pn, int HV, int K, int V) {
   const int P = PF > 0 ? PF : Pn;
@@ -1149,8 +1153,9 @@ __global__ __launch_bounds__(4 * KT) void segment_scan_kernel(const float* __res
   // range of one matrix: rows >= K fall past the range and columns >= V start at kOutOfRange,
   // so they read zeros and their stores are dropped, without a branch (branches around each
   // access made the compiler wait for all memory operations before each one).
-  const unsigned kv = (unsigned)K * V * 4, kk = (unsigned)K * K * 4;
-  const unsigned vrow = (unsigned)V * 4;
+  const unsigned kv = (unsigned)K * V * 4;
+  const unsigned vrow = (unsigned)V * 4, mrow = (unsigned)(V + K) * 4;
+  const size_t mstride = (size_t)K * (V + K);
   const unsigned lcol = col < V ? (unsigned)col * 4 : kOutOfRange;
   auto mat_kv = [&](const float* base, size_t m) { return make_rsrc(base + m * K * V, kv); };
 
@@ -1175,16 +1180,18 @@ __global__ __launch_bounds__(4 * KT) void segment_scan_kernel(const float* __res
   const int row = 16 * w + j;  // this lane's row of A_p
   auto load_step = [&](int pp, f32x4 (&a4)[NS / 4], f32x4& bm) {
     const size_t seg = (size_t)(b * P + pp) * HV + hv;
-    const auto rb_ = mat_kv(Bm, seg);
+    // Bm: columns 0 .. V - 1 of the segment's maps; A: columns V .. V + K - 1 (a range that
+    // starts at A's first column and ends with the matrix)
+    const auto rb_ = make_rsrc(Mp + seg * mstride, (unsigned)K * mrow);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       bm[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                            rb_, lcol + (unsigned)(16 * w + 4 * q + i) * vrow, 0, 0));
-    const auto ra = make_rsrc(Am + seg * K * K, kk);
+                                            rb_, lcol + (unsigned)(16 * w + 4 * q + i) * mrow, 0, 0));
+    const auto ra = make_rsrc(Mp + seg * mstride + V, (unsigned)K * mrow - (unsigned)V * 4);
 #pragma unroll
     for (int m = 0; m < NS / 4; ++m) {
       const int k = NS * q + 4 * m;  // K % 8 == 0: a piece is wholly inside or outside
-      const unsigned off = (row < K && k < K) ? (unsigned)(row * K + k) * 4 : kOutOfRange;
+      const unsigned off = (row < K && k < K) ? (unsigned)row * mrow + (unsigned)k * 4 : kOutOfRange;
       a4[m] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0));
     }
   };
@@ -1240,12 +1247,14 @@ __global__ __launch_bounds__(4 * KT) void segment_scan_kernel(const float* __res
   }
 }
 
-// n identity matrices of K x K (the state entering each segment when its map A is traced).
-__global__ __launch_bounds__(256) void eye_kernel(float* __restrict__ out, size_t n, int K) {
-  const size_t total = n * K * K;
+// n matrices K x (V + K) = [0 | I]: the state entering each segment when its maps [Bm | A]
+// are traced (Bm from a zero state with v, A from the identity with v = 0).
+__global__ __launch_bounds__(256) void seg_map_init_kernel(float* __restrict__ out, size_t n, int K, int V) {
+  const int W = V + K;
+  const size_t total = n * K * W;
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (size_t)gridDim.x * 256) {
-    const int e = (int)(i % ((size_t)K * K));
-    out[i] = (e / K == e % K) ? 1.f : 0.f;
+    const int e = (int)(i % ((size_t)K * W)), r = e / W, c = e % W;
+    out[i] = (c - V == r) ? 1.f : 0.f;
   }
 }
 
@@ -1309,18 +1318,17 @@ static hipError_t launch_wy(const wy::WyArgs& a, hipStream_t stream) {
 
 namespace wy {
 // Workspace of the segmented prefill: the factor blocks of the B * P segment-sequences, then
-// per segment the maps A [K x K] and Bm [K x V] and the entering states S_in [K x V], fp32.
+// per segment the maps [Bm | A] (K x (V + K)) and the entering state S_in (K x V), fp32.
 struct SegLayout {
-  size_t blocks, am, bm, sin, total;
+  size_t blocks, maps, sin, total;
 };
 SegLayout seg_layout(int B, int T, int HV, int K, int V, int P) {
   auto al = [](size_t x) { return (x + 255) / 256 * 256; };
   const size_t heads = (size_t)B * P * HV;
   SegLayout l{};
   l.blocks = 0;
-  l.am = al(wy_workspace_bytes(B * P, T / P, HV, K));
-  l.bm = l.am + al(heads * K * K * 4);
-  l.sin = l.bm + al(heads * K * V * 4);
+  l.maps = al(wy_workspace_bytes(B * P, T / P, HV, K));
+  l.sin = l.maps + al(heads * K * (V + K) * 4);
   l.total = l.sin + al(heads * K * V * 4);
   return l;
 }
@@ -1328,19 +1336,20 @@ SegLayout seg_layout(int B, int T, int HV, int K, int V, int P) {
 
 // Segments for a fixed-length bf16 prefill: P > 1 cuts each sequence into P segments (P a
 // power of two, T % (64 P) == 0, at least 4 chunks per segment) when the state pass would
-// otherwise leave most CUs idle. The segmented path runs three state passes (the maps Bm and A,
-// then the outputs) and a scan, so it pays only from P >= 8 (measured: P = 4 at B1 T32768 H16
-// ties with the plain path, P = 16 at H4 is 2.7 times faster): it is used then, else P = 1.
+// otherwise leave most CUs idle: the largest P whose output pass still fits the chip in one
+// round. The segmented path runs two state passes (the maps [Bm | A] over V + K columns, then
+// the outputs) and a scan, so it pays from P >= 4; at P = 2 it loses (measured at B1 T32768,
+// K = V = 128: H16 P = 4 698 us against 957 plain, H32 P = 2 1,350 against 1,166).
 // The choice is a function of the arguments alone, taken for a full gfx950 chip (256 CUs),
 // so the workspace size a caller queries and the launch agree whatever device is current.
 constexpr int kSegmentCus = 256;
 int wy_segments(int B, int T, int HV, int V) {
   const int cus = kSegmentCus;
   const int units = B * HV * ((V + 31) / 32);  // state-pass workgroups at 32 columns each
-  if (units * 8 > cus) return 1;
+  if (units * 4 > cus) return 1;
   int P = 1;
   while (2 * P * units <= cus && T % (64 * 2 * P) == 0 && T / (64 * 2 * P) >= 4) P *= 2;
-  return P >= 8 ? P : 1;
+  return P >= 4 ? P : 1;
 }
 
 size_t wy_segmented_workspace_bytes(int B, int T, int HV, int K, int V, int P) {
@@ -1348,16 +1357,15 @@ size_t wy_segmented_workspace_bytes(int B, int T, int HV, int K, int V, int P) {
 }
 
 // The segmented prefill (P > 1, T % (64 P) == 0): factors once for all segments, then the
-// state pass three times over the B * P segment-sequences: Bm (zero entering state, v, no
-// outputs), A (identity entering state, v = 0, V = K columns, no outputs), and, after the scan
-// has made every segment's entering state, the outputs from those states.
+// state pass twice over the B * P segment-sequences: the maps, as one state [Bm | A] of V + K
+// columns entering as [0 | I] with v in the first V columns and zeros in the rest (no outputs),
+// and, after the scan has made every segment's entering state, the outputs from those states.
 hipError_t launch_prefill_wy_segmented(const PrefillArgs& p, int P, void* workspace,
                                        hipStream_t stream) {
   using namespace wy;
   const SegLayout l = seg_layout(p.B, p.T, p.HV, p.K, p.V, P);
   unsigned char* ws = static_cast<unsigned char*>(workspace);
-  float* Am = reinterpret_cast<float*>(ws + l.am);
-  float* Bm = reinterpret_cast<float*>(ws + l.bm);
+  float* maps = reinterpret_cast<float*>(ws + l.maps);
   float* Sin = reinterpret_cast<float*>(ws + l.sin);
   const int cus = device_cu_count();
   PrefillArgs ps = p;
@@ -1366,24 +1374,19 @@ hipError_t launch_prefill_wy_segmented(const PrefillArgs& p, int P, void* worksp
   WyArgs a{ps, ws + l.blocks, (ps.T + kC - 1) / kC, nullptr, nullptr, nullptr, 0};
   hipError_t e = launch_factors_any(a, cus, stream);
   if (e != hipSuccess) return e;
-  WyArgs ab = a;  // Bm: the state leaving each segment from a zero entering state
-  ab.p.s0 = nullptr;
-  ab.p.sT = Bm;
-  ab.p.o = nullptr;
-  if ((e = launch_state_any(ab, cus, stream)) != hipSuccess) return e;
   const size_t nmat = (size_t)ps.B * p.HV;
-  hipLaunchKernelGGL(eye_kernel, dim3(1024), dim3(256), 0, stream, Am, nmat, p.K);
+  hipLaunchKernelGGL(seg_map_init_kernel, dim3(1024), dim3(256), 0, stream, maps, nmat, p.K, p.V);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  WyArgs aa = a;  // A: the map of the entering state (identity in, v = 0, K columns)
-  aa.p.V = p.K;
-  aa.p.v = nullptr;
-  aa.p.s0 = Am;
-  aa.p.sT = Am;
-  aa.p.o = nullptr;
-  if ((e = launch_state_any(aa, cus, stream)) != hipSuccess) return e;
+  WyArgs am = a;  // [Bm | A], in place: the state leaving each segment from [0 | I]
+  am.p.V = p.V + p.K;
+  am.vw = p.V;
+  am.p.s0 = maps;
+  am.p.sT = maps;
+  am.p.o = nullptr;
+  if ((e = launch_state_any(am, cus, stream)) != hipSuccess) return e;
   const int ntile = (p.V + 15) / 16;
   auto scan = [&](auto kernel, int threads) {
-    hipLaunchKernelGGL(kernel, dim3(p.B * p.HV * ntile), dim3(threads), 0, stream, Am, Bm, p.s0, Sin,
+    hipLaunchKernelGGL(kernel, dim3(p.B * p.HV * ntile), dim3(threads), 0, stream, maps, p.s0, Sin,
                        p.sT, P, p.HV, p.K, p.V);
   };
   // the segment counts the automatic route picks have unrolled instantiations

@@ -368,13 +368,13 @@ int kda_recurrent_step_gated(const void* q, const void* k, const void* v, const 
  * `segments` equal parts and runs them side by side: the state leaving a segment is an affine
  * map of the state entering it, S_out = A S_in + Bm (K3 README, roadmap row L2, step 4: the
  * state passed between chunks, composed over a segment's chunks), so one pass over all
- * segments gives every Bm (zero entering state), one more gives every A (identity entering
- * state, v = 0), a scan composes them in segment order into each segment's entering state and
- * the final state, and a last pass makes o from those entering states. Same arithmetic per
- * chunk as kda_chunk_fwd_ex's two-kernel path; the result differs from it by rounding only.
- * kda_chunk_fwd / kda_chunk_fwd_ex / kda_chunk_fwd_gated take this route by themselves when it
- * pays (eight or more segments fit a full chip's 256 CUs), and size their workspace
- * for it.
+ * segments gives every [Bm | A] (a state of V + K columns entering as [0 | I], with v in the
+ * first V columns and zeros in the rest), a scan composes them in segment order into each
+ * segment's entering state and the final state, and a last pass makes o from those entering
+ * states. Same arithmetic per chunk as kda_chunk_fwd_ex's two-kernel path; the result differs
+ * from it by rounding only. kda_chunk_fwd / kda_chunk_fwd_ex / kda_chunk_fwd_gated take this
+ * route by themselves when it pays (four or more segments fit a full chip's 256 CUs), and size
+ * their workspace for it.
  *
  *   segments     >= 1, T % (64 * segments) == 0 (else KDA_ERR_INVALID); 1 is the plain
  *                two-kernel path

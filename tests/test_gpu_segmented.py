@@ -87,6 +87,27 @@ def test_auto_selects_segments_for_few_heads():
     _check(o1, s1, inp)
 
 
+def test_auto_selects_four_segments_for_sixteen_heads():
+    """B=1, T=4096, 16 heads: the automatic route takes 4 segments (the largest count whose
+    output pass fits a 256-CU chip in one round); its result is that of the explicit 4-segment
+    call, bit for bit, and within the bf16 tolerance of the oracle."""
+    B, T, H, HV, K, V = 1, 4096, 16, 16, 128, 128
+    lib = kda.library()
+    four = lib.kda_chunk_fwd_segmented_workspace_size(B, T, H, HV, K, V, 4, 1)
+    auto = lib.kda_chunk_fwd_workspace_size(B, T, H, HV, K, V, 64, 1)
+    log(f"workspace four segments {four} auto {auto}")
+    assert auto == four
+    inp = prefill_inputs(B, T, H, HV, K, V, "bf16", True, seed=57, gate="slow")
+    d = gpu(inp)
+    o, s = kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], inp["scale"],
+                             d["initial_state"])
+    o4, s4 = kda.kda_chunk_fwd_segmented(d["q"], d["k"], d["v"], d["g"], d["beta"], 4,
+                                         inp["scale"], d["initial_state"])
+    torch.cuda.synchronize()
+    assert torch.equal(o, o4) and torch.equal(s, s4)
+    _check(o, s, inp)
+
+
 def test_segmented_with_the_fused_gate():
     B, T, H, HV, K, V = 1, 2048, 2, 2, 64, 64
     inp = prefill_inputs(B, T, H, HV, K, V, "bf16", True, seed=52)
