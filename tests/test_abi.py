@@ -447,10 +447,21 @@ def test_segmented_workspace_sizes(lib):
     plain = ws(1, 4096, 2, 2, 128, 128, 1, 1)
     assert plain == 1 * 2 * (4096 // 64) * lib.kda_chunk_fwd_workspace_size(1, 64, 1, 1, 128, 128, 64, 1)
     seg = ws(1, 4096, 2, 2, 128, 128, 16, 1)
-    # the same factor blocks plus, per segment and head, A (K x K), Bm and S_in (K x V) in fp32
-    assert seg == plain + 3 * 16 * 2 * 128 * 128 * 4
+    # the same factor blocks plus, per segment and head, the maps [Bm | A] (K x (V + K)) and
+    # S_in (K x V) in fp32
+    assert seg == plain + 16 * 2 * 128 * (2 * 128 + 128) * 4
+    plain64 = ws(1, 4096, 2, 2, 64, 128, 1, 1)
+    assert ws(1, 4096, 2, 2, 64, 128, 8, 1) == plain64 + 8 * 2 * 64 * (2 * 128 + 64) * 4
     assert ws(1, 4096, 2, 2, 128, 128, 3, 1) == 0     # 4096 is not a multiple of 64 * 3
     assert ws(1, 4096, 2, 2, 128, 128, 16, 0) == 0    # bf16 only
+
+
+@pytest.mark.parametrize("HV,segments", [(2, 16), (4, 16), (8, 8), (16, 4), (32, 1), (64, 1)])
+def test_automatic_segment_count(lib, HV, segments):
+    # B = 1, T = 4096 (64 chunks), K = V = 128: the largest power of two P with
+    # P * HV * ceil(V / 32) <= 256, at least 4 chunks per segment, taken from P = 4 on
+    auto = lib.kda_chunk_fwd_workspace_size(1, 4096, HV, HV, 128, 128, 64, 1)
+    assert auto == lib.kda_chunk_fwd_segmented_workspace_size(1, 4096, HV, HV, 128, 128, segments, 1)
 
 
 def _noalloc(lib, **kw):
