@@ -1116,9 +1116,10 @@ hipError_t launch_state(const WyArgs& a, hipStream_t stream) {
 //
 // One workgroup of KT / 16 waves per (b, hv, 16-column tile). The products run on fp32 MFMA
 // (v_mfma_f32_16x16x4_f32) with the contraction index permuted so that lane group q = l / 16
-// covers k = NS q .. NS q + NS - 1 (NS = KT / 4): every wave keeps the whole K x 16 state tile
-// in registers as B operands (lane (q, j) holds column j's rows NS q ..), and a lane's A operands
-// are NS consecutive floats of one row of A_p, loaded as 16-byte pieces. Wave w computes row
+// covers k = 16 i + 4 q + e (i < KT / 16, e < 4; NS = KT / 4 values): every wave keeps the whole
+// K x 16 state tile in registers as B operands (lane (q, j) holds column j's rows of group q),
+// and a lane's A operands are the same NS floats of one row of A_p, loaded as 16-byte pieces,
+// the four lane groups of a row reading 64 contiguous bytes per load. Wave w computes row
 // block w; the new rows meet in LDS once per step and come back as B operands. A wave's rows of
 // A_(p+2) and Bm_(p+2) load during step p: they do not depend on the state, and two steps of
 // products hide their latency (with four waves of two row blocks each and the next block's
@@ -1159,23 +1160,26 @@ __global__ __launch_bounds__(4 * KT) void segment_scan_kernel(const float* __res
   const unsigned lcol = col < V ? (unsigned)col * 4 : kOutOfRange;
   auto mat_kv = [&](const float* base, size_t m) { return make_rsrc(base + m * K * V, kv); };
 
-  float Sb[NS];  // B operands: S[NS q + s][col]
+  // lane group q's contraction index in product st: the four groups of a row read 64
+  // contiguous bytes of it per load (16 rows a load instruction, not 64 scattered pieces)
+  auto krow = [&](int st) { return 16 * (st >> 2) + 4 * q + (st & 3); };
+  float Sb[NS];  // B operands: S[krow(s)][col]
   {
     const auto r0 = mat_kv(s0, bh);
 #pragma unroll
     for (int st = 0; st < NS; ++st)
       Sb[st] = s0 ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                                  r0, lcol + (unsigned)(NS * q + st) * vrow, 0, 0))
+                                                  r0, lcol + (unsigned)krow(st) * vrow, 0, 0))
                   : 0.f;
   }
-  // rows NS q .. of column col go out from wave q % NRB (each row once)
+  // rows krow(.) of column col go out from wave q % NRB (each row once)
   auto store_rows = [&](float* dst, size_t m) {
     const auto rd = mat_kv(dst, m);
     const unsigned base = w == q % NRB ? lcol : kOutOfRange;
 #pragma unroll
     for (int st = 0; st < NS; ++st)
       __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, Sb[st]), rd,
-                                            base + (unsigned)(NS * q + st) * vrow, 0, 0);
+                                            base + (unsigned)krow(st) * vrow, 0, 0);
   };
   const int row = 16 * w + j;  // this lane's row of A_p
   auto load_step = [&](int pp, f32x4 (&a4)[NS / 4], f32x4& bm) {
@@ -1190,7 +1194,7 @@ __global__ __launch_bounds__(4 * KT) void segment_scan_kernel(const float* __res
     const auto ra = make_rsrc(Mp + seg * mstride + V, (unsigned)K * mrow - (unsigned)V * 4);
 #pragma unroll
     for (int m = 0; m < NS / 4; ++m) {
-      const int k = NS * q + 4 * m;  // K % 8 == 0: a piece is wholly inside or outside
+      const int k = 16 * m + 4 * q;  // K % 8 == 0: a piece is wholly inside or outside
       const unsigned off = (row < K && k < K) ? (unsigned)row * mrow + (unsigned)k * 4 : kOutOfRange;
       a4[m] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0));
     }
@@ -1228,7 +1232,7 @@ __global__ __launch_bounds__(4 * KT) void segment_scan_kernel(const float* __res
     }
     lds_barrier();
 #pragma unroll
-    for (int st = 0; st < NS; ++st) Sb[st] = sS[NS * q + st][j];
+    for (int st = 0; st < NS; ++st) Sb[st] = sS[krow(st)][j];
     lds_barrier();
   };
   if constexpr (PF > 0) {
