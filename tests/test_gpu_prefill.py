@@ -69,13 +69,22 @@ def test_small_shapes(shape, dtype):
     _check_full(inp, dtype, chunk=8, what=str(shape), elem=shape["V"] % 8 == 0)
 
 
+@pytest.mark.parametrize("plain", [False, True], ids=["auto-4-segments", "plain"])
 @pytest.mark.parametrize("gate,beta", [("slow", "default"), ("zero", "default"),
                                        ("bound", "default"), ("default", "small"),
                                        ("default", "large"), ("slow", "large")])
-def test_stress_gates(gate, beta):
-    log(f"prefill stress gate={gate} beta={beta} (B1 T1024 H=HV=16 K=V=128 bf16)")
+def test_stress_gates(gate, beta, plain):
+    # B1 T1024 H16: kda_chunk_fwd's own route is the segmented one (4 segments); plain forces
+    # the two-kernel path (one segment)
+    log(f"prefill stress gate={gate} beta={beta} plain={plain} (B1 T1024 H=HV=16 K=V=128 bf16)")
     inp = prefill_inputs(1, 1024, 16, 16, 128, 128, "bf16", True, 77, gate=gate, beta=beta)
-    o, s = _gpu_fwd(inp)
+    if plain:
+        d = gpu(inp)
+        o, s = kda.kda_chunk_fwd_segmented(d["q"], d["k"], d["v"], d["g"], d["beta"], 1,
+                                           d["scale"], d["initial_state"])
+        torch.cuda.synchronize()
+    else:
+        o, s = _gpu_fwd(inp)
     # beta ~ 1e-3 with the default decay: o is the initial state's readout (Q*Gam) S for a
     # few tokens and ~0 after, so RMS(o) is far below those tokens' terms and one bf16
     # rounding of Q*Gam and of S there exceeds 2e-2 RMS; the per-element bound is logged

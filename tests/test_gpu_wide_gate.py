@@ -27,21 +27,29 @@ from tests.helpers import assert_parity, gpu, log, to64
 pytestmark = pytest.mark.gpu
 
 
-def _fwd_case(B, T, H, HV, K, V, gate_mode, seed, chunk=64, workspace=True):
+def _fwd_case(B, T, H, HV, K, V, gate_mode, seed, chunk=64, workspace=True, segments=None):
+    # segments None: kda_chunk_fwd's own route; else kda_chunk_fwd_segmented with that count
+    # (1: the plain two-kernel path)
     inp = prefill_inputs(B, T, H, HV, K, V, "bf16", True, seed, gate=gate_mode)
     d = gpu(inp)
-    o, s = kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["scale"],
-                             d["initial_state"], chunk_size=chunk)
+    if segments is None:
+        o, s = kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["scale"],
+                                 d["initial_state"], chunk_size=chunk)
+    else:
+        o, s = kda.kda_chunk_fwd_segmented(d["q"], d["k"], d["v"], d["g"], d["beta"], segments,
+                                           d["scale"], d["initial_state"])
     torch.cuda.synchronize()
     ref_o, ref_s = recurrent(**inp)
     assert_parity(to64(o), ref_o, torch.bfloat16, f"o ({gate_mode})")
     assert_parity(to64(s), ref_s, torch.bfloat16, f"state ({gate_mode})")
 
 
+@pytest.mark.parametrize("segments", [None, 1], ids=["auto-4-segments", "plain"])
 @pytest.mark.parametrize("gate_mode", ["const:-8", "const:-20", "const:-100", "mixed"])
-def test_two_kernel_prefill_wide_decay(gate_mode):
-    log(f"two-kernel prefill B1 T1024 H16 K128 g={gate_mode}")
-    _fwd_case(1, 1024, 16, 16, 128, 128, gate_mode, seed=301)
+def test_two_kernel_prefill_wide_decay(gate_mode, segments):
+    # B1 T1024 H16: kda_chunk_fwd's own route is the segmented one (4 segments)
+    log(f"prefill B1 T1024 H16 K128 g={gate_mode} segments={segments or 'auto'}")
+    _fwd_case(1, 1024, 16, 16, 128, 128, gate_mode, seed=301, segments=segments)
 
 
 @pytest.mark.parametrize("shape", [
