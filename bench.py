@@ -12,7 +12,7 @@ reported under its own key:
   than the last-level cache, as the layers of a model would be);
 * "backward": kda_chunk_bwd (dq, dk, dv, dg, dbeta, dh0) of the prefill workload for a
   seeded dO;
-* "few_heads": the prefill at B=1, T=32768 on 4 and 8 heads (segmented when it pays);
+* "few_heads": the prefill at B=1, T=32768 on 4, 8 and 16 heads (segmented when it pays);
 * "gate": kda_gate_fwd / kda_gate_bwd on the prefill layer's [B, T, HV, K] gate input,
   and the gate fused into the prefill.
 
@@ -674,12 +674,15 @@ def main():
     if not args.no_segmented:
         from synth import prefill_inputs
         result["few_heads"] = []
-        for (fb, ft, fh) in ((1, 32768, 4), (1, 32768, 8)):
+        for (fb, ft, fh) in ((1, 32768, 4), (1, 32768, 8), (1, 32768, 16)):
             log(f"bench: few heads B={fb} T={ft} H=HV={fh}")
             fi = prefill_inputs(fb, ft, fh, fh, 128, 128, "bf16", True, seed=4323)
             fd = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in fi.items()}
             del fi
             segs = kda.library().kda_chunk_fwd_workspace_size(fb, ft, fh, fh, 128, 128, 64, 1)
+            nseg = next(P for P in (1, 2, 4, 8, 16, 32, 64) if segs ==
+                        kda.library().kda_chunk_fwd_segmented_workspace_size(fb, ft, fh, fh, 128,
+                                                                             128, P, 1))
             auto = lambda: kda.kda_chunk_fwd(fd["q"], fd["k"], fd["v"], fd["g"], fd["beta"],
                                              fd["scale"], fd["initial_state"])
             plain = lambda: kda.kda_chunk_fwd_segmented(fd["q"], fd["k"], fd["v"], fd["g"],
@@ -695,7 +698,7 @@ def main():
                 "default_tokens_per_s": fb * ft / (a_avg * 1e-3),
                 "default_roofline_frac": fbytes / (a_avg * 1e-3) / 1e9 / HBM_PEAK_GBS,
                 "plain_two_kernel_ms": p_avg, "plain_two_kernel_median_ms": p_med,
-                "workspace_bytes": segs,
+                "workspace_bytes": segs, "segments": nseg,
                 "kernel": "kda_chunk_fwd (segmented when few heads) against "
                           "kda_chunk_fwd_segmented(segments=1)"})
             del fd
