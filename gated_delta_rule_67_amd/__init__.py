@@ -108,6 +108,8 @@ def library():
     lib.kda_chunk_fwd_segmented_workspace_size.restype = sz
     lib.kda_chunk_fwd_noalloc.argtypes = [vp] * 8 + [i] * 6 + [f, i, i, ctypes.c_uint, vp]
     lib.kda_chunk_fwd_noalloc.restype = i
+    lib.kda_stream_copy.argtypes = [vp, vp, sz, vp]
+    lib.kda_stream_copy.restype = i
     lib.kda_status_string.argtypes = [i]
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_version.argtypes = []
@@ -589,3 +591,16 @@ def kda_chunk_fwd_noalloc(q, k, v, g, beta, o, final_state=None, scale=None, ini
                                        _flags(qk_l2norm, beta_sigmoid), ctypes.c_void_p(stream))
     _check(rc)
     return o
+
+
+def stream_copy(src, dst):
+    """kda_stream_copy: copy the bytes of contiguous device tensor src into dst (same byte
+    size, 16-byte aligned, not overlapping) with the library's streaming copy kernel. A
+    measuring stick for HBM figures, not part of the operator."""
+    _require(src.is_cuda and dst.is_cuda, "tensors must be on a GPU")
+    _require(src.is_contiguous() and dst.is_contiguous(), "tensors must be contiguous")
+    nbytes = src.numel() * src.element_size()
+    _require(dst.numel() * dst.element_size() == nbytes, "src and dst must have the same byte size")
+    with torch.cuda.device(src.device):
+        stream = torch.cuda.current_stream(src.device).cuda_stream
+        _check(library().kda_stream_copy(_ptr(src), _ptr(dst), nbytes, ctypes.c_void_p(stream)))

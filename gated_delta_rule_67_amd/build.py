@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libkda.so")
 SOURCES = ["kda_api.hip", "kda_decode.hip", "kda_prefill.hip", "kda_chunk_bf16.hip",
-           "kda_chunk_wy.hip", "kda_chunk_bwd.hip", "kda_gate.hip"]
+           "kda_chunk_wy.hip", "kda_chunk_bwd.hip", "kda_gate.hip", "kda_stream.hip"]
 
 
 def hipcc():

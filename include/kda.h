@@ -402,10 +402,11 @@ int kda_chunk_fwd_segmented(const void* q, const void* k, const void* v, const v
  * KDA_NOALLOC_SCRATCH_BYTES that the library's code object holds on every GPU it is loaded
  * on, until the process ends (its address on the current device is looked up once per
  * device). Same arguments, arithmetic and results as kda_chunk_fwd_ex with a workspace of
- * kda_chunk_fwd_workspace_size() bytes, bit for bit: when that size exceeds the array (the
- * segmented route for few heads), the plain two-kernel path is taken if its own workspace
- * fits, else the call returns KDA_ERR_SCRATCH before anything is enqueued. Calls whose path
- * needs no workspace (float32, K % 8 != 0, ...) run as kda_chunk_fwd_ex without one.
+ * kda_chunk_fwd_workspace_size() bytes, bit for bit, whenever that size fits the array. When
+ * it does not (the segmented route for few heads), the plain two-kernel path is taken if its
+ * own workspace fits (results as kda_chunk_fwd_segmented with one segment), else the call
+ * returns KDA_ERR_SCRATCH before anything is enqueued. Calls whose path needs no workspace
+ * (float32, K % 8 != 0, ...) run as kda_chunk_fwd_ex without one.
  *
  * The current device must be the device of `stream` (as for torch's current stream). Every
  * call on a GPU shares that GPU's array: calls that overlap on one GPU (two streams, two
@@ -419,6 +420,15 @@ int kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const voi
                           const void* beta, const float* initial_state, float* final_state,
                           void* o, int B, int T, int H, int HV, int K, int V, float scale,
                           int chunk_size, int dtype, unsigned flags, void* stream);
+
+/*
+ * A plain streaming copy of `bytes` bytes from src to dst (device memory, 16-byte aligned,
+ * not overlapping; bytes % 16 == 0; else KDA_ERR_INVALID; 0 bytes: nothing is enqueued),
+ * with non-temporal 16-byte loads and stores. Not part of the operator: it measures the read +
+ * write bandwidth a simple kernel reaches on the device, the practical ceiling against which
+ * the kernels' HBM figures are read (the benchmark's copy ceiling).
+ */
+int kda_stream_copy(const void* src, void* dst, size_t bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -493,3 +493,19 @@ def test_noalloc_scratch_constant_matches_header():
 def test_noalloc_rejects_before_any_launch(lib, bad, rc):
     assert _noalloc(lib, **bad) == rc
     assert "scratch" in kda.status_string(kda.KDA_ERR_SCRATCH)
+
+
+@pytest.mark.parametrize("src,dst,nbytes", [
+    (None, ctypes.c_void_p(0x2000), 64),                     # null source
+    (ctypes.c_void_p(0x1000), None, 64),                     # null destination
+    (ctypes.c_void_p(0x1000), ctypes.c_void_p(0x100000), 24),  # not a multiple of 16 bytes
+    (ctypes.c_void_p(0x1008), ctypes.c_void_p(0x100000), 64),  # misaligned source
+    (ctypes.c_void_p(0x1000), ctypes.c_void_p(0x1020), 64),    # overlapping ranges
+])
+def test_stream_copy_rejects_invalid_arguments(lib, src, dst, nbytes):
+    # every call fails validation before anything is enqueued (the pointers are never touched)
+    assert lib.kda_stream_copy(src, dst, nbytes, None) == kda.KDA_ERR_INVALID
+
+
+def test_stream_copy_of_nothing_is_ok(lib):
+    assert lib.kda_stream_copy(None, None, 0, None) == kda.KDA_OK
