@@ -6,6 +6,8 @@
 // kernel with ordinary cached accesses).
 #include <hip/hip_runtime.h>
 
+#include <cstdint>
+
 #include "kda.h"
 
 namespace kda {
@@ -39,10 +41,11 @@ __global__ __launch_bounds__(256) void stream_copy_kernel(const u32x4* __restric
 extern "C" int kda_stream_copy(const void* src, void* dst, size_t bytes, void* stream) {
   if (bytes == 0) return KDA_OK;
   if (!src || !dst || bytes % 16 != 0) return KDA_ERR_INVALID;
-  if ((reinterpret_cast<size_t>(src) | reinterpret_cast<size_t>(dst)) % 16 != 0) return KDA_ERR_INVALID;
-  const char* s = static_cast<const char*>(src);
-  const char* d = static_cast<const char*>(dst);
-  if (s < d + bytes && d < s + bytes) return KDA_ERR_INVALID;  // overlapping ranges
+  const uintptr_t s = reinterpret_cast<uintptr_t>(src), d = reinterpret_cast<uintptr_t>(dst);
+  if ((s | d) % 16 != 0) return KDA_ERR_INVALID;
+  // overlapping ranges (as integers: either range ending past the address space is rejected)
+  if (s > UINTPTR_MAX - bytes || d > UINTPTR_MAX - bytes) return KDA_ERR_INVALID;
+  if (s < d + bytes && d < s + bytes) return KDA_ERR_INVALID;
   const size_t n = bytes / 16;
   const size_t rounds = (n + 256 * kda::kUnroll - 1) / (256 * kda::kUnroll);
   const int grid = rounds < (size_t)kda::kGrid ? (int)rounds : kda::kGrid;
