@@ -58,10 +58,10 @@ MFMA_BF16_PEAK_TFS = 2516.6     # MI355X dense bf16 MFMA, published (no sparsity
 METRIC = "KDA prefill tokens/s + MFMA util (H=16,K=V=128,T=8192); decode state HBM GB/s"
 PREFILL_KERNELS = ["kda::wy::factors_kernel<128, false, false, false>",
                    "kda::wy::factors_exact_kernel<128, false, false, false>",
-                   "kda::wy::state_kernel<128, 2, false>"]
+                   "kda::wy::state_kernel<128, 2, false, true>"]
 LONG_KERNELS = ["kda::wy::factors_kernel<128, false, false, false>",
                 "kda::wy::factors_exact_kernel<128, false, false, false>",
-                "kda::wy::state_kernel<128, 4, false>"]
+                "kda::wy::state_kernel<128, 4, false, true>"]
 PREFILL_WORKLOAD = "prefill-B4-T8192-H16-K128"
 LONG_WORKLOAD = "prefill-B1-T32768-H96-K128"
 DECODE_WORKLOAD = "decode-B256-H16-K128-64steps"

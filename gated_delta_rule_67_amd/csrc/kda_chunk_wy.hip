@@ -753,7 +753,9 @@ __device__ __forceinline__ void wait_vmem() {
 // perm32(rho)); the DMA waves stream the next chunk's factors into the other LDS buffer, so
 // the compute waves never wait on memory issue.
 
-template <int KT, int NW, bool VARLEN>
+// OUT = false: no o (the segmented path's maps pass); the readout P, O and its tiles are left
+// out of the chunk step (an instantiation of its own, so the other keeps its registers).
+template <int KT, int NW, bool VARLEN, bool OUT = true>
 __global__ __launch_bounds__(64 * (NW + kDmaWaves)) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void state_kernel(WyArgs a) {
   using W = Blk<KT>;
@@ -899,6 +901,7 @@ void state_kernel(WyArgs a) {
       }
   }
 
+  constexpr bool out = OUT;
   auto step = [&](const unsigned char* bk, lds_u8* bkl, int n) {
     const int t0 = n * kC, nrow = min(kC, len - t0);
     auto frag_q = [&](int tile, int J, int m) {  // rows of Q*Gam / K*Gam
@@ -919,7 +922,7 @@ void state_kernel(WyArgs a) {
 #pragma unroll
     for (int J = 0; J < 4; ++J) {
       fx[0][J] = frag_q(W::kg, J, 0);
-      fx[0][4 + J] = frag_q(W::qg, J, 0);
+      if constexpr (out) fx[0][4 + J] = frag_q(W::qg, J, 0);
     }
     bf16x8 ft[6], fa[6];  // T and Aq fragments (I, m <= I/2), loaded under the X/P products
 #pragma unroll
@@ -928,7 +931,7 @@ void state_kernel(WyArgs a) {
 #pragma unroll
         for (int J = 0; J < 4; ++J) {
           fx[(m + 1) & 1][J] = frag_q(W::kg, J, m + 1);
-          fx[(m + 1) & 1][4 + J] = frag_q(W::qg, J, m + 1);
+          if constexpr (out) fx[(m + 1) & 1][4 + J] = frag_q(W::qg, J, m + 1);
         }
       }
       if (m == NKS - 1) {
@@ -937,14 +940,14 @@ void state_kernel(WyArgs a) {
 #pragma unroll
           for (int mm = 0; mm <= I / 2; ++mm, ++f) {
             ft[f] = frag_tri(W::t, 16 * I + lr, mm);
-            fa[f] = frag_tri(W::aq, 16 * I + lr, mm);
+            if constexpr (out) fa[f] = frag_tri(W::aq, 16 * I + lr, mm);
           }
       }
       const bf16x8 sb = cat8(cvt4(S[2 * m]), cvt4(S[2 * m + 1]));
 #pragma unroll
       for (int J = 0; J < 4; ++J) {
         X[J] = mfma32(fx[m & 1][J], sb, X[J]);
-        P[J] = mfma32(fx[m & 1][4 + J], sb, P[J]);
+        if constexpr (out) P[J] = mfma32(fx[m & 1][4 + J], sb, P[J]);
       }
     }
     // beta (V - X) as bf16 pairs (hi + lo), B operands of the 32-token steps
@@ -999,32 +1002,34 @@ void state_kernel(WyArgs a) {
       ub[m] = cat8(h0, h1);
       ul[m] = cat8(l0, l1);
     }
-    // O = scale (P + Aq U), Aq's diagonal tiles with their residual (Blk::aql). In the A
-    // fragment of step I/2, element e of lane (lr, lq) is token 16 (e >> 2) + 4 lq + (e & 3)
-    // of the step (the order of the U operand), so block I's diagonal tile fills elements
-    // 4 (I & 1) .. + 3 of every lane and the other four are zero.
-    bf16x8 fl[4];
+    if constexpr (out) {
+      // O = scale (P + Aq U), Aq's diagonal tiles with their residual (Blk::aql). In the A
+      // fragment of step I/2, element e of lane (lr, lq) is token 16 (e >> 2) + 4 lq + (e & 3)
+      // of the step (the order of the U operand), so block I's diagonal tile fills elements
+      // 4 (I & 1) .. + 3 of every lane and the other four are zero.
+      bf16x8 fl[4];
 #pragma unroll
-    for (int I = 0; I < 4; ++I) {
-      const bf16x4 t = load4(bk + W::aql + ((16 * I + lr) * 16 + 4 * lq) * 2);
-      fl[I] = (I & 1) ? cat8(bf16x4{}, t) : cat8(t, bf16x4{});
+      for (int I = 0; I < 4; ++I) {
+        const bf16x4 t = load4(bk + W::aql + ((16 * I + lr) * 16 + 4 * lq) * 2);
+        fl[I] = (I & 1) ? cat8(bf16x4{}, t) : cat8(t, bf16x4{});
+      }
+      f32x4 O[4];
+      O[0] = mfma32(fl[0], ub[0], mfma32(fa[0], ul[0], mfma32(fa[0], ub[0], P[0])));
+      O[1] = mfma32(fl[1], ub[0], mfma32(fa[1], ul[0], mfma32(fa[1], ub[0], P[1])));
+      O[2] = mfma32(fl[2], ub[1], mfma32(fa[3], ul[1], mfma32(fa[3], ub[1],
+             mfma32(fa[2], ul[0], mfma32(fa[2], ub[0], P[2])))));
+      O[3] = mfma32(fl[3], ub[1], mfma32(fa[5], ul[1], mfma32(fa[5], ub[1],
+             mfma32(fa[4], ul[0], mfma32(fa[4], ub[0], P[3])))));
+      // stores go out before the state update so they drain under its products
+      const auto ro_ = make_rsrc(static_cast<const bf16*>(p.o) + (((size_t)bos + t0) * p.HV + hv) * VW,
+                                 p.o ? (unsigned)nrow * rowb : 0u);  // no o: stores dropped
+#pragma unroll
+      for (int I = 0; I < 4; ++I)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, static_cast<bf16>(p.scale * O[I][r])),
+                                                ro_, vlane, (16 * I + r) * rowb, 0);
     }
-    f32x4 O[4];
-    O[0] = mfma32(fl[0], ub[0], mfma32(fa[0], ul[0], mfma32(fa[0], ub[0], P[0])));
-    O[1] = mfma32(fl[1], ub[0], mfma32(fa[1], ul[0], mfma32(fa[1], ub[0], P[1])));
-    O[2] = mfma32(fl[2], ub[1], mfma32(fa[3], ul[1], mfma32(fa[3], ub[1],
-           mfma32(fa[2], ul[0], mfma32(fa[2], ub[0], P[2])))));
-    O[3] = mfma32(fl[3], ub[1], mfma32(fa[5], ul[1], mfma32(fa[5], ub[1],
-           mfma32(fa[4], ul[0], mfma32(fa[4], ub[0], P[3])))));
-    // stores go out before the state update so they drain under its products
-    const auto ro_ = make_rsrc(static_cast<const bf16*>(p.o) + (((size_t)bos + t0) * p.HV + hv) * VW,
-                               p.o ? (unsigned)nrow * rowb : 0u);  // no o: stores dropped
-#pragma unroll
-    for (int I = 0; I < 4; ++I)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, static_cast<bf16>(p.scale * O[I][r])),
-                                              ro_, vlane, (16 * I + r) * rowb, 0);
     // S = diag(Gam_C) S + (K*Gam_C/Gam)^T U
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct)
@@ -1103,8 +1108,10 @@ hipError_t launch_state(const WyArgs& a, hipStream_t stream) {
   const dim3 grid(a.p.B * a.p.HV * nvt), block(64 * (NW + kDmaWaves));
   if (vl)
     hipLaunchKernelGGL((state_kernel<KT, NW, true>), grid, block, 0, stream, a);
-  else
+  else if (a.p.o)
     hipLaunchKernelGGL((state_kernel<KT, NW, false>), grid, block, 0, stream, a);
+  else  // no outputs: the segmented path's maps
+    hipLaunchKernelGGL((state_kernel<KT, NW, false, false>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
